@@ -1,0 +1,352 @@
+/*
+ * hstu_oracle.c -- fp64 CPU oracle of the HSTU pointwise aggregated attention
+ * path (attention core, LayerNorm*U gate, layer with f1/f2, M-FALCON scores,
+ * and a brute-force enumeration of the non-empty (query tile, key tile) set).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library.  It shares no code,
+ * header, table or helper with the HIP path.
+ *
+ * Everything is a plain loop in double precision, written from the
+ * definitions, with no blocking, fusion or reordering:
+ *   - "生成式推荐（一）：HSTU", section "高性能自注意力Encoder：HSTU": a layer is
+ *     pointwise projection -> spatial aggregation -> pointwise transformation;
+ *     f1 and f2 are single linear layers, phi1 = phi2 = SiLU, Norm = LayerNorm,
+ *     rab^{p,t} combines position and time.
+ *   - same page, section "Pointwise aggregated attention": the aggregated
+ *     output enters the layer as Norm(A(X)V(X)) (.) U(X); weights are not
+ *     normalised over the sequence (no softmax).
+ *   - "Meta HSTU: как действия пользователя стали основой большой
+ *     рекомендательной модели", section "Что меняется внутри HSTU по сравнению
+ *     с обычным Transformer": Q, K, V and U are built together; aggregation
+ *     uses relative position and time biases; the result is normalised, gated
+ *     by U, transformed, and added through a residual.
+ *   - "行动胜于言语：万亿参数序列转导器用于生成式推荐", section "7. 模型细节":
+ *     normalised attention without softmax (a fixed 1/n scale, given here as
+ *     alpha); section "2.3 M-FALCON算法" and the page "生成式推荐（一）：HSTU",
+ *     section "M-FALCON": b_m candidates share one pass through a modified
+ *     mask and bias.
+ * Readings taken where the pages are silent are listed in the design notes
+ * and repeated at each function below.
+ *
+ * Parallelism: OpenMP over independent (sequence, head) units only.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ACT_SILU 0
+#define ORACLE_ACT_IDENTITY 1
+
+/* ------------------------------------------------------------------------ */
+/* Scalar definitions                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Number of significant bits of x (0 for x == 0). */
+static int bit_length_u64(uint64_t x) {
+    int n = 0;
+    while (x != 0) {
+        ++n;
+        x >>= 1;
+    }
+    return n;
+}
+
+/* Time bucket of a pair: log2 buckets of the absolute time gap in seconds,
+ * bucket = min(NT - 1, bit_length(|t_i - t_j|)).  Reading of "rab^{p,t}"
+ * ("生成式推荐（一）：HSTU", symbol list of the layer equations). */
+int32_t hstu_oracle_time_bucket(int64_t t_i, int64_t t_j, int32_t num_time_buckets) {
+    uint64_t gap = (t_i >= t_j) ? (uint64_t)t_i - (uint64_t)t_j : (uint64_t)t_j - (uint64_t)t_i;
+    int b = bit_length_u64(gap);
+    return b < num_time_buckets - 1 ? b : num_time_buckets - 1;
+}
+
+/* Position of row i in a sequence with n_hist history rows: history rows keep
+ * their index, every candidate row sits at position n_hist (just after the
+ * history).  Reading of the M-FALCON bias change ("生成式推荐（一）：HSTU",
+ * section "M-FALCON"): each candidate sees the history exactly as a single
+ * appended target would. */
+static int32_t position_of(int32_t i, int32_t n_hist) { return i < n_hist ? i : n_hist; }
+
+/* Position bucket: min(p(i) - p(j), P - 1); p(i) >= p(j) for visible pairs. */
+int32_t hstu_oracle_pos_bucket(int32_t i, int32_t j, int32_t n_hist, int32_t num_pos_buckets) {
+    int32_t diff = position_of(i, n_hist) - position_of(j, n_hist);
+    if (diff < 0) diff = 0; /* never reached for a visible pair */
+    return diff < num_pos_buckets - 1 ? diff : num_pos_buckets - 1;
+}
+
+/* Visibility of key j from query i in a sequence of L rows whose first n_hist
+ * rows are history (n_hist == L: plain causal sequence).
+ *   history row i:   sees j <= i (causal: an event sees itself and the past);
+ *   candidate row i: sees every history row and itself, no other candidate.
+ */
+int32_t hstu_oracle_visible(int32_t i, int32_t j, int32_t L, int32_t n_hist) {
+    if (i < 0 || j < 0 || i >= L || j >= L) return 0;
+    if (i < n_hist) return j <= i;
+    return (j < n_hist) || (j == i);
+}
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + e^{-x}). */
+double hstu_oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* ------------------------------------------------------------------------ */
+/* Jagged batch helpers                                                      */
+/* ------------------------------------------------------------------------ */
+
+static int32_t seq_len(const int32_t* offsets, const int32_t* lengths, int32_t b) {
+    return lengths ? lengths[b] : offsets[b + 1] - offsets[b];
+}
+
+static int32_t seq_hist(const int32_t* offsets, const int32_t* lengths,
+                        const int32_t* num_candidates, int32_t b) {
+    int32_t L = seq_len(offsets, lengths, b);
+    return num_candidates ? L - num_candidates[b] : L;
+}
+
+static void set_threads(int32_t num_threads) {
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+}
+
+int32_t hstu_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention core                                                            */
+/*   O[i, h, :] = alpha * sum_{j visible from i} act(S_ij) * V[j, h, :]       */
+/*   S_ij = <Q[i, h, :], K[j, h, :]> + rab_pos[pb(i,j)] + rab_time[tb(i,j)]   */
+/* Sums run over j ascending.  Row r of sequence b is offsets[b] + r.        */
+/* Tables are per head when rab_head_stride > 0, shared when it is 0.        */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_attn(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                      const int32_t* offsets, const int32_t* lengths,
+                      const int32_t* num_candidates,
+                      const double* q, int64_t q_stride,
+                      const double* k, int64_t k_stride,
+                      const double* v, int64_t v_stride,
+                      const int64_t* timestamps,
+                      const double* rab_pos, int32_t num_pos_buckets,
+                      const double* rab_time, int32_t num_time_buckets,
+                      int64_t rab_pos_head_stride, int64_t rab_time_head_stride,
+                      double alpha, int32_t act,
+                      double* o, int64_t o_stride, int32_t num_threads) {
+    set_threads(num_threads);
+    int64_t units = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t unit = 0; unit < units; ++unit) {
+        int32_t b = (int32_t)(unit / H);
+        int32_t h = (int32_t)(unit % H);
+        int32_t L = seq_len(offsets, lengths, b);
+        int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+        int64_t base = offsets[b];
+        const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
+        const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
+        double* acc = (double*)malloc(sizeof(double) * (size_t)(d_v > 0 ? d_v : 1));
+        for (int32_t i = 0; i < L; ++i) {
+            const double* qi = q + (base + i) * q_stride + (int64_t)h * d_qk;
+            for (int32_t c = 0; c < d_v; ++c) acc[c] = 0.0;
+            for (int32_t j = 0; j < L; ++j) {
+                if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
+                const double* kj = k + (base + j) * k_stride + (int64_t)h * d_qk;
+                double s = 0.0;
+                for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
+                s += rp[hstu_oracle_pos_bucket(i, j, n_hist, num_pos_buckets)];
+                s += rt[hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j],
+                                                num_time_buckets)];
+                double a = (act == ORACLE_ACT_IDENTITY) ? s : hstu_oracle_silu(s);
+                const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
+                for (int32_t c = 0; c < d_v; ++c) acc[c] += a * vj[c];
+            }
+            double* oi = o + (base + i) * o_stride + (int64_t)h * d_v;
+            for (int32_t c = 0; c < d_v; ++c) oi[c] = alpha * acc[c];
+        }
+        free(acc);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pointwise transformation gate: Y = LayerNorm(o) (.) U per row.            */
+/* LayerNorm over the row's `width` values (all heads concatenated), biased  */
+/* variance, no affine parameters, eps added to the variance.                */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_ln_gate(int64_t rows, int32_t width,
+                         const double* o, int64_t o_stride,
+                         const double* u, int64_t u_stride,
+                         double eps, double* y, int64_t y_stride, int32_t num_threads) {
+    set_threads(num_threads);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* orow = o + r * o_stride;
+        const double* urow = u + r * u_stride;
+        double* yrow = y + r * y_stride;
+        double mean = 0.0;
+        for (int32_t c = 0; c < width; ++c) mean += orow[c];
+        mean /= (double)width;
+        double var = 0.0;
+        for (int32_t c = 0; c < width; ++c) var += (orow[c] - mean) * (orow[c] - mean);
+        var /= (double)width;
+        double inv = 1.0 / sqrt(var + eps);
+        for (int32_t c = 0; c < width; ++c) yrow[c] = (orow[c] - mean) * inv * urow[c];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Linear layer: out[t, n] = bias[n] + sum_k x[t, k] * w[n, k]  (w is out x in) */
+/* ------------------------------------------------------------------------ */
+static void linear(int64_t rows, int32_t n_out, int32_t n_in, const double* x, int64_t x_stride,
+                   const double* w, const double* bias, double* out, int64_t out_stride) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < rows; ++t) {
+        for (int32_t n = 0; n < n_out; ++n) {
+            double s = bias ? bias[n] : 0.0;
+            for (int32_t kk = 0; kk < n_in; ++kk) s += x[t * x_stride + kk] * w[(int64_t)n * n_in + kk];
+            out[t * out_stride + n] = s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* One HSTU layer over a packed jagged batch (rows offsets[0] .. offsets[B]). */
+/*   Z = SiLU(X W1^T + b1), split by columns into U | V | Q | K (each H*d,    */
+/*   head h at sub-columns h*d .. h*d+d-1);                                   */
+/*   O = attention(Q, K, V);  Y = LayerNorm(O) (.) U;                         */
+/*   X_out = X + Y W2^T + b2.                                                 */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_layer(int32_t B, int32_t H, int32_t d, int32_t D,
+                       const int32_t* offsets, const int32_t* num_candidates,
+                       const double* x, const double* w1, const double* b1,
+                       const double* w2, const double* b2,
+                       const int64_t* timestamps,
+                       const double* rab_pos, int32_t num_pos_buckets,
+                       const double* rab_time, int32_t num_time_buckets,
+                       double alpha, double eps, double* x_out, int32_t num_threads) {
+    set_threads(num_threads);
+    int64_t row0 = offsets[0];
+    int64_t T = (int64_t)offsets[B] - row0;
+    int32_t hd = H * d;
+    int32_t zw = 4 * hd;
+    double* z = (double*)malloc(sizeof(double) * (size_t)(T * zw + 1));
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(T * hd + 1));
+    double* yb = (double*)malloc(sizeof(double) * (size_t)(T * hd + 1));
+    /* offsets rebased to the start of the packed buffers */
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B + 1));
+    for (int32_t b = 0; b <= B; ++b) off[b] = (int32_t)(offsets[b] - row0);
+
+    linear(T, zw, D, x + row0 * D, D, w1, b1, z, zw);
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < T * zw; ++e) z[e] = hstu_oracle_silu(z[e]);
+
+    const double* U = z + 0 * hd;
+    const double* V = z + 1 * hd;
+    const double* Q = z + 2 * hd;
+    const double* K = z + 3 * hd;
+    hstu_oracle_attn(B, H, d, d, off, NULL, num_candidates, Q, zw, K, zw, V, zw,
+                     timestamps + row0, rab_pos, num_pos_buckets, rab_time, num_time_buckets,
+                     0, 0, alpha, ORACLE_ACT_SILU, ob, hd, num_threads);
+    hstu_oracle_ln_gate(T, hd, ob, hd, U, zw, eps, yb, hd, num_threads);
+    linear(T, D, hd, yb, hd, w2, b2, x_out + row0 * D, D);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t m = 0; m < D; ++m) x_out[(row0 + t) * D + m] += x[(row0 + t) * D + m];
+    free(off);
+    free(yb);
+    free(ob);
+    free(z);
+}
+
+/* ------------------------------------------------------------------------ */
+/* M-FALCON ranking scores: for candidate c of sequence b,                    */
+/*   s[b, c] = < Y[n_b + c, :], w >,  Y = LayerNorm(O) (.) U over H*d_v.       */
+/* The attention output is computed for all rows in one pass (history rows   */
+/* causal, candidates see the history and themselves).                        */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_mfalcon_score(int32_t B, int32_t H, int32_t d,
+                               const int32_t* offsets, const int32_t* num_candidates,
+                               const double* q, const double* k, const double* v,
+                               const double* u, int64_t stride,
+                               const int64_t* timestamps,
+                               const double* rab_pos, int32_t num_pos_buckets,
+                               const double* rab_time, int32_t num_time_buckets,
+                               double alpha, double eps, const double* w,
+                               double* scores, int32_t score_stride, int32_t num_threads) {
+    set_threads(num_threads);
+    int64_t T = offsets[B];
+    int32_t hd = H * d;
+    double* ob = (double*)malloc(sizeof(double) * (size_t)(T * hd + 1));
+    double* yrow = (double*)malloc(sizeof(double) * (size_t)hd);
+    hstu_oracle_attn(B, H, d, d, offsets, NULL, num_candidates, q, stride, k, stride, v, stride,
+                     timestamps, rab_pos, num_pos_buckets, rab_time, num_time_buckets, 0, 0,
+                     alpha, ORACLE_ACT_SILU, ob, hd, num_threads);
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t L = offsets[b + 1] - offsets[b];
+        int32_t c_b = num_candidates[b];
+        int32_t n_b = L - c_b;
+        for (int32_t c = 0; c < c_b; ++c) {
+            int64_t row = (int64_t)offsets[b] + n_b + c;
+            hstu_oracle_ln_gate(1, hd, ob + row * hd, hd, u + row * stride, stride, eps, yrow, hd, 1);
+            double s = 0.0;
+            for (int32_t m = 0; m < hd; ++m) s += yrow[m] * w[m];
+            scores[(int64_t)b * score_stride + c] = s;
+        }
+    }
+    free(yrow);
+    free(ob);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Brute-force set of non-empty tiles: (b, query tile, key tile) such that   */
+/* some visible pair (i, j) has i / tile_m == query tile and j / tile_n ==    */
+/* key tile.  Written in ascending (b, qt, kt) order; returns the count.     */
+/* ------------------------------------------------------------------------ */
+int64_t hstu_oracle_tiles(int32_t B, const int32_t* offsets, const int32_t* lengths,
+                          const int32_t* num_candidates, int32_t tile_m, int32_t tile_n,
+                          int32_t* out, int64_t cap) {
+    int64_t count = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t L = seq_len(offsets, lengths, b);
+        int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+        int32_t nq = (L + tile_m - 1) / tile_m;
+        int32_t nk = (L + tile_n - 1) / tile_n;
+        unsigned char* mark = (unsigned char*)calloc((size_t)nq * nk + 1, 1);
+        for (int32_t i = 0; i < L; ++i)
+            for (int32_t j = 0; j < L; ++j)
+                if (hstu_oracle_visible(i, j, L, n_hist)) mark[(i / tile_m) * nk + (j / tile_n)] = 1;
+        for (int32_t qt = 0; qt < nq; ++qt)
+            for (int32_t kt = 0; kt < nk; ++kt)
+                if (mark[qt * nk + kt]) {
+                    if (count < cap) {
+                        out[3 * count + 0] = b;
+                        out[3 * count + 1] = qt;
+                        out[3 * count + 2] = kt;
+                    }
+                    ++count;
+                }
+        free(mark);
+    }
+    return count;
+}
+
+/* Number of visible (i, j) pairs over the batch, by enumeration. */
+int64_t hstu_oracle_count_visible(int32_t B, const int32_t* offsets, const int32_t* lengths,
+                                  const int32_t* num_candidates) {
+    int64_t count = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t L = seq_len(offsets, lengths, b);
+        int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+        for (int32_t i = 0; i < L; ++i)
+            for (int32_t j = 0; j < L; ++j) count += hstu_oracle_visible(i, j, L, n_hist);
+    }
+    return count;
+}
