@@ -1,0 +1,65 @@
+"""Build libhstu.so (gfx950) from csrc/ with hipcc, in-tree.
+
+Usage: python -m hstu_sequential_transducer_causal_amd.build [-v]
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libhstu.so")
+ARCH = os.environ.get("HSTU_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["abi.hip", "sched.hip", "attn_bf16.hip", "attn_f32.hip", "epilogue.hip", "gemm.hip"]
+
+CXXFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    # packed fp32 VALU ops stay off: they are not trusted on this hardware
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(os.path.dirname(HERE), "include"),
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    p = os.path.join(rocm, "bin", "hipcc")
+    return p if os.path.exists(p) else "hipcc"
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+    if out.strip() and verbose:
+        print(out, flush=True)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libhstu.so (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,437 @@
+// abi.hip -- the C ABI of libhstu.so (declared in include/hstu.h): argument
+// validation, workspace carving and kernel dispatch on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+#include "../../include/hstu.h"
+
+namespace hstu {
+
+int device_cu_count() {
+    static int counts[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (counts[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        counts[dev] = c;
+    }
+    return counts[dev];
+}
+
+}  // namespace hstu
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hstu_status fail(hstu_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+hstu_status ok() {
+    g_last_error[0] = '\0';
+    return HSTU_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int tile_m_for(int dtype) { return dtype == HSTU_BF16 ? hstu::kBf16TileM : hstu::kF32TileM; }
+int tile_n_for(int dtype) { return dtype == HSTU_BF16 ? hstu::kBf16TileN : hstu::kF32TileN; }
+
+// Checks everything that can be checked on the host; with need_epi the
+// LN*U epilogue arguments are required even if y is NULL.
+hstu_status validate_attn(const hstu_attn_args* a, bool need_epi) {
+    if (!a) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (a->struct_size != sizeof(hstu_attn_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_attn_args) %zu", a->struct_size,
+                    sizeof(hstu_attn_args));
+    if (a->B < 0) return fail(HSTU_ERR_ARG, "B = %d < 0", a->B);
+    if (a->H < 1) return fail(HSTU_ERR_ARG, "H = %d < 1", a->H);
+    if (a->d_qk < 1 || a->d_v < 1) return fail(HSTU_ERR_ARG, "head dims must be >= 1");
+    if (a->max_seq_len < 0 || a->max_seq_len > hstu::kMaxSeqLen)
+        return fail(HSTU_ERR_ARG, "max_seq_len %d outside [0, %d]", a->max_seq_len, hstu::kMaxSeqLen);
+    if (a->num_rows < 0) return fail(HSTU_ERR_ARG, "num_rows < 0");
+    if (a->dtype != HSTU_F32 && a->dtype != HSTU_BF16) return fail(HSTU_ERR_ARG, "unknown dtype %d", a->dtype);
+    if (a->act != HSTU_ACT_SILU && a->act != HSTU_ACT_IDENTITY) return fail(HSTU_ERR_ARG, "unknown act %d", a->act);
+    if (a->dtype == HSTU_BF16 && !(a->d_qk == 128 && a->d_v == 128))
+        return fail(HSTU_ERR_UNSUPPORTED, "bf16 needs d_qk = d_v = 128 (got %d, %d)", a->d_qk, a->d_v);
+    if (a->dtype == HSTU_F32 && !(a->d_qk == a->d_v && (a->d_qk == 32 || a->d_qk == 64)))
+        return fail(HSTU_ERR_UNSUPPORTED, "fp32 needs d_qk = d_v in {32, 64} (got %d, %d)", a->d_qk, a->d_v);
+    if (a->num_pos_buckets < 1 || a->num_pos_buckets > hstu::kMaxPosBuckets)
+        return fail(HSTU_ERR_ARG, "num_pos_buckets %d outside [1, %d]", a->num_pos_buckets, hstu::kMaxPosBuckets);
+    if (a->num_time_buckets < 1) return fail(HSTU_ERR_ARG, "num_time_buckets %d < 1", a->num_time_buckets);
+    if (a->rab_pos_head_stride < 0 || a->rab_time_head_stride < 0)
+        return fail(HSTU_ERR_ARG, "negative bias-table head stride");
+    if (!std::isfinite(a->alpha)) return fail(HSTU_ERR_ARG, "alpha is not finite");
+    const int64_t hq = int64_t(a->H) * a->d_qk, hv = int64_t(a->H) * a->d_v;
+    if (a->q_stride < hq || a->k_stride < hq) return fail(HSTU_ERR_ARG, "q/k stride < H*d_qk");
+    if (a->v_stride < hv || a->o_stride < hv) return fail(HSTU_ERR_ARG, "v/o stride < H*d_v");
+    const bool epi = need_epi || a->y != nullptr;
+    if (epi) {
+        if (!(a->ln_eps > 0.0f) || !std::isfinite(a->ln_eps)) return fail(HSTU_ERR_ARG, "ln_eps must be > 0");
+        if (a->u_stride < hv) return fail(HSTU_ERR_ARG, "u stride < H*d_v");
+        if (a->y && a->y_stride < hv) return fail(HSTU_ERR_ARG, "y stride < H*d_v");
+        if (hv % 8 != 0 || hv > 4096) return fail(HSTU_ERR_UNSUPPORTED, "epilogue needs H*d_v %% 8 == 0 and <= 4096");
+    }
+    if (a->B > 0) {
+        if (!a->seq_offsets) return fail(HSTU_ERR_ARG, "seq_offsets is NULL");
+        if (!a->q || !a->k || !a->v || !a->o) return fail(HSTU_ERR_ARG, "q, k, v and o must be non-NULL");
+        if (!a->timestamps) return fail(HSTU_ERR_ARG, "timestamps is NULL");
+        if (!a->rab_pos || !a->rab_time) return fail(HSTU_ERR_ARG, "bias tables must be non-NULL");
+        if (epi && !a->u) return fail(HSTU_ERR_ARG, "u is NULL but the LN*U epilogue is requested");
+        if (a->dtype == HSTU_BF16) {
+            if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || (a->q_stride % 8) || (a->k_stride % 8) ||
+                (a->v_stride % 8))
+                return fail(HSTU_ERR_UNSUPPORTED, "bf16 q/k/v rows must be 16-byte aligned");
+        }
+        if (epi) {
+            const int64_t vec = a->dtype == HSTU_BF16 ? 8 : 4;
+            if (!aligned16(a->o) || (a->o_stride % vec) || !aligned16(a->u) || (a->u_stride % vec) ||
+                (a->y && (!aligned16(a->y) || (a->y_stride % vec))))
+                return fail(HSTU_ERR_UNSUPPORTED, "epilogue rows must be 16-byte aligned");
+        }
+    }
+    return HSTU_OK;
+}
+
+hstu_status check_workspace(void* ws, size_t have, size_t need) {
+    if (need == 0) return HSTU_OK;
+    if (!ws) return fail(HSTU_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(ws)) return fail(HSTU_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (have < need) return fail(HSTU_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+    return HSTU_OK;
+}
+
+hstu_status device_error(hipError_t e, const char* what) {
+    return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Sched {
+    hstu::SchedLayout layout;
+    int32_t* ctrl;
+    int32_t* qscan;
+    hstu::WorkItem* items;
+};
+
+Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
+    Sched s;
+    s.layout = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), base);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    s.ctrl = reinterpret_cast<int32_t*>(w + s.layout.off_ctrl);
+    s.qscan = reinterpret_cast<int32_t*>(w + s.layout.off_qscan);
+    s.items = reinterpret_cast<hstu::WorkItem*>(w + s.layout.off_items);
+    return s;
+}
+
+hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
+    hstu::SchedArgs sa;
+    sa.B = a->B;
+    sa.offsets = a->seq_offsets;
+    sa.lengths = a->seq_lengths;
+    sa.ncand = a->num_candidates;
+    sa.tile_m = tile_m_for(a->dtype);
+    sa.tile_n = tile_n_for(a->dtype);
+    sa.ctrl = s.ctrl;
+    sa.qscan = s.qscan;
+    sa.items = s.items;
+    return hstu::launch_sched(sa, stream);
+}
+
+hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
+    hstu::AttnCoreArgs c;
+    c.H = a->H;
+    c.d = a->d_qk;
+    c.offsets = a->seq_offsets;
+    c.lengths = a->seq_lengths;
+    c.ncand = a->num_candidates;
+    c.q = a->q; c.q_stride = a->q_stride;
+    c.k = a->k; c.k_stride = a->k_stride;
+    c.v = a->v; c.v_stride = a->v_stride;
+    c.ts = a->timestamps;
+    c.rab_pos = a->rab_pos; c.P = a->num_pos_buckets; c.rp_head_stride = a->rab_pos_head_stride;
+    c.rab_time = a->rab_time; c.NT = a->num_time_buckets; c.rt_head_stride = a->rab_time_head_stride;
+    c.alpha = a->alpha;
+    c.act = a->act;
+    c.o = a->o; c.o_stride = a->o_stride;
+    c.items = s.items;
+    c.ctrl = s.ctrl;
+    c.cursor = s.ctrl + 1;
+    hipError_t e;
+    if (a->ev_core_begin) {
+        e = hipEventRecord(static_cast<hipEvent_t>(a->ev_core_begin), stream);
+        if (e != hipSuccess) return e;
+    }
+    e = a->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(c, stream) : hstu::launch_attn_f32(c, stream);
+    if (e != hipSuccess) return e;
+    if (a->ev_core_end) e = hipEventRecord(static_cast<hipEvent_t>(a->ev_core_end), stream);
+    return e;
+}
+
+hipError_t run_ln_gate(const hstu_attn_args* a, const float* w, float* scores, int score_stride,
+                       hipStream_t stream) {
+    hstu::LnGateArgs l;
+    l.B = a->B;
+    l.num_rows = a->num_rows;
+    l.width = a->H * a->d_v;
+    l.dtype = a->dtype;
+    l.offsets = a->seq_offsets;
+    l.lengths = a->seq_lengths;
+    l.ncand = a->num_candidates;
+    l.o = a->o; l.o_stride = a->o_stride;
+    l.u = a->u; l.u_stride = a->u_stride;
+    l.y = a->y; l.y_stride = a->y_stride;
+    l.eps = a->ln_eps;
+    l.w = w;
+    l.scores = scores;
+    l.score_stride = score_stride;
+    return hstu::launch_ln_gate(l, stream);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+const char* hstu_status_string(hstu_status s) {
+    switch (s) {
+        case HSTU_OK: return "HSTU_OK";
+        case HSTU_ERR_ARG: return "HSTU_ERR_ARG: invalid argument";
+        case HSTU_ERR_UNSUPPORTED: return "HSTU_ERR_UNSUPPORTED: no kernel for this shape or dtype";
+        case HSTU_ERR_WORKSPACE: return "HSTU_ERR_WORKSPACE: workspace missing or too small";
+        case HSTU_ERR_DEVICE: return "HSTU_ERR_DEVICE: HIP call or kernel launch failed";
+        default: return "unknown hstu_status";
+    }
+}
+
+const char* hstu_last_error(void) { return g_last_error; }
+
+size_t hstu_attn_workspace_bytes(const hstu_attn_args* a) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_attn(a, false);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+}
+
+hstu_status hstu_attn_fwd(const hstu_attn_args* a, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_attn(a, false);
+    if (st != HSTU_OK) return st;
+    if (a->B == 0) return ok();
+    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    st = check_workspace(ws, ws_bytes, need);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Sched s = carve_sched(a, ws, 0);
+    hipError_t e = run_sched(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    e = run_core(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+    if (a->y) {
+        e = run_ln_gate(a, nullptr, nullptr, 0, stream);
+        if (e != hipSuccess) return device_error(e, "epilogue launch");
+    }
+    return ok();
+}
+
+size_t hstu_mfalcon_workspace_bytes(const hstu_mfalcon_args* m) {
+    if (!m || m->struct_size != sizeof(hstu_mfalcon_args)) return 0;
+    return hstu_attn_workspace_bytes(&m->attn);
+}
+
+hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes, void* stream_) {
+    if (!m) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (m->struct_size != sizeof(hstu_mfalcon_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_mfalcon_args) %zu", m->struct_size,
+                    sizeof(hstu_mfalcon_args));
+    const hstu_attn_args* a = &m->attn;
+    hstu_status st = validate_attn(a, true);
+    if (st != HSTU_OK) return st;
+    if (m->score_stride < 1) return fail(HSTU_ERR_ARG, "score_stride < 1");
+    if (a->B == 0) return ok();
+    if (!a->num_candidates) return fail(HSTU_ERR_ARG, "num_candidates is required for M-FALCON");
+    if (!m->w || !m->scores) return fail(HSTU_ERR_ARG, "w and scores must be non-NULL");
+    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    st = check_workspace(ws, ws_bytes, need);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Sched s = carve_sched(a, ws, 0);
+    hipError_t e = run_sched(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    e = run_core(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+    e = run_ln_gate(a, m->w, m->scores, m->score_stride, stream);
+    if (e != hipSuccess) return device_error(e, "epilogue launch");
+    return ok();
+}
+
+namespace {
+
+hstu_status validate_layer(const hstu_layer_args* l) {
+    if (!l) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (l->struct_size != sizeof(hstu_layer_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_layer_args) %zu", l->struct_size,
+                    sizeof(hstu_layer_args));
+    if (l->B < 0 || l->H < 1 || l->D < 1) return fail(HSTU_ERR_ARG, "B >= 0, H >= 1, D >= 1 required");
+    if (l->d != 128) return fail(HSTU_ERR_UNSUPPORTED, "layer needs d = 128 (got %d)", l->d);
+    if (l->D % 128 != 0 || (4 * l->H * l->d) % 128 != 0)
+        return fail(HSTU_ERR_UNSUPPORTED, "layer needs D %% 128 == 0");
+    if (l->max_seq_len < 0 || l->max_seq_len > hstu::kMaxSeqLen)
+        return fail(HSTU_ERR_ARG, "max_seq_len %d outside [0, %d]", l->max_seq_len, hstu::kMaxSeqLen);
+    if (l->num_rows < 0) return fail(HSTU_ERR_ARG, "num_rows < 0");
+    if (l->num_pos_buckets < 1 || l->num_pos_buckets > hstu::kMaxPosBuckets)
+        return fail(HSTU_ERR_ARG, "num_pos_buckets outside [1, %d]", hstu::kMaxPosBuckets);
+    if (l->num_time_buckets < 1) return fail(HSTU_ERR_ARG, "num_time_buckets < 1");
+    if (!std::isfinite(l->alpha)) return fail(HSTU_ERR_ARG, "alpha is not finite");
+    if (!(l->ln_eps > 0.0f) || !std::isfinite(l->ln_eps)) return fail(HSTU_ERR_ARG, "ln_eps must be > 0");
+    if (l->B > 0) {
+        if (!l->seq_offsets || !l->x || !l->w1 || !l->w2 || !l->x_out || !l->timestamps || !l->rab_pos ||
+            !l->rab_time)
+            return fail(HSTU_ERR_ARG, "a required pointer is NULL");
+        if (!aligned16(l->x) || !aligned16(l->w1) || !aligned16(l->w2) || !aligned16(l->x_out))
+            return fail(HSTU_ERR_UNSUPPORTED, "layer buffers must be 16-byte aligned");
+    }
+    return HSTU_OK;
+}
+
+struct LayerWs {
+    size_t z, o, y, sched, total;
+};
+
+LayerWs layer_ws(const hstu_layer_args* l) {
+    LayerWs w;
+    const size_t T = size_t(l->num_rows);
+    const size_t hd = size_t(l->H) * l->d;
+    w.z = 0;
+    w.o = align256(w.z + T * 4 * hd * 2);
+    w.y = align256(w.o + T * hd * 2);
+    w.sched = align256(w.y + T * hd * 2);
+    w.total = hstu::sched_layout(l->B, l->max_seq_len, hstu::kBf16TileM, w.sched).bytes;
+    return w;
+}
+
+}  // namespace
+
+size_t hstu_layer_workspace_bytes(const hstu_layer_args* l) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_layer(l);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return layer_ws(l).total;
+}
+
+hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_layer(l);
+    if (st != HSTU_OK) return st;
+    if (l->B == 0 || l->num_rows == 0) return ok();
+    const LayerWs lw = layer_ws(l);
+    st = check_workspace(ws, ws_bytes, lw.total);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const int hd = l->H * l->d;
+    uint16_t* z = reinterpret_cast<uint16_t*>(w + lw.z);
+    uint16_t* o = reinterpret_cast<uint16_t*>(w + lw.o);
+    uint16_t* y = reinterpret_cast<uint16_t*>(w + lw.y);
+
+    // f1 + SiLU: Z = SiLU(X W1^T + b1) -> U | V | Q | K
+    hstu::GemmArgs g1;
+    g1.M = l->num_rows; g1.N = 4 * hd; g1.K = l->D;
+    g1.a = l->x; g1.lda = l->D;
+    g1.b = l->w1; g1.ldb = l->D;
+    g1.bias = l->b1;
+    g1.residual = nullptr; g1.ldr = 0;
+    g1.c = z; g1.ldc = 4 * hd;
+    g1.silu = 1;
+    hipError_t e = hstu::launch_gemm_bf16(g1, stream);
+    if (e != hipSuccess) return device_error(e, "f1 launch");
+
+    hstu_attn_args a;
+    memset(&a, 0, sizeof(a));
+    a.struct_size = sizeof(a);
+    a.B = l->B; a.H = l->H; a.d_qk = l->d; a.d_v = l->d;
+    a.max_seq_len = l->max_seq_len;
+    a.num_rows = l->num_rows;
+    a.seq_offsets = l->seq_offsets;
+    a.num_candidates = l->num_candidates;
+    a.dtype = HSTU_BF16;
+    a.act = HSTU_ACT_SILU;
+    a.u = z;              a.u_stride = 4 * hd;
+    a.v = z + 1 * hd;     a.v_stride = 4 * hd;
+    a.q = z + 2 * hd;     a.q_stride = 4 * hd;
+    a.k = z + 3 * hd;     a.k_stride = 4 * hd;
+    a.timestamps = l->timestamps;
+    a.rab_pos = l->rab_pos; a.num_pos_buckets = l->num_pos_buckets;
+    a.rab_time = l->rab_time; a.num_time_buckets = l->num_time_buckets;
+    a.alpha = l->alpha;
+    a.o = o; a.o_stride = hd;
+    a.y = y; a.y_stride = hd;
+    a.ln_eps = l->ln_eps;
+    Sched s = carve_sched(&a, ws, lw.sched);
+    e = run_sched(&a, s, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    e = run_core(&a, s, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+    e = run_ln_gate(&a, nullptr, nullptr, 0, stream);
+    if (e != hipSuccess) return device_error(e, "epilogue launch");
+
+    // f2 + residual: X_out = X + Y W2^T + b2
+    hstu::GemmArgs g2;
+    g2.M = l->num_rows; g2.N = l->D; g2.K = hd;
+    g2.a = y; g2.lda = hd;
+    g2.b = l->w2; g2.ldb = hd;
+    g2.bias = l->b2;
+    g2.residual = l->x; g2.ldr = l->D;
+    g2.c = l->x_out; g2.ldc = l->D;
+    g2.silu = 0;
+    e = hstu::launch_gemm_bf16(g2, stream);
+    if (e != hipSuccess) return device_error(e, "f2 launch");
+    return ok();
+}
+
+hstu_status hstu_attn_schedule(const hstu_attn_args* a, void* ws, size_t ws_bytes, int32_t* items_out,
+                               int64_t cap, int64_t* count_out, int32_t* tile_m_out, int32_t* tile_n_out,
+                               void* stream_) {
+    hstu_status st = validate_attn(a, false);
+    if (st != HSTU_OK) return st;
+    if (!count_out) return fail(HSTU_ERR_ARG, "count_out is NULL");
+    if (tile_m_out) *tile_m_out = tile_m_for(a->dtype);
+    if (tile_n_out) *tile_n_out = tile_n_for(a->dtype);
+    *count_out = 0;
+    if (a->B == 0) return ok();
+    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    st = check_workspace(ws, ws_bytes, need);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Sched s = carve_sched(a, ws, 0);
+    hipError_t e = run_sched(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    int32_t count = 0;
+    e = hipMemcpyAsync(&count, s.ctrl, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return device_error(e, "reading the item count");
+    *count_out = count;
+    const int64_t n = count < cap ? count : cap;
+    if (n > 0 && items_out) {
+        e = hipMemcpyAsync(items_out, s.items, size_t(n) * sizeof(hstu::WorkItem), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return device_error(e, "reading the work list");
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// epilogue.hip -- pointwise transformation gate Y = LayerNorm(O) (.) U, and the
+// M-FALCON candidate score <Y, w>.
+//
+// "生成式推荐（一）：HSTU", section "Pointwise aggregated attention": the
+// aggregated attention enters the layer as Norm(A(X)V(X)) (.) U(X), with
+// Norm = LayerNorm; "Meta HSTU: как действия пользователя стали основой
+// большой рекомендательной модели", section "Что меняется внутри HSTU по
+// сравнению с обычным Transformer": normalise, then gate elementwise by U.
+// LayerNorm runs over all H*d_v values of a row (biased variance, eps added
+// to the variance, no affine parameters).
+//
+// HBM-bound: one wave per row, 16-byte vector loads, the row held in
+// registers for a two-pass (mean, then centred variance) reduction with
+// wavefront shuffles; no LDS.
+#include "internal.h"
+#include "hstu_device.h"
+#include "../../include/hstu.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / 64;
+
+// Largest b in [0, B) with offsets[b] <= row (row must be < offsets[B]).
+__device__ __forceinline__ int seq_of_row(const int32_t* off, int B, int64_t row) {
+    int lo = 0, hi = B;  // off[lo] <= row < off[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (off[mid] <= row) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// Elements per lane per chunk: 8 (one 16-byte bf16 load or two fp32 loads).
+template <bool BF16>
+struct Vec8 {
+    static __device__ __forceinline__ void load(const void* base, int64_t idx, float* x) {
+        if constexpr (BF16) {
+            u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = __uint_as_float(r[e] << 16);
+                x[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+            }
+        } else {
+            const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+            f32x4 a = p[0], b = p[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+        }
+    }
+    static __device__ __forceinline__ void store(void* base, int64_t idx, const float* x) {
+        if constexpr (BF16) {
+            u32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx) = r;
+        } else {
+            f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx);
+            p[0] = f32x4{x[0], x[1], x[2], x[3]};
+            p[1] = f32x4{x[4], x[5], x[6], x[7]};
+        }
+    }
+};
+
+template <bool BF16, int NCH>
+__global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (a.B <= 0 || row >= a.num_rows) return;
+    if (row < a.offsets[0] || row >= a.offsets[a.B]) return;
+    const int b = seq_of_row(a.offsets, a.B, row);
+    const int r = (int)(row - a.offsets[b]);
+    const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
+    if (r >= L) return;  // padding row: never read or written
+    const int n = a.ncand ? L - a.ncand[b] : L;
+    const bool want_score = a.w != nullptr && r >= n;
+    if (a.y == nullptr && !want_score) return;
+
+    const int W = a.width;
+    float x[NCH][8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+            Vec8<BF16>::load(a.o, row * a.o_stride + col, x[c]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += x[c][e];
+        }
+    }
+    const float mean = wave_sum(sum) / (float)W;
+    float sq = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dlt = x[c][e] - mean;
+                sq = fmaf(dlt, dlt, sq);
+            }
+        }
+    }
+    const float var = wave_sum(sq) / (float)W;
+    const float rstd = 1.0f / sqrtf(var + a.eps);
+    float dot = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+            float u[8];
+            Vec8<BF16>::load(a.u, row * a.u_stride + col, u);
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * rstd * u[e];
+            if (a.y) Vec8<BF16>::store(a.y, row * a.y_stride + col, y);
+            if (want_score) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = fmaf(y[e], a.w[col + e], dot);
+            }
+        }
+    }
+    if (want_score) {
+        dot = wave_sum(dot);
+        if (lane == 0) a.scores[(int64_t)b * a.score_stride + (r - n)] = dot;
+    }
+}
+
+template <bool BF16>
+hipError_t launch_typed(const LnGateArgs& a, hipStream_t stream) {
+    const int nch = (a.width + 511) / 512;
+    const dim3 grid((unsigned)((a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    switch (nch) {
+        case 1: hipLaunchKernelGGL((ln_gate_kernel<BF16, 1>), grid, dim3(kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((ln_gate_kernel<BF16, 2>), grid, dim3(kThreads), 0, stream, a); break;
+        case 3:
+        case 4: hipLaunchKernelGGL((ln_gate_kernel<BF16, 4>), grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((ln_gate_kernel<BF16, 8>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ln_gate(const LnGateArgs& a, hipStream_t stream) {
+    if (a.num_rows <= 0) return hipSuccess;
+    return a.dtype == HSTU_BF16 ? launch_typed<true>(a, stream) : launch_typed<false>(a, stream);
+}
+
+}  // namespace hstu

@@ -1,0 +1,219 @@
+"""Python binding of libhstu.so: torch tensors in, torch tensors out.
+
+Argument marshalling only -- every step of the path runs in the HIP kernels
+behind include/hstu.h.  PyTorch provides device memory and the stream.
+Names follow the C ABI: hstu_attn_fwd, mfalcon_score, hstu_layer_fwd,
+hstu_attn_schedule.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.HSTU_F32, torch.bfloat16: _lib.HSTU_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _head_view_stride(t: torch.Tensor, H: int, d: int) -> int:
+    """Row stride of a [rows, H, d] (or [rows, H*d]) view with dense heads."""
+    if t.dim() == 3:
+        if t.shape[1:] != (H, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"expected [rows, {H}, {d}] with dense heads, got {tuple(t.shape)} "
+                             f"strides {t.stride()}")
+        return t.stride(0)
+    if t.dim() == 2:
+        if t.shape[1] != H * d or t.stride(1) != 1:
+            raise ValueError(f"expected [rows, {H * d}] with unit column stride")
+        return t.stride(0)
+    raise ValueError("expected a 2-D or 3-D tensor")
+
+
+def _empty_ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
+                   max_seq_len: int, o: torch.Tensor, seq_lengths=None, num_candidates=None,
+                   u=None, y=None, ln_eps: float = 1e-5, act: int = _lib.HSTU_ACT_SILU,
+                   ev_core_begin=None, ev_core_end=None) -> _lib.AttnArgs:
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    H, d_qk = (q.shape[1], q.shape[2]) if q.dim() == 3 else (None, None)
+    if H is None:
+        raise ValueError("q must be [rows, H, d_qk]")
+    d_v = v.shape[2] if v.dim() == 3 else v.shape[1] // H
+    rp_hs = rab_pos.shape[-1] if rab_pos.dim() == 2 else 0
+    rt_hs = rab_time.shape[-1] if rab_time.dim() == 2 else 0
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.B = seq_offsets.numel() - 1
+    a.H = H
+    a.d_qk = d_qk
+    a.d_v = d_v
+    a.max_seq_len = int(max_seq_len)
+    a.num_rows = q.shape[0]
+    a.seq_offsets = _ptr(seq_offsets)
+    a.seq_lengths = _ptr(seq_lengths)
+    a.num_candidates = _ptr(num_candidates)
+    a.dtype = _DTYPES[q.dtype]
+    a.act = act
+    a.q, a.q_stride = q.data_ptr(), _head_view_stride(q, H, d_qk)
+    a.k, a.k_stride = k.data_ptr(), _head_view_stride(k, H, d_qk)
+    a.v, a.v_stride = v.data_ptr(), _head_view_stride(v, H, d_v)
+    a.timestamps = timestamps.data_ptr()
+    a.rab_pos = rab_pos.data_ptr()
+    a.num_pos_buckets = rab_pos.shape[-1]
+    a.rab_pos_head_stride = rp_hs
+    a.rab_time = rab_time.data_ptr()
+    a.num_time_buckets = rab_time.shape[-1]
+    a.rab_time_head_stride = rt_hs
+    a.alpha = float(alpha)
+    a.o, a.o_stride = o.data_ptr(), _head_view_stride(o, H, d_v)
+    if u is not None:
+        a.u, a.u_stride = u.data_ptr(), _head_view_stride(u, H, d_v)
+    if y is not None:
+        a.y, a.y_stride = y.data_ptr(), _head_view_stride(y, H, d_v)
+    a.ln_eps = float(ln_eps)
+    a.ev_core_begin = ev_core_begin
+    a.ev_core_end = ev_core_end
+    return a
+
+
+def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
+                  max_seq_len: int, seq_lengths=None, num_candidates=None, u=None,
+                  ln_eps: float = 1e-5, act: int = _lib.HSTU_ACT_SILU, o=None, y=None,
+                  workspace=None, stream=None, ev_core_begin=None, ev_core_end=None):
+    """O (and Y = LayerNorm(O) * U when ``u`` is given) of the jagged batch.
+
+    q, k: [rows, H, d_qk]; v, u: [rows, H, d_v]; seq_offsets int32 [B+1];
+    timestamps int64 [rows]; rab_pos float32 [P] or [H, P]; rab_time float32
+    [NT] or [H, NT].  Returns (o, y) with y None when u is None.
+    """
+    lib = _lib.load()
+    if o is None:
+        o = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
+    if u is not None and y is None:
+        y = torch.empty_like(o)
+    args = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                          max_seq_len=max_seq_len, o=o, seq_lengths=seq_lengths,
+                          num_candidates=num_candidates, u=u, y=y if u is not None else None,
+                          ln_eps=ln_eps, act=act, ev_core_begin=ev_core_begin,
+                          ev_core_end=ev_core_end)
+    need = lib.hstu_attn_workspace_bytes(ctypes.byref(args))
+    if workspace is None:
+        workspace = _empty_ws(need, q.device)
+    _lib.check(lib.hstu_attn_fwd(ctypes.byref(args), workspace.data_ptr(), workspace.numel(),
+                                 _stream_ptr(stream)))
+    return o, (y if u is not None else None)
+
+
+def attn_workspace_bytes(args: _lib.AttnArgs) -> int:
+    return int(_lib.load().hstu_attn_workspace_bytes(ctypes.byref(args)))
+
+
+def mfalcon_score(q, k, v, u, seq_offsets, num_candidates, timestamps, rab_pos, rab_time, alpha,
+                  w, *, max_seq_len: int, score_stride: int, ln_eps: float = 1e-5, o=None,
+                  y=None, scores=None, workspace=None, stream=None, ev_core_begin=None,
+                  ev_core_end=None):
+    """M-FALCON ranking scores [B, score_stride] (fp32) of every candidate."""
+    lib = _lib.load()
+    B = seq_offsets.numel() - 1
+    if o is None:
+        o = torch.empty(q.shape[0], q.shape[1], v.shape[2], dtype=q.dtype, device=q.device)
+    if scores is None:
+        scores = torch.zeros(B, score_stride, dtype=torch.float32, device=q.device)
+    m = _lib.MfalconArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconArgs)
+    m.attn = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                            max_seq_len=max_seq_len, o=o, num_candidates=num_candidates, u=u,
+                            y=y, ln_eps=ln_eps, ev_core_begin=ev_core_begin,
+                            ev_core_end=ev_core_end)
+    m.w = w.data_ptr()
+    m.scores = scores.data_ptr()
+    m.score_stride = int(score_stride)
+    need = lib.hstu_mfalcon_workspace_bytes(ctypes.byref(m))
+    if workspace is None:
+        workspace = _empty_ws(need, q.device)
+    _lib.check(lib.mfalcon_score(ctypes.byref(m), workspace.data_ptr(), workspace.numel(),
+                                 _stream_ptr(stream)))
+    return scores, o, y
+
+
+def make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,
+                    d: int, max_seq_len: int, x_out, b1=None, b2=None, num_candidates=None,
+                    ln_eps: float = 1e-5) -> _lib.LayerArgs:
+    l = _lib.LayerArgs()
+    l.struct_size = ctypes.sizeof(_lib.LayerArgs)
+    l.B = seq_offsets.numel() - 1
+    l.H, l.d, l.D = H, d, x.shape[1]
+    l.max_seq_len = int(max_seq_len)
+    l.num_rows = x.shape[0]
+    l.seq_offsets = seq_offsets.data_ptr()
+    l.num_candidates = _ptr(num_candidates)
+    for name, t in (("x", x), ("w1", w1), ("w2", w2), ("x_out", x_out)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    l.x, l.w1, l.w2, l.x_out = x.data_ptr(), w1.data_ptr(), w2.data_ptr(), x_out.data_ptr()
+    l.b1, l.b2 = _ptr(b1), _ptr(b2)
+    l.timestamps = timestamps.data_ptr()
+    l.rab_pos, l.num_pos_buckets = rab_pos.data_ptr(), rab_pos.shape[-1]
+    l.rab_time, l.num_time_buckets = rab_time.data_ptr(), rab_time.shape[-1]
+    l.alpha = float(alpha)
+    l.ln_eps = float(ln_eps)
+    return l
+
+
+def hstu_layer_fwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,
+                   d: int, max_seq_len: int, b1=None, b2=None, num_candidates=None,
+                   ln_eps: float = 1e-5, x_out=None, workspace=None, stream=None):
+    """One HSTU layer (f1 + SiLU, attention, LN * U, f2 + residual); returns X_out."""
+    lib = _lib.load()
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    l = make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, H=H, d=d,
+                        max_seq_len=max_seq_len, x_out=x_out, b1=b1, b2=b2,
+                        num_candidates=num_candidates, ln_eps=ln_eps)
+    need = lib.hstu_layer_workspace_bytes(ctypes.byref(l))
+    if workspace is None:
+        workspace = _empty_ws(need, x.device)
+    _lib.check(lib.hstu_layer_fwd(ctypes.byref(l), workspace.data_ptr(), workspace.numel(),
+                                  _stream_ptr(stream)))
+    return x_out
+
+
+def layer_workspace_bytes(l: _lib.LayerArgs) -> int:
+    return int(_lib.load().hstu_layer_workspace_bytes(ctypes.byref(l)))
+
+
+def hstu_attn_schedule(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, *, max_seq_len: int,
+                       seq_lengths=None, num_candidates=None, stream=None):
+    """The device-built work list as a host int32 array [count, 4] plus (tile_m, tile_n)."""
+    import numpy as np
+    lib = _lib.load()
+    args = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, 1.0,
+                          max_seq_len=max_seq_len, o=torch.empty_like(v),
+                          seq_lengths=seq_lengths, num_candidates=num_candidates)
+    need = lib.hstu_attn_workspace_bytes(ctypes.byref(args))
+    ws = _empty_ws(need, q.device)
+    B = seq_offsets.numel() - 1
+    cap = max(1, B * ((max_seq_len + 63) // 64))
+    items = np.zeros((cap, 4), dtype=np.int32)
+    count = ctypes.c_int64(0)
+    tm, tn = ctypes.c_int32(0), ctypes.c_int32(0)
+    _lib.check(lib.hstu_attn_schedule(ctypes.byref(args), ws.data_ptr(), ws.numel(),
+                                      items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap,
+                                      ctypes.byref(count), ctypes.byref(tm), ctypes.byref(tn),
+                                      _stream_ptr(stream)))
+    return items[:count.value], tm.value, tn.value

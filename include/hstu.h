@@ -1,0 +1,216 @@
+/*
+ * hstu.h -- C ABI of the MI355X (gfx950) HSTU pointwise aggregated attention
+ * library (libhstu.so).
+ *
+ * What the library computes (per head h, for a jagged batch of user-action
+ * sequences):
+ *
+ *   S_ij = <Q_i, K_j> + rab_pos[pb(i, j)] + rab_time[tb(i, j)]
+ *   O_i  = alpha * sum_{j visible from i} SiLU(S_ij) * V_j          (no softmax)
+ *   Y_i  = LayerNorm(concat_h O_i) (.) U_i                         (optional)
+ *
+ * following the layer described on the pages
+ *   "生成式推荐（一）：HSTU" (sections "高性能自注意力Encoder：HSTU" and
+ *   "Pointwise aggregated attention": SiLU activations, LayerNorm, the
+ *   Norm(A(X)V(X)) (.) U(X) gate, rab^{p,t} from position and time),
+ *   "Meta HSTU: как действия пользователя стали основой большой
+ *   рекомендательной модели" (section "Что меняется внутри HSTU по сравнению
+ *   с обычным Transformer": Q, K, V, U built together, position and time
+ *   biases, normalise-then-gate, residual) and
+ *   "行动胜于言语：万亿参数序列转导器用于生成式推荐" (section "7. 模型细节":
+ *   normalised attention without softmax; section "2.3 M-FALCON算法").
+ *
+ * Definitions used throughout (row r of sequence b is buffer row
+ * seq_offsets[b] + r; L_b rows; n_b = L_b - num_candidates[b] history rows):
+ *   visible(i, j): i < n_b: j <= i (causal, the diagonal included);
+ *                  i >= n_b (a ranking candidate): j < n_b or j == i.
+ *   position p(i) = min(i, n_b)       (every candidate sits just after the
+ *                                      history, as a single appended target)
+ *   pb(i, j) = min(p(i) - p(j), num_pos_buckets - 1)
+ *   tb(i, j) = min(num_time_buckets - 1, bit_length(|t_i - t_j|)),
+ *              t in int64 seconds, bit_length(0) = 0.
+ *
+ * Conventions
+ *   - All data pointers are DEVICE pointers unless stated otherwise.  The
+ *     caller owns every buffer; the library never allocates or frees device
+ *     memory.  Scratch memory is a caller-provided workspace whose size is
+ *     returned by the matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every entry point
+ *     checks its arguments synchronously, then enqueues its kernels on
+ *     `stream` and returns without synchronising.  Device-side faults surface
+ *     at the caller's next synchronisation.
+ *   - Strides are in ELEMENTS between consecutive rows.  Head h of row r of Q
+ *     starts at q + r * q_stride + h * d_qk (same for K; V, O with d_v).
+ *   - On any error no kernel has been launched; hstu_last_error() returns a
+ *     thread-local message for the last failing call on that thread.
+ *   - Device data (offsets, lengths, candidate counts) is trusted: it must
+ *     satisfy 0 <= seq_offsets[b] <= seq_offsets[b+1] <= num_rows,
+ *     0 <= L_b <= max_seq_len, 0 <= num_candidates[b] <= L_b; violating it is
+ *     undefined behaviour (not checked on the device).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+/* ------------------------------------------------------------------ status */
+typedef int32_t hstu_status;
+#define HSTU_OK 0
+#define HSTU_ERR_ARG (-1)          /* invalid argument (NULL, bad size, ...) */
+#define HSTU_ERR_UNSUPPORTED (-2)  /* valid, but no kernel for this shape/dtype */
+#define HSTU_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than required */
+#define HSTU_ERR_DEVICE (-4)       /* a HIP call or kernel launch failed */
+
+/* ------------------------------------------------------------------- enums */
+#define HSTU_F32 0   /* float32 Q/K/V/U/O/Y, fp32 arithmetic */
+#define HSTU_BF16 1  /* bfloat16 Q/K/V/U/O/Y, bf16 MFMA with fp32 accumulation */
+
+#define HSTU_ACT_SILU 0      /* the method's activation */
+#define HSTU_ACT_IDENTITY 1  /* test mode: A = S (no activation) */
+
+/* Shapes compiled into this build:
+ *   HSTU_BF16: d_qk = d_v = 128, any H >= 1.
+ *   HSTU_F32:  d_qk = d_v in {32, 64}, any H >= 1.
+ *   max_seq_len <= 65536; num_pos_buckets in [1, 8192]; num_time_buckets >= 1.
+ *   bf16 buffers need 16-byte aligned row starts (pointer and stride*2). */
+
+/* ------------------------------------------------------- attention (core) */
+typedef struct hstu_attn_args {
+    uint32_t struct_size;          /* = sizeof(hstu_attn_args) */
+    int32_t B;                     /* sequences, >= 0 */
+    int32_t H;                     /* heads, >= 1 */
+    int32_t d_qk, d_v;             /* head dims */
+    int32_t max_seq_len;           /* upper bound on every L_b */
+    int64_t num_rows;              /* rows in the jagged buffers (>= seq_offsets[B]) */
+    const int32_t* seq_offsets;    /* [B+1] first row of each sequence */
+    const int32_t* seq_lengths;    /* [B] L_b, or NULL: L_b = offsets[b+1]-offsets[b].
+                                      Rows offsets[b]+L_b .. offsets[b+1]-1 are padding:
+                                      never read, never written. */
+    const int32_t* num_candidates; /* [B] candidates at the end of each sequence
+                                      (M-FALCON), or NULL: all rows are history */
+    int32_t dtype;                 /* HSTU_F32 | HSTU_BF16 (Q, K, V, U, O, Y) */
+    int32_t act;                   /* HSTU_ACT_SILU | HSTU_ACT_IDENTITY */
+    const void* q; int64_t q_stride;
+    const void* k; int64_t k_stride;
+    const void* v; int64_t v_stride;
+    const int64_t* timestamps;     /* [num_rows] seconds */
+    const float* rab_pos;          /* [num_pos_buckets] (+ h*rab_pos_head_stride) */
+    int32_t num_pos_buckets;
+    int32_t rab_pos_head_stride;   /* 0: one table shared by all heads */
+    const float* rab_time;         /* [num_time_buckets] (+ h*rab_time_head_stride) */
+    int32_t num_time_buckets;
+    int32_t rab_time_head_stride;
+    float alpha;                   /* output scale (1/n), finite */
+    void* o; int64_t o_stride;     /* out: [rows, H*d_v] attention output O */
+    /* optional epilogue Y = LayerNorm(O_row) (.) U_row over all H*d_v values */
+    const void* u; int64_t u_stride;   /* [rows, H*d_v]; required when y != NULL */
+    void* y; int64_t y_stride;         /* out, or NULL to skip the epilogue */
+    float ln_eps;                      /* > 0, added to the variance */
+    /* optional hipEvent_t recorded on `stream` just before / after the
+       attention-core kernel (for timing that kernel alone); NULL = none */
+    void* ev_core_begin;
+    void* ev_core_end;
+} hstu_attn_args;
+
+/* Version of this ABI (HSTU_ABI_VERSION). */
+int hstu_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* hstu_status_string(hstu_status s);
+
+/* Thread-local detail of the last error on this thread ("" if none). */
+const char* hstu_last_error(void);
+
+/* Workspace bytes needed by hstu_attn_fwd for these arguments (0 on invalid
+ * arguments; call hstu_attn_fwd to get the reason).  Depends only on B,
+ * max_seq_len and dtype. */
+size_t hstu_attn_workspace_bytes(const hstu_attn_args* args);
+
+/* Pointwise aggregated attention over a jagged batch.  Builds the jagged
+ * tile work list (skipping fully masked tiles) on the device, runs the
+ * attention core into `o`, then (if y != NULL) the LayerNorm(O) (.) U
+ * epilogue into `y`.  `o` must not alias any input.
+ * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE,
+ * HSTU_ERR_DEVICE. */
+hstu_status hstu_attn_fwd(const hstu_attn_args* args, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* --------------------------------------------------- M-FALCON ranking pass */
+/* One forward pass scoring b_m candidates per user against the shared
+ * history: "行动胜于言语：万亿参数序列转导器用于生成式推荐", section
+ * "2.3 M-FALCON算法"; "生成式推荐（一）：HSTU", section "M-FALCON"; "Meta HSTU",
+ * section "M-FALCON переиспользует историю между кандидатами".
+ *   scores[b * score_stride + c] = < Y[n_b + c, :], w >,
+ * Y = LayerNorm(O) (.) U as in hstu_attn_fwd, for c < num_candidates[b]. */
+typedef struct hstu_mfalcon_args {
+    uint32_t struct_size;     /* = sizeof(hstu_mfalcon_args) */
+    hstu_attn_args attn;      /* num_candidates and u are required; attn.y may be
+                                 NULL (Y not stored) or a buffer for Y */
+    const float* w;           /* [H*d_v] score vector */
+    float* scores;            /* out: [B * score_stride] fp32 */
+    int32_t score_stride;     /* >= max candidates per sequence */
+} hstu_mfalcon_args;
+
+size_t hstu_mfalcon_workspace_bytes(const hstu_mfalcon_args* args);
+
+hstu_status mfalcon_score(const hstu_mfalcon_args* args, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ HSTU layer */
+/* One HSTU layer over a packed jagged batch (bf16, d = 128):
+ *   Z = SiLU(X W1^T + b1)  split by columns into U | V | Q | K (H*d each,
+ *                          head h at sub-columns h*d .. h*d+d-1)
+ *   O = attention(Q, K, V) as hstu_attn_fwd (causal, or M-FALCON)
+ *   Y = LayerNorm(O) (.) U
+ *   X_out = X + Y W2^T + b2
+ * ("生成式推荐（一）：HSTU", section "高性能自注意力Encoder：HSTU": pointwise
+ * projection f1 with SiLU, spatial aggregation, pointwise transformation
+ * with f2; residual between identical layers.) */
+typedef struct hstu_layer_args {
+    uint32_t struct_size;          /* = sizeof(hstu_layer_args) */
+    int32_t B, H, d, D;            /* d must be 128; D (model width) % 64 == 0 */
+    int32_t max_seq_len;
+    int64_t num_rows;              /* = seq_offsets[B] (packed layout) */
+    const int32_t* seq_offsets;    /* [B+1] */
+    const int32_t* num_candidates; /* [B] or NULL */
+    const void* x;                 /* [num_rows, D] bf16 */
+    const void* w1;                /* [4*H*d, D] bf16 (out x in) */
+    const float* b1;               /* [4*H*d] or NULL */
+    const void* w2;                /* [D, H*d] bf16 (out x in) */
+    const float* b2;               /* [D] or NULL */
+    const int64_t* timestamps;     /* [num_rows] */
+    const float* rab_pos; int32_t num_pos_buckets;
+    const float* rab_time; int32_t num_time_buckets;
+    float alpha;
+    float ln_eps;
+    void* x_out;                   /* [num_rows, D] bf16; may alias x */
+} hstu_layer_args;
+
+size_t hstu_layer_workspace_bytes(const hstu_layer_args* args);
+
+hstu_status hstu_layer_fwd(const hstu_layer_args* args, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------ scheduler access */
+/* Builds only the jagged tile work list into `workspace` (same layout as the
+ * one hstu_attn_fwd builds) and copies it to the HOST array `items_out`
+ * (capacity `cap` rows of 4 int32: b, query tile, end of the first key-tile
+ * range [0, a_end), second range packed as begin | end << 16).  `count_out`
+ * (host) receives the number of items.  Synchronises `stream`.  For tests of
+ * the scheduler against a brute-force tile enumeration. */
+hstu_status hstu_attn_schedule(const hstu_attn_args* args, void* workspace, size_t workspace_bytes,
+                               int32_t* items_out, int64_t cap, int64_t* count_out,
+                               int32_t* tile_m_out, int32_t* tile_n_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

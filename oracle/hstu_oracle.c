@@ -29,7 +29,8 @@
  * Readings taken where the pages are silent are listed in the design notes
  * and repeated at each function below.
  *
- * Parallelism: OpenMP over independent (sequence, head) units only.
+ * Parallelism: OpenMP over independent (head, query row) pairs of a sequence,
+ * and over rows in the row-wise functions.
  */
 #include <math.h>
 #include <stdint.h>
@@ -143,36 +144,39 @@ void hstu_oracle_attn(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                       double alpha, int32_t act,
                       double* o, int64_t o_stride, int32_t num_threads) {
     set_threads(num_threads);
-    int64_t units = (int64_t)B * H;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t unit = 0; unit < units; ++unit) {
-        int32_t b = (int32_t)(unit / H);
-        int32_t h = (int32_t)(unit % H);
+    for (int32_t b = 0; b < B; ++b) {
         int32_t L = seq_len(offsets, lengths, b);
         int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
         int64_t base = offsets[b];
-        const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
-        const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
-        double* acc = (double*)malloc(sizeof(double) * (size_t)(d_v > 0 ? d_v : 1));
-        for (int32_t i = 0; i < L; ++i) {
-            const double* qi = q + (base + i) * q_stride + (int64_t)h * d_qk;
-            for (int32_t c = 0; c < d_v; ++c) acc[c] = 0.0;
-            for (int32_t j = 0; j < L; ++j) {
-                if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
-                const double* kj = k + (base + j) * k_stride + (int64_t)h * d_qk;
-                double s = 0.0;
-                for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
-                s += rp[hstu_oracle_pos_bucket(i, j, n_hist, num_pos_buckets)];
-                s += rt[hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j],
-                                                num_time_buckets)];
-                double a = (act == ORACLE_ACT_IDENTITY) ? s : hstu_oracle_silu(s);
-                const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
-                for (int32_t c = 0; c < d_v; ++c) acc[c] += a * vj[c];
+        /* every (head, query row) of the sequence is independent */
+#pragma omp parallel
+        {
+            double* acc = (double*)malloc(sizeof(double) * (size_t)(d_v > 0 ? d_v : 1));
+#pragma omp for collapse(2) schedule(dynamic, 4)
+            for (int32_t h = 0; h < H; ++h) {
+                for (int32_t i = 0; i < L; ++i) {
+                    const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
+                    const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
+                    const double* qi = q + (base + i) * q_stride + (int64_t)h * d_qk;
+                    for (int32_t c = 0; c < d_v; ++c) acc[c] = 0.0;
+                    for (int32_t j = 0; j < L; ++j) {
+                        if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
+                        const double* kj = k + (base + j) * k_stride + (int64_t)h * d_qk;
+                        double s = 0.0;
+                        for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
+                        s += rp[hstu_oracle_pos_bucket(i, j, n_hist, num_pos_buckets)];
+                        s += rt[hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j],
+                                                        num_time_buckets)];
+                        double a = (act == ORACLE_ACT_IDENTITY) ? s : hstu_oracle_silu(s);
+                        const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
+                        for (int32_t c = 0; c < d_v; ++c) acc[c] += a * vj[c];
+                    }
+                    double* oi = o + (base + i) * o_stride + (int64_t)h * d_v;
+                    for (int32_t c = 0; c < d_v; ++c) oi[c] = alpha * acc[c];
+                }
             }
-            double* oi = o + (base + i) * o_stride + (int64_t)h * d_v;
-            for (int32_t c = 0; c < d_v; ++c) oi[c] = alpha * acc[c];
+            free(acc);
         }
-        free(acc);
     }
 }
 

@@ -1,0 +1,175 @@
+"""CPU-only checks of the C ABI boundary: the library loads, exports every
+symbol include/hstu.h declares, the ctypes structs match the C layout, and
+every host-side validation error is returned before any launch (no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from hstu_sequential_transducer_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from hstu_sequential_transducer_causal_amd import build
+        build.build()
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("sizeof",)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in declared:
+        assert name in exported, name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.hstu_abi_version() == 1
+    for s in [0, -1, -2, -3, -4, 99]:
+        assert lib.hstu_status_string(s)
+
+
+_STRUCTS = {
+    "hstu_attn_args": _lib.AttnArgs,
+    "hstu_mfalcon_args": _lib.MfalconArgs,
+    "hstu_layer_args": _lib.LayerArgs,
+}
+
+
+def test_ctypes_layout_matches_c(tmp_path):
+    src = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
+    for cname, cls in _STRUCTS.items():
+        src.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            src.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(c)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    for line in out.splitlines():
+        cname, fname, val = line.split()
+        cls = _STRUCTS[cname]
+        want = ctypes.sizeof(cls) if fname == "size" else getattr(cls, fname).offset
+        assert int(val) == want, line
+
+
+def _valid_args():
+    """A fully valid bf16 argument set with fake (never dereferenced) device pointers."""
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.B, a.H, a.d_qk, a.d_v, a.max_seq_len, a.num_rows = 2, 4, 128, 128, 100, 200
+    fake = 0x10000
+    a.seq_offsets = fake
+    a.dtype, a.act = _lib.HSTU_BF16, _lib.HSTU_ACT_SILU
+    a.q = a.k = a.v = a.o = fake
+    a.q_stride = a.k_stride = a.v_stride = a.o_stride = 512
+    a.timestamps = a.rab_pos = a.rab_time = fake
+    a.num_pos_buckets, a.num_time_buckets = 1024, 32
+    a.alpha = 1.0 / 1024
+    a.ln_eps = 1e-5
+    return a
+
+
+def _call(lib, a, ws=None, nbytes=0):
+    return lib.hstu_attn_fwd(ctypes.byref(a), ws, nbytes, None)
+
+
+MUTATIONS = [
+    ("struct_size", lambda a: setattr(a, "struct_size", 8), _lib.HSTU_ERR_ARG),
+    ("B<0", lambda a: setattr(a, "B", -1), _lib.HSTU_ERR_ARG),
+    ("H<1", lambda a: setattr(a, "H", 0), _lib.HSTU_ERR_ARG),
+    ("dtype", lambda a: setattr(a, "dtype", 7), _lib.HSTU_ERR_ARG),
+    ("act", lambda a: setattr(a, "act", 5), _lib.HSTU_ERR_ARG),
+    ("bf16 d=64", lambda a: (setattr(a, "d_qk", 64), setattr(a, "d_v", 64)), _lib.HSTU_ERR_UNSUPPORTED),
+    ("f32 d=128", lambda a: setattr(a, "dtype", _lib.HSTU_F32), _lib.HSTU_ERR_UNSUPPORTED),
+    ("P=0", lambda a: setattr(a, "num_pos_buckets", 0), _lib.HSTU_ERR_ARG),
+    ("P too big", lambda a: setattr(a, "num_pos_buckets", 100000), _lib.HSTU_ERR_ARG),
+    ("NT=0", lambda a: setattr(a, "num_time_buckets", 0), _lib.HSTU_ERR_ARG),
+    ("alpha nan", lambda a: setattr(a, "alpha", float("nan")), _lib.HSTU_ERR_ARG),
+    ("alpha inf", lambda a: setattr(a, "alpha", float("inf")), _lib.HSTU_ERR_ARG),
+    ("max_seq_len", lambda a: setattr(a, "max_seq_len", 1 << 20), _lib.HSTU_ERR_ARG),
+    ("offsets NULL", lambda a: setattr(a, "seq_offsets", None), _lib.HSTU_ERR_ARG),
+    ("q NULL", lambda a: setattr(a, "q", None), _lib.HSTU_ERR_ARG),
+    ("ts NULL", lambda a: setattr(a, "timestamps", None), _lib.HSTU_ERR_ARG),
+    ("tables NULL", lambda a: setattr(a, "rab_time", None), _lib.HSTU_ERR_ARG),
+    ("q stride small", lambda a: setattr(a, "q_stride", 100), _lib.HSTU_ERR_ARG),
+    ("misaligned q", lambda a: setattr(a, "q", 0x10002), _lib.HSTU_ERR_UNSUPPORTED),
+    ("y without u", lambda a: setattr(a, "y", 0x10000), _lib.HSTU_ERR_ARG),
+    ("eps<=0", lambda a: (setattr(a, "y", 0x10000), setattr(a, "u", 0x10000),
+                          setattr(a, "u_stride", 512), setattr(a, "y_stride", 512),
+                          setattr(a, "ln_eps", 0.0)), _lib.HSTU_ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("name,mut,status", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_validation_errors_before_any_launch(lib, name, mut, status):
+    a = _valid_args()
+    mut(a)
+    assert _call(lib, a) == status
+    assert lib.hstu_last_error()
+    assert lib.hstu_attn_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_null_args_and_workspace_errors(lib):
+    assert lib.hstu_attn_fwd(None, None, 0, None) == _lib.HSTU_ERR_ARG
+    a = _valid_args()
+    need = lib.hstu_attn_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    assert _call(lib, a, None, 0) == _lib.HSTU_ERR_WORKSPACE
+    assert _call(lib, a, 0x20000, need - 1) == _lib.HSTU_ERR_WORKSPACE
+    assert _call(lib, a, 0x20001, need) == _lib.HSTU_ERR_WORKSPACE   # misaligned
+    assert b"workspace" in lib.hstu_last_error()
+
+
+def test_empty_batch_is_a_no_op(lib):
+    a = _valid_args()
+    a.B = 0
+    assert _call(lib, a) == _lib.HSTU_OK
+
+
+def test_mfalcon_and_layer_validation(lib):
+    m = _lib.MfalconArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconArgs)
+    m.attn = _valid_args()
+    m.score_stride = 4
+    # u required for the scores' LayerNorm
+    assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    m.attn.u, m.attn.u_stride = 0x10000, 512
+    assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG  # no candidates
+    m.struct_size = 4
+    assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+
+    l = _lib.LayerArgs()
+    l.struct_size = ctypes.sizeof(_lib.LayerArgs)
+    l.B, l.H, l.d, l.D, l.max_seq_len, l.num_rows = 2, 4, 128, 512, 100, 200
+    fake = 0x10000
+    l.seq_offsets = l.x = l.w1 = l.w2 = l.x_out = l.timestamps = l.rab_pos = l.rab_time = fake
+    l.num_pos_buckets, l.num_time_buckets = 1024, 32
+    l.alpha, l.ln_eps = 1.0 / 4096, 1e-5
+    need = lib.hstu_layer_workspace_bytes(ctypes.byref(l))
+    assert need >= 200 * (4 * 512 + 2 * 512) * 2
+    assert lib.hstu_layer_fwd(ctypes.byref(l), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    l.d = 64
+    assert lib.hstu_layer_fwd(ctypes.byref(l), None, 0, None) == _lib.HSTU_ERR_UNSUPPORTED
+    l.d, l.D = 128, 100
+    assert lib.hstu_layer_fwd(ctypes.byref(l), None, 0, None) == _lib.HSTU_ERR_UNSUPPORTED
