@@ -1,0 +1,305 @@
+"""Benchmark of the HSTU attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of the long-sequence
+workload (16 jagged sequences, lognormal lengths clipped to [1024, 8192],
+stochastic length capped at 8192**0.85 = 2120, 8 heads, d = 128, bf16):
+the device-side jagged tile scheduler, the bf16 MFMA attention core and the
+LayerNorm(O) * U epilogue, all through hstu_attn_fwd.  Inputs are resident
+in HBM before the timed region.
+
+Prints ONE JSON line.  `value` is unmasked attention TFLOP/s of the whole
+step; `roofline` is the attention-core kernel alone, timed with HIP events
+recorded around its launch on the same stream; `cpu_baseline` is the fp64
+oracle on a bounded sample of the same workload (host cores of this machine).
+Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) are
+timed briefly and reported under "other_workloads".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=3, help="workload number 2..5 for the main line")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-others", action="store_true")
+    p.add_argument("--cpu-sample-seqs", type=int, default=0, help="0: all sequences")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
+    return p.parse_args()
+
+
+def up(a, dtype, dev):
+    import torch
+    import hstu_synth as synth
+    if dtype == "bf16":
+        return torch.from_numpy(synth.bf16_bits(a).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+
+class AttnCase:
+    def __init__(self, x, dev, with_scores=False):
+        import torch
+        from hstu_sequential_transducer_causal_amd import ops
+        self.x = x
+        self.q, self.k, self.v, self.u = (up(a, x.dtype, dev) for a in (x.q, x.k, x.v, x.u))
+        self.off = torch.from_numpy(x.offsets).to(dev)
+        self.ts = torch.from_numpy(x.ts).to(dev)
+        self.rp = torch.from_numpy(x.rab_pos).to(dev)
+        self.rt = torch.from_numpy(x.rab_time).to(dev)
+        self.nc = None if x.num_candidates is None else torch.from_numpy(x.num_candidates).to(dev)
+        self.w = None if x.w is None else torch.from_numpy(x.w).to(dev)
+        self.max_len = int(np.diff(x.offsets).max())
+        self.o = torch.empty_like(self.q)
+        self.y = torch.empty_like(self.q)
+        self.with_scores = with_scores
+        if with_scores:
+            self.cmax = int(x.num_candidates.max())
+            self.scores = torch.zeros(x.B, self.cmax, dtype=torch.float32, device=dev)
+        args = ops.make_attn_args(self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt,
+                                  x.alpha, max_seq_len=self.max_len, o=self.o,
+                                  num_candidates=self.nc, u=self.u, y=self.y)
+        self.ws = torch.empty(max(1, ops.attn_workspace_bytes(args)), dtype=torch.uint8, device=dev)
+
+    def step(self, ev0=None, ev1=None):
+        from hstu_sequential_transducer_causal_amd import ops
+        if self.with_scores:
+            ops.mfalcon_score(self.q, self.k, self.v, self.u, self.off, self.nc, self.ts, self.rp,
+                              self.rt, self.x.alpha, self.w, max_seq_len=self.max_len,
+                              score_stride=self.cmax, ln_eps=self.x.eps, o=self.o, y=None,
+                              scores=self.scores, workspace=self.ws, ev_core_begin=ev0,
+                              ev_core_end=ev1)
+        else:
+            ops.hstu_attn_fwd(self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt,
+                              self.x.alpha, max_seq_len=self.max_len, num_candidates=self.nc,
+                              u=self.u, ln_eps=self.x.eps, o=self.o, y=self.y, workspace=self.ws,
+                              ev_core_begin=ev0, ev_core_end=ev1)
+
+
+class StackCase:
+    def __init__(self, x, dev):
+        import torch
+        from hstu_sequential_transducer_causal_amd import ops
+        self.x = x
+        self.xin = up(x.x, "bf16", dev)
+        self.bufs = [torch.empty_like(self.xin), torch.empty_like(self.xin)]
+        self.w1 = [up(w, "bf16", dev) for w in x.w1]
+        self.w2 = [up(w, "bf16", dev) for w in x.w2]
+        self.rp = [torch.from_numpy(r).to(dev) for r in x.rab_pos]
+        self.rt = [torch.from_numpy(r).to(dev) for r in x.rab_time]
+        self.off = torch.from_numpy(x.offsets).to(dev)
+        self.ts = torch.from_numpy(x.ts).to(dev)
+        self.max_len = int(np.diff(x.offsets).max())
+        l = ops.make_layer_args(self.xin, self.w1[0], self.w2[0], self.off, self.ts, self.rp[0],
+                                self.rt[0], x.alpha, H=x.H, d=x.d, max_seq_len=self.max_len,
+                                x_out=self.bufs[0])
+        self.ws = torch.empty(ops.layer_workspace_bytes(l), dtype=torch.uint8, device=dev)
+
+    def step(self, ev0=None, ev1=None):
+        from hstu_sequential_transducer_causal_amd import ops
+        cur = self.xin
+        for l in range(self.x.layers):
+            out = self.bufs[l % 2]
+            ops.hstu_layer_fwd(cur, self.w1[l], self.w2[l], self.off, self.ts, self.rp[l],
+                               self.rt[l], self.x.alpha, H=self.x.H, d=self.x.d,
+                               max_seq_len=self.max_len, ln_eps=self.x.eps, x_out=out,
+                               workspace=self.ws)
+            cur = out
+
+
+def time_case(case, steps, warmup, core_events=True):
+    """Wall time per step (synchronised bracket) and mean core-kernel time (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize()
+    evs = []
+    if core_events:
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(); b.record()           # materialise the HIP events
+            evs.append((a, b))
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if core_events:
+            case.step(evs[i][0].cuda_event, evs[i][1].cuda_event)
+        else:
+            case.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    core_ms = None
+    if core_events:
+        core_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return ms_step, core_ms
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longseq_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc", "attn_bf16.hip")
+
+
+def kernel_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention core from the committed counter
+    runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor), or None
+    when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return int(t["bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    n = 256 * 1024 * 1024
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(x, nseq):
+    """The oracle as it stands, on the first nseq sequences of the workload."""
+    import oracle
+    from hstu_sequential_transducer_causal_amd import flops
+    seqs = list(range(x.B if nseq <= 0 else min(nseq, x.B)))
+    L = np.diff(x.offsets)
+    s1 = int(x.offsets[seqs[-1] + 1])
+    t0 = time.perf_counter()
+    oracle.attn(x.q[:s1], x.k[:s1], x.v[:s1], x.offsets[:len(seqs) + 1], x.ts[:s1], x.rab_pos,
+                x.rab_time, x.alpha)
+    dt = time.perf_counter() - t0
+    fl = flops.attn_flops(L[seqs], x.H, x.d, x.d)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"fp64 oracle attention (no epilogue) on sequences {seqs} of the same "
+                      f"workload (lengths {[int(v) for v in L[seqs]]}, {x.H} heads), "
+                      f"{fl / 1e9:.1f} GFLOP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    import hstu_synth as synth
+    from hstu_sequential_transducer_causal_amd import _lib, flops
+
+    _lib.load()
+    dev = torch.device("cuda:0")
+    wl = args.workload
+    log(f"generating workload {wl}")
+    x = synth.config(wl)
+    L = np.diff(x.offsets)
+    if wl == 5:
+        case = StackCase(x, dev)
+        fl = 0
+        for _ in range(x.layers):
+            lf = flops.layer_flops(L, x.H, x.d, x.D)
+            fl += lf["f1"] + lf["attn"] + lf["f2"]
+        attn_fl_core = flops.attn_flops(L, x.H, x.d, x.d)
+    else:
+        case = AttnCase(x, dev, with_scores=(wl == 4))
+        fl = flops.attn_flops(L, x.H, x.d, x.d, x.num_candidates)
+        attn_fl_core = fl
+    log(f"workload {x.name}: B={x.B} T={x.T} GFLOP/step={fl / 1e9:.2f}")
+    ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5))
+    value = fl / (ms_step * 1e-3) / 1e12
+    tokens_s = x.T / (ms_step * 1e-3)
+    log(f"step {ms_step:.3f} ms, core {core_ms} ms, {value:.1f} TFLOP/s")
+
+    roofline = None
+    if core_ms:
+        ach = attn_fl_core / (core_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                    "kernel": "attn_bf16_kernel", "core_ms": round(core_ms, 4)}
+
+    line = {
+        "metric": "HSTU attention fwd TFLOP/s (unmasked) + jagged tokens/s; % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": x.name, "global_batch": x.B, "tokens": x.T,
+                   "max_seq_len": int(L.max()), "heads": x.H, "head_dim": x.d},
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+    }
+
+    if not args.no_others:
+        others = {}
+        for w in (2, 4, 5):
+            if w == wl:
+                continue
+            xo = synth.config(w)
+            Lo = np.diff(xo.offsets)
+            if w == 5:
+                c = StackCase(xo, dev)
+                flo = sum(sum(flops.layer_flops(Lo, xo.H, xo.d, xo.D).values()) for _ in range(xo.layers))
+                st, ce = time_case(c, max(2, args.steps // 10), 1, core_events=False)
+            else:
+                c = AttnCase(xo, dev, with_scores=(w == 4))
+                flo = flops.attn_flops(Lo, xo.H, xo.d, xo.d, xo.num_candidates)
+                st, ce = time_case(c, max(3, args.steps // 3), 2)
+            rec = {"ms_per_step": round(st, 4), "tflops": round(flo / (st * 1e-3) / 1e12, 2),
+                   "tokens_per_s": round(xo.T / (st * 1e-3), 1), "tokens": xo.T}
+            if ce:
+                rec["core_ms"] = round(ce, 4)
+                rec["core_tflops"] = round(flo / (ce * 1e-3) / 1e12, 2)
+            if w == 4:
+                rec["candidates_per_s"] = round(int(xo.num_candidates.sum()) / (st * 1e-3), 1)
+            others[xo.name] = rec
+            log(f"{xo.name}: {rec}")
+            del c
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
+
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline and wl != 5:
+        log("timing the oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,6 +90,9 @@ hstu_status validate_attn(const hstu_attn_args* a, bool need_epi) {
         if (!a->rab_pos || !a->rab_time) return fail(HSTU_ERR_ARG, "bias tables must be non-NULL");
         if (epi && !a->u) return fail(HSTU_ERR_ARG, "u is NULL but the LN*U epilogue is requested");
         if (a->dtype == HSTU_BF16) {
+            const int64_t row_bytes = 2 * (a->k_stride > a->v_stride ? a->k_stride : a->v_stride);
+            if (int64_t(a->max_seq_len) * row_bytes > int64_t(0x7fffffff))
+                return fail(HSTU_ERR_UNSUPPORTED, "max_seq_len * K/V row bytes must stay below 2^31");
             if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || (a->q_stride % 8) || (a->k_stride % 8) ||
                 (a->v_stride % 8))
                 return fail(HSTU_ERR_UNSUPPORTED, "bf16 q/k/v rows must be 16-byte aligned");
@@ -120,16 +123,28 @@ struct Sched {
     hstu::SchedLayout layout;
     int32_t* ctrl;
     int32_t* qscan;
+    int32_t* bscan;
     hstu::WorkItem* items;
+    uint32_t* stats;
+    uint32_t* enc;
 };
+
+// The fp32 core needs neither row codes nor block ranges.
+hstu::SchedLayout sched_layout_for(const hstu_attn_args* a, size_t base) {
+    const bool bf16 = a->dtype == HSTU_BF16;
+    return hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), bf16 ? a->num_rows : 0, base);
+}
 
 Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
     Sched s;
-    s.layout = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), base);
+    s.layout = sched_layout_for(a, base);
     uint8_t* w = static_cast<uint8_t*>(ws);
     s.ctrl = reinterpret_cast<int32_t*>(w + s.layout.off_ctrl);
     s.qscan = reinterpret_cast<int32_t*>(w + s.layout.off_qscan);
+    s.bscan = reinterpret_cast<int32_t*>(w + s.layout.off_bscan);
     s.items = reinterpret_cast<hstu::WorkItem*>(w + s.layout.off_items);
+    s.stats = reinterpret_cast<uint32_t*>(w + s.layout.off_stats);
+    s.enc = reinterpret_cast<uint32_t*>(w + s.layout.off_enc);
     return s;
 }
 
@@ -143,8 +158,20 @@ hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream
     sa.tile_n = tile_n_for(a->dtype);
     sa.ctrl = s.ctrl;
     sa.qscan = s.qscan;
+    sa.bscan = s.bscan;
     sa.items = s.items;
-    return hstu::launch_sched(sa, stream);
+    hipError_t e = hstu::launch_sched(sa, stream);
+    if (e != hipSuccess || a->dtype != HSTU_BF16) return e;
+    hstu::TsPrepArgs tp;
+    tp.B = a->B;
+    tp.offsets = a->seq_offsets;
+    tp.lengths = a->seq_lengths;
+    tp.ts = a->timestamps;
+    tp.bscan = s.bscan;
+    tp.enc = s.enc;
+    tp.stats = s.stats;
+    tp.cap_blk = (int64_t)s.layout.cap_blk;
+    return hstu::launch_ts_prep(tp, stream);
 }
 
 hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
@@ -166,6 +193,10 @@ hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream)
     c.items = s.items;
     c.ctrl = s.ctrl;
     c.cursor = s.ctrl + 1;
+    c.bscan = s.bscan;
+    c.stats = s.stats;
+    c.enc = s.enc;
+    c.num_rows = a->num_rows;
     hipError_t e;
     if (a->ev_core_begin) {
         e = hipEventRecord(static_cast<hipEvent_t>(a->ev_core_begin), stream);
@@ -224,14 +255,14 @@ size_t hstu_attn_workspace_bytes(const hstu_attn_args* a) {
     hstu_status st = validate_attn(a, false);
     memcpy(g_last_error, saved, sizeof(saved));
     if (st != HSTU_OK) return 0;
-    return hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    return sched_layout_for(a, 0).bytes;
 }
 
 hstu_status hstu_attn_fwd(const hstu_attn_args* a, void* ws, size_t ws_bytes, void* stream_) {
     hstu_status st = validate_attn(a, false);
     if (st != HSTU_OK) return st;
     if (a->B == 0) return ok();
-    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    const size_t need = sched_layout_for(a, 0).bytes;
     st = check_workspace(ws, ws_bytes, need);
     if (st != HSTU_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -264,7 +295,7 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
     if (a->B == 0) return ok();
     if (!a->num_candidates) return fail(HSTU_ERR_ARG, "num_candidates is required for M-FALCON");
     if (!m->w || !m->scores) return fail(HSTU_ERR_ARG, "w and scores must be non-NULL");
-    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    const size_t need = sched_layout_for(a, 0).bytes;
     st = check_workspace(ws, ws_bytes, need);
     if (st != HSTU_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -292,6 +323,8 @@ hstu_status validate_layer(const hstu_layer_args* l) {
     if (l->max_seq_len < 0 || l->max_seq_len > hstu::kMaxSeqLen)
         return fail(HSTU_ERR_ARG, "max_seq_len %d outside [0, %d]", l->max_seq_len, hstu::kMaxSeqLen);
     if (l->num_rows < 0) return fail(HSTU_ERR_ARG, "num_rows < 0");
+    if (int64_t(l->max_seq_len) * 4 * l->H * l->d * 2 > int64_t(0x7fffffff))
+        return fail(HSTU_ERR_UNSUPPORTED, "max_seq_len * Z row bytes must stay below 2^31");
     if (l->num_pos_buckets < 1 || l->num_pos_buckets > hstu::kMaxPosBuckets)
         return fail(HSTU_ERR_ARG, "num_pos_buckets outside [1, %d]", hstu::kMaxPosBuckets);
     if (l->num_time_buckets < 1) return fail(HSTU_ERR_ARG, "num_time_buckets < 1");
@@ -319,7 +352,7 @@ LayerWs layer_ws(const hstu_layer_args* l) {
     w.o = align256(w.z + T * 4 * hd * 2);
     w.y = align256(w.o + T * hd * 2);
     w.sched = align256(w.y + T * hd * 2);
-    w.total = hstu::sched_layout(l->B, l->max_seq_len, hstu::kBf16TileM, w.sched).bytes;
+    w.total = hstu::sched_layout(l->B, l->max_seq_len, hstu::kBf16TileM, l->num_rows, w.sched).bytes;
     return w;
 }
 
@@ -413,7 +446,7 @@ hstu_status hstu_attn_schedule(const hstu_attn_args* a, void* ws, size_t ws_byte
     if (tile_n_out) *tile_n_out = tile_n_for(a->dtype);
     *count_out = 0;
     if (a->B == 0) return ok();
-    const size_t need = hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), 0).bytes;
+    const size_t need = sched_layout_for(a, 0).bytes;
     st = check_workspace(ws, ws_bytes, need);
     if (st != HSTU_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);

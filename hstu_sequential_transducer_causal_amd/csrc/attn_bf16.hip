@@ -8,26 +8,35 @@
 // "Pointwise aggregated attention": SiLU in place of softmax, no
 // normalisation over the sequence, a relative bias from position and time.)
 //
-// Design (one workgroup = 4 waves = one work item of 128 query rows x 1 head):
-//   * Each wave owns 32 query rows.  It computes S^T = K Q^T with
-//     v_mfma_f32_16x16x32_bf16 so that, in the accumulator, lane l holds
-//     query row (l % 16) against 4 consecutive keys: after the bias, SiLU,
-//     mask and bf16 packing these registers are directly the A operand of
-//     the second product O += A V.  Q stays in registers for the whole item.
-//   * K tiles (64 keys x 128) are staged row-major in LDS with a 16-byte XOR
-//     swizzle; V tiles are transposed while staging (d-major) so that the B
-//     operand of A V is two 8-byte LDS reads.  The next tile's global loads
-//     are issued before the current tile's math (register prefetch).
-//   * The relative bias enters as the MFMA's initial accumulator:
-//       position: a per-item LDS table E[u] = rab_pos[clamp(u - 64, 0, P-1)];
-//         a lane's 16 bias entries of a 16x16 block sit at fixed offsets
-//         from one clamped base index, so no per-element index math;
-//       time: timestamps are re-encoded per tile as e = 2 (t - t_first) + 2^31
-//         (exact when all |t - t_first| < 2^30, checked per tile), so
-//         |e_i - e_j| + 1 = 2|dt| + 1 is one v_sad_u32 and its leading-zero
-//         count c = 31 - bit_length(|dt|) indexes a 32-entry LDS table;
-//         tiles outside that range use 64-bit arithmetic.
-//   * Tiles whose pairs are all visible skip the mask; the others select
+// Design: one workgroup = 4 waves = one work item of 128 query rows x 1 head;
+// each wave owns 32 query rows; key tiles of 32 keys; v_mfma_f32_32x32x16_bf16.
+//
+//   * S^T = K Q^T per 32-key tile: in the accumulator lane l holds query row
+//     (l % 32) against 16 keys, which after bias + SiLU + bf16 packing are
+//     directly the A operand of O += A V.  Q stays in registers.
+//   * K and V tiles are staged row-major into a 4-stage LDS ring by buffer
+//     loads that write LDS directly (no registers, no VALU; rows past the
+//     sequence end fall outside the buffer's range and arrive as zeros), three
+//     tiles ahead of their use.  V is read transposed by ds_read_b64_tr_b16,
+//     so the B operand of A V needs no shuffle.
+//   * Timestamps arrive pre-encoded (a small preparation kernel): per row
+//     e = 2 (t - t_first) + 2^31, exact when |t - t_first| < 2^30, and per
+//     32-row block the range [min e, max e] (or a "wide" mark).
+//   * The relative bias is the MFMA's initial accumulator, chosen per 32 x 32
+//     block with wave-uniform (scalar) tests:
+//       - time bucket constant over the block (from the row and key blocks'
+//         ranges): no per-element time work; the constant folds into the first
+//         FMA of the activation;
+//       - position bucket clamped over the whole block: no position reads;
+//       - otherwise position entries come from a reversed LDS table (2 shifted
+//         copies, so a lane reads 2 entries with one 8-byte load) and the time
+//         bucket per element: |e_i - e_j| + 1 = 2|dt| + 1 is one v_sad_u32 and
+//         its leading-zero count c = 31 - bit_length(|dt|) indexes a 32-entry
+//         LDS table;
+//       - blocks outside the 2^30 range use 64-bit arithmetic.
+//   * SiLU in exp2 form: t = -log2(e) (S + c), A' = t / (1 + 2^t); the factor
+//     -ln 2 that turns A' into SiLU(S) is folded into alpha.
+//   * Blocks whose pairs are all visible skip the mask; the others select
 //     (never multiply) so that padding and masked garbage cannot leak.
 //   * Persistent grid: workgroups pull items (longest first) from the
 //     scheduler's list through an atomic cursor until it is exhausted.
@@ -39,11 +48,14 @@ namespace hstu {
 namespace {
 
 constexpr int BM = kBf16TileM;   // 128 query rows per item
-constexpr int BN = kBf16TileN;   // 64 keys per tile
+constexpr int BN = kBf16TileN;   // 32 keys per tile
 constexpr int HD = 128;          // head dim
 constexpr int kThreads = 256;
-constexpr int kPosMargin = 64;   // table entries below diff 0
-constexpr int kPosExtra = 64;    // table entries beyond P-1 (clamped values)
+constexpr int kRowBytes = HD * 2;
+constexpr int kStages = 4;       // LDS ring depth: tiles t .. t+3 in flight
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
     int H;
@@ -57,301 +69,357 @@ struct Params {
     const float* rab_pos; int P; int rp_hs;
     const float* rab_time; int NT; int rt_hs;
     float alpha;
-    int act;
     uint16_t* o; int64_t os;
     const WorkItem* items;
     const int32_t* ctrl;
     int32_t* cursor;
+    const int32_t* bscan;
+    const uint32_t* stats;
+    const uint32_t* enc;
+    int pos_copy;   // floats per shifted copy of the reversed position table
 };
 
 struct Smem {
-    uint8_t k[BN * HD * 2];         // [64 keys][128 d] bf16, 16-B chunks swizzled by key & 15
-    uint8_t vt[HD * BN * 2];        // [128 d][64 keys] bf16, 8-B chunks swizzled by d & 14
-    uint32_t tsenc[BN];             // 2 (t - t_first) + 2^31
-    int64_t ts64[BN];
-    float tt_fast[32];              // by leading-zero count of 2|dt|+1
-    float tt_wide[65];              // by bit length of |dt|
+    uint8_t k[kStages][BN * kRowBytes];   // [32 keys][128 d], 16-B chunk c of row r at c ^ (r & 15)
+    uint8_t v[kStages][BN * kRowBytes];   // [32 keys][128 d], 16-B chunk c of row r at c ^ 4 (r & 3)
+    uint32_t tsk[kStages][64];            // [0..31] key codes, [32..33] key block range
+    float tt_fast[32];                    // by leading-zero count of 2|dt| + 1
+    float tt_wide[65];                    // by bit length of |dt|
     int32_t item[4];
-    int32_t head;
-    int32_t flags;
+    int32_t work;
 };
 
-
-__device__ __forceinline__ bool narrow_delta(int64_t d) {
-    return d > -(int64_t(1) << 30) && d < (int64_t(1) << 30);
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t encode_ts(int64_t d) {
-    return uint32_t(int32_t(d) * 2) + 0x80000000u;
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniu(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 4 bf16 of V^T through the LDS transpose read: within each 16-lane group,
+// output lane i, element k comes from input lane 4k + i/4, element i % 4.
+__device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p);
+    return __builtin_bit_cast(u32x2, r);
 }
 
-// Global -> register part of staging one key tile.
-struct Prefetch {
-    u32x4 kr[4];
-    u32x4 vr[4];
-    int64_t t;
+__device__ __forceinline__ int kswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
+__device__ __forceinline__ int vswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 3) << 2)) << 4); }
+
+// vmcnt(n) with the other counters left alone (n <= 15).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Per-item state of the tile loads.  Wave w fills key rows 8w .. 8w+7 of the
+// K and V tiles with 2 buffer loads each: lane l of load m writes 16 bytes at
+// row 8w + 4m + l/16, physical chunk l % 16, so it fetches the logical chunk
+// that the swizzle puts there.  Wave 0 also loads the 32 key codes and the key
+// block's range (lanes 32, 33) with one 4-byte-per-lane load.
+struct TileDma {
+    __amdgpu_buffer_rsrc_t krs, vrs, wrs;
+    uint32_t koff[2], voff[2];
+    uint32_t ktile, vtile;        // bytes per key tile in K and V
+    int64_t enc_row0;             // byte offset of the sequence's first code in the workspace
+    int64_t stats0;               // byte offset of the sequence's first block range
 };
 
-__device__ __forceinline__ void prefetch_tile(const Params& p, Prefetch& pf, int64_t row0, int L, int h,
-                                              int j0) {
-    const int tid = threadIdx.x;
-    const int chunk = tid & 15;
-    const int rsub = tid >> 4;   // 0..15
+__device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, int L, int wave,
+                                           int lane) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        int j = j0 + r4 * 16 + rsub;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        pf.kr[r4] = z;
-        if (j < L)
-            pf.kr[r4] = *reinterpret_cast<const u32x4*>(p.k + (row0 + j) * p.ks + h * HD + chunk * 8);
+    for (int m = 0; m < 2; ++m) {
+        const int blk = (2 * wave + m) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.krs, (lds_void*)(uintptr_t)(s.k[stage] + blk), 16, d.koff[m],
+                                                 kt * d.ktile, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.vrs, (lds_void*)(uintptr_t)(s.v[stage] + blk), 16, d.voff[m],
+                                                 kt * d.vtile, 0, 0);
     }
-    // V: this thread owns keys j0 + 4*rsub + 0..3 at d = 8*chunk .. 8*chunk+7
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        int j = j0 + 4 * rsub + r;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        pf.vr[r] = z;
-        if (j < L)
-            pf.vr[r] = *reinterpret_cast<const u32x4*>(p.v + (row0 + j) * p.vs + h * HD + chunk * 8);
+    if (wave == 0) {
+        const int j = kt * BN + lane;
+        uint32_t off = 0x80000000u;   // out of range: lands as 0
+        if (lane < 32 && j < L) off = (uint32_t)(d.enc_row0 + 4 * (int64_t)j);
+        if (lane == 32 || lane == 33) off = (uint32_t)(d.stats0 + 8 * (int64_t)kt + 4 * (lane - 32));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.wrs, (lds_void*)(uintptr_t)(s.tsk[stage]), 4, off, 0, 0, 0);
     }
-    pf.t = 0;
-    if (tid < BN && j0 + tid < L) pf.t = p.ts[row0 + j0 + tid];
 }
 
-// Register -> LDS part of staging; returns this thread's "tile is wide" vote.
-__device__ __forceinline__ bool store_tile(Smem& s, const Prefetch& pf, int L, int j0, int64_t t_first) {
-    const int tid = threadIdx.x;
-    const int chunk = tid & 15;
-    const int rsub = tid >> 4;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        int row = r4 * 16 + rsub;
-        *reinterpret_cast<u32x4*>(s.k + row * (HD * 2) + ((chunk ^ (row & 15)) << 4)) = pf.kr[r4];
-    }
-    // transpose 4 keys x 8 d into 8 rows of V^T, 4 keys (8 bytes) each
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        uint32_t x0 = (pf.vr[0][w] >> sh) & 0xffffu;
-        uint32_t x1 = (pf.vr[1][w] >> sh) & 0xffffu;
-        uint32_t x2 = (pf.vr[2][w] >> sh) & 0xffffu;
-        uint32_t x3 = (pf.vr[3][w] >> sh) & 0xffffu;
-        u32x2 val = {x0 | (x1 << 16), x2 | (x3 << 16)};
-        int d = chunk * 8 + e;
-        *reinterpret_cast<u32x2*>(s.vt + d * (BN * 2) + ((rsub ^ (d & 14)) << 3)) = val;
-    }
-    bool wide = false;
-    if (tid < BN) {
-        int64_t t = (j0 + tid < L) ? pf.t : t_first;
-        int64_t dlt = t - t_first;
-        wide = !narrow_delta(dlt);
-        s.tsenc[tid] = encode_ts(dlt);
-        s.ts64[tid] = t;
-    }
-    return wide;
-}
+// Bucket index (leading zeros of 2|dt| + 1) of an encoded gap 2|dt|.
+__device__ __forceinline__ uint32_t clz_gap(uint32_t gap2) { return __builtin_clz(gap2 + 1u); }
 
-__global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p) {
+template <bool kSilu>
+__global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const void* ws_base, uint32_t ws_bytes) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     Smem& s = *reinterpret_cast<Smem*>(smem_raw);
-    float* epos = reinterpret_cast<float*>(smem_raw + sizeof(Smem));   // [P + 128]
+    float* ptab = reinterpret_cast<float*>(smem_raw + ((sizeof(Smem) + 15) & ~size_t(15)));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int c16 = lane & 15;
-    const int g = lane >> 4;
+    const int l32 = lane & 31;
+    const int h2 = lane >> 5;            // which 8-wide k slice / 4-key group of the lane
     const int total_work = p.ctrl[0] * p.H;
     const bool shared_tables = (p.rp_hs == 0) && (p.rt_hs == 0);
+    const int P = p.P;
+    const int Dhi = P + 63;              // position difference of reversed-table entry 0
+    const int CS = p.pos_copy;
+    const float kNegLog2e = -kLog2e;
+    const float alpha_eff = kSilu ? -p.alpha * 0.69314718055994531f : p.alpha;
+    const int per_tile = wave == 0 ? 5 : 4;   // buffer loads per tile of this wave
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)ws_base, (short)0, (int)ws_bytes,
+                                                                        0x00020000);
+    const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
+    const int64_t stats_base = (const uint8_t*)p.stats - (const uint8_t*)ws_base;
     int loaded_head = -1;
 
     for (;;) {
         if (tid == 0) {
-            int w = atomicAdd(p.cursor, 1);
-            s.head = w;
+            const int w = atomicAdd(p.cursor, 1);
+            s.work = w;
             if (w < total_work) {
-                WorkItem it = p.items[w / p.H];
+                const WorkItem it = p.items[w / p.H];
                 s.item[0] = it.b; s.item[1] = it.qt; s.item[2] = it.a_end; s.item[3] = it.kb;
             }
         }
         __syncthreads();
-        const int w = s.head;
+        const int w = uni(s.work);
         if (w >= total_work) break;
-        const int b = s.item[0], qt = s.item[1], a_end = s.item[2];
-        const int kb_begin = s.item[3] & 0xffff, kb_end = s.item[3] >> 16;
+        const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
+        const int kbw = uni(s.item[3]);
+        const int kb_begin = kbw & 0xffff, kb_end = kbw >> 16;
         const int h = w % p.H;
 
         const int64_t row0 = p.offsets[b];
         const int L = p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0;
         const int n = p.ncand ? L - p.ncand[b] : L;
-        const int64_t t_first = p.ts[row0];
+        const int bbase = p.bscan[b];
 
-        // ---- relative-bias tables (per head only when tables differ by head)
+        // ---- bias tables (reloaded only when they differ by head)
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
             const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
             const float* rt = p.rab_time + (int64_t)h * p.rt_hs;
-            const int ne = p.P + kPosMargin + kPosExtra;
-            for (int u = tid; u < ne; u += kThreads) {
-                int dd = min(max(u - kPosMargin, 0), p.P - 1);
-                epos[u] = rp[dd];
+            // copy c holds Rv[w - c], Rv[u] = rab_pos[clamp(Dhi - u, 0, P-1)]
+            for (int e = tid; e < 2 * CS; e += kThreads) {
+                const int c = e / CS;
+                const int u = e - c * CS - c;
+                const int dd = min(max(Dhi - u, 0), P - 1);
+                ptab[e] = rp[dd];
             }
             if (tid < 32) s.tt_fast[tid] = rt[min(p.NT - 1, 31 - tid)];
             if (tid < 65) s.tt_wide[tid] = rt[min(p.NT - 1, tid)];
             loaded_head = h;
         }
 
-        // ---- this wave's query rows: Q fragments, timestamps, positions
+        // ---- this wave's 32 query rows (all its global reads precede the tile loads)
         const int wrow0 = qt * BM + wave * 32;
-        bf16x8 qf[2][4];
-        uint32_t tsi[2];
-        int64_t ts64i[2];
-        int prow[2];
-        bool narrow_q = true;
+        const int i = wrow0 + l32;               // this lane's query row
+        const bool row_valid = i < L;
+        bf16x8 qf[8];
+        {
+            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int i = wrow0 + qb * 16 + c16;
-            const bool valid = i < L;
-            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + g * 8;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int kc = 0; kc < 8; ++kc) {
                 u32x4 z = {0u, 0u, 0u, 0u};
-                if (valid) z = *reinterpret_cast<const u32x4*>(qp + c * 32);
-                qf[qb][c] = __builtin_bit_cast(bf16x8, z);
+                if (row_valid) z = *reinterpret_cast<const u32x4*>(qp + kc * 16);
+                qf[kc] = __builtin_bit_cast(bf16x8, z);
             }
-            int64_t t = valid ? p.ts[row0 + i] : t_first;
-            narrow_q = narrow_q && narrow_delta(t - t_first);
-            tsi[qb] = encode_ts(t - t_first);
-            ts64i[qb] = t;
-            prow[qb] = min(i, n);
         }
+        const int64_t t_first = p.ts[row0];
+        const int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
+        const uint32_t tie = row_valid ? p.enc[row0 + i] : 0x80000000u;
+        const int qblk = bbase + qt * (BM / 32) + wave;   // this wave's 32-row block
+        const bool wave_rows = wrow0 < L;
+        uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
+        uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
+        rmin = uniu(rmin);
+        rmax = uniu(rmax);
+        const bool rows_wide = rmin > rmax;
+        const int prow = min(i, n);
+        const int prow_min = uni(min(wrow0, n));
 
-        f32x4 oacc[2][8];
+        f32x16 oacc[4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) oacc[qb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
 
+        TileDma dma;
+        {
+            const uint16_t* kb0 = p.k + row0 * p.ks + h * HD;
+            const uint16_t* vb0 = p.v + row0 * p.vs + h * HD;
+            dma.krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb0, (short)0, (int)(L * p.ks * 2), 0x00020000);
+            dma.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb0, (short)0, (int)(L * p.vs * 2), 0x00020000);
+            dma.wrs = wrs;
+            const int pc = lane & 15;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int rr = 8 * wave + 4 * m + (lane >> 4);
+                dma.koff[m] = (uint32_t)(rr * p.ks * 2 + ((pc ^ (rr & 15)) << 4));
+                dma.voff[m] = (uint32_t)(rr * p.vs * 2 + ((pc ^ ((rr & 3) << 2)) << 4));
+            }
+            dma.ktile = (uint32_t)(BN * p.ks * 2);
+            dma.vtile = (uint32_t)(BN * p.vs * 2);
+            dma.enc_row0 = enc_base + 4 * row0;
+            dma.stats0 = stats_base + 8 * (int64_t)bbase;
+        }
         const int ntiles = a_end + (kb_end - kb_begin);
-        Prefetch pf;
-        if (ntiles > 0) prefetch_tile(p, pf, row0, L, h, 0 < a_end ? 0 : kb_begin * BN);
-        __syncthreads();  // tables visible; previous item's LDS reads done
+        auto tile_of = [&](int it) { return it < a_end ? it : kb_begin + (it - a_end); };
+#pragma unroll
+        for (int pre = 0; pre < kStages - 1; ++pre)
+            if (pre < ntiles) issue_tile(dma, s, pre, tile_of(pre), L, wave, lane);
 
         for (int it = 0; it < ntiles; ++it) {
-            const int kt = it < a_end ? it : kb_begin + (it - a_end);
+            const int kt = tile_of(it);
             const int j0 = kt * BN;
-            const bool wide_vote = store_tile(s, pf, L, j0, t_first);
-            const int wide = __syncthreads_or(wide_vote ? 1 : 0) || !narrow_q;
-            if (it + 1 < ntiles) {
-                const int kt1 = (it + 1) < a_end ? (it + 1) : kb_begin + (it + 1 - a_end);
-                prefetch_tile(p, pf, row0, L, h, kt1 * BN);
-            }
+            const int stage = it & (kStages - 1);
+            // this tile's loads have landed once at most the later tiles' are outstanding
+            const int later = min(kStages - 2, ntiles - 1 - it);
+            wait_vmcnt(later * per_tile);
+            __syncthreads();   // everyone's loads for this tile are visible; tile it-1 is done
+            if (it + kStages - 1 < ntiles)
+                issue_tile(dma, s, (it + kStages - 1) & (kStages - 1), tile_of(it + kStages - 1), L, wave, lane);
+            const uint8_t* k_lds = s.k[stage];
+            const uint8_t* v_lds = s.v[stage];
+            const uint32_t* tsk = s.tsk[stage];
 
-            // Pairs of this wave's rows in this tile: all visible?
-            const bool full = (j0 + BN <= n) && (j0 + BN - 1 <= wrow0);
+            // ---------- block-uniform facts (scalar)
+            const uint32_t kmn = uniu(tsk[32]), kmx = uniu(tsk[33]);
+            const bool wide = rows_wide || kmn > kmx;
+            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
+            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
+            const uint32_t czlo = clz_gap(lo), czhi = clz_gap(hi);
+            const bool time_uniform = !wide && czlo == czhi;
+            const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
+            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
 
-            // ---------------- S^T = K Q^T + bias
-            f32x4 sacc[2][4];
-            int pbase[2];
+            // ---------- initial accumulator: the relative bias
+            f32x16 acc;
+            float cadd = 0.0f;
+            if (time_uniform) cadd = s.tt_fast[czlo];
+            if (pos_clamped) {
+                cadd += ptab[0];      // entry u = 0 is difference Dhi >= P-1: rab_pos[P-1]
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                int x = prow[qb] - (j0 + 4 * g);
-                x = min(max(x, 0), p.P + 50);
-                pbase[qb] = x + kPosMargin;
-            }
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            } else {
+                int x = prow - (j0 + 4 * h2);
+                x = min(max(x, 0), P + 26);
+                const int u0 = Dhi - x;
+                const int c = u0 & 1;
+                const float* pp = ptab + c * CS + (u0 + c);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int krow = kb * 16 + c16;
-                bf16x8 kf[4];
+                for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    kf[c] = *reinterpret_cast<const bf16x8*>(s.k + krow * (HD * 2) + (((4 * c + g) ^ c16) << 4));
-                const u32x4 tj = *reinterpret_cast<const u32x4*>(&s.tsenc[kb * 16 + 4 * g]);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    f32x4 init;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float tb;
-                        if (!wide) {
-                            uint32_t x = sad_u32(tsi[qb], tj[r], 1u);
-                            tb = s.tt_fast[__builtin_clz(x)];
-                        } else {
-                            int64_t dt = ts64i[qb] - s.ts64[kb * 16 + 4 * g + r];
-                            uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                            tb = s.tt_wide[bit_length_u64(ad)];
-                        }
-                        init[r] = epos[pbase[qb] - 16 * kb - r] + tb;
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const float2 pv = *reinterpret_cast<const float2*>(pp + 8 * q + 2 * t2);
+                        acc[4 * q + 2 * t2] = pv.x;
+                        acc[4 * q + 2 * t2 + 1] = pv.y;
                     }
-                    f32x4 acc = init;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc = mfma16x16x32(kf[c], qf[qb][c], acc);
-                    sacc[qb][kb] = acc;
                 }
             }
-
-            // ---------------- activation, mask, pack to bf16 (A operand)
-            bf16x8 pa[2][2];
+            if (!time_uniform) {
+                if (!wide) {
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int i = wrow0 + qb * 16 + c16;
+                    for (int q = 0; q < 4; ++q) {
+                        const u32x4 tj = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    uint32_t wv[4];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int kb = 2 * c2 + hh;
-                        float a4[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float sv = sacc[qb][kb][r];
-                            float a = (p.act == 0) ? silu_fast(sv) : sv;
-                            if (!full) {
-                                const int j = j0 + kb * 16 + 4 * g + r;
-                                const bool vis = (j < L) && (i < n ? (j <= i) : (j < n || j == i));
-                                a = vis ? a : 0.0f;
-                            }
-                            a4[r] = a;
-                        }
-                        wv[hh * 2 + 0] = pack_bf16x2(a4[0], a4[1]);
-                        wv[hh * 2 + 1] = pack_bf16x2(a4[2], a4[3]);
+                        for (int t = 0; t < 4; ++t) acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, tj[t], 1u))];
                     }
-                    u32x4 packed = {wv[0], wv[1], wv[2], wv[3]};
-                    pa[qb][c2] = __builtin_bit_cast(bf16x8, packed);
+                } else {
+                    const int64_t* tsb = p.ts + row0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const int j = j0 + 8 * q + 4 * h2 + t;
+                            const int64_t tj = j < L ? tsb[j] : t_first;
+                            const int64_t dt = ti64 - tj;
+                            const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
+                            acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
+                        }
+                    }
                 }
             }
 
-            // ---------------- O += A V
+            // ---------- S^T = K Q^T (+ bias)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int kc = 0; kc < 8; ++kc) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
+                acc = mfma32(kf, qf[kc], acc);
+            }
+
+            // ---------- activation, mask, bf16 packing
+            float a[16];
+            if (kSilu) {
+                const float c2 = cadd * kNegLog2e;
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    const int d = nb * 16 + c16;
-                    const uint8_t* vrow = s.vt + d * (BN * 2);
-                    u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (((c2 * 8 + g) ^ (d & 14)) << 3));
-                    u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (((c2 * 8 + 4 + g) ^ (d & 14)) << 3));
-                    u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-                    bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+                for (int r = 0; r < 16; ++r) {
+                    const float t = __builtin_fmaf(acc[r], kNegLog2e, c2);
+                    const float e = __builtin_amdgcn_exp2f(t);
+                    a[r] = t * __builtin_amdgcn_rcpf(1.0f + e);
+                }
+            } else {
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) oacc[qb][nb] = mfma16x16x32(pa[qb][c2], vf, oacc[qb][nb]);
+                for (int r = 0; r < 16; ++r) a[r] = acc[r] + cadd;
+            }
+            if (!full) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int j = j0 + 8 * q + 4 * h2 + t;
+                        const bool vis = (j < L) && (i < n ? (j <= i) : (j < n || j == i));
+                        a[4 * q + t] = vis ? a[4 * q + t] : 0.0f;
+                    }
                 }
             }
-            __syncthreads();  // all waves done with this tile's LDS before it is overwritten
+
+            // ---------- O += A V for the tile's two 16-key chunks
+            //            (V^T fragments by transposed LDS reads)
+            const int m = lane & 15;
+            const int dsub = ((lane >> 4) & 1) * 16;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 pk;
+                pk[0] = pack_bf16x2(a[8 * c + 0], a[8 * c + 1]);
+                pk[1] = pack_bf16x2(a[8 * c + 2], a[8 * c + 3]);
+                pk[2] = pack_bf16x2(a[8 * c + 4], a[8 * c + 5]);
+                pk[3] = pack_bf16x2(a[8 * c + 6], a[8 * c + 7]);
+                const bf16x8 pa = __builtin_bit_cast(bf16x8, pk);
+                const int key0 = c * 16 + 4 * h2 + (m >> 2);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int col = nb * 32 + dsub + 4 * (m & 3);      // element column
+                    const int chunk = col >> 3;
+                    const int within = (col & 7) * 2;
+                    const u32x2 v0 = ds_read_tr(v_lds + vswz(key0, chunk) + within);
+                    const u32x2 v1 = ds_read_tr(v_lds + vswz(key0 + 8, chunk) + within);
+                    const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
+                    oacc[nb] = mfma32(pa, __builtin_bit_cast(bf16x8, vv), oacc[nb]);
+                }
+            }
         }
 
-        // ---------------- O = alpha * acc, bf16, rows < L only
+        // ---------- O = alpha * acc, bf16, rows < L only
+        // lane holds O[row 8 (r / 4) + 4 h2 + r % 4][d = nb * 32 + l32]
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int r = 0; r < 16; ++r) {
+            const int ro = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (ro < L) {
+                uint16_t* op = p.o + (row0 + ro) * p.os + h * HD + l32;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = wrow0 + qb * 16 + 4 * g + r;
-                if (i < L) {
-                    uint16_t* op = p.o + (row0 + i) * p.os + h * HD + c16;
-#pragma unroll
-                    for (int nb = 0; nb < 8; ++nb) op[nb * 16] = f32_to_bf16_bits(p.alpha * oacc[qb][nb][r]);
-                }
+                for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
             }
         }
+        __syncthreads();   // this item's LDS use is over before the next item starts
     }
 }
 
@@ -367,17 +435,27 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.ts = a.ts;
     p.rab_pos = a.rab_pos; p.P = a.P; p.rp_hs = a.rp_head_stride;
     p.rab_time = a.rab_time; p.NT = a.NT; p.rt_hs = a.rt_head_stride;
-    p.alpha = a.alpha; p.act = a.act;
+    p.alpha = a.alpha;
     p.o = static_cast<uint16_t*>(a.o); p.os = a.o_stride;
     p.items = a.items; p.ctrl = a.ctrl; p.cursor = a.cursor;
-    const size_t smem = sizeof(Smem) + sizeof(float) * size_t(a.P + kPosMargin + kPosExtra);
+    p.bscan = a.bscan; p.stats = a.stats; p.enc = a.enc;
+    p.pos_copy = ((a.P + 128 + 4) + 3) & ~3;
+    const size_t smem = ((sizeof(Smem) + 15) & ~size_t(15)) + sizeof(float) * 2 * size_t(p.pos_copy);
+    const void* fn = a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true>)
+                                : reinterpret_cast<const void*>(attn_bf16_kernel<false>);
     if (smem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bf16_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
     }
     const int grid = device_cu_count() * 2;
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(grid), dim3(kThreads), smem, stream, p);
+    // one buffer resource covers the block ranges and the row codes
+    const void* ws_base = a.stats;
+    const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
+    const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
+    if (a.act == 0)
+        hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), smem, stream, p, ws_base, wsb);
+    else
+        hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), smem, stream, p, ws_base, wsb);
     return hipGetLastError();
 }
 

@@ -22,16 +22,25 @@ struct WorkItem {
 constexpr int kMaxSeqLen = 65536;
 constexpr int kMaxPosBuckets = 8192;
 
-// Workspace carve-up of the scheduler (all offsets 256-byte aligned).
+// Rows per timestamp block: the attention core's key tile and its wave's
+// query-row slice.
+constexpr int kTsBlock = 32;
+
+// Workspace carve-up of the scheduler and the timestamp preparation (all
+// offsets 256-byte aligned).
 struct SchedLayout {
     size_t off_ctrl;   // int32[64]: [0] item count, [1] work cursor of the persistent kernel
     size_t off_qscan;  // int32[B + 1] exclusive prefix of query tiles per sequence
+    size_t off_bscan;  // int32[B + 1] exclusive prefix of 32-row timestamp blocks per sequence
     size_t off_items;  // WorkItem[cap]
+    size_t off_stats;  // uint32x2[cap_blk]: encoded timestamp range of each 32-row block
+    size_t off_enc;    // uint32[num_rows]: encoded timestamp of each row
     size_t cap;        // item capacity = B * ceil(max_seq_len / BM)
+    size_t cap_blk;    // block capacity = B * ceil(max_seq_len / 32)
     size_t bytes;      // total
 };
 
-SchedLayout sched_layout(int B, int max_seq_len, int tile_m, size_t base_offset);
+SchedLayout sched_layout(int B, int max_seq_len, int tile_m, int64_t num_rows, size_t base_offset);
 
 struct SchedArgs {
     int B;
@@ -41,14 +50,31 @@ struct SchedArgs {
     int tile_m, tile_n;
     int32_t* ctrl;
     int32_t* qscan;
+    int32_t* bscan;
     WorkItem* items;
 };
+
+// Per-row timestamp code e = 2 (t - t_first) + 2^31 (t_first: the sequence's
+// first row) and, per 32-row block of a sequence, the range [min e, max e];
+// a block with some |t - t_first| >= 2^30 gets the range {0xffffffff, 0}.
+struct TsPrepArgs {
+    int B;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const int64_t* ts;
+    const int32_t* bscan;
+    uint32_t* enc;
+    uint32_t* stats;     // pairs (min, max)
+    int64_t cap_blk;
+};
+
+hipError_t launch_ts_prep(const TsPrepArgs& a, hipStream_t stream);
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
 
 // Attention core, bf16 with MFMA, d_qk = d_v = 128.
 constexpr int kBf16TileM = 128;
-constexpr int kBf16TileN = 64;
+constexpr int kBf16TileN = 32;
 
 // Attention core, fp32 (VALU), d in {32, 64}.
 constexpr int kF32TileM = 64;
@@ -71,6 +97,10 @@ struct AttnCoreArgs {
     const WorkItem* items;
     const int32_t* ctrl;   // [0] = item count
     int32_t* cursor;       // persistent work cursor (zeroed by the scheduler)
+    const int32_t* bscan;  // timestamp blocks (bf16 core only)
+    const uint32_t* stats;
+    const uint32_t* enc;
+    int64_t num_rows;
 };
 
 hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream);

@@ -31,7 +31,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxBins = kMaxSeqLen / 64 + 2;  // cost <= number of key tiles of a sequence
+constexpr int kMaxBins = kMaxSeqLen / 32 + 2;  // cost <= number of key tiles of a sequence
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -108,21 +108,38 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
     if (tid == 0) carry_s = 0;
     __syncthreads();
 
-    // 1. query tiles per sequence -> exclusive prefix qscan[0..B]
+    // 1. query tiles and 32-row timestamp blocks per sequence -> exclusive
+    //    prefixes qscan[0..B] and bscan[0..B]
+    __shared__ int bcarry_s;
+    if (tid == 0) bcarry_s = 0;
     for (int base = 0; base < a.B; base += kThreads) {
         int b = base + tid;
-        int nq = 0;
-        if (b < a.B) nq = ceil_div(seq_length(a, b), BM);
-        int total;
+        int nq = 0, nblk = 0;
+        if (b < a.B) {
+            const int L = seq_length(a, b);
+            nq = ceil_div(L, BM);
+            nblk = ceil_div(L, kTsBlock);
+        }
+        int total, btotal;
         int ex = block_exclusive_scan(nq, wave_tot, total);
-        int carry = carry_s;
-        if (b < a.B) a.qscan[b] = carry + ex;
+        int bex = block_exclusive_scan(nblk, wave_tot, btotal);
+        int carry = carry_s, bcarry = bcarry_s;
+        if (b < a.B) {
+            a.qscan[b] = carry + ex;
+            a.bscan[b] = bcarry + bex;
+        }
         __syncthreads();
-        if (tid == 0) carry_s = carry + total;
+        if (tid == 0) {
+            carry_s = carry + total;
+            bcarry_s = bcarry + btotal;
+        }
         __syncthreads();
     }
     const int nitems = carry_s;
-    if (tid == 0) a.qscan[a.B] = nitems;
+    if (tid == 0) {
+        a.qscan[a.B] = nitems;
+        a.bscan[a.B] = bcarry_s;
+    }
     __syncthreads();
 
     // 2. histogram of item costs (key tiles per item)
@@ -171,20 +188,69 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// One wave per two 32-row blocks (lanes 0-31 and 32-63).
+__global__ void __launch_bounds__(256) ts_prep_kernel(TsPrepArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t f = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+    const int nblk = a.bscan[a.B];
+    const bool active = f < nblk && f < a.cap_blk;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    bool narrow = true;
+    int64_t fi = 0;
+    if (active) {
+        fi = f;
+        const int b = find_seq(a.bscan, a.B, (int)f);
+        const int64_t row0 = a.offsets[b];
+        const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - (int)row0;
+        const int j = ((int)f - a.bscan[b]) * kTsBlock + (lane & 31);
+        if (j < L) {
+            const int64_t t_first = a.ts[row0];
+            const int64_t d = a.ts[row0 + j] - t_first;
+            narrow = d > -(int64_t(1) << 30) && d < (int64_t(1) << 30);
+            const uint32_t e = uint32_t(int32_t(d) * 2) + 0x80000000u;
+            a.enc[row0 + j] = e;
+            mn = e;
+            mx = e;
+        }
+    }
+    int nar = narrow ? 1 : 0;
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, m, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
+        nar &= __shfl_xor(nar, m, 64);
+    }
+    if (active && (lane & 31) == 0) {
+        a.stats[2 * fi] = nar ? mn : 0xffffffffu;
+        a.stats[2 * fi + 1] = nar ? mx : 0u;
+    }
+}
+
 }  // namespace
 
-SchedLayout sched_layout(int B, int max_seq_len, int tile_m, size_t base) {
+SchedLayout sched_layout(int B, int max_seq_len, int tile_m, int64_t num_rows, size_t base) {
     SchedLayout l;
     l.off_ctrl = align256(base);
     l.off_qscan = align256(l.off_ctrl + 64 * sizeof(int32_t));
-    l.off_items = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
+    l.off_bscan = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
+    l.off_items = align256(l.off_bscan + (size_t(B) + 1) * sizeof(int32_t));
     l.cap = size_t(B) * size_t((max_seq_len + tile_m - 1) / tile_m);
-    l.bytes = align256(l.off_items + l.cap * sizeof(WorkItem));
+    l.cap_blk = size_t(B) * size_t((max_seq_len + kTsBlock - 1) / kTsBlock);
+    l.off_stats = align256(l.off_items + l.cap * sizeof(WorkItem));
+    l.off_enc = align256(l.off_stats + l.cap_blk * 2 * sizeof(uint32_t));
+    l.bytes = align256(l.off_enc + size_t(num_rows) * sizeof(uint32_t));
     return l;
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ts_prep(const TsPrepArgs& a, hipStream_t stream) {
+    if (a.cap_blk <= 0) return hipSuccess;
+    const int64_t blocks = (a.cap_blk + 7) / 8;
+    hipLaunchKernelGGL(ts_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
