@@ -109,6 +109,51 @@ __device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p) {
 __device__ __forceinline__ int kswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
 __device__ __forceinline__ int vswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 3) << 2)) << 4); }
 
+// Each block opens with 5 wait states: the compiler does not look inside
+// inline assembly for hazards, and a VALU write of an SGPR (a v_readlane
+// reloading a spilled descriptor, say) needs 5 before a vector memory
+// instruction may read that SGPR (the M0 write needs 1).
+//
+// The tile loads are issued from inline assembly, so the compiler sees no
+// LDS write it has to wait for: it cannot tell the ring stage being filled
+// from the one being read, and with the loads visible to it would wait for
+// every load in flight before each LDS read.  The waits are explicit
+// instead: the vmcnt below before a stage is read, then a bare s_barrier (the
+// memory clobber keeps LDS accesses on their side of it).  Loads complete in
+// issue order, and loads the compiler issues itself after these only make
+// its own vmcnt waits stricter, never looser.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "{m0}"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// This wave's LDS accesses (ordinary stores included) are complete.
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Barrier after which every wave sees the others' ordinary LDS stores; vector
+// memory operations (the output stores of the previous item) stay in flight.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Buffer resource: base, stride 0, num_records bytes (accesses at or past it
+// read as zero).
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = uniu((uint32_t)a);
+    r[1] = uniu((uint32_t)(a >> 32) & 0xffffu);
+    r[2] = uniu(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
 // vmcnt(n) with the other counters left alone (n <= 15).
 __device__ __forceinline__ void wait_vmcnt(int n) {
     switch (n) {
@@ -127,7 +172,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // that the swizzle puts there.  Wave 0 also loads the 32 key codes and the key
 // block's range (lanes 32, 33) with one 4-byte-per-lane load.
 struct TileDma {
-    __amdgpu_buffer_rsrc_t krs, vrs, wrs;
+    u32x4 krs, vrs, wrs;
     uint32_t koff[2], voff[2];
     uint32_t ktile, vtile;        // bytes per key tile in K and V
     int64_t enc_row0;             // byte offset of the sequence's first code in the workspace
@@ -136,20 +181,38 @@ struct TileDma {
 
 __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, int L, int wave,
                                            int lane) {
+    const uint32_t kl = lds_addr(s.k[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+    const uint32_t vl = lds_addr(s.v[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+    const uint32_t ksoff = uniu((uint32_t)kt * d.ktile), vsoff = uniu((uint32_t)kt * d.vtile);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        const int blk = (2 * wave + m) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.krs, (lds_void*)(uintptr_t)(s.k[stage] + blk), 16, d.koff[m],
-                                                 kt * d.ktile, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.vrs, (lds_void*)(uintptr_t)(s.v[stage] + blk), 16, d.voff[m],
-                                                 kt * d.vtile, 0, 0);
+        dma16(d.krs, uniu(kl + m * 1024), d.koff[m], ksoff);
+        dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
     }
     if (wave == 0) {
         const int j = kt * BN + lane;
         uint32_t off = 0x80000000u;   // out of range: lands as 0
         if (lane < 32 && j < L) off = (uint32_t)(d.enc_row0 + 4 * (int64_t)j);
         if (lane == 32 || lane == 33) off = (uint32_t)(d.stats0 + 8 * (int64_t)kt + 4 * (lane - 32));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.wrs, (lds_void*)(uintptr_t)(s.tsk[stage]), 4, off, 0, 0, 0);
+        dma4(d.wrs, uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4)), off);
+    }
+}
+
+// B operand fragments of O += A V for 16-key chunk c of a V tile: for each
+// 32-column block nb, keys c*16 + 8 h2' .. (two transposed reads of 4 keys x
+// 4 columns per 16-lane group).
+__device__ __forceinline__ void read_v_chunk(const uint8_t* v_lds, int c, int lane, u32x4 (&vf)[4]) {
+    const int m = lane & 15;
+    const int dsub = ((lane >> 4) & 1) * 16;
+    const int key0 = c * 16 + 4 * (lane >> 5) + (m >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int col = nb * 32 + dsub + 4 * (m & 3);      // element column
+        const int chunk = col >> 3;
+        const int within = (col & 7) * 2;
+        const u32x2 v0 = ds_read_tr(v_lds + vswz(key0, chunk) + within);
+        const u32x2 v1 = ds_read_tr(v_lds + vswz(key0 + 8, chunk) + within);
+        vf[nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
     }
 }
 
@@ -164,7 +227,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = uni(tid >> 6);
     const int l32 = lane & 31;
     const int h2 = lane >> 5;            // which 8-wide k slice / 4-key group of the lane
     const int total_work = p.ctrl[0] * p.H;
@@ -174,9 +237,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
     const int CS = p.pos_copy;
     const float kNegLog2e = -kLog2e;
     const float alpha_eff = kSilu ? -p.alpha * 0.69314718055994531f : p.alpha;
-    const int per_tile = wave == 0 ? 5 : 4;   // buffer loads per tile of this wave
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void*)ws_base, (short)0, (int)ws_bytes,
-                                                                        0x00020000);
+    const int per_tile = uni(wave == 0 ? 5 : 4);   // buffer loads per tile of this wave
+    const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
     const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
     const int64_t stats_base = (const uint8_t*)p.stats - (const uint8_t*)ws_base;
     int loaded_head = -1;
@@ -190,7 +252,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 s.item[0] = it.b; s.item[1] = it.qt; s.item[2] = it.a_end; s.item[3] = it.kb;
             }
         }
-        __syncthreads();
+        lds_sync();
         const int w = uni(s.work);
         if (w >= total_work) break;
         const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
@@ -198,10 +260,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const int kb_begin = kbw & 0xffff, kb_end = kbw >> 16;
         const int h = w % p.H;
 
-        const int64_t row0 = p.offsets[b];
-        const int L = p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0;
-        const int n = p.ncand ? L - p.ncand[b] : L;
-        const int bbase = p.bscan[b];
+        // wave-uniform by construction; readfirstlane lets the compiler keep
+        // them (and the buffer descriptors built from them) in SGPRs
+        const int64_t row0 = uni(p.offsets[b]);
+        const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
+        const int n = uni(p.ncand ? L - p.ncand[b] : L);
+        const int bbase = uni(p.bscan[b]);
 
         // ---- bias tables (reloaded only when they differ by head)
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
@@ -217,47 +281,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             if (tid < 32) s.tt_fast[tid] = rt[min(p.NT - 1, 31 - tid)];
             if (tid < 65) s.tt_wide[tid] = rt[min(p.NT - 1, tid)];
             loaded_head = h;
+            lds_wait();   // visible to all after the first tile's barrier
         }
 
-        // ---- this wave's 32 query rows (all its global reads precede the tile loads)
-        const int wrow0 = qt * BM + wave * 32;
-        const int i = wrow0 + l32;               // this lane's query row
-        const bool row_valid = i < L;
-        bf16x8 qf[8];
-        {
-            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (row_valid) z = *reinterpret_cast<const u32x4*>(qp + kc * 16);
-                qf[kc] = __builtin_bit_cast(bf16x8, z);
-            }
-        }
-        const int64_t t_first = p.ts[row0];
-        const int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
-        const uint32_t tie = row_valid ? p.enc[row0 + i] : 0x80000000u;
-        const int qblk = bbase + qt * (BM / 32) + wave;   // this wave's 32-row block
-        const bool wave_rows = wrow0 < L;
-        uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
-        uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
-        rmin = uniu(rmin);
-        rmax = uniu(rmax);
-        const bool rows_wide = rmin > rmax;
-        const int prow = min(i, n);
-        const int prow_min = uni(min(wrow0, n));
-
-        f32x16 oacc[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
-
+        // ---- tile loads: the first kStages - 1 tiles go out before this
+        //      item's other global reads, so that all of them share one latency
         TileDma dma;
         {
             const uint16_t* kb0 = p.k + row0 * p.ks + h * HD;
             const uint16_t* vb0 = p.v + row0 * p.vs + h * HD;
-            dma.krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb0, (short)0, (int)(L * p.ks * 2), 0x00020000);
-            dma.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb0, (short)0, (int)(L * p.vs * 2), 0x00020000);
+            dma.krs = make_rsrc(kb0, (uint32_t)(L * p.ks * 2));
+            dma.vrs = make_rsrc(vb0, (uint32_t)(L * p.vs * 2));
             dma.wrs = wrs;
             const int pc = lane & 15;
 #pragma unroll
@@ -277,6 +311,46 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         for (int pre = 0; pre < kStages - 1; ++pre)
             if (pre < ntiles) issue_tile(dma, s, pre, tile_of(pre), L, wave, lane);
 
+        // ---- this wave's 32 query rows
+        const int wrow0 = qt * BM + wave * 32;
+        const int i = wrow0 + l32;               // this lane's query row
+        const bool row_valid = i < L;
+        bf16x8 qf[8];
+        {
+            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                if (row_valid) z = *reinterpret_cast<const u32x4*>(qp + kc * 16);
+                qf[kc] = __builtin_bit_cast(bf16x8, z);
+            }
+        }
+        const int64_t t_first = p.ts[row0];
+        const int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
+        uint32_t tie = row_valid ? p.enc[row0 + i] : 0x80000000u;
+        const int qblk = bbase + qt * (BM / 32) + wave;   // this wave's 32-row block
+        const bool wave_rows = wrow0 < L;
+        uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
+        uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
+        rmin = uniu(rmin);
+        rmax = uniu(rmax);
+        const bool rows_wide = rmin > rmax;
+        const int prow = min(i, n);
+        // time table by leading-zero count, one entry per lane (lanes 32-63
+        // repeat 0-31), read with readlane for block-uniform buckets
+        int ttv = __builtin_bit_cast(int, p.rab_time[(int64_t)h * p.rt_hs + min(p.NT - 1, 31 - l32)]);
+        // These item-level loads complete here: a value still in flight at
+        // the loop entry would make the compiler wait for every load (the
+        // tile loads included) at its first use in each iteration.
+        asm volatile("" : "+v"(ttv), "+v"(tie), "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
+                     "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]));
+
+        f32x16 oacc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
+
         for (int it = 0; it < ntiles; ++it) {
             const int kt = tile_of(it);
             const int j0 = kt * BN;
@@ -284,32 +358,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             // this tile's loads have landed once at most the later tiles' are outstanding
             const int later = min(kStages - 2, ntiles - 1 - it);
             wait_vmcnt(later * per_tile);
-            __syncthreads();   // everyone's loads for this tile are visible; tile it-1 is done
+            lds_barrier();   // everyone's loads for this tile are visible; tile it-1 is done
             if (it + kStages - 1 < ntiles)
                 issue_tile(dma, s, (it + kStages - 1) & (kStages - 1), tile_of(it + kStages - 1), L, wave, lane);
             const uint8_t* k_lds = s.k[stage];
             const uint8_t* v_lds = s.v[stage];
             const uint32_t* tsk = s.tsk[stage];
 
-            // ---------- block-uniform facts (scalar)
-            const uint32_t kmn = uniu(tsk[32]), kmx = uniu(tsk[33]);
-            const bool wide = rows_wide || kmn > kmx;
-            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
-            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
-            const uint32_t czlo = clz_gap(lo), czhi = clz_gap(hi);
-            const bool time_uniform = !wide && czlo == czhi;
-            const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
-            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
-
-            // ---------- initial accumulator: the relative bias
-            f32x16 acc;
-            float cadd = 0.0f;
-            if (time_uniform) cadd = s.tt_fast[czlo];
-            if (pos_clamped) {
-                cadd += ptab[0];      // entry u = 0 is difference Dhi >= P-1: rab_pos[P-1]
+            // ---------- every LDS read of the tile, issued up front in the order
+            //            of use (LDS returns in order): key block range, key
+            //            codes, position entries, K, V
+            const u32x2 krange = *reinterpret_cast<const u32x2*>(&tsk[32]);
+            u32x4 codes[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            } else {
+            for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
+            // position bias as the initial accumulator: lane (row i, keys
+            // j0 + 8q + 4h2 + t) reads reversed-table entries u0 + 8q + t; a
+            // clamped x gives rab_pos[P-1] throughout, which is exact there
+            f32x16 acc;
+            {
                 int x = prow - (j0 + 4 * h2);
                 x = min(max(x, 0), P + 26);
                 const int u0 = Dhi - x;
@@ -325,35 +392,72 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     }
                 }
             }
-            if (!time_uniform) {
-                if (!wide) {
+            bf16x8 kf[8];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const u32x4 tj = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, tj[t], 1u))];
-                    }
+            for (int kc = 0; kc < 8; ++kc) kf[kc] = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
+            // V^T fragments of the tile's first 16-key chunk (the second
+            // chunk's are read while the QK^T products run)
+            u32x4 vf[2][4];
+            read_v_chunk(v_lds, 0, lane, vf[0]);
+
+            // ---------- block-uniform facts (scalar)
+            const uint32_t kmn = uniu(krange[0]), kmx = uniu(krange[1]);
+            const bool wide = rows_wide || kmn > kmx;
+            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
+            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
+            const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
+            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
+
+            // ---------- time bias: constant over the block (most blocks), one
+            //            of two buckets split at a power of two, or per element
+            float cadd = 0.0f;
+            if (!wide && czlo - czhi <= 1) {
+                const float tlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czlo));
+                if (czlo == czhi) {
+                    cadd = tlo;
                 } else {
-                    const int64_t* tsb = p.ts + row0;
+                    // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
+                    const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
+                    const uint32_t thr = 1u << (32 - czlo);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const int j = j0 + 8 * q + 4 * h2 + t;
-                            const int64_t tj = j < L ? tsb[j] : t_first;
-                            const int64_t dt = ti64 - tj;
-                            const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                            acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
-                        }
+                        for (int t = 0; t < 4; ++t) acc[4 * q + t] += sad_u32(tie, codes[q][t], 1u) >= thr ? thi : tlo;
+                }
+            } else if (!wide) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, codes[q][t], 1u))];
+            } else {
+                const int64_t* tsb = p.ts + row0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int j = j0 + 8 * q + 4 * h2 + t;
+                        const int64_t tj = j < L ? tsb[j] : t_first;
+                        const int64_t dt = ti64 - tj;
+                        const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
+                        acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
                     }
                 }
             }
 
-            // ---------- S^T = K Q^T (+ bias)
+            // ---------- S^T = K Q^T (+ bias), as two interleaved accumulation
+            //            chains (a lone dependent chain issues at ~2/3 rate)
+            {
+                f32x16 acc2;
 #pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
-                acc = mfma32(kf, qf[kc], acc);
+                for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
+#pragma unroll
+                for (int kc = 0; kc < 8; kc += 2) {
+                    acc = mfma32(kf[kc], qf[kc], acc);
+                    acc2 = mfma32(kf[kc + 1], qf[kc + 1], acc2);
+                }
+                read_v_chunk(v_lds, 1, lane, vf[1]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
             }
 
             // ---------- activation, mask, bf16 packing
@@ -383,9 +487,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             }
 
             // ---------- O += A V for the tile's two 16-key chunks
-            //            (V^T fragments by transposed LDS reads)
-            const int m = lane & 15;
-            const int dsub = ((lane >> 4) & 1) * 16;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 u32x4 pk;
@@ -394,17 +495,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 pk[2] = pack_bf16x2(a[8 * c + 4], a[8 * c + 5]);
                 pk[3] = pack_bf16x2(a[8 * c + 6], a[8 * c + 7]);
                 const bf16x8 pa = __builtin_bit_cast(bf16x8, pk);
-                const int key0 = c * 16 + 4 * h2 + (m >> 2);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const int col = nb * 32 + dsub + 4 * (m & 3);      // element column
-                    const int chunk = col >> 3;
-                    const int within = (col & 7) * 2;
-                    const u32x2 v0 = ds_read_tr(v_lds + vswz(key0, chunk) + within);
-                    const u32x2 v1 = ds_read_tr(v_lds + vswz(key0 + 8, chunk) + within);
-                    const u32x4 vv = {v0[0], v0[1], v1[0], v1[1]};
-                    oacc[nb] = mfma32(pa, __builtin_bit_cast(bf16x8, vv), oacc[nb]);
-                }
+                for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma32(pa, __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
             }
         }
 
@@ -419,7 +511,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
             }
         }
-        __syncthreads();   // this item's LDS use is over before the next item starts
+        lds_barrier();   // this item's LDS use is over before the next item starts
     }
 }
 
