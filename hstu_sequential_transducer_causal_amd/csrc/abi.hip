@@ -151,6 +151,8 @@ Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
 hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
     hstu::SchedArgs sa;
     sa.B = a->B;
+    sa.max_seq_len = a->max_seq_len;
+    sa.cap = (int64_t)s.layout.cap;
     sa.offsets = a->seq_offsets;
     sa.lengths = a->seq_lengths;
     sa.ncand = a->num_candidates;
@@ -197,15 +199,10 @@ hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream)
     c.stats = s.stats;
     c.enc = s.enc;
     c.num_rows = a->num_rows;
-    hipError_t e;
-    if (a->ev_core_begin) {
-        e = hipEventRecord(static_cast<hipEvent_t>(a->ev_core_begin), stream);
-        if (e != hipSuccess) return e;
-    }
-    e = a->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(c, stream) : hstu::launch_attn_f32(c, stream);
-    if (e != hipSuccess) return e;
-    if (a->ev_core_end) e = hipEventRecord(static_cast<hipEvent_t>(a->ev_core_end), stream);
-    return e;
+    // the events travel with the launch itself (no marker packets around it)
+    c.ev_begin = static_cast<hipEvent_t>(a->ev_core_begin);
+    c.ev_end = static_cast<hipEvent_t>(a->ev_core_end);
+    return a->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(c, stream) : hstu::launch_attn_f32(c, stream);
 }
 
 hipError_t run_ln_gate(const hstu_attn_args* a, const float* w, float* scores, int score_stride,

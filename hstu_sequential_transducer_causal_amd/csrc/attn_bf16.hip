@@ -40,6 +40,8 @@
 //     (never multiply) so that padding and masked garbage cannot leak.
 //   * Persistent grid: workgroups pull items (longest first) from the
 //     scheduler's list through an atomic cursor until it is exhausted.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "hstu_device.h"
 
@@ -169,33 +171,41 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // Per-item state of the tile loads.  Wave w fills key rows 8w .. 8w+7 of the
 // K and V tiles with 2 buffer loads each: lane l of load m writes 16 bytes at
 // row 8w + 4m + l/16, physical chunk l % 16, so it fetches the logical chunk
-// that the swizzle puts there.  Wave 0 also loads the 32 key codes and the key
-// block's range (lanes 32, 33) with one 4-byte-per-lane load.
+// that the swizzle puts there.  Wave 0 also loads the 32 key codes with one
+// 4-byte-per-lane load.
 struct TileDma {
     u32x4 krs, vrs, wrs;
     uint32_t koff[2], voff[2];
     uint32_t ktile, vtile;        // bytes per key tile in K and V
     int64_t enc_row0;             // byte offset of the sequence's first code in the workspace
-    int64_t stats0;               // byte offset of the sequence's first block range
 };
 
+// The three parts of a tile's loads go out at different points of the
+// previous tiles' work, so that no wave stalls long on a full load queue.
+__device__ __forceinline__ void issue_k(const TileDma& d, Smem& s, int stage, int kt, int wave) {
+    const uint32_t kl = lds_addr(s.k[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+    const uint32_t ksoff = uniu((uint32_t)kt * d.ktile);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) dma16(d.krs, uniu(kl + m * 1024), d.koff[m], ksoff);
+}
+__device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, int kt, int wave) {
+    const uint32_t vl = lds_addr(s.v[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+    const uint32_t vsoff = uniu((uint32_t)kt * d.vtile);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
+}
+// Wave 0 only: the tile's 32 key codes (lanes 32-63 write zeros).
+__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt, int L, int lane) {
+    const int j = kt * BN + lane;
+    uint32_t off = 0x80000000u;   // out of range: lands as 0
+    if (lane < 32 && j < L) off = (uint32_t)(d.enc_row0 + 4 * (int64_t)j);
+    dma4(d.wrs, uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4)), off);
+}
 __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, int L, int wave,
                                            int lane) {
-    const uint32_t kl = lds_addr(s.k[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
-    const uint32_t vl = lds_addr(s.v[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
-    const uint32_t ksoff = uniu((uint32_t)kt * d.ktile), vsoff = uniu((uint32_t)kt * d.vtile);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        dma16(d.krs, uniu(kl + m * 1024), d.koff[m], ksoff);
-        dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
-    }
-    if (wave == 0) {
-        const int j = kt * BN + lane;
-        uint32_t off = 0x80000000u;   // out of range: lands as 0
-        if (lane < 32 && j < L) off = (uint32_t)(d.enc_row0 + 4 * (int64_t)j);
-        if (lane == 32 || lane == 33) off = (uint32_t)(d.stats0 + 8 * (int64_t)kt + 4 * (lane - 32));
-        dma4(d.wrs, uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4)), off);
-    }
+    issue_k(d, s, stage, kt, wave);
+    issue_v(d, s, stage, kt, wave);
+    if (wave == 0) issue_codes(d, s, stage, kt, L, lane);
 }
 
 // B operand fragments of O += A V for 16-key chunk c of a V tile: for each
@@ -240,7 +250,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
     const int per_tile = uni(wave == 0 ? 5 : 4);   // buffer loads per tile of this wave
     const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
     const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
-    const int64_t stats_base = (const uint8_t*)p.stats - (const uint8_t*)ws_base;
+    // key block ranges through the scalar cache (uniform addresses)
+    const __attribute__((address_space(4))) u32x2* kstats =
+        (const __attribute__((address_space(4))) u32x2*)(uintptr_t)p.stats;
     int loaded_head = -1;
 
     for (;;) {
@@ -303,7 +315,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             dma.ktile = (uint32_t)(BN * p.ks * 2);
             dma.vtile = (uint32_t)(BN * p.vs * 2);
             dma.enc_row0 = enc_base + 4 * row0;
-            dma.stats0 = stats_base + 8 * (int64_t)bbase;
         }
         const int ntiles = a_end + (kb_end - kb_begin);
         auto tile_of = [&](int it) { return it < a_end ? it : kb_begin + (it - a_end); };
@@ -336,13 +347,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         rmax = uniu(rmax);
         const bool rows_wide = rmin > rmax;
         const int prow = min(i, n);
+        const int prow_min = uni(min(wrow0, n));
         // time table by leading-zero count, one entry per lane (lanes 32-63
         // repeat 0-31), read with readlane for block-uniform buckets
         int ttv = __builtin_bit_cast(int, p.rab_time[(int64_t)h * p.rt_hs + min(p.NT - 1, 31 - l32)]);
+        float pos_far = p.rab_pos[(int64_t)h * p.rp_hs + P - 1];   // every clamped difference
         // These item-level loads complete here: a value still in flight at
         // the loop entry would make the compiler wait for every load (the
         // tile loads included) at its first use in each iteration.
-        asm volatile("" : "+v"(ttv), "+v"(tie), "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
+        asm volatile("" : "+v"(pos_far), "+v"(ttv), "+v"(tie), "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
                      "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]));
 
         f32x16 oacc[4];
@@ -351,32 +364,52 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
 
+        u32x2 krange_next = kstats[bbase + tile_of(0)];
         for (int it = 0; it < ntiles; ++it) {
             const int kt = tile_of(it);
             const int j0 = kt * BN;
             const int stage = it & (kStages - 1);
+            const bool issue = it + kStages - 1 < ntiles;
+            const int st3 = (it + kStages - 1) & (kStages - 1), kt3 = issue ? tile_of(it + kStages - 1) : 0;
             // this tile's loads have landed once at most the later tiles' are outstanding
             const int later = min(kStages - 2, ntiles - 1 - it);
             wait_vmcnt(later * per_tile);
             lds_barrier();   // everyone's loads for this tile are visible; tile it-1 is done
-            if (it + kStages - 1 < ntiles)
-                issue_tile(dma, s, (it + kStages - 1) & (kStages - 1), tile_of(it + kStages - 1), L, wave, lane);
+            if (issue) issue_k(dma, s, st3, kt3, wave);
             const uint8_t* k_lds = s.k[stage];
             const uint8_t* v_lds = s.v[stage];
             const uint32_t* tsk = s.tsk[stage];
 
-            // ---------- every LDS read of the tile, issued up front in the order
-            //            of use (LDS returns in order): key block range, key
-            //            codes, position entries, K, V
-            const u32x2 krange = *reinterpret_cast<const u32x2*>(&tsk[32]);
+            // ---------- block-uniform facts (scalar; the key block's code
+            //            range was loaded one tile ahead)
+            const uint32_t kmn = uniu(krange_next[0]), kmx = uniu(krange_next[1]);
+            if (it + 1 < ntiles) krange_next = kstats[bbase + tile_of(it + 1)];
+            const bool wide = rows_wide || kmn > kmx;
+            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
+            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
+            const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
+            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
+            const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
+            const bool need_codes = !wide && czlo != czhi;
+
+            // ---------- this tile's LDS reads, issued up front in the order of
+            //            use (LDS returns in order): key codes and position
+            //            entries when needed, K, V
             u32x4 codes[4];
+            if (need_codes) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
+                for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
+            }
             // position bias as the initial accumulator: lane (row i, keys
             // j0 + 8q + 4h2 + t) reads reversed-table entries u0 + 8q + t; a
-            // clamped x gives rab_pos[P-1] throughout, which is exact there
+            // block whose differences all clamp takes rab_pos[P-1] as a constant
             f32x16 acc;
-            {
+            float cadd = 0.0f;
+            if (pos_clamped) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+                cadd = pos_far;
+            } else {
                 int x = prow - (j0 + 4 * h2);
                 x = min(max(x, 0), P + 26);
                 const int u0 = Dhi - x;
@@ -400,21 +433,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             u32x4 vf[2][4];
             read_v_chunk(v_lds, 0, lane, vf[0]);
 
-            // ---------- block-uniform facts (scalar)
-            const uint32_t kmn = uniu(krange[0]), kmx = uniu(krange[1]);
-            const bool wide = rows_wide || kmn > kmx;
-            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
-            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
-            const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
-            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
-
             // ---------- time bias: constant over the block (most blocks), one
             //            of two buckets split at a power of two, or per element
-            float cadd = 0.0f;
             if (!wide && czlo - czhi <= 1) {
                 const float tlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czlo));
                 if (czlo == czhi) {
-                    cadd = tlo;
+                    cadd += tlo;
                 } else {
                     // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
                     const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
@@ -456,6 +480,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     acc2 = mfma32(kf[kc + 1], qf[kc + 1], acc2);
                 }
                 read_v_chunk(v_lds, 1, lane, vf[1]);
+                if (issue) issue_v(dma, s, st3, kt3, wave);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
             }
@@ -485,6 +510,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     }
                 }
             }
+
+            if (issue && wave == 0) issue_codes(dma, s, st3, kt3, L, lane);
 
             // ---------- O += A V for the tile's two 16-key chunks
 #pragma unroll
@@ -545,9 +572,11 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
     const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
     if (a.act == 0)
-        hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), smem, stream, p, ws_base, wsb);
+        hipExtLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), smem, stream,
+                              a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
     else
-        hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), smem, stream, p, ws_base, wsb);
+        hipExtLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), smem, stream,
+                              a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
     return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 // One wave per work item (64 query rows of one head); each lane owns one
 // query row with Q and the accumulator in registers; key tiles of 64 rows are
 // staged in LDS and read as broadcasts.  fp32 throughout, accurate expf.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "hstu_device.h"
 
@@ -129,9 +131,11 @@ hipError_t launch_attn_f32(const AttnCoreArgs& a, hipStream_t stream) {
     p.items = a.items; p.ctrl = a.ctrl; p.cursor = a.cursor;
     const int grid = device_cu_count() * 4;
     if (a.d == 32) {
-        hipLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(64), 0, stream, p);
+        hipExtLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(64), 0, stream,
+                              a.ev_begin, a.ev_end, 0, p);
     } else {
-        hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(64), 0, stream, p);
+        hipExtLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(64), 0, stream,
+                              a.ev_begin, a.ev_end, 0, p);
     }
     return hipGetLastError();
 }

@@ -71,22 +71,36 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (a.B <= 0 || row >= a.num_rows) return;
     if (row < a.offsets[0] || row >= a.offsets[a.B]) return;
-    const int b = seq_of_row(a.offsets, a.B, row);
-    const int r = (int)(row - a.offsets[b]);
-    const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
-    if (r >= L) return;  // padding row: never read or written
-    const int n = a.ncand ? L - a.ncand[b] : L;
-    const bool want_score = a.w != nullptr && r >= n;
+    // A packed causal batch needs no sequence lookup: every row in range is a
+    // valid history row.
+    int b = 0, r = 0, n = 0;
+    bool want_score = false;
+    if (a.lengths || a.ncand) {
+        b = seq_of_row(a.offsets, a.B, row);
+        r = (int)(row - a.offsets[b]);
+        const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
+        if (r >= L) return;  // padding row: never read or written
+        n = a.ncand ? L - a.ncand[b] : L;
+        want_score = a.w != nullptr && r >= n;
+    }
     if (a.y == nullptr && !want_score) return;
 
     const int W = a.width;
-    float x[NCH][8];
-    float sum = 0.0f;
+    // both operand rows are fetched before any arithmetic
+    float x[NCH][8], u[NCH][8];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int col = (c * 64 + lane) * 8;
         if (col < W) {
             Vec8<BF16>::load(a.o, row * a.o_stride + col, x[c]);
+            Vec8<BF16>::load(a.u, row * a.u_stride + col, u[c]);
+        }
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sum += x[c][e];
         }
@@ -111,11 +125,9 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
     for (int c = 0; c < NCH; ++c) {
         const int col = (c * 64 + lane) * 8;
         if (col < W) {
-            float u[8];
-            Vec8<BF16>::load(a.u, row * a.u_stride + col, u);
             float y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * rstd * u[e];
+            for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * rstd * u[c][e];
             if (a.y) Vec8<BF16>::store(a.y, row * a.y_stride + col, y);
             if (want_score) {
 #pragma unroll

@@ -44,6 +44,8 @@ SchedLayout sched_layout(int B, int max_seq_len, int tile_m, int64_t num_rows, s
 
 struct SchedArgs {
     int B;
+    int max_seq_len;   // bound on every sequence length (sizes the cost histogram)
+    int64_t cap;       // item capacity of `items`
     const int32_t* offsets;
     const int32_t* lengths;
     const int32_t* ncand;
@@ -101,6 +103,7 @@ struct AttnCoreArgs {
     const uint32_t* stats;
     const uint32_t* enc;
     int64_t num_rows;
+    hipEvent_t ev_begin, ev_end;   // optional: stamped at the kernel's own start and end
 };
 
 hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream);

@@ -32,6 +32,10 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBins = kMaxSeqLen / 32 + 2;  // cost <= number of key tiles of a sequence
+// Batches of up to this many sequences keep their per-sequence data in LDS
+// (the binary searches below then never wait on memory); larger ones use the
+// workspace copies.
+constexpr int kLdsSeq = 4096;
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -88,7 +92,8 @@ __device__ __forceinline__ int seq_history(const SchedArgs& a, int b, int L) {
 }
 
 // Sequence of flat query tile f: the last b with qscan[b] <= f.
-__device__ __forceinline__ int find_seq(const int32_t* qscan, int B, int f) {
+template <typename Ptr>
+__device__ __forceinline__ int find_seq(Ptr qscan, int B, int f) {
     int lo = 0, hi = B;  // qscan[lo] <= f < qscan[hi]
     while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
@@ -100,18 +105,25 @@ __device__ __forceinline__ int find_seq(const int32_t* qscan, int B, int f) {
 __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
     __shared__ int hist[kMaxBins];
     __shared__ int wave_tot[kWaves];
-    __shared__ int carry_s;
+    __shared__ int carry_s, bcarry_s;
+    __shared__ int qscan_s[kLdsSeq + 1];
+    __shared__ int len_s[kLdsSeq];
+    __shared__ int hist_s[kLdsSeq];   // history rows n_b
     const int tid = threadIdx.x;
     const int BM = a.tile_m, BN = a.tile_n;
+    const bool in_lds = a.B <= kLdsSeq;
+    // costs (key tiles of an item) lie in [0, ceil(max_seq_len / BN)]
+    const int nbins = min(kMaxBins, ceil_div(a.max_seq_len, BN) + 2);
 
-    for (int i = tid; i < kMaxBins; i += kThreads) hist[i] = 0;
-    if (tid == 0) carry_s = 0;
+    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
+    if (tid == 0) {
+        carry_s = 0;
+        bcarry_s = 0;
+    }
     __syncthreads();
 
     // 1. query tiles and 32-row timestamp blocks per sequence -> exclusive
     //    prefixes qscan[0..B] and bscan[0..B]
-    __shared__ int bcarry_s;
-    if (tid == 0) bcarry_s = 0;
     for (int base = 0; base < a.B; base += kThreads) {
         int b = base + tid;
         int nq = 0, nblk = 0;
@@ -119,6 +131,10 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
             const int L = seq_length(a, b);
             nq = ceil_div(L, BM);
             nblk = ceil_div(L, kTsBlock);
+            if (in_lds) {
+                len_s[b] = L;
+                hist_s[b] = seq_history(a, b, L);
+            }
         }
         int total, btotal;
         int ex = block_exclusive_scan(nq, wave_tot, total);
@@ -127,6 +143,7 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
         if (b < a.B) {
             a.qscan[b] = carry + ex;
             a.bscan[b] = bcarry + bex;
+            if (in_lds) qscan_s[b] = carry + ex;
         }
         __syncthreads();
         if (tid == 0) {
@@ -139,23 +156,40 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
     if (tid == 0) {
         a.qscan[a.B] = nitems;
         a.bscan[a.B] = bcarry_s;
+        if (in_lds) qscan_s[a.B] = nitems;
     }
     __syncthreads();
 
+    // the item of flat query tile f
+    auto item_of = [&](int f, int& b, int& qt) -> Ranges {
+        int L, n;
+        if (in_lds) {
+            b = find_seq(qscan_s, a.B, f);
+            qt = f - qscan_s[b];
+            L = len_s[b];
+            n = hist_s[b];
+        } else {
+            b = find_seq(a.qscan, a.B, f);
+            qt = f - a.qscan[b];
+            L = seq_length(a, b);
+            n = seq_history(a, b, L);
+        }
+        return tile_ranges(L, n, qt, BM, BN);
+    };
+
     // 2. histogram of item costs (key tiles per item)
     for (int f = tid; f < nitems; f += kThreads) {
-        int b = find_seq(a.qscan, a.B, f);
-        int L = seq_length(a, b);
-        Ranges r = tile_ranges(L, seq_history(a, b, L), f - a.qscan[b], BM, BN);
-        atomicAdd(&hist[r.a_end + (r.kb_end - r.kb_begin)], 1);
+        int b, qt;
+        const Ranges r = item_of(f, b, qt);
+        atomicAdd(&hist[min(r.a_end + (r.kb_end - r.kb_begin), nbins - 1)], 1);
     }
     __syncthreads();
 
     // 3. start position of each cost bin, largest cost first
     if (tid == 0) carry_s = 0;
     __syncthreads();
-    for (int base = 0; base < kMaxBins; base += kThreads) {
-        int bin = kMaxBins - 1 - (base + tid);
+    for (int base = 0; base < nbins; base += kThreads) {
+        int bin = nbins - 1 - (base + tid);
         int c = bin >= 0 ? hist[bin] : 0;
         int total;
         int ex = block_exclusive_scan(c, wave_tot, total);
@@ -168,20 +202,18 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
 
     // 4. scatter the items into their bins
     for (int f = tid; f < nitems; f += kThreads) {
-        int b = find_seq(a.qscan, a.B, f);
-        int L = seq_length(a, b);
-        int qt = f - a.qscan[b];
-        Ranges r = tile_ranges(L, seq_history(a, b, L), qt, BM, BN);
-        int pos = atomicAdd(&hist[r.a_end + (r.kb_end - r.kb_begin)], 1);
+        int b, qt;
+        const Ranges r = item_of(f, b, qt);
+        int pos = atomicAdd(&hist[min(r.a_end + (r.kb_end - r.kb_begin), nbins - 1)], 1);
         WorkItem it;
         it.b = b;
         it.qt = qt;
         it.a_end = r.a_end;
         it.kb = r.kb_begin | (r.kb_end << 16);
-        a.items[pos] = it;
+        if (pos < a.cap) a.items[pos] = it;   // (lengths within max_seq_len always fit)
     }
     if (tid == 0) {
-        a.ctrl[0] = nitems;
+        a.ctrl[0] = (int)min((int64_t)nitems, a.cap);
         a.ctrl[1] = 0;
     }
 }
@@ -190,19 +222,24 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // One wave per two 32-row blocks (lanes 0-31 and 32-63).
 __global__ void __launch_bounds__(256) ts_prep_kernel(TsPrepArgs a) {
+    __shared__ int bscan_s[kLdsSeq + 1];
+    const bool in_lds = a.B <= kLdsSeq;
+    if (in_lds)
+        for (int i = threadIdx.x; i <= a.B; i += 256) bscan_s[i] = a.bscan[i];
+    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int64_t f = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
-    const int nblk = a.bscan[a.B];
+    const int nblk = in_lds ? bscan_s[a.B] : a.bscan[a.B];
     const bool active = f < nblk && f < a.cap_blk;
     uint32_t mn = 0xffffffffu, mx = 0u;
     bool narrow = true;
     int64_t fi = 0;
     if (active) {
         fi = f;
-        const int b = find_seq(a.bscan, a.B, (int)f);
+        const int b = in_lds ? find_seq(bscan_s, a.B, (int)f) : find_seq(a.bscan, a.B, (int)f);
         const int64_t row0 = a.offsets[b];
         const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - (int)row0;
-        const int j = ((int)f - a.bscan[b]) * kTsBlock + (lane & 31);
+        const int j = ((int)f - (in_lds ? bscan_s[b] : a.bscan[b])) * kTsBlock + (lane & 31);
         if (j < L) {
             const int64_t t_first = a.ts[row0];
             const int64_t d = a.ts[row0 + j] - t_first;

@@ -113,8 +113,9 @@ typedef struct hstu_attn_args {
     const void* u; int64_t u_stride;   /* [rows, H*d_v]; required when y != NULL */
     void* y; int64_t y_stride;         /* out, or NULL to skip the epilogue */
     float ln_eps;                      /* > 0, added to the variance */
-    /* optional hipEvent_t recorded on `stream` just before / after the
-       attention-core kernel (for timing that kernel alone); NULL = none */
+    /* optional hipEvent_t stamped with the start / end of the attention-core
+       kernel itself (they travel with its launch on `stream`, adding no
+       packets between kernels); for timing that kernel alone; NULL = none */
     void* ev_core_begin;
     void* ev_core_end;
 } hstu_attn_args;
@@ -130,7 +131,8 @@ const char* hstu_last_error(void);
 
 /* Workspace bytes needed by hstu_attn_fwd for these arguments (0 on invalid
  * arguments; call hstu_attn_fwd to get the reason).  Depends only on B,
- * max_seq_len and dtype. */
+ * max_seq_len, dtype and (for HSTU_BF16, which keeps a 4-byte timestamp
+ * code per row) num_rows. */
 size_t hstu_attn_workspace_bytes(const hstu_attn_args* args);
 
 /* Pointwise aggregated attention over a jagged batch.  Builds the jagged
