@@ -347,6 +347,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         rmax = uniu(rmax);
         const bool rows_wide = rmin > rmax;
         const int prow = min(i, n);
+        // visibility of row i (rows past L see nothing): keys j <= vis_lim,
+        // and j == vis_self for a candidate row
+        const int vis_lim = i >= L ? -1 : (i < n ? i : n - 1);
+        const int vis_self = (i >= n && i < L) ? i : -1;
+        const bool cand_rows = wrow0 + 31 >= n;   // the block holds candidate rows
         const int prow_min = uni(min(wrow0, n));
         // time table by leading-zero count, one entry per lane (lanes 32-63
         // repeat 0-31), read with readlane for block-uniform buckets
@@ -500,14 +505,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int r = 0; r < 16; ++r) a[r] = acc[r] + cadd;
             }
             if (!full) {
+                // key j = j0 + 4h2 + c (c = 8q + t) is visible when
+                // j <= vis_lim (causal history, or all history for a
+                // candidate) or j == vis_self (a candidate's own key)
+                const int jb = j0 + 4 * h2;
+                const int xl = vis_lim - jb, xs = vis_self - jb;
+                if (cand_rows) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int j = j0 + 8 * q + 4 * h2 + t;
-                        const bool vis = (j < L) && (i < n ? (j <= i) : (j < n || j == i));
-                        a[4 * q + t] = vis ? a[4 * q + t] : 0.0f;
-                    }
+                        for (int t = 0; t < 4; ++t)
+                            a[4 * q + t] = ((xl >= 8 * q + t) | (xs == 8 * q + t)) ? a[4 * q + t] : 0.0f;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) a[4 * q + t] = xl >= 8 * q + t ? a[4 * q + t] : 0.0f;
                 }
             }
 
