@@ -58,7 +58,7 @@ def up(a, dtype, dev):
 
 
 class AttnCase:
-    def __init__(self, x, dev, with_scores=False):
+    def __init__(self, x, dev, with_scores=False, candidates_only=False):
         import torch
         from hstu_sequential_transducer_causal_amd import ops
         self.x = x
@@ -73,6 +73,7 @@ class AttnCase:
         self.o = torch.empty_like(self.q)
         self.y = torch.empty_like(self.q)
         self.with_scores = with_scores
+        self.candidates_only = candidates_only
         if with_scores:
             self.cmax = int(x.num_candidates.max())
             self.scores = torch.zeros(x.B, self.cmax, dtype=torch.float32, device=dev)
@@ -88,7 +89,7 @@ class AttnCase:
                               self.rt, self.x.alpha, self.w, max_seq_len=self.max_len,
                               score_stride=self.cmax, ln_eps=self.x.eps, o=self.o, y=None,
                               scores=self.scores, workspace=self.ws, ev_core_begin=ev0,
-                              ev_core_end=ev1)
+                              ev_core_end=ev1, candidates_only=self.candidates_only)
         else:
             ops.hstu_attn_fwd(self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt,
                               self.x.alpha, max_seq_len=self.max_len, num_candidates=self.nc,
@@ -292,6 +293,23 @@ def main():
             log(f"{xo.name}: {rec}")
             del c
             torch.cuda.empty_cache()
+            if w == 4:
+                # scores only: the query tiles holding candidate rows (their
+                # unmasked pairs: b_m (n + 1) per user); same scores
+                c = AttnCase(xo, dev, with_scores=True, candidates_only=True)
+                st, ce = time_case(c, max(3, args.steps // 3), 2)
+                n_hist = Lo - xo.num_candidates
+                fc = float(np.sum(xo.num_candidates * (n_hist + 1))) * 4 * xo.d * xo.H
+                rec = {"ms_per_step": round(st, 4),
+                       "candidates_per_s": round(int(xo.num_candidates.sum()) / (st * 1e-3), 1),
+                       "candidate_pair_tflops": round(fc / (st * 1e-3) / 1e12, 2),
+                       "speedup_vs_full_pass": round(others[xo.name]["ms_per_step"] / st, 2)}
+                if ce:
+                    rec["core_ms"] = round(ce, 4)
+                others[xo.name + "_candidates_only"] = rec
+                log(f"{xo.name} candidates only: {rec}")
+                del c
+                torch.cuda.empty_cache()
         line["other_workloads"] = others
 
     line["cpu_baseline"] = None

@@ -58,6 +58,7 @@ class MfalconArgs(ctypes.Structure):
         ("w", _vp),
         ("scores", _vp),
         ("score_stride", _i32),
+        ("candidates_only", _i32),
     ]
 
 

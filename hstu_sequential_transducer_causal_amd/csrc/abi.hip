@@ -148,8 +148,9 @@ Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
     return s;
 }
 
-hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
+hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream, bool cand_only = false) {
     hstu::SchedArgs sa;
+    sa.cand_only = cand_only ? 1 : 0;
     sa.B = a->B;
     sa.max_seq_len = a->max_seq_len;
     sa.cap = (int64_t)s.layout.cap;
@@ -292,12 +293,14 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
     if (a->B == 0) return ok();
     if (!a->num_candidates) return fail(HSTU_ERR_ARG, "num_candidates is required for M-FALCON");
     if (!m->w || !m->scores) return fail(HSTU_ERR_ARG, "w and scores must be non-NULL");
+    if (m->candidates_only && a->y)
+        return fail(HSTU_ERR_ARG, "candidates_only leaves history rows of O unwritten: attn.y must be NULL");
     const size_t need = sched_layout_for(a, 0).bytes;
     st = check_workspace(ws, ws_bytes, need);
     if (st != HSTU_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     Sched s = carve_sched(a, ws, 0);
-    hipError_t e = run_sched(a, s, stream);
+    hipError_t e = run_sched(a, s, stream, m->candidates_only != 0);
     if (e != hipSuccess) return device_error(e, "scheduler launch");
     e = run_core(a, s, stream);
     if (e != hipSuccess) return device_error(e, "attention launch");

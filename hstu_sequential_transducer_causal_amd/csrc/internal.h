@@ -46,6 +46,7 @@ struct SchedArgs {
     int B;
     int max_seq_len;   // bound on every sequence length (sizes the cost histogram)
     int64_t cap;       // item capacity of `items`
+    int cand_only;     // M-FALCON: only the query tiles that hold candidate rows
     const int32_t* offsets;
     const int32_t* lengths;
     const int32_t* ncand;

@@ -91,6 +91,17 @@ __device__ __forceinline__ int seq_history(const SchedArgs& a, int b, int L) {
     return a.ncand ? L - a.ncand[b] : L;
 }
 
+// First query tile of a sequence in the work list: 0, or with cand_only the
+// tile holding the first candidate row.
+__device__ __forceinline__ int first_tile(const SchedArgs& a, int n, int BM) { return a.cand_only ? n / BM : 0; }
+
+// Query tiles of a sequence in the work list (with cand_only, none for a
+// sequence without candidates).
+__device__ __forceinline__ int tile_count(const SchedArgs& a, int L, int n, int BM) {
+    if (a.cand_only && L <= n) return 0;
+    return ceil_div(L, BM) - first_tile(a, n, BM);
+}
+
 // Sequence of flat query tile f: the last b with qscan[b] <= f.
 template <typename Ptr>
 __device__ __forceinline__ int find_seq(Ptr qscan, int B, int f) {
@@ -129,11 +140,12 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
         int nq = 0, nblk = 0;
         if (b < a.B) {
             const int L = seq_length(a, b);
-            nq = ceil_div(L, BM);
+            const int n = seq_history(a, b, L);
+            nq = tile_count(a, L, n, BM);
             nblk = ceil_div(L, kTsBlock);
             if (in_lds) {
                 len_s[b] = L;
-                hist_s[b] = seq_history(a, b, L);
+                hist_s[b] = n;
             }
         }
         int total, btotal;
@@ -174,6 +186,7 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
             L = seq_length(a, b);
             n = seq_history(a, b, L);
         }
+        qt += first_tile(a, n, BM);
         return tile_ranges(L, n, qt, BM, BN);
     };
 

@@ -126,8 +126,11 @@ def attn_workspace_bytes(args: _lib.AttnArgs) -> int:
 def mfalcon_score(q, k, v, u, seq_offsets, num_candidates, timestamps, rab_pos, rab_time, alpha,
                   w, *, max_seq_len: int, score_stride: int, ln_eps: float = 1e-5, o=None,
                   y=None, scores=None, workspace=None, stream=None, ev_core_begin=None,
-                  ev_core_end=None):
-    """M-FALCON ranking scores [B, score_stride] (fp32) of every candidate."""
+                  ev_core_end=None, candidates_only: bool = False):
+    """M-FALCON ranking scores [B, score_stride] (fp32) of every candidate.
+
+    candidates_only: compute only the query tiles that hold candidate rows
+    (y must be None; history rows of `o` outside those tiles stay unwritten)."""
     lib = _lib.load()
     B = seq_offsets.numel() - 1
     if o is None:
@@ -143,6 +146,7 @@ def mfalcon_score(q, k, v, u, seq_offsets, num_candidates, timestamps, rab_pos, 
     m.w = w.data_ptr()
     m.scores = scores.data_ptr()
     m.score_stride = int(score_stride)
+    m.candidates_only = 1 if candidates_only else 0
     need = lib.hstu_mfalcon_workspace_bytes(ctypes.byref(m))
     if workspace is None:
         workspace = _empty_ws(need, q.device)

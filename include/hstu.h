@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -150,7 +150,12 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* args, void* workspace, size_t wo
  * "2.3 M-FALCON算法"; "生成式推荐（一）：HSTU", section "M-FALCON"; "Meta HSTU",
  * section "M-FALCON переиспользует историю между кандидатами".
  *   scores[b * score_stride + c] = < Y[n_b + c, :], w >,
- * Y = LayerNorm(O) (.) U as in hstu_attn_fwd, for c < num_candidates[b]. */
+ * Y = LayerNorm(O) (.) U as in hstu_attn_fwd, for c < num_candidates[b].
+ * A candidate row's output depends on the history rows' keys and values only,
+ * never on their outputs, so with candidates_only set (and attn.y == NULL)
+ * just the query tiles that hold candidate rows are computed: the O rows of
+ * history outside those tiles are left unwritten, and the scores are
+ * bit-identical to those of the full pass. */
 typedef struct hstu_mfalcon_args {
     uint32_t struct_size;     /* = sizeof(hstu_mfalcon_args) */
     hstu_attn_args attn;      /* num_candidates and u are required; attn.y may be
@@ -158,6 +163,8 @@ typedef struct hstu_mfalcon_args {
     const float* w;           /* [H*d_v] score vector */
     float* scores;            /* out: [B * score_stride] fp32 */
     int32_t score_stride;     /* >= max candidates per sequence */
+    int32_t candidates_only;  /* nonzero: only the query tiles holding candidate
+                                 rows (requires attn.y == NULL) */
 } hstu_mfalcon_args;
 
 size_t hstu_mfalcon_workspace_bytes(const hstu_mfalcon_args* args);

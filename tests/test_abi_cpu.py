@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 1
+    assert lib.hstu_abi_version() == 2
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -156,6 +156,16 @@ def test_mfalcon_and_layer_validation(lib):
     assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
     m.attn.u, m.attn.u_stride = 0x10000, 512
     assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG  # no candidates
+    m.attn.num_candidates = 0x10000
+    m.w = m.scores = 0x10000
+    need = lib.hstu_mfalcon_workspace_bytes(ctypes.byref(m))
+    assert need > 0
+    assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    # candidates only: Y would be incomplete, so it must not be requested
+    m.candidates_only = 1
+    m.attn.y, m.attn.y_stride = 0x10000, 512
+    assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    assert b"candidates_only" in lib.hstu_last_error()
     m.struct_size = 4
     assert lib.mfalcon_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
 

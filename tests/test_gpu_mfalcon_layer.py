@@ -30,6 +30,38 @@ def _scores_gpu(x):
     return host_f32(scores), host_f32(o), host_f32(y)
 
 
+def _scores_candidates_only(x):
+    import torch
+    from hstu_sequential_transducer_causal_amd import ops
+    d = DeviceAttn(x)
+    cmax = int(x.num_candidates.max())
+    scores, _, _ = ops.mfalcon_score(d.q, d.k, d.v, d.u, d.offsets, d.ncand, d.ts, d.rab_pos,
+                                     d.rab_time, x.alpha, d.w, max_seq_len=d.max_seq_len,
+                                     score_stride=cmax, ln_eps=x.eps, candidates_only=True)
+    torch.cuda.synchronize()
+    return host_f32(scores)
+
+
+@pytest.mark.parametrize("case", ["ragged", "cfg4"])
+def test_mfalcon_candidates_only_equals_full_pass(case):
+    """Computing only the query tiles that hold candidate rows gives the very
+    same scores as the full pass (candidates read history K/V, never history
+    outputs), including users whose candidates start mid-tile or who have
+    none."""
+    if case == "ragged":
+        x = synth.make_attn(52, [100, 300, 129, 256, 40], H=4, d=128, P=1024, NT=32,
+                            alpha=1 / 512, dtype="bf16", num_candidates=[1, 200, 65, 0, 40],
+                            with_w=True)
+    else:
+        x = synth.config(4)
+    full, _, _ = _scores_gpu(x)
+    part = _scores_candidates_only(x)
+    for b in range(x.B):
+        c = int(x.num_candidates[b])
+        assert np.array_equal(part[b, :c], full[b, :c]), b
+    log(f"candidates-only scores identical to the full pass ({case}, B={x.B})")
+
+
 def test_mfalcon_scores_small():
     x = synth.config(4, batch=3, max_len=256)
     log(f"cfg4 reduced: B={x.B} T={x.T}")
