@@ -1,5 +1,6 @@
 // abi.hip -- the C ABI of libhstu.so (declared in include/hstu.h): argument
 // validation, workspace carving and kernel dispatch on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -123,16 +124,19 @@ struct Sched {
     hstu::SchedLayout layout;
     int32_t* ctrl;
     int32_t* qscan;
-    int32_t* bscan;
     hstu::WorkItem* items;
+    hstu::SplitBlock* split;
+    float* partial;
     uint32_t* stats;
     uint32_t* enc;
+    int32_t* rowmap;   // NULL unless row blocks may be split
 };
 
-// The fp32 core needs neither row codes nor block ranges.
+// The fp32 core needs neither row codes nor block ranges, and never splits.
 hstu::SchedLayout sched_layout_for(const hstu_attn_args* a, size_t base) {
     const bool bf16 = a->dtype == HSTU_BF16;
-    return hstu::sched_layout(a->B, a->max_seq_len, tile_m_for(a->dtype), bf16 ? a->num_rows : 0, base);
+    return hstu::sched_layout(a->B, a->H, a->max_seq_len, tile_m_for(a->dtype), bf16 ? a->d_v : 0,
+                              bf16 ? a->num_rows : 0, base);
 }
 
 Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
@@ -141,10 +145,12 @@ Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
     uint8_t* w = static_cast<uint8_t*>(ws);
     s.ctrl = reinterpret_cast<int32_t*>(w + s.layout.off_ctrl);
     s.qscan = reinterpret_cast<int32_t*>(w + s.layout.off_qscan);
-    s.bscan = reinterpret_cast<int32_t*>(w + s.layout.off_bscan);
     s.items = reinterpret_cast<hstu::WorkItem*>(w + s.layout.off_items);
+    s.split = reinterpret_cast<hstu::SplitBlock*>(w + s.layout.off_split);
+    s.partial = reinterpret_cast<float*>(w + s.layout.off_part);
     s.stats = reinterpret_cast<uint32_t*>(w + s.layout.off_stats);
     s.enc = reinterpret_cast<uint32_t*>(w + s.layout.off_enc);
+    s.rowmap = s.layout.part_slots > 0 ? reinterpret_cast<int32_t*>(w + s.layout.off_rowmap) : nullptr;
     return s;
 }
 
@@ -154,6 +160,11 @@ hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream
     sa.B = a->B;
     sa.max_seq_len = a->max_seq_len;
     sa.cap = (int64_t)s.layout.cap;
+    sa.cap_pieces = (int64_t)s.layout.cap_pieces;
+    sa.H = a->H;
+    sa.slots = a->dtype == HSTU_BF16 ? hstu::attn_bf16_slots() : 0;
+    sa.part_slots = s.layout.part_slots;
+    sa.split = s.split;
     sa.offsets = a->seq_offsets;
     sa.lengths = a->seq_lengths;
     sa.ncand = a->num_candidates;
@@ -161,20 +172,14 @@ hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream
     sa.tile_n = tile_n_for(a->dtype);
     sa.ctrl = s.ctrl;
     sa.qscan = s.qscan;
-    sa.bscan = s.bscan;
     sa.items = s.items;
-    hipError_t e = hstu::launch_sched(sa, stream);
-    if (e != hipSuccess || a->dtype != HSTU_BF16) return e;
-    hstu::TsPrepArgs tp;
-    tp.B = a->B;
-    tp.offsets = a->seq_offsets;
-    tp.lengths = a->seq_lengths;
-    tp.ts = a->timestamps;
-    tp.bscan = s.bscan;
-    tp.enc = s.enc;
-    tp.stats = s.stats;
-    tp.cap_blk = (int64_t)s.layout.cap_blk;
-    return hstu::launch_ts_prep(tp, stream);
+    const bool bf16 = a->dtype == HSTU_BF16;
+    sa.ts = a->timestamps;
+    sa.enc = bf16 ? s.enc : nullptr;
+    sa.stats = s.stats;
+    sa.nblk = s.layout.nblk;
+    sa.cap_blk = bf16 ? (int64_t)s.layout.cap_blk : 0;
+    return hstu::launch_sched(sa, stream);
 }
 
 hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
@@ -196,7 +201,9 @@ hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream)
     c.items = s.items;
     c.ctrl = s.ctrl;
     c.cursor = s.ctrl + 1;
-    c.bscan = s.bscan;
+    c.partial = s.partial;
+    c.rowmap = s.rowmap;
+    c.nblk = s.layout.nblk;
     c.stats = s.stats;
     c.enc = s.enc;
     c.num_rows = a->num_rows;
@@ -206,8 +213,26 @@ hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream)
     return a->dtype == HSTU_BF16 ? hstu::launch_attn_bf16(c, stream) : hstu::launch_attn_f32(c, stream);
 }
 
-hipError_t run_ln_gate(const hstu_attn_args* a, const float* w, float* scores, int score_stride,
-                       hipStream_t stream) {
+// Adds up the partial sums of split row blocks into O (bf16 core only).
+hipError_t run_combine(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
+    if (a->dtype != HSTU_BF16 || s.layout.part_slots <= 0 || a->H <= 0) return hipSuccess;
+    hstu::CombineArgs c;
+    c.H = a->H;
+    c.d = a->d_v;
+    c.BM = hstu::kBf16TileM;
+    c.offsets = a->seq_offsets;
+    c.lengths = a->seq_lengths;
+    c.ctrl = s.ctrl;
+    c.split = s.split;
+    c.partial = s.partial;
+    c.o = a->o; c.o_stride = a->o_stride;
+    // a split block takes at least two slots per head
+    c.max_blocks = std::min<int64_t>((int64_t)s.layout.cap, s.layout.part_slots / (2 * a->H));
+    return hstu::launch_combine(c, stream);
+}
+
+hipError_t run_ln_gate(const hstu_attn_args* a, const Sched& s, const float* w, float* scores,
+                       int score_stride, bool cand_only, hipStream_t stream) {
     hstu::LnGateArgs l;
     l.B = a->B;
     l.num_rows = a->num_rows;
@@ -223,6 +248,13 @@ hipError_t run_ln_gate(const hstu_attn_args* a, const float* w, float* scores, i
     l.w = w;
     l.scores = scores;
     l.score_stride = score_stride;
+    // split row blocks are added up here (no separate combine pass)
+    l.rowmap = s.rowmap;
+    l.partial = s.partial;
+    l.H = a->H;
+    l.d = a->d_v;
+    l.BM = hstu::kBf16TileM;
+    l.cand_only = cand_only ? 1 : 0;
     return hstu::launch_ln_gate(l, stream);
 }
 
@@ -270,8 +302,11 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, void* ws, size_t ws_bytes, vo
     e = run_core(a, s, stream);
     if (e != hipSuccess) return device_error(e, "attention launch");
     if (a->y) {
-        e = run_ln_gate(a, nullptr, nullptr, 0, stream);
+        e = run_ln_gate(a, s, nullptr, nullptr, 0, false, stream);
         if (e != hipSuccess) return device_error(e, "epilogue launch");
+    } else {
+        e = run_combine(a, s, stream);
+        if (e != hipSuccess) return device_error(e, "split combine launch");
     }
     return ok();
 }
@@ -304,7 +339,7 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
     if (e != hipSuccess) return device_error(e, "scheduler launch");
     e = run_core(a, s, stream);
     if (e != hipSuccess) return device_error(e, "attention launch");
-    e = run_ln_gate(a, m->w, m->scores, m->score_stride, stream);
+    e = run_ln_gate(a, s, m->w, m->scores, m->score_stride, m->candidates_only != 0, stream);
     if (e != hipSuccess) return device_error(e, "epilogue launch");
     return ok();
 }
@@ -352,7 +387,7 @@ LayerWs layer_ws(const hstu_layer_args* l) {
     w.o = align256(w.z + T * 4 * hd * 2);
     w.y = align256(w.o + T * hd * 2);
     w.sched = align256(w.y + T * hd * 2);
-    w.total = hstu::sched_layout(l->B, l->max_seq_len, hstu::kBf16TileM, l->num_rows, w.sched).bytes;
+    w.total = hstu::sched_layout(l->B, l->H, l->max_seq_len, hstu::kBf16TileM, l->d, l->num_rows, w.sched).bytes;
     return w;
 }
 
@@ -419,7 +454,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     if (e != hipSuccess) return device_error(e, "scheduler launch");
     e = run_core(&a, s, stream);
     if (e != hipSuccess) return device_error(e, "attention launch");
-    e = run_ln_gate(&a, nullptr, nullptr, 0, stream);
+    e = run_ln_gate(&a, s, nullptr, nullptr, 0, false, stream);
     if (e != hipSuccess) return device_error(e, "epilogue launch");
 
     // f2 + residual: X_out = X + Y W2^T + b2

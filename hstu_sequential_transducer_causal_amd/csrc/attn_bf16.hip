@@ -75,7 +75,9 @@ struct Params {
     const WorkItem* items;
     const int32_t* ctrl;
     int32_t* cursor;
-    const int32_t* bscan;
+    float* partial;
+    int32_t* rowmap;
+    int nblk;
     const uint32_t* stats;
     const uint32_t* enc;
     int pos_copy;   // floats per shifted copy of the reversed position table
@@ -87,7 +89,7 @@ struct Smem {
     uint32_t tsk[kStages][64];            // [0..31] key codes, [32..33] key block range
     float tt_fast[32];                    // by leading-zero count of 2|dt| + 1
     float tt_wide[65];                    // by bit length of |dt|
-    int32_t item[4];
+    int32_t item[8];
     int32_t work;
 };
 
@@ -262,6 +264,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             if (w < total_work) {
                 const WorkItem it = p.items[w / p.H];
                 s.item[0] = it.b; s.item[1] = it.qt; s.item[2] = it.a_end; s.item[3] = it.kb;
+                s.item[4] = it.pr; s.item[5] = it.slot; s.item[6] = it.k; s.item[7] = it.n;
             }
         }
         lds_sync();
@@ -270,6 +273,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
         const int kbw = uni(s.item[3]);
         const int kb_begin = kbw & 0xffff, kb_end = kbw >> 16;
+        const int prw = uni(s.item[4]);
+        const int p0 = prw & 0xffff, p1 = prw >> 16;   // this piece's positions in the tile list
+        const int slot = uni(s.item[5]), piece = uni(s.item[6]), npieces = uni(s.item[7]);
         const int h = w % p.H;
 
         // wave-uniform by construction; readfirstlane lets the compiler keep
@@ -277,7 +283,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const int64_t row0 = uni(p.offsets[b]);
         const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
         const int n = uni(p.ncand ? L - p.ncand[b] : L);
-        const int bbase = uni(p.bscan[b]);
+        const int bbase = b * p.nblk;
 
         // ---- bias tables (reloaded only when they differ by head)
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
@@ -316,8 +322,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             dma.vtile = (uint32_t)(BN * p.vs * 2);
             dma.enc_row0 = enc_base + 4 * row0;
         }
-        const int ntiles = a_end + (kb_end - kb_begin);
-        auto tile_of = [&](int it) { return it < a_end ? it : kb_begin + (it - a_end); };
+        const int ntiles = p1 - p0;
+        auto tile_of = [&](int it) {
+            const int pos = p0 + it;
+            return pos < a_end ? pos : kb_begin + (pos - a_end);
+        };
 #pragma unroll
         for (int pre = 0; pre < kStages - 1; ++pre)
             if (pre < ntiles) issue_tile(dma, s, pre, tile_of(pre), L, wave, lane);
@@ -540,22 +549,43 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             }
         }
 
-        // ---------- O = alpha * acc, bf16, rows < L only
+        // ---------- O = alpha * acc, rows < L only: bf16 into O, or fp32 into
+        //            the piece's partial slot when the row block is split
         // lane holds O[row 8 (r / 4) + 4 h2 + r % 4][d = nb * 32 + l32]
+        if (slot < 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ro = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (ro < L) {
-                uint16_t* op = p.o + (row0 + ro) * p.os + h * HD + l32;
+            for (int r = 0; r < 16; ++r) {
+                const int ro = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                if (ro < L) {
+                    uint16_t* op = p.o + (row0 + ro) * p.os + h * HD + l32;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
+                    for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
+                }
             }
+        } else {
+            float* pp = p.partial + ((int64_t)(slot + piece) * p.H + h) * (BM * HD);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = wave * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                if (qt * BM + lr < L) {
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) pp[lr * HD + nb * 32 + l32] = alpha_eff * oacc[nb][r];
+                }
+            }
+        }
+        // the row map tells the epilogue which rows to sum from partial slots
+        if (p.rowmap && h == 0 && piece == 0 && lane < 32) {
+            const int lr = wave * 32 + lane;
+            if (qt * BM + lr < L)
+                p.rowmap[row0 + qt * BM + lr] = slot < 0 ? -1 : (slot | (npieces << 16) | (lr << 23));
         }
         lds_barrier();   // this item's LDS use is over before the next item starts
     }
 }
 
 }  // namespace
+
+int attn_bf16_slots() { return device_cu_count() * 2; }
 
 hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     Params p;
@@ -570,7 +600,8 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.alpha = a.alpha;
     p.o = static_cast<uint16_t*>(a.o); p.os = a.o_stride;
     p.items = a.items; p.ctrl = a.ctrl; p.cursor = a.cursor;
-    p.bscan = a.bscan; p.stats = a.stats; p.enc = a.enc;
+    p.stats = a.stats; p.enc = a.enc;
+    p.partial = a.partial; p.rowmap = a.rowmap; p.nblk = a.nblk;
     p.pos_copy = ((a.P + 128 + 4) + 3) & ~3;
     const size_t smem = ((sizeof(Smem) + 15) & ~size_t(15)) + sizeof(float) * 2 * size_t(p.pos_copy);
     const void* fn = a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true>)
@@ -579,7 +610,7 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
     }
-    const int grid = device_cu_count() * 2;
+    const int grid = attn_bf16_slots();
     // one buffer resource covers the block ranges and the row codes
     const void* ws_base = a.stats;
     const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);

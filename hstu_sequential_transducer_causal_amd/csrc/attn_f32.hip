@@ -72,9 +72,11 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(Params p) {
         const int64_t ti = valid ? p.ts[row0 + i] : 0;
         const int pi = min(i, n);
 
-        const int ntiles = it.a_end + (kb_end - kb_begin);
+        const int p0 = it.pr & 0xffff, p1 = it.pr >> 16;   // (never split: the whole list)
+        const int ntiles = p1 - p0;
         for (int t = 0; t < ntiles; ++t) {
-            const int kt = t < it.a_end ? t : kb_begin + (t - it.a_end);
+            const int pos = p0 + t;
+            const int kt = pos < it.a_end ? pos : kb_begin + (pos - it.a_end);
             const int j0 = kt * BN;
             {
                 const int j = j0 + lane;

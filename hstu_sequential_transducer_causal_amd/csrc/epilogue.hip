@@ -12,6 +12,10 @@
 // HBM-bound: one wave per row, 16-byte vector loads, the row held in
 // registers for a two-pass (mean, then centred variance) reduction with
 // wavefront shuffles; no LDS.
+//
+// Rows of a row block that the bf16 attention core split over key ranges
+// arrive as fp32 partial sums: their O is the sum of those, rounded to bf16
+// as the core rounds O, and is written to O here before it is normalised.
 #include "internal.h"
 #include "hstu_device.h"
 #include "../../include/hstu.h"
@@ -83,18 +87,56 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
         n = a.ncand ? L - a.ncand[b] : L;
         want_score = a.w != nullptr && r >= n;
     }
-    if (a.y == nullptr && !want_score) return;
+    // (with cand_only only the candidate rows are covered by this call's map)
+    const bool mapped = BF16 && a.rowmap != nullptr && (want_score || !a.cand_only);
+    if (a.y == nullptr && !want_score && !mapped) return;
 
     const int W = a.width;
-    // both operand rows are fetched before any arithmetic
+    // the map entry and both operand rows are fetched before any arithmetic
+    const int code = mapped ? a.rowmap[row] : -1;
     float x[NCH][8], u[NCH][8];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int col = (c * 64 + lane) * 8;
         if (col < W) {
             Vec8<BF16>::load(a.o, row * a.o_stride + col, x[c]);
-            Vec8<BF16>::load(a.u, row * a.u_stride + col, u[c]);
+            if (a.y || want_score) Vec8<BF16>::load(a.u, row * a.u_stride + col, u[c]);
         }
+    }
+    if constexpr (BF16) {
+        if (code >= 0) {
+            // O of a split row: slot | pieces << 16 | (row within block) << 23
+            const int slot = code & 0xffff, np = (code >> 16) & 0x7f, lr = code >> 23;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int col = (c * 64 + lane) * 8;
+                if (col < W) {
+                    const int h = col / a.d;
+                    const int cc = col - h * a.d;
+                    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    for (int k = 0; k < np; ++k) {
+                        const float* src = a.partial + ((int64_t)(slot + k) * a.H + h) * a.BM * a.d +
+                                           (int64_t)lr * a.d + cc;
+                        const f32x4 p0 = *reinterpret_cast<const f32x4*>(src);
+                        const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[e] += p0[e];
+                            acc[4 + e] += p1[e];
+                        }
+                    }
+                    u32x4 r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        r[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+                        x[c][2 * e] = __uint_as_float(r[e] << 16);
+                        x[c][2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+                    }
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + row * a.o_stride + col) = r;
+                }
+            }
+        }
+        if (a.y == nullptr && !want_score) return;
     }
     float sum = 0.0f;
 #pragma unroll

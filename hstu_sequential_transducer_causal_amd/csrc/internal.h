@@ -7,17 +7,39 @@
 
 namespace hstu {
 
-// Jagged tile work list.  One item covers BM query rows of one sequence
-// (all heads share the item list; the head is the fastest-varying index of
-// the flattened work index item * H + h).  Its key tiles (BN keys each) are
-// [0, a_end) followed by [kb_begin, kb_end); every other key tile of the row
-// block has no visible pair and is skipped.
+// Jagged tile work list.  One entry (a piece) covers BM query rows of one
+// sequence (all heads share the list; the head is the fastest-varying index
+// of the flattened work index piece * H + h).  The row block's key tiles (BN
+// keys each) are [0, a_end) followed by [kb_begin, kb_end) -- every other key
+// tile of the block has no visible pair -- and the piece takes positions
+// [p0, p1) of that list.  A block whose list is long next to the work per
+// workgroup is split into several pieces ("split-K": without a softmax the
+// partial sums over key ranges simply add); each piece then writes fp32
+// partial sums to partial slot (slot + k), and the LN(O) * U epilogue -- or,
+// without one, a combine pass -- adds them up.
 struct WorkItem {
     int32_t b;
     int32_t qt;
     int32_t a_end;
-    int32_t kb;  // kb_begin | kb_end << 16
+    int32_t kb;     // kb_begin | kb_end << 16
+    int32_t pr;     // p0 | p1 << 16
+    int32_t slot;   // first partial slot of the block, or -1: not split (O written directly)
+    int32_t k;      // piece index within the block
+    int32_t n;      // pieces of the block
 };
+
+// A split row block: its pieces' partial sums sit in slots slot .. slot+n-1.
+struct SplitBlock {
+    int32_t b;
+    int32_t qt;
+    int32_t slot;
+    int32_t n;
+};
+
+// Partial slots (one per split piece and head, BM x d fp32 each) a call may use.
+constexpr int kMaxPartialSlots = 1024;
+// Pieces are never shorter than this many key tiles.
+constexpr int kMinPieceTiles = 8;
 
 constexpr int kMaxSeqLen = 65536;
 constexpr int kMaxPosBuckets = 8192;
@@ -29,50 +51,57 @@ constexpr int kTsBlock = 32;
 // Workspace carve-up of the scheduler and the timestamp preparation (all
 // offsets 256-byte aligned).
 struct SchedLayout {
-    size_t off_ctrl;   // int32[64]: [0] item count, [1] work cursor of the persistent kernel
+    size_t off_ctrl;   // int32[64]: [0] piece count, [1] work cursor of the persistent kernel,
+                       // [2] split-block count
     size_t off_qscan;  // int32[B + 1] exclusive prefix of query tiles per sequence
-    size_t off_bscan;  // int32[B + 1] exclusive prefix of 32-row timestamp blocks per sequence
-    size_t off_items;  // WorkItem[cap]
-    size_t off_stats;  // uint32x2[cap_blk]: encoded timestamp range of each 32-row block
+    size_t off_items;  // WorkItem[cap_pieces]
+    size_t off_split;  // SplitBlock[cap]
+    size_t off_part;   // float[part_slots][BM][d]: partial sums of split pieces
+    size_t off_stats;  // uint32x2[cap_blk]: encoded timestamp range of 32-row block j of
+                       // sequence b at index b * nblk + j
     size_t off_enc;    // uint32[num_rows]: encoded timestamp of each row
-    size_t cap;        // item capacity = B * ceil(max_seq_len / BM)
-    size_t cap_blk;    // block capacity = B * ceil(max_seq_len / 32)
+    size_t off_rowmap; // int32[num_rows]: split map of each row (see AttnCoreArgs::rowmap)
+    size_t cap;        // row-block capacity = B * ceil(max_seq_len / BM)
+    size_t cap_pieces; // piece capacity = cap + part_slots / H
+    size_t cap_blk;    // block capacity = B * nblk
+    int nblk;          // 32-row blocks per sequence = ceil(max_seq_len / 32)
+    int part_slots;    // partial slots (split pieces x heads); 0: no splitting
     size_t bytes;      // total
 };
 
-SchedLayout sched_layout(int B, int max_seq_len, int tile_m, int64_t num_rows, size_t base_offset);
+// split_d: head dim of the partial slots (0 disables splitting).
+SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d, int64_t num_rows,
+                         size_t base_offset);
 
 struct SchedArgs {
     int B;
     int max_seq_len;   // bound on every sequence length (sizes the cost histogram)
-    int64_t cap;       // item capacity of `items`
+    int64_t cap;       // row-block capacity (split-block list)
+    int64_t cap_pieces;   // piece capacity of `items`
     int cand_only;     // M-FALCON: only the query tiles that hold candidate rows
+    int H;
+    int slots;         // workgroups of the attention core (the work per workgroup sets the piece size)
+    int part_slots;    // partial slots available (0: no splitting)
+    SplitBlock* split;
     const int32_t* offsets;
     const int32_t* lengths;
     const int32_t* ncand;
     int tile_m, tile_n;
     int32_t* ctrl;
     int32_t* qscan;
-    int32_t* bscan;
     WorkItem* items;
-};
-
-// Per-row timestamp code e = 2 (t - t_first) + 2^31 (t_first: the sequence's
-// first row) and, per 32-row block of a sequence, the range [min e, max e];
-// a block with some |t - t_first| >= 2^30 gets the range {0xffffffff, 0}.
-struct TsPrepArgs {
-    int B;
-    const int32_t* offsets;
-    const int32_t* lengths;
+    // Timestamp codes (bf16 core; enc == NULL skips them): per row
+    // e = 2 (t - t_first) + 2^31 (t_first: the sequence's first row) and,
+    // per 32-row block, the range [min e, max e]; a block with some
+    // |t - t_first| >= 2^30 gets the range {0xffffffff, 0}.
     const int64_t* ts;
-    const int32_t* bscan;
     uint32_t* enc;
-    uint32_t* stats;     // pairs (min, max)
+    uint32_t* stats;     // pairs (min, max), block j of sequence b at b * nblk + j
+    int nblk;
     int64_t cap_blk;
 };
 
-hipError_t launch_ts_prep(const TsPrepArgs& a, hipStream_t stream);
-
+// Work list and timestamp codes, in one launch.
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
 
 // Attention core, bf16 with MFMA, d_qk = d_v = 128.
@@ -100,7 +129,11 @@ struct AttnCoreArgs {
     const WorkItem* items;
     const int32_t* ctrl;   // [0] = item count
     int32_t* cursor;       // persistent work cursor (zeroed by the scheduler)
-    const int32_t* bscan;  // timestamp blocks (bf16 core only)
+    float* partial;        // partial slots of split pieces (bf16 core only)
+    // bf16 core only: per row of every row block it computes, -1 (O written)
+    // or, for a split block, slot | pieces << 16 | (row within block) << 23
+    int32_t* rowmap;
+    int nblk;              // timestamp blocks per sequence in `stats`
     const uint32_t* stats;
     const uint32_t* enc;
     int64_t num_rows;
@@ -108,6 +141,23 @@ struct AttnCoreArgs {
 };
 
 hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream);
+
+// Workgroups of the persistent bf16 attention core.
+int attn_bf16_slots();
+
+// Sums the partial slots of every split row block into its bf16 O rows.
+struct CombineArgs {
+    int H, d, BM;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const int32_t* ctrl;        // [2] = split-block count
+    const SplitBlock* split;
+    const float* partial;
+    void* o; int64_t o_stride;
+    int64_t max_blocks;         // capacity of the split-block list
+};
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnCoreArgs& a, hipStream_t stream);
 
 // LayerNorm(O_row) * U_row epilogue, optionally scored against w for the
@@ -120,12 +170,19 @@ struct LnGateArgs {
     const int32_t* offsets;
     const int32_t* lengths;
     const int32_t* ncand;
-    const void* o; int64_t o_stride;
+    void* o; int64_t o_stride;     // read, and written for split rows
     const void* u; int64_t u_stride;
     void* y; int64_t y_stride;   // may be NULL when scores are requested
     float eps;
     const float* w;       // NULL: no scores
     float* scores; int score_stride;
+    // bf16 with split row blocks: rows whose map entry is >= 0 sum their
+    // block's partial slots (BM x d fp32 each, head-major per piece) and
+    // write that sum to O before normalising it.  NULL: O holds every row.
+    const int32_t* rowmap;
+    const float* partial;
+    int H, d, BM;
+    int cand_only;        // the core computed only candidate-row blocks: map only those rows
 };
 
 hipError_t launch_ln_gate(const LnGateArgs& a, hipStream_t stream);

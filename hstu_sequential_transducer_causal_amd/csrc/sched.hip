@@ -22,6 +22,8 @@
 //
 // One workgroup of 1024 threads runs the whole build; it is a few
 // microseconds of work next to the attention core.
+#include <algorithm>
+
 #include "internal.h"
 #include "hstu_device.h"
 
@@ -36,6 +38,11 @@ constexpr int kMaxBins = kMaxSeqLen / 32 + 2;  // cost <= number of key tiles of
 // (the binary searches below then never wait on memory); larger ones use the
 // workspace copies.
 constexpr int kLdsSeq = 4096;
+// Up to this many row blocks keep their cost (key tiles) in LDS between the
+// passes; longer lists recompute it.
+constexpr int kLdsItems = 8192;
+// 32-row timestamp blocks per workgroup of the timestamp role.
+constexpr int kTsPerGroup = kThreads / 32;
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -57,6 +64,18 @@ __device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int 
     }
     return r;
 }
+
+struct SchedSmem {
+    int hist[kMaxBins];
+    int wave_tot[kWaves];
+    long long wave_sum[kWaves];
+    int wave_max[kWaves];
+    int carry, carry2;
+    int qscan[kLdsSeq + 1];
+    int len[kLdsSeq];
+    int nhist[kLdsSeq];          // history rows n_b
+    uint16_t cost[kLdsItems];
+};
 
 // Exclusive scan of one value per thread over the workgroup; also returns
 // the workgroup total.  All threads must call it.
@@ -83,6 +102,33 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
     return before + x - v;
 }
 
+// Workgroup sum (64-bit) and maximum of one value per thread; all threads
+// must call it.
+__device__ long long block_sum_max(long long v, int m, SchedSmem& s, int& mx) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        v += __shfl_xor(v, o, 64);
+        m = max(m, __shfl_xor(m, o, 64));
+    }
+    if (lane == 0) {
+        s.wave_sum[w] = v;
+        s.wave_max[w] = m;
+    }
+    __syncthreads();
+    long long t = 0;
+    int tm = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        t += s.wave_sum[i];
+        tm = max(tm, s.wave_max[i]);
+    }
+    __syncthreads();
+    mx = tm;
+    return t;
+}
+
 __device__ __forceinline__ int seq_length(const SchedArgs& a, int b) {
     return a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
 }
@@ -102,6 +148,16 @@ __device__ __forceinline__ int tile_count(const SchedArgs& a, int L, int n, int 
     return ceil_div(L, BM) - first_tile(a, n, BM);
 }
 
+// Pieces of a row block of c key tiles at piece size `chunk` (a block is
+// split only when it exceeds 1.5 chunks: a little over the mean work per
+// workgroup does not hold up the grid's end, while the split costs partial
+// traffic), and the end (exclusive, in list positions) of piece k;
+// piece_end(c, n, -1) = 0.
+__device__ __forceinline__ int pieces_of(int c, int chunk) {
+    return 2 * (int64_t)c > 3 * (int64_t)chunk ? min(ceil_div(c, chunk), 64) : 1;
+}
+__device__ __forceinline__ int piece_end(int c, int n, int k) { return (int)(((int64_t)c * (k + 1)) / n); }
+
 // Sequence of flat query tile f: the last b with qscan[b] <= f.
 template <typename Ptr>
 __device__ __forceinline__ int find_seq(Ptr qscan, int B, int f) {
@@ -113,73 +169,58 @@ __device__ __forceinline__ int find_seq(Ptr qscan, int B, int f) {
     return lo;
 }
 
-__global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
-    __shared__ int hist[kMaxBins];
-    __shared__ int wave_tot[kWaves];
-    __shared__ int carry_s, bcarry_s;
-    __shared__ int qscan_s[kLdsSeq + 1];
-    __shared__ int len_s[kLdsSeq];
-    __shared__ int hist_s[kLdsSeq];   // history rows n_b
+// Workgroup 0 of the preparation launch: the work list.
+__device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
     const int tid = threadIdx.x;
     const int BM = a.tile_m, BN = a.tile_n;
     const bool in_lds = a.B <= kLdsSeq;
     // costs (key tiles of an item) lie in [0, ceil(max_seq_len / BN)]
     const int nbins = min(kMaxBins, ceil_div(a.max_seq_len, BN) + 2);
 
-    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
-    if (tid == 0) {
-        carry_s = 0;
-        bcarry_s = 0;
-    }
+    for (int i = tid; i < nbins; i += kThreads) s.hist[i] = 0;
+    if (tid == 0) s.carry = 0;
     __syncthreads();
 
-    // 1. query tiles and 32-row timestamp blocks per sequence -> exclusive
-    //    prefixes qscan[0..B] and bscan[0..B]
+    // 1. query tiles per sequence -> exclusive prefix qscan[0..B]
     for (int base = 0; base < a.B; base += kThreads) {
-        int b = base + tid;
-        int nq = 0, nblk = 0;
+        const int b = base + tid;
+        int nq = 0;
         if (b < a.B) {
             const int L = seq_length(a, b);
             const int n = seq_history(a, b, L);
             nq = tile_count(a, L, n, BM);
-            nblk = ceil_div(L, kTsBlock);
             if (in_lds) {
-                len_s[b] = L;
-                hist_s[b] = n;
+                s.len[b] = L;
+                s.nhist[b] = n;
             }
         }
-        int total, btotal;
-        int ex = block_exclusive_scan(nq, wave_tot, total);
-        int bex = block_exclusive_scan(nblk, wave_tot, btotal);
-        int carry = carry_s, bcarry = bcarry_s;
+        int total;
+        const int ex = block_exclusive_scan(nq, s.wave_tot, total);
+        const int carry = s.carry;
         if (b < a.B) {
             a.qscan[b] = carry + ex;
-            a.bscan[b] = bcarry + bex;
-            if (in_lds) qscan_s[b] = carry + ex;
+            if (in_lds) s.qscan[b] = carry + ex;
         }
         __syncthreads();
-        if (tid == 0) {
-            carry_s = carry + total;
-            bcarry_s = bcarry + btotal;
-        }
+        if (tid == 0) s.carry = carry + total;
         __syncthreads();
     }
-    const int nitems = carry_s;
+    const int nitems = s.carry;
     if (tid == 0) {
         a.qscan[a.B] = nitems;
-        a.bscan[a.B] = bcarry_s;
-        if (in_lds) qscan_s[a.B] = nitems;
+        if (in_lds) s.qscan[a.B] = nitems;
     }
     __syncthreads();
+    const bool cost_in_lds = in_lds && nitems <= kLdsItems;
 
-    // the item of flat query tile f
+    // the row block of flat query tile f
     auto item_of = [&](int f, int& b, int& qt) -> Ranges {
         int L, n;
         if (in_lds) {
-            b = find_seq(qscan_s, a.B, f);
-            qt = f - qscan_s[b];
-            L = len_s[b];
-            n = hist_s[b];
+            b = find_seq(s.qscan, a.B, f);
+            qt = f - s.qscan[b];
+            L = s.len[b];
+            n = s.nhist[b];
         } else {
             b = find_seq(a.qscan, a.B, f);
             qt = f - a.qscan[b];
@@ -189,79 +230,186 @@ __global__ void __launch_bounds__(kThreads) sched_kernel(SchedArgs a) {
         qt += first_tile(a, n, BM);
         return tile_ranges(L, n, qt, BM, BN);
     };
-
-    // 2. histogram of item costs (key tiles per item)
-    for (int f = tid; f < nitems; f += kThreads) {
+    auto cost_of = [](const Ranges& r) { return r.a_end + (r.kb_end - r.kb_begin); };
+    auto cost_at = [&](int f) {
+        if (cost_in_lds) return (int)s.cost[f];
         int b, qt;
-        const Ranges r = item_of(f, b, qt);
-        atomicAdd(&hist[min(r.a_end + (r.kb_end - r.kb_begin), nbins - 1)], 1);
+        return cost_of(item_of(f, b, qt));
+    };
+
+    // 2. costs, their total (key tiles over all blocks) and maximum
+    long long work;
+    int max_cost;
+    {
+        long long mine = 0;
+        int mx = 0;
+        for (int f = tid; f < nitems; f += kThreads) {
+            int b, qt;
+            const int c = cost_of(item_of(f, b, qt));
+            if (cost_in_lds) s.cost[f] = (uint16_t)c;
+            mine += c;
+            mx = max(mx, c);
+        }
+        work = block_sum_max(mine, mx, s, max_cost);   // (its barriers publish s.cost)
+    }
+
+    // 3. piece size: only blocks longer than the mean work per workgroup --
+    //    which would hold up the persistent grid's end -- are split, within
+    //    the partial-slot budget
+    int chunk = 1 << 30;
+    if (a.part_slots > 0 && a.slots > 0) {
+        const unsigned long long units = (unsigned long long)work * (unsigned long long)a.H;
+        chunk = max(kMinPieceTiles, (int)min((units + a.slots - 1) / (unsigned long long)a.slots, 1ull << 20));
+        for (int round = 0; round < 24 && pieces_of(max_cost, chunk) > 1; ++round) {
+            int mine = 0;
+            for (int f = tid; f < nitems; f += kThreads) {
+                const int np = pieces_of(cost_at(f), chunk);
+                mine += np > 1 ? np : 0;
+            }
+            int unused;
+            const long long sp = block_sum_max(mine, 0, s, unused);
+            if (sp * a.H <= a.part_slots) break;
+            chunk *= 2;
+        }
+        if (pieces_of(max_cost, chunk) > 1) {
+            // (the budget loop ended without fitting: cannot happen for
+            // lengths within max_seq_len, but never overrun the slots)
+            int mine = 0;
+            for (int f = tid; f < nitems; f += kThreads) {
+                const int np = pieces_of(cost_at(f), chunk);
+                mine += np > 1 ? np : 0;
+            }
+            int unused;
+            if (block_sum_max(mine, 0, s, unused) * a.H > a.part_slots) chunk = 1 << 30;
+        }
+    }
+    const bool any_split = pieces_of(max_cost, chunk) > 1;
+
+    // 4. histogram of piece costs
+    for (int f = tid; f < nitems; f += kThreads) {
+        const int c = cost_at(f);
+        const int np = any_split ? pieces_of(c, chunk) : 1;
+        if (np == 1) {
+            atomicAdd(&s.hist[min(c, nbins - 1)], 1);
+        } else {
+            for (int k = 0; k < np; ++k)
+                atomicAdd(&s.hist[min(piece_end(c, np, k) - piece_end(c, np, k - 1), nbins - 1)], 1);
+        }
     }
     __syncthreads();
 
-    // 3. start position of each cost bin, largest cost first
-    if (tid == 0) carry_s = 0;
+    // 5. start position of each cost bin, largest cost first
+    if (tid == 0) s.carry = 0;
     __syncthreads();
     for (int base = 0; base < nbins; base += kThreads) {
-        int bin = nbins - 1 - (base + tid);
-        int c = bin >= 0 ? hist[bin] : 0;
+        const int bin = nbins - 1 - (base + tid);
+        const int c = bin >= 0 ? s.hist[bin] : 0;
         int total;
-        int ex = block_exclusive_scan(c, wave_tot, total);
-        int carry = carry_s;
-        if (bin >= 0) hist[bin] = carry + ex;
+        const int ex = block_exclusive_scan(c, s.wave_tot, total);
+        const int carry = s.carry;
+        if (bin >= 0) s.hist[bin] = carry + ex;
         __syncthreads();
-        if (tid == 0) carry_s = carry + total;
+        if (tid == 0) s.carry = carry + total;
         __syncthreads();
     }
+    const int npieces = s.carry;
 
-    // 4. scatter the items into their bins
-    for (int f = tid; f < nitems; f += kThreads) {
-        int b, qt;
-        const Ranges r = item_of(f, b, qt);
-        int pos = atomicAdd(&hist[min(r.a_end + (r.kb_end - r.kb_begin), nbins - 1)], 1);
-        WorkItem it;
-        it.b = b;
-        it.qt = qt;
-        it.a_end = r.a_end;
-        it.kb = r.kb_begin | (r.kb_end << 16);
-        if (pos < a.cap) a.items[pos] = it;   // (lengths within max_seq_len always fit)
+    // 6. scatter the pieces into their bins; split blocks get consecutive
+    //    partial slots and an entry in the split-block list
+    if (tid == 0) {
+        s.carry = 0;    // split blocks so far
+        s.carry2 = 0;   // partial slots so far
+    }
+    __syncthreads();
+    for (int base = 0; base < nitems; base += kThreads) {
+        const int f = base + tid;
+        int b = 0, qt = 0, c = 0, np = 1;
+        Ranges r = {0, 0, 0};
+        if (f < nitems) {
+            r = item_of(f, b, qt);
+            c = cost_of(r);
+            np = any_split ? pieces_of(c, chunk) : 1;
+        }
+        int sx = 0, px = 0, nsplit = 0, nslots = 0;
+        if (any_split) {
+            // one scan of (split blocks << 17 | their slots): at most 1024
+            // blocks of at most 64 pieces in a pass
+            int tot;
+            const int packed = np > 1 ? (1 << 17) | np : 0;
+            const int ex = block_exclusive_scan(packed, s.wave_tot, tot);
+            sx = ex >> 17;
+            px = ex & 0x1ffff;
+            nsplit = tot >> 17;
+            nslots = tot & 0x1ffff;
+        }
+        const int scarry = s.carry, pcarry = s.carry2;
+        if (f < nitems) {
+            const int slot = np > 1 ? pcarry + px : -1;
+            if (np > 1 && scarry + sx < a.cap) {
+                SplitBlock sb;
+                sb.b = b; sb.qt = qt; sb.slot = slot; sb.n = np;
+                a.split[scarry + sx] = sb;
+            }
+            for (int k = 0; k < np; ++k) {
+                const int p0 = piece_end(c, np, k - 1), p1 = piece_end(c, np, k);
+                const int pos = atomicAdd(&s.hist[min(p1 - p0, nbins - 1)], 1);
+                WorkItem it;
+                it.b = b;
+                it.qt = qt;
+                it.a_end = r.a_end;
+                it.kb = r.kb_begin | (r.kb_end << 16);
+                it.pr = p0 | (p1 << 16);
+                it.slot = slot;
+                it.k = k;
+                it.n = np;
+                if (pos < a.cap_pieces) a.items[pos] = it;   // (lengths within max_seq_len always fit)
+            }
+        }
+        if (any_split) {
+            __syncthreads();
+            if (tid == 0) {
+                s.carry = scarry + nsplit;
+                s.carry2 = pcarry + nslots;
+            }
+            __syncthreads();
+        }
     }
     if (tid == 0) {
-        a.ctrl[0] = (int)min((int64_t)nitems, a.cap);
+        a.ctrl[0] = (int)min((int64_t)npieces, a.cap_pieces);
         a.ctrl[1] = 0;
+        a.ctrl[2] = any_split ? (int)min((int64_t)s.carry, a.cap) : 0;
     }
 }
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// One wave per two 32-row blocks (lanes 0-31 and 32-63).
-__global__ void __launch_bounds__(256) ts_prep_kernel(TsPrepArgs a) {
-    __shared__ int bscan_s[kLdsSeq + 1];
-    const bool in_lds = a.B <= kLdsSeq;
-    if (in_lds)
-        for (int i = threadIdx.x; i <= a.B; i += 256) bscan_s[i] = a.bscan[i];
-    __syncthreads();
+// Workgroups 1.. of the preparation launch: per row the timestamp code
+// e = 2 (t - t_first) + 2^31 (t_first: the sequence's first row) and, per
+// 32-row block (sequence b, block j at index b * nblk + j), the code range
+// [min e, max e]; a block with some |t - t_first| >= 2^30 gets the range
+// {0xffffffff, 0}.  One half-wave per block.
+__device__ void encode_timestamps(const SchedArgs& a) {
     const int lane = threadIdx.x & 63;
-    const int64_t f = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + (lane >> 5);
-    const int nblk = in_lds ? bscan_s[a.B] : a.bscan[a.B];
-    const bool active = f < nblk && f < a.cap_blk;
+    const int64_t g = ((int64_t)blockIdx.x - 1) * kTsPerGroup + (threadIdx.x >> 5);
+    const int b = (int)(g / a.nblk);
+    const int j0 = (int)(g - (int64_t)b * a.nblk) * kTsBlock;
+    bool active = g < a.cap_blk;
+    int64_t row0 = 0;
+    int L = 0;
+    if (active) {
+        row0 = a.offsets[b];
+        L = seq_length(a, b);
+        active = j0 < L;
+    }
     uint32_t mn = 0xffffffffu, mx = 0u;
     bool narrow = true;
-    int64_t fi = 0;
-    if (active) {
-        fi = f;
-        const int b = in_lds ? find_seq(bscan_s, a.B, (int)f) : find_seq(a.bscan, a.B, (int)f);
-        const int64_t row0 = a.offsets[b];
-        const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - (int)row0;
-        const int j = ((int)f - (in_lds ? bscan_s[b] : a.bscan[b])) * kTsBlock + (lane & 31);
-        if (j < L) {
-            const int64_t t_first = a.ts[row0];
-            const int64_t d = a.ts[row0 + j] - t_first;
-            narrow = d > -(int64_t(1) << 30) && d < (int64_t(1) << 30);
-            const uint32_t e = uint32_t(int32_t(d) * 2) + 0x80000000u;
-            a.enc[row0 + j] = e;
-            mn = e;
-            mx = e;
-        }
+    const int j = j0 + (lane & 31);
+    if (active && j < L) {
+        const int64_t t_first = a.ts[row0];
+        const int64_t d = a.ts[row0 + j] - t_first;
+        narrow = d > -(int64_t(1) << 30) && d < (int64_t(1) << 30);
+        const uint32_t e = uint32_t(int32_t(d) * 2) + 0x80000000u;
+        a.enc[row0 + j] = e;
+        mn = e;
+        mx = e;
     }
     int nar = narrow ? 1 : 0;
 #pragma unroll
@@ -271,36 +419,99 @@ __global__ void __launch_bounds__(256) ts_prep_kernel(TsPrepArgs a) {
         nar &= __shfl_xor(nar, m, 64);
     }
     if (active && (lane & 31) == 0) {
-        a.stats[2 * fi] = nar ? mn : 0xffffffffu;
-        a.stats[2 * fi + 1] = nar ? mx : 0u;
+        a.stats[2 * g] = nar ? mn : 0xffffffffu;
+        a.stats[2 * g + 1] = nar ? mx : 0u;
     }
 }
 
+// One launch prepares everything the attention core reads besides the
+// inputs: workgroup 0 builds the work list while the others (bf16 core
+// only) encode the timestamps.
+__global__ void __launch_bounds__(kThreads) prep_kernel(SchedArgs a) {
+    __shared__ SchedSmem s;
+    if (blockIdx.x == 0)
+        build_work_list(a, s);
+    else
+        encode_timestamps(a);
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
-SchedLayout sched_layout(int B, int max_seq_len, int tile_m, int64_t num_rows, size_t base) {
+SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d, int64_t num_rows,
+                         size_t base) {
     SchedLayout l;
+    l.cap = size_t(B) * size_t((max_seq_len + tile_m - 1) / tile_m);
+    l.nblk = (max_seq_len + kTsBlock - 1) / kTsBlock;
+    l.cap_blk = size_t(B) * size_t(l.nblk);
+    // partial slots: at most kMaxPartialSlots, and no more than 8 per row block and head
+    l.part_slots = split_d > 0 && H > 0 ? (int)std::min<size_t>(kMaxPartialSlots, l.cap * size_t(H) * 8) : 0;
+    l.cap_pieces = l.cap + (H > 0 ? size_t(l.part_slots) / size_t(H) : 0);
     l.off_ctrl = align256(base);
     l.off_qscan = align256(l.off_ctrl + 64 * sizeof(int32_t));
-    l.off_bscan = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
-    l.off_items = align256(l.off_bscan + (size_t(B) + 1) * sizeof(int32_t));
-    l.cap = size_t(B) * size_t((max_seq_len + tile_m - 1) / tile_m);
-    l.cap_blk = size_t(B) * size_t((max_seq_len + kTsBlock - 1) / kTsBlock);
-    l.off_stats = align256(l.off_items + l.cap * sizeof(WorkItem));
+    l.off_items = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
+    l.off_split = align256(l.off_items + l.cap_pieces * sizeof(WorkItem));
+    l.off_part = align256(l.off_split + l.cap * sizeof(SplitBlock));
+    l.off_stats = align256(l.off_part + size_t(l.part_slots) * size_t(tile_m) * size_t(split_d) * sizeof(float));
     l.off_enc = align256(l.off_stats + l.cap_blk * 2 * sizeof(uint32_t));
-    l.bytes = align256(l.off_enc + size_t(num_rows) * sizeof(uint32_t));
+    l.off_rowmap = align256(l.off_enc + size_t(num_rows) * sizeof(uint32_t));
+    l.bytes = align256(l.off_rowmap + (split_d > 0 ? size_t(num_rows) * sizeof(int32_t) : 0));
     return l;
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+    const int64_t ts_groups = a.enc ? (a.cap_blk + kTsPerGroup - 1) / kTsPerGroup : 0;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + ts_groups)), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_ts_prep(const TsPrepArgs& a, hipStream_t stream) {
-    if (a.cap_blk <= 0) return hipSuccess;
-    const int64_t blocks = (a.cap_blk + 7) / 8;
-    hipLaunchKernelGGL(ts_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+namespace {
+
+__device__ __forceinline__ void combine_one(const CombineArgs& a, int64_t t, int per_row, int64_t per_block) {
+    const int64_t sb_i = t / per_block;
+    const int64_t rem = t - sb_i * per_block;
+    const int h = (int)(rem / (a.BM * per_row));
+    const int lr = (int)(rem / per_row) % a.BM;
+    const int c8 = (int)(rem % per_row) * 8;
+    const SplitBlock sb = a.split[sb_i];
+    const int64_t row0 = a.offsets[sb.b];
+    const int L = a.lengths ? a.lengths[sb.b] : a.offsets[sb.b + 1] - (int)row0;
+    const int r = sb.qt * a.BM + lr;
+    if (r >= L) return;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < sb.n; ++k) {
+        const float* src = a.partial + ((int64_t)(sb.slot + k) * a.H + h) * a.BM * a.d + (int64_t)lr * a.d + c8;
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
+        acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+    }
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    uint16_t* dst = static_cast<uint16_t*>(a.o) + (row0 + r) * a.o_stride + h * a.d + c8;
+    *reinterpret_cast<u32x4*>(dst) = pk;
+}
+
+// Grid-stride over (split block, head, row, 8 columns): the sum of the
+// block's partial slots, rounded to bf16 into O (rows past L are skipped).
+// With no split block every thread exits at once.
+__global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
+    const int per_row = a.d / 8;
+    const int64_t per_block = (int64_t)a.H * a.BM * per_row;
+    const int64_t nsb = min((int64_t)a.ctrl[2], a.max_blocks);
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < nsb * per_block; t += (int64_t)gridDim.x * 256)
+        combine_one(a, t, per_row, per_block);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    if (a.max_blocks <= 0) return hipSuccess;
+    const int64_t threads = a.max_blocks * a.H * a.BM * (a.d / 8);
+    const int64_t blocks = std::min<int64_t>((threads + 255) / 256, (int64_t)device_cu_count());
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

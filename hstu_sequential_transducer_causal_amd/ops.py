@@ -203,7 +203,7 @@ def layer_workspace_bytes(l: _lib.LayerArgs) -> int:
 
 def hstu_attn_schedule(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, *, max_seq_len: int,
                        seq_lengths=None, num_candidates=None, stream=None):
-    """The device-built work list as a host int32 array [count, 4] plus (tile_m, tile_n)."""
+    """The device-built work list as a host int32 array [count, 8] plus (tile_m, tile_n)."""
     import numpy as np
     lib = _lib.load()
     args = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, 1.0,
@@ -212,8 +212,8 @@ def hstu_attn_schedule(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, *, m
     need = lib.hstu_attn_workspace_bytes(ctypes.byref(args))
     ws = _empty_ws(need, q.device)
     B = seq_offsets.numel() - 1
-    cap = max(1, B * ((max_seq_len + 63) // 64))
-    items = np.zeros((cap, 4), dtype=np.int32)
+    cap = max(1, B * ((max_seq_len + 63) // 64)) + 1024   # row blocks + split pieces
+    items = np.zeros((cap, 8), dtype=np.int32)
     count = ctypes.c_int64(0)
     tm, tn = ctypes.c_int32(0), ctypes.c_int32(0)
     _lib.check(lib.hstu_attn_schedule(ctypes.byref(args), ws.data_ptr(), ws.numel(),

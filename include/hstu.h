@@ -131,8 +131,10 @@ const char* hstu_last_error(void);
 
 /* Workspace bytes needed by hstu_attn_fwd for these arguments (0 on invalid
  * arguments; call hstu_attn_fwd to get the reason).  Depends only on B,
- * max_seq_len, dtype and (for HSTU_BF16, which keeps a 4-byte timestamp
- * code per row) num_rows. */
+ * max_seq_len, dtype and, for HSTU_BF16, H and d_v (fp32 partial sums of
+ * row blocks split over their key tiles, at most 1024 slots of 128 x d_v)
+ * and num_rows (a 4-byte timestamp code and a 4-byte split-map entry per
+ * row). */
 size_t hstu_attn_workspace_bytes(const hstu_attn_args* args);
 
 /* Pointwise aggregated attention over a jagged batch.  Builds the jagged
@@ -210,10 +212,15 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* args, void* workspace, size_t 
 /* ------------------------------------------------------ scheduler access */
 /* Builds only the jagged tile work list into `workspace` (same layout as the
  * one hstu_attn_fwd builds) and copies it to the HOST array `items_out`
- * (capacity `cap` rows of 4 int32: b, query tile, end of the first key-tile
- * range [0, a_end), second range packed as begin | end << 16).  `count_out`
- * (host) receives the number of items.  Synchronises `stream`.  For tests of
- * the scheduler against a brute-force tile enumeration. */
+ * (capacity `cap` rows of 8 int32 per piece: b, query tile, end of the first
+ * key-tile range [0, a_end), second range packed as begin | end << 16, the
+ * piece's positions in that tile list packed as p0 | p1 << 16, the row
+ * block's first partial slot (-1: not split), the piece index, the number
+ * of pieces of the row block).  A row
+ * block whose tile list is long next to the work per workgroup is split into
+ * pieces over disjoint position ranges.  `count_out` (host) receives the
+ * number of pieces.  Synchronises `stream`.  For tests of the scheduler
+ * against a brute-force tile enumeration. */
 hstu_status hstu_attn_schedule(const hstu_attn_args* args, void* workspace, size_t workspace_bytes,
                                int32_t* items_out, int64_t cap, int64_t* count_out,
                                int32_t* tile_m_out, int32_t* tile_n_out, void* stream);

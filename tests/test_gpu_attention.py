@@ -113,6 +113,20 @@ def test_bf16_mfalcon_edge_counts():
     _check_full(x, "bf16 M-FALCON edge counts")
 
 
+@pytest.mark.parametrize("with_u", [True, False])
+def test_bf16_split_row_blocks(with_u):
+    """Few, long row blocks: the scheduler splits them over their key tiles.
+    The partial sums are added up by the LN*U epilogue when it runs, else by
+    the combine pass; O (and Y) must match the oracle either way."""
+    from hstu_sequential_transducer_causal_amd import ops
+    x = synth.config(3, batch=2, max_len=1200)
+    d = DeviceAttn(x)
+    items, _, _ = ops.hstu_attn_schedule(d.q, d.k, d.v, d.offsets, d.ts, d.rab_pos, d.rab_time,
+                                         max_seq_len=d.max_seq_len)
+    assert (items[:, 5] >= 0).any(), "this case is meant to split row blocks"
+    _check_full(x, f"bf16 split blocks, {'epilogue' if with_u else 'combine pass'}", with_u=with_u)
+
+
 @pytest.mark.parametrize("cfg,seqs", [(2, [0, 17, 63]), (3, [0, 5, 15])])
 def test_full_size_sampled_sequences(cfg, seqs):
     """The full workload on the GPU, checked on whole sampled sequences (each

@@ -24,17 +24,36 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _tile_list(a_end, kb):
+    return list(range(a_end)) + list(range(kb & 0xFFFF, kb >> 16))
+
+
 def _items_to_tiles(items):
+    """Tiles covered by the pieces, checking that the pieces of each row block
+    split its tile list into disjoint, complete position ranges."""
     tiles = set()
-    for b, qt, a_end, kb in items.tolist():
-        for kt in range(a_end):
+    cover = {}
+    for b, qt, a_end, kb, pr, slot, k, n in items.tolist():
+        lst = _tile_list(a_end, kb)
+        p0, p1 = pr & 0xFFFF, pr >> 16
+        assert 0 <= p0 < p1 <= len(lst)
+        for kt in lst[p0:p1]:
             tiles.add((b, qt, kt))
-        for kt in range(kb & 0xFFFF, kb >> 16):
-            tiles.add((b, qt, kt))
+        cover.setdefault((b, qt), []).append((p0, p1, slot, k, len(lst), n))
+    for key, parts in cover.items():
+        parts.sort()
+        assert parts[0][0] == 0 and parts[-1][1] == parts[-1][4], key
+        assert all(parts[i][1] == parts[i + 1][0] for i in range(len(parts) - 1)), key
+        assert all(p[5] == len(parts) for p in parts), key     # every piece knows the count
+        if len(parts) == 1:
+            assert parts[0][2] == -1 and parts[0][3] == 0, key     # not split
+        else:
+            assert len({p[2] for p in parts}) == 1 and parts[0][2] >= 0, key
+            assert sorted(p[3] for p in parts) == list(range(len(parts))), key
     return tiles
 
 
-@pytest.mark.parametrize("case", ["causal", "mfalcon", "padded", "empty", "cfg3", "f32"])
+@pytest.mark.parametrize("case", ["causal", "mfalcon", "padded", "empty", "cfg3", "cfg4", "f32"])
 def test_schedule_matches_bruteforce_tiles(case):
     from hstu_sequential_transducer_causal_amd import ops
     if case == "causal":
@@ -49,6 +68,8 @@ def test_schedule_matches_bruteforce_tiles(case):
         x = synth.make_attn(5, [0, 0, 5, 0], H=1, d=128, P=64, NT=32, alpha=1.0, dtype="bf16")
     elif case == "cfg3":
         x = synth.config(3)
+    elif case == "cfg4":
+        x = synth.config(4)   # long row blocks next to the work per workgroup: split pieces
     else:
         x = synth.config(1, batch=11)
     d = DeviceAttn(x)
@@ -60,11 +81,11 @@ def test_schedule_matches_bruteforce_tiles(case):
                                        num_candidates=x.num_candidates).tolist()))
     log(f"schedule {case}: {len(items)} items, {len(got)} tiles (tile {tm}x{tn})")
     assert got == want
-    # one item per (sequence, query tile), no duplicates
-    keys = [(int(b), int(qt)) for b, qt, _, _ in items.tolist()]
+    # no duplicate pieces
+    keys = [(int(r[0]), int(r[1]), int(r[6])) for r in items.tolist()]
     assert len(keys) == len(set(keys))
-    # longest first
-    cost = [a + ((kb >> 16) - (kb & 0xFFFF)) for _, _, a, kb in items.tolist()]
+    # longest piece first
+    cost = [(r[4] >> 16) - (r[4] & 0xFFFF) for r in items.tolist()]
     assert cost == sorted(cost, reverse=True)
 
 

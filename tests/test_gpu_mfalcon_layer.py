@@ -43,23 +43,36 @@ def _scores_candidates_only(x):
 
 
 @pytest.mark.parametrize("case", ["ragged", "cfg4"])
-def test_mfalcon_candidates_only_equals_full_pass(case):
-    """Computing only the query tiles that hold candidate rows gives the very
-    same scores as the full pass (candidates read history K/V, never history
-    outputs), including users whose candidates start mid-tile or who have
-    none."""
+def test_mfalcon_candidates_only_scores(case):
+    """Computing only the query tiles that hold candidate rows (candidates read
+    history K/V, never history outputs) gives the oracle's scores, including
+    users whose candidates start mid-tile or who have none.  With few row
+    blocks left the long ones are split over their key tiles (partial sums
+    added in fp32), so the result matches the full pass within tolerance, and
+    exactly where neither pass split."""
     if case == "ragged":
         x = synth.make_attn(52, [100, 300, 129, 256, 40], H=4, d=128, P=1024, NT=32,
                             alpha=1 / 512, dtype="bf16", num_candidates=[1, 200, 65, 0, 40],
                             with_w=True)
+        users = list(range(x.B))
     else:
         x = synth.config(4)
+        users = [0, 7]
     full, _, _ = _scores_gpu(x)
     part = _scores_candidates_only(x)
+    for b in users:
+        c = int(x.num_candidates[b])
+        if c == 0:
+            continue
+        s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
+        sl = slice(s0, s1)
+        ref = oracle.mfalcon_score(x.q[sl], x.k[sl], x.v[sl], x.u[sl], [0, s1 - s0], [c],
+                                   x.ts[sl], x.rab_pos, x.rab_time, x.alpha, x.w, eps=x.eps)
+        assert_close(part[b, :c], ref[0, :c], "bf16", f"candidates-only scores {case} user {b}")
     for b in range(x.B):
         c = int(x.num_candidates[b])
-        assert np.array_equal(part[b, :c], full[b, :c]), b
-    log(f"candidates-only scores identical to the full pass ({case}, B={x.B})")
+        assert_close(part[b, :c], full[b, :c], "bf16", f"candidates-only vs full pass user {b}")
+    log(f"candidates-only scores ({case}, B={x.B}) match the oracle and the full pass")
 
 
 def test_mfalcon_scores_small():
