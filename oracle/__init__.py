@@ -48,6 +48,8 @@ def _lib():
         lib.hstu_oracle_max_threads.restype = ctypes.c_int32
         lib.hstu_oracle_attn.restype = None
         lib.hstu_oracle_ln_gate.restype = None
+        lib.hstu_oracle_attn_bwd.restype = None
+        lib.hstu_oracle_ln_gate_bwd.restype = None
         lib.hstu_oracle_layer.restype = None
         lib.hstu_oracle_mfalcon_score.restype = None
         lib.hstu_oracle_tiles.restype = ctypes.c_int64
@@ -138,6 +140,60 @@ def ln_gate(o, u, eps=1e-5, num_threads=0) -> np.ndarray:
         _ptr(u2, _f64p), ctypes.c_int64(width), ctypes.c_double(eps), _ptr(y, _f64p),
         ctypes.c_int64(width), ctypes.c_int32(num_threads))
     return y
+
+
+def attn_bwd(q, k, v, offsets, ts, rab_pos, rab_time, alpha, dout, *, lengths=None,
+             num_candidates=None, act=ACT_SILU, num_threads=0):
+    """Gradients of the attention core for an upstream gradient ``dout`` of O.
+
+    Returns (dq, dk, dv, drab_pos, drab_time): dq, dk [T, H, d_qk], dv
+    [T, H, d_v] (padding rows 0), and the table gradients shaped like the
+    tables ([P] / [NT] summed over heads when shared, [H, P] / [H, NT] per
+    head).  Chain rule through the forward definition, one (sequence, head)
+    at a time, i then j ascending.  Pinned by central finite differences of
+    ``attn`` (tests/test_oracle_pins.py).
+    """
+    q = _f64(q); k = _f64(k); v = _f64(v); g = _f64(dout)
+    T, H, dqk = q.shape
+    dv_ = v.shape[2]
+    off = _i32(offsets)
+    B = len(off) - 1
+    rp = _f64(rab_pos); rt = _f64(rab_time)
+    P = rp.shape[-1]; NT = rt.shape[-1]
+    rps = P if rp.ndim == 2 else 0
+    rts = NT if rt.ndim == 2 else 0
+    dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
+    drp = np.zeros_like(rp); drt = np.zeros_like(rt)
+    tsa = np.ascontiguousarray(ts, dtype=np.int64)
+    ln = _i32(lengths); nc = _i32(num_candidates)
+    _lib().hstu_oracle_attn_bwd(
+        ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(dqk), ctypes.c_int32(dv_),
+        _ptr(off, _i32p), _ptr(ln, _i32p), _ptr(nc, _i32p),
+        _ptr(q, _f64p), _ptr(k, _f64p), _ptr(v, _f64p), ctypes.c_int64(H * dqk),
+        ctypes.c_int64(H * dv_), _ptr(tsa, _i64p),
+        _ptr(rp, _f64p), ctypes.c_int32(P), _ptr(rt, _f64p), ctypes.c_int32(NT),
+        ctypes.c_int64(rps), ctypes.c_int64(rts), ctypes.c_double(alpha), ctypes.c_int32(act),
+        _ptr(g, _f64p), _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p),
+        _ptr(drp, _f64p), _ptr(drt, _f64p), ctypes.c_int32(num_threads))
+    return dq, dk, dv, drp, drt
+
+
+def ln_gate_bwd(o, u, dy, eps=1e-5, num_threads=0):
+    """Gradients (dO, dU) of Y = LayerNorm(o) * u for an upstream gradient dy
+    (rows of any width; closed form of the LayerNorm derivative, pinned by
+    finite differences of ``ln_gate``)."""
+    o2 = _f64(o).reshape(o.shape[0], -1)
+    u2 = _f64(u).reshape(u.shape[0], -1)
+    g2 = _f64(dy).reshape(dy.shape[0], -1)
+    rows, width = o2.shape
+    do = np.empty_like(o2)
+    du = np.empty_like(o2)
+    _lib().hstu_oracle_ln_gate_bwd(
+        ctypes.c_int64(rows), ctypes.c_int32(width), _ptr(o2, _f64p), ctypes.c_int64(width),
+        _ptr(u2, _f64p), ctypes.c_int64(width), _ptr(g2, _f64p), ctypes.c_int64(width),
+        ctypes.c_double(eps), _ptr(do, _f64p), ctypes.c_int64(width), _ptr(du, _f64p),
+        ctypes.c_int64(width), ctypes.c_int32(num_threads))
+    return do, du
 
 
 def layer(x, w1, w2, offsets, ts, rab_pos, rab_time, alpha, H, d, *, b1=None, b2=None,

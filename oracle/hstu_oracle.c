@@ -1,7 +1,8 @@
 /*
  * hstu_oracle.c -- fp64 CPU oracle of the HSTU pointwise aggregated attention
- * path (attention core, LayerNorm*U gate, layer with f1/f2, M-FALCON scores,
- * and a brute-force enumeration of the non-empty (query tile, key tile) set).
+ * path (attention core and its gradients, LayerNorm*U gate and its gradients,
+ * layer with f1/f2, M-FALCON scores, and a brute-force enumeration of the
+ * non-empty (query tile, key tile) set).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this file's library.  It shares no code,
@@ -203,6 +204,162 @@ void hstu_oracle_ln_gate(int64_t rows, int32_t width,
         var /= (double)width;
         double inv = 1.0 / sqrt(var + eps);
         for (int32_t c = 0; c < width; ++c) yrow[c] = (orow[c] - mean) * inv * urow[c];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention core, gradients.  With dO = dLoss/dO given, the chain rule      */
+/* through O[i] = alpha * sum_j act(S_ij) V[j] gives, per visible pair:      */
+/*   dV[j]           += alpha * act(S_ij) * dO[i]                            */
+/*   G_ij             = alpha * <dO[i], V[j]> * act'(S_ij)   (= dLoss/dS_ij) */
+/*   dQ[i]           += G_ij * K[j]          dK[j] += G_ij * Q[i]            */
+/*   drab_pos[pb(i,j)] += G_ij             drab_time[tb(i,j)] += G_ij       */
+/* act' of SiLU: sigma(x) (1 + x (1 - sigma(x))); of the identity: 1.         */
+/* The S_ij, masks and buckets are those of the forward above ("生成式推荐   */
+/* （一）：HSTU", sections "高性能自注意力Encoder：HSTU" and "Pointwise      */
+/* aggregated attention").  Valid rows of dQ, dK, dV are overwritten          */
+/* (padding rows untouched); the table gradients are overwritten: [P] / [NT]  */
+/* summed over heads for shared tables, [H][P] / [H][NT] for per-head ones.   */
+/* Loops run i ascending, then j ascending, within one (sequence, head).      */
+/* ------------------------------------------------------------------------ */
+static double act_value(double s, int32_t act) {
+    return act == ORACLE_ACT_IDENTITY ? s : hstu_oracle_silu(s);
+}
+
+static double act_slope(double s, int32_t act) {
+    if (act == ORACLE_ACT_IDENTITY) return 1.0;
+    double sg = 1.0 / (1.0 + exp(-s));
+    return sg * (1.0 + s * (1.0 - sg));
+}
+
+void hstu_oracle_attn_bwd(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                          const int32_t* offsets, const int32_t* lengths,
+                          const int32_t* num_candidates,
+                          const double* q, const double* k, const double* v,
+                          int64_t qk_stride, int64_t v_stride,
+                          const int64_t* timestamps,
+                          const double* rab_pos, int32_t num_pos_buckets,
+                          const double* rab_time, int32_t num_time_buckets,
+                          int64_t rab_pos_head_stride, int64_t rab_time_head_stride,
+                          double alpha, int32_t act, const double* dout,
+                          double* dq, double* dk, double* dv,
+                          double* drab_pos, double* drab_time, int32_t num_threads) {
+    set_threads(num_threads);
+    const int32_t P = num_pos_buckets, NT = num_time_buckets;
+    /* per-head table gradients, summed over heads at the end when shared */
+    double* gp = (double*)calloc((size_t)H * (size_t)P, sizeof(double));
+    double* gt = (double*)calloc((size_t)H * (size_t)NT, sizeof(double));
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t L = seq_len(offsets, lengths, b);
+        int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+        int64_t base = offsets[b];
+        for (int32_t r = 0; r < L; ++r) {
+            for (int32_t c = 0; c < H * d_qk; ++c) {
+                dq[(base + r) * qk_stride + c] = 0.0;
+                dk[(base + r) * qk_stride + c] = 0.0;
+            }
+            for (int32_t c = 0; c < H * d_v; ++c) dv[(base + r) * v_stride + c] = 0.0;
+        }
+        /* heads are independent: each writes its own columns and table row */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int32_t h = 0; h < H; ++h) {
+            const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
+            const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
+            for (int32_t i = 0; i < L; ++i) {
+                const double* qi = q + (base + i) * qk_stride + (int64_t)h * d_qk;
+                const double* gi = dout + (base + i) * v_stride + (int64_t)h * d_v;
+                double* dqi = dq + (base + i) * qk_stride + (int64_t)h * d_qk;
+                for (int32_t j = 0; j < L; ++j) {
+                    if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
+                    const double* kj = k + (base + j) * qk_stride + (int64_t)h * d_qk;
+                    const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
+                    int32_t pb = hstu_oracle_pos_bucket(i, j, n_hist, P);
+                    int32_t tb = hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j], NT);
+                    double s = rp[pb] + rt[tb];
+                    for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
+                    double a = act_value(s, act);
+                    double* dvj = dv + (base + j) * v_stride + (int64_t)h * d_v;
+                    double dov = 0.0;
+                    for (int32_t c = 0; c < d_v; ++c) {
+                        dvj[c] += alpha * a * gi[c];
+                        dov += gi[c] * vj[c];
+                    }
+                    double g = alpha * dov * act_slope(s, act);
+                    double* dkj = dk + (base + j) * qk_stride + (int64_t)h * d_qk;
+                    for (int32_t c = 0; c < d_qk; ++c) {
+                        dqi[c] += g * kj[c];
+                        dkj[c] += g * qi[c];
+                    }
+                    gp[(int64_t)h * P + pb] += g;
+                    gt[(int64_t)h * NT + tb] += g;
+                }
+            }
+        }
+    }
+    if (rab_pos_head_stride > 0) {
+        for (int64_t e = 0; e < (int64_t)H * P; ++e) drab_pos[e] = gp[e];
+    } else {
+        for (int32_t e = 0; e < P; ++e) {
+            double t = 0.0;
+            for (int32_t h = 0; h < H; ++h) t += gp[(int64_t)h * P + e];
+            drab_pos[e] = t;
+        }
+    }
+    if (rab_time_head_stride > 0) {
+        for (int64_t e = 0; e < (int64_t)H * NT; ++e) drab_time[e] = gt[e];
+    } else {
+        for (int32_t e = 0; e < NT; ++e) {
+            double t = 0.0;
+            for (int32_t h = 0; h < H; ++h) t += gt[(int64_t)h * NT + e];
+            drab_time[e] = t;
+        }
+    }
+    free(gp);
+    free(gt);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gate gradients.  With y = xhat (.) u, xhat = (o - mean) / sqrt(var + eps) */
+/* over the row and dY given:                                                */
+/*   dU = xhat (.) dY;   g = dY (.) u;                                       */
+/*   dO = (g - mean(g) - xhat * mean(g (.) xhat)) / sqrt(var + eps)          */
+/* (the derivative of a LayerNorm without affine parameters, biased          */
+/* variance, of the forward gate above).                                     */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_ln_gate_bwd(int64_t rows, int32_t width,
+                             const double* o, int64_t o_stride,
+                             const double* u, int64_t u_stride,
+                             const double* dy, int64_t dy_stride, double eps,
+                             double* dout, int64_t dout_stride,
+                             double* du, int64_t du_stride, int32_t num_threads) {
+    set_threads(num_threads);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* orow = o + r * o_stride;
+        const double* urow = u + r * u_stride;
+        const double* dyrow = dy + r * dy_stride;
+        double mean = 0.0;
+        for (int32_t c = 0; c < width; ++c) mean += orow[c];
+        mean /= (double)width;
+        double var = 0.0;
+        for (int32_t c = 0; c < width; ++c) var += (orow[c] - mean) * (orow[c] - mean);
+        var /= (double)width;
+        double inv = 1.0 / sqrt(var + eps);
+        double mg = 0.0, mgx = 0.0;
+        for (int32_t c = 0; c < width; ++c) {
+            double xh = (orow[c] - mean) * inv;
+            double g = dyrow[c] * urow[c];
+            du[r * du_stride + c] = xh * dyrow[c];
+            mg += g;
+            mgx += g * xh;
+        }
+        mg /= (double)width;
+        mgx /= (double)width;
+        for (int32_t c = 0; c < width; ++c) {
+            double xh = (orow[c] - mean) * inv;
+            double g = dyrow[c] * urow[c];
+            dout[r * dout_stride + c] = inv * (g - mg - xh * mgx);
+        }
     }
 }
 
