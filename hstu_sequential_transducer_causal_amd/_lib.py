@@ -62,6 +62,22 @@ class MfalconArgs(ctypes.Structure):
     ]
 
 
+class AttnBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("attn", AttnArgs),
+        ("dy", _vp), ("dy_stride", _i64),
+        ("dout", _vp), ("dout_stride", _i64),
+        ("dq", _vp), ("dq_stride", _i64),
+        ("dk", _vp), ("dk_stride", _i64),
+        ("dv", _vp), ("dv_stride", _i64),
+        ("du", _vp), ("du_stride", _i64),
+        ("drab_pos", _vp), ("drab_time", _vp),
+        ("ev_dq_begin", _vp), ("ev_dq_end", _vp),
+        ("ev_dkv_begin", _vp), ("ev_dkv_end", _vp),
+    ]
+
+
 class LayerArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32),
@@ -84,6 +100,7 @@ EXPORTS = [
     "hstu_attn_workspace_bytes", "hstu_attn_fwd",
     "hstu_mfalcon_workspace_bytes", "mfalcon_score",
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
+    "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
     "hstu_attn_schedule",
 ]
 
@@ -122,6 +139,10 @@ def load(path: str = LIB_PATH):
     lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
     lib.hstu_layer_fwd.restype = _i32
     lib.hstu_layer_fwd.argtypes = [ctypes.POINTER(LayerArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.hstu_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnBwdArgs)]
+    lib.hstu_attn_bwd.restype = _i32
+    lib.hstu_attn_bwd.argtypes = [ctypes.POINTER(AttnBwdArgs), _vp, ctypes.c_size_t, _vp]
     lib.hstu_attn_schedule.restype = _i32
     lib.hstu_attn_schedule.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t,
                                        ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64),

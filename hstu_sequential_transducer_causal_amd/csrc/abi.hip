@@ -154,9 +154,10 @@ Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
     return s;
 }
 
-hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream, bool cand_only = false) {
+hstu::SchedArgs make_sched_args(const hstu_attn_args* a, const Sched& s, bool cand_only) {
     hstu::SchedArgs sa;
     sa.cand_only = cand_only ? 1 : 0;
+    sa.kv_mode = 0;
     sa.B = a->B;
     sa.max_seq_len = a->max_seq_len;
     sa.cap = (int64_t)s.layout.cap;
@@ -179,7 +180,11 @@ hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream
     sa.stats = s.stats;
     sa.nblk = s.layout.nblk;
     sa.cap_blk = bf16 ? (int64_t)s.layout.cap_blk : 0;
-    return hstu::launch_sched(sa, stream);
+    return sa;
+}
+
+hipError_t run_sched(const hstu_attn_args* a, const Sched& s, hipStream_t stream, bool cand_only = false) {
+    return hstu::launch_sched(make_sched_args(a, s, cand_only), stream);
 }
 
 hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream) {
@@ -259,6 +264,79 @@ hipError_t run_ln_gate(const hstu_attn_args* a, const Sched& s, const float* w, 
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- gradients
+
+hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
+    if (!g) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (g->struct_size != sizeof(hstu_attn_bwd_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_attn_bwd_args) %zu", g->struct_size,
+                    sizeof(hstu_attn_bwd_args));
+    const bool with_dy = g->dy != nullptr;
+    hstu_attn_args a = g->attn;
+    a.y = nullptr;
+    if (!with_dy && a.o == nullptr) {   // O is read only to differentiate the gate
+        a.o = const_cast<void*>(a.v);
+        a.o_stride = a.v_stride;
+    }
+    hstu_status st = validate_attn(&a, with_dy);
+    if (st != HSTU_OK) return st;
+    if (a.dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "gradients need bf16 inputs (d = 128)");
+    if (!hstu::attn_bwd_tables_fit(a.num_pos_buckets, a.num_time_buckets))
+        return fail(HSTU_ERR_UNSUPPORTED, "gradients support num_pos_buckets + num_time_buckets up to ~4100");
+    const int64_t hd = int64_t(a.H) * a.d_v;
+    if (g->dq_stride < hd || g->dk_stride < hd || g->dv_stride < hd)
+        return fail(HSTU_ERR_ARG, "dq/dk/dv stride < H*d");
+    if (with_dy && (g->dy_stride < hd || (g->du && g->du_stride < hd)))
+        return fail(HSTU_ERR_ARG, "dy/du stride < H*d");
+    if (!with_dy && g->dout_stride < hd) return fail(HSTU_ERR_ARG, "dout stride < H*d");
+    if (a.B > 0) {
+        if (!g->dq || !g->dk || !g->dv) return fail(HSTU_ERR_ARG, "dq, dk and dv must be non-NULL");
+        if (!with_dy && !g->dout) return fail(HSTU_ERR_ARG, "one of dy and dout is required");
+        auto rows_ok = [](const void* p, int64_t stride) { return aligned16(p) && stride % 8 == 0; };
+        if (!rows_ok(g->dq, g->dq_stride) || !rows_ok(g->dk, g->dk_stride) || !rows_ok(g->dv, g->dv_stride) ||
+            (with_dy && !rows_ok(g->dy, g->dy_stride)) || (g->du && !rows_ok(g->du, g->du_stride)) ||
+            (!with_dy && !rows_ok(g->dout, g->dout_stride)))
+            return fail(HSTU_ERR_UNSUPPORTED, "gradient rows must be 16-byte aligned");
+        const int64_t gstride = with_dy ? hd : g->dout_stride;
+        const int64_t widest = std::max(a.q_stride, gstride);
+        if (int64_t(a.max_seq_len) * 2 * widest > int64_t(0x7fffffff))
+            return fail(HSTU_ERR_UNSUPPORTED, "max_seq_len * Q/dO row bytes must stay below 2^31");
+    }
+    return HSTU_OK;
+}
+
+struct BwdWs {
+    hstu::SchedLayout q, kv;   // query-major and key-major work lists
+    size_t dout, part, total;
+};
+
+BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
+    const hstu_attn_args& a = g->attn;
+    BwdWs w;
+    w.q = hstu::sched_layout(a.B, a.H, a.max_seq_len, hstu::kBf16TileM, 0, a.num_rows, 0);
+    w.kv = hstu::sched_layout(a.B, a.H, a.max_seq_len, hstu::kBf16TileM, 0, 0, w.q.bytes);
+    w.dout = align256(w.kv.bytes);
+    w.part = align256(w.dout + (g->dy ? size_t(a.num_rows) * size_t(a.H) * size_t(a.d_v) * 2 : 0));
+    w.total = align256(w.part + sizeof(float) * hstu::attn_bwd_rab_part_floats(
+                                                    (int64_t)w.q.cap, a.H, a.num_pos_buckets, a.num_time_buckets));
+    return w;
+}
+
+Sched carve_layout(const hstu::SchedLayout& l, void* ws) {
+    Sched s;
+    s.layout = l;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    s.ctrl = reinterpret_cast<int32_t*>(w + l.off_ctrl);
+    s.qscan = reinterpret_cast<int32_t*>(w + l.off_qscan);
+    s.items = reinterpret_cast<hstu::WorkItem*>(w + l.off_items);
+    s.split = reinterpret_cast<hstu::SplitBlock*>(w + l.off_split);
+    s.partial = nullptr;
+    s.stats = reinterpret_cast<uint32_t*>(w + l.off_stats);
+    s.enc = reinterpret_cast<uint32_t*>(w + l.off_enc);
+    s.rowmap = nullptr;
+    return s;
+}
 
 }  // namespace
 
@@ -468,6 +546,107 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     g2.silu = 0;
     e = hstu::launch_gemm_bf16(g2, stream);
     if (e != hipSuccess) return device_error(e, "f2 launch");
+    return ok();
+}
+
+size_t hstu_attn_bwd_workspace_bytes(const hstu_attn_bwd_args* g) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_bwd(g);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return bwd_ws(g).total;
+}
+
+hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_bwd(g);
+    if (st != HSTU_OK) return st;
+    const hstu_attn_args* a = &g->attn;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int P = a->num_pos_buckets, NT = a->num_time_buckets;
+    if (a->B == 0) {   // empty batch: zero table gradients
+        const int hp = a->rab_pos_head_stride > 0 ? a->H : 1, ht = a->rab_time_head_stride > 0 ? a->H : 1;
+        hipError_t e = hipSuccess;
+        if (g->drab_pos) e = hipMemsetAsync(g->drab_pos, 0, sizeof(float) * size_t(hp) * P, stream);
+        if (e == hipSuccess && g->drab_time) e = hipMemsetAsync(g->drab_time, 0, sizeof(float) * size_t(ht) * NT, stream);
+        return e == hipSuccess ? ok() : device_error(e, "clearing the table gradients");
+    }
+    const BwdWs w = bwd_ws(g);
+    st = check_workspace(ws, ws_bytes, w.total);
+    if (st != HSTU_OK) return st;
+    uint8_t* wb = static_cast<uint8_t*>(ws);
+    const Sched sq = carve_layout(w.q, ws);
+    const Sched skv = carve_layout(w.kv, ws);
+    const int hd = a->H * a->d_v;
+    hipError_t e;
+
+    // upstream gradient of O
+    const void* dout = g->dout;
+    int64_t dout_stride = g->dout_stride;
+    if (g->dy) {
+        hstu::LnGateBwdArgs l;
+        l.B = a->B;
+        l.num_rows = a->num_rows;
+        l.width = hd;
+        l.offsets = a->seq_offsets;
+        l.lengths = a->seq_lengths;
+        l.o = a->o; l.o_stride = a->o_stride;
+        l.u = a->u; l.u_stride = a->u_stride;
+        l.dy = g->dy; l.dy_stride = g->dy_stride;
+        l.dout = wb + w.dout; l.dout_stride = hd;
+        l.du = g->du; l.du_stride = g->du_stride;
+        l.eps = a->ln_eps;
+        e = hstu::launch_ln_gate_bwd(l, stream);
+        if (e != hipSuccess) return device_error(e, "gate gradient launch");
+        dout = wb + w.dout;
+        dout_stride = hd;
+    }
+
+    // work lists: query-major (no split pieces) with the timestamp codes,
+    // then key-major
+    hstu::SchedArgs qa = make_sched_args(a, sq, false);
+    qa.slots = 0;
+    qa.part_slots = 0;
+    e = hstu::launch_sched(qa, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    hstu::SchedArgs ka = make_sched_args(a, skv, false);
+    ka.kv_mode = 1;
+    ka.slots = 0;
+    ka.part_slots = 0;
+    ka.enc = nullptr;
+    ka.cap_blk = 0;
+    e = hstu::launch_sched(ka, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+
+    hstu::AttnBwdArgs b;
+    b.H = a->H;
+    b.offsets = a->seq_offsets; b.lengths = a->seq_lengths; b.ncand = a->num_candidates;
+    b.q = a->q; b.q_stride = a->q_stride;
+    b.k = a->k; b.k_stride = a->k_stride;
+    b.v = a->v; b.v_stride = a->v_stride;
+    b.dout = dout; b.dout_stride = dout_stride;
+    b.ts = a->timestamps;
+    b.rab_pos = a->rab_pos; b.P = P; b.rp_head_stride = a->rab_pos_head_stride;
+    b.rab_time = a->rab_time; b.NT = NT; b.rt_head_stride = a->rab_time_head_stride;
+    b.alpha = a->alpha;
+    b.act = a->act;
+    b.dq = g->dq; b.dq_stride = g->dq_stride;
+    b.dk = g->dk; b.dk_stride = g->dk_stride;
+    b.dv = g->dv; b.dv_stride = g->dv_stride;
+    b.drab_pos = g->drab_pos; b.drab_time = g->drab_time;
+    b.q_items = sq.items; b.q_ctrl = sq.ctrl;
+    b.kv_items = skv.items; b.kv_ctrl = skv.ctrl;
+    b.nblk = w.q.nblk;
+    b.stats = sq.stats;
+    b.enc = sq.enc;
+    b.num_rows = a->num_rows;
+    b.rab_part = reinterpret_cast<float*>(wb + w.part);
+    b.ev_dq_begin = static_cast<hipEvent_t>(g->ev_dq_begin);
+    b.ev_dq_end = static_cast<hipEvent_t>(g->ev_dq_end);
+    b.ev_dkv_begin = static_cast<hipEvent_t>(g->ev_dkv_begin);
+    b.ev_dkv_end = static_cast<hipEvent_t>(g->ev_dkv_end);
+    e = hstu::launch_attn_bwd(b, stream);
+    if (e != hipSuccess) return device_error(e, "gradient kernels launch");
     return ok();
 }
 

@@ -44,6 +44,7 @@
 
 #include "internal.h"
 #include "hstu_device.h"
+#include "tile_ops.h"
 
 namespace hstu {
 
@@ -53,11 +54,8 @@ constexpr int BM = kBf16TileM;   // 128 query rows per item
 constexpr int BN = kBf16TileN;   // 32 keys per tile
 constexpr int HD = 128;          // head dim
 constexpr int kThreads = 256;
-constexpr int kRowBytes = HD * 2;
 constexpr int kStages = 4;       // LDS ring depth: tiles t .. t+3 in flight
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
     int H;
@@ -92,83 +90,6 @@ struct Smem {
     int32_t item[8];
     int32_t work;
 };
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ uint32_t uniu(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 4 bf16 of V^T through the LDS transpose read: within each 16-lane group,
-// output lane i, element k comes from input lane 4k + i/4, element i % 4.
-__device__ __forceinline__ u32x2 ds_read_tr(const uint8_t* p) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p);
-    return __builtin_bit_cast(u32x2, r);
-}
-
-__device__ __forceinline__ int kswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 15)) << 4); }
-__device__ __forceinline__ int vswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row & 3) << 2)) << 4); }
-
-// Each block opens with 5 wait states: the compiler does not look inside
-// inline assembly for hazards, and a VALU write of an SGPR (a v_readlane
-// reloading a spilled descriptor, say) needs 5 before a vector memory
-// instruction may read that SGPR (the M0 write needs 1).
-//
-// The tile loads are issued from inline assembly, so the compiler sees no
-// LDS write it has to wait for: it cannot tell the ring stage being filled
-// from the one being read, and with the loads visible to it would wait for
-// every load in flight before each LDS read.  The waits are explicit
-// instead: the vmcnt below before a stage is read, then a bare s_barrier (the
-// memory clobber keeps LDS accesses on their side of it).  Loads complete in
-// issue order, and loads the compiler issues itself after these only make
-// its own vmcnt waits stricter, never looser.
-__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "{m0}"(lds)
-                 : "memory");
-}
-__device__ __forceinline__ void dma4(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
-    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds)
-                 : "memory");
-}
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// This wave's LDS accesses (ordinary stores included) are complete.
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// Barrier after which every wave sees the others' ordinary LDS stores; vector
-// memory operations (the output stores of the previous item) stay in flight.
-__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Buffer resource: base, stride 0, num_records bytes (accesses at or past it
-// read as zero).
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    u32x4 r;
-    r[0] = uniu((uint32_t)a);
-    r[1] = uniu((uint32_t)(a >> 32) & 0xffffu);
-    r[2] = uniu(bytes);
-    r[3] = 0x00020000u;
-    return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const lds_void*)p;
-}
-
-// vmcnt(n) with the other counters left alone (n <= 15).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-        case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
 
 // Per-item state of the tile loads.  Wave w fills key rows 8w .. 8w+7 of the
 // K and V tiles with 2 buffer loads each: lane l of load m writes 16 bytes at
@@ -209,27 +130,6 @@ __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage,
     issue_v(d, s, stage, kt, wave);
     if (wave == 0) issue_codes(d, s, stage, kt, L, lane);
 }
-
-// B operand fragments of O += A V for 16-key chunk c of a V tile: for each
-// 32-column block nb, keys c*16 + 8 h2' .. (two transposed reads of 4 keys x
-// 4 columns per 16-lane group).
-__device__ __forceinline__ void read_v_chunk(const uint8_t* v_lds, int c, int lane, u32x4 (&vf)[4]) {
-    const int m = lane & 15;
-    const int dsub = ((lane >> 4) & 1) * 16;
-    const int key0 = c * 16 + 4 * (lane >> 5) + (m >> 2);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int col = nb * 32 + dsub + 4 * (m & 3);      // element column
-        const int chunk = col >> 3;
-        const int within = (col & 7) * 2;
-        const u32x2 v0 = ds_read_tr(v_lds + vswz(key0, chunk) + within);
-        const u32x2 v1 = ds_read_tr(v_lds + vswz(key0 + 8, chunk) + within);
-        vf[nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
-    }
-}
-
-// Bucket index (leading zeros of 2|dt| + 1) of an encoded gap 2|dt|.
-__device__ __forceinline__ uint32_t clz_gap(uint32_t gap2) { return __builtin_clz(gap2 + 1u); }
 
 template <bool kSilu>
 __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const void* ws_base, uint32_t ws_bytes) {

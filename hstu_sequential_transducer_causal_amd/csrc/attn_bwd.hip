@@ -1,0 +1,761 @@
+// attn_bwd.hip -- gradients of the attention core for gfx950: bf16 inputs,
+// fp32 accumulation, d_qk = d_v = 128.
+//
+// The forward ("生成式推荐（一）：HSTU", sections "高性能自注意力Encoder：HSTU"
+// and "Pointwise aggregated attention") computes, per head and visible pair
+// (i, j) of a jagged sequence,
+//   S_ij = <Q_i, K_j> + rab_pos[pb(i, j)] + rab_time[tb(i, j)],
+//   O_i  = alpha * sum_j SiLU(S_ij) V_j.
+// With dO = dLoss/dO given, the chain rule gives
+//   dV_j += alpha SiLU(S_ij) dO_i,
+//   G_ij  = alpha <dO_i, V_j> SiLU'(S_ij)            (= dLoss/dS_ij),
+//   dQ_i += G_ij K_j,   dK_j += G_ij Q_i,
+//   drab_pos[pb(i, j)] += G_ij,   drab_time[tb(i, j)] += G_ij,
+// with SiLU'(x) = s + SiLU(x) (1 - s), s = sigmoid(x) (identity: 1).
+//
+// Two persistent kernels, with no atomics on the gradients of Q, K and V:
+//   * attn_bwd_dq_kernel: one work item = 128 query rows x 1 head (the
+//     forward's work list).  Per 32-key tile: S^T = K Q^T and (dO V^T)^T =
+//     V dO^T with Q and dO in registers, then G^T and dQ += G K.  G is also
+//     summed by position and time bucket into LDS histograms, written as one
+//     partial row per work item and added up in a fixed order by
+//     rab_grad_reduce_kernel (so the table gradients do not depend on which
+//     workgroup took which item).
+//   * attn_bwd_dkv_kernel: one work item = 128 keys x 1 head (a key-major
+//     work list: the 32-row query tiles that see the keys).  Per query tile:
+//     S = Q K^T and dO V^T with K and V in registers, then dV += A^T dO and
+//     dK += G^T Q (A = SiLU(S) masked).
+// Both recompute S.  A tile feeds two products that read it in different
+// orders (rows as M, and rows as the contraction); it is staged twice, in the
+// two swizzles those reads are conflict-free in.  Tiles arrive by
+// direct-to-LDS buffer loads two tiles ahead of use (a 3-stage ring).  The
+// relative bias takes the forward's block-uniform shortcuts (a constant time
+// bucket, a fully clamped position bucket) and otherwise reads per element.
+#include <hip/hip_ext.h>
+
+#include "internal.h"
+#include "hstu_device.h"
+#include "tile_ops.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int HD = 128;
+constexpr int kThreads = 256;
+constexpr int kBlk = 128;          // query rows (dq) or keys (dkv) per work item
+constexpr int kStages = 3;         // tiles t .. t+2 in flight
+constexpr int kTileBytes = 32 * kRowBytes;
+
+struct BwdParams {
+    int H;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const int32_t* ncand;
+    const uint16_t* q; int64_t qs;
+    const uint16_t* k; int64_t ks;
+    const uint16_t* v; int64_t vs;
+    const uint16_t* g; int64_t gs;          // dO
+    const int64_t* ts;
+    const float* rab_pos; int P; int rp_hs;
+    const float* rab_time; int NT; int rt_hs;
+    float alpha;
+    int act;                                // 0: SiLU, 1: identity
+    uint16_t* dq; int64_t dqs;
+    uint16_t* dk; int64_t dks;
+    uint16_t* dv; int64_t dvs;
+    const WorkItem* items;
+    const int32_t* ctrl;
+    int32_t* cursor;
+    int nblk;
+    const uint32_t* stats;
+    const uint32_t* enc;
+    float* rab_part;                        // [work][P + NT] (dq kernel)
+};
+
+// Small LDS state after the tile ring.
+struct Small {
+    uint32_t codes[kStages][64];   // the streamed tile's 32 row codes (the loads write 64 lanes)
+    float tt_fast[32];             // by leading-zero count of 2|dt| + 1
+    float tt_wide[65];             // by bit length of |dt|
+    int32_t item[8];
+    int32_t work;
+};
+
+template <int kTiles>
+__device__ __forceinline__ Small& small_of(uint8_t* smem) {
+    return *reinterpret_cast<Small*>(smem + kTiles * kStages * kTileBytes);
+}
+template <int kTiles>
+__device__ __forceinline__ float* ptab_of(uint8_t* smem) {
+    return reinterpret_cast<float*>(smem + kTiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15)));
+}
+
+// Loads of one 32-row tile of a [rows][128] bf16 matrix (one head's columns of
+// one sequence) into a ring stage: wave w writes tile rows 8w .. 8w+7 with two
+// 1 KiB buffer loads; lane l of load m writes row 8w + 4m + l / 16 at physical
+// chunk l % 16, so it fetches the logical chunk the swizzle puts there.
+struct TileSrc {
+    u32x4 rs;
+    uint32_t off[2];       // per-lane byte offsets of the two loads
+    uint32_t tile_bytes;   // scalar step per 32-row tile
+};
+
+__device__ __forceinline__ TileSrc tile_src(const uint16_t* base, int64_t stride, int L, int lane, int wave,
+                                            bool vlayout) {
+    TileSrc t;
+    t.rs = make_rsrc(base, (uint32_t)(L * stride * 2));
+    const int pc = lane & 15;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int r = 8 * wave + 4 * m + (lane >> 4);
+        const int c = vlayout ? (pc ^ ((r & 3) << 2)) : (pc ^ (r & 15));
+        t.off[m] = (uint32_t)(r * stride * 2 + c * 16);
+    }
+    t.tile_bytes = (uint32_t)(32 * stride * 2);
+    return t;
+}
+
+__device__ __forceinline__ void issue_part(const TileSrc& t, const uint8_t* ring, int stage, int tile, int wave) {
+    const uint32_t l0 = lds_addr(ring) + (uint32_t)(stage * kTileBytes + 2 * wave * 1024);
+    const uint32_t soff = uniu((uint32_t)tile * t.tile_bytes);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) dma16(t.rs, uniu(l0 + m * 1024), t.off[m], soff);
+}
+
+// Wave 0 only: the 32 row codes of tile `tile` (lanes 32-63 write zeros).
+__device__ __forceinline__ void issue_codes(const u32x4& wrs, int64_t enc_row0, Small& s, int stage, int tile,
+                                            int L, int lane) {
+    const int j = tile * 32 + lane;
+    uint32_t off = 0x80000000u;   // out of range: lands as 0
+    if (lane < 32 && j < L) off = (uint32_t)(enc_row0 + 4 * (int64_t)j);
+    dma4(wrs, uniu(lds_addr(s.codes[0]) + (uint32_t)(stage * 64 * 4)), off);
+}
+
+__device__ __forceinline__ void wait_tile(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+        case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+// Keeps a value loaded before the tile loop out of the loop's wait counts:
+// its load is waited for here, once.
+template <typename T>
+__device__ __forceinline__ void settle(T& x) { asm volatile("" : "+v"(x)); }
+
+// Bias tables of head h into LDS: rab_pos in bucket order, and the time
+// table by leading-zero count of 2|dt| + 1 and by bit length of |dt|.
+__device__ __forceinline__ void load_tables(const BwdParams& p, int h, float* ptab, Small& s, int tid) {
+    const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
+    const float* rt = p.rab_time + (int64_t)h * p.rt_hs;
+    for (int e = tid; e < p.P; e += kThreads) ptab[e] = rp[e];
+    if (tid < 32) s.tt_fast[tid] = rt[min(p.NT - 1, 31 - tid)];
+    if (tid < 65) s.tt_wide[tid] = rt[min(p.NT - 1, tid)];
+}
+
+// Time buckets of one 32 x 32 block from the two 32-row blocks' code ranges:
+// the bucket (as a leading-zero count) is the same for every pair when the
+// range of gaps stays within one power of two.
+struct TimeBlock {
+    bool wide;       // some gap needs 64-bit arithmetic
+    bool constant;   // one bucket for the block
+    int cz;          // its leading-zero count
+};
+
+__device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint32_t bmn, uint32_t bmx) {
+    TimeBlock t;
+    t.wide = amn > amx || bmn > bmx;
+    const uint32_t lo = amn >= bmx ? amn - bmx : (bmn >= amx ? bmn - amx : 0u);
+    const uint32_t hi = max(amx >= bmn ? amx - bmn : 0u, bmx >= amn ? bmx - amn : 0u);
+    const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);
+    t.constant = !t.wide && czlo == czhi;
+    t.cz = czlo;
+    return t;
+}
+
+// Activation value and slope: SiLU (x s, s + x s (1 - s) with s = sigmoid(x))
+// or the identity (x, 1).
+__device__ __forceinline__ void act_and_slope(float x, bool silu, float& a, float& slope) {
+    if (silu) {
+        const float e = __builtin_amdgcn_exp2f(-x * kLog2e);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+        a = x * sg;
+        slope = sg + a * (1.0f - sg);
+    } else {
+        a = x;
+        slope = 1.0f;
+    }
+}
+
+// 16 values (the 32x32 accumulator's order) -> two A operands of 16-long
+// contraction chunks.
+__device__ __forceinline__ void pack_a(const float (&x)[16], bf16x8 (&pa)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(x[8 * c + 2 * e], x[8 * c + 2 * e + 1]);
+        pa[c] = __builtin_bit_cast(bf16x8, pk);
+    }
+}
+
+__device__ __forceinline__ bf16x8 load_frag(const uint16_t* p, bool valid) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (valid) z = *reinterpret_cast<const u32x4*>(p);
+    return __builtin_bit_cast(bf16x8, z);
+}
+
+// Block code ranges through the scalar cache (uniform addresses): these loads
+// count in lgkmcnt, so waiting for them never waits for the tile loads.
+typedef const __attribute__((address_space(4))) u32x2* StatsPtr;
+__device__ __forceinline__ StatsPtr stats_ptr(const uint32_t* p) { return (StatsPtr)(uintptr_t)p; }
+
+// Item fetch through the persistent cursor (thread 0), then shared.
+__device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int total_work, int tid) {
+    if (tid == 0) {
+        const int w = atomicAdd(p.cursor, 1);
+        s.work = w;
+        if (w < total_work) {
+            const WorkItem it = p.items[w / p.H];
+            s.item[0] = it.b; s.item[1] = it.qt; s.item[2] = it.a_end; s.item[3] = it.kb;
+            s.item[4] = it.pr;
+        }
+    }
+    lds_sync();
+}
+
+// ---------------------------------------------------------------------------
+// dQ and the table gradients (query-major)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, const void* ws_base, uint32_t ws_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* ring_k = smem;                          // K, kswz: A operand of S^T = K Q^T
+    uint8_t* ring_kt = smem + kStages * kTileBytes;  // K, vswz: B operand of dQ += G K
+    uint8_t* ring_v = smem + 2 * kStages * kTileBytes;   // V, kswz: A operand of V dO^T
+    Small& s = small_of<3>(smem);
+    float* ptab = ptab_of<3>(smem);
+    // one histogram per wave ([P] position, then [NT] time buckets), so that
+    // the order of the additions into each does not depend on how the waves
+    // interleave; added in wave order at the end of the item
+    const int hw = (p.P + p.NT + 3) & ~3;
+    float* hist_all = ptab + ((p.P + 3) & ~3);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uni(tid >> 6);
+    const int l32 = lane & 31;
+    const int h2 = lane >> 5;
+    const int total_work = p.ctrl[0] * p.H;
+    const bool shared_tables = (p.rp_hs == 0) && (p.rt_hs == 0);
+    const bool silu = p.act == 0;
+    const int P = p.P, NT = p.NT;
+    const int per_tile = uni(wave == 0 ? 7 : 6);
+    const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
+    const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
+    int loaded_head = -1;
+
+    float* hist = hist_all + wave * hw;
+    for (int e = tid; e < 4 * hw; e += kThreads) hist_all[e] = 0.0f;
+
+    for (;;) {
+        fetch_item(p, s, total_work, tid);
+        const int w = uni(s.work);
+        if (w >= total_work) break;
+        const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
+        const int kbw = uni(s.item[3]);
+        const int kb_begin = kbw & 0xffff;
+        const int ntiles = uni(s.item[4]) >> 16;
+        const int h = w % p.H;
+        const int64_t row0 = uni(p.offsets[b]);
+        const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
+        const int n = uni(p.ncand ? L - p.ncand[b] : L);
+        const int bbase = b * p.nblk;
+
+        if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
+            load_tables(p, h, ptab, s, tid);
+            loaded_head = h;
+            lds_wait();   // visible to all after the first tile's barrier
+        }
+
+        auto tile_of = [&](int pos) { return pos < a_end ? pos : kb_begin + (pos - a_end); };
+        const TileSrc sk = tile_src(p.k + row0 * p.ks + h * HD, p.ks, L, lane, wave, false);
+        const TileSrc skt = tile_src(p.k + row0 * p.ks + h * HD, p.ks, L, lane, wave, true);
+        const TileSrc sv = tile_src(p.v + row0 * p.vs + h * HD, p.vs, L, lane, wave, false);
+        const int64_t enc_row0 = enc_base + 4 * row0;
+        auto issue = [&](int stage, int tile) {
+            issue_part(sk, ring_k, stage, tile, wave);
+            issue_part(skt, ring_kt, stage, tile, wave);
+            issue_part(sv, ring_v, stage, tile, wave);
+            if (wave == 0) issue_codes(wrs, enc_row0, s, stage, tile, L, lane);
+        };
+#pragma unroll
+        for (int pre = 0; pre < kStages - 1; ++pre)
+            if (pre < ntiles) issue(pre, tile_of(pre));
+
+        // ---- this wave's 32 query rows: Q and dO as B operands (lane = row)
+        const int wrow0 = qt * kBlk + wave * 32;
+        const int i = wrow0 + l32;
+        const bool row_valid = i < L;
+        bf16x8 qf[8], gf[8];
+        {
+            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
+            const uint16_t* gp = p.g + (row0 + i) * p.gs + h * HD + h2 * 8;
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                qf[kc] = load_frag(qp + kc * 16, row_valid);
+                gf[kc] = load_frag(gp + kc * 16, row_valid);
+            }
+        }
+        const int64_t t_first = p.ts[row0];
+        int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
+        uint32_t ei = row_valid ? p.enc[row0 + i] : 0x80000000u;
+        const bool wave_rows = wrow0 < L;
+        const int qblk = bbase + qt * (kBlk / 32) + wave;
+        uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
+        uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+            settle(qf[kc]);
+            settle(gf[kc]);
+        }
+        settle(ti64);
+        settle(ei);
+        settle(rmin);
+        settle(rmax);
+        rmin = uniu(rmin);
+        rmax = uniu(rmax);
+        const int prow = min(i, n);
+        const int prow_min = uni(min(wrow0, n));
+        const int vis_lim = i >= L ? -1 : (i < n ? i : n - 1);
+        const int vis_self = (i >= n && i < L) ? i : -1;
+
+        f32x16 dqa[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dqa[nb][r] = 0.0f;
+
+        const StatsPtr kstats = stats_ptr(p.stats);
+        for (int it = 0; it < ntiles; ++it) {
+            const int kt = tile_of(it);
+            const int j0 = kt * 32;
+            const int stage = it % kStages;
+            const u32x2 kr = kstats[bbase + kt];   // in flight during the wait
+            wait_tile(it + 1 < ntiles ? per_tile : 0);
+            lds_barrier();
+            if (it + kStages - 1 < ntiles) issue((it + kStages - 1) % kStages, tile_of(it + kStages - 1));
+
+            const uint8_t* k_lds = ring_k + stage * kTileBytes;
+            const uint8_t* kt_lds = ring_kt + stage * kTileBytes;
+            const uint8_t* v_lds = ring_v + stage * kTileBytes;
+            const uint32_t* codes = s.codes[stage];
+
+            // block-uniform bias shortcuts
+            const TimeBlock tb = time_block(rmin, rmax, kr[0], kr[1]);
+            const bool pos_clamped = prow_min - min(j0 + 31, n) >= P - 1;
+            float cadd = 0.0f;
+            if (pos_clamped) cadd += ptab[P - 1];
+            if (tb.constant) cadd += s.tt_fast[tb.cz];
+
+            // S^T = K Q^T and (dO V^T)^T = V dO^T: lane = row i, keys
+            // j0 + 8 (r / 4) + 4 h2 + r % 4
+            f32x16 sacc, gacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = 0.0f;
+                gacc[r] = 0.0f;
+            }
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
+                const bf16x8 va = *reinterpret_cast<const bf16x8*>(v_lds + kswz(l32, 2 * kc + h2));
+                sacc = mfma32(ka, qf[kc], sacc);
+                gacc = mfma32(va, gf[kc], gacc);
+            }
+
+            float gv[16];
+            float gsum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                const int j = j0 + c;
+                const bool vis = (j <= vis_lim) | (j == vis_self);
+                int pb = P - 1;
+                float bias = cadd;
+                if (!pos_clamped) {
+                    pb = min(max(prow - min(j, n), 0), P - 1);
+                    bias += ptab[pb];
+                }
+                int tbk = 0;
+                if (!tb.constant) {
+                    if (!tb.wide) {
+                        const uint32_t z = __builtin_clz(sad_u32(ei, codes[c], 1u));
+                        bias += s.tt_fast[z];
+                        tbk = min(NT - 1, 31 - (int)z);
+                    } else {
+                        const int64_t tj = j < L ? p.ts[row0 + j] : t_first;
+                        const int64_t dt = ti64 - tj;
+                        const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
+                        const int bl = bit_length_u64(ad);
+                        bias += s.tt_wide[bl];
+                        tbk = min(NT - 1, bl);
+                    }
+                }
+                float a, slope;
+                act_and_slope(sacc[r] + bias, silu, a, slope);
+                const float g = vis ? gacc[r] * slope : 0.0f;
+                gv[r] = g;
+                gsum += g;
+                if (vis) {
+                    if (!pos_clamped) atomicAdd(&hist[pb], g);
+                    if (!tb.constant) atomicAdd(&hist[P + tbk], g);
+                }
+            }
+            if (pos_clamped || tb.constant) {
+                gsum = wave_sum(gsum);
+                if (lane == 0) {
+                    if (pos_clamped) atomicAdd(&hist[P - 1], gsum);
+                    if (tb.constant) atomicAdd(&hist[P + min(NT - 1, 31 - tb.cz)], gsum);
+                }
+            }
+
+            // dQ += G K over the tile's two 16-key chunks
+            bf16x8 pg[2];
+            pack_a(gv, pg);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 kf[4];
+                read_v_chunk(kt_lds, c, lane, kf);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, kf[nb]), dqa[nb]);
+            }
+        }
+
+        // ---- dQ = alpha * acc for rows < L; lane holds column nb*32 + l32 at
+        //      rows wrow0 + 8 (r / 4) + 4 h2 + r % 4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ro = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (ro < L) {
+                uint16_t* op = p.dq + (row0 + ro) * p.dqs + h * HD + l32;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(p.alpha * dqa[nb][r]);
+            }
+        }
+        // ---- this item's table-gradient histogram -> its partial row
+        lds_sync();
+        float* part = p.rab_part + (int64_t)w * (P + NT);
+        for (int e = tid; e < P + NT; e += kThreads) {
+            part[e] = ((hist_all[e] + hist_all[hw + e]) + hist_all[2 * hw + e]) + hist_all[3 * hw + e];
+            hist_all[e] = hist_all[hw + e] = hist_all[2 * hw + e] = hist_all[3 * hw + e] = 0.0f;
+        }
+        lds_sync();   // histogram cleared and LDS free before the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV (key-major)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, const void* ws_base, uint32_t ws_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* ring_q = smem;                               // Q, kswz: A operand of S = Q K^T
+    uint8_t* ring_qt = smem + kStages * kTileBytes;       // Q, vswz: B operand of dK += G^T Q
+    uint8_t* ring_g = smem + 2 * kStages * kTileBytes;    // dO, kswz: A operand of dO V^T
+    uint8_t* ring_gt = smem + 3 * kStages * kTileBytes;   // dO, vswz: B operand of dV += A^T dO
+    Small& s = small_of<4>(smem);
+    float* ptab = ptab_of<4>(smem);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uni(tid >> 6);
+    const int l32 = lane & 31;
+    const int h2 = lane >> 5;
+    const int total_work = p.ctrl[0] * p.H;
+    const bool shared_tables = (p.rp_hs == 0) && (p.rt_hs == 0);
+    const bool silu = p.act == 0;
+    const int P = p.P;
+    const int per_tile = uni(wave == 0 ? 9 : 8);
+    const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
+    const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
+    int loaded_head = -1;
+
+    for (;;) {
+        fetch_item(p, s, total_work, tid);
+        const int w = uni(s.work);
+        if (w >= total_work) break;
+        const int b = uni(s.item[0]), kblock = uni(s.item[1]);
+        const int kbw = uni(s.item[3]);
+        const int rt_begin = kbw & 0xffff;
+        const int ntiles = uni(s.item[4]) >> 16;
+        const int h = w % p.H;
+        const int64_t row0 = uni(p.offsets[b]);
+        const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
+        const int n = uni(p.ncand ? L - p.ncand[b] : L);
+        const int bbase = b * p.nblk;
+
+        if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
+            load_tables(p, h, ptab, s, tid);
+            loaded_head = h;
+            lds_wait();
+        }
+
+        const TileSrc sq = tile_src(p.q + row0 * p.qs + h * HD, p.qs, L, lane, wave, false);
+        const TileSrc sqt = tile_src(p.q + row0 * p.qs + h * HD, p.qs, L, lane, wave, true);
+        const TileSrc sg = tile_src(p.g + row0 * p.gs + h * HD, p.gs, L, lane, wave, false);
+        const TileSrc sgt = tile_src(p.g + row0 * p.gs + h * HD, p.gs, L, lane, wave, true);
+        const int64_t enc_row0 = enc_base + 4 * row0;
+        auto issue = [&](int stage, int tile) {
+            issue_part(sq, ring_q, stage, tile, wave);
+            issue_part(sqt, ring_qt, stage, tile, wave);
+            issue_part(sg, ring_g, stage, tile, wave);
+            issue_part(sgt, ring_gt, stage, tile, wave);
+            if (wave == 0) issue_codes(wrs, enc_row0, s, stage, tile, L, lane);
+        };
+#pragma unroll
+        for (int pre = 0; pre < kStages - 1; ++pre)
+            if (pre < ntiles) issue(pre, rt_begin + pre);
+
+        // ---- this wave's 32 keys: K and V as B operands (lane = key)
+        const int k0w = kblock * kBlk + wave * 32;
+        const int j = k0w + l32;
+        const bool key_valid = j < L;
+        bf16x8 kf[8], vf[8];
+        {
+            const uint16_t* kp = p.k + (row0 + j) * p.ks + h * HD + h2 * 8;
+            const uint16_t* vp = p.v + (row0 + j) * p.vs + h * HD + h2 * 8;
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                kf[kc] = load_frag(kp + kc * 16, key_valid);
+                vf[kc] = load_frag(vp + kc * 16, key_valid);
+            }
+        }
+        const int64_t t_first = p.ts[row0];
+        int64_t tj64 = key_valid ? p.ts[row0 + j] : t_first;
+        uint32_t ej = key_valid ? p.enc[row0 + j] : 0x80000000u;
+        const bool wave_keys = k0w < L;
+        const int kblk = bbase + kblock * (kBlk / 32) + wave;
+        uint32_t kmn = wave_keys ? p.stats[2 * kblk] : 0x80000000u;
+        uint32_t kmx = wave_keys ? p.stats[2 * kblk + 1] : 0x80000000u;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+            settle(kf[kc]);
+            settle(vf[kc]);
+        }
+        settle(tj64);
+        settle(ej);
+        settle(kmn);
+        settle(kmx);
+        kmn = uniu(kmn);
+        kmx = uniu(kmx);
+        const int pkey = min(j, n);
+        const int pkey_max = uni(min(k0w + 31, n));
+
+        f32x16 dka[4], dva[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dka[nb][r] = 0.0f;
+                dva[nb][r] = 0.0f;
+            }
+
+        const StatsPtr rstats = stats_ptr(p.stats);
+        for (int it = 0; it < ntiles; ++it) {
+            const int rt = rt_begin + it;
+            const int r0 = rt * 32;
+            const int stage = it % kStages;
+            const u32x2 rr = rstats[bbase + rt];   // in flight during the wait
+            wait_tile(it + 1 < ntiles ? per_tile : 0);
+            lds_barrier();
+            if (it + kStages - 1 < ntiles) issue((it + kStages - 1) % kStages, rt + kStages - 1);
+
+            const uint8_t* q_lds = ring_q + stage * kTileBytes;
+            const uint8_t* qt_lds = ring_qt + stage * kTileBytes;
+            const uint8_t* g_lds = ring_g + stage * kTileBytes;
+            const uint8_t* gt_lds = ring_gt + stage * kTileBytes;
+            const uint32_t* codes = s.codes[stage];
+
+            const TimeBlock tb = time_block(rr[0], rr[1], kmn, kmx);
+            const bool pos_clamped = min(r0, n) - pkey_max >= P - 1;
+            float cadd = 0.0f;
+            if (pos_clamped) cadd += ptab[P - 1];
+            if (tb.constant) cadd += s.tt_fast[tb.cz];
+
+            // S = Q K^T and dO V^T: lane = key j, rows r0 + 8 (r / 4) + 4 h2 + r % 4
+            f32x16 sacc, gacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] = 0.0f;
+                gacc[r] = 0.0f;
+            }
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_lds + kswz(l32, 2 * kc + h2));
+                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(g_lds + kswz(l32, 2 * kc + h2));
+                sacc = mfma32(qa, kf[kc], sacc);
+                gacc = mfma32(ga, vf[kc], gacc);
+            }
+
+            float av[16], gv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                const int i = r0 + c;
+                const bool vis = (i < L) & (j < L) & ((i < n) ? (j <= i) : ((j < n) | (j == i)));
+                float bias = cadd;
+                if (!pos_clamped) bias += ptab[min(max(min(i, n) - pkey, 0), P - 1)];
+                if (!tb.constant) {
+                    if (!tb.wide) {
+                        bias += s.tt_fast[__builtin_clz(sad_u32(codes[c], ej, 1u))];
+                    } else {
+                        const int64_t ti = i < L ? p.ts[row0 + i] : t_first;
+                        const int64_t dt = ti - tj64;
+                        const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
+                        bias += s.tt_wide[bit_length_u64(ad)];
+                    }
+                }
+                float a, slope;
+                act_and_slope(sacc[r] + bias, silu, a, slope);
+                av[r] = vis ? a : 0.0f;
+                gv[r] = vis ? gacc[r] * slope : 0.0f;
+            }
+
+            // dV += A^T dO and dK += G^T Q over the tile's two 16-row chunks
+            bf16x8 pa[2], pg[2];
+            pack_a(av, pa);
+            pack_a(gv, pg);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 tf[4];
+                read_v_chunk(gt_lds, c, lane, tf);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) dva[nb] = mfma32(pa[c], __builtin_bit_cast(bf16x8, tf[nb]), dva[nb]);
+                read_v_chunk(qt_lds, c, lane, tf);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) dka[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, tf[nb]), dka[nb]);
+            }
+        }
+
+        // ---- dK, dV = alpha * acc for keys < L; lane holds column nb*32 +
+        //      l32 at keys k0w + 8 (r / 4) + 4 h2 + r % 4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ko = k0w + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (ko < L) {
+                uint16_t* kp = p.dk + (row0 + ko) * p.dks + h * HD + l32;
+                uint16_t* vp = p.dv + (row0 + ko) * p.dvs + h * HD + l32;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    kp[nb * 32] = f32_to_bf16_bits(p.alpha * dka[nb][r]);
+                    vp[nb * 32] = f32_to_bf16_bits(p.alpha * dva[nb][r]);
+                }
+            }
+        }
+        lds_barrier();   // this item's LDS use is over before the next item starts
+    }
+}
+
+// Table gradients: column e of the partial rows, summed in work order; the
+// per-head case keeps the rows of head h (work index w has head w % H).
+__global__ void __launch_bounds__(256) rab_grad_reduce_kernel(const float* part, const int32_t* ctrl, int H,
+                                                              int P, int NT, int per_head_pos, int per_head_time,
+                                                              float alpha, float* drab_pos, float* drab_time) {
+    const int width = P + NT;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int h = blockIdx.y;
+    if (e >= width) return;
+    const bool is_pos = e < P;
+    const bool per_head = is_pos ? per_head_pos != 0 : per_head_time != 0;
+    if (!per_head && h > 0) return;
+    float* dst = is_pos ? drab_pos : drab_time;
+    if (!dst) return;
+    const int idx = is_pos ? e : e - P;
+    const int nwork = ctrl[0] * H;
+    float acc = 0.0f;
+    for (int w = per_head ? h : 0; w < nwork; w += per_head ? H : 1) acc += part[(int64_t)w * width + e];
+    dst[(per_head ? h * (is_pos ? P : NT) : 0) + idx] = alpha * acc;
+}
+
+size_t smem_bytes(int tiles, int P, int NT, bool hist) {
+    size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
+    b += sizeof(float) * (size_t)((P + 3) & ~3);
+    if (hist) b += sizeof(float) * 4 * (size_t)((P + NT + 3) & ~3);
+    return b;
+}
+
+BwdParams make_params(const AttnBwdArgs& a) {
+    BwdParams p;
+    p.H = a.H;
+    p.offsets = a.offsets; p.lengths = a.lengths; p.ncand = a.ncand;
+    p.q = static_cast<const uint16_t*>(a.q); p.qs = a.q_stride;
+    p.k = static_cast<const uint16_t*>(a.k); p.ks = a.k_stride;
+    p.v = static_cast<const uint16_t*>(a.v); p.vs = a.v_stride;
+    p.g = static_cast<const uint16_t*>(a.dout); p.gs = a.dout_stride;
+    p.ts = a.ts;
+    p.rab_pos = a.rab_pos; p.P = a.P; p.rp_hs = a.rp_head_stride;
+    p.rab_time = a.rab_time; p.NT = a.NT; p.rt_hs = a.rt_head_stride;
+    p.alpha = a.alpha;
+    p.act = a.act;
+    p.dq = static_cast<uint16_t*>(a.dq); p.dqs = a.dq_stride;
+    p.dk = static_cast<uint16_t*>(a.dk); p.dks = a.dk_stride;
+    p.dv = static_cast<uint16_t*>(a.dv); p.dvs = a.dv_stride;
+    p.nblk = a.nblk;
+    p.stats = a.stats;
+    p.enc = a.enc;
+    p.rab_part = a.rab_part;
+    return p;
+}
+
+}  // namespace
+
+bool attn_bwd_tables_fit(int P, int NT) { return smem_bytes(3, P, NT, true) <= 160 * 1024; }
+
+size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT) {
+    return (size_t)cap * (size_t)H * (size_t)(P + NT);
+}
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
+    const int grid = device_cu_count();
+    const void* ws_base = a.stats;
+    const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
+    const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
+
+    BwdParams pq = make_params(a);
+    pq.items = a.q_items; pq.ctrl = a.q_ctrl; pq.cursor = a.q_ctrl + 1;
+    const size_t smq = smem_bytes(3, a.P, a.NT, true);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dq_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smq);
+    if (e != hipSuccess) return e;
+    hipExtLaunchKernelGGL(attn_bwd_dq_kernel, dim3(grid), dim3(kThreads), smq, stream, a.ev_dq_begin,
+                          a.ev_dq_end, 0, pq, ws_base, wsb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    BwdParams pk = make_params(a);
+    pk.items = a.kv_items; pk.ctrl = a.kv_ctrl; pk.cursor = a.kv_ctrl + 1;
+    const size_t smk = smem_bytes(4, a.P, a.NT, false);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dkv_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smk);
+    if (e != hipSuccess) return e;
+    hipExtLaunchKernelGGL(attn_bwd_dkv_kernel, dim3(grid), dim3(kThreads), smk, stream, a.ev_dkv_begin,
+                          a.ev_dkv_end, 0, pk, ws_base, wsb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    if (a.drab_pos || a.drab_time) {
+        const int width = a.P + a.NT;
+        const int hy = (a.rp_head_stride > 0 || a.rt_head_stride > 0) ? a.H : 1;
+        hipLaunchKernelGGL(rab_grad_reduce_kernel, dim3((unsigned)((width + 255) / 256), (unsigned)hy), dim3(256),
+                           0, stream, a.rab_part, a.q_ctrl, a.H, a.P, a.NT, a.rp_head_stride > 0 ? 1 : 0,
+                           a.rt_head_stride > 0 ? 1 : 0, a.alpha, a.drab_pos, a.drab_time);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace hstu

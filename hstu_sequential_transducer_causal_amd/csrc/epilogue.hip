@@ -183,6 +183,82 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
     }
 }
 
+// Gradients of Y = LN(O) (.) U for bf16 rows (one wave per row): with
+// xhat = (O - mean) rstd,
+//   dU = xhat (.) dY,   g = dY (.) U,   dO = rstd (g - mean(g) - xhat mean(g xhat))
+// (the derivative of a LayerNorm without affine parameters).  Padding rows
+// are skipped.
+template <int NCH>
+__global__ void __launch_bounds__(kThreads) ln_gate_bwd_kernel(LnGateBwdArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (a.B <= 0 || row >= a.num_rows) return;
+    if (row < a.offsets[0] || row >= a.offsets[a.B]) return;
+    if (a.lengths) {
+        const int b = seq_of_row(a.offsets, a.B, row);
+        if ((int)(row - a.offsets[b]) >= a.lengths[b]) return;
+    }
+    const int W = a.width;
+    float x[NCH][8], u[NCH][8], gy[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+            Vec8<true>::load(a.o, row * a.o_stride + col, x[c]);
+            Vec8<true>::load(a.u, row * a.u_stride + col, u[c]);
+            Vec8<true>::load(a.dy, row * a.dy_stride + col, gy[c]);
+        }
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if ((c * 64 + lane) * 8 < W)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += x[c][e];
+    const float mean = wave_sum(sum) / (float)W;
+    float sq = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if ((c * 64 + lane) * 8 < W)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dlt = x[c][e] - mean;
+                sq = fmaf(dlt, dlt, sq);
+            }
+    const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)W + a.eps);
+    float mg = 0.0f, mgx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+            float du[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xh = (x[c][e] - mean) * rstd;
+                const float g = gy[c][e] * u[c][e];
+                du[e] = xh * gy[c][e];
+                mg += g;
+                mgx = fmaf(g, xh, mgx);
+                x[c][e] = xh;
+                u[c][e] = g;
+            }
+            if (a.du) Vec8<true>::store(a.du, row * a.du_stride + col, du);
+        }
+    }
+    mg = wave_sum(mg) / (float)W;
+    mgx = wave_sum(mgx) / (float)W;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < W) {
+            float d[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] = rstd * (u[c][e] - mg - x[c][e] * mgx);
+            Vec8<true>::store(a.dout, row * a.dout_stride + col, d);
+        }
+    }
+}
+
 template <bool BF16>
 hipError_t launch_typed(const LnGateArgs& a, hipStream_t stream) {
     const int nch = (a.width + 511) / 512;
@@ -198,6 +274,20 @@ hipError_t launch_typed(const LnGateArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_ln_gate_bwd(const LnGateBwdArgs& a, hipStream_t stream) {
+    if (a.num_rows <= 0 || a.B <= 0) return hipSuccess;
+    const int nch = (a.width + 511) / 512;
+    const dim3 grid((unsigned)((a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    switch (nch) {
+        case 1: hipLaunchKernelGGL((ln_gate_bwd_kernel<1>), grid, dim3(kThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((ln_gate_bwd_kernel<2>), grid, dim3(kThreads), 0, stream, a); break;
+        case 3:
+        case 4: hipLaunchKernelGGL((ln_gate_bwd_kernel<4>), grid, dim3(kThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL((ln_gate_bwd_kernel<8>), grid, dim3(kThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_ln_gate(const LnGateArgs& a, hipStream_t stream) {
     if (a.num_rows <= 0) return hipSuccess;

@@ -79,6 +79,7 @@ struct SchedArgs {
     int64_t cap;       // row-block capacity (split-block list)
     int64_t cap_pieces;   // piece capacity of `items`
     int cand_only;     // M-FALCON: only the query tiles that hold candidate rows
+    int kv_mode;       // items are blocks of tile_m keys with their tile_n-row query tiles
     int H;
     int slots;         // workgroups of the attention core (the work per workgroup sets the piece size)
     int part_slots;    // partial slots available (0: no splitting)
@@ -159,6 +160,62 @@ struct CombineArgs {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnCoreArgs& a, hipStream_t stream);
+
+// Gradients of the bf16 attention core (d = 128): dQ by a query-major pass
+// over the forward's work list (which also writes one table-gradient partial
+// row per work item), dK and dV by a key-major pass over a list built with
+// kv_mode, then the partial rows summed in work order.
+struct AttnBwdArgs {
+    int H;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const int32_t* ncand;
+    const void* q; int64_t q_stride;
+    const void* k; int64_t k_stride;
+    const void* v; int64_t v_stride;
+    const void* dout; int64_t dout_stride;
+    const int64_t* ts;
+    const float* rab_pos; int P; int rp_head_stride;
+    const float* rab_time; int NT; int rt_head_stride;
+    float alpha;
+    int act;
+    void* dq; int64_t dq_stride;
+    void* dk; int64_t dk_stride;
+    void* dv; int64_t dv_stride;
+    float* drab_pos;             // [P] or [H][P]; NULL: not computed
+    float* drab_time;            // [NT] or [H][NT]; NULL: not computed
+    const WorkItem* q_items;  int32_t* q_ctrl;    // query-major list (ctrl[1] is its cursor)
+    const WorkItem* kv_items; int32_t* kv_ctrl;   // key-major list
+    int nblk;
+    const uint32_t* stats;
+    const uint32_t* enc;
+    int64_t num_rows;
+    float* rab_part;             // [work][P + NT]
+    hipEvent_t ev_dq_begin, ev_dq_end, ev_dkv_begin, ev_dkv_end;   // optional
+};
+
+size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT);
+// The dQ kernel keeps the position and time tables and four per-wave
+// histograms of their gradients in LDS next to its tile ring.
+bool attn_bwd_tables_fit(int P, int NT);
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
+// Gradients of Y = LayerNorm(O) * U (rows of width H * d_v, bf16): dO and dU.
+struct LnGateBwdArgs {
+    int B;
+    int64_t num_rows;
+    int width;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const void* o; int64_t o_stride;
+    const void* u; int64_t u_stride;
+    const void* dy; int64_t dy_stride;
+    void* dout; int64_t dout_stride;
+    void* du; int64_t du_stride;
+    float eps;
+};
+
+hipError_t launch_ln_gate_bwd(const LnGateBwdArgs& a, hipStream_t stream);
 
 // LayerNorm(O_row) * U_row epilogue, optionally scored against w for the
 // candidate rows (M-FALCON).

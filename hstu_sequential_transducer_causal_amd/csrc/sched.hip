@@ -15,6 +15,8 @@
 //   otherwise:                [0, ceil(n / BN)) for the history columns, plus
 //                             the tiles of the candidates' own diagonal
 //                             [max(q0, n) / BN, ceil(q1 / BN)) beyond it.
+// In key-major mode (the key and value gradients) an item is a block of BM
+// keys instead, with the one range of BN-row query tiles that see them.
 //
 // Items are written longest first (counting sort on the number of key
 // tiles) so that the persistent attention kernel, which takes items in list
@@ -50,7 +52,19 @@ struct Ranges {
     int a_end, kb_begin, kb_end;
 };
 
-__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int BN) {
+__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int BN, bool kv_mode) {
+    if (kv_mode) {
+        // key block [k0, k1): the 32-row query tiles from k0's on -- to the
+        // end for a block holding history keys (every later row and every
+        // candidate sees them), to k1 for a block of candidates only (each is
+        // seen by itself alone)
+        const int k0 = qt * BM, k1 = min(k0 + BM, L);
+        Ranges r;
+        r.a_end = 0;
+        r.kb_begin = k0 / BN;
+        r.kb_end = ceil_div(k0 < n ? L : k1, BN);
+        return r;
+    }
     int q0 = qt * BM;
     int q1 = min(q0 + BM, L);
     Ranges r;
@@ -228,7 +242,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
             n = seq_history(a, b, L);
         }
         qt += first_tile(a, n, BM);
-        return tile_ranges(L, n, qt, BM, BN);
+        return tile_ranges(L, n, qt, BM, BN, a.kv_mode != 0);
     };
     auto cost_of = [](const Ranges& r) { return r.a_end + (r.kb_end - r.kb_begin); };
     auto cost_at = [&](int f) {

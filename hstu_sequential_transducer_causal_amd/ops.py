@@ -2,8 +2,8 @@
 
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
-Names follow the C ABI: hstu_attn_fwd, mfalcon_score, hstu_layer_fwd,
-hstu_attn_schedule.
+Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score,
+hstu_layer_fwd, hstu_attn_schedule.
 """
 from __future__ import annotations
 
@@ -117,6 +117,67 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
     _lib.check(lib.hstu_attn_fwd(ctypes.byref(args), workspace.data_ptr(), workspace.numel(),
                                  _stream_ptr(stream)))
     return o, (y if u is not None else None)
+
+
+def hstu_attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
+                  max_seq_len: int, dout=None, dy=None, o=None, u=None, ln_eps: float = 1e-5,
+                  seq_lengths=None, num_candidates=None, act: int = _lib.HSTU_ACT_SILU,
+                  want_rab: bool = True, dq=None, dk=None, dv=None, du=None, drab_pos=None,
+                  drab_time=None, workspace=None, stream=None, events=None):
+    """Gradients of the attention path (bf16, d = 128).
+
+    The upstream gradient is ``dout`` = dLoss/dO, or ``dy`` = dLoss/dY of
+    Y = LayerNorm(O) * U (then ``o`` = the forward's O and ``u`` are
+    required).  Returns (dq, dk, dv, du, drab_pos, drab_time): du is None
+    without dy, the table gradients (float32, shaped like the tables) None
+    unless ``want_rab``.  ``events`` = (dq begin, dq end, dkv begin, dkv end)
+    raw hipEvent_t handles or None.
+    """
+    lib = _lib.load()
+    if (dout is None) == (dy is None):
+        raise ValueError("give exactly one of dout and dy")
+    args = _lib.AttnBwdArgs()
+    args.struct_size = ctypes.sizeof(_lib.AttnBwdArgs)
+    H, d = q.shape[1], v.shape[2]
+    args.attn = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                               max_seq_len=max_seq_len, o=o if o is not None else v,
+                               seq_lengths=seq_lengths, num_candidates=num_candidates, u=u,
+                               ln_eps=ln_eps, act=act)
+    if o is None:
+        args.attn.o = None
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dy is not None:
+        args.dy, args.dy_stride = dy.data_ptr(), _head_view_stride(dy, H, d)
+        if du is None:
+            du = torch.empty_like(v)
+        args.du, args.du_stride = du.data_ptr(), _head_view_stride(du, H, d)
+    else:
+        args.dout, args.dout_stride = dout.data_ptr(), _head_view_stride(dout, H, d)
+        du = None
+    args.dq, args.dq_stride = dq.data_ptr(), _head_view_stride(dq, H, q.shape[2])
+    args.dk, args.dk_stride = dk.data_ptr(), _head_view_stride(dk, H, q.shape[2])
+    args.dv, args.dv_stride = dv.data_ptr(), _head_view_stride(dv, H, d)
+    if want_rab:
+        if drab_pos is None:
+            drab_pos = torch.empty(rab_pos.shape, dtype=torch.float32, device=q.device)
+        if drab_time is None:
+            drab_time = torch.empty(rab_time.shape, dtype=torch.float32, device=q.device)
+        args.drab_pos, args.drab_time = drab_pos.data_ptr(), drab_time.data_ptr()
+    else:
+        drab_pos = drab_time = None
+    if events is not None:
+        args.ev_dq_begin, args.ev_dq_end, args.ev_dkv_begin, args.ev_dkv_end = events
+    need = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(args))
+    if need == 0:
+        # invalid arguments: let the call itself report why
+        _lib.check(lib.hstu_attn_bwd(ctypes.byref(args), None, 0, _stream_ptr(stream)))
+    if workspace is None:
+        workspace = _empty_ws(need, q.device)
+    _lib.check(lib.hstu_attn_bwd(ctypes.byref(args), workspace.data_ptr(), workspace.numel(),
+                                 _stream_ptr(stream)))
+    return dq, dk, dv, du, drab_pos, drab_time
 
 
 def attn_workspace_bytes(args: _lib.AttnArgs) -> int:

@@ -161,6 +161,12 @@ def _normal(rng, shape, std, bf16: bool) -> np.ndarray:
     return bf16_round(x) if bf16 else x
 
 
+def upstream_grad(seed: int, shape, std: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """Seeded upstream gradient (dLoss/dO, dLoss/dY, or a stand-in forward
+    output) of the given shape, N(0, std) rounded to bf16 for dtype bf16."""
+    return _normal(np.random.default_rng(seed), shape, std, dtype == "bf16")
+
+
 def _offsets(lengths) -> np.ndarray:
     off = np.zeros(len(lengths) + 1, dtype=np.int32)
     off[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -208,6 +208,59 @@ size_t hstu_layer_workspace_bytes(const hstu_layer_args* args);
 
 hstu_status hstu_layer_fwd(const hstu_layer_args* args, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------- attention (gradients) */
+/* Gradients of the attention path for training (bf16, d_qk = d_v = 128):
+ * the chain rule through the forward definition of hstu_attn_fwd ("生成式推荐
+ * （一）：HSTU", sections "高性能自注意力Encoder：HSTU" and "Pointwise
+ * aggregated attention"; training is what the pages' speed-ups are quoted
+ * for).  Per head and visible pair (i, j), with S_ij the forward's logit:
+ *   dV_j += alpha SiLU(S_ij) dO_i
+ *   G_ij  = alpha <dO_i, V_j> SiLU'(S_ij)
+ *   dQ_i += G_ij K_j,  dK_j += G_ij Q_i,
+ *   drab_pos[pb(i, j)] += G_ij,  drab_time[tb(i, j)] += G_ij.
+ * The upstream gradient is either dout = dLoss/dO, or dy = dLoss/dY of the
+ * forward's Y = LayerNorm(O) (.) U (then attn.o must hold the forward's O,
+ * attn.u its U, attn.ln_eps its eps; dO and, if du != NULL, dU are derived
+ * first).  O and Y are not recomputed; S is.
+ * Outputs: the valid rows of dq, dk, dv (bf16, [rows, H*128] with strides in
+ * elements, 16-byte aligned rows) are overwritten, padding rows untouched;
+ * drab_pos / drab_time (fp32, device) are overwritten with the table
+ * gradients, shaped like the tables: [num_pos_buckets] summed over heads for
+ * a shared table, [H][num_pos_buckets] (dense, stride num_pos_buckets) for
+ * per-head tables; NULL skips one.  The table gradients are summed in a
+ * fixed order (run-to-run identical).  attn.y, attn.o (without dy) and the
+ * attention events are not used.
+ * Limits: bf16 with d = 128; num_pos_buckets + num_time_buckets at most
+ * about 4100 (the tables and per-wave histograms of their gradients share a
+ * workgroup's LDS with the tile ring).
+ * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED (fp32, d != 128, tables too
+ * long), HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
+typedef struct hstu_attn_bwd_args {
+    uint32_t struct_size;               /* = sizeof(hstu_attn_bwd_args) */
+    hstu_attn_args attn;                /* the forward's arguments */
+    const void* dy; int64_t dy_stride;  /* [rows, H*d_v] bf16, or NULL */
+    const void* dout; int64_t dout_stride;   /* [rows, H*d_v] bf16 when dy == NULL */
+    void* dq; int64_t dq_stride;
+    void* dk; int64_t dk_stride;
+    void* dv; int64_t dv_stride;
+    void* du; int64_t du_stride;        /* with dy: dLoss/dU, or NULL */
+    float* drab_pos;
+    float* drab_time;
+    /* optional hipEvent_t stamped with the start / end of the dQ kernel and of
+       the dK/dV kernel (travel with those launches); NULL = none */
+    void* ev_dq_begin; void* ev_dq_end;
+    void* ev_dkv_begin; void* ev_dkv_end;
+} hstu_attn_bwd_args;
+
+/* Workspace bytes for hstu_attn_bwd (0 on invalid arguments): two work lists,
+ * the timestamp codes, dO when dy is given (rows x H*128 bf16) and one fp32
+ * row of num_pos_buckets + num_time_buckets table-gradient partial sums per
+ * (128-row block, head). */
+size_t hstu_attn_bwd_workspace_bytes(const hstu_attn_bwd_args* args);
+
+hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* args, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ------------------------------------------------------ scheduler access */
 /* Builds only the jagged tile work list into `workspace` (same layout as the

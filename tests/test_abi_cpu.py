@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 2
+    assert lib.hstu_abi_version() == 3
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -51,6 +51,7 @@ _STRUCTS = {
     "hstu_attn_args": _lib.AttnArgs,
     "hstu_mfalcon_args": _lib.MfalconArgs,
     "hstu_layer_args": _lib.LayerArgs,
+    "hstu_attn_bwd_args": _lib.AttnBwdArgs,
 }
 
 
@@ -183,3 +184,57 @@ def test_mfalcon_and_layer_validation(lib):
     assert lib.hstu_layer_fwd(ctypes.byref(l), None, 0, None) == _lib.HSTU_ERR_UNSUPPORTED
     l.d, l.D = 128, 100
     assert lib.hstu_layer_fwd(ctypes.byref(l), None, 0, None) == _lib.HSTU_ERR_UNSUPPORTED
+
+
+def _valid_bwd():
+    g = _lib.AttnBwdArgs()
+    g.struct_size = ctypes.sizeof(_lib.AttnBwdArgs)
+    g.attn = _valid_args()
+    fake = 0x10000
+    g.dout, g.dout_stride = fake, 512
+    g.dq = g.dk = g.dv = fake
+    g.dq_stride = g.dk_stride = g.dv_stride = 512
+    return g
+
+
+BWD_MUTATIONS = [
+    ("struct_size", lambda g: setattr(g, "struct_size", 8), _lib.HSTU_ERR_ARG),
+    ("fp32", lambda g: (setattr(g.attn, "dtype", _lib.HSTU_F32), setattr(g.attn, "d_qk", 64),
+                        setattr(g.attn, "d_v", 64)), _lib.HSTU_ERR_UNSUPPORTED),
+    ("no upstream gradient", lambda g: setattr(g, "dout", None), _lib.HSTU_ERR_ARG),
+    ("dq NULL", lambda g: setattr(g, "dq", None), _lib.HSTU_ERR_ARG),
+    ("dk stride small", lambda g: setattr(g, "dk_stride", 100), _lib.HSTU_ERR_ARG),
+    ("misaligned dv", lambda g: setattr(g, "dv", 0x10004), _lib.HSTU_ERR_UNSUPPORTED),
+    ("dy without u", lambda g: (setattr(g, "dy", 0x10000), setattr(g, "dy_stride", 512)),
+     _lib.HSTU_ERR_ARG),
+    ("dy without o", lambda g: (setattr(g, "dy", 0x10000), setattr(g, "dy_stride", 512),
+                                setattr(g.attn, "u", 0x10000), setattr(g.attn, "u_stride", 512),
+                                setattr(g.attn, "o", None)), _lib.HSTU_ERR_ARG),
+    ("forward args", lambda g: setattr(g.attn, "H", 0), _lib.HSTU_ERR_ARG),
+    ("tables too long", lambda g: setattr(g.attn, "num_pos_buckets", 8192), _lib.HSTU_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,mut,status", BWD_MUTATIONS, ids=[m[0] for m in BWD_MUTATIONS])
+def test_bwd_validation_errors_before_any_launch(lib, name, mut, status):
+    g = _valid_bwd()
+    mut(g)
+    assert lib.hstu_attn_bwd(ctypes.byref(g), None, 0, None) == status
+    assert lib.hstu_last_error()
+    assert lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(g)) == 0
+
+
+def test_bwd_workspace_errors_and_size(lib):
+    assert lib.hstu_attn_bwd(None, None, 0, None) == _lib.HSTU_ERR_ARG
+    g = _valid_bwd()
+    g.attn.o = None      # not read without dy
+    need = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(g))
+    assert need > 0
+    assert lib.hstu_attn_bwd(ctypes.byref(g), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_attn_bwd(ctypes.byref(g), 0x20000, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
+    # with dy the workspace also holds dO: rows x H x 128 bf16
+    g.dy, g.dy_stride = 0x10000, 512
+    g.attn.o = g.attn.u = 0x10000
+    g.attn.u_stride = 512
+    need_dy = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(g))
+    assert need_dy >= need + g.attn.num_rows * 512 * 2
