@@ -11,8 +11,10 @@ Prints ONE JSON line.  `value` is unmasked attention TFLOP/s of the whole
 step; `roofline` is the attention-core kernel alone, timed with HIP events
 recorded around its launch on the same stream; `cpu_baseline` is the fp64
 oracle on a bounded sample of the same workload (host cores of this machine).
-Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) are
-timed briefly and reported under "other_workloads".
+Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) and
+the attention gradients (hstu_attn_bwd from dLoss/dY on the long-sequence
+and M-FALCON workloads) are timed briefly and reported under
+"other_workloads".
 """
 from __future__ import annotations
 
@@ -44,6 +46,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=0, help="0: all sequences")
+    p.add_argument("--only-bwd", action="store_true",
+                   help="only time the attention gradients on --workload (for kernel traces)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
@@ -126,6 +130,89 @@ class StackCase:
                                max_seq_len=self.max_len, ln_eps=self.x.eps, x_out=out,
                                workspace=self.ws)
             cur = out
+
+
+class BwdCase:
+    """Gradients of the attention path from dLoss/dY (gate derivative, both
+    work lists, the dQ and dK/dV kernels, the table-gradient reduction)."""
+
+    def __init__(self, x, dev):
+        import torch
+        import hstu_synth as synth
+        from hstu_sequential_transducer_causal_amd import ops
+        self.x = x
+        self.q, self.k, self.v, self.u = (up(a, "bf16", dev) for a in (x.q, x.k, x.v, x.u))
+        self.o = up(synth.upstream_grad(8, x.v.shape, std=0.02), "bf16", dev)
+        self.dy = up(synth.upstream_grad(9, x.v.shape), "bf16", dev)
+        self.off = torch.from_numpy(x.offsets).to(dev)
+        self.ts = torch.from_numpy(x.ts).to(dev)
+        self.rp = torch.from_numpy(x.rab_pos).to(dev)
+        self.rt = torch.from_numpy(x.rab_time).to(dev)
+        self.nc = None if x.num_candidates is None else torch.from_numpy(x.num_candidates).to(dev)
+        self.max_len = int(np.diff(x.offsets).max())
+        self.out = [torch.empty_like(self.q) for _ in range(4)]
+        self.drp = torch.empty_like(self.rp)
+        self.drt = torch.empty_like(self.rt)
+        a = ops.make_attn_bwd_args(self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt,
+                                   x.alpha, max_seq_len=self.max_len, dq=self.out[0],
+                                   dk=self.out[1], dv=self.out[2], dy=self.dy, o=self.o, u=self.u,
+                                   du=self.out[3], ln_eps=x.eps, num_candidates=self.nc,
+                                   drab_pos=self.drp, drab_time=self.drt)
+        self.ws = torch.empty(max(1, ops.attn_bwd_workspace_bytes(a)), dtype=torch.uint8, device=dev)
+
+    def step(self, events=None):
+        from hstu_sequential_transducer_causal_amd import ops
+        ops.hstu_attn_bwd(
+            self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt, self.x.alpha,
+            max_seq_len=self.max_len, dy=self.dy, o=self.o, u=self.u, ln_eps=self.x.eps,
+            num_candidates=self.nc, dq=self.out[0], dk=self.out[1], dv=self.out[2],
+            du=self.out[3], drab_pos=self.drp, drab_time=self.drt, workspace=self.ws,
+            events=events)
+
+
+def time_bwd(case, steps, warmup):
+    """Wall time per step and the mean dQ / dK-dV kernel times (HIP events
+    carried by those launches)."""
+    import torch
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for ev in e:
+            ev.record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        case.step(tuple(ev.cuda_event for ev in evs[i]))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    dq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dkv = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    return ms, dq, dkv
+
+
+def bwd_record(x, dev, steps):
+    from hstu_sequential_transducer_causal_amd import flops
+    c = BwdCase(x, dev)
+    ms, dq, dkv = time_bwd(c, steps, 2)
+    L = np.diff(x.offsets)
+    pairs = flops.visible_pairs(L, x.num_candidates)
+    alg = flops.attn_bwd_flops(L, x.H, x.d, x.num_candidates)
+    ex_dq = pairs * x.H * 6 * x.d      # S, dO V^T, dQ
+    ex_dkv = pairs * x.H * 8 * x.d     # S, dO V^T, dV, dK
+    rec = {"ms_per_step": round(ms, 4), "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
+           "tokens_per_s": round(x.T / (ms * 1e-3), 1), "tokens": x.T,
+           "dq_kernel_ms": round(dq, 4), "dkv_kernel_ms": round(dkv, 4),
+           "dq_kernel_tflops_executed": round(ex_dq / (dq * 1e-3) / 1e12, 2),
+           "dkv_kernel_tflops_executed": round(ex_dkv / (dkv * 1e-3) / 1e12, 2),
+           "dkv_kernel_frac_bf16_peak": round(ex_dkv / (dkv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "flop_convention": "tflops: 8*d per visible pair and head (dV, dO V^T, dQ, dK); "
+                              "executed: with the recomputed S in each kernel"}
+    del c
+    return rec
 
 
 def time_case(case, steps, warmup, core_events=True):
@@ -230,6 +317,10 @@ def main():
     wl = args.workload
     log(f"generating workload {wl}")
     x = synth.config(wl)
+    if args.only_bwd:
+        rec = bwd_record(x, dev, args.steps)
+        print(json.dumps({"workload": x.name + "_bwd", **rec}), flush=True)
+        return
     L = np.diff(x.offsets)
     if wl == 5:
         case = StackCase(x, dev)
@@ -310,6 +401,12 @@ def main():
                 log(f"{xo.name} candidates only: {rec}")
                 del c
                 torch.cuda.empty_cache()
+        for w in (3, 4):
+            xb = x if w == wl else synth.config(w)
+            rec = bwd_record(xb, dev, max(3, args.steps // 3))
+            others[xb.name + "_bwd"] = rec
+            log(f"{xb.name} gradients: {rec}")
+            torch.cuda.empty_cache()
         line["other_workloads"] = others
 
     line["cpu_baseline"] = None

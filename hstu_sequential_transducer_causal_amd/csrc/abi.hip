@@ -308,7 +308,7 @@ hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
 
 struct BwdWs {
     hstu::SchedLayout q, kv;   // query-major and key-major work lists
-    size_t dout, part, total;
+    size_t dout, part, part2, total;
 };
 
 BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
@@ -318,8 +318,10 @@ BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
     w.kv = hstu::sched_layout(a.B, a.H, a.max_seq_len, hstu::kBf16TileM, 0, 0, w.q.bytes);
     w.dout = align256(w.kv.bytes);
     w.part = align256(w.dout + (g->dy ? size_t(a.num_rows) * size_t(a.H) * size_t(a.d_v) * 2 : 0));
-    w.total = align256(w.part + sizeof(float) * hstu::attn_bwd_rab_part_floats(
+    w.part2 = align256(w.part + sizeof(float) * hstu::attn_bwd_rab_part_floats(
                                                     (int64_t)w.q.cap, a.H, a.num_pos_buckets, a.num_time_buckets));
+    w.total = align256(w.part2 + sizeof(float) * hstu::attn_bwd_rab_part2_floats(a.H, a.num_pos_buckets,
+                                                                                  a.num_time_buckets));
     return w;
 }
 
@@ -641,6 +643,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
     b.enc = sq.enc;
     b.num_rows = a->num_rows;
     b.rab_part = reinterpret_cast<float*>(wb + w.part);
+    b.rab_part2 = reinterpret_cast<float*>(wb + w.part2);
     b.ev_dq_begin = static_cast<hipEvent_t>(g->ev_dq_begin);
     b.ev_dq_end = static_cast<hipEvent_t>(g->ev_dq_end);
     b.ev_dkv_begin = static_cast<hipEvent_t>(g->ev_dkv_begin);

@@ -660,12 +660,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
     }
 }
 
-// Table gradients: column e of the partial rows, summed in work order; the
-// per-head case keeps the rows of head h (work index w has head w % H).
-__global__ void __launch_bounds__(256) rab_grad_reduce_kernel(const float* part, const int32_t* ctrl, int H,
-                                                              int P, int NT, int per_head_pos, int per_head_time,
-                                                              float alpha, float* drab_pos, float* drab_time) {
-    const int width = P + NT;
+// Table gradients, in two fixed-order passes over the partial rows (one per
+// work item w, head w % H).  Pass 1: chunk c of kChunks sums its rows (of
+// head h, or all heads for a shared table) for one column e, in row order
+// with four interleaved accumulators added in a fixed order at the end.
+// Pass 2: the chunks in order, times alpha.
+constexpr int kChunks = 64;
+
+__global__ void __launch_bounds__(256) rab_grad_partial_kernel(const float* part, const int32_t* ctrl, int H,
+                                                               int width, int P, int per_head_pos,
+                                                               int per_head_time, float* part2) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y;
+    const int h = blockIdx.z;
+    if (e >= width) return;
+    const bool per_head = e < P ? per_head_pos != 0 : per_head_time != 0;
+    const int step = per_head ? H : 1;
+    const int nrows = per_head ? (ctrl[0] * H - h + H - 1) / H : ctrl[0] * H;   // rows of this head
+    const int per_chunk = (nrows + kChunks - 1) / kChunks;
+    const int r0 = c * per_chunk, r1 = min(nrows, r0 + per_chunk);
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    int r = r0;
+    const int64_t base = per_head ? h : 0;
+    for (; r + 4 <= r1; r += 4) {
+        a0 += part[(base + (int64_t)(r + 0) * step) * width + e];
+        a1 += part[(base + (int64_t)(r + 1) * step) * width + e];
+        a2 += part[(base + (int64_t)(r + 2) * step) * width + e];
+        a3 += part[(base + (int64_t)(r + 3) * step) * width + e];
+    }
+    for (; r < r1; ++r) a0 += part[(base + (int64_t)r * step) * width + e];
+    part2[((int64_t)h * kChunks + c) * width + e] = (a0 + a1) + (a2 + a3);
+}
+
+__global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2, int width, int P, int NT,
+                                                             int per_head_pos, int per_head_time, float alpha,
+                                                             float* drab_pos, float* drab_time) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     const int h = blockIdx.y;
     if (e >= width) return;
@@ -674,10 +703,9 @@ __global__ void __launch_bounds__(256) rab_grad_reduce_kernel(const float* part,
     if (!per_head && h > 0) return;
     float* dst = is_pos ? drab_pos : drab_time;
     if (!dst) return;
-    const int idx = is_pos ? e : e - P;
-    const int nwork = ctrl[0] * H;
     float acc = 0.0f;
-    for (int w = per_head ? h : 0; w < nwork; w += per_head ? H : 1) acc += part[(int64_t)w * width + e];
+    for (int c = 0; c < kChunks; ++c) acc += part2[((int64_t)h * kChunks + c) * width + e];
+    const int idx = is_pos ? e : e - P;
     dst[(per_head ? h * (is_pos ? P : NT) : 0) + idx] = alpha * acc;
 }
 
@@ -719,6 +747,8 @@ size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT) {
     return (size_t)cap * (size_t)H * (size_t)(P + NT);
 }
 
+size_t attn_bwd_rab_part2_floats(int H, int P, int NT) { return (size_t)H * kChunks * (size_t)(P + NT); }
+
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     const int grid = device_cu_count();
     const void* ws_base = a.stats;
@@ -750,9 +780,15 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     if (a.drab_pos || a.drab_time) {
         const int width = a.P + a.NT;
         const int hy = (a.rp_head_stride > 0 || a.rt_head_stride > 0) ? a.H : 1;
-        hipLaunchKernelGGL(rab_grad_reduce_kernel, dim3((unsigned)((width + 255) / 256), (unsigned)hy), dim3(256),
-                           0, stream, a.rab_part, a.q_ctrl, a.H, a.P, a.NT, a.rp_head_stride > 0 ? 1 : 0,
-                           a.rt_head_stride > 0 ? 1 : 0, a.alpha, a.drab_pos, a.drab_time);
+        const unsigned gx = (unsigned)((width + 255) / 256);
+        hipLaunchKernelGGL(rab_grad_partial_kernel, dim3(gx, kChunks, (unsigned)hy), dim3(256), 0, stream,
+                           a.rab_part, a.q_ctrl, a.H, width, a.P, a.rp_head_stride > 0 ? 1 : 0,
+                           a.rt_head_stride > 0 ? 1 : 0, a.rab_part2);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(rab_grad_final_kernel, dim3(gx, (unsigned)hy), dim3(256), 0, stream, a.rab_part2,
+                           width, a.P, a.NT, a.rp_head_stride > 0 ? 1 : 0, a.rt_head_stride > 0 ? 1 : 0,
+                           a.alpha, a.drab_pos, a.drab_time);
         e = hipGetLastError();
     }
     return e;

@@ -191,10 +191,12 @@ struct AttnBwdArgs {
     const uint32_t* enc;
     int64_t num_rows;
     float* rab_part;             // [work][P + NT]
+    float* rab_part2;            // [heads][chunks][P + NT]
     hipEvent_t ev_dq_begin, ev_dq_end, ev_dkv_begin, ev_dkv_end;   // optional
 };
 
 size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT);
+size_t attn_bwd_rab_part2_floats(int H, int P, int NT);
 // The dQ kernel keeps the position and time tables and four per-wave
 // histograms of their gradients in LDS next to its tile ring.
 bool attn_bwd_tables_fit(int P, int NT);

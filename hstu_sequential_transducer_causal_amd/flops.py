@@ -33,6 +33,13 @@ def attn_flops(lengths, H: int, d_qk: int, d_v: int, num_candidates=None) -> int
     return int(visible_pairs(lengths, num_candidates)) * H * (2 * d_qk + 2 * d_v)
 
 
+def attn_bwd_flops(lengths, H: int, d: int, num_candidates=None) -> int:
+    """Algorithmic FLOPs of the attention gradients: the four products over
+    visible pairs (dV = A^T dO, dO V^T, dQ = G K, dK = G^T Q), 2*d each per
+    pair and head -- twice the forward's count.  Recomputing S is not counted."""
+    return int(visible_pairs(lengths, num_candidates)) * H * 8 * d
+
+
 def dense_attn_flops(T: int, d: int) -> int:
     """Dense count of both products over all T^2 pairs: 2 * 2 * T^2 * d."""
     return 2 * 2 * T * T * d

@@ -119,6 +119,42 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
     return o, (y if u is not None else None)
 
 
+def make_attn_bwd_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
+                       max_seq_len: int, dq, dk, dv, dout=None, dy=None, o=None, u=None,
+                       du=None, ln_eps: float = 1e-5, seq_lengths=None, num_candidates=None,
+                       act: int = _lib.HSTU_ACT_SILU, drab_pos=None, drab_time=None,
+                       events=None) -> _lib.AttnBwdArgs:
+    if (dout is None) == (dy is None):
+        raise ValueError("give exactly one of dout and dy")
+    args = _lib.AttnBwdArgs()
+    args.struct_size = ctypes.sizeof(_lib.AttnBwdArgs)
+    H, d = q.shape[1], v.shape[2]
+    args.attn = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                               max_seq_len=max_seq_len, o=o if o is not None else v,
+                               seq_lengths=seq_lengths, num_candidates=num_candidates, u=u,
+                               ln_eps=ln_eps, act=act)
+    if o is None:
+        args.attn.o = None
+    if dy is not None:
+        args.dy, args.dy_stride = dy.data_ptr(), _head_view_stride(dy, H, d)
+        if du is not None:
+            args.du, args.du_stride = du.data_ptr(), _head_view_stride(du, H, d)
+    else:
+        args.dout, args.dout_stride = dout.data_ptr(), _head_view_stride(dout, H, d)
+    args.dq, args.dq_stride = dq.data_ptr(), _head_view_stride(dq, H, q.shape[2])
+    args.dk, args.dk_stride = dk.data_ptr(), _head_view_stride(dk, H, q.shape[2])
+    args.dv, args.dv_stride = dv.data_ptr(), _head_view_stride(dv, H, d)
+    args.drab_pos = _ptr(drab_pos)
+    args.drab_time = _ptr(drab_time)
+    if events is not None:
+        args.ev_dq_begin, args.ev_dq_end, args.ev_dkv_begin, args.ev_dkv_end = events
+    return args
+
+
+def attn_bwd_workspace_bytes(args: _lib.AttnBwdArgs) -> int:
+    return int(_lib.load().hstu_attn_bwd_workspace_bytes(ctypes.byref(args)))
+
+
 def hstu_attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
                   max_seq_len: int, dout=None, dy=None, o=None, u=None, ln_eps: float = 1e-5,
                   seq_lengths=None, num_candidates=None, act: int = _lib.HSTU_ACT_SILU,
@@ -134,41 +170,25 @@ def hstu_attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
     raw hipEvent_t handles or None.
     """
     lib = _lib.load()
-    if (dout is None) == (dy is None):
-        raise ValueError("give exactly one of dout and dy")
-    args = _lib.AttnBwdArgs()
-    args.struct_size = ctypes.sizeof(_lib.AttnBwdArgs)
-    H, d = q.shape[1], v.shape[2]
-    args.attn = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
-                               max_seq_len=max_seq_len, o=o if o is not None else v,
-                               seq_lengths=seq_lengths, num_candidates=num_candidates, u=u,
-                               ln_eps=ln_eps, act=act)
-    if o is None:
-        args.attn.o = None
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if dy is not None:
-        args.dy, args.dy_stride = dy.data_ptr(), _head_view_stride(dy, H, d)
-        if du is None:
-            du = torch.empty_like(v)
-        args.du, args.du_stride = du.data_ptr(), _head_view_stride(du, H, d)
-    else:
-        args.dout, args.dout_stride = dout.data_ptr(), _head_view_stride(dout, H, d)
+    if dy is not None and du is None:
+        du = torch.empty_like(v)
+    if dy is None:
         du = None
-    args.dq, args.dq_stride = dq.data_ptr(), _head_view_stride(dq, H, q.shape[2])
-    args.dk, args.dk_stride = dk.data_ptr(), _head_view_stride(dk, H, q.shape[2])
-    args.dv, args.dv_stride = dv.data_ptr(), _head_view_stride(dv, H, d)
     if want_rab:
         if drab_pos is None:
             drab_pos = torch.empty(rab_pos.shape, dtype=torch.float32, device=q.device)
         if drab_time is None:
             drab_time = torch.empty(rab_time.shape, dtype=torch.float32, device=q.device)
-        args.drab_pos, args.drab_time = drab_pos.data_ptr(), drab_time.data_ptr()
     else:
         drab_pos = drab_time = None
-    if events is not None:
-        args.ev_dq_begin, args.ev_dq_end, args.ev_dkv_begin, args.ev_dkv_end = events
+    args = make_attn_bwd_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                              max_seq_len=max_seq_len, dq=dq, dk=dk, dv=dv, dout=dout, dy=dy,
+                              o=o, u=u, du=du, ln_eps=ln_eps, seq_lengths=seq_lengths,
+                              num_candidates=num_candidates, act=act, drab_pos=drab_pos,
+                              drab_time=drab_time, events=events)
     need = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(args))
     if need == 0:
         # invalid arguments: let the call itself report why
