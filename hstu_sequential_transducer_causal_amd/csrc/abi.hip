@@ -283,7 +283,7 @@ hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
     if (st != HSTU_OK) return st;
     if (a.dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "gradients need bf16 inputs (d = 128)");
     if (!hstu::attn_bwd_tables_fit(a.num_pos_buckets, a.num_time_buckets))
-        return fail(HSTU_ERR_UNSUPPORTED, "gradients support num_pos_buckets + num_time_buckets up to ~4100");
+        return fail(HSTU_ERR_UNSUPPORTED, "gradients support num_pos_buckets + num_time_buckets up to ~2600");
     const int64_t hd = int64_t(a.H) * a.d_v;
     if (g->dq_stride < hd || g->dk_stride < hd || g->dv_stride < hd)
         return fail(HSTU_ERR_ARG, "dq/dk/dv stride < H*d");

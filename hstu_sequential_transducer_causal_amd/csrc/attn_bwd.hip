@@ -17,10 +17,14 @@
 //   * attn_bwd_dq_kernel: one work item = 128 query rows x 1 head (the
 //     forward's work list).  Per 32-key tile: S^T = K Q^T and (dO V^T)^T =
 //     V dO^T with Q and dO in registers, then G^T and dQ += G K.  G is also
-//     summed by position and time bucket into LDS histograms, written as one
-//     partial row per work item and added up in a fixed order by
-//     rab_grad_reduce_kernel (so the table gradients do not depend on which
-//     workgroup took which item).
+//     summed by position and time bucket into per-wave LDS histograms,
+//     written as one partial row per work item and added up in a fixed order
+//     by rab_grad_partial_kernel and rab_grad_final_kernel (so the table
+//     gradients do not depend on which workgroup took which item).  LDS float
+//     atomics are slow, so the common cases avoid them per element: a block
+//     of history rows sums its 63 position diagonals through a skewed LDS
+//     scratch, and a block spanning at most four time buckets sums them in
+//     registers; one atomic per bucket then adds each sum.
 //   * attn_bwd_dkv_kernel: one work item = 128 keys x 1 head (a key-major
 //     work list: the 32-row query tiles that see the keys).  Per query tile:
 //     S = Q K^T and dO V^T with K and V in registers, then dV += A^T dO and
@@ -164,7 +168,8 @@ __device__ __forceinline__ void load_tables(const BwdParams& p, int h, float* pt
 struct TimeBlock {
     bool wide;       // some gap needs 64-bit arithmetic
     bool constant;   // one bucket for the block
-    int cz;          // its leading-zero count
+    int cz;          // its leading-zero count (the block's smallest gap)
+    int czhi;        // leading-zero count of its largest gap (<= cz)
 };
 
 __device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint32_t bmn, uint32_t bmx) {
@@ -175,6 +180,7 @@ __device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint
     const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);
     t.constant = !t.wide && czlo == czhi;
     t.cz = czlo;
+    t.czhi = czhi;
     return t;
 }
 
@@ -208,6 +214,32 @@ __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p, bool valid) {
     u32x4 z = {0u, 0u, 0u, 0u};
     if (valid) z = *reinterpret_cast<const u32x4*>(p);
     return __builtin_bit_cast(bf16x8, z);
+}
+
+// Sum over the wave's 64 lanes, complete in lane 63 (DPP row shifts, then
+// the row broadcasts 15 and 31; no LDS traffic).  Fixed order, so the same
+// inputs give the same bits.
+__device__ __forceinline__ float wave_total(float v) {
+    auto dpp = [](float x, int ctrl_id) -> float {
+        int xi = __builtin_bit_cast(int, x);
+        int r;
+        switch (ctrl_id) {
+            case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xF, 0xF, true); break;   // row_shr:1
+            case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xF, 0xF, true); break;   // row_shr:2
+            case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x114, 0xF, 0xF, true); break;   // row_shr:4
+            case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x118, 0xF, 0xF, true); break;   // row_shr:8
+            case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x142, 0xA, 0xF, false); break;  // row_bcast:15
+            default: r = __builtin_amdgcn_update_dpp(0, xi, 0x143, 0xC, 0xF, false); break; // row_bcast:31
+        }
+        return __builtin_bit_cast(float, r);
+    };
+    v = v + dpp(v, 0);
+    v = v + dpp(v, 1);
+    v = v + dpp(v, 2);
+    v = v + dpp(v, 3);
+    v = v + dpp(v, 4);
+    v = v + dpp(v, 5);
+    return v;
 }
 
 // Block code ranges through the scalar cache (uniform addresses): these loads
@@ -244,6 +276,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     // interleave; added in wave order at the end of the item
     const int hw = (p.P + p.NT + 3) & ~3;
     float* hist_all = ptab + ((p.P + 3) & ~3);
+    // per wave, a 32 x 64 scratch in which the block's G is written skewed
+    // (row rho, column rho - c + 31), so that each column holds one diagonal.
+    // Only the band rho <= column <= rho + 31 is ever written, so with the
+    // scratch zeroed once the rest reads as zero.
+    float* scratch_all = hist_all + 4 * hw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -260,7 +297,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     int loaded_head = -1;
 
     float* hist = hist_all + wave * hw;
-    for (int e = tid; e < 4 * hw; e += kThreads) hist_all[e] = 0.0f;
+    float* scratch = scratch_all + wave * (32 * 64);
+    for (int e = tid; e < 4 * hw + 4 * 32 * 64; e += kThreads) hist_all[e] = 0.0f;
 
     for (;;) {
         fetch_item(p, s, total_work, tid);
@@ -378,53 +416,72 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 gacc = mfma32(va, gf[kc], gacc);
             }
 
-            float gv[16];
-            float gsum = 0.0f;
+            // time buckets of the block: [tlo, thi]; up to 4 of them are
+            // summed in registers (a per-element atomic on a few addresses
+            // would serialise the lanes), more per element
+            const int tlo = min(NT - 1, 31 - tb.cz), thi = min(NT - 1, 31 - tb.czhi);
+            const bool few_buckets = !tb.constant && !tb.wide && thi - tlo < 4;
+
+            // (1) buckets and bias reads of all 16 elements.  LDS operations
+            //     complete in order, so nothing here may queue behind the
+            //     histogram atomics: those go out last, after the products.
+            int pbv[16], tbv[16];
+            float bias[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
                 const int j = j0 + c;
-                const bool vis = (j <= vis_lim) | (j == vis_self);
-                int pb = P - 1;
-                float bias = cadd;
+                pbv[r] = P - 1;
+                bias[r] = cadd;
                 if (!pos_clamped) {
-                    pb = min(max(prow - min(j, n), 0), P - 1);
-                    bias += ptab[pb];
+                    pbv[r] = min(max(prow - min(j, n), 0), P - 1);
+                    bias[r] += ptab[pbv[r]];
                 }
-                int tbk = 0;
+                tbv[r] = 0;
                 if (!tb.constant) {
                     if (!tb.wide) {
                         const uint32_t z = __builtin_clz(sad_u32(ei, codes[c], 1u));
-                        bias += s.tt_fast[z];
-                        tbk = min(NT - 1, 31 - (int)z);
+                        bias[r] += s.tt_fast[z];
+                        tbv[r] = min(NT - 1, 31 - (int)z);
                     } else {
                         const int64_t tj = j < L ? p.ts[row0 + j] : t_first;
                         const int64_t dt = ti64 - tj;
                         const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
                         const int bl = bit_length_u64(ad);
-                        bias += s.tt_wide[bl];
-                        tbk = min(NT - 1, bl);
+                        bias[r] += s.tt_wide[bl];
+                        tbv[r] = min(NT - 1, bl);
                     }
                 }
+            }
+            // (2) G = dA * act'(S), masked (a block of history keys that all
+            //     precede every row of the wave needs no mask)
+            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0) && (wrow0 + 31 < L);
+            float gv[16];
+            float gsum = 0.0f;
+            float tsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                const bool vis = full || (j <= vis_lim) | (j == vis_self);
                 float a, slope;
-                act_and_slope(sacc[r] + bias, silu, a, slope);
+                act_and_slope(sacc[r] + bias[r], silu, a, slope);
                 const float g = vis ? gacc[r] * slope : 0.0f;
                 gv[r] = g;
                 gsum += g;
-                if (vis) {
-                    if (!pos_clamped) atomicAdd(&hist[pb], g);
-                    if (!tb.constant) atomicAdd(&hist[P + tbk], g);
+                if (few_buckets) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) tsum[k] += (tbv[r] - tlo == k) ? g : 0.0f;
                 }
             }
-            if (pos_clamped || tb.constant) {
-                gsum = wave_sum(gsum);
-                if (lane == 0) {
-                    if (pos_clamped) atomicAdd(&hist[P - 1], gsum);
-                    if (tb.constant) atomicAdd(&hist[P + min(NT - 1, 31 - tb.cz)], gsum);
-                }
+            // (3) block sums (cross-lane, no LDS)
+            if (pos_clamped || tb.constant) gsum = wave_total(gsum);
+            if (few_buckets) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (tlo + k <= thi) tsum[k] = wave_total(tsum[k]);
             }
 
-            // dQ += G K over the tile's two 16-key chunks
+            // (4) dQ += G K over the tile's two 16-key chunks
             bf16x8 pg[2];
             pack_a(gv, pg);
 #pragma unroll
@@ -433,6 +490,43 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 read_v_chunk(kt_lds, c, lane, kf);
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, kf[nb]), dqa[nb]);
+            }
+
+            // (5) the histogram updates.  When the wave's rows are all history
+            //     rows, the position bucket of a visible pair is
+            //     min(i - j, P - 1): the block's 63 diagonals, summed through
+            //     the skewed scratch with plain LDS writes and reads, take one
+            //     atomic each (LDS float atomics are slow).  Otherwise, and
+            //     for time buckets beyond the register sums, per element.
+            const bool diag = !pos_clamped && wrow0 + 31 < n;
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    scratch[l32 * 64 + (l32 + 31 - c)] = gv[r];
+                }
+                // lane u: diagonal rho - c = u - 31 (cells off the band are 0)
+                float dsum = 0.0f;
+#pragma unroll
+                for (int rho = 0; rho < 32; ++rho) dsum += scratch[rho * 64 + lane];
+                const int pb = wrow0 - j0 + lane - 31;
+                if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (gv[r] != 0.0f) {
+                    if (!pos_clamped && !diag) atomicAdd(&hist[pbv[r]], gv[r]);
+                    if (!tb.constant && !few_buckets) atomicAdd(&hist[P + tbv[r]], gv[r]);
+                }
+            }
+            if (lane == 63) {
+                if (pos_clamped) atomicAdd(&hist[P - 1], gsum);
+                if (tb.constant) atomicAdd(&hist[P + tlo], gsum);
+                if (few_buckets) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (tlo + k <= thi) atomicAdd(&hist[P + tlo + k], tsum[k]);
+                }
             }
         }
 
@@ -712,7 +806,7 @@ __global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2,
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
     b += sizeof(float) * (size_t)((P + 3) & ~3);
-    if (hist) b += sizeof(float) * 4 * (size_t)((P + NT + 3) & ~3);
+    if (hist) b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 32 * 64);
     return b;
 }
 

@@ -232,7 +232,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* args, void* workspace, size_t 
  * fixed order (run-to-run identical).  attn.y, attn.o (without dy) and the
  * attention events are not used.
  * Limits: bf16 with d = 128; num_pos_buckets + num_time_buckets at most
- * about 4100 (the tables and per-wave histograms of their gradients share a
+ * about 2600 (the tables and per-wave histograms of their gradients share a
  * workgroup's LDS with the tile ring).
  * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED (fp32, d != 128, tables too
  * long), HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
