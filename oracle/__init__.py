@@ -50,6 +50,7 @@ def _lib():
         lib.hstu_oracle_ln_gate.restype = None
         lib.hstu_oracle_attn_bwd.restype = None
         lib.hstu_oracle_ln_gate_bwd.restype = None
+        lib.hstu_oracle_layer_bwd.restype = None
         lib.hstu_oracle_layer.restype = None
         lib.hstu_oracle_mfalcon_score.restype = None
         lib.hstu_oracle_tiles.restype = ctypes.c_int64
@@ -217,6 +218,43 @@ def layer(x, w1, w2, offsets, ts, rab_pos, rab_time, alpha, H, d, *, b1=None, b2
         _ptr(w2, _f64p), _ptr(b2a, _f64p), _ptr(tsa, _i64p),
         _ptr(rp, _f64p), ctypes.c_int32(rp.shape[-1]), _ptr(rt, _f64p), ctypes.c_int32(rt.shape[-1]),
         ctypes.c_double(alpha), ctypes.c_double(eps), _ptr(out, _f64p), ctypes.c_int32(num_threads))
+    return out
+
+
+def layer_bwd(x, w1, w2, offsets, ts, rab_pos, rab_time, alpha, H, d, dx_out, *, b1=None,
+              b2=None, eps=1e-5, num_candidates=None, num_threads=0) -> dict:
+    """Gradients of one HSTU layer (``layer``) for an upstream gradient dx_out.
+
+    Returns a dict with dx [T, D], dw1 [4Hd, D], db1 [4Hd], dw2 [D, Hd],
+    db2 [D], drab_pos [P], drab_time [NT] (shared tables).  Chain rule through
+    f2, the gate, the attention and f1 + SiLU (pinned by central finite
+    differences of ``layer``).
+    """
+    x = _f64(x)
+    T, D = x.shape
+    off = _i32(offsets)
+    B = len(off) - 1
+    w1 = _f64(w1); w2 = _f64(w2)
+    zw, hd = 4 * H * d, H * d
+    assert w1.shape == (zw, D) and w2.shape == (D, hd)
+    b1a = None if b1 is None else _f64(b1)
+    b2a = None if b2 is None else _f64(b2)
+    rp = _f64(rab_pos); rt = _f64(rab_time)
+    g = _f64(dx_out)
+    out = {"dx": np.zeros_like(x), "dw1": np.zeros((zw, D)), "db1": np.zeros(zw),
+           "dw2": np.zeros((D, hd)), "db2": np.zeros(D), "drab_pos": np.zeros_like(rp),
+           "drab_time": np.zeros_like(rt)}
+    tsa = np.ascontiguousarray(ts, dtype=np.int64)
+    nc = _i32(num_candidates)
+    _lib().hstu_oracle_layer_bwd(
+        ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(d), ctypes.c_int32(D),
+        _ptr(off, _i32p), _ptr(nc, _i32p), _ptr(x, _f64p), _ptr(w1, _f64p), _ptr(b1a, _f64p),
+        _ptr(w2, _f64p), _ptr(b2a, _f64p), _ptr(tsa, _i64p),
+        _ptr(rp, _f64p), ctypes.c_int32(rp.shape[-1]), _ptr(rt, _f64p), ctypes.c_int32(rt.shape[-1]),
+        ctypes.c_double(alpha), ctypes.c_double(eps), _ptr(g, _f64p),
+        _ptr(out["dx"], _f64p), _ptr(out["dw1"], _f64p), _ptr(out["db1"], _f64p),
+        _ptr(out["dw2"], _f64p), _ptr(out["db2"], _f64p), _ptr(out["drab_pos"], _f64p),
+        _ptr(out["drab_time"], _f64p), ctypes.c_int32(num_threads))
     return out
 
 

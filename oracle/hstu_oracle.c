@@ -428,6 +428,117 @@ void hstu_oracle_layer(int32_t B, int32_t H, int32_t d, int32_t D,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Layer gradients: with dX_out = dLoss/dX_out given, the chain rule through */
+/* the layer above, in reverse:                                               */
+/*   f2:   dY = dX_out W2;  dW2 = dX_out^T Y;  db2 = sum_t dX_out             */
+/*   gate and attention: dO, dU, then dQ, dK, dV and the table gradients     */
+/*         (hstu_oracle_ln_gate_bwd, hstu_oracle_attn_bwd)                     */
+/*   f1:   dP = dZ (.) SiLU'(P) with P = X W1^T + b1 and dZ = dU | dV | dQ | dK */
+/*         dX = dX_out + dP W1;  dW1 = dP^T X;  db1 = sum_t dP               */
+/* (the residual passes dX_out straight through).  Shared tables.  Sums over */
+/* tokens run in row order.                                                   */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_layer_bwd(int32_t B, int32_t H, int32_t d, int32_t D,
+                           const int32_t* offsets, const int32_t* num_candidates,
+                           const double* x, const double* w1, const double* b1,
+                           const double* w2, const double* b2,
+                           const int64_t* timestamps,
+                           const double* rab_pos, int32_t num_pos_buckets,
+                           const double* rab_time, int32_t num_time_buckets,
+                           double alpha, double eps, const double* dx_out,
+                           double* dx, double* dw1, double* db1, double* dw2, double* db2,
+                           double* drab_pos, double* drab_time, int32_t num_threads) {
+    set_threads(num_threads);
+    (void)b2;
+    int64_t row0 = offsets[0];
+    int64_t T = (int64_t)offsets[B] - row0;
+    int32_t hd = H * d;
+    int32_t zw = 4 * hd;
+    size_t tz = (size_t)(T * zw + 1), th = (size_t)(T * hd + 1);
+    double* pre = (double*)malloc(sizeof(double) * tz);
+    double* z = (double*)malloc(sizeof(double) * tz);
+    double* dz = (double*)calloc(tz, sizeof(double));
+    double* gz = (double*)calloc(tz, sizeof(double));   /* dO at the V columns' stride */
+    double* ob = (double*)malloc(sizeof(double) * th);
+    double* yb = (double*)malloc(sizeof(double) * th);
+    double* dy = (double*)malloc(sizeof(double) * th);
+    double* dob = (double*)malloc(sizeof(double) * th);
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B + 1));
+    for (int32_t b = 0; b <= B; ++b) off[b] = (int32_t)(offsets[b] - row0);
+    const double* xr = x + row0 * D;
+    const double* gr = dx_out + row0 * D;
+
+    /* forward intermediates */
+    linear(T, zw, D, xr, D, w1, b1, pre, zw);
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < T * zw; ++e) z[e] = hstu_oracle_silu(pre[e]);
+    hstu_oracle_attn(B, H, d, d, off, NULL, num_candidates, z + 2 * hd, zw, z + 3 * hd, zw, z + hd, zw,
+                     timestamps + row0, rab_pos, num_pos_buckets, rab_time, num_time_buckets,
+                     0, 0, alpha, ORACLE_ACT_SILU, ob, hd, num_threads);
+    hstu_oracle_ln_gate(T, hd, ob, hd, z, zw, eps, yb, hd, num_threads);
+
+    /* f2 */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < hd; ++h) {
+            double s = 0.0;
+            for (int32_t m = 0; m < D; ++m) s += gr[t * D + m] * w2[(int64_t)m * hd + h];
+            dy[t * hd + h] = s;
+        }
+#pragma omp parallel for schedule(static)
+    for (int32_t m = 0; m < D; ++m) {
+        for (int32_t h = 0; h < hd; ++h) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += gr[t * D + m] * yb[t * hd + h];
+            dw2[(int64_t)m * hd + h] = s;
+        }
+        if (db2) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += gr[t * D + m];
+            db2[m] = s;
+        }
+    }
+
+    /* gate (dU into dZ's U columns) and attention (dV, dQ, dK into theirs) */
+    hstu_oracle_ln_gate_bwd(T, hd, ob, hd, z, zw, dy, hd, eps, dob, hd, dz, zw, num_threads);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t h = 0; h < hd; ++h) gz[t * zw + h] = dob[t * hd + h];
+    hstu_oracle_attn_bwd(B, H, d, d, off, NULL, num_candidates, z + 2 * hd, z + 3 * hd, z + hd, zw, zw,
+                         timestamps + row0, rab_pos, num_pos_buckets, rab_time, num_time_buckets, 0, 0,
+                         alpha, ORACLE_ACT_SILU, gz, dz + 2 * hd, dz + 3 * hd, dz + hd, drab_pos, drab_time,
+                         num_threads);
+
+    /* f1 + SiLU */
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < T * zw; ++e) {
+        double sg = 1.0 / (1.0 + exp(-pre[e]));
+        dz[e] *= sg * (1.0 + pre[e] * (1.0 - sg));
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t k = 0; k < D; ++k) {
+            double s = gr[t * D + k];
+            for (int32_t n = 0; n < zw; ++n) s += dz[t * zw + n] * w1[(int64_t)n * D + k];
+            dx[(row0 + t) * D + k] = s;
+        }
+#pragma omp parallel for schedule(static)
+    for (int32_t n = 0; n < zw; ++n) {
+        for (int32_t k = 0; k < D; ++k) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += dz[t * zw + n] * xr[t * D + k];
+            dw1[(int64_t)n * D + k] = s;
+        }
+        if (db1) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t) s += dz[t * zw + n];
+            db1[n] = s;
+        }
+    }
+    free(off); free(dob); free(dy); free(yb); free(ob); free(gz); free(dz); free(z); free(pre);
+}
+
+/* ------------------------------------------------------------------------ */
 /* M-FALCON ranking scores: for candidate c of sequence b,                    */
 /*   s[b, c] = < Y[n_b + c, :], w >,  Y = LayerNorm(O) (.) U over H*d_v.       */
 /* The attention output is computed for all rows in one pass (history rows   */

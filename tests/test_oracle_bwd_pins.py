@@ -143,3 +143,68 @@ def test_ln_gate_bwd_matches_finite_differences_and_torch():
     y.backward(torch.tensor(dy))
     np.testing.assert_allclose(do, ot.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(du, ut.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _layer_case(seed=0, with_bias=True, mfalcon=False):
+    rng = np.random.default_rng(seed)
+    H, d, D = 2, 2, 4
+    offsets = np.array([0, 5, 8], dtype=np.int32)
+    T = int(offsets[-1])
+    x = rng.normal(0, 0.7, size=(T, D))
+    w1 = rng.normal(0, 0.5, size=(4 * H * d, D))
+    w2 = rng.normal(0, 0.5, size=(D, H * d))
+    b1 = rng.normal(0, 0.2, size=4 * H * d) if with_bias else None
+    b2 = rng.normal(0, 0.2, size=D) if with_bias else None
+    ts = np.cumsum(rng.integers(1, 40, size=T)).astype(np.int64)
+    rp = rng.normal(0, 0.3, size=4)
+    rt = rng.normal(0, 0.3, size=5)
+    nc = np.array([2, 1], dtype=np.int32) if mfalcon else None
+    return dict(x=x, w1=w1, w2=w2, b1=b1, b2=b2, offsets=offsets, ts=ts, rp=rp, rt=rt, H=H, d=d,
+                alpha=0.41, eps=1e-3, nc=nc)
+
+
+def _layer_loss(c, g, **over):
+    a = dict(c)
+    a.update(over)
+    y = oracle.layer(a["x"], a["w1"], a["w2"], a["offsets"], a["ts"], a["rp"], a["rt"], a["alpha"],
+                     a["H"], a["d"], b1=a["b1"], b2=a["b2"], eps=a["eps"], num_candidates=a["nc"])
+    return float(np.sum(y * g))
+
+
+@pytest.mark.parametrize("mfalcon", [False, True])
+def test_layer_bwd_matches_finite_differences(mfalcon):
+    c = _layer_case(1, mfalcon=mfalcon)
+    g = np.random.default_rng(2).normal(size=c["x"].shape)
+    got = oracle.layer_bwd(c["x"], c["w1"], c["w2"], c["offsets"], c["ts"], c["rp"], c["rt"],
+                           c["alpha"], c["H"], c["d"], g, b1=c["b1"], b2=c["b2"], eps=c["eps"],
+                           num_candidates=c["nc"])
+    for name, key in [("x", "dx"), ("w1", "dw1"), ("b1", "db1"), ("w2", "dw2"), ("b2", "db2"),
+                      ("rp", "drab_pos"), ("rt", "drab_time")]:
+        arr = c[name]
+        ref = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a1 = arr.copy(); a1[idx] += STEP
+            a0 = arr.copy(); a0[idx] -= STEP
+            ref[idx] = (_layer_loss(c, g, **{name: a1}) - _layer_loss(c, g, **{name: a0})) / (2 * STEP)
+        np.testing.assert_allclose(got[key], ref, rtol=1e-6, atol=1e-8, err_msg=f"layer d{name}")
+
+
+def test_layer_bwd_residual_and_bias_identities():
+    """dX - dX_out is the part through f1 alone, and the bias gradients are the
+    token sums of the pre-activation gradients: db2 = sum_t dX_out, and with
+    x = 0 rows db1 equals the gradient through a constant input column."""
+    c = _layer_case(3)
+    g = np.random.default_rng(4).normal(size=c["x"].shape)
+    got = oracle.layer_bwd(c["x"], c["w1"], c["w2"], c["offsets"], c["ts"], c["rp"], c["rt"],
+                           c["alpha"], c["H"], c["d"], g, b1=c["b1"], b2=c["b2"], eps=c["eps"])
+    np.testing.assert_allclose(got["db2"], g.sum(axis=0), rtol=1e-12, atol=1e-12)
+    # a bias is a weight on an all-ones input column: extend X with ones and W1 with b1
+    x1 = np.concatenate([c["x"], np.ones((c["x"].shape[0], 1))], axis=1)
+    w11 = np.concatenate([c["w1"], c["b1"][:, None]], axis=1)
+    g1 = np.concatenate([g, np.zeros((g.shape[0], 1))], axis=1)
+    w21 = np.concatenate([c["w2"], np.zeros((1, c["w2"].shape[1]))], axis=0)
+    b21 = np.concatenate([c["b2"], [0.0]])
+    ext = oracle.layer_bwd(x1, w11, w21, c["offsets"], c["ts"], c["rp"], c["rt"], c["alpha"],
+                           c["H"], c["d"], g1, b2=b21, eps=c["eps"])
+    np.testing.assert_allclose(ext["dw1"][:, -1], got["db1"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ext["dw1"][:, :-1], got["dw1"], rtol=1e-10, atol=1e-12)
