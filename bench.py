@@ -245,13 +245,18 @@ def time_case(case, steps, warmup, core_events=True):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longseq_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc", "attn_bf16.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc", f)
+               for f in ("attn_bf16.hip", "tile_ops.h", "hstu_device.h")]
 
 
 def kernel_hash() -> str:
+    """Hash of the sources the attention-core kernel is compiled from."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for src in KERNEL_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
