@@ -94,6 +94,16 @@ class LayerArgs(ctypes.Structure):
     ]
 
 
+class LayerBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("layer", LayerArgs),
+        ("dx_out", _vp), ("dx", _vp),
+        ("dw1", _vp), ("db1", _vp), ("dw2", _vp), ("db2", _vp),
+        ("drab_pos", _vp), ("drab_time", _vp),
+    ]
+
+
 # every symbol include/hstu.h declares
 EXPORTS = [
     "hstu_abi_version", "hstu_status_string", "hstu_last_error",
@@ -101,6 +111,7 @@ EXPORTS = [
     "hstu_mfalcon_workspace_bytes", "mfalcon_score",
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
     "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
+    "hstu_layer_bwd_workspace_bytes", "hstu_layer_bwd",
     "hstu_attn_schedule",
 ]
 
@@ -143,6 +154,10 @@ def load(path: str = LIB_PATH):
     lib.hstu_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnBwdArgs)]
     lib.hstu_attn_bwd.restype = _i32
     lib.hstu_attn_bwd.argtypes = [ctypes.POINTER(AttnBwdArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_layer_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.hstu_layer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LayerBwdArgs)]
+    lib.hstu_layer_bwd.restype = _i32
+    lib.hstu_layer_bwd.argtypes = [ctypes.POINTER(LayerBwdArgs), _vp, ctypes.c_size_t, _vp]
     lib.hstu_attn_schedule.restype = _i32
     lib.hstu_attn_schedule.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t,
                                        ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64),

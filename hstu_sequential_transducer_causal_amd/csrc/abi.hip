@@ -455,6 +455,34 @@ hstu_status validate_layer(const hstu_layer_args* l) {
     return HSTU_OK;
 }
 
+// The attention arguments of a layer whose Z (U | V | Q | K), O and Y sit in
+// the given buffers.
+hstu_attn_args layer_attn_args(const hstu_layer_args* l, uint16_t* z, uint16_t* o, uint16_t* y) {
+    const int hd = l->H * l->d;
+    hstu_attn_args a;
+    memset(&a, 0, sizeof(a));
+    a.struct_size = sizeof(a);
+    a.B = l->B; a.H = l->H; a.d_qk = l->d; a.d_v = l->d;
+    a.max_seq_len = l->max_seq_len;
+    a.num_rows = l->num_rows;
+    a.seq_offsets = l->seq_offsets;
+    a.num_candidates = l->num_candidates;
+    a.dtype = HSTU_BF16;
+    a.act = HSTU_ACT_SILU;
+    a.u = z;              a.u_stride = 4 * hd;
+    a.v = z + 1 * hd;     a.v_stride = 4 * hd;
+    a.q = z + 2 * hd;     a.q_stride = 4 * hd;
+    a.k = z + 3 * hd;     a.k_stride = 4 * hd;
+    a.timestamps = l->timestamps;
+    a.rab_pos = l->rab_pos; a.num_pos_buckets = l->num_pos_buckets;
+    a.rab_time = l->rab_time; a.num_time_buckets = l->num_time_buckets;
+    a.alpha = l->alpha;
+    a.o = o; a.o_stride = hd;
+    a.y = y; a.y_stride = hd;
+    a.ln_eps = l->ln_eps;
+    return a;
+}
+
 struct LayerWs {
     size_t z, o, y, sched, total;
 };
@@ -468,6 +496,88 @@ LayerWs layer_ws(const hstu_layer_args* l) {
     w.y = align256(w.o + T * hd * 2);
     w.sched = align256(w.y + T * hd * 2);
     w.total = hstu::sched_layout(l->B, l->H, l->max_seq_len, hstu::kBf16TileM, l->d, l->num_rows, w.sched).bytes;
+    return w;
+}
+
+// ---- layer gradients
+
+// The attention-gradient arguments of a layer (U | V | Q | K, O, Y and the
+// gradient buffers in the layer's workspace).
+hstu_attn_bwd_args layer_attn_bwd_args(const hstu_layer_args* l, uint16_t* z, uint16_t* o, uint16_t* y,
+                                       uint16_t* dy, uint16_t* dz, float* drp, float* drt) {
+    const int hd = l->H * l->d;
+    hstu_attn_bwd_args g;
+    memset(&g, 0, sizeof(g));
+    g.struct_size = sizeof(g);
+    g.attn = layer_attn_args(l, z, o, y);
+    g.attn.y = nullptr;
+    g.dy = dy; g.dy_stride = hd;
+    g.du = dz;              g.du_stride = 4 * hd;
+    g.dv = dz + 1 * hd;     g.dv_stride = 4 * hd;
+    g.dq = dz + 2 * hd;     g.dq_stride = 4 * hd;
+    g.dk = dz + 3 * hd;     g.dk_stride = 4 * hd;
+    g.drab_pos = drp;
+    g.drab_time = drt;
+    return g;
+}
+
+hstu_status validate_layer_bwd(const hstu_layer_bwd_args* g) {
+    if (!g) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (g->struct_size != sizeof(hstu_layer_bwd_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_layer_bwd_args) %zu", g->struct_size,
+                    sizeof(hstu_layer_bwd_args));
+    hstu_layer_args l = g->layer;
+    if (!l.x_out) l.x_out = const_cast<void*>(l.x);   // not written by the gradients
+    hstu_status st = validate_layer(&l);
+    if (st != HSTU_OK) return st;
+    const int hd = l.H * l.d;
+    if (l.D % 128 != 0 || hd % 128 != 0)
+        return fail(HSTU_ERR_UNSUPPORTED, "layer gradients need D %% 128 == 0 and H*d %% 128 == 0");
+    if (int64_t(l.num_rows) * 2 * std::max(4 * hd, l.D) > int64_t(0x7fffffff))
+        return fail(HSTU_ERR_UNSUPPORTED, "num_rows * row bytes must stay below 2^31");
+    if (l.B > 0 && l.num_rows > 0) {
+        if (!g->dx_out || !g->dx || !g->dw1 || !g->dw2)
+            return fail(HSTU_ERR_ARG, "dx_out, dx, dw1 and dw2 must be non-NULL");
+        if (!aligned16(g->dx_out) || !aligned16(g->dx))
+            return fail(HSTU_ERR_UNSUPPORTED, "dx_out and dx must be 16-byte aligned");
+    }
+    // the attention part's own limits (its buffers are the workspace's: a
+    // stand-in address, never dereferenced, checks the rest)
+    uint16_t* fake = reinterpret_cast<uint16_t*>(uintptr_t(0x10000));
+    float* fakef = reinterpret_cast<float*>(uintptr_t(0x10000));
+    hstu_attn_bwd_args ab = layer_attn_bwd_args(&l, fake, fake, fake, fake, fake, fakef, fakef);
+    return validate_bwd(&ab);
+}
+
+struct LayerBwdWs {
+    size_t z, pre, o, y, dy, dz, w1t, w2t, sched, attn, part, colsum, total;
+};
+
+LayerBwdWs layer_bwd_ws(const hstu_layer_bwd_args* g) {
+    const hstu_layer_args* l = &g->layer;
+    LayerBwdWs w;
+    const size_t T = size_t(l->num_rows);
+    const size_t hd = size_t(l->H) * l->d, zw = 4 * hd, D = size_t(l->D);
+    w.z = 0;
+    w.pre = align256(w.z + T * zw * 2);
+    w.o = align256(w.pre + T * zw * 2);
+    w.y = align256(w.o + T * hd * 2);
+    w.dy = align256(w.y + T * hd * 2);
+    w.dz = align256(w.dy + T * hd * 2);
+    w.w1t = align256(w.dz + T * zw * 2);
+    w.w2t = align256(w.w1t + D * zw * 2);
+    w.sched = align256(w.w2t + hd * D * 2);
+    const size_t sched_end = hstu::sched_layout(l->B, l->H, l->max_seq_len, hstu::kBf16TileM, l->d, l->num_rows,
+                                                w.sched).bytes;
+    w.attn = align256(sched_end);
+    uint16_t* fake = reinterpret_cast<uint16_t*>(uintptr_t(0x10000));   // sizes only
+    float* fakef = reinterpret_cast<float*>(uintptr_t(0x10000));
+    hstu_attn_bwd_args ab = layer_attn_bwd_args(l, fake, fake, fake, fake, fake, fakef, fakef);
+    w.part = align256(w.attn + bwd_ws(&ab).total);
+    const size_t p1 = size_t(hstu::gemm_tn_splits(l->num_rows, int(zw), l->D)) * zw * D;
+    const size_t p2 = size_t(hstu::gemm_tn_splits(l->num_rows, l->D, int(hd))) * D * hd;
+    w.colsum = align256(w.part + sizeof(float) * std::max(p1, p2));
+    w.total = align256(w.colsum + sizeof(float) * hstu::colsum_part_floats(int(std::max(zw, D))));
     return w;
 }
 
@@ -508,27 +618,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     hipError_t e = hstu::launch_gemm_bf16(g1, stream);
     if (e != hipSuccess) return device_error(e, "f1 launch");
 
-    hstu_attn_args a;
-    memset(&a, 0, sizeof(a));
-    a.struct_size = sizeof(a);
-    a.B = l->B; a.H = l->H; a.d_qk = l->d; a.d_v = l->d;
-    a.max_seq_len = l->max_seq_len;
-    a.num_rows = l->num_rows;
-    a.seq_offsets = l->seq_offsets;
-    a.num_candidates = l->num_candidates;
-    a.dtype = HSTU_BF16;
-    a.act = HSTU_ACT_SILU;
-    a.u = z;              a.u_stride = 4 * hd;
-    a.v = z + 1 * hd;     a.v_stride = 4 * hd;
-    a.q = z + 2 * hd;     a.q_stride = 4 * hd;
-    a.k = z + 3 * hd;     a.k_stride = 4 * hd;
-    a.timestamps = l->timestamps;
-    a.rab_pos = l->rab_pos; a.num_pos_buckets = l->num_pos_buckets;
-    a.rab_time = l->rab_time; a.num_time_buckets = l->num_time_buckets;
-    a.alpha = l->alpha;
-    a.o = o; a.o_stride = hd;
-    a.y = y; a.y_stride = hd;
-    a.ln_eps = l->ln_eps;
+    hstu_attn_args a = layer_attn_args(l, z, o, y);
     Sched s = carve_sched(&a, ws, lw.sched);
     e = run_sched(&a, s, stream);
     if (e != hipSuccess) return device_error(e, "scheduler launch");
@@ -548,6 +638,126 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     g2.silu = 0;
     e = hstu::launch_gemm_bf16(g2, stream);
     if (e != hipSuccess) return device_error(e, "f2 launch");
+    return ok();
+}
+
+size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* g) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_layer_bwd(g);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return layer_bwd_ws(g).total;
+}
+
+hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_layer_bwd(g);
+    if (st != HSTU_OK) return st;
+    const hstu_layer_args* l = &g->layer;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (l->B == 0 || l->num_rows == 0) {   // empty batch: zero parameter gradients
+        const size_t zw4 = size_t(4) * l->H * l->d;
+        hipError_t e = hipSuccess;
+        auto clear = [&](void* p, size_t bytes) {
+            if (p && e == hipSuccess) e = hipMemsetAsync(p, 0, bytes, stream);
+        };
+        clear(g->dw1, sizeof(float) * zw4 * l->D);
+        clear(g->db1, sizeof(float) * zw4);
+        clear(g->dw2, sizeof(float) * size_t(l->D) * l->H * l->d);
+        clear(g->db2, sizeof(float) * l->D);
+        clear(g->drab_pos, sizeof(float) * l->num_pos_buckets);
+        clear(g->drab_time, sizeof(float) * l->num_time_buckets);
+        return e == hipSuccess ? ok() : device_error(e, "clearing the gradients");
+    }
+    const LayerBwdWs lw = layer_bwd_ws(g);
+    st = check_workspace(ws, ws_bytes, lw.total);
+    if (st != HSTU_OK) return st;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const int hd = l->H * l->d, zw = 4 * hd, D = l->D;
+    const int64_t T = l->num_rows;
+    uint16_t* z = reinterpret_cast<uint16_t*>(w + lw.z);
+    uint16_t* pre = reinterpret_cast<uint16_t*>(w + lw.pre);
+    uint16_t* o = reinterpret_cast<uint16_t*>(w + lw.o);
+    uint16_t* y = reinterpret_cast<uint16_t*>(w + lw.y);
+    uint16_t* dy = reinterpret_cast<uint16_t*>(w + lw.dy);
+    uint16_t* dz = reinterpret_cast<uint16_t*>(w + lw.dz);
+    uint16_t* w1t = reinterpret_cast<uint16_t*>(w + lw.w1t);
+    uint16_t* w2t = reinterpret_cast<uint16_t*>(w + lw.w2t);
+    float* part = reinterpret_cast<float*>(w + lw.part);
+    float* cpart = reinterpret_cast<float*>(w + lw.colsum);
+
+    // forward recomputation: Z and its pre-activation, then O and Y
+    hstu::GemmArgs g1;
+    g1.M = T; g1.N = zw; g1.K = D;
+    g1.a = l->x; g1.lda = D;
+    g1.b = l->w1; g1.ldb = D;
+    g1.bias = l->b1;
+    g1.residual = nullptr; g1.ldr = 0;
+    g1.c = z; g1.ldc = zw;
+    g1.silu = 1;
+    g1.c_pre = pre; g1.ldcp = zw;
+    hipError_t e = hstu::launch_gemm_bf16(g1, stream);
+    if (e != hipSuccess) return device_error(e, "f1 launch");
+    hstu_attn_args a = layer_attn_args(l, z, o, y);
+    Sched s = carve_sched(&a, ws, lw.sched);
+    e = run_sched(&a, s, stream);
+    if (e == hipSuccess) e = run_core(&a, s, stream);
+    if (e == hipSuccess) e = run_ln_gate(&a, s, nullptr, nullptr, 0, false, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+
+    // f2: dY = dX_out W2 (through W2^T), dW2 = dX_out^T Y, db2 = sum_t dX_out
+    e = hstu::launch_transpose(l->w2, D, hd, w2t, stream);
+    if (e == hipSuccess) e = hstu::launch_transpose(l->w1, zw, D, w1t, stream);
+    if (e != hipSuccess) return device_error(e, "transpose launch");
+    hstu::GemmArgs gy;
+    gy.M = T; gy.N = hd; gy.K = D;
+    gy.a = g->dx_out; gy.lda = D;
+    gy.b = w2t; gy.ldb = D;
+    gy.bias = nullptr;
+    gy.residual = nullptr; gy.ldr = 0;
+    gy.c = dy; gy.ldc = hd;
+    gy.silu = 0;
+    e = hstu::launch_gemm_bf16(gy, stream);
+    if (e != hipSuccess) return device_error(e, "dY launch");
+    hstu::GemmTnArgs t2;
+    t2.a = g->dx_out; t2.lda = D;
+    t2.b = y; t2.ldb = hd;
+    t2.T = T; t2.M = D; t2.N = hd;
+    t2.splits = hstu::gemm_tn_splits(T, D, hd);
+    t2.part = part;
+    t2.c = g->dw2;
+    e = hstu::launch_gemm_tn(t2, stream);
+    if (e == hipSuccess && g->db2) e = hstu::launch_colsum(g->dx_out, D, T, D, cpart, g->db2, stream);
+    if (e != hipSuccess) return device_error(e, "dW2 launch");
+
+    // gate and attention: dU | dV | dQ | dK into dZ
+    hstu_attn_bwd_args ab = layer_attn_bwd_args(l, z, o, y, dy, dz, g->drab_pos, g->drab_time);
+    st = hstu_attn_bwd(&ab, w + lw.attn, lw.part - lw.attn, stream);
+    if (st != HSTU_OK) return st;
+
+    // f1 + SiLU: dP = dZ SiLU'(P), dX = dX_out + dP W1, dW1 = dP^T X, db1 = sum_t dP
+    e = hstu::launch_silu_grad(dz, pre, T * zw, stream);
+    if (e != hipSuccess) return device_error(e, "SiLU slope launch");
+    hstu::GemmTnArgs t1;
+    t1.a = dz; t1.lda = zw;
+    t1.b = l->x; t1.ldb = D;
+    t1.T = T; t1.M = zw; t1.N = D;
+    t1.splits = hstu::gemm_tn_splits(T, zw, D);
+    t1.part = part;
+    t1.c = g->dw1;
+    e = hstu::launch_gemm_tn(t1, stream);
+    if (e == hipSuccess && g->db1) e = hstu::launch_colsum(dz, zw, T, zw, cpart, g->db1, stream);
+    if (e != hipSuccess) return device_error(e, "dW1 launch");
+    hstu::GemmArgs gx;
+    gx.M = T; gx.N = D; gx.K = zw;
+    gx.a = dz; gx.lda = zw;
+    gx.b = w1t; gx.ldb = zw;
+    gx.bias = nullptr;
+    gx.residual = g->dx_out; gx.ldr = D;
+    gx.c = g->dx; gx.ldc = D;
+    gx.silu = 0;
+    e = hstu::launch_gemm_bf16(gx, stream);
+    if (e != hipSuccess) return device_error(e, "dX launch");
     return ok();
 }
 

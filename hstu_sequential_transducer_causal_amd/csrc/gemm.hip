@@ -30,6 +30,7 @@ struct Params {
     const uint16_t* res; int64_t ldr;
     uint16_t* c; int64_t ldc;
     int silu;
+    uint16_t* cp; int64_t ldcp;   // optional pre-activation output
 };
 
 // Row r of a [128][64] bf16 tile occupies 128 bytes = 8 chunks of 16 bytes;
@@ -111,6 +112,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_bf16_kernel(Params p) {
                 const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + r;
                 if (m < p.M) {
                     float x = acc[i][j][r] + bias;
+                    if (p.cp) p.cp[m * p.ldcp + n] = f32_to_bf16_bits(x);
                     if (p.silu) x = silu_fast(x);
                     if (p.res) x += bf16_to_f32(p.res[m * p.ldr + n]);
                     p.c[m * p.ldc + n] = f32_to_bf16_bits(x);
@@ -132,6 +134,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
     p.res = static_cast<const uint16_t*>(g.residual); p.ldr = g.ldr;
     p.c = static_cast<uint16_t*>(g.c); p.ldc = g.ldc;
     p.silu = g.silu;
+    p.cp = static_cast<uint16_t*>(g.c_pre); p.ldcp = g.ldcp;
     dim3 grid(g.N / TN, (unsigned)((g.M + TM - 1) / TM));
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();

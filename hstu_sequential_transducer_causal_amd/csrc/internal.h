@@ -257,9 +257,35 @@ struct GemmArgs {
     int64_t ldr;
     void* c; int64_t ldc;
     int silu;                // apply SiLU to the result
+    void* c_pre = nullptr;   // with silu: also the value before it (bf16), or NULL
+    int64_t ldcp = 0;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
+
+// Weight gradients: C[M, N] (fp32) = sum_t A[t, M] B[t, N] over T tokens,
+// A and B bf16 token-major; M, N multiples of 128.  The tokens are split over
+// `splits` workgroup layers whose fp32 partials ([splits][M][N]) are added
+// in split order.
+struct GemmTnArgs {
+    const void* a; int64_t lda;
+    const void* b; int64_t ldb;
+    int64_t T;
+    int M, N;
+    int splits;
+    float* part;
+    float* c;
+};
+int gemm_tn_splits(int64_t T, int M, int N);
+hipError_t launch_gemm_tn(const GemmTnArgs& g, hipStream_t stream);
+
+// Column sums of a bf16 [T, C] matrix (fixed order), partials [64][C].
+size_t colsum_part_floats(int C);
+hipError_t launch_colsum(const void* x, int64_t ld, int64_t T, int C, float* part, float* out, hipStream_t stream);
+// dZ (.)= SiLU'(P), elementwise over `count` bf16 values (count % 8 == 0).
+hipError_t launch_silu_grad(void* dz, const void* pre, int64_t count, hipStream_t stream);
+// out[c][r] = in[r][c], bf16.
+hipError_t launch_transpose(const void* in, int R, int C, void* out, hipStream_t stream);
 
 int device_cu_count();
 

@@ -3,7 +3,7 @@
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
 Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score,
-hstu_layer_fwd, hstu_attn_schedule.
+hstu_layer_fwd, hstu_layer_bwd, hstu_attn_schedule.
 """
 from __future__ import annotations
 
@@ -276,6 +276,59 @@ def hstu_layer_fwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha,
     _lib.check(lib.hstu_layer_fwd(ctypes.byref(l), workspace.data_ptr(), workspace.numel(),
                                   _stream_ptr(stream)))
     return x_out
+
+
+def make_layer_bwd_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out, *,
+                        H: int, d: int, max_seq_len: int, dx, dw1, dw2, b1=None, b2=None, db1=None,
+                        db2=None, drab_pos=None, drab_time=None, num_candidates=None,
+                        ln_eps: float = 1e-5) -> _lib.LayerBwdArgs:
+    g = _lib.LayerBwdArgs()
+    g.struct_size = ctypes.sizeof(_lib.LayerBwdArgs)
+    g.layer = make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, H=H, d=d,
+                              max_seq_len=max_seq_len, x_out=x, b1=b1, b2=b2,
+                              num_candidates=num_candidates, ln_eps=ln_eps)
+    g.layer.x_out = None
+    g.dx_out, g.dx = dx_out.data_ptr(), dx.data_ptr()
+    g.dw1, g.dw2 = dw1.data_ptr(), dw2.data_ptr()
+    g.db1, g.db2 = _ptr(db1), _ptr(db2)
+    g.drab_pos, g.drab_time = _ptr(drab_pos), _ptr(drab_time)
+    return g
+
+
+def layer_bwd_workspace_bytes(g: _lib.LayerBwdArgs) -> int:
+    return int(_lib.load().hstu_layer_bwd_workspace_bytes(ctypes.byref(g)))
+
+
+def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out, *, H: int,
+                   d: int, max_seq_len: int, b1=None, b2=None, num_candidates=None,
+                   ln_eps: float = 1e-5, want_bias: bool = True, want_rab: bool = True, dx=None,
+                   workspace=None, stream=None):
+    """Gradients of one HSTU layer for dLoss/dX_out: returns a dict with dx
+    (bf16 [rows, D]), dw1 [4Hd, D], dw2 [D, Hd] and, if asked for, db1, db2,
+    drab_pos, drab_time (all float32)."""
+    lib = _lib.load()
+    dev = x.device
+    zw, D = 4 * H * d, x.shape[1]
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x) if dx is None else dx,
+           "dw1": torch.empty(zw, D, **f32), "dw2": torch.empty(D, H * d, **f32),
+           "db1": torch.empty(zw, **f32) if want_bias else None,
+           "db2": torch.empty(D, **f32) if want_bias else None,
+           "drab_pos": torch.empty(rab_pos.shape, **f32) if want_rab else None,
+           "drab_time": torch.empty(rab_time.shape, **f32) if want_rab else None}
+    g = make_layer_bwd_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out,
+                            H=H, d=d, max_seq_len=max_seq_len, dx=out["dx"], dw1=out["dw1"],
+                            dw2=out["dw2"], b1=b1, b2=b2, db1=out["db1"], db2=out["db2"],
+                            drab_pos=out["drab_pos"], drab_time=out["drab_time"],
+                            num_candidates=num_candidates, ln_eps=ln_eps)
+    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(g))
+    if need == 0:
+        _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), None, 0, _stream_ptr(stream)))
+    if workspace is None:
+        workspace = _empty_ws(need, dev)
+    _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), workspace.data_ptr(), workspace.numel(),
+                                  _stream_ptr(stream)))
+    return out
 
 
 def layer_workspace_bytes(l: _lib.LayerArgs) -> int:

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -261,6 +261,40 @@ size_t hstu_attn_bwd_workspace_bytes(const hstu_attn_bwd_args* args);
 
 hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* args, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* ----------------------------------------------------- layer (gradients) */
+/* Gradients of one HSTU layer (hstu_layer_fwd) for training: the chain rule
+ * through f2 + residual, the LayerNorm (.) U gate, the attention and
+ * f1 + SiLU ("生成式推荐（一）：HSTU", section "高性能自注意力Encoder：HSTU"):
+ *   dY = dX_out W2,  dW2 = dX_out^T Y,  db2 = sum_t dX_out,
+ *   dO, dU from the gate; dQ, dK, dV and the table gradients as in
+ *   hstu_attn_bwd;  dP = (dU | dV | dQ | dK) (.) SiLU'(X W1^T + b1),
+ *   dX = dX_out + dP W1,  dW1 = dP^T X,  db1 = sum_t dP.
+ * The forward intermediates (Z, O, Y) are recomputed from layer's inputs.
+ * Token sums run in a fixed order (run-to-run identical results).
+ * Requirements beyond hstu_layer_fwd's: D % 128 == 0, H*d % 128 == 0,
+ * num_pos_buckets + num_time_buckets <= ~2600.
+ * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
+typedef struct hstu_layer_bwd_args {
+    uint32_t struct_size;      /* = sizeof(hstu_layer_bwd_args) */
+    hstu_layer_args layer;     /* the forward's arguments (layer.x_out unused) */
+    const void* dx_out;        /* [num_rows, D] bf16: dLoss/dX_out */
+    void* dx;                  /* out [num_rows, D] bf16; may alias dx_out */
+    float* dw1;                /* out [4*H*d, D] fp32 */
+    float* db1;                /* out [4*H*d] fp32, or NULL */
+    float* dw2;                /* out [D, H*d] fp32 */
+    float* db2;                /* out [D] fp32, or NULL */
+    float* drab_pos;           /* out [num_pos_buckets] fp32, or NULL */
+    float* drab_time;          /* out [num_time_buckets] fp32, or NULL */
+} hstu_layer_bwd_args;
+
+/* Workspace bytes for hstu_layer_bwd (0 on invalid arguments): the
+ * recomputed Z, its pre-activation, O, Y (bf16), dY, dZ, transposed weights,
+ * the attention's and the weight products' scratch. */
+size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* args);
+
+hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* args, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* ------------------------------------------------------ scheduler access */
 /* Builds only the jagged tile work list into `workspace` (same layout as the

@@ -477,26 +477,30 @@ void hstu_oracle_layer_bwd(int32_t B, int32_t H, int32_t d, int32_t D,
                      0, 0, alpha, ORACLE_ACT_SILU, ob, hd, num_threads);
     hstu_oracle_ln_gate(T, hd, ob, hd, z, zw, eps, yb, hd, num_threads);
 
-    /* f2 */
+    /* f2 (each sum accumulates its terms in index order: m for dY, t for
+       dW2 and db2; the loops are ordered for contiguous reads) */
 #pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < T; ++t)
-        for (int32_t h = 0; h < hd; ++h) {
-            double s = 0.0;
-            for (int32_t m = 0; m < D; ++m) s += gr[t * D + m] * w2[(int64_t)m * hd + h];
-            dy[t * hd + h] = s;
+    for (int64_t t = 0; t < T; ++t) {
+        double* dyr = dy + t * hd;
+        for (int32_t h = 0; h < hd; ++h) dyr[h] = 0.0;
+        for (int32_t m = 0; m < D; ++m) {
+            const double a = gr[t * D + m];
+            const double* w2r = w2 + (int64_t)m * hd;
+            for (int32_t h = 0; h < hd; ++h) dyr[h] += a * w2r[h];
         }
+    }
 #pragma omp parallel for schedule(static)
     for (int32_t m = 0; m < D; ++m) {
-        for (int32_t h = 0; h < hd; ++h) {
-            double s = 0.0;
-            for (int64_t t = 0; t < T; ++t) s += gr[t * D + m] * yb[t * hd + h];
-            dw2[(int64_t)m * hd + h] = s;
+        double* dw2r = dw2 + (int64_t)m * hd;
+        for (int32_t h = 0; h < hd; ++h) dw2r[h] = 0.0;
+        double sb = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double a = gr[t * D + m];
+            const double* yr = yb + t * hd;
+            for (int32_t h = 0; h < hd; ++h) dw2r[h] += a * yr[h];
+            sb += a;
         }
-        if (db2) {
-            double s = 0.0;
-            for (int64_t t = 0; t < T; ++t) s += gr[t * D + m];
-            db2[m] = s;
-        }
+        if (db2) db2[m] = sb;
     }
 
     /* gate (dU into dZ's U columns) and attention (dV, dQ, dK into theirs) */
@@ -516,24 +520,27 @@ void hstu_oracle_layer_bwd(int32_t B, int32_t H, int32_t d, int32_t D,
         dz[e] *= sg * (1.0 + pre[e] * (1.0 - sg));
     }
 #pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < T; ++t)
-        for (int32_t k = 0; k < D; ++k) {
-            double s = gr[t * D + k];
-            for (int32_t n = 0; n < zw; ++n) s += dz[t * zw + n] * w1[(int64_t)n * D + k];
-            dx[(row0 + t) * D + k] = s;
+    for (int64_t t = 0; t < T; ++t) {
+        double* dxr = dx + (row0 + t) * D;
+        for (int32_t k = 0; k < D; ++k) dxr[k] = gr[t * D + k];
+        for (int32_t n = 0; n < zw; ++n) {
+            const double a = dz[t * zw + n];
+            const double* w1r = w1 + (int64_t)n * D;
+            for (int32_t k = 0; k < D; ++k) dxr[k] += a * w1r[k];
         }
+    }
 #pragma omp parallel for schedule(static)
     for (int32_t n = 0; n < zw; ++n) {
-        for (int32_t k = 0; k < D; ++k) {
-            double s = 0.0;
-            for (int64_t t = 0; t < T; ++t) s += dz[t * zw + n] * xr[t * D + k];
-            dw1[(int64_t)n * D + k] = s;
+        double* dw1r = dw1 + (int64_t)n * D;
+        for (int32_t k = 0; k < D; ++k) dw1r[k] = 0.0;
+        double sb = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double a = dz[t * zw + n];
+            const double* xrow = xr + t * D;
+            for (int32_t k = 0; k < D; ++k) dw1r[k] += a * xrow[k];
+            sb += a;
         }
-        if (db1) {
-            double s = 0.0;
-            for (int64_t t = 0; t < T; ++t) s += dz[t * zw + n];
-            db1[n] = s;
-        }
+        if (db1) db1[n] = sb;
     }
     free(off); free(dob); free(dy); free(yb); free(ob); free(gz); free(dz); free(z); free(pre);
 }

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 3
+    assert lib.hstu_abi_version() == 4
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -52,6 +52,7 @@ _STRUCTS = {
     "hstu_mfalcon_args": _lib.MfalconArgs,
     "hstu_layer_args": _lib.LayerArgs,
     "hstu_attn_bwd_args": _lib.AttnBwdArgs,
+    "hstu_layer_bwd_args": _lib.LayerBwdArgs,
 }
 
 
@@ -238,3 +239,46 @@ def test_bwd_workspace_errors_and_size(lib):
     g.attn.u_stride = 512
     need_dy = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(g))
     assert need_dy >= need + g.attn.num_rows * 512 * 2
+
+
+def _valid_layer_bwd():
+    g = _lib.LayerBwdArgs()
+    g.struct_size = ctypes.sizeof(_lib.LayerBwdArgs)
+    l = g.layer
+    l.struct_size = ctypes.sizeof(_lib.LayerArgs)
+    l.B, l.H, l.d, l.D, l.max_seq_len, l.num_rows = 2, 4, 128, 512, 100, 200
+    fake = 0x10000
+    l.seq_offsets = l.x = l.w1 = l.w2 = l.timestamps = l.rab_pos = l.rab_time = fake
+    l.num_pos_buckets, l.num_time_buckets = 1024, 32
+    l.alpha, l.ln_eps = 1.0 / 4096, 1e-5
+    g.dx_out = g.dx = g.dw1 = g.dw2 = fake
+    return g
+
+
+LAYER_BWD_MUTATIONS = [
+    ("struct_size", lambda g: setattr(g, "struct_size", 4), _lib.HSTU_ERR_ARG),
+    ("dw1 NULL", lambda g: setattr(g, "dw1", None), _lib.HSTU_ERR_ARG),
+    ("dx_out NULL", lambda g: setattr(g, "dx_out", None), _lib.HSTU_ERR_ARG),
+    ("misaligned dx", lambda g: setattr(g, "dx", 0x10002), _lib.HSTU_ERR_UNSUPPORTED),
+    ("D % 128", lambda g: setattr(g.layer, "D", 448), _lib.HSTU_ERR_UNSUPPORTED),
+    ("d != 128", lambda g: setattr(g.layer, "d", 64), _lib.HSTU_ERR_UNSUPPORTED),
+    ("tables too long", lambda g: setattr(g.layer, "num_pos_buckets", 8000), _lib.HSTU_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,mut,status", LAYER_BWD_MUTATIONS, ids=[m[0] for m in LAYER_BWD_MUTATIONS])
+def test_layer_bwd_validation_errors_before_any_launch(lib, name, mut, status):
+    g = _valid_layer_bwd()
+    mut(g)
+    assert lib.hstu_layer_bwd(ctypes.byref(g), None, 0, None) == status
+    assert lib.hstu_last_error()
+    assert lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(g)) == 0
+
+
+def test_layer_bwd_workspace_errors(lib):
+    g = _valid_layer_bwd()
+    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(g))
+    # at least Z, its pre-activation and dZ (rows x 4Hd bf16 each)
+    assert need >= 3 * 200 * 2048 * 2
+    assert lib.hstu_layer_bwd(ctypes.byref(g), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_layer_bwd(ctypes.byref(g), 0x20000, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
