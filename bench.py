@@ -12,9 +12,9 @@ step; `roofline` is the attention-core kernel alone, timed with HIP events
 recorded around its launch on the same stream; `cpu_baseline` is the fp64
 oracle on a bounded sample of the same workload (host cores of this machine).
 Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) and
-the attention gradients (hstu_attn_bwd from dLoss/dY on the long-sequence
-and M-FALCON workloads) are timed briefly and reported under
-"other_workloads".
+the gradients (hstu_attn_bwd from dLoss/dY on the long-sequence and M-FALCON
+workloads; hstu_layer_bwd on one layer of the stack) are timed briefly and
+reported under "other_workloads".
 """
 from __future__ import annotations
 
@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--cpu-sample-seqs", type=int, default=0, help="0: all sequences")
     p.add_argument("--only-bwd", action="store_true",
                    help="only time the attention gradients on --workload (for kernel traces)")
+    p.add_argument("--only-layer-bwd", action="store_true",
+                   help="only time the gradients of one layer of the stack workload (for kernel traces)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device copy (reference for the HBM byte counters)")
     return p.parse_args()
@@ -215,6 +217,43 @@ def bwd_record(x, dev, steps):
     return rec
 
 
+class LayerBwdCase:
+    """Gradients of one layer (layer 0 of the stack workload) from dLoss/dX_out."""
+
+    def __init__(self, x, dev):
+        import torch
+        import hstu_synth as synth
+        from hstu_sequential_transducer_causal_amd import ops
+        self.x = x
+        self.xin = up(x.x, "bf16", dev)
+        self.g = up(synth.upstream_grad(310, x.x.shape), "bf16", dev)
+        self.w1, self.w2 = up(x.w1[0], "bf16", dev), up(x.w2[0], "bf16", dev)
+        self.rp = torch.from_numpy(x.rab_pos[0]).to(dev)
+        self.rt = torch.from_numpy(x.rab_time[0]).to(dev)
+        self.off = torch.from_numpy(x.offsets).to(dev)
+        self.ts = torch.from_numpy(x.ts).to(dev)
+        self.max_len = int(np.diff(x.offsets).max())
+        f32 = dict(dtype=torch.float32, device=dev)
+        zw = 4 * x.H * x.d
+        self.out = dict(dx=torch.empty_like(self.xin), dw1=torch.empty(zw, x.D, **f32),
+                        dw2=torch.empty(x.D, x.H * x.d, **f32), drab_pos=torch.empty_like(self.rp),
+                        drab_time=torch.empty_like(self.rt))
+        a = ops.make_layer_bwd_args(self.xin, self.w1, self.w2, self.off, self.ts, self.rp, self.rt,
+                                    x.alpha, self.g, H=x.H, d=x.d, max_seq_len=self.max_len,
+                                    dx=self.out["dx"], dw1=self.out["dw1"], dw2=self.out["dw2"],
+                                    drab_pos=self.out["drab_pos"], drab_time=self.out["drab_time"])
+        self.args = a
+        self.ws = torch.empty(max(1, ops.layer_bwd_workspace_bytes(a)), dtype=torch.uint8, device=dev)
+
+    def step(self, ev0=None, ev1=None):
+        import ctypes
+        import torch
+        from hstu_sequential_transducer_causal_amd import _lib
+        lib = _lib.load()
+        _lib.check(lib.hstu_layer_bwd(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(),
+                                      torch.cuda.current_stream().cuda_stream))
+
+
 def time_case(case, steps, warmup, core_events=True):
     """Wall time per step (synchronised bracket) and mean core-kernel time (HIP events)."""
     import torch
@@ -322,6 +361,14 @@ def main():
     wl = args.workload
     log(f"generating workload {wl}")
     x = synth.config(wl)
+    if args.only_layer_bwd:
+        xl = synth.config(5)
+        c = LayerBwdCase(xl, dev)
+        st, _ = time_case(c, args.steps, args.warmup, core_events=False)
+        lf = flops.layer_bwd_flops(np.diff(xl.offsets), xl.H, xl.d, xl.D)
+        print(json.dumps({"workload": xl.name + "_layer0_bwd", "ms_per_step": round(st, 4),
+                          "tflops": round(lf / (st * 1e-3) / 1e12, 2)}), flush=True)
+        return
     if args.only_bwd:
         rec = bwd_record(x, dev, args.steps)
         print(json.dumps({"workload": x.name + "_bwd", **rec}), flush=True)
@@ -406,6 +453,18 @@ def main():
                 log(f"{xo.name} candidates only: {rec}")
                 del c
                 torch.cuda.empty_cache()
+        xl = synth.config(5)
+        c = LayerBwdCase(xl, dev)
+        st, _ = time_case(c, max(2, args.steps // 10), 1, core_events=False)
+        lf = flops.layer_bwd_flops(np.diff(xl.offsets), xl.H, xl.d, xl.D)
+        rec = {"ms_per_step": round(st, 4), "tflops": round(lf / (st * 1e-3) / 1e12, 2),
+               "tokens_per_s": round(xl.T / (st * 1e-3), 1), "tokens": xl.T,
+               "flop_convention": "attention gradients at 8*d per visible pair and head plus the four "
+                                  "weight/data products of f1 and f2; the recomputed forward not counted"}
+        others[xl.name + "_layer0_bwd"] = rec
+        log(f"{xl.name} layer-0 gradients: {rec}")
+        del c
+        torch.cuda.empty_cache()
         for w in (3, 4):
             xb = x if w == wl else synth.config(w)
             rec = bwd_record(xb, dev, max(3, args.steps // 3))

@@ -40,6 +40,15 @@ def attn_bwd_flops(lengths, H: int, d: int, num_candidates=None) -> int:
     return int(visible_pairs(lengths, num_candidates)) * H * 8 * d
 
 
+def layer_bwd_flops(lengths, H: int, d: int, D: int) -> int:
+    """Algorithmic FLOPs of one layer's gradients: the attention gradients
+    plus four products -- dY = dX_out W2 and dW2 = dX_out^T Y (2*T*D*H*d
+    each), dX = dP W1 and dW1 = dP^T X (2*T*4*H*d*D each).  The recomputed
+    forward is not counted."""
+    T = int(np.sum(np.asarray(lengths, dtype=np.int64)))
+    return attn_bwd_flops(lengths, H, d) + 2 * gemm_flops(T, D, H * d) + 2 * gemm_flops(T, 4 * H * d, D)
+
+
 def dense_attn_flops(T: int, d: int) -> int:
     """Dense count of both products over all T^2 pairs: 2 * 2 * T^2 * d."""
     return 2 * 2 * T * T * d
