@@ -104,6 +104,30 @@ class LayerBwdArgs(ctypes.Structure):
     ]
 
 
+SL_MAX_TENSORS = 8
+
+
+class SlArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", _i32),
+        ("num_rows", _i64),
+        ("seq_offsets", _vp),
+        ("cap", _i32),
+        ("caps", _vp),
+        ("seed", ctypes.c_uint64),
+        ("step", ctypes.c_uint64),
+        ("out_offsets", _vp),
+        ("out_index", _vp),
+        ("num_tensors", _i32),
+        ("src", _vp * SL_MAX_TENSORS),
+        ("src_stride", _i64 * SL_MAX_TENSORS),
+        ("dst", _vp * SL_MAX_TENSORS),
+        ("dst_stride", _i64 * SL_MAX_TENSORS),
+        ("row_bytes", _i32 * SL_MAX_TENSORS),
+    ]
+
+
 # every symbol include/hstu.h declares
 EXPORTS = [
     "hstu_abi_version", "hstu_status_string", "hstu_last_error",
@@ -112,6 +136,7 @@ EXPORTS = [
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
     "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
     "hstu_layer_bwd_workspace_bytes", "hstu_layer_bwd",
+    "hstu_stochastic_length",
     "hstu_attn_schedule",
 ]
 
@@ -158,6 +183,8 @@ def load(path: str = LIB_PATH):
     lib.hstu_layer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LayerBwdArgs)]
     lib.hstu_layer_bwd.restype = _i32
     lib.hstu_layer_bwd.argtypes = [ctypes.POINTER(LayerBwdArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_stochastic_length.restype = _i32
+    lib.hstu_stochastic_length.argtypes = [ctypes.POINTER(SlArgs), _vp]
     lib.hstu_attn_schedule.restype = _i32
     lib.hstu_attn_schedule.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t,
                                        ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64),

@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhstu.so")
 ARCH = os.environ.get("HSTU_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.hip", "sched.hip", "attn_bf16.hip", "attn_bwd.hip", "layer_bwd.hip", "attn_f32.hip", "epilogue.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "sched.hip", "attn_bf16.hip", "attn_bwd.hip", "layer_bwd.hip", "sl.hip", "attn_f32.hip", "epilogue.hip", "gemm.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

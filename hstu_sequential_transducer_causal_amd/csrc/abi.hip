@@ -863,6 +863,51 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
     return ok();
 }
 
+hstu_status hstu_stochastic_length(const hstu_sl_args* a, void* stream_) {
+    if (!a) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (a->struct_size != sizeof(hstu_sl_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_sl_args) %zu", a->struct_size, sizeof(hstu_sl_args));
+    if (a->B < 0 || a->num_rows < 0) return fail(HSTU_ERR_ARG, "B and num_rows must be >= 0");
+    if (!a->caps && a->cap < 0) return fail(HSTU_ERR_ARG, "cap must be >= 0");
+    if (a->num_tensors < 0 || a->num_tensors > HSTU_SL_MAX_TENSORS)
+        return fail(HSTU_ERR_ARG, "num_tensors outside [0, %d]", HSTU_SL_MAX_TENSORS);
+    if (a->B > 0 && (!a->seq_offsets || !a->out_offsets || !a->out_index))
+        return fail(HSTU_ERR_ARG, "seq_offsets, out_offsets and out_index must be non-NULL");
+    for (int t = 0; t < a->num_tensors; ++t) {
+        if (!a->src[t] || !a->dst[t]) return fail(HSTU_ERR_ARG, "tensor %d: NULL pointer", t);
+        if (a->row_bytes[t] <= 0 || a->row_bytes[t] % 4 != 0)
+            return fail(HSTU_ERR_ARG, "tensor %d: row_bytes must be a positive multiple of 4", t);
+        if (a->src_stride[t] < a->row_bytes[t] || a->dst_stride[t] < a->row_bytes[t] || a->src_stride[t] % 4 ||
+            a->dst_stride[t] % 4)
+            return fail(HSTU_ERR_ARG, "tensor %d: strides must be multiples of 4 and >= row_bytes", t);
+        if ((reinterpret_cast<uintptr_t>(a->src[t]) | reinterpret_cast<uintptr_t>(a->dst[t])) & 3u)
+            return fail(HSTU_ERR_ARG, "tensor %d: rows must be 4-byte aligned", t);
+    }
+    if (a->B == 0) return ok();
+    hstu::SlArgs s;
+    s.B = a->B;
+    s.num_rows = a->num_rows;
+    s.offsets = a->seq_offsets;
+    s.cap = a->cap;
+    s.caps = a->caps;
+    s.seed = a->seed;
+    s.step = a->step;
+    s.out_offsets = a->out_offsets;
+    s.out_index = a->out_index;
+    s.num_tensors = a->num_tensors;
+    for (int t = 0; t < hstu::kSlMaxTensors; ++t) {
+        const bool used = t < a->num_tensors;
+        s.src[t] = used ? a->src[t] : nullptr;
+        s.src_stride[t] = used ? a->src_stride[t] : 0;
+        s.dst[t] = used ? a->dst[t] : nullptr;
+        s.dst_stride[t] = used ? a->dst_stride[t] : 0;
+        s.row_bytes[t] = used ? a->row_bytes[t] : 0;
+    }
+    hipError_t e = hstu::launch_stochastic_length(s, static_cast<hipStream_t>(stream_));
+    if (e != hipSuccess) return device_error(e, "stochastic length launch");
+    return ok();
+}
+
 hstu_status hstu_attn_schedule(const hstu_attn_args* a, void* ws, size_t ws_bytes, int32_t* items_out,
                                int64_t cap, int64_t* count_out, int32_t* tile_m_out, int32_t* tile_n_out,
                                void* stream_) {

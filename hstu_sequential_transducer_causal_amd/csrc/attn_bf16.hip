@@ -382,22 +382,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 }
             }
 
-            // ---------- S^T = K Q^T (+ bias), as two interleaved accumulation
-            //            chains (a lone dependent chain issues at ~2/3 rate)
-            {
-                f32x16 acc2;
+            // ---------- S^T = K Q^T (+ bias): one accumulation chain (a
+            //            second chain to hide the MFMA dependency measured
+            //            1 % slower: its merge costs 32 VALU per tile and the
+            //            other wave on the SIMD fills the dependency gaps)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc2[r] = 0.0f;
-#pragma unroll
-                for (int kc = 0; kc < 8; kc += 2) {
-                    acc = mfma32(kf[kc], qf[kc], acc);
-                    acc2 = mfma32(kf[kc + 1], qf[kc + 1], acc2);
-                }
-                read_v_chunk(v_lds, 1, lane, vf[1]);
-                if (issue) issue_v(dma, s, st3, kt3, wave);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] += acc2[r];
-            }
+            for (int kc = 0; kc < 8; ++kc) acc = mfma32(kf[kc], qf[kc], acc);
+            read_v_chunk(v_lds, 1, lane, vf[1]);
+            if (issue) issue_v(dma, s, st3, kt3, wave);
 
             // ---------- activation, mask, bf16 packing
             float a[16];

@@ -287,6 +287,25 @@ hipError_t launch_silu_grad(void* dz, const void* pre, int64_t count, hipStream_
 // out[c][r] = in[r][c], bf16.
 hipError_t launch_transpose(const void* in, int R, int C, void* out, hipStream_t stream);
 
+// Stochastic length: kept rows of every sequence (min(cap_b, L_b) by
+// smallest Philox key, in order) and the gather of their rows.
+constexpr int kSlMaxTensors = 8;
+struct SlArgs {
+    int B;
+    int64_t num_rows;
+    const int32_t* offsets;
+    int cap;
+    const int32_t* caps;
+    uint64_t seed, step;
+    int32_t* out_offsets;
+    int64_t* out_index;
+    int num_tensors;
+    const void* src[kSlMaxTensors]; int64_t src_stride[kSlMaxTensors];
+    void* dst[kSlMaxTensors]; int64_t dst_stride[kSlMaxTensors];
+    int row_bytes[kSlMaxTensors];
+};
+hipError_t launch_stochastic_length(const SlArgs& a, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace hstu

@@ -3,7 +3,7 @@
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
 Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score,
-hstu_layer_fwd, hstu_layer_bwd, hstu_attn_schedule.
+hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule.
 """
 from __future__ import annotations
 
@@ -329,6 +329,52 @@ def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha,
     _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), workspace.data_ptr(), workspace.numel(),
                                   _stream_ptr(stream)))
     return out
+
+
+def stochastic_length(seq_offsets, cap, *, seed: int, step: int = 0, caps=None, tensors=(),
+                      out_index=None, stream=None):
+    """Seeded order-preserving subsampling of every sequence to at most
+    ``cap`` (or ``caps[b]``) rows, with the kept rows of ``tensors`` (each
+    [rows, ...] with contiguous rows) gathered into packed outputs.
+
+    Returns (out_offsets int32 [B+1], out_index int64 [rows] -- valid up to
+    out_offsets[B] -- and the list of gathered tensors, each with as many
+    rows as its source; rows past out_offsets[B] are left unwritten).
+    """
+    lib = _lib.load()
+    dev = seq_offsets.device
+    B = seq_offsets.numel() - 1
+    rows = tensors[0].shape[0] if tensors else None
+    a = _lib.SlArgs()
+    a.struct_size = ctypes.sizeof(_lib.SlArgs)
+    a.B = B
+    out_off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if rows is None:
+        rows = int(seq_offsets[-1].item()) if B > 0 else 0
+    a.num_rows = rows
+    out_index = torch.empty(max(rows, 1), dtype=torch.int64, device=dev) if out_index is None else out_index
+    a.seq_offsets = seq_offsets.data_ptr()
+    a.cap = int(cap)
+    a.caps = _ptr(caps)
+    a.seed = int(seed) & ((1 << 64) - 1)
+    a.step = int(step) & ((1 << 64) - 1)
+    a.out_offsets = out_off.data_ptr()
+    a.out_index = out_index.data_ptr()
+    if len(tensors) > _lib.SL_MAX_TENSORS:
+        raise ValueError(f"at most {_lib.SL_MAX_TENSORS} tensors")
+    outs = []
+    a.num_tensors = len(tensors)
+    for t, x in enumerate(tensors):
+        if x.shape[0] != rows or not x[0].is_contiguous():
+            raise ValueError("tensors need the same row count and contiguous rows")
+        y = torch.empty_like(x)
+        rb = x[0].numel() * x.element_size()
+        a.src[t], a.src_stride[t] = x.data_ptr(), x.stride(0) * x.element_size()
+        a.dst[t], a.dst_stride[t] = y.data_ptr(), y.stride(0) * y.element_size()
+        a.row_bytes[t] = rb
+        outs.append(y)
+    _lib.check(lib.hstu_stochastic_length(ctypes.byref(a), _stream_ptr(stream)))
+    return out_off, out_index, outs
 
 
 def layer_workspace_bytes(l: _lib.LayerArgs) -> int:

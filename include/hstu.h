@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 4
+#define HSTU_ABI_VERSION 5
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -295,6 +295,45 @@ size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* args);
 
 hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* args, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------------ stochastic length */
+/* Stochastic length on the device ("行动胜于言语：万亿参数序列转导器用于生成式
+ * 推荐", section "2.1"; the GRs summary page, section 2.1): each sequence
+ * longer than its cap is replaced by a random order-preserving subsequence of
+ * cap events, and the kept rows of up to 8 row-major tensors are gathered
+ * into a packed jagged batch.  Sampler: event j of sequence b gets the top 32
+ * bits of the first word of Philox-4x64-10 (Salmon et al., SC'11) for counter
+ * (j, b, step, 0) and key (seed, 0x534c); the sequence keeps its
+ * min(cap_b, L_b) events with the smallest (key, j), in order (a pure
+ * function of its inputs: run-to-run identical; every subset of that size
+ * is equally likely).  For the cap of "N^(alpha/2)" with the exponent being
+ * swept, pass the caps the host computes.
+ * Outputs: out_offsets [B+1] (device) of the kept rows; out_index (device,
+ * capacity num_rows) the source row of each kept row, in order; dst[t] row r
+ * = src[t] row out_index[r] (row_bytes[t] bytes, a multiple of 4; strides in
+ * bytes; 16-byte rows and strides copy 16 bytes at a time).  No workspace.
+ * Errors: HSTU_ERR_ARG, HSTU_ERR_DEVICE. */
+#define HSTU_SL_MAX_TENSORS 8
+typedef struct hstu_sl_args {
+    uint32_t struct_size;          /* = sizeof(hstu_sl_args) */
+    int32_t B;                     /* sequences, >= 0 */
+    int64_t num_rows;              /* rows of the input tensors (>= seq_offsets[B]) */
+    const int32_t* seq_offsets;    /* [B+1] device */
+    int32_t cap;                   /* cap of every sequence (>= 0) when caps == NULL */
+    const int32_t* caps;           /* [B] device per-sequence caps, or NULL */
+    uint64_t seed;                 /* Philox key word 0 */
+    uint64_t step;                 /* Philox counter word 2 (e.g. the training step) */
+    int32_t* out_offsets;          /* out [B+1] device */
+    int64_t* out_index;            /* out [num_rows] device */
+    int32_t num_tensors;           /* 0 .. HSTU_SL_MAX_TENSORS */
+    const void* src[HSTU_SL_MAX_TENSORS];
+    int64_t src_stride[HSTU_SL_MAX_TENSORS];
+    void* dst[HSTU_SL_MAX_TENSORS];
+    int64_t dst_stride[HSTU_SL_MAX_TENSORS];
+    int32_t row_bytes[HSTU_SL_MAX_TENSORS];
+} hstu_sl_args;
+
+hstu_status hstu_stochastic_length(const hstu_sl_args* args, void* stream);
 
 /* ------------------------------------------------------ scheduler access */
 /* Builds only the jagged tile work list into `workspace` (same layout as the

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 4
+    assert lib.hstu_abi_version() == 5
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -53,6 +53,7 @@ _STRUCTS = {
     "hstu_layer_args": _lib.LayerArgs,
     "hstu_attn_bwd_args": _lib.AttnBwdArgs,
     "hstu_layer_bwd_args": _lib.LayerBwdArgs,
+    "hstu_sl_args": _lib.SlArgs,
 }
 
 
@@ -282,3 +283,36 @@ def test_layer_bwd_workspace_errors(lib):
     assert need >= 3 * 200 * 2048 * 2
     assert lib.hstu_layer_bwd(ctypes.byref(g), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_layer_bwd(ctypes.byref(g), 0x20000, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
+
+
+def _valid_sl():
+    a = _lib.SlArgs()
+    a.struct_size = ctypes.sizeof(_lib.SlArgs)
+    a.B, a.num_rows, a.cap = 3, 100, 10
+    a.seq_offsets = a.out_offsets = a.out_index = 0x10000
+    a.num_tensors = 1
+    a.src[0] = a.dst[0] = 0x10000
+    a.src_stride[0] = a.dst_stride[0] = 1024
+    a.row_bytes[0] = 1024
+    return a
+
+
+SL_MUTATIONS = [
+    ("struct_size", lambda a: setattr(a, "struct_size", 4)),
+    ("B<0", lambda a: setattr(a, "B", -1)),
+    ("cap<0", lambda a: setattr(a, "cap", -1)),
+    ("too many tensors", lambda a: setattr(a, "num_tensors", 9)),
+    ("offsets NULL", lambda a: setattr(a, "seq_offsets", None)),
+    ("row_bytes % 4", lambda a: a.row_bytes.__setitem__(0, 6)),
+    ("stride < row", lambda a: a.src_stride.__setitem__(0, 512)),
+    ("misaligned dst", lambda a: a.dst.__setitem__(0, 0x10002)),
+    ("NULL src", lambda a: a.src.__setitem__(0, None)),
+]
+
+
+@pytest.mark.parametrize("name,mut", SL_MUTATIONS, ids=[m[0] for m in SL_MUTATIONS])
+def test_sl_validation_errors_before_any_launch(lib, name, mut):
+    a = _valid_sl()
+    mut(a)
+    assert lib.hstu_stochastic_length(ctypes.byref(a), None) == _lib.HSTU_ERR_ARG
+    assert lib.hstu_last_error()
