@@ -13,8 +13,9 @@ recorded around its launch on the same stream; `cpu_baseline` is the fp64
 oracle on a bounded sample of the same workload (host cores of this machine).
 Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) and
 the gradients (hstu_attn_bwd from dLoss/dY on the long-sequence and M-FALCON
-workloads; hstu_layer_bwd on one layer of the stack) are timed briefly and
-reported under "other_workloads".
+workloads; hstu_layer_bwd on one layer of the stack) and stochastic length
+with its gather (the long-sequence workload's raw batch) are timed briefly
+and reported under "other_workloads".
 """
 from __future__ import annotations
 
@@ -254,6 +255,34 @@ class LayerBwdCase:
                                       torch.cuda.current_stream().cuda_stream))
 
 
+def sl_record(dev, steps):
+    """Stochastic length with the gather of the rows of Q, K, V, U (8 heads of
+    128, bf16) and timestamps, on the long-sequence workload's raw batch."""
+    import torch
+    import hstu_synth as synth
+    from hstu_sequential_transducer_causal_amd import ops
+    L = synth.longseq_raw_lengths()
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)).to(dev)
+    T = int(L.sum())
+    g = torch.Generator(device=dev).manual_seed(5)
+    rows = [torch.randn(T, 1024, generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
+    ts = torch.arange(T, dtype=torch.int64, device=dev) * 60
+    tensors = (*rows, ts)
+    for _ in range(2):
+        ops.stochastic_length(off, synth.SL_CAP, seed=1, step=0, tensors=tensors)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        oo, _, _ = ops.stochastic_length(off, synth.SL_CAP, seed=1, step=i, tensors=tensors)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kept = int(oo[-1].item())
+    moved = 2 * kept * (4 * 1024 * 2 + 8)   # read + write of every kept row
+    return {"ms_per_step": round(ms, 4), "raw_rows": T, "kept_rows": kept,
+            "gbytes_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def time_case(case, steps, warmup, core_events=True):
     """Wall time per step (synchronised bracket) and mean core-kernel time (HIP events)."""
     import torch
@@ -362,6 +391,9 @@ def main():
     log(f"generating workload {wl}")
     x = synth.config(wl)
     if args.only_layer_bwd:
+        sl_rec = sl_record(dev, max(3, args.steps // 3))
+        others["hstu_sl_gather_longseq_raw_b16_cap2120"] = sl_rec
+        log(f"stochastic length + gather: {sl_rec}")
         xl = synth.config(5)
         c = LayerBwdCase(xl, dev)
         st, _ = time_case(c, args.steps, args.warmup, core_events=False)
@@ -453,6 +485,9 @@ def main():
                 log(f"{xo.name} candidates only: {rec}")
                 del c
                 torch.cuda.empty_cache()
+        sl_rec = sl_record(dev, max(3, args.steps // 3))
+        others["hstu_sl_gather_longseq_raw_b16_cap2120"] = sl_rec
+        log(f"stochastic length + gather: {sl_rec}")
         xl = synth.config(5)
         c = LayerBwdCase(xl, dev)
         st, _ = time_case(c, max(2, args.steps // 10), 1, core_events=False)

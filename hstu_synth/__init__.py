@@ -272,6 +272,13 @@ def _lognormal_lengths(rng, B, median, sigma, lo, hi):
     return np.clip(raw, lo, hi)
 
 
+def longseq_raw_lengths(batch: int = 16, seed: int = 3) -> np.ndarray:
+    """Raw (before stochastic length) lengths of the long-sequence workload:
+    the same draws ``config(3)`` makes."""
+    rng = np.random.default_rng(1000 + seed)
+    return _lognormal_lengths(rng, batch, 3000, 0.5, 1024, SL_MAX_RAW)
+
+
 def config(n: int, *, batch: Optional[int] = None, max_len: Optional[int] = None,
            seed: Optional[int] = None):
     """Inputs of workload ``n`` (1..5), seeded with ``n`` unless ``seed`` is given.
