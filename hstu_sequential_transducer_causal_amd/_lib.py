@@ -62,6 +62,33 @@ class MfalconArgs(ctypes.Structure):
     ]
 
 
+class MfalconCachedArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("B", _i32), ("H", _i32), ("d", _i32),
+        ("max_hist_len", _i32), ("max_cands", _i32),
+        ("hist_offsets", _vp), ("num_hist_rows", _i64),
+        ("k_hist", _vp), ("k_hist_stride", _i64),
+        ("v_hist", _vp), ("v_hist_stride", _i64),
+        ("ts_hist", _vp),
+        ("cand_offsets", _vp), ("num_cand_rows", _i64),
+        ("q", _vp), ("q_stride", _i64),
+        ("k", _vp), ("k_stride", _i64),
+        ("v", _vp), ("v_stride", _i64),
+        ("u", _vp), ("u_stride", _i64),
+        ("ts_cand", _vp),
+        ("rab_pos", _vp), ("num_pos_buckets", _i32), ("rab_pos_head_stride", _i32),
+        ("rab_time", _vp), ("num_time_buckets", _i32), ("rab_time_head_stride", _i32),
+        ("alpha", _f32),
+        ("ln_eps", _f32),
+        ("w", _vp),
+        ("scores", _vp),
+        ("score_stride", _i32),
+        ("o", _vp), ("o_stride", _i64),
+        ("ev_core_begin", _vp), ("ev_core_end", _vp),
+    ]
+
+
 class AttnBwdArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32),
@@ -133,6 +160,7 @@ EXPORTS = [
     "hstu_abi_version", "hstu_status_string", "hstu_last_error",
     "hstu_attn_workspace_bytes", "hstu_attn_fwd",
     "hstu_mfalcon_workspace_bytes", "mfalcon_score",
+    "hstu_mfalcon_cached_workspace_bytes", "mfalcon_score_cached",
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
     "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
     "hstu_layer_bwd_workspace_bytes", "hstu_layer_bwd",
@@ -171,6 +199,10 @@ def load(path: str = LIB_PATH):
     lib.hstu_mfalcon_workspace_bytes.argtypes = [ctypes.POINTER(MfalconArgs)]
     lib.mfalcon_score.restype = _i32
     lib.mfalcon_score.argtypes = [ctypes.POINTER(MfalconArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_mfalcon_cached_workspace_bytes.restype = ctypes.c_size_t
+    lib.hstu_mfalcon_cached_workspace_bytes.argtypes = [ctypes.POINTER(MfalconCachedArgs)]
+    lib.mfalcon_score_cached.restype = _i32
+    lib.mfalcon_score_cached.argtypes = [ctypes.POINTER(MfalconCachedArgs), _vp, ctypes.c_size_t, _vp]
     lib.hstu_layer_workspace_bytes.restype = ctypes.c_size_t
     lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
     lib.hstu_layer_fwd.restype = _i32

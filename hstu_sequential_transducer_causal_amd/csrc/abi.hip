@@ -265,6 +265,62 @@ hipError_t run_ln_gate(const hstu_attn_args* a, const Sched& s, const float* w, 
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// ---- M-FALCON against a history cache
+
+hstu_status validate_cached(const hstu_mfalcon_cached_args* m) {
+    if (!m) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (m->struct_size != sizeof(hstu_mfalcon_cached_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_mfalcon_cached_args) %zu", m->struct_size,
+                    sizeof(hstu_mfalcon_cached_args));
+    if (m->B < 0 || m->H < 1) return fail(HSTU_ERR_ARG, "B >= 0 and H >= 1 required");
+    if (m->d != 128) return fail(HSTU_ERR_UNSUPPORTED, "d must be 128 (got %d)", m->d);
+    if (m->max_hist_len < 0 || m->max_hist_len > hstu::kMaxSeqLen || m->max_cands < 0 ||
+        m->max_cands > hstu::kMaxSeqLen)
+        return fail(HSTU_ERR_ARG, "max_hist_len and max_cands must lie in [0, %d]", hstu::kMaxSeqLen);
+    if (m->num_hist_rows < 0 || m->num_cand_rows < 0) return fail(HSTU_ERR_ARG, "row counts must be >= 0");
+    if (m->num_pos_buckets < 1 || m->num_pos_buckets > hstu::kMaxPosBuckets)
+        return fail(HSTU_ERR_ARG, "num_pos_buckets outside [1, %d]", hstu::kMaxPosBuckets);
+    if (m->num_time_buckets < 1) return fail(HSTU_ERR_ARG, "num_time_buckets < 1");
+    if (m->rab_pos_head_stride < 0 || m->rab_time_head_stride < 0) return fail(HSTU_ERR_ARG, "negative head stride");
+    if (!std::isfinite(m->alpha)) return fail(HSTU_ERR_ARG, "alpha is not finite");
+    if (!(m->ln_eps > 0.0f) || !std::isfinite(m->ln_eps)) return fail(HSTU_ERR_ARG, "ln_eps must be > 0");
+    if (m->score_stride < std::max(1, m->max_cands)) return fail(HSTU_ERR_ARG, "score_stride < max_cands");
+    const int64_t hd = int64_t(m->H) * m->d;
+    if (hd > 4096) return fail(HSTU_ERR_UNSUPPORTED, "H*d must be <= 4096");
+    const int64_t strides[7] = {m->k_hist_stride, m->v_hist_stride, m->q_stride, m->k_stride, m->v_stride,
+                                m->u_stride, m->o ? m->o_stride : hd};
+    for (int64_t st : strides)
+        if (st < hd || st % 8) return fail(HSTU_ERR_ARG, "row strides must be >= H*d and multiples of 8");
+    if (int64_t(m->max_hist_len) * 2 * std::max(m->k_hist_stride, m->v_hist_stride) > int64_t(0x7fffffff))
+        return fail(HSTU_ERR_UNSUPPORTED, "max_hist_len * K/V row bytes must stay below 2^31");
+    if (m->B > 0) {
+        if (!m->hist_offsets || !m->cand_offsets || !m->k_hist || !m->v_hist || !m->ts_hist || !m->q || !m->k ||
+            !m->v || !m->u || !m->ts_cand || !m->rab_pos || !m->rab_time || !m->w || !m->scores)
+            return fail(HSTU_ERR_ARG, "a required pointer is NULL");
+        const void* ptrs[7] = {m->k_hist, m->v_hist, m->q, m->k, m->v, m->u, m->o ? m->o : m->q};
+        for (const void* ptr : ptrs)
+            if (!aligned16(ptr)) return fail(HSTU_ERR_UNSUPPORTED, "bf16 rows must be 16-byte aligned");
+    }
+    return HSTU_OK;
+}
+
+struct CachedWs {
+    hstu::SchedLayout cand;      // candidates' work list, codes, split slots, row map
+    size_t kstats, kenc, o, total;
+    int nblk_k;
+};
+
+CachedWs cached_ws(const hstu_mfalcon_cached_args* m) {
+    CachedWs w;
+    w.cand = hstu::sched_layout(m->B, m->H, m->max_cands, hstu::kBf16TileM, m->d, m->num_cand_rows, 0);
+    w.nblk_k = (m->max_hist_len + hstu::kTsBlock - 1) / hstu::kTsBlock;
+    w.kstats = align256(w.cand.bytes);
+    w.kenc = align256(w.kstats + size_t(m->B) * w.nblk_k * 2 * sizeof(uint32_t));
+    w.o = align256(w.kenc + size_t(m->num_hist_rows) * sizeof(uint32_t));
+    w.total = align256(w.o + (m->o ? 0 : size_t(m->num_cand_rows) * m->H * m->d * 2));
+    return w;
+}
+
 // ---- gradients
 
 hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
@@ -638,6 +694,108 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     g2.silu = 0;
     e = hstu::launch_gemm_bf16(g2, stream);
     if (e != hipSuccess) return device_error(e, "f2 launch");
+    return ok();
+}
+
+size_t hstu_mfalcon_cached_workspace_bytes(const hstu_mfalcon_cached_args* m) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_cached(m);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return cached_ws(m).total;
+}
+
+hstu_status mfalcon_score_cached(const hstu_mfalcon_cached_args* m, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_cached(m);
+    if (st != HSTU_OK) return st;
+    if (m->B == 0 || m->num_cand_rows == 0) return ok();
+    const CachedWs w = cached_ws(m);
+    st = check_workspace(ws, ws_bytes, w.total);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    uint8_t* wb = static_cast<uint8_t*>(ws);
+    const Sched sc = carve_layout(w.cand, ws);
+    float* partial = reinterpret_cast<float*>(wb + w.cand.off_part);
+    int32_t* rowmap = reinterpret_cast<int32_t*>(wb + w.cand.off_rowmap);
+    uint32_t* kstats = reinterpret_cast<uint32_t*>(wb + w.kstats);
+    uint32_t* kenc = reinterpret_cast<uint32_t*>(wb + w.kenc);
+    void* o = m->o ? m->o : static_cast<void*>(wb + w.o);
+    const int64_t o_stride = m->o ? m->o_stride : int64_t(m->H) * m->d;
+
+    // history codes (relative to each history's first event)
+    hstu::SchedArgs ha;
+    ha.B = m->B;
+    ha.max_seq_len = m->max_hist_len;
+    ha.cap = 0; ha.cap_pieces = 0;
+    ha.cand_only = 0; ha.kv_mode = 0; ha.H = m->H; ha.slots = 0; ha.part_slots = 0;
+    ha.split = nullptr;
+    ha.offsets = m->hist_offsets; ha.lengths = nullptr; ha.ncand = nullptr;
+    ha.tile_m = hstu::kBf16TileM; ha.tile_n = hstu::kBf16TileN;
+    ha.ctrl = nullptr; ha.qscan = nullptr; ha.items = nullptr;
+    ha.ts = m->ts_hist; ha.enc = kenc; ha.stats = kstats;
+    ha.nblk = w.nblk_k; ha.cap_blk = int64_t(m->B) * w.nblk_k;
+    ha.skip_list = 1;
+    hipError_t e = ha.cap_blk > 0 ? hstu::launch_sched(ha, stream) : hipSuccess;
+    if (e != hipSuccess) return device_error(e, "history code launch");
+
+    // the candidates' work list (all history tiles per row block, split when
+    // long) and their codes relative to the history's first event
+    hstu::SchedArgs ca;
+    ca.B = m->B;
+    ca.max_seq_len = std::max(m->max_cands, m->max_hist_len);
+    ca.cap = (int64_t)w.cand.cap; ca.cap_pieces = (int64_t)w.cand.cap_pieces;
+    ca.cand_only = 0; ca.kv_mode = 0; ca.H = m->H;
+    ca.slots = hstu::attn_bf16_slots(); ca.part_slots = w.cand.part_slots;
+    ca.split = sc.split;
+    ca.offsets = m->cand_offsets; ca.lengths = nullptr; ca.ncand = nullptr;
+    ca.tile_m = hstu::kBf16TileM; ca.tile_n = hstu::kBf16TileN;
+    ca.ctrl = sc.ctrl; ca.qscan = sc.qscan; ca.items = sc.items;
+    ca.ts = m->ts_cand; ca.enc = sc.enc; ca.stats = sc.stats;
+    ca.nblk = w.cand.nblk; ca.cap_blk = (int64_t)w.cand.cap_blk;
+    ca.kv_offsets = m->hist_offsets; ca.ref_offsets = m->hist_offsets; ca.ref_ts = m->ts_hist;
+    e = hstu::launch_sched(ca, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+
+    hstu::AttnCoreArgs c;
+    c.H = m->H; c.d = m->d;
+    c.offsets = m->hist_offsets; c.lengths = nullptr; c.ncand = nullptr;
+    c.q = m->q; c.q_stride = m->q_stride;
+    c.k = m->k_hist; c.k_stride = m->k_hist_stride;
+    c.v = m->v_hist; c.v_stride = m->v_hist_stride;
+    c.ts = m->ts_hist;
+    c.rab_pos = m->rab_pos; c.P = m->num_pos_buckets; c.rp_head_stride = m->rab_pos_head_stride;
+    c.rab_time = m->rab_time; c.NT = m->num_time_buckets; c.rt_head_stride = m->rab_time_head_stride;
+    c.alpha = m->alpha; c.act = HSTU_ACT_SILU;
+    c.o = o; c.o_stride = o_stride;
+    c.items = sc.items; c.ctrl = sc.ctrl; c.cursor = sc.ctrl + 1;
+    c.partial = partial; c.rowmap = rowmap;
+    c.nblk = w.nblk_k; c.stats = kstats; c.enc = kenc; c.num_rows = m->num_hist_rows;
+    c.ev_begin = static_cast<hipEvent_t>(m->ev_core_begin);
+    c.ev_end = static_cast<hipEvent_t>(m->ev_core_end);
+    c.q_offsets = m->cand_offsets; c.ts_q = m->ts_cand; c.enc_q = sc.enc; c.stats_q = sc.stats;
+    c.nblk_q = w.cand.nblk;
+    e = hstu::launch_attn_bf16(c, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+
+    hstu::LnGateArgs l;
+    l.B = m->B; l.num_rows = m->num_cand_rows; l.width = m->H * m->d; l.dtype = HSTU_BF16;
+    l.offsets = m->cand_offsets; l.lengths = nullptr; l.ncand = nullptr;
+    l.o = o; l.o_stride = o_stride;
+    l.u = m->u; l.u_stride = m->u_stride;
+    l.y = nullptr; l.y_stride = 0;
+    l.eps = m->ln_eps;
+    l.w = m->w; l.scores = m->scores; l.score_stride = m->score_stride;
+    l.rowmap = rowmap; l.partial = partial; l.H = m->H; l.d = m->d; l.BM = hstu::kBf16TileM; l.cand_only = 0;
+    l.cross = 1;
+    l.sq = m->q; l.sqs = m->q_stride;
+    l.sk = m->k; l.sks = m->k_stride;
+    l.sv = m->v; l.svs = m->v_stride;
+    l.rab_pos = m->rab_pos; l.rp_hs = m->rab_pos_head_stride;
+    l.rab_time = m->rab_time; l.rt_hs = m->rab_time_head_stride;
+    l.alpha = m->alpha;
+    e = hstu::launch_ln_gate(l, stream);
+    if (e != hipSuccess) return device_error(e, "epilogue launch");
     return ok();
 }
 

@@ -79,6 +79,13 @@ struct Params {
     const uint32_t* stats;
     const uint32_t* enc;
     int pos_copy;   // floats per shifted copy of the reversed position table
+    // cross mode: queries (and O) in their own row space; the fields above
+    // then describe the keys (a history cache)
+    const int32_t* q_offsets;
+    const int64_t* ts_q;
+    const uint32_t* enc_q;
+    const uint32_t* stats_q;
+    int nblk_q;
 };
 
 struct Smem {
@@ -131,7 +138,10 @@ __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage,
     if (wave == 0) issue_codes(d, s, stage, kt, L, lane);
 }
 
-template <bool kSilu>
+// kCross: the queries are candidates in their own buffers, each seeing every
+// key of its sequence's history (position n, no mask beyond the key count);
+// their own key is added by the epilogue.
+template <bool kSilu, bool kCross>
 __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const void* ws_base, uint32_t ws_bytes) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     Smem& s = *reinterpret_cast<Smem*>(smem_raw);
@@ -182,8 +192,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // them (and the buffer descriptors built from them) in SGPRs
         const int64_t row0 = uni(p.offsets[b]);
         const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
-        const int n = uni(p.ncand ? L - p.ncand[b] : L);
+        const int n = kCross ? L : uni(p.ncand ? L - p.ncand[b] : L);
         const int bbase = b * p.nblk;
+        // query rows: the sequence's own, or (cross) the candidates'
+        const int64_t row0q = kCross ? (int64_t)uni(p.q_offsets[b]) : row0;
+        const int Lq = kCross ? uni(p.q_offsets[b + 1] - (int)row0q) : L;
 
         // ---- bias tables (reloaded only when they differ by head)
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
@@ -234,10 +247,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // ---- this wave's 32 query rows
         const int wrow0 = qt * BM + wave * 32;
         const int i = wrow0 + l32;               // this lane's query row
-        const bool row_valid = i < L;
+        const bool row_valid = i < Lq;
         bf16x8 qf[8];
         {
-            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
+            const uint16_t* qp = p.q + (row0q + i) * p.qs + h * HD + h2 * 8;
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) {
                 u32x4 z = {0u, 0u, 0u, 0u};
@@ -245,23 +258,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 qf[kc] = __builtin_bit_cast(bf16x8, z);
             }
         }
-        const int64_t t_first = p.ts[row0];
-        const int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
-        uint32_t tie = row_valid ? p.enc[row0 + i] : 0x80000000u;
-        const int qblk = bbase + qt * (BM / 32) + wave;   // this wave's 32-row block
-        const bool wave_rows = wrow0 < L;
-        uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
-        uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
+        // (cross: a user without history has no keys, and no rows to read)
+        const int64_t t_first = (!kCross || L > 0) ? p.ts[row0] : 0;
+        const int64_t ti64 = row_valid ? (kCross ? p.ts_q[row0q + i] : p.ts[row0 + i]) : t_first;
+        uint32_t tie = row_valid ? (kCross ? p.enc_q[row0q + i] : p.enc[row0 + i]) : 0x80000000u;
+        const int qblk = (kCross ? b * p.nblk_q : bbase) + qt * (BM / 32) + wave;   // this wave's 32-row block
+        const uint32_t* qstats = kCross ? p.stats_q : p.stats;
+        const bool wave_rows = wrow0 < Lq;
+        uint32_t rmin = wave_rows ? qstats[2 * qblk] : 0x80000000u;
+        uint32_t rmax = wave_rows ? qstats[2 * qblk + 1] : 0x80000000u;
         rmin = uniu(rmin);
         rmax = uniu(rmax);
         const bool rows_wide = rmin > rmax;
-        const int prow = min(i, n);
+        const int prow = kCross ? n : min(i, n);
         // visibility of row i (rows past L see nothing): keys j <= vis_lim,
-        // and j == vis_self for a candidate row
-        const int vis_lim = i >= L ? -1 : (i < n ? i : n - 1);
-        const int vis_self = (i >= n && i < L) ? i : -1;
-        const bool cand_rows = wrow0 + 31 >= n;   // the block holds candidate rows
-        const int prow_min = uni(min(wrow0, n));
+        // and j == vis_self for a candidate row (cross: every history key)
+        const int vis_lim = kCross ? (i < Lq ? n - 1 : -1) : (i >= L ? -1 : (i < n ? i : n - 1));
+        const int vis_self = kCross ? -1 : ((i >= n && i < L) ? i : -1);
+        const bool cand_rows = kCross ? false : wrow0 + 31 >= n;   // the block holds candidate rows
+        const int prow_min = kCross ? n : uni(min(wrow0, n));
         // time table by leading-zero count, one entry per lane (lanes 32-63
         // repeat 0-31), read with readlane for block-uniform buckets
         int ttv = __builtin_bit_cast(int, p.rab_time[(int64_t)h * p.rt_hs + min(p.NT - 1, 31 - l32)]);
@@ -278,7 +293,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
 
-        u32x2 krange_next = kstats[bbase + tile_of(0)];
+        u32x2 krange_next = {0u, 0u};
+        if (!kCross || ntiles > 0) krange_next = kstats[bbase + tile_of(0)];
         for (int it = 0; it < ntiles; ++it) {
             const int kt = tile_of(it);
             const int j0 = kt * BN;
@@ -302,7 +318,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
             const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
             const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
-            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0);
+            const bool full = (j0 + 32 <= n) && (kCross || j0 + 31 <= wrow0);
             const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
             const bool need_codes = !wide && czlo != czhi;
 
@@ -448,8 +464,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ro = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                if (ro < L) {
-                    uint16_t* op = p.o + (row0 + ro) * p.os + h * HD + l32;
+                if (ro < Lq) {
+                    uint16_t* op = p.o + (row0q + ro) * p.os + h * HD + l32;
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
                 }
@@ -459,7 +475,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lr = wave * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                if (qt * BM + lr < L) {
+                if (qt * BM + lr < Lq) {
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb) pp[lr * HD + nb * 32 + l32] = alpha_eff * oacc[nb][r];
                 }
@@ -468,8 +484,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // the row map tells the epilogue which rows to sum from partial slots
         if (p.rowmap && h == 0 && piece == 0 && lane < 32) {
             const int lr = wave * 32 + lane;
-            if (qt * BM + lr < L)
-                p.rowmap[row0 + qt * BM + lr] = slot < 0 ? -1 : (slot | (npieces << 16) | (lr << 23));
+            if (qt * BM + lr < Lq)
+                p.rowmap[row0q + qt * BM + lr] = slot < 0 ? -1 : (slot | (npieces << 16) | (lr << 23));
         }
         lds_barrier();   // this item's LDS use is over before the next item starts
     }
@@ -495,9 +511,13 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.stats = a.stats; p.enc = a.enc;
     p.partial = a.partial; p.rowmap = a.rowmap; p.nblk = a.nblk;
     p.pos_copy = ((a.P + 128 + 4) + 3) & ~3;
+    p.q_offsets = a.q_offsets; p.ts_q = a.ts_q; p.enc_q = a.enc_q; p.stats_q = a.stats_q; p.nblk_q = a.nblk_q;
+    const bool cross = a.q_offsets != nullptr;
     const size_t smem = ((sizeof(Smem) + 15) & ~size_t(15)) + sizeof(float) * 2 * size_t(p.pos_copy);
-    const void* fn = a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true>)
-                                : reinterpret_cast<const void*>(attn_bf16_kernel<false>);
+    const void* fn = cross ? (a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true, true>)
+                                         : reinterpret_cast<const void*>(attn_bf16_kernel<false, true>))
+                           : (a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true, false>)
+                                         : reinterpret_cast<const void*>(attn_bf16_kernel<false, false>));
     if (smem > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
@@ -507,12 +527,20 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     const void* ws_base = a.stats;
     const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
     const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
-    if (a.act == 0)
-        hipExtLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), smem, stream,
+    if (cross) {
+        if (a.act == 0)
+            hipExtLaunchKernelGGL((attn_bf16_kernel<true, true>), dim3(grid), dim3(kThreads), smem, stream,
+                                  a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
+        else
+            hipExtLaunchKernelGGL((attn_bf16_kernel<false, true>), dim3(grid), dim3(kThreads), smem, stream,
+                                  a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
+    } else if (a.act == 0) {
+        hipExtLaunchKernelGGL((attn_bf16_kernel<true, false>), dim3(grid), dim3(kThreads), smem, stream,
                               a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
-    else
-        hipExtLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), smem, stream,
+    } else {
+        hipExtLaunchKernelGGL((attn_bf16_kernel<false, false>), dim3(grid), dim3(kThreads), smem, stream,
                               a.ev_begin, a.ev_end, 0, p, ws_base, wsb);
+    }
     return hipGetLastError();
 }
 

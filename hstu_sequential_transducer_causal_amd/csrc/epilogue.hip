@@ -79,12 +79,12 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
     // valid history row.
     int b = 0, r = 0, n = 0;
     bool want_score = false;
-    if (a.lengths || a.ncand) {
+    if (a.lengths || a.ncand || a.cross) {
         b = seq_of_row(a.offsets, a.B, row);
         r = (int)(row - a.offsets[b]);
         const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
         if (r >= L) return;  // padding row: never read or written
-        n = a.ncand ? L - a.ncand[b] : L;
+        n = a.cross ? 0 : (a.ncand ? L - a.ncand[b] : L);
         want_score = a.w != nullptr && r >= n;
     }
     // (with cand_only only the candidate rows are covered by this call's map)
@@ -133,6 +133,38 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
                         x[c][2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
                     }
                     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + row * a.o_stride + col) = r;
+                }
+            }
+        }
+        if (a.cross) {
+            // the candidate's own key: per head (16 lanes of 8 columns),
+            // s = q.k + rab_pos[0] + rab_time[0], O += alpha SiLU(s) v
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int col = (c * 64 + lane) * 8;
+                float q8[8], k8[8], v8[8];
+                float dot = 0.0f;
+                if (col < W) {
+                    Vec8<true>::load(a.sq, row * a.sqs + col, q8);
+                    Vec8<true>::load(a.sk, row * a.sks + col, k8);
+                    Vec8<true>::load(a.sv, row * a.svs + col, v8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dot = fmaf(q8[e], k8[e], dot);
+                }
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) dot += __shfl_xor(dot, m, 64);
+                if (col < W) {
+                    const int h = col / a.d;
+                    const float sv = dot + a.rab_pos[(int64_t)h * a.rp_hs] + a.rab_time[(int64_t)h * a.rt_hs];
+                    const float act = a.alpha * silu_fast(sv);
+                    u32x4 rr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        rr[e] = pack_bf16x2(fmaf(act, v8[2 * e], x[c][2 * e]), fmaf(act, v8[2 * e + 1], x[c][2 * e + 1]));
+                        x[c][2 * e] = __uint_as_float(rr[e] << 16);
+                        x[c][2 * e + 1] = __uint_as_float(rr[e] & 0xffff0000u);
+                    }
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + row * a.o_stride + col) = rr;
                 }
             }
         }

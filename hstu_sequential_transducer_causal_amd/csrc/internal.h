@@ -100,6 +100,13 @@ struct SchedArgs {
     uint32_t* stats;     // pairs (min, max), block j of sequence b at b * nblk + j
     int nblk;
     int64_t cap_blk;
+    // cross mode: the rows are candidates, each item's key tiles are the
+    // whole history of its sequence (kv_offsets), and the codes count from
+    // the history's first event (ref_offsets, ref_ts); skip_list: codes only
+    const int32_t* kv_offsets = nullptr;
+    const int32_t* ref_offsets = nullptr;
+    const int64_t* ref_ts = nullptr;
+    int skip_list = 0;
 };
 
 // Work list and timestamp codes, in one launch.
@@ -139,6 +146,14 @@ struct AttnCoreArgs {
     const uint32_t* enc;
     int64_t num_rows;
     hipEvent_t ev_begin, ev_end;   // optional: stamped at the kernel's own start and end
+    // cross mode (bf16 core; q_offsets != NULL): queries, their timestamps,
+    // codes and block ranges in their own row space; offsets, ts, enc and
+    // stats above are the keys' (a history cache), every key visible
+    const int32_t* q_offsets = nullptr;
+    const int64_t* ts_q = nullptr;
+    const uint32_t* enc_q = nullptr;
+    const uint32_t* stats_q = nullptr;
+    int nblk_q = 0;
 };
 
 hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream);
@@ -242,6 +257,16 @@ struct LnGateArgs {
     const float* partial;
     int H, d, BM;
     int cand_only;        // the core computed only candidate-row blocks: map only those rows
+    // cross mode (bf16, d = 128): every row is a candidate scored against a
+    // history cache; its own key adds alpha SiLU(q.k + rab_pos[0] +
+    // rab_time[0]) v per head to O (written back) before the LayerNorm
+    int cross = 0;
+    const void* sq = nullptr; int64_t sqs = 0;
+    const void* sk = nullptr; int64_t sks = 0;
+    const void* sv = nullptr; int64_t svs = 0;
+    const float* rab_pos = nullptr; int rp_hs = 0;
+    const float* rab_time = nullptr; int rt_hs = 0;
+    float alpha = 0.0f;
 };
 
 hipError_t launch_ln_gate(const LnGateArgs& a, hipStream_t stream);

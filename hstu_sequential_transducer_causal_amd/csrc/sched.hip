@@ -52,7 +52,14 @@ struct Ranges {
     int a_end, kb_begin, kb_end;
 };
 
-__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int BN, bool kv_mode) {
+__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int BN, bool kv_mode, bool cross) {
+    if (cross) {
+        // candidate rows against a history cache of n keys: all of them
+        Ranges r;
+        r.a_end = ceil_div(n, BN);
+        r.kb_begin = r.kb_end = r.a_end;
+        return r;
+    }
     if (kv_mode) {
         // key block [k0, k1): the 32-row query tiles from k0's on -- to the
         // end for a block holding history keys (every later row and every
@@ -148,6 +155,7 @@ __device__ __forceinline__ int seq_length(const SchedArgs& a, int b) {
 }
 
 __device__ __forceinline__ int seq_history(const SchedArgs& a, int b, int L) {
+    if (a.kv_offsets) return a.kv_offsets[b + 1] - a.kv_offsets[b];   // cross: the history cache
     return a.ncand ? L - a.ncand[b] : L;
 }
 
@@ -242,7 +250,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
             n = seq_history(a, b, L);
         }
         qt += first_tile(a, n, BM);
-        return tile_ranges(L, n, qt, BM, BN, a.kv_mode != 0);
+        return tile_ranges(L, n, qt, BM, BN, a.kv_mode != 0, a.kv_offsets != nullptr);
     };
     auto cost_of = [](const Ranges& r) { return r.a_end + (r.kb_end - r.kb_begin); };
     auto cost_at = [&](int f) {
@@ -417,7 +425,10 @@ __device__ void encode_timestamps(const SchedArgs& a) {
     bool narrow = true;
     const int j = j0 + (lane & 31);
     if (active && j < L) {
-        const int64_t t_first = a.ts[row0];
+        // codes relative to the sequence's first event, or to its history's
+        // first event when the rows are candidates scored against a cache
+        int64_t t_first = a.ts[row0];
+        if (a.ref_offsets && a.ref_offsets[b + 1] > a.ref_offsets[b]) t_first = a.ref_ts[a.ref_offsets[b]];
         const int64_t d = a.ts[row0 + j] - t_first;
         narrow = d > -(int64_t(1) << 30) && d < (int64_t(1) << 30);
         const uint32_t e = uint32_t(int32_t(d) * 2) + 0x80000000u;
@@ -443,10 +454,11 @@ __device__ void encode_timestamps(const SchedArgs& a) {
 // only) encode the timestamps.
 __global__ void __launch_bounds__(kThreads) prep_kernel(SchedArgs a) {
     __shared__ SchedSmem s;
-    if (blockIdx.x == 0)
-        build_work_list(a, s);
-    else
+    if (blockIdx.x == 0) {
+        if (!a.skip_list) build_work_list(a, s);
+    } else {
         encode_timestamps(a);
+    }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

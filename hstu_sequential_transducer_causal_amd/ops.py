@@ -2,7 +2,7 @@
 
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
-Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score,
+Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score, mfalcon_score_cached,
 hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule.
 """
 from __future__ import annotations
@@ -234,6 +234,69 @@ def mfalcon_score(q, k, v, u, seq_offsets, num_candidates, timestamps, rab_pos, 
     _lib.check(lib.mfalcon_score(ctypes.byref(m), workspace.data_ptr(), workspace.numel(),
                                  _stream_ptr(stream)))
     return scores, o, y
+
+
+def make_mfalcon_cached_args(k_hist, v_hist, hist_offsets, ts_hist, q, k, v, u, cand_offsets,
+                             ts_cand, rab_pos, rab_time, alpha, w, *, max_hist_len: int,
+                             max_cands: int, scores, score_stride: int, o=None,
+                             ln_eps: float = 1e-5, ev_core_begin=None,
+                             ev_core_end=None) -> _lib.MfalconCachedArgs:
+    if q.dim() != 3:
+        raise ValueError("q must be [candidate rows, H, d]")
+    H, d = q.shape[1], q.shape[2]
+    m = _lib.MfalconCachedArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconCachedArgs)
+    m.B = hist_offsets.numel() - 1
+    m.H, m.d = H, d
+    m.max_hist_len, m.max_cands = int(max_hist_len), int(max_cands)
+    m.hist_offsets, m.num_hist_rows = hist_offsets.data_ptr(), k_hist.shape[0]
+    m.k_hist, m.k_hist_stride = _ptr(k_hist), _head_view_stride(k_hist, H, d)
+    m.v_hist, m.v_hist_stride = _ptr(v_hist), _head_view_stride(v_hist, H, d)
+    m.ts_hist = ts_hist.data_ptr()
+    m.cand_offsets, m.num_cand_rows = cand_offsets.data_ptr(), q.shape[0]
+    m.q, m.q_stride = _ptr(q), _head_view_stride(q, H, d)
+    m.k, m.k_stride = _ptr(k), _head_view_stride(k, H, d)
+    m.v, m.v_stride = _ptr(v), _head_view_stride(v, H, d)
+    m.u, m.u_stride = _ptr(u), _head_view_stride(u, H, d)
+    m.ts_cand = ts_cand.data_ptr()
+    m.rab_pos, m.num_pos_buckets = rab_pos.data_ptr(), rab_pos.shape[-1]
+    m.rab_pos_head_stride = rab_pos.shape[-1] if rab_pos.dim() == 2 else 0
+    m.rab_time, m.num_time_buckets = rab_time.data_ptr(), rab_time.shape[-1]
+    m.rab_time_head_stride = rab_time.shape[-1] if rab_time.dim() == 2 else 0
+    m.alpha, m.ln_eps = float(alpha), float(ln_eps)
+    m.w, m.scores, m.score_stride = w.data_ptr(), scores.data_ptr(), int(score_stride)
+    m.o, m.o_stride = (_ptr(o), _head_view_stride(o, H, d)) if o is not None else (None, 0)
+    m.ev_core_begin, m.ev_core_end = ev_core_begin, ev_core_end
+    return m
+
+
+def mfalcon_cached_workspace_bytes(m: _lib.MfalconCachedArgs) -> int:
+    return int(_lib.load().hstu_mfalcon_cached_workspace_bytes(ctypes.byref(m)))
+
+
+def mfalcon_score_cached(k_hist, v_hist, hist_offsets, ts_hist, q, k, v, u, cand_offsets,
+                         ts_cand, rab_pos, rab_time, alpha, w, *, max_hist_len: int,
+                         max_cands: int, score_stride: int, ln_eps: float = 1e-5, o=None,
+                         scores=None, workspace=None, stream=None, ev_core_begin=None,
+                         ev_core_end=None):
+    """Scores [B, score_stride] (fp32) of every candidate against a cached
+    history (keys/values [hist rows, H, d]); returns (scores, o) where o is
+    the candidates' attention output when given, else None."""
+    lib = _lib.load()
+    B = hist_offsets.numel() - 1
+    if scores is None:
+        scores = torch.zeros(B, score_stride, dtype=torch.float32, device=q.device)
+    m = make_mfalcon_cached_args(k_hist, v_hist, hist_offsets, ts_hist, q, k, v, u, cand_offsets,
+                                 ts_cand, rab_pos, rab_time, alpha, w, max_hist_len=max_hist_len,
+                                 max_cands=max_cands, scores=scores, score_stride=score_stride,
+                                 o=o, ln_eps=ln_eps, ev_core_begin=ev_core_begin,
+                                 ev_core_end=ev_core_end)
+    need = lib.hstu_mfalcon_cached_workspace_bytes(ctypes.byref(m))
+    if workspace is None:
+        workspace = _empty_ws(need, q.device)
+    _lib.check(lib.mfalcon_score_cached(ctypes.byref(m), workspace.data_ptr(), workspace.numel(),
+                                        _stream_ptr(stream)))
+    return scores, o
 
 
 def make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,

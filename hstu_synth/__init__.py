@@ -224,6 +224,45 @@ def make_attn(seed: int, lengths, H: int, d: int, P: int, NT: int, alpha: float,
                       dtype=dtype, num_candidates=nc, w=w, name=name)
 
 
+@dataclasses.dataclass
+class CachedSplit:
+    """An M-FALCON batch cut into a history KV cache and candidate rows.
+
+    ``hist_rows`` / ``cand_rows`` index the combined [history | candidates]
+    layout of the source batch; the cache holds each user's history keys and
+    values back to back (``hist_offsets``), the candidates theirs
+    (``cand_offsets``).  ``ts`` is the combined layout's timestamps after the
+    candidates' were redrawn (so the two layouts agree row for row)."""
+    hist_offsets: np.ndarray   # int32 [B+1]
+    cand_offsets: np.ndarray   # int32 [B+1]
+    hist_rows: np.ndarray      # int64 [history rows]
+    cand_rows: np.ndarray      # int64 [candidate rows]
+    ts: np.ndarray             # int64 [T]
+
+
+def split_cached(x: AttnInputs, seed: int, max_gap: int = 0) -> CachedSplit:
+    """Cut ``x`` (built with ``num_candidates``) into cache and candidates.
+    With ``max_gap`` > 0 every candidate's timestamp is redrawn as the user's
+    last history timestamp plus a uniform gap in [0, max_gap] seconds (the
+    request time of each candidate need not be the last event's)."""
+    rng = np.random.default_rng(seed)
+    nc = np.asarray(x.num_candidates, dtype=np.int64)
+    L = np.diff(x.offsets.astype(np.int64))
+    n = L - nc
+    hist_rows = np.concatenate([np.arange(x.offsets[b], x.offsets[b] + n[b]) for b in range(x.B)]
+                               + [np.zeros(0, np.int64)]).astype(np.int64)
+    cand_rows = np.concatenate([np.arange(x.offsets[b] + n[b], x.offsets[b + 1]) for b in range(x.B)]
+                               + [np.zeros(0, np.int64)]).astype(np.int64)
+    ts = x.ts.copy()
+    if max_gap > 0:
+        for b in range(x.B):
+            c0, c1 = int(x.offsets[b] + n[b]), int(x.offsets[b + 1])
+            last = ts[c0 - 1] if n[b] > 0 else TS_EPOCH
+            ts[c0:c1] = last + rng.integers(0, max_gap + 1, size=c1 - c0)
+    return CachedSplit(hist_offsets=_offsets(n), cand_offsets=_offsets(nc), hist_rows=hist_rows,
+                       cand_rows=cand_rows, ts=ts)
+
+
 def make_layer_stack(seed: int, lengths, H: int, d: int, D: int, layers: int, P: int,
                      NT: int, alpha: float, *, x_std: float = 0.5, rab_std: float = 0.1,
                      mean_gap: float = 60.0, name: str = "") -> LayerInputs:

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 5
+#define HSTU_ABI_VERSION 6
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -173,6 +173,55 @@ size_t hstu_mfalcon_workspace_bytes(const hstu_mfalcon_args* args);
 
 hstu_status mfalcon_score(const hstu_mfalcon_args* args, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ----------------------------------- M-FALCON against a history KV cache */
+/* Scores of many candidates per user against a cached history: M-FALCON at
+ * scale ("行动胜于言语：万亿参数序列转导器用于生成式推荐", section "2.3 M-FALCON
+ * 算法": candidates in microbatches, the history's keys and values computed
+ * once and cached).  Each candidate c of user b sees the user's n_b history
+ * keys and itself, at position n_b -- exactly the rows of mfalcon_score for
+ * the sequence [history | candidates] -- so, without a softmax, its output is
+ * a sum over the cached history plus its own term:
+ *   O_c = alpha (sum_{j<n_b} SiLU(S_cj) V_j + SiLU(q_c.k_c + rab_pos[0]
+ *         + rab_time[0]) v_c),   S_cj = q_c.K_j + rab_pos[min(n_b - j, P-1)]
+ *         + rab_time[tb(t_c, t_j)],
+ *   scores[b * score_stride + c] = < LN(O_c) (.) U_c, w >.
+ * Any number of candidates per call (a call is one or many microbatches);
+ * candidate timestamps are given per candidate.  bf16, d = 128.
+ * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
+typedef struct hstu_mfalcon_cached_args {
+    uint32_t struct_size;          /* = sizeof(hstu_mfalcon_cached_args) */
+    int32_t B, H, d;               /* users, heads, head dim (128) */
+    int32_t max_hist_len;          /* >= every n_b */
+    int32_t max_cands;             /* >= every candidate count */
+    const int32_t* hist_offsets;   /* [B+1] device: rows of the history cache */
+    int64_t num_hist_rows;
+    const void* k_hist; int64_t k_hist_stride;   /* [hist rows, H*d] bf16 cached keys */
+    const void* v_hist; int64_t v_hist_stride;   /* cached values */
+    const int64_t* ts_hist;        /* [hist rows] seconds */
+    const int32_t* cand_offsets;   /* [B+1] device: rows of the candidates */
+    int64_t num_cand_rows;
+    const void* q; int64_t q_stride;   /* [cand rows, H*d] bf16, the candidates' */
+    const void* k; int64_t k_stride;
+    const void* v; int64_t v_stride;
+    const void* u; int64_t u_stride;
+    const int64_t* ts_cand;        /* [cand rows] */
+    const float* rab_pos; int32_t num_pos_buckets; int32_t rab_pos_head_stride;
+    const float* rab_time; int32_t num_time_buckets; int32_t rab_time_head_stride;
+    float alpha;
+    float ln_eps;
+    const float* w;                /* [H*d] */
+    float* scores;                 /* out [B * score_stride] */
+    int32_t score_stride;          /* >= max_cands */
+    void* o; int64_t o_stride;     /* out: candidates' O [cand rows, H*d] bf16, or NULL */
+    void* ev_core_begin;           /* optional hipEvent_t around the attention core */
+    void* ev_core_end;
+} hstu_mfalcon_cached_args;
+
+size_t hstu_mfalcon_cached_workspace_bytes(const hstu_mfalcon_cached_args* args);
+
+hstu_status mfalcon_score_cached(const hstu_mfalcon_cached_args* args, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------ HSTU layer */
 /* One HSTU layer over a packed jagged batch (bf16, d = 128):

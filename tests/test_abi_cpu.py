@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 5
+    assert lib.hstu_abi_version() == 6
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -50,6 +50,7 @@ def test_abi_version_and_status_strings(lib):
 _STRUCTS = {
     "hstu_attn_args": _lib.AttnArgs,
     "hstu_mfalcon_args": _lib.MfalconArgs,
+    "hstu_mfalcon_cached_args": _lib.MfalconCachedArgs,
     "hstu_layer_args": _lib.LayerArgs,
     "hstu_attn_bwd_args": _lib.AttnBwdArgs,
     "hstu_layer_bwd_args": _lib.LayerBwdArgs,
@@ -316,3 +317,66 @@ def test_sl_validation_errors_before_any_launch(lib, name, mut):
     mut(a)
     assert lib.hstu_stochastic_length(ctypes.byref(a), None) == _lib.HSTU_ERR_ARG
     assert lib.hstu_last_error()
+
+
+def _valid_cached():
+    m = _lib.MfalconCachedArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconCachedArgs)
+    m.B, m.H, m.d, m.max_hist_len, m.max_cands = 2, 4, 128, 1000, 300
+    fake = 0x10000
+    m.hist_offsets = m.cand_offsets = m.ts_hist = m.ts_cand = fake
+    m.num_hist_rows, m.num_cand_rows = 2000, 600
+    m.k_hist = m.v_hist = m.q = m.k = m.v = m.u = fake
+    m.k_hist_stride = m.v_hist_stride = m.q_stride = m.k_stride = m.v_stride = m.u_stride = 512
+    m.rab_pos, m.num_pos_buckets = fake, 1024
+    m.rab_time, m.num_time_buckets = fake, 32
+    m.alpha, m.ln_eps = 1.0 / 1000, 1e-5
+    m.w = m.scores = fake
+    m.score_stride = 300
+    return m
+
+
+CACHED_MUTATIONS = [
+    ("struct_size", lambda m: setattr(m, "struct_size", 4), _lib.HSTU_ERR_ARG),
+    ("H<1", lambda m: setattr(m, "H", 0), _lib.HSTU_ERR_ARG),
+    ("d=64", lambda m: setattr(m, "d", 64), _lib.HSTU_ERR_UNSUPPORTED),
+    ("max_hist_len<0", lambda m: setattr(m, "max_hist_len", -1), _lib.HSTU_ERR_ARG),
+    ("max_cands too big", lambda m: setattr(m, "max_cands", 1 << 30), _lib.HSTU_ERR_ARG),
+    ("score_stride<max_cands", lambda m: setattr(m, "score_stride", 299), _lib.HSTU_ERR_ARG),
+    ("P=0", lambda m: setattr(m, "num_pos_buckets", 0), _lib.HSTU_ERR_ARG),
+    ("NT=0", lambda m: setattr(m, "num_time_buckets", 0), _lib.HSTU_ERR_ARG),
+    ("alpha inf", lambda m: setattr(m, "alpha", float("inf")), _lib.HSTU_ERR_ARG),
+    ("eps 0", lambda m: setattr(m, "ln_eps", 0.0), _lib.HSTU_ERR_ARG),
+    ("k_hist stride", lambda m: setattr(m, "k_hist_stride", 500), _lib.HSTU_ERR_ARG),
+    ("u stride % 8", lambda m: setattr(m, "u_stride", 516), _lib.HSTU_ERR_ARG),
+    ("H*d > 4096", lambda m: setattr(m, "H", 64), _lib.HSTU_ERR_UNSUPPORTED),
+    ("v_hist NULL", lambda m: setattr(m, "v_hist", None), _lib.HSTU_ERR_ARG),
+    ("ts_cand NULL", lambda m: setattr(m, "ts_cand", None), _lib.HSTU_ERR_ARG),
+    ("w NULL", lambda m: setattr(m, "w", None), _lib.HSTU_ERR_ARG),
+    ("misaligned q", lambda m: setattr(m, "q", 0x10008), _lib.HSTU_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,mut,status", CACHED_MUTATIONS, ids=[m[0] for m in CACHED_MUTATIONS])
+def test_cached_validation_errors_before_any_launch(lib, name, mut, status):
+    m = _valid_cached()
+    mut(m)
+    assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == status
+    assert lib.hstu_last_error()
+    assert lib.hstu_mfalcon_cached_workspace_bytes(ctypes.byref(m)) == 0
+
+
+def test_cached_workspace_errors_and_size(lib):
+    m = _valid_cached()
+    need = lib.hstu_mfalcon_cached_workspace_bytes(ctypes.byref(m))
+    # at least the candidates' O (no o given) and the history's row codes
+    assert need >= 600 * 512 * 2 + 2000 * 4
+    assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.mfalcon_score_cached(ctypes.byref(m), 0x20000, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
+    m.o, m.o_stride = 0x10000, 512
+    assert lib.hstu_mfalcon_cached_workspace_bytes(ctypes.byref(m)) == need - 600 * 512 * 2
+    # nothing to score: no launch, no workspace needed
+    m.num_cand_rows = 0
+    assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == _lib.HSTU_OK
+    m.num_cand_rows, m.B = 600, 0
+    assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == _lib.HSTU_OK
