@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--cpu-sample-seqs", type=int, default=0, help="0: all sequences")
     p.add_argument("--only-bwd", action="store_true",
                    help="only time the attention gradients on --workload (for kernel traces)")
+    p.add_argument("--only-cached", action="store_true",
+                   help="only the M-FALCON pass against a history KV cache")
     p.add_argument("--only-layer-bwd", action="store_true",
                    help="only time the gradients of one layer of the stack workload (for kernel traces)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -255,6 +257,70 @@ class LayerBwdCase:
                                       torch.cuda.current_stream().cuda_stream))
 
 
+class CachedCase:
+    """M-FALCON against a history KV cache: every user's candidates scored
+    over the cached history keys/values (mfalcon_score_cached)."""
+
+    def __init__(self, dev, B=4, n=2048, c=16384, seed=41):
+        import torch
+        import hstu_synth as synth
+        from hstu_sequential_transducer_causal_amd import ops
+        x = synth.make_attn(seed, [n + c] * B, H=4, d=128, P=1024, NT=32, alpha=1.0 / (n + 512),
+                            dtype="bf16", num_candidates=[c] * B, with_w=True)
+        sp = synth.split_cached(x, seed=seed + 1, max_gap=86_400)
+        self.name = f"mfalcon_cached_bf16_b{B}_n{n}_c{c}_h4_d128"
+        self.B, self.n, self.c, self.H, self.d = B, n, c, x.H, x.d
+        hr, cr = sp.hist_rows, sp.cand_rows
+        self.k_hist, self.v_hist = up(x.k[hr], "bf16", dev), up(x.v[hr], "bf16", dev)
+        self.q, self.k, self.v, self.u = (up(a[cr], "bf16", dev) for a in (x.q, x.k, x.v, x.u))
+        self.ts_hist = torch.from_numpy(np.ascontiguousarray(sp.ts[hr])).to(dev)
+        self.ts_cand = torch.from_numpy(np.ascontiguousarray(sp.ts[cr])).to(dev)
+        self.hoff = torch.from_numpy(sp.hist_offsets).to(dev)
+        self.coff = torch.from_numpy(sp.cand_offsets).to(dev)
+        self.rp = torch.from_numpy(x.rab_pos).to(dev)
+        self.rt = torch.from_numpy(x.rab_time).to(dev)
+        self.w = torch.from_numpy(x.w).to(dev)
+        self.alpha, self.eps = x.alpha, x.eps
+        self.o = torch.empty_like(self.q)
+        self.scores = torch.zeros(B, c, dtype=torch.float32, device=dev)
+        m = ops.make_mfalcon_cached_args(self.k_hist, self.v_hist, self.hoff, self.ts_hist, self.q,
+                                         self.k, self.v, self.u, self.coff, self.ts_cand, self.rp,
+                                         self.rt, self.alpha, self.w, max_hist_len=n, max_cands=c,
+                                         scores=self.scores, score_stride=c, o=self.o)
+        self.ws = torch.empty(max(1, ops.mfalcon_cached_workspace_bytes(m)), dtype=torch.uint8,
+                              device=dev)
+        self.x, self.dev = x, dev
+
+    def step(self, ev0=None, ev1=None):
+        from hstu_sequential_transducer_causal_amd import ops
+        ops.mfalcon_score_cached(self.k_hist, self.v_hist, self.hoff, self.ts_hist, self.q, self.k,
+                                 self.v, self.u, self.coff, self.ts_cand, self.rp, self.rt,
+                                 self.alpha, self.w, max_hist_len=self.n, max_cands=self.c,
+                                 score_stride=self.c, ln_eps=self.eps, o=self.o,
+                                 scores=self.scores, workspace=self.ws, ev_core_begin=ev0,
+                                 ev_core_end=ev1)
+
+    def record(self, steps):
+        st, ce = time_case(self, steps, 2)
+        ncand = self.B * self.c
+        # unmasked pairs: every candidate with the n history keys and itself
+        fc = float(ncand) * (self.n + 1) * 4 * self.d * self.H
+        rec = {"ms_per_step": round(st, 4), "candidates_per_s": round(ncand / (st * 1e-3), 1),
+               "candidate_pair_tflops": round(fc / (st * 1e-3) / 1e12, 2)}
+        if ce:
+            rec["core_ms"] = round(ce, 4)
+            rec["core_tflops"] = round(fc / (ce * 1e-3) / 1e12, 2)
+        # the same scores from the combined [history | candidates] layout,
+        # computing only the query tiles that hold candidates
+        import torch
+        comb = AttnCase(self.x, self.dev, with_scores=True, candidates_only=True)
+        st2, _ = time_case(comb, steps, 2)
+        rec["combined_layout_candidates_only_ms"] = round(st2, 4)
+        del comb
+        torch.cuda.empty_cache()
+        return rec
+
+
 def sl_record(dev, steps):
     """Stochastic length with the gather of the rows of Q, K, V, U (8 heads of
     128, bf16) and timestamps, on the long-sequence workload's raw batch."""
@@ -390,10 +456,11 @@ def main():
     wl = args.workload
     log(f"generating workload {wl}")
     x = synth.config(wl)
+    if args.only_cached:
+        c = CachedCase(dev)
+        print(json.dumps({"workload": c.name, **c.record(args.steps)}), flush=True)
+        return
     if args.only_layer_bwd:
-        sl_rec = sl_record(dev, max(3, args.steps // 3))
-        others["hstu_sl_gather_longseq_raw_b16_cap2120"] = sl_rec
-        log(f"stochastic length + gather: {sl_rec}")
         xl = synth.config(5)
         c = LayerBwdCase(xl, dev)
         st, _ = time_case(c, args.steps, args.warmup, core_events=False)
@@ -483,6 +550,13 @@ def main():
                     rec["core_ms"] = round(ce, 4)
                 others[xo.name + "_candidates_only"] = rec
                 log(f"{xo.name} candidates only: {rec}")
+                del c
+                torch.cuda.empty_cache()
+                # many candidates per user against a cached history
+                c = CachedCase(dev)
+                rec = c.record(max(3, args.steps // 3))
+                others[c.name] = rec
+                log(f"{c.name}: {rec}")
                 del c
                 torch.cuda.empty_cache()
         sl_rec = sl_record(dev, max(3, args.steps // 3))
