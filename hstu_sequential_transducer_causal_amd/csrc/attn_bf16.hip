@@ -38,6 +38,13 @@
 //     -ln 2 that turns A' into SiLU(S) is folded into alpha.
 //   * Blocks whose pairs are all visible skip the mask; the others select
 //     (never multiply) so that padding and masked garbage cannot leak.
+//   * Software pipeline over the key tiles: while S(t) is being built (its
+//     LDS reads, bias, and the dependent chain of 8 QK^T MFMAs), the
+//     activation of S(t-1) runs on the VALU between those MFMAs, and then
+//     O += A(t-1) V(t-1) is issued; V(t) is read into registers at the end of
+//     the step.  Fragment addresses are one per-lane base XOR constants, so
+//     the loop keeps two address registers and never touches scratch (a
+//     scratch reload would wait for every tile load in flight).
 //   * Persistent grid: workgroups pull items (longest first) from the
 //     scheduler's list through an atomic cursor until it is exhausted.
 #include <hip/hip_ext.h>
@@ -136,6 +143,45 @@ __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage,
     issue_k(d, s, stage, kt, wave);
     issue_v(d, s, stage, kt, wave);
     if (wave == 0) issue_codes(d, s, stage, kt, L, lane);
+}
+
+// Fragment reads by 32-bit LDS address.  Every per-lane address of a tile is
+// one base XOR a constant: K fragment kc of lane l (row l % 32, chunk
+// 2 kc + l / 32, swizzled by row & 15) sits at base ^ (kc << 5), and the V^T
+// fragment for column block nb at base ^ (nb << 6) (the swizzle moves whole
+// 64-byte quarters by row & 3), with the chunk and the second row group as
+// immediate offsets.  Only the two bases stay live across the tile loop.
+__device__ __forceinline__ uint32_t k_lane_offset(int lane) {
+    const int l32 = lane & 31, h2 = lane >> 5;
+    return (uint32_t)(l32 * kRowBytes + ((h2 ^ (l32 & 15)) << 4));
+}
+__device__ __forceinline__ uint32_t v_lane_offset(int lane) {
+    const int m = lane & 15;
+    const int row = 4 * (lane >> 5) + (m >> 2);                  // key row of chunk 0
+    const int x = ((lane >> 4) & 1) * 2 + ((m & 3) >> 1);         // 16-byte chunk within the column quarter
+    return (uint32_t)(row * kRowBytes + ((((row & 3) << 2) | x) << 4) + 8 * (m & 1));
+}
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    return *(lds_bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+    return __builtin_bit_cast(u32x2, r);
+}
+// V^T fragments of a tile's two 16-key chunks (the layout of read_v_chunk)
+__device__ __forceinline__ void read_v_tile(uint32_t stage_base, uint32_t voff, u32x4 (&vf)[2][4]) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const uint32_t a = stage_base + (voff ^ (uint32_t)(nb << 6));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x2 v0 = lds_read_tr(a + c * 16 * kRowBytes);
+            const u32x2 v1 = lds_read_tr(a + c * 16 * kRowBytes + 8 * kRowBytes);
+            vf[c][nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        }
+    }
 }
 
 // kCross: the queries are candidates in their own buffers, each seeing every
@@ -293,48 +339,57 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
 
+        // ---- software pipeline over the key tiles.  Iteration it builds
+        //      S(it) while it finishes tile it-1: the activation of S(it-1)
+        //      runs on the VALU while S(it)'s LDS reads are in flight, then
+        //      the MFMAs of S(it) = K Q^T and of O += A(it-1) V(it-1) go out
+        //      interleaved (two independent chains keep the matrix pipe
+        //      busy), and V(it) is read into registers for the next iteration.
         u32x2 krange_next = {0u, 0u};
         if (!kCross || ntiles > 0) krange_next = kstats[bbase + tile_of(0)];
-        for (int it = 0; it < ntiles; ++it) {
+        u32x4 vf[2][4];
+        const uint32_t koff_lane = k_lane_offset(lane), voff_lane = v_lane_offset(lane);
+
+        // the barrier of tile it (its loads have landed, every wave is done
+        // with tile it-1's stage: V(it-1) was read before it), then the K
+        // part of tile it+3's loads into that stage
+        auto tile_sync = [&](int it) {
+            const int later = min(kStages - 2, ntiles - 1 - it);
+            wait_vmcnt(later * per_tile);
+            lds_sync();
+            if (it + kStages - 1 < ntiles)
+                issue_k(dma, s, (it + kStages - 1) & (kStages - 1), tile_of(it + kStages - 1), wave);
+        };
+
+        // bias of tile it (as the initial accumulator, plus a constant) and
+        // its K fragments; the time part follows in time_bias (after other
+        // work has covered the LDS latency of the codes)
+        struct TileFacts {
+            bool wide;
+            int czlo, czhi, j0;
+        };
+        auto tile_bias = [&](int it, f32x16& acc, float& cadd, bf16x8 (&kf)[8]) -> TileFacts {
             const int kt = tile_of(it);
             const int j0 = kt * BN;
             const int stage = it & (kStages - 1);
-            const bool issue = it + kStages - 1 < ntiles;
-            const int st3 = (it + kStages - 1) & (kStages - 1), kt3 = issue ? tile_of(it + kStages - 1) : 0;
-            // this tile's loads have landed once at most the later tiles' are outstanding
-            const int later = min(kStages - 2, ntiles - 1 - it);
-            wait_vmcnt(later * per_tile);
-            lds_barrier();   // everyone's loads for this tile are visible; tile it-1 is done
-            if (issue) issue_k(dma, s, st3, kt3, wave);
             const uint8_t* k_lds = s.k[stage];
-            const uint8_t* v_lds = s.v[stage];
-            const uint32_t* tsk = s.tsk[stage];
 
-            // ---------- block-uniform facts (scalar; the key block's code
-            //            range was loaded one tile ahead)
+            // block-uniform facts (scalar; the key block's code range was
+            // loaded one tile ahead)
             const uint32_t kmn = uniu(krange_next[0]), kmx = uniu(krange_next[1]);
             if (it + 1 < ntiles) krange_next = kstats[bbase + tile_of(it + 1)];
             const bool wide = rows_wide || kmn > kmx;
             const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
             const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
             const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
-            const bool full = (j0 + 32 <= n) && (kCross || j0 + 31 <= wrow0);
             const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
-            const bool need_codes = !wide && czlo != czhi;
 
-            // ---------- this tile's LDS reads, issued up front in the order of
-            //            use (LDS returns in order): key codes and position
-            //            entries when needed, K, V
-            u32x4 codes[4];
-            if (need_codes) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
-            }
-            // position bias as the initial accumulator: lane (row i, keys
-            // j0 + 8q + 4h2 + t) reads reversed-table entries u0 + 8q + t; a
-            // block whose differences all clamp takes rab_pos[P-1] as a constant
-            f32x16 acc;
-            float cadd = 0.0f;
+            // LDS reads: position entries when needed, then K (the key codes,
+            // when needed, are read by time_bias)
+            // position bias: lane (row i, keys j0 + 8q + 4h2 + t) reads
+            // reversed-table entries u0 + 8q + t; a block whose differences
+            // all clamp takes rab_pos[P-1] as a constant
+            cadd = 0.0f;
             if (pos_clamped) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -355,76 +410,84 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     }
                 }
             }
-            bf16x8 kf[8];
+            uint32_t ko = koff_lane;
+            asm volatile("" : "+v"(ko));   // recomputed per tile: keeps one register live, not eight
+            const uint32_t kb = lds_addr(k_lds) + ko;
 #pragma unroll
-            for (int kc = 0; kc < 8; ++kc) kf[kc] = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
-            // V^T fragments of the tile's first 16-key chunk (the second
-            // chunk's are read while the QK^T products run)
-            u32x4 vf[2][4];
-            read_v_chunk(v_lds, 0, lane, vf[0]);
-
-            // ---------- time bias: constant over the block (most blocks), one
-            //            of two buckets split at a power of two, or per element
-            if (!wide && czlo - czhi <= 1) {
-                const float tlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czlo));
-                if (czlo == czhi) {
-                    cadd += tlo;
-                } else {
-                    // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
-                    const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
-                    const uint32_t thr = 1u << (32 - czlo);
+            for (int kc = 0; kc < 8; ++kc) kf[kc] = lds_read_b128(kb ^ (uint32_t)(kc << 5));
+            return TileFacts{wide, czlo, czhi, j0};
+        };
+        auto time_bias = [&](int it, const TileFacts& f, f32x16& acc, float& cadd) {
+                const bool wide = f.wide;
+                const int czlo = f.czlo, czhi = f.czhi, j0 = f.j0;
+                const uint32_t* tsk = s.tsk[it & (kStages - 1)];
+                u32x4 codes[4];
+                if (!wide && czlo != czhi) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
+                }
+                // time bias: constant over the block (most blocks), one of two
+                // buckets split at a power of two, or per element
+                if (!wide && czlo - czhi <= 1) {
+                    const float tlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czlo));
+                    if (czlo == czhi) {
+                        cadd += tlo;
+                    } else {
+                        // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
+                        const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
+                        const uint32_t thr = 1u << (32 - czlo);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                acc[4 * q + t] += sad_u32(tie, codes[q][t], 1u) >= thr ? thi : tlo;
+                    }
+                } else if (!wide) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) acc[4 * q + t] += sad_u32(tie, codes[q][t], 1u) >= thr ? thi : tlo;
-                }
-            } else if (!wide) {
+                        for (int t = 0; t < 4; ++t)
+                            acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, codes[q][t], 1u))];
+                } else {
+                    const int64_t* tsb = p.ts + row0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, codes[q][t], 1u))];
-            } else {
-                const int64_t* tsb = p.ts + row0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int j = j0 + 8 * q + 4 * h2 + t;
-                        const int64_t tj = j < L ? tsb[j] : t_first;
-                        const int64_t dt = ti64 - tj;
-                        const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                        acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
+                        for (int t = 0; t < 4; ++t) {
+                            const int j = j0 + 8 * q + 4 * h2 + t;
+                            const int64_t tj = j < L ? tsb[j] : t_first;
+                            const int64_t dt = ti64 - tj;
+                            const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
+                            acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
+                        }
                     }
                 }
-            }
+        };
 
-            // ---------- S^T = K Q^T (+ bias): one accumulation chain (a
-            //            second chain to hide the MFMA dependency measured
-            //            1 % slower: its merge costs 32 VALU per tile and the
-            //            other wave on the SIMD fills the dependency gaps)
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) acc = mfma32(kf[kc], qf[kc], acc);
-            read_v_chunk(v_lds, 1, lane, vf[1]);
-            if (issue) issue_v(dma, s, st3, kt3, wave);
-
-            // ---------- activation, mask, bf16 packing
-            float a[16];
+        // activation of element r of S(it) (in place)
+        auto act_one = [&](f32x16& acc, float c2, int r) {
             if (kSilu) {
-                const float c2 = cadd * kNegLog2e;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float t = __builtin_fmaf(acc[r], kNegLog2e, c2);
-                    const float e = __builtin_amdgcn_exp2f(t);
-                    a[r] = t * __builtin_amdgcn_rcpf(1.0f + e);
-                }
+                const float t = __builtin_fmaf(acc[r], kNegLog2e, c2);
+                const float e = __builtin_amdgcn_exp2f(t);
+                acc[r] = t * __builtin_amdgcn_rcpf(1.0f + e);
             } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) a[r] = acc[r] + cadd;
+                acc[r] = acc[r] + c2;
             }
+        };
+        auto act_const = [&](float cadd) { return kSilu ? cadd * kNegLog2e : cadd; };
+
+        // mask of the activated S(it), packed to bf16: the A operand of
+        // O += A V for the tile's two 16-key chunks
+        auto tile_pack = [&](int it, const f32x16& a_in, u32x4 (&pk)[2]) {
+            const int j0 = tile_of(it) * BN;
+            const bool full = (j0 + 32 <= n) && (kCross || j0 + 31 <= wrow0);
+            float a[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[r] = a_in[r];
             if (!full) {
-                // key j = j0 + 4h2 + c (c = 8q + t) is visible when
-                // j <= vis_lim (causal history, or all history for a
-                // candidate) or j == vis_self (a candidate's own key)
+                // key j = j0 + 4h2 + c (c = 8q + t) is visible when j <=
+                // vis_lim (causal history, or all history for a candidate) or
+                // j == vis_self (a candidate's own key)
                 const int jb = j0 + 4 * h2;
                 const int xl = vis_lim - jb, xs = vis_self - jb;
                 if (cand_rows) {
@@ -440,21 +503,102 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                         for (int t = 0; t < 4; ++t) a[4 * q + t] = xl >= 8 * q + t ? a[4 * q + t] : 0.0f;
                 }
             }
-
-            if (issue && wave == 0) issue_codes(dma, s, st3, kt3, L, lane);
-
-            // ---------- O += A V for the tile's two 16-key chunks
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 pk;
-                pk[0] = pack_bf16x2(a[8 * c + 0], a[8 * c + 1]);
-                pk[1] = pack_bf16x2(a[8 * c + 2], a[8 * c + 3]);
-                pk[2] = pack_bf16x2(a[8 * c + 4], a[8 * c + 5]);
-                pk[3] = pack_bf16x2(a[8 * c + 6], a[8 * c + 7]);
-                const bf16x8 pa = __builtin_bit_cast(bf16x8, pk);
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) oacc[nb] = mfma32(pa, __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
+                for (int e = 0; e < 4; ++e) pk[c][e] = pack_bf16x2(a[8 * c + 2 * e], a[8 * c + 2 * e + 1]);
+        };
+
+        // the V and key-code parts of tile it+3's loads
+        auto issue_rest = [&](int it) {
+            if (it + kStages - 1 < ntiles) {
+                const int st3 = (it + kStages - 1) & (kStages - 1), kt3 = tile_of(it + kStages - 1);
+                issue_v(dma, s, st3, kt3, wave);
+                if (wave == 0) issue_codes(dma, s, st3, kt3, L, lane);
             }
+        };
+
+        auto read_v = [&](int it) {
+            uint32_t vo = voff_lane;
+            asm volatile("" : "+v"(vo));
+            read_v_tile(lds_addr(s.v[it & (kStages - 1)]), vo, vf);
+        };
+
+        // one pipeline step: S(it) into accN while tile it-1 (S in accC)
+        // is finished
+        auto step = [&](int it, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
+            tile_sync(it);
+            bf16x8 kf[8];
+            const TileFacts f = tile_bias(it, accN, caddN, kf);
+            const float c2 = act_const(caddC);
+            // the first activations cover the LDS latency of this tile's reads
+#pragma unroll
+            for (int r = 0; r < 4; ++r) act_one(accC, c2, r);
+            time_bias(it, f, accN, caddN);
+            issue_rest(it);
+            // S(it) = K Q^T: a dependent chain of 8 MFMAs, each followed by
+            // the activation of 1.5 elements of S(it-1)
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                accN = mfma32(kf[kc], qf[kc], accN);
+                if (kc < 6) {
+                    act_one(accC, c2, 4 + 2 * kc);
+                    act_one(accC, c2, 5 + 2 * kc);
+                }
+            }
+#pragma unroll
+            for (int kc = 0; kc < 6; ++kc) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // then VALU
+            }
+            u32x4 pk[2];
+            tile_pack(it - 1, accC, pk);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
+            read_v(it);
+        };
+
+        if (ntiles > 0) {
+            f32x16 accA, accB;
+            float caddA = 0.0f, caddB = 0.0f;
+            // prologue: S(0), V(0)
+            {
+                tile_sync(0);
+                bf16x8 kf[8];
+                const TileFacts f = tile_bias(0, accA, caddA, kf);
+                time_bias(0, f, accA, caddA);
+                issue_rest(0);
+#pragma unroll
+                for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], accA);
+                read_v(0);
+            }
+            int it = 1;
+            for (; it + 1 < ntiles; it += 2) {
+                step(it, accA, caddA, accB, caddB);
+                step(it + 1, accB, caddB, accA, caddA);
+            }
+            if (it < ntiles) {
+                step(it, accA, caddA, accB, caddB);
+                accA = accB;
+                caddA = caddB;
+                ++it;
+            }
+            // epilogue: finish the last tile
+            {
+                const float c2 = act_const(caddA);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) act_one(accA, c2, r);
+            }
+            u32x4 pk[2];
+            tile_pack(ntiles - 1, accA, pk);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
         }
 
         // ---------- O = alpha * acc, rows < L only: bf16 into O, or fp32 into
