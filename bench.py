@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -41,14 +42,16 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=3, help="workload number 2..5 for the main line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=0, help="0: all sequences")
     p.add_argument("--only-bwd", action="store_true",
                    help="only time the attention gradients on --workload (for kernel traces)")
+    p.add_argument("--only-sl-sweep", action="store_true",
+                   help="only the stochastic-length exponent sweep")
     p.add_argument("--only-cached", action="store_true",
                    help="only the M-FALCON pass against a history KV cache")
     p.add_argument("--only-layer-bwd", action="store_true",
@@ -349,6 +352,55 @@ def sl_record(dev, steps):
             "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def sl_sweep_record(dev, steps):
+    """Stochastic-length exponent sweep on the long-sequence workload's raw
+    batch (16 sequences, 8 heads of 128): per alpha the cap is
+    floor(8192 ** (alpha / 2)); a step is the seeded subsampling with the
+    gather of Q, K, V, U and timestamps, then hstu_attn_fwd (with LN * U)
+    on the kept rows."""
+    import torch
+    import hstu_synth as synth
+    from hstu_sequential_transducer_causal_amd import flops, ops
+    L = synth.longseq_raw_lengths()
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)).to(dev)
+    T = int(L.sum())
+    H, d = 8, 128
+    g = torch.Generator(device=dev).manual_seed(6)
+    rows = [(0.5 * torch.randn(T, H * d, generator=g, device=dev)).to(torch.bfloat16) for _ in range(4)]
+    ts = torch.cumsum(torch.randint(1, 120, (T,), generator=g, device=dev), 0).to(torch.int64)
+    rp = (0.1 * torch.randn(1024, generator=g, device=dev)).float()
+    rt = (0.1 * torch.randn(32, generator=g, device=dev)).float()
+    out = {}
+    for alpha in (1.6, 1.7, 1.8, 1.9, 2.0):
+        cap = int(math.floor(synth.SL_MAX_RAW ** (alpha / 2)))
+        kept = np.minimum(L, cap)
+        o = torch.empty(T, H, d, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(o)
+
+        def step(i):
+            oo, _, (q, k, v, u, t) = ops.stochastic_length(off, cap, seed=7, step=i,
+                                                           tensors=(*rows, ts))
+            ops.hstu_attn_fwd(q.view(T, H, d), k.view(T, H, d), v.view(T, H, d), oo, t, rp, rt,
+                              1.0 / synth.SL_MAX_RAW, max_seq_len=cap, u=u.view(T, H, d), o=o, y=y)
+
+        for i in range(2):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        fl = flops.attn_flops(kept, H, d, d)
+        out[f"alpha_{alpha}"] = {"cap": cap, "kept_tokens": int(kept.sum()), "ms_per_step": round(ms, 4),
+                                 "attn_gflop": round(fl / 1e9, 1),
+                                 "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+        log(f"stochastic length alpha {alpha}: {out[f'alpha_{alpha}']}")
+        del o, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_case(case, steps, warmup, core_events=True):
     """Wall time per step (synchronised bracket) and mean core-kernel time (HIP events)."""
     import torch
@@ -456,6 +508,10 @@ def main():
     wl = args.workload
     log(f"generating workload {wl}")
     x = synth.config(wl)
+    if args.only_sl_sweep:
+        print(json.dumps({"workload": "hstu_sl_alpha_sweep_longseq_raw_b16_h8_d128",
+                          **sl_sweep_record(dev, args.steps)}), flush=True)
+        return
     if args.only_cached:
         c = CachedCase(dev)
         print(json.dumps({"workload": c.name, **c.record(args.steps)}), flush=True)
@@ -562,6 +618,7 @@ def main():
         sl_rec = sl_record(dev, max(3, args.steps // 3))
         others["hstu_sl_gather_longseq_raw_b16_cap2120"] = sl_rec
         log(f"stochastic length + gather: {sl_rec}")
+        others["hstu_sl_alpha_sweep_longseq_raw_b16_h8_d128"] = sl_sweep_record(dev, max(3, args.steps // 6))
         xl = synth.config(5)
         c = LayerBwdCase(xl, dev)
         st, _ = time_case(c, max(2, args.steps // 10), 1, core_events=False)
