@@ -480,6 +480,8 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
     return ok();
 }
 
+}  // extern "C"
+
 namespace {
 
 hstu_status validate_layer(const hstu_layer_args* l) {
@@ -638,6 +640,8 @@ LayerBwdWs layer_bwd_ws(const hstu_layer_bwd_args* g) {
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t hstu_layer_workspace_bytes(const hstu_layer_args* l) {
     char saved[sizeof(g_last_error)];

@@ -39,6 +39,9 @@ def test_exports_every_declared_symbol(lib):
     exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
     for name in declared:
         assert name in exported, name
+    # no other C-linkage symbol leaks out (internal C++ names are mangled)
+    plain = set(n for n in exported if not n.startswith("_Z"))
+    assert plain == set(declared), sorted(plain - set(declared))
 
 
 def test_abi_version_and_status_strings(lib):
