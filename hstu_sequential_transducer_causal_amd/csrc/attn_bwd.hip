@@ -152,6 +152,10 @@ __device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint
     return t;
 }
 
+// Floats per copy of the dK/dV kernel's padded position table (P + 128,
+// rounded up to a multiple of 4).
+__host__ __device__ __forceinline__ int ptab2_width(int P) { return (P + 128 + 3) & ~3; }
+
 // Activation value and slope: SiLU (x s, s + x s (1 - s) with s = sigmoid(x))
 // or the identity (x, 1).
 __device__ __forceinline__ void act_and_slope(float x, bool silu, float& a, float& slope) {
@@ -531,6 +535,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
     uint8_t* ring_gt = smem + 3 * kStages * kTileBytes;   // dO, vswz: B operand of dV += A^T dO
     Small& s = small_of<4>(smem);
     float* ptab = ptab_of<4>(smem);
+    // the position table padded for blocks of history rows: copy c holds
+    // T[x - c] at x, T[u] = rab_pos[clamp(u - 32, 0, P - 1)]
+    const int pw = ptab2_width(p.P);
+    float* ptab2 = ptab + ((p.P + 3) & ~3);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -562,9 +570,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
 
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
             load_tables(p, h, ptab, s, tid);
+            const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
+            for (int e = tid; e < 2 * pw; e += kThreads) {
+                const int c = e >= pw ? 1 : 0;
+                const int u = e - c * pw - c;
+                ptab2[e] = rp[min(max(u - 32, 0), P - 1)];
+            }
             loaded_head = h;
             lds_wait();
         }
+        const float pos_far = p.rab_pos[(int64_t)h * p.rp_hs + P - 1];
 
         const TileSrc sq = tile_src(p.q + row0 * p.qs + h * HD, p.qs, L, lane, wave, false);
         const TileSrc sqt = tile_src(p.q + row0 * p.qs + h * HD, p.qs, L, lane, wave, true);
@@ -627,80 +642,194 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
             }
 
         const StatsPtr rstats = stats_ptr(p.stats);
-        for (int it = 0; it < ntiles; ++it) {
-            const int rt = rt_begin + it;
+        // ---- software pipeline over the query tiles: step t builds S(t)
+        //      (bias as the initial accumulator) and dP(t) = dO V^T while the
+        //      activation, slope and G of tile t-1 run on the VALU between
+        //      those MFMAs; then dV += A^T dO and dK += G^T Q for tile t-1.
+        //      The transposed fragments of tile t are read into registers at
+        //      the end of step t, so its stage may be refilled after the next
+        //      barrier.
+        const uint32_t a_off = k_lane_offset(lane), t_off = v_lane_offset(lane);
+        u32x4 trq[2][4], trg[2][4];   // Q^T and dO^T fragments of the tile being finished
+        struct Tile {
+            float cadd;
+            int r0;
+            bool full;
+        };
+
+        auto sync = [&](int t) {
+            wait_tile(t + 1 < ntiles ? per_tile : 0);   // tile t has landed (t+1 may be in flight)
+            lds_sync();                                   // and every wave is done with tile t-1's stage
+            if (t + kStages - 1 < ntiles) issue((t + kStages - 1) % kStages, rt_begin + t + kStages - 1);
+        };
+
+        // bias of tile t into sacc (position, then time per element when the
+        // block needs it); the block-uniform rest goes into the returned cadd
+        auto prep = [&](int t, f32x16& sacc, bf16x8 (&qa)[8], bf16x8 (&ga)[8]) -> Tile {
+            const int rt = rt_begin + t;
             const int r0 = rt * 32;
-            const int stage = it % kStages;
-            const u32x2 rr = rstats[bbase + rt];   // in flight during the wait
-            wait_tile(it + 1 < ntiles ? per_tile : 0);
-            lds_barrier();
-            if (it + kStages - 1 < ntiles) issue((it + kStages - 1) % kStages, rt + kStages - 1);
-
-            const uint8_t* q_lds = ring_q + stage * kTileBytes;
-            const uint8_t* qt_lds = ring_qt + stage * kTileBytes;
-            const uint8_t* g_lds = ring_g + stage * kTileBytes;
-            const uint8_t* gt_lds = ring_gt + stage * kTileBytes;
-            const uint32_t* codes = s.codes[stage];
-
+            const int stage = t % kStages;
+            const u32x2 rr = rstats[bbase + rt];
             const TimeBlock tb = time_block(rr[0], rr[1], kmn, kmx);
             const bool pos_clamped = min(r0, n) - pkey_max >= P - 1;
-            float cadd = 0.0f;
-            if (pos_clamped) cadd += ptab[P - 1];
-            if (tb.constant) cadd += s.tt_fast[tb.cz];
-
-            // S = Q K^T and dO V^T: lane = key j, rows r0 + 8 (r / 4) + 4 h2 + r % 4
-            f32x16 sacc, gacc;
+            const bool hist_rows = r0 + 31 < n;
+            Tile st;
+            st.r0 = r0;
+            st.full = (r0 + 31 < L) && (k0w + 31 < n) && (k0w + 31 <= r0);
+            st.cadd = 0.0f;
+            if (pos_clamped) st.cadd += pos_far;
+            if (tb.constant) st.cadd += s.tt_fast[tb.cz];
+            if (pos_clamped) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] = 0.0f;
-                gacc[r] = 0.0f;
+                for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+            } else if (hist_rows) {
+                // rows i = r0 + c (c = 8q + 4h2 + t): entries x0 + 8q + t of
+                // the padded table, two per 8-byte read
+                const int x0 = min(max(r0 - pkey + 32 + 4 * h2, 0), pw - 32);
+                const int c = x0 & 1;
+                const float* pp = ptab2 + c * pw + (x0 + c);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const float2 pv = *reinterpret_cast<const float2*>(pp + 8 * q + 2 * t2);
+                        sacc[4 * q + 2 * t2] = pv.x;
+                        sacc[4 * q + 2 * t2 + 1] = pv.y;
+                    }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = r0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    sacc[r] = ptab[min(max(min(i, n) - pkey, 0), P - 1)];
+                }
             }
+            const uint8_t* q_lds = ring_q + stage * kTileBytes;
+            const uint8_t* g_lds = ring_g + stage * kTileBytes;
+            uint32_t ao = a_off;
+            asm volatile("" : "+v"(ao));
+            const uint32_t qb = lds_addr(q_lds) + ao, gb = lds_addr(g_lds) + ao;
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_lds + kswz(l32, 2 * kc + h2));
-                const bf16x8 ga = *reinterpret_cast<const bf16x8*>(g_lds + kswz(l32, 2 * kc + h2));
-                sacc = mfma32(qa, kf[kc], sacc);
-                gacc = mfma32(ga, vf[kc], gacc);
+                qa[kc] = lds_read_b128(qb ^ (uint32_t)(kc << 5));
+                ga[kc] = lds_read_b128(gb ^ (uint32_t)(kc << 5));
             }
-
-            float av[16], gv[16];
+            if (!tb.constant) {
+                const uint32_t* codes = s.codes[stage];
+                if (!tb.wide) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                const int i = r0 + c;
-                const bool vis = (i < L) & (j < L) & ((i < n) ? (j <= i) : ((j < n) | (j == i)));
-                float bias = cadd;
-                if (!pos_clamped) bias += ptab[min(max(min(i, n) - pkey, 0), P - 1)];
-                if (!tb.constant) {
-                    if (!tb.wide) {
-                        bias += s.tt_fast[__builtin_clz(sad_u32(codes[c], ej, 1u))];
-                    } else {
+                    for (int r = 0; r < 16; ++r) {
+                        const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        sacc[r] += s.tt_fast[__builtin_clz(sad_u32(codes[c], ej, 1u))];
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = r0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
                         const int64_t ti = i < L ? p.ts[row0 + i] : t_first;
                         const int64_t dt = ti - tj64;
                         const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                        bias += s.tt_wide[bit_length_u64(ad)];
+                        sacc[r] += s.tt_wide[bit_length_u64(ad)];
                     }
                 }
-                float a, slope;
-                act_and_slope(sacc[r] + bias, silu, a, slope);
-                av[r] = vis ? a : 0.0f;
-                gv[r] = vis ? gacc[r] * slope : 0.0f;
             }
+            return st;
+        };
 
-            // dV += A^T dO and dK += G^T Q over the tile's two 16-row chunks
+        // activation, slope and G of element r of a finished S / dP
+        auto act_elem = [&](const f32x16& sacc, const f32x16& gacc, float cadd, int r, float (&av)[16],
+                            float (&gv)[16]) {
+            float a, slope;
+            act_and_slope(sacc[r] + cadd, silu, a, slope);
+            av[r] = a;
+            gv[r] = gacc[r] * slope;
+        };
+
+        // mask (blocks with invisible pairs), pack, dV += A^T dO, dK += G^T Q
+        auto finish = [&](const Tile& st, float (&av)[16], float (&gv)[16]) {
+            if (!st.full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = st.r0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    const bool vis = (i < L) & (j < L) & ((i < n) ? (j <= i) : ((j < n) | (j == i)));
+                    av[r] = vis ? av[r] : 0.0f;
+                    gv[r] = vis ? gv[r] : 0.0f;
+                }
+            }
             bf16x8 pa[2], pg[2];
             pack_a(av, pa);
             pack_a(gv, pg);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 tf[4];
-                read_v_chunk(gt_lds, c, lane, tf);
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) dva[nb] = mfma32(pa[c], __builtin_bit_cast(bf16x8, tf[nb]), dva[nb]);
-                read_v_chunk(qt_lds, c, lane, tf);
+                for (int nb = 0; nb < 4; ++nb) {
+                    dva[nb] = mfma32(pa[c], __builtin_bit_cast(bf16x8, trg[c][nb]), dva[nb]);
+                    dka[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, trq[c][nb]), dka[nb]);
+                }
+        };
+
+        auto read_tr = [&](int t) {
+            const int stage = t % kStages;
+            uint32_t to = t_off;
+            asm volatile("" : "+v"(to));
+            read_v_tile(lds_addr(ring_gt + stage * kTileBytes), to, trg);
+            read_v_tile(lds_addr(ring_qt + stage * kTileBytes), to, trq);
+        };
+
+        auto step = [&](int t, f32x16& sC, f32x16& gC, const Tile& stC, f32x16& sN, f32x16& gN) -> Tile {
+            sync(t);
+            bf16x8 qa[8], ga[8];
+            const Tile stN = prep(t, sN, qa, ga);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) dka[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, tf[nb]), dka[nb]);
+            for (int r = 0; r < 16; ++r) gN[r] = 0.0f;
+            float av[16], gv[16];
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                gN = mfma32(ga[kc], vf[kc], gN);
+                act_elem(sC, gC, stC.cadd, 2 * kc, av, gv);
+                sN = mfma32(qa[kc], kf[kc], sN);
+                act_elem(sC, gC, stC.cadd, 2 * kc + 1, av, gv);
             }
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // then VALU
+            }
+            finish(stC, av, gv);
+            read_tr(t);
+            return stN;
+        };
+
+        if (ntiles > 0) {
+            f32x16 sA, gA, sB, gB;
+            Tile stA, stB;
+            {
+                sync(0);
+                bf16x8 qa[8], ga[8];
+                stA = prep(0, sA, qa, ga);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) gA[r] = 0.0f;
+#pragma unroll
+                for (int kc = 0; kc < 8; ++kc) {
+                    gA = mfma32(ga[kc], vf[kc], gA);
+                    sA = mfma32(qa[kc], kf[kc], sA);
+                }
+                read_tr(0);
+            }
+            int t = 1;
+            for (; t + 1 < ntiles; t += 2) {
+                stB = step(t, sA, gA, stA, sB, gB);
+                stA = step(t + 1, sB, gB, stB, sA, gA);
+            }
+            if (t < ntiles) {
+                stB = step(t, sA, gA, stA, sB, gB);
+                sA = sB;
+                gA = gB;
+                stA = stB;
+            }
+            float av[16], gv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) act_elem(sA, gA, stA.cadd, r, av, gv);
+            finish(stA, av, gv);
         }
 
         // ---- dK, dV = alpha * acc for keys < L; lane holds column nb*32 +
@@ -775,6 +904,7 @@ size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
     b += sizeof(float) * (size_t)((P + 3) & ~3);
     if (hist) b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 32 * 64);
+    else b += sizeof(float) * 2 * (size_t)ptab2_width(P);   // the dK/dV kernel's padded table
     return b;
 }
 
@@ -803,7 +933,9 @@ BwdParams make_params(const AttnBwdArgs& a) {
 
 }  // namespace
 
-bool attn_bwd_tables_fit(int P, int NT) { return smem_bytes(3, P, NT, true) <= 160 * 1024; }
+bool attn_bwd_tables_fit(int P, int NT) {
+    return smem_bytes(3, P, NT, true) <= 160 * 1024 && smem_bytes(4, P, NT, false) <= 160 * 1024;
+}
 
 size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT) {
     return (size_t)cap * (size_t)H * (size_t)(P + NT);

@@ -117,6 +117,45 @@ __device__ __forceinline__ void read_v_chunk(const uint8_t* v_lds, int c, int la
     }
 }
 
+// Fragment reads by 32-bit LDS address.  Every per-lane address of a tile is
+// one base XOR a constant: K fragment kc of lane l (row l % 32, chunk
+// 2 kc + l / 32, swizzled by row & 15) sits at base ^ (kc << 5), and the V^T
+// fragment for column block nb at base ^ (nb << 6) (the swizzle moves whole
+// 64-byte quarters by row & 3), with the chunk and the second row group as
+// immediate offsets.  Only the two bases stay live across the tile loop.
+__device__ __forceinline__ uint32_t k_lane_offset(int lane) {
+    const int l32 = lane & 31, h2 = lane >> 5;
+    return (uint32_t)(l32 * kRowBytes + ((h2 ^ (l32 & 15)) << 4));
+}
+__device__ __forceinline__ uint32_t v_lane_offset(int lane) {
+    const int m = lane & 15;
+    const int row = 4 * (lane >> 5) + (m >> 2);                  // key row of chunk 0
+    const int x = ((lane >> 4) & 1) * 2 + ((m & 3) >> 1);         // 16-byte chunk within the column quarter
+    return (uint32_t)(row * kRowBytes + ((((row & 3) << 2) | x) << 4) + 8 * (m & 1));
+}
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    return *(lds_bf16x8*)(uintptr_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
+    return __builtin_bit_cast(u32x2, r);
+}
+// V^T fragments of a tile's two 16-key chunks (the layout of read_v_chunk)
+__device__ __forceinline__ void read_v_tile(uint32_t stage_base, uint32_t voff, u32x4 (&vf)[2][4]) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const uint32_t a = stage_base + (voff ^ (uint32_t)(nb << 6));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x2 v0 = lds_read_tr(a + c * 16 * kRowBytes);
+            const u32x2 v1 = lds_read_tr(a + c * 16 * kRowBytes + 8 * kRowBytes);
+            vf[c][nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        }
+    }
+}
+
 // Bucket index (leading zeros of 2|dt| + 1) of an encoded gap 2|dt|.
 __device__ __forceinline__ uint32_t clz_gap(uint32_t gap2) { return __builtin_clz(gap2 + 1u); }
 
