@@ -351,126 +351,136 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             for (int r = 0; r < 16; ++r) dqa[nb][r] = 0.0f;
 
         const StatsPtr kstats = stats_ptr(p.stats);
-        for (int it = 0; it < ntiles; ++it) {
-            const int kt = tile_of(it);
+        // ---- software pipeline over the key tiles: step t builds S^T(t)
+        //      (bias as the initial accumulator) and (dO V^T)^T(t) while the
+        //      activation slope and G of tile t-1 run on the VALU between those
+        //      MFMAs; then tile t-1's mask, block sums, dQ += G K and histogram
+        //      updates.  Tile t's K^T fragments (for dQ) are read into
+        //      registers at the end of step t, and its time buckets are kept
+        //      packed, so its stage may be refilled after the next barrier.
+        const uint32_t a_off = k_lane_offset(lane), t_off = v_lane_offset(lane);
+        const float pos_far = ptab[P - 1];
+        u32x4 trk[2][4];   // K^T fragments of the tile being finished
+        struct Tile {
+            float cadd;
+            int j0, tlo, thi;
+            bool full, pos_clamped, tconst, few;
+            uint32_t tb4[4];   // time bucket of element r in byte r % 4 of word r / 4
+        };
+
+        auto sync = [&](int t) {
+            wait_tile(t + 1 < ntiles ? per_tile : 0);   // tile t has landed (t+1 may be in flight)
+            lds_sync();                                   // and every wave is done with tile t-1's stage
+            if (t + kStages - 1 < ntiles) issue((t + kStages - 1) % kStages, tile_of(t + kStages - 1));
+        };
+
+        auto prep = [&](int t, f32x16& sacc, bf16x8 (&ka)[8], bf16x8 (&va)[8]) -> Tile {
+            const int kt = tile_of(t);
             const int j0 = kt * 32;
-            const int stage = it % kStages;
-            const u32x2 kr = kstats[bbase + kt];   // in flight during the wait
-            wait_tile(it + 1 < ntiles ? per_tile : 0);
-            lds_barrier();
-            if (it + kStages - 1 < ntiles) issue((it + kStages - 1) % kStages, tile_of(it + kStages - 1));
-
-            const uint8_t* k_lds = ring_k + stage * kTileBytes;
-            const uint8_t* kt_lds = ring_kt + stage * kTileBytes;
-            const uint8_t* v_lds = ring_v + stage * kTileBytes;
-            const uint32_t* codes = s.codes[stage];
-
-            // block-uniform bias shortcuts
+            const int stage = t % kStages;
+            const u32x2 kr = kstats[bbase + kt];
             const TimeBlock tb = time_block(rmin, rmax, kr[0], kr[1]);
-            const bool pos_clamped = prow_min - min(j0 + 31, n) >= P - 1;
-            float cadd = 0.0f;
-            if (pos_clamped) cadd += ptab[P - 1];
-            if (tb.constant) cadd += s.tt_fast[tb.cz];
-
-            // S^T = K Q^T and (dO V^T)^T = V dO^T: lane = row i, keys
-            // j0 + 8 (r / 4) + 4 h2 + r % 4
-            f32x16 sacc, gacc;
+            Tile st;
+            st.j0 = j0;
+            st.pos_clamped = prow_min - min(j0 + 31, n) >= P - 1;
+            st.tconst = tb.constant;
+            st.tlo = min(NT - 1, 31 - tb.cz);
+            st.thi = min(NT - 1, 31 - tb.czhi);
+            st.few = !tb.constant && !tb.wide && st.thi - st.tlo < 4;
+            st.full = (j0 + 32 <= n) && (j0 + 31 <= wrow0) && (wrow0 + 31 < L);
+            st.cadd = 0.0f;
+            if (st.pos_clamped) st.cadd += pos_far;
+            if (tb.constant) st.cadd += s.tt_fast[tb.cz];
+            // position bias per element (keys j = j0 + c, c = 8q + 4h2 + t)
+            if (st.pos_clamped) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] = 0.0f;
-                gacc[r] = 0.0f;
+                for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    sacc[r] = ptab[min(max(prow - min(j, n), 0), P - 1)];
+                }
             }
+            const uint8_t* k_lds = ring_k + stage * kTileBytes;
+            const uint8_t* v_lds = ring_v + stage * kTileBytes;
+            uint32_t ao = a_off;
+            asm volatile("" : "+v"(ao));
+            const uint32_t kb = lds_addr(k_lds) + ao, vb = lds_addr(v_lds) + ao;
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + kswz(l32, 2 * kc + h2));
-                const bf16x8 va = *reinterpret_cast<const bf16x8*>(v_lds + kswz(l32, 2 * kc + h2));
-                sacc = mfma32(ka, qf[kc], sacc);
-                gacc = mfma32(va, gf[kc], gacc);
+                ka[kc] = lds_read_b128(kb ^ (uint32_t)(kc << 5));
+                va[kc] = lds_read_b128(vb ^ (uint32_t)(kc << 5));
             }
-
-            // time buckets of the block: [tlo, thi]; up to 4 of them are
-            // summed in registers (a per-element atomic on a few addresses
-            // would serialise the lanes), more per element
-            const int tlo = min(NT - 1, 31 - tb.cz), thi = min(NT - 1, 31 - tb.czhi);
-            const bool few_buckets = !tb.constant && !tb.wide && thi - tlo < 4;
-
-            // (1) buckets and bias reads of all 16 elements.  LDS operations
-            //     complete in order, so nothing here may queue behind the
-            //     histogram atomics: those go out last, after the products.
-            int pbv[16], tbv[16];
-            float bias[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                const int j = j0 + c;
-                pbv[r] = P - 1;
-                bias[r] = cadd;
-                if (!pos_clamped) {
-                    pbv[r] = min(max(prow - min(j, n), 0), P - 1);
-                    bias[r] += ptab[pbv[r]];
-                }
-                tbv[r] = 0;
-                if (!tb.constant) {
+            for (int w4 = 0; w4 < 4; ++w4) st.tb4[w4] = 0u;
+            if (!tb.constant) {
+                const uint32_t* codes = s.codes[stage];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    int tbr;
                     if (!tb.wide) {
                         const uint32_t z = __builtin_clz(sad_u32(ei, codes[c], 1u));
-                        bias[r] += s.tt_fast[z];
-                        tbv[r] = min(NT - 1, 31 - (int)z);
+                        sacc[r] += s.tt_fast[z];
+                        tbr = min(NT - 1, 31 - (int)z);
                     } else {
+                        const int j = j0 + c;
                         const int64_t tj = j < L ? p.ts[row0 + j] : t_first;
                         const int64_t dt = ti64 - tj;
                         const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
                         const int bl = bit_length_u64(ad);
-                        bias[r] += s.tt_wide[bl];
-                        tbv[r] = min(NT - 1, bl);
+                        sacc[r] += s.tt_wide[bl];
+                        tbr = min(NT - 1, bl);
                     }
+                    st.tb4[r >> 2] |= (uint32_t)tbr << (8 * (r & 3));
                 }
             }
-            // (2) G = dA * act'(S), masked (a block of history keys that all
-            //     precede every row of the wave needs no mask)
-            const bool full = (j0 + 32 <= n) && (j0 + 31 <= wrow0) && (wrow0 + 31 < L);
-            float gv[16];
+            return st;
+        };
+
+        auto finish = [&](const Tile& st, float (&gv)[16]) {
+            // mask (blocks with invisible pairs)
+            if (!st.full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = st.j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    gv[r] = ((j <= vis_lim) | (j == vis_self)) ? gv[r] : 0.0f;
+                }
+            }
+            auto tbv = [&](int r) { return (int)((st.tb4[r >> 2] >> (8 * (r & 3))) & 0xffu); };
+            // block sums (cross-lane, no LDS)
             float gsum = 0.0f;
             float tsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                const bool vis = full || (j <= vis_lim) | (j == vis_self);
-                float a, slope;
-                act_and_slope(sacc[r] + bias[r], silu, a, slope);
-                const float g = vis ? gacc[r] * slope : 0.0f;
-                gv[r] = g;
-                gsum += g;
-                if (few_buckets) {
+                gsum += gv[r];
+                if (st.few) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) tsum[k] += (tbv[r] - tlo == k) ? g : 0.0f;
+                    for (int k = 0; k < 4; ++k) tsum[k] += (tbv(r) - st.tlo == k) ? gv[r] : 0.0f;
                 }
             }
-            // (3) block sums (cross-lane, no LDS)
-            if (pos_clamped || tb.constant) gsum = wave_total(gsum);
-            if (few_buckets) {
+            if (st.pos_clamped || st.tconst) gsum = wave_total(gsum);
+            if (st.few) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    if (tlo + k <= thi) tsum[k] = wave_total(tsum[k]);
+                    if (st.tlo + k <= st.thi) tsum[k] = wave_total(tsum[k]);
             }
-
-            // (4) dQ += G K over the tile's two 16-key chunks
+            // dQ += G K over the tile's two 16-key chunks
             bf16x8 pg[2];
             pack_a(gv, pg);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 kf[4];
-                read_v_chunk(kt_lds, c, lane, kf);
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, kf[nb]), dqa[nb]);
-            }
-
-            // (5) the histogram updates.  When the wave's rows are all history
-            //     rows, the position bucket of a visible pair is
-            //     min(i - j, P - 1): the block's 63 diagonals, summed through
-            //     the skewed scratch with plain LDS writes and reads, take one
-            //     atomic each (LDS float atomics are slow).  Otherwise, and
-            //     for time buckets beyond the register sums, per element.
-            const bool diag = !pos_clamped && wrow0 + 31 < n;
+                for (int nb = 0; nb < 4; ++nb)
+                    dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, trk[c][nb]), dqa[nb]);
+            // histogram updates.  When the wave's rows are all history rows,
+            // the position bucket of a visible pair is min(i - j, P - 1): the
+            // block's 63 diagonals, summed through the skewed scratch with
+            // plain LDS writes and reads, take one atomic each (LDS float
+            // atomics are slow).  Otherwise, and for time buckets beyond the
+            // register sums, per element.
+            const bool diag = !st.pos_clamped && wrow0 + 31 < n;
             if (diag) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -481,25 +491,97 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 float dsum = 0.0f;
 #pragma unroll
                 for (int rho = 0; rho < 32; ++rho) dsum += scratch[rho * 64 + lane];
-                const int pb = wrow0 - j0 + lane - 31;
+                const int pb = wrow0 - st.j0 + lane - 31;
                 if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 if (gv[r] != 0.0f) {
-                    if (!pos_clamped && !diag) atomicAdd(&hist[pbv[r]], gv[r]);
-                    if (!tb.constant && !few_buckets) atomicAdd(&hist[P + tbv[r]], gv[r]);
+                    if (!st.pos_clamped && !diag) {
+                        const int j = st.j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        atomicAdd(&hist[min(max(prow - min(j, n), 0), P - 1)], gv[r]);
+                    }
+                    if (!st.tconst && !st.few) atomicAdd(&hist[P + tbv(r)], gv[r]);
                 }
             }
             if (lane == 63) {
-                if (pos_clamped) atomicAdd(&hist[P - 1], gsum);
-                if (tb.constant) atomicAdd(&hist[P + tlo], gsum);
-                if (few_buckets) {
+                if (st.pos_clamped) atomicAdd(&hist[P - 1], gsum);
+                if (st.tconst) atomicAdd(&hist[P + st.tlo], gsum);
+                if (st.few) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        if (tlo + k <= thi) atomicAdd(&hist[P + tlo + k], tsum[k]);
+                        if (st.tlo + k <= st.thi) atomicAdd(&hist[P + st.tlo + k], tsum[k]);
                 }
             }
+        };
+
+        auto read_tr = [&](int t) {
+            uint32_t to = t_off;
+            asm volatile("" : "+v"(to));
+            read_v_tile(lds_addr(ring_kt + (t % kStages) * kTileBytes), to, trk);
+        };
+
+        auto act_g = [&](const f32x16& sacc, const f32x16& gacc, float cadd, int r, float (&gv)[16]) {
+            float a, slope;
+            act_and_slope(sacc[r] + cadd, silu, a, slope);
+            gv[r] = gacc[r] * slope;
+        };
+
+        auto step = [&](int t, f32x16& sC, f32x16& gC, const Tile& stC, f32x16& sN, f32x16& gN) -> Tile {
+            sync(t);
+            bf16x8 ka[8], va[8];
+            const Tile stN = prep(t, sN, ka, va);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) gN[r] = 0.0f;
+            float gv[16];
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) {
+                gN = mfma32(va[kc], gf[kc], gN);
+                act_g(sC, gC, stC.cadd, 2 * kc, gv);
+                sN = mfma32(ka[kc], qf[kc], sN);
+                act_g(sC, gC, stC.cadd, 2 * kc + 1, gv);
+            }
+#pragma unroll
+            for (int kc = 0; kc < 16; ++kc) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
+            }
+            finish(stC, gv);
+            read_tr(t);
+            return stN;
+        };
+
+        if (ntiles > 0) {
+            f32x16 sA, gA, sB, gB;
+            Tile stA, stB;
+            {
+                sync(0);
+                bf16x8 ka[8], va[8];
+                stA = prep(0, sA, ka, va);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) gA[r] = 0.0f;
+#pragma unroll
+                for (int kc = 0; kc < 8; ++kc) {
+                    gA = mfma32(va[kc], gf[kc], gA);
+                    sA = mfma32(ka[kc], qf[kc], sA);
+                }
+                read_tr(0);
+            }
+            int t = 1;
+            for (; t + 1 < ntiles; t += 2) {
+                stB = step(t, sA, gA, stA, sB, gB);
+                stA = step(t + 1, sB, gB, stB, sA, gA);
+            }
+            if (t < ntiles) {
+                stB = step(t, sA, gA, stA, sB, gB);
+                sA = sB;
+                gA = gB;
+                stA = stB;
+            }
+            float gv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) act_g(sA, gA, stA.cadd, r, gv);
+            finish(stA, gv);
         }
 
         // ---- dQ = alpha * acc for rows < L; lane holds column nb*32 + l32 at
