@@ -50,6 +50,7 @@ constexpr int HD = 128;
 constexpr int kThreads = 256;
 constexpr int kBlk = 128;          // query rows (dq) or keys (dkv) per work item
 constexpr int kStages = 3;         // tiles t .. t+2 in flight
+constexpr int kDiagPitch = 36;     // floats per column of the dQ kernel's diagonal scratch
 
 struct BwdParams {
     int H;
@@ -248,10 +249,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     // interleave; added in wave order at the end of the item
     const int hw = (p.P + p.NT + 3) & ~3;
     float* hist_all = ptab + ((p.P + 3) & ~3);
-    // per wave, a 32 x 64 scratch in which the block's G is written skewed
-    // (row rho, column rho - c + 31), so that each column holds one diagonal.
-    // Only the band rho <= column <= rho + 31 is ever written, so with the
-    // scratch zeroed once the rest reads as zero.
+    // per wave, a scratch in which the block's G is written skewed and
+    // transposed (column rho - c + 31, row rho; kDiagPitch floats per
+    // column), so that each column holds one diagonal and its 32 entries are
+    // read with 8 16-byte loads.  Only the band rho <= column <= rho + 31 is
+    // ever written, so with the scratch zeroed once the rest reads as zero.
     float* scratch_all = hist_all + 4 * hw;
 
     const int tid = threadIdx.x;
@@ -269,8 +271,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     int loaded_head = -1;
 
     float* hist = hist_all + wave * hw;
-    float* scratch = scratch_all + wave * (32 * 64);
-    for (int e = tid; e < 4 * hw + 4 * 32 * 64; e += kThreads) hist_all[e] = 0.0f;
+    float* scratch = scratch_all + wave * (64 * kDiagPitch);
+    for (int e = tid; e < 4 * hw + 4 * 64 * kDiagPitch; e += kThreads) hist_all[e] = 0.0f;
 
     for (;;) {
         fetch_item(p, s, total_work, tid);
@@ -450,21 +452,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             }
             auto tbv = [&](int r) { return (int)((st.tb4[r >> 2] >> (8 * (r & 3))) & 0xffu); };
             // block sums (cross-lane, no LDS)
+            // (a block spanning few time buckets sums buckets tlo+1 .. thi
+            // per element and takes bucket tlo as the rest of the total)
             float gsum = 0.0f;
             float tsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                gsum += gv[r];
-                if (st.few) {
+            for (int r = 0; r < 16; ++r) gsum += gv[r];
+            if (st.few) {
+                const int nk = st.thi - st.tlo;   // 1 .. 3
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) tsum[k] += (tbv(r) - st.tlo == k) ? gv[r] : 0.0f;
+                for (int r = 0; r < 16; ++r) {
+                    const int k = tbv(r) - st.tlo;
+                    tsum[1] += (k == 1) ? gv[r] : 0.0f;
+                    if (nk >= 2) {
+                        tsum[2] += (k == 2) ? gv[r] : 0.0f;
+                        tsum[3] += (k == 3) ? gv[r] : 0.0f;
+                    }
                 }
             }
-            if (st.pos_clamped || st.tconst) gsum = wave_total(gsum);
+            if (st.pos_clamped || st.tconst || st.few) gsum = wave_total(gsum);
             if (st.few) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                for (int k = 1; k < 4; ++k)
                     if (st.tlo + k <= st.thi) tsum[k] = wave_total(tsum[k]);
+                tsum[0] = ((gsum - tsum[1]) - tsum[2]) - tsum[3];
             }
             // dQ += G K over the tile's two 16-key chunks
             bf16x8 pg[2];
@@ -485,12 +496,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    scratch[l32 * 64 + (l32 + 31 - c)] = gv[r];
+                    scratch[(l32 + 31 - c) * kDiagPitch + l32] = gv[r];
                 }
                 // lane u: diagonal rho - c = u - 31 (cells off the band are 0)
                 float dsum = 0.0f;
+                const f32x4* col = reinterpret_cast<const f32x4*>(scratch + lane * kDiagPitch);
 #pragma unroll
-                for (int rho = 0; rho < 32; ++rho) dsum += scratch[rho * 64 + lane];
+                for (int k = 0; k < 8; ++k) {
+                    const f32x4 x = col[k];
+                    dsum += x[0];
+                    dsum += x[1];
+                    dsum += x[2];
+                    dsum += x[3];
+                }
                 const int pb = wrow0 - st.j0 + lane - 31;
                 if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             }
@@ -985,7 +1003,7 @@ __global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2,
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
     b += sizeof(float) * (size_t)((P + 3) & ~3);
-    if (hist) b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 32 * 64);
+    if (hist) b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch);
     else b += sizeof(float) * 2 * (size_t)ptab2_width(P);   // the dK/dV kernel's padded table
     return b;
 }
