@@ -156,6 +156,10 @@ __device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint
 // Floats per copy of the dK/dV kernel's padded position table (P + 128,
 // rounded up to a multiple of 4).
 __host__ __device__ __forceinline__ int ptab2_width(int P) { return (P + 128 + 3) & ~3; }
+// Floats per copy of the dQ kernel's reversed position table (covers the
+// entries u0 + 0 .. 31 for every clamped u0 = P + 63 - x, x in [0, P + 26],
+// plus the shift of the second copy).
+__host__ __device__ __forceinline__ int rtab_width(int P) { return (P + 132 + 3) & ~3; }
 
 // Activation value and slope: SiLU (x s, s + x s (1 - s) with s = sigmoid(x))
 // or the identity (x, 1).
@@ -243,12 +247,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     uint8_t* ring_kt = smem + kStages * kTileBytes;  // K, vswz: B operand of dQ += G K
     uint8_t* ring_v = smem + 2 * kStages * kTileBytes;   // V, kswz: A operand of V dO^T
     Small& s = small_of<3>(smem);
-    float* ptab = ptab_of<3>(smem);
+    // the position table reversed, in two copies shifted by one (as in the
+    // forward): copy c holds R[w - c] at w, R[u] = rab_pos[clamp(Dhi - u, 0,
+    // P - 1)], so a lane reads the entries of its row against 2 keys with one
+    // aligned 8-byte load; rab_pos[pb] itself is R[Dhi - pb]
+    const int rw = rtab_width(p.P);
+    const int Dhi = p.P + 63;
+    float* rtab = ptab_of<3>(smem);
     // one histogram per wave ([P] position, then [NT] time buckets), so that
     // the order of the additions into each does not depend on how the waves
     // interleave; added in wave order at the end of the item
     const int hw = (p.P + p.NT + 3) & ~3;
-    float* hist_all = ptab + ((p.P + 3) & ~3);
+    float* hist_all = rtab + 2 * rw;
     // per wave, a scratch in which the block's G is written skewed and
     // transposed (column rho - c + 31, row rho; kDiagPitch floats per
     // column), so that each column holds one diagonal and its 32 entries are
@@ -289,7 +299,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
         const int bbase = b * p.nblk;
 
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
-            load_tables(p, h, ptab, s, tid);
+            const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
+            const float* rt = p.rab_time + (int64_t)h * p.rt_hs;
+            for (int e = tid; e < 2 * rw; e += kThreads) {
+                const int c = e >= rw ? 1 : 0;
+                const int u = e - c * rw - c;
+                rtab[e] = rp[min(max(Dhi - u, 0), P - 1)];
+            }
+            if (tid < 32) s.tt_fast[tid] = rt[min(NT - 1, 31 - tid)];
+            if (tid < 65) s.tt_wide[tid] = rt[min(NT - 1, tid)];
             loaded_head = h;
             lds_wait();   // visible to all after the first tile's barrier
         }
@@ -361,7 +379,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
         //      registers at the end of step t, and its time buckets are kept
         //      packed, so its stage may be refilled after the next barrier.
         const uint32_t a_off = k_lane_offset(lane), t_off = v_lane_offset(lane);
-        const float pos_far = ptab[P - 1];
+        const float pos_far = rtab[Dhi - (P - 1)];
         u32x4 trk[2][4];   // K^T fragments of the tile being finished
         struct Tile {
             float cadd;
@@ -393,15 +411,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             st.cadd = 0.0f;
             if (st.pos_clamped) st.cadd += pos_far;
             if (tb.constant) st.cadd += s.tt_fast[tb.cz];
-            // position bias per element (keys j = j0 + c, c = 8q + 4h2 + t)
+            // position bias (keys j = j0 + c, c = 8q + 4h2 + t): a block of
+            // history keys reads entries u0 + 8q + t of the reversed table,
+            // a block holding candidate keys per element
             if (st.pos_clamped) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+            } else if (j0 + 31 < n) {
+                const int x = min(max(prow - (j0 + 4 * h2), 0), P + 26);
+                const int u0 = Dhi - x;
+                const int c = u0 & 1;
+                const float* pp = rtab + c * rw + (u0 + c);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        const float2 pv = *reinterpret_cast<const float2*>(pp + 8 * q + 2 * t2);
+                        sacc[4 * q + 2 * t2] = pv.x;
+                        sacc[4 * q + 2 * t2 + 1] = pv.y;
+                    }
             } else {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    sacc[r] = ptab[min(max(prow - min(j, n), 0), P - 1)];
+                    sacc[r] = rtab[Dhi - min(max(prow - min(j, n), 0), P - 1)];
                 }
             }
             const uint8_t* k_lds = ring_k + stage * kTileBytes;
@@ -1002,9 +1035,10 @@ __global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2,
 
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
-    b += sizeof(float) * (size_t)((P + 3) & ~3);
-    if (hist) b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch);
-    else b += sizeof(float) * 2 * (size_t)ptab2_width(P);   // the dK/dV kernel's padded table
+    if (hist)   // the dQ kernel: reversed table, histograms, diagonal scratch
+        b += sizeof(float) * (2 * (size_t)rtab_width(P) + 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch));
+    else        // the dK/dV kernel: the table and its padded copies
+        b += sizeof(float) * ((size_t)((P + 3) & ~3) + 2 * (size_t)ptab2_width(P));
     return b;
 }
 
