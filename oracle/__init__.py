@@ -47,6 +47,7 @@ def _lib():
         lib.hstu_oracle_silu.argtypes = [ctypes.c_double]
         lib.hstu_oracle_max_threads.restype = ctypes.c_int32
         lib.hstu_oracle_attn.restype = None
+        lib.hstu_oracle_attn_rows.restype = None
         lib.hstu_oracle_ln_gate.restype = None
         lib.hstu_oracle_attn_bwd.restype = None
         lib.hstu_oracle_ln_gate_bwd.restype = None
@@ -128,6 +129,34 @@ def attn(q, k, v, offsets, ts, rab_pos, rab_time, alpha, *, lengths=None,
         ctypes.c_int64(rps), ctypes.c_int64(rts), ctypes.c_double(alpha), ctypes.c_int32(act),
         _ptr(o, _f64p), ctypes.c_int64(H * dv), ctypes.c_int32(num_threads))
     return o
+
+
+def attn_rows(q, k, v, offsets, ts, rab_pos, rab_time, alpha, rows, *, lengths=None,
+              num_candidates=None, act=ACT_SILU, num_threads=0) -> np.ndarray:
+    """O[rows[r], H, d_v] of selected rows of the jagged batch (the definition
+    of ``attn``, evaluated row by row: O(L d) per row)."""
+    q = _f64(q); k = _f64(k); v = _f64(v)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    off = _i32(offsets)
+    B = len(off) - 1
+    rp = _f64(rab_pos); rt = _f64(rab_time)
+    P = rp.shape[-1]; NT = rt.shape[-1]
+    rps = P if rp.ndim == 2 else 0
+    rts = NT if rt.ndim == 2 else 0
+    rw = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((len(rw), H, dv), dtype=np.float64)
+    tsa = np.ascontiguousarray(ts, dtype=np.int64)
+    ln = _i32(lengths); nc = _i32(num_candidates)
+    _lib().hstu_oracle_attn_rows(
+        ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(dqk), ctypes.c_int32(dv),
+        _ptr(off, _i32p), _ptr(ln, _i32p), _ptr(nc, _i32p),
+        _ptr(q, _f64p), ctypes.c_int64(H * dqk), _ptr(k, _f64p), ctypes.c_int64(H * dqk),
+        _ptr(v, _f64p), ctypes.c_int64(H * dv), _ptr(tsa, _i64p),
+        _ptr(rp, _f64p), ctypes.c_int32(P), _ptr(rt, _f64p), ctypes.c_int32(NT),
+        ctypes.c_int64(rps), ctypes.c_int64(rts), ctypes.c_double(alpha), ctypes.c_int32(act),
+        ctypes.c_int64(len(rw)), _ptr(rw, _i64p), _ptr(out, _f64p), ctypes.c_int32(num_threads))
+    return out
 
 
 def ln_gate(o, u, eps=1e-5, num_threads=0) -> np.ndarray:

@@ -132,6 +132,33 @@ int32_t hstu_oracle_max_threads(void) {
 /* Sums run over j ascending.  Row r of sequence b is offsets[b] + r.        */
 /* Tables are per head when rab_head_stride > 0, shared when it is 0.        */
 /* ------------------------------------------------------------------------ */
+/* One output row of one head: acc = sum over visible j (ascending) of
+ * act(S_ij) V[j], then O[i] = alpha * acc. */
+static void attn_row(int32_t i, int32_t h, int32_t L, int32_t n_hist, int64_t base, int32_t d_qk,
+                     int32_t d_v, const double* q, int64_t q_stride, const double* k, int64_t k_stride,
+                     const double* v, int64_t v_stride, const int64_t* timestamps,
+                     const double* rab_pos, int32_t num_pos_buckets, const double* rab_time,
+                     int32_t num_time_buckets, int64_t rab_pos_head_stride,
+                     int64_t rab_time_head_stride, double alpha, int32_t act, double* acc,
+                     double* oi) {
+    const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
+    const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
+    const double* qi = q + (base + i) * q_stride + (int64_t)h * d_qk;
+    for (int32_t c = 0; c < d_v; ++c) acc[c] = 0.0;
+    for (int32_t j = 0; j < L; ++j) {
+        if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
+        const double* kj = k + (base + j) * k_stride + (int64_t)h * d_qk;
+        double s = 0.0;
+        for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
+        s += rp[hstu_oracle_pos_bucket(i, j, n_hist, num_pos_buckets)];
+        s += rt[hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j], num_time_buckets)];
+        double a = (act == ORACLE_ACT_IDENTITY) ? s : hstu_oracle_silu(s);
+        const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
+        for (int32_t c = 0; c < d_v; ++c) acc[c] += a * vj[c];
+    }
+    for (int32_t c = 0; c < d_v; ++c) oi[c] = alpha * acc[c];
+}
+
 void hstu_oracle_attn(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                       const int32_t* offsets, const int32_t* lengths,
                       const int32_t* num_candidates,
@@ -156,28 +183,52 @@ void hstu_oracle_attn(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
 #pragma omp for collapse(2) schedule(dynamic, 4)
             for (int32_t h = 0; h < H; ++h) {
                 for (int32_t i = 0; i < L; ++i) {
-                    const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
-                    const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
-                    const double* qi = q + (base + i) * q_stride + (int64_t)h * d_qk;
-                    for (int32_t c = 0; c < d_v; ++c) acc[c] = 0.0;
-                    for (int32_t j = 0; j < L; ++j) {
-                        if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
-                        const double* kj = k + (base + j) * k_stride + (int64_t)h * d_qk;
-                        double s = 0.0;
-                        for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
-                        s += rp[hstu_oracle_pos_bucket(i, j, n_hist, num_pos_buckets)];
-                        s += rt[hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j],
-                                                        num_time_buckets)];
-                        double a = (act == ORACLE_ACT_IDENTITY) ? s : hstu_oracle_silu(s);
-                        const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
-                        for (int32_t c = 0; c < d_v; ++c) acc[c] += a * vj[c];
-                    }
-                    double* oi = o + (base + i) * o_stride + (int64_t)h * d_v;
-                    for (int32_t c = 0; c < d_v; ++c) oi[c] = alpha * acc[c];
+                    attn_row(i, h, L, n_hist, base, d_qk, d_v, q, q_stride, k, k_stride, v, v_stride,
+                             timestamps, rab_pos, num_pos_buckets, rab_time, num_time_buckets,
+                             rab_pos_head_stride, rab_time_head_stride, alpha, act, acc,
+                             o + (base + i) * o_stride + (int64_t)h * d_v);
                 }
             }
             free(acc);
         }
+    }
+}
+
+/* The same outputs for selected rows only: rows[r] is a row of the jagged
+ * batch (offsets[b] <= rows[r] < offsets[b] + L_b); out[r, h, :] receives
+ * its O for every head.  For checks of batches too large for the full
+ * oracle: each row costs O(L d), not O(L^2 d). */
+void hstu_oracle_attn_rows(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                           const int32_t* offsets, const int32_t* lengths,
+                           const int32_t* num_candidates,
+                           const double* q, int64_t q_stride,
+                           const double* k, int64_t k_stride,
+                           const double* v, int64_t v_stride,
+                           const int64_t* timestamps,
+                           const double* rab_pos, int32_t num_pos_buckets,
+                           const double* rab_time, int32_t num_time_buckets,
+                           int64_t rab_pos_head_stride, int64_t rab_time_head_stride,
+                           double alpha, int32_t act, int64_t nrows, const int64_t* rows,
+                           double* out, int32_t num_threads) {
+    set_threads(num_threads);
+#pragma omp parallel
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)(d_v > 0 ? d_v : 1));
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            for (int32_t h = 0; h < H; ++h) {
+                int32_t b = 0;
+                while (b + 1 < B && offsets[b + 1] <= rows[r]) ++b;
+                const int32_t L = seq_len(offsets, lengths, b);
+                const int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+                const int32_t i = (int32_t)(rows[r] - offsets[b]);
+                attn_row(i, h, L, n_hist, offsets[b], d_qk, d_v, q, q_stride, k, k_stride, v, v_stride,
+                         timestamps, rab_pos, num_pos_buckets, rab_time, num_time_buckets,
+                         rab_pos_head_stride, rab_time_head_stride, alpha, act, acc,
+                         out + (r * H + h) * d_v);
+            }
+        }
+        free(acc);
     }
 }
 

@@ -400,3 +400,25 @@ def test_tiles_cover_every_visible_pair_and_nothing_else():
                 if (i < n and j <= i) or (i >= n and (j < n or j == i)):
                     want.add((b, i // BM, j // BN))
     assert got == want
+
+
+def test_attn_rows_equals_full_oracle_at_those_rows():
+    """The row-by-row entry (for batches too large for the full oracle) gives
+    exactly the full oracle's values at the selected rows: padded rows,
+    candidates, per-head tables, rows from every sequence, repeated rows."""
+    x = synth.make_attn(81, [37, 1, 90, 64], H=2, d=16, P=40, NT=12, alpha=0.125, dtype="f32",
+                        num_candidates=[5, 0, 30, 64])
+    rng = np.random.default_rng(82)
+    rp = rng.normal(0, 0.1, size=(2, 40))
+    rt = rng.normal(0, 0.1, size=(2, 12))
+    full = oracle.attn(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha,
+                       num_candidates=x.num_candidates)
+    rows = np.array([0, 36, 37, 38, 50, 127, 128, 191, 60, 0])
+    got = oracle.attn_rows(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha, rows,
+                           num_candidates=x.num_candidates)
+    assert np.array_equal(got, full[rows])
+    got_id = oracle.attn_rows(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha, rows,
+                              num_candidates=x.num_candidates, act=oracle.ACT_IDENTITY)
+    full_id = oracle.attn(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha,
+                          num_candidates=x.num_candidates, act=oracle.ACT_IDENTITY)
+    assert np.array_equal(got_id, full_id[rows])
