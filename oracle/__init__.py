@@ -50,6 +50,7 @@ def _lib():
         lib.hstu_oracle_attn_rows.restype = None
         lib.hstu_oracle_ln_gate.restype = None
         lib.hstu_oracle_attn_bwd.restype = None
+        lib.hstu_oracle_attn_bwd_rows.restype = None
         lib.hstu_oracle_ln_gate_bwd.restype = None
         lib.hstu_oracle_layer_bwd.restype = None
         lib.hstu_oracle_layer.restype = None
@@ -206,6 +207,39 @@ def attn_bwd(q, k, v, offsets, ts, rab_pos, rab_time, alpha, dout, *, lengths=No
         _ptr(g, _f64p), _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p),
         _ptr(drp, _f64p), _ptr(drt, _f64p), ctypes.c_int32(num_threads))
     return dq, dk, dv, drp, drt
+
+
+def attn_bwd_rows(q, k, v, offsets, ts, rab_pos, rab_time, alpha, dout, qrows, krows, *,
+                  lengths=None, num_candidates=None, act=ACT_SILU, num_threads=0):
+    """dQ at the query rows ``qrows`` and dK, dV at the key rows ``krows`` of
+    the jagged batch: the sums of ``attn_bwd``, in its order, per row
+    (O(L d) each; no table gradients).  Returns (dq [nq, H, d_qk],
+    dk [nk, H, d_qk], dv [nk, H, d_v])."""
+    q = _f64(q); k = _f64(k); v = _f64(v); g = _f64(dout)
+    T, H, dqk = q.shape
+    dv_ = v.shape[2]
+    off = _i32(offsets)
+    B = len(off) - 1
+    rp = _f64(rab_pos); rt = _f64(rab_time)
+    P = rp.shape[-1]; NT = rt.shape[-1]
+    rps = P if rp.ndim == 2 else 0
+    rts = NT if rt.ndim == 2 else 0
+    qr = np.ascontiguousarray(qrows, dtype=np.int64)
+    kr = np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.zeros((len(qr), H, dqk)); dk = np.zeros((len(kr), H, dqk)); dvo = np.zeros((len(kr), H, dv_))
+    tsa = np.ascontiguousarray(ts, dtype=np.int64)
+    ln = _i32(lengths); nc = _i32(num_candidates)
+    _lib().hstu_oracle_attn_bwd_rows(
+        ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(dqk), ctypes.c_int32(dv_),
+        _ptr(off, _i32p), _ptr(ln, _i32p), _ptr(nc, _i32p),
+        _ptr(q, _f64p), _ptr(k, _f64p), _ptr(v, _f64p), ctypes.c_int64(H * dqk),
+        ctypes.c_int64(H * dv_), _ptr(tsa, _i64p),
+        _ptr(rp, _f64p), ctypes.c_int32(P), _ptr(rt, _f64p), ctypes.c_int32(NT),
+        ctypes.c_int64(rps), ctypes.c_int64(rts), ctypes.c_double(alpha), ctypes.c_int32(act),
+        _ptr(g, _f64p), ctypes.c_int64(len(qr)), _ptr(qr, _i64p), _ptr(dq, _f64p),
+        ctypes.c_int64(len(kr)), _ptr(kr, _i64p), _ptr(dk, _f64p), _ptr(dvo, _f64p),
+        ctypes.c_int32(num_threads))
+    return dq, dk, dvo
 
 
 def ln_gate_bwd(o, u, dy, eps=1e-5, num_threads=0):

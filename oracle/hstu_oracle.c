@@ -283,6 +283,37 @@ static double act_slope(double s, int32_t act) {
     return sg * (1.0 + s * (1.0 - sg));
 }
 
+/* The chain rule at one visible pair (i, j) of head h: S_ij, A_ij =
+ * act(S_ij), dov = <dO_i, V_j> and G_ij = alpha dov act'(S_ij). */
+typedef struct {
+    double a, g;
+    int32_t pb, tb;
+} bwd_pair_t;
+
+static bwd_pair_t bwd_pair(int32_t i, int32_t j, int32_t h, int32_t n_hist, int64_t base, int32_t d_qk,
+                           int32_t d_v, const double* q, const double* k, const double* v,
+                           int64_t qk_stride, int64_t v_stride, const int64_t* timestamps,
+                           const double* rab_pos, int32_t P, const double* rab_time, int32_t NT,
+                           int64_t rab_pos_head_stride, int64_t rab_time_head_stride, double alpha,
+                           int32_t act, const double* dout) {
+    const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
+    const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
+    const double* qi = q + (base + i) * qk_stride + (int64_t)h * d_qk;
+    const double* gi = dout + (base + i) * v_stride + (int64_t)h * d_v;
+    const double* kj = k + (base + j) * qk_stride + (int64_t)h * d_qk;
+    const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
+    bwd_pair_t r;
+    r.pb = hstu_oracle_pos_bucket(i, j, n_hist, P);
+    r.tb = hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j], NT);
+    double s = rp[r.pb] + rt[r.tb];
+    for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
+    r.a = act_value(s, act);
+    double dov = 0.0;
+    for (int32_t c = 0; c < d_v; ++c) dov += gi[c] * vj[c];
+    r.g = alpha * dov * act_slope(s, act);
+    return r;
+}
+
 void hstu_oracle_attn_bwd(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                           const int32_t* offsets, const int32_t* lengths,
                           const int32_t* num_candidates,
@@ -314,35 +345,26 @@ void hstu_oracle_attn_bwd(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
         /* heads are independent: each writes its own columns and table row */
 #pragma omp parallel for schedule(dynamic, 1)
         for (int32_t h = 0; h < H; ++h) {
-            const double* rp = rab_pos + (int64_t)h * rab_pos_head_stride;
-            const double* rt = rab_time + (int64_t)h * rab_time_head_stride;
             for (int32_t i = 0; i < L; ++i) {
                 const double* qi = q + (base + i) * qk_stride + (int64_t)h * d_qk;
                 const double* gi = dout + (base + i) * v_stride + (int64_t)h * d_v;
                 double* dqi = dq + (base + i) * qk_stride + (int64_t)h * d_qk;
                 for (int32_t j = 0; j < L; ++j) {
                     if (!hstu_oracle_visible(i, j, L, n_hist)) continue;
+                    const bwd_pair_t pr = bwd_pair(i, j, h, n_hist, base, d_qk, d_v, q, k, v, qk_stride,
+                                                   v_stride, timestamps, rab_pos, P, rab_time, NT,
+                                                   rab_pos_head_stride, rab_time_head_stride, alpha, act,
+                                                   dout);
                     const double* kj = k + (base + j) * qk_stride + (int64_t)h * d_qk;
-                    const double* vj = v + (base + j) * v_stride + (int64_t)h * d_v;
-                    int32_t pb = hstu_oracle_pos_bucket(i, j, n_hist, P);
-                    int32_t tb = hstu_oracle_time_bucket(timestamps[base + i], timestamps[base + j], NT);
-                    double s = rp[pb] + rt[tb];
-                    for (int32_t c = 0; c < d_qk; ++c) s += qi[c] * kj[c];
-                    double a = act_value(s, act);
                     double* dvj = dv + (base + j) * v_stride + (int64_t)h * d_v;
-                    double dov = 0.0;
-                    for (int32_t c = 0; c < d_v; ++c) {
-                        dvj[c] += alpha * a * gi[c];
-                        dov += gi[c] * vj[c];
-                    }
-                    double g = alpha * dov * act_slope(s, act);
+                    for (int32_t c = 0; c < d_v; ++c) dvj[c] += alpha * pr.a * gi[c];
                     double* dkj = dk + (base + j) * qk_stride + (int64_t)h * d_qk;
                     for (int32_t c = 0; c < d_qk; ++c) {
-                        dqi[c] += g * kj[c];
-                        dkj[c] += g * qi[c];
+                        dqi[c] += pr.g * kj[c];
+                        dkj[c] += pr.g * qi[c];
                     }
-                    gp[(int64_t)h * P + pb] += g;
-                    gt[(int64_t)h * NT + tb] += g;
+                    gp[(int64_t)h * P + pr.pb] += pr.g;
+                    gt[(int64_t)h * NT + pr.tb] += pr.g;
                 }
             }
         }
@@ -367,6 +389,68 @@ void hstu_oracle_attn_bwd(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
     }
     free(gp);
     free(gt);
+}
+
+/* The same dQ, dK and dV for selected rows only (no table gradients): the
+ * query rows qrows[r] get dQ (sum over their visible keys, ascending), the
+ * key rows krows[r] get dK and dV (sum over the rows that see them,
+ * ascending) -- the full oracle's sums, in its order.  O(L d) per row. */
+void hstu_oracle_attn_bwd_rows(int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                               const int32_t* offsets, const int32_t* lengths,
+                               const int32_t* num_candidates,
+                               const double* q, const double* k, const double* v,
+                               int64_t qk_stride, int64_t v_stride,
+                               const int64_t* timestamps,
+                               const double* rab_pos, int32_t num_pos_buckets,
+                               const double* rab_time, int32_t num_time_buckets,
+                               int64_t rab_pos_head_stride, int64_t rab_time_head_stride,
+                               double alpha, int32_t act, const double* dout,
+                               int64_t nq, const int64_t* qrows, double* dq_out,
+                               int64_t nk, const int64_t* krows, double* dk_out, double* dv_out,
+                               int32_t num_threads) {
+    set_threads(num_threads);
+    const int32_t P = num_pos_buckets, NT = num_time_buckets;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int64_t r = 0; r < nq + nk; ++r) {
+        for (int32_t h = 0; h < H; ++h) {
+            const int64_t row = r < nq ? qrows[r] : krows[r - nq];
+            int32_t b = 0;
+            while (b + 1 < B && offsets[b + 1] <= row) ++b;
+            const int32_t L = seq_len(offsets, lengths, b);
+            const int32_t n_hist = seq_hist(offsets, lengths, num_candidates, b);
+            const int64_t base = offsets[b];
+            const int32_t x = (int32_t)(row - base);
+            if (r < nq) {
+                double* acc = dq_out + (r * H + h) * d_qk;
+                for (int32_t c = 0; c < d_qk; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j < L; ++j) {
+                    if (!hstu_oracle_visible(x, j, L, n_hist)) continue;
+                    const bwd_pair_t pr = bwd_pair(x, j, h, n_hist, base, d_qk, d_v, q, k, v, qk_stride,
+                                                   v_stride, timestamps, rab_pos, P, rab_time, NT,
+                                                   rab_pos_head_stride, rab_time_head_stride, alpha, act,
+                                                   dout);
+                    const double* kj = k + (base + j) * qk_stride + (int64_t)h * d_qk;
+                    for (int32_t c = 0; c < d_qk; ++c) acc[c] += pr.g * kj[c];
+                }
+            } else {
+                double* dka = dk_out + ((r - nq) * H + h) * d_qk;
+                double* dva = dv_out + ((r - nq) * H + h) * d_v;
+                for (int32_t c = 0; c < d_qk; ++c) dka[c] = 0.0;
+                for (int32_t c = 0; c < d_v; ++c) dva[c] = 0.0;
+                for (int32_t i = 0; i < L; ++i) {
+                    if (!hstu_oracle_visible(i, x, L, n_hist)) continue;
+                    const bwd_pair_t pr = bwd_pair(i, x, h, n_hist, base, d_qk, d_v, q, k, v, qk_stride,
+                                                   v_stride, timestamps, rab_pos, P, rab_time, NT,
+                                                   rab_pos_head_stride, rab_time_head_stride, alpha, act,
+                                                   dout);
+                    const double* qi = q + (base + i) * qk_stride + (int64_t)h * d_qk;
+                    const double* gi = dout + (base + i) * v_stride + (int64_t)h * d_v;
+                    for (int32_t c = 0; c < d_v; ++c) dva[c] += alpha * pr.a * gi[c];
+                    for (int32_t c = 0; c < d_qk; ++c) dka[c] += pr.g * qi[c];
+                }
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -10,6 +10,7 @@ least one of them.
 import numpy as np
 import pytest
 
+import hstu_synth as synth
 import oracle
 
 STEP = 1e-6
@@ -208,3 +209,25 @@ def test_layer_bwd_residual_and_bias_identities():
                            c["H"], c["d"], g1, b2=b21, eps=c["eps"])
     np.testing.assert_allclose(ext["dw1"][:, -1], got["db1"], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(ext["dw1"][:, :-1], got["dw1"], rtol=1e-10, atol=1e-12)
+
+
+def test_attn_bwd_rows_equals_full_oracle_at_those_rows():
+    """The row-by-row gradient entry gives exactly the full oracle's dQ at the
+    selected query rows and dK, dV at the selected key rows: candidates, a
+    sequence of candidates only, per-head tables, identity activation."""
+    x = synth.make_attn(83, [37, 1, 90, 64], H=2, d=16, P=40, NT=12, alpha=0.125, dtype="f32",
+                        num_candidates=[5, 0, 30, 64])
+    rng = np.random.default_rng(84)
+    rp = rng.normal(0, 0.1, size=(2, 40))
+    rt = rng.normal(0, 0.1, size=(2, 12))
+    dout = rng.normal(0, 1.0, size=x.v.shape)
+    qrows = np.array([0, 36, 37, 38, 50, 127, 128, 191])
+    krows = np.array([1, 37, 40, 100, 127, 130, 191, 0])
+    for act in (oracle.ACT_SILU, oracle.ACT_IDENTITY):
+        dq, dk, dv, _, _ = oracle.attn_bwd(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha, dout,
+                                           num_candidates=x.num_candidates, act=act)
+        rq, rk, rv = oracle.attn_bwd_rows(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha, dout,
+                                          qrows, krows, num_candidates=x.num_candidates, act=act)
+        assert np.array_equal(rq, dq[qrows])
+        assert np.array_equal(rk, dk[krows])
+        assert np.array_equal(rv, dv[krows])
