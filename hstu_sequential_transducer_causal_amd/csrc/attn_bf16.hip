@@ -114,7 +114,7 @@ struct TileDma {
     u32x4 krs, vrs, wrs;
     uint32_t koff[2], voff[2];
     uint32_t ktile, vtile;        // bytes per key tile in K and V
-    int64_t enc_row0;             // byte offset of the sequence's first code in the workspace
+    uint32_t code_off;            // lane < 32: byte offset of the sequence's code `lane`; else out of range
 };
 
 // The three parts of a tile's loads go out at different points of the
@@ -131,18 +131,21 @@ __device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, in
 #pragma unroll
     for (int m = 0; m < 2; ++m) dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
 }
-// Wave 0 only: the tile's 32 key codes (lanes 32-63 write zeros).
-__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt, int L, int lane) {
-    const int j = kt * BN + lane;
-    uint32_t off = 0x80000000u;   // out of range: lands as 0
-    if (lane < 32 && j < L) off = (uint32_t)(d.enc_row0 + 4 * (int64_t)j);
-    dma4(d.wrs, uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4)), off);
+// Wave 0 only: the tile's 32 key codes (lanes 32-63 write zeros; codes of
+// keys past the sequence end are other rows' or zeros, and those keys are
+// masked).  The lane's offset is fixed per item, the tile is the scalar offset.
+__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt) {
+    const uint32_t lds = uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4));
+    const uint32_t soff = uniu((uint32_t)kt * (uint32_t)(BN * 4));
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(d.code_off), "s"(d.wrs), "s"(soff),
+                 "{m0}"(lds)
+                 : "memory");
 }
 __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, int L, int wave,
                                            int lane) {
     issue_k(d, s, stage, kt, wave);
     issue_v(d, s, stage, kt, wave);
-    if (wave == 0) issue_codes(d, s, stage, kt, L, lane);
+    if (wave == 0) issue_codes(d, s, stage, kt);
 }
 
 // kCross: the queries are candidates in their own buffers, each seeing every
@@ -240,7 +243,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             }
             dma.ktile = (uint32_t)(BN * p.ks * 2);
             dma.vtile = (uint32_t)(BN * p.vs * 2);
-            dma.enc_row0 = enc_base + 4 * row0;
+            dma.code_off = lane < 32 ? (uint32_t)(enc_base + 4 * (row0 + lane)) : 0x80000000u;
         }
         const int ntiles = p1 - p0;
         auto tile_of = [&](int it) {
@@ -310,6 +313,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         if (!kCross || ntiles > 0) krange_next = kstats[bbase + tile_of(0)];
         u32x4 vf[2][4];
         const uint32_t koff_lane = k_lane_offset(lane), voff_lane = v_lane_offset(lane);
+        const uint32_t ptab_lds = lds_addr(ptab);
+        const int prow4 = prow - 4 * h2;   // the position term's row part for this lane's keys
 
         // the barrier of tile it (its loads have landed, every wave is done
         // with tile it-1's stage: V(it-1) was read before it), then the K
@@ -356,18 +361,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
                 cadd = pos_far;
             } else {
-                int x = prow - (j0 + 4 * h2);
-                x = min(max(x, 0), P + 26);
+                // entries u0 + 8q + t, u0 = Dhi - x, from copy c = u0 & 1 at
+                // float index c * (CS + 1) + u0: one base, immediate offsets
+                const int x = min(max(prow4 - j0, 0), P + 26);
                 const int u0 = Dhi - x;
-                const int c = u0 & 1;
-                const float* pp = ptab + c * CS + (u0 + c);
+                const uint32_t pa = ptab_lds + 4u * (uint32_t)u0 + (uint32_t)(u0 & 1) * (4u * (uint32_t)CS + 4u);
+                typedef float f32x2v __attribute__((ext_vector_type(2)));
+                typedef __attribute__((address_space(3))) const f32x2v lds_f2;
+                const lds_f2* pp = (const lds_f2*)(uintptr_t)pa;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
 #pragma unroll
                     for (int t2 = 0; t2 < 2; ++t2) {
-                        const float2 pv = *reinterpret_cast<const float2*>(pp + 8 * q + 2 * t2);
-                        acc[4 * q + 2 * t2] = pv.x;
-                        acc[4 * q + 2 * t2 + 1] = pv.y;
+                        const f32x2v pv = pp[4 * q + t2];
+                        acc[4 * q + 2 * t2] = pv[0];
+                        acc[4 * q + 2 * t2 + 1] = pv[1];
                     }
                 }
             }
@@ -396,7 +404,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     } else {
                         // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
                         const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
-                        const uint32_t thr = 1u << (32 - czlo);
+                        uint32_t thr = 1u << (32 - czlo);
+                        asm volatile("" : "+s"(thr));   // opaque: one compare per element, not a shift and a compare
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -475,7 +484,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             if (it + kStages - 1 < ntiles) {
                 const int st3 = (it + kStages - 1) & (kStages - 1), kt3 = tile_of(it + kStages - 1);
                 issue_v(dma, s, st3, kt3, wave);
-                if (wave == 0) issue_codes(dma, s, st3, kt3, L, lane);
+                if (wave == 0) issue_codes(dma, s, st3, kt3);
             }
         };
 
