@@ -324,6 +324,39 @@ class CachedCase:
         return rec
 
 
+class LastLayerCase:
+    """The last layer of an M-FALCON stack, scores only (mfalcon_layer_score):
+    8 users x (2048 history + 512 candidates), D = 512, 4 heads of 128."""
+
+    def __init__(self, dev, candidates_only=True, B=8, n=2048, c=512, seed=43):
+        import torch
+        import hstu_synth as synth
+        x = synth.make_layer_stack(seed, [n + c] * B, H=4, d=128, D=512, layers=1, P=1024, NT=32,
+                                   alpha=1.0 / (n + c))
+        self.name = f"mfalcon_last_layer_bf16_b{B}_n{n}_bm{c}_D512_h4_d128"
+        self.B, self.n, self.c, self.H, self.d = B, n, c, x.H, x.d
+        self.T = x.T
+        self.x = up(x.x, "bf16", dev)
+        self.w1 = up(x.w1[0], "bf16", dev)
+        self.off = torch.from_numpy(x.offsets).to(dev)
+        self.nc = torch.full((B,), c, dtype=torch.int32, device=dev)
+        self.ts = torch.from_numpy(x.ts).to(dev)
+        self.rp = torch.from_numpy(x.rab_pos[0]).to(dev)
+        self.rt = torch.from_numpy(x.rab_time[0]).to(dev)
+        self.w = torch.from_numpy(np.random.default_rng(seed + 1).normal(
+            0, 1 / np.sqrt(512), size=512).astype(np.float32)).to(dev)
+        self.alpha, self.eps = x.alpha, x.eps
+        self.scores = torch.zeros(B, c, dtype=torch.float32, device=dev)
+        self.candidates_only = candidates_only
+
+    def step(self, ev0=None, ev1=None):
+        from hstu_sequential_transducer_causal_amd import ops
+        ops.mfalcon_layer_score(self.x, self.w1, self.off, self.nc, self.ts, self.rp, self.rt,
+                                self.alpha, self.w, H=self.H, d=self.d, max_seq_len=self.n + self.c,
+                                score_stride=self.c, ln_eps=self.eps,
+                                candidates_only=self.candidates_only, scores=self.scores)
+
+
 def sl_record(dev, steps):
     """Stochastic length with the gather of the rows of Q, K, V, U (8 heads of
     128, bf16) and timestamps, on the long-sequence workload's raw batch."""
@@ -608,6 +641,19 @@ def main():
                 log(f"{xo.name} candidates only: {rec}")
                 del c
                 torch.cuda.empty_cache()
+                # the last layer of an M-FALCON stack, scores only
+                recs = {}
+                for co in (True, False):
+                    c = LastLayerCase(dev, candidates_only=co)
+                    st, _ = time_case(c, max(3, args.steps // 3), 2, core_events=False)
+                    recs[co] = st
+                    name = c.name
+                    del c
+                    torch.cuda.empty_cache()
+                others[name] = {"ms_per_step": round(recs[True], 4),
+                                "candidates_per_s": round(8 * 512 / (recs[True] * 1e-3), 1),
+                                "all_rows_attention_ms": round(recs[False], 4)}
+                log(f"{name}: {others[name]}")
                 # many candidates per user against a cached history
                 c = CachedCase(dev)
                 rec = c.record(max(3, args.steps // 3))

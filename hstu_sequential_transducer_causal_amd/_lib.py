@@ -121,6 +121,17 @@ class LayerArgs(ctypes.Structure):
     ]
 
 
+class MfalconLayerArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("layer", LayerArgs),
+        ("w", _vp),
+        ("scores", _vp),
+        ("score_stride", _i32),
+        ("candidates_only", _i32),
+    ]
+
+
 class LayerBwdArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32),
@@ -162,6 +173,7 @@ EXPORTS = [
     "hstu_mfalcon_workspace_bytes", "mfalcon_score",
     "hstu_mfalcon_cached_workspace_bytes", "mfalcon_score_cached",
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
+    "hstu_mfalcon_layer_workspace_bytes", "mfalcon_layer_score",
     "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
     "hstu_layer_bwd_workspace_bytes", "hstu_layer_bwd",
     "hstu_stochastic_length",
@@ -207,6 +219,10 @@ def load(path: str = LIB_PATH):
     lib.hstu_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
     lib.hstu_layer_fwd.restype = _i32
     lib.hstu_layer_fwd.argtypes = [ctypes.POINTER(LayerArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_mfalcon_layer_workspace_bytes.restype = ctypes.c_size_t
+    lib.hstu_mfalcon_layer_workspace_bytes.argtypes = [ctypes.POINTER(MfalconLayerArgs)]
+    lib.mfalcon_layer_score.restype = _i32
+    lib.mfalcon_layer_score.argtypes = [ctypes.POINTER(MfalconLayerArgs), _vp, ctypes.c_size_t, _vp]
     lib.hstu_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.hstu_attn_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnBwdArgs)]
     lib.hstu_attn_bwd.restype = _i32

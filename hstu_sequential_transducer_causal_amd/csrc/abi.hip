@@ -484,7 +484,7 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
 
 namespace {
 
-hstu_status validate_layer(const hstu_layer_args* l) {
+hstu_status validate_layer(const hstu_layer_args* l, bool f2 = true) {
     if (!l) return fail(HSTU_ERR_ARG, "args is NULL");
     if (l->struct_size != sizeof(hstu_layer_args))
         return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_layer_args) %zu", l->struct_size,
@@ -504,10 +504,10 @@ hstu_status validate_layer(const hstu_layer_args* l) {
     if (!std::isfinite(l->alpha)) return fail(HSTU_ERR_ARG, "alpha is not finite");
     if (!(l->ln_eps > 0.0f) || !std::isfinite(l->ln_eps)) return fail(HSTU_ERR_ARG, "ln_eps must be > 0");
     if (l->B > 0) {
-        if (!l->seq_offsets || !l->x || !l->w1 || !l->w2 || !l->x_out || !l->timestamps || !l->rab_pos ||
-            !l->rab_time)
+        if (!l->seq_offsets || !l->x || !l->w1 || (f2 && (!l->w2 || !l->x_out)) || !l->timestamps ||
+            !l->rab_pos || !l->rab_time)
             return fail(HSTU_ERR_ARG, "a required pointer is NULL");
-        if (!aligned16(l->x) || !aligned16(l->w1) || !aligned16(l->w2) || !aligned16(l->x_out))
+        if (!aligned16(l->x) || !aligned16(l->w1) || (f2 && (!aligned16(l->w2) || !aligned16(l->x_out))))
             return fail(HSTU_ERR_UNSUPPORTED, "layer buffers must be 16-byte aligned");
     }
     return HSTU_OK;
@@ -544,6 +544,37 @@ hstu_attn_args layer_attn_args(const hstu_layer_args* l, uint16_t* z, uint16_t* 
 struct LayerWs {
     size_t z, o, y, sched, total;
 };
+
+hstu_status validate_mfalcon_layer(const hstu_mfalcon_layer_args* m) {
+    if (!m) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (m->struct_size != sizeof(hstu_mfalcon_layer_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_mfalcon_layer_args) %zu", m->struct_size,
+                    sizeof(hstu_mfalcon_layer_args));
+    hstu_status st = validate_layer(&m->layer, false);
+    if (st != HSTU_OK) return st;
+    if (m->score_stride < 1) return fail(HSTU_ERR_ARG, "score_stride < 1");
+    if (m->layer.B > 0) {
+        if (!m->layer.num_candidates) return fail(HSTU_ERR_ARG, "layer.num_candidates is required");
+        if (!m->w || !m->scores) return fail(HSTU_ERR_ARG, "w and scores must be non-NULL");
+    }
+    return HSTU_OK;
+}
+
+// Z, then O (no Y: the scores are taken in the epilogue), then the schedule.
+struct MfalconLayerWs {
+    size_t z, o, sched, total;
+};
+
+MfalconLayerWs mfalcon_layer_ws(const hstu_layer_args* l) {
+    MfalconLayerWs w;
+    const size_t T = size_t(l->num_rows);
+    const size_t hd = size_t(l->H) * l->d;
+    w.z = 0;
+    w.o = align256(w.z + T * 4 * hd * 2);
+    w.sched = align256(w.o + T * hd * 2);
+    w.total = hstu::sched_layout(l->B, l->H, l->max_seq_len, hstu::kBf16TileM, l->d, l->num_rows, w.sched).bytes;
+    return w;
+}
 
 LayerWs layer_ws(const hstu_layer_args* l) {
     LayerWs w;
@@ -698,6 +729,53 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     g2.silu = 0;
     e = hstu::launch_gemm_bf16(g2, stream);
     if (e != hipSuccess) return device_error(e, "f2 launch");
+    return ok();
+}
+
+size_t hstu_mfalcon_layer_workspace_bytes(const hstu_mfalcon_layer_args* m) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_mfalcon_layer(m);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return mfalcon_layer_ws(&m->layer).total;
+}
+
+hstu_status mfalcon_layer_score(const hstu_mfalcon_layer_args* m, void* ws, size_t ws_bytes, void* stream_) {
+    hstu_status st = validate_mfalcon_layer(m);
+    if (st != HSTU_OK) return st;
+    const hstu_layer_args* l = &m->layer;
+    if (l->B == 0 || l->num_rows == 0) return ok();
+    const MfalconLayerWs lw = mfalcon_layer_ws(l);
+    st = check_workspace(ws, ws_bytes, lw.total);
+    if (st != HSTU_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const int hd = l->H * l->d;
+    uint16_t* z = reinterpret_cast<uint16_t*>(w + lw.z);
+    uint16_t* o = reinterpret_cast<uint16_t*>(w + lw.o);
+
+    // f1 + SiLU over every row: the candidates read the history's K and V
+    hstu::GemmArgs g1;
+    g1.M = l->num_rows; g1.N = 4 * hd; g1.K = l->D;
+    g1.a = l->x; g1.lda = l->D;
+    g1.b = l->w1; g1.ldb = l->D;
+    g1.bias = l->b1;
+    g1.residual = nullptr; g1.ldr = 0;
+    g1.c = z; g1.ldc = 4 * hd;
+    g1.silu = 1;
+    hipError_t e = hstu::launch_gemm_bf16(g1, stream);
+    if (e != hipSuccess) return device_error(e, "f1 launch");
+
+    hstu_attn_args a = layer_attn_args(l, z, o, nullptr);
+    const bool cand_only = m->candidates_only != 0;
+    Sched s = carve_sched(&a, ws, lw.sched);
+    e = run_sched(&a, s, stream, cand_only);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    e = run_core(&a, s, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+    e = run_ln_gate(&a, s, m->w, m->scores, m->score_stride, cand_only, stream);
+    if (e != hipSuccess) return device_error(e, "epilogue launch");
     return ok();
 }
 

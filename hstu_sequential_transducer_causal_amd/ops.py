@@ -3,7 +3,7 @@
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
 Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score, mfalcon_score_cached,
-hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule.
+mfalcon_layer_score, hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule.
 """
 from __future__ import annotations
 
@@ -302,6 +302,8 @@ def mfalcon_score_cached(k_hist, v_hist, hist_offsets, ts_hist, q, k, v, u, cand
 def make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,
                     d: int, max_seq_len: int, x_out, b1=None, b2=None, num_candidates=None,
                     ln_eps: float = 1e-5) -> _lib.LayerArgs:
+    """Argument struct of one layer; w2 and x_out may be None for the scoring
+    layer (mfalcon_layer_score)."""
     l = _lib.LayerArgs()
     l.struct_size = ctypes.sizeof(_lib.LayerArgs)
     l.B = seq_offsets.numel() - 1
@@ -311,9 +313,9 @@ def make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha
     l.seq_offsets = seq_offsets.data_ptr()
     l.num_candidates = _ptr(num_candidates)
     for name, t in (("x", x), ("w1", w1), ("w2", w2), ("x_out", x_out)):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
-    l.x, l.w1, l.w2, l.x_out = x.data_ptr(), w1.data_ptr(), w2.data_ptr(), x_out.data_ptr()
+    l.x, l.w1, l.w2, l.x_out = x.data_ptr(), w1.data_ptr(), _ptr(w2), _ptr(x_out)
     l.b1, l.b2 = _ptr(b1), _ptr(b2)
     l.timestamps = timestamps.data_ptr()
     l.rab_pos, l.num_pos_buckets = rab_pos.data_ptr(), rab_pos.shape[-1]
@@ -321,6 +323,31 @@ def make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha
     l.alpha = float(alpha)
     l.ln_eps = float(ln_eps)
     return l
+
+
+def mfalcon_layer_score(x, w1, seq_offsets, num_candidates, timestamps, rab_pos, rab_time, alpha,
+                        w, *, H: int, d: int, max_seq_len: int, score_stride: int, b1=None,
+                        ln_eps: float = 1e-5, candidates_only: bool = True, scores=None,
+                        workspace=None, stream=None):
+    """Scores [B, score_stride] (fp32) of every candidate after the last layer
+    (f1 + SiLU over all rows, attention, LN * U on the candidate rows)."""
+    lib = _lib.load()
+    B = seq_offsets.numel() - 1
+    if scores is None:
+        scores = torch.zeros(B, score_stride, dtype=torch.float32, device=x.device)
+    m = _lib.MfalconLayerArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconLayerArgs)
+    m.layer = make_layer_args(x, w1, None, seq_offsets, timestamps, rab_pos, rab_time, alpha, H=H,
+                              d=d, max_seq_len=max_seq_len, x_out=None, b1=b1,
+                              num_candidates=num_candidates, ln_eps=ln_eps)
+    m.w, m.scores, m.score_stride = w.data_ptr(), scores.data_ptr(), int(score_stride)
+    m.candidates_only = 1 if candidates_only else 0
+    need = lib.hstu_mfalcon_layer_workspace_bytes(ctypes.byref(m))
+    if workspace is None:
+        workspace = _empty_ws(need, x.device)
+    _lib.check(lib.mfalcon_layer_score(ctypes.byref(m), workspace.data_ptr(), workspace.numel(),
+                                       _stream_ptr(stream)))
+    return scores
 
 
 def hstu_layer_fwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 6
+#define HSTU_ABI_VERSION 7
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -257,6 +257,30 @@ size_t hstu_layer_workspace_bytes(const hstu_layer_args* args);
 
 hstu_status hstu_layer_fwd(const hstu_layer_args* args, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* The last layer of an M-FALCON stack, candidate rows only ("生成式推荐（一）：
+ * HSTU", section "M-FALCON"; "行动胜于言语：万亿参数序列转导器用于生成式推荐",
+ * section "2.3 M-FALCON 算法": the ranking pass needs the outputs of the
+ * candidates alone): Z = SiLU(X W1^T + b1) for every row (the history's K
+ * and V are needed), attention, and for each candidate c of sequence b
+ *   scores[b * score_stride + c] = < LN(O[n_b + c]) (.) U[n_b + c], w >.
+ * With candidates_only the attention computes only the query tiles that
+ * hold candidate rows.  layer.w2, layer.b2 and layer.x_out are not used
+ * (may be NULL); layer.num_candidates is required.
+ * Errors: as hstu_layer_fwd, HSTU_ERR_ARG without candidates, w or scores. */
+typedef struct hstu_mfalcon_layer_args {
+    uint32_t struct_size;          /* = sizeof(hstu_mfalcon_layer_args) */
+    hstu_layer_args layer;
+    const float* w;                /* [H*d] */
+    float* scores;                 /* out [B * score_stride] */
+    int32_t score_stride;          /* >= every candidate count */
+    int32_t candidates_only;
+} hstu_mfalcon_layer_args;
+
+size_t hstu_mfalcon_layer_workspace_bytes(const hstu_mfalcon_layer_args* args);
+
+hstu_status mfalcon_layer_score(const hstu_mfalcon_layer_args* args, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------- attention (gradients) */
 /* Gradients of the attention path for training (bf16, d_qk = d_v = 128):

@@ -55,6 +55,7 @@ def _lib():
         lib.hstu_oracle_layer_bwd.restype = None
         lib.hstu_oracle_layer.restype = None
         lib.hstu_oracle_mfalcon_score.restype = None
+        lib.hstu_oracle_layer_scores.restype = None
         lib.hstu_oracle_tiles.restype = ctypes.c_int64
         lib.hstu_oracle_count_visible.restype = ctypes.c_int64
         _LIB = lib
@@ -340,6 +341,31 @@ def mfalcon_score(q, k, v, u, offsets, num_candidates, ts, rab_pos, rab_time, al
         ctypes.c_int32(rt.shape[-1]), ctypes.c_double(alpha), ctypes.c_double(eps),
         _ptr(wa, _f64p), _ptr(scores, _f64p), ctypes.c_int32(scores.shape[1]),
         ctypes.c_int32(num_threads))
+    return scores[:, :cmax]
+
+
+def layer_scores(x, w1, offsets, num_candidates, ts, rab_pos, rab_time, alpha, w, H, d, *,
+                 b1=None, eps=1e-5, num_threads=0) -> np.ndarray:
+    """scores[b, c] after the last layer: Z = SiLU(X W1^T + b1) split into
+    U | V | Q | K, then ``mfalcon_score`` of that attention."""
+    x = _f64(x)
+    T, D = x.shape
+    off = _i32(offsets)
+    nc = _i32(num_candidates)
+    B = len(off) - 1
+    w1 = _f64(w1)
+    assert w1.shape == (4 * H * d, D)
+    b1a = None if b1 is None else _f64(b1)
+    cmax = int(nc.max()) if B else 0
+    scores = np.zeros((B, max(cmax, 1)), dtype=np.float64)
+    rp = _f64(rab_pos); rt = _f64(rab_time); wa = _f64(w)
+    tsa = np.ascontiguousarray(ts, dtype=np.int64)
+    _lib().hstu_oracle_layer_scores(
+        ctypes.c_int32(B), ctypes.c_int32(H), ctypes.c_int32(d), ctypes.c_int32(D),
+        _ptr(off, _i32p), _ptr(nc, _i32p), _ptr(x, _f64p), _ptr(w1, _f64p), _ptr(b1a, _f64p),
+        _ptr(tsa, _i64p), _ptr(rp, _f64p), ctypes.c_int32(rp.shape[-1]), _ptr(rt, _f64p),
+        ctypes.c_int32(rt.shape[-1]), ctypes.c_double(alpha), ctypes.c_double(eps), _ptr(wa, _f64p),
+        _ptr(scores, _f64p), ctypes.c_int32(scores.shape[1]), ctypes.c_int32(num_threads))
     return scores[:, :cmax]
 
 

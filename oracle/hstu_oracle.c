@@ -720,6 +720,37 @@ void hstu_oracle_mfalcon_score(int32_t B, int32_t H, int32_t d,
 }
 
 /* ------------------------------------------------------------------------ */
+/* The last layer of an M-FALCON stack, scores only: Z = SiLU(X W1^T + b1)   */
+/* split into U | V | Q | K as in hstu_oracle_layer, then the M-FALCON       */
+/* scores of that attention ("生成式推荐（一）：HSTU", section "M-FALCON").    */
+/* ------------------------------------------------------------------------ */
+void hstu_oracle_layer_scores(int32_t B, int32_t H, int32_t d, int32_t D,
+                              const int32_t* offsets, const int32_t* num_candidates,
+                              const double* x, const double* w1, const double* b1,
+                              const int64_t* timestamps,
+                              const double* rab_pos, int32_t num_pos_buckets,
+                              const double* rab_time, int32_t num_time_buckets,
+                              double alpha, double eps, const double* w,
+                              double* scores, int32_t score_stride, int32_t num_threads) {
+    set_threads(num_threads);
+    int64_t row0 = offsets[0];
+    int64_t T = (int64_t)offsets[B] - row0;
+    int32_t hd = H * d;
+    int32_t zw = 4 * hd;
+    double* z = (double*)malloc(sizeof(double) * (size_t)(T * zw + 1));
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * (size_t)(B + 1));
+    for (int32_t b = 0; b <= B; ++b) off[b] = (int32_t)(offsets[b] - row0);
+    linear(T, zw, D, x + row0 * D, D, w1, b1, z, zw);
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < T * zw; ++e) z[e] = hstu_oracle_silu(z[e]);
+    hstu_oracle_mfalcon_score(B, H, d, off, num_candidates, z + 2 * hd, z + 3 * hd, z + 1 * hd, z, zw,
+                              timestamps + row0, rab_pos, num_pos_buckets, rab_time, num_time_buckets,
+                              alpha, eps, w, scores, score_stride, num_threads);
+    free(off);
+    free(z);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Brute-force set of non-empty tiles: (b, query tile, key tile) such that   */
 /* some visible pair (i, j) has i / tile_m == query tile and j / tile_n ==    */
 /* key tile.  Written in ascending (b, qt, kt) order; returns the count.     */

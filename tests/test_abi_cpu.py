@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 6
+    assert lib.hstu_abi_version() == 7
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -54,6 +54,7 @@ _STRUCTS = {
     "hstu_attn_args": _lib.AttnArgs,
     "hstu_mfalcon_args": _lib.MfalconArgs,
     "hstu_mfalcon_cached_args": _lib.MfalconCachedArgs,
+    "hstu_mfalcon_layer_args": _lib.MfalconLayerArgs,
     "hstu_layer_args": _lib.LayerArgs,
     "hstu_attn_bwd_args": _lib.AttnBwdArgs,
     "hstu_layer_bwd_args": _lib.LayerBwdArgs,
@@ -383,3 +384,34 @@ def test_cached_workspace_errors_and_size(lib):
     assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == _lib.HSTU_OK
     m.num_cand_rows, m.B = 600, 0
     assert lib.mfalcon_score_cached(ctypes.byref(m), None, 0, None) == _lib.HSTU_OK
+
+
+def test_mfalcon_layer_validation(lib):
+    m = _lib.MfalconLayerArgs()
+    m.struct_size = ctypes.sizeof(_lib.MfalconLayerArgs)
+    l = m.layer
+    l.struct_size = ctypes.sizeof(_lib.LayerArgs)
+    l.B, l.H, l.d, l.D, l.max_seq_len, l.num_rows = 2, 4, 128, 512, 100, 200
+    fake = 0x10000
+    l.seq_offsets = l.x = l.w1 = l.timestamps = l.rab_pos = l.rab_time = fake
+    l.num_pos_buckets, l.num_time_buckets = 1024, 32
+    l.alpha, l.ln_eps = 1.0 / 4096, 1e-5
+    m.score_stride = 16
+    # candidates, w and scores are required; w2 and x_out are not
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    assert b"num_candidates" in lib.hstu_last_error()
+    l.num_candidates = fake
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    m.w = m.scores = fake
+    need = lib.hstu_mfalcon_layer_workspace_bytes(ctypes.byref(m))
+    assert need >= 200 * (4 * 512 + 512) * 2
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
+    m.score_stride = 0
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    m.score_stride = 16
+    l.d = 64
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_UNSUPPORTED
+    l.d = 128
+    m.struct_size = 4
+    assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
+    assert lib.hstu_mfalcon_layer_workspace_bytes(ctypes.byref(m)) == 0

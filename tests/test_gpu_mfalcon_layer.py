@@ -174,3 +174,57 @@ def test_layer_stack_full_size_sampled_sequences():
     for b in seqs:
         s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
         assert_close(got[s0:s1], refs[b], "bf16", f"cfg5 seq {b} (L={s1 - s0}) X_out")
+
+
+def _layer_scores_gpu(x, ncand, w, candidates_only):
+    import torch
+    from hstu_sequential_transducer_causal_amd import ops
+    xd = dev_tensor(x.x, "bf16")
+    w1 = dev_tensor(x.w1[0], "bf16")
+    off = torch.from_numpy(x.offsets.astype(np.int32)).cuda()
+    nc = torch.from_numpy(np.asarray(ncand, dtype=np.int32)).cuda()
+    ts = torch.from_numpy(x.ts).cuda()
+    rp = torch.from_numpy(x.rab_pos[0]).cuda()
+    rt = torch.from_numpy(x.rab_time[0]).cuda()
+    wd = torch.from_numpy(w.astype(np.float32)).cuda()
+    cmax = max(1, int(max(ncand)))
+    s = ops.mfalcon_layer_score(xd, w1, off, nc, ts, rp, rt, x.alpha, wd, H=x.H, d=x.d,
+                                max_seq_len=int(np.diff(x.offsets).max()), score_stride=cmax,
+                                ln_eps=x.eps, candidates_only=candidates_only)
+    torch.cuda.synchronize()
+    return host_f32(s)
+
+
+@pytest.mark.parametrize("candidates_only", [True, False])
+def test_mfalcon_last_layer_scores_ragged(candidates_only):
+    """The last layer of an M-FALCON stack, candidate rows only: f1 + SiLU
+    over every row, attention (only the query tiles holding candidates, or
+    all), LN * U and the score -- against the oracle's scoring layer; users
+    without candidates, of candidates only, and with candidates mid-tile."""
+    lengths = [300, 129, 64, 520, 200]
+    ncand = [40, 0, 64, 257, 1]
+    x = synth.make_layer_stack(96, lengths, H=4, d=128, D=512, layers=1, P=1024, NT=32,
+                               alpha=1 / 1024)
+    w = np.random.default_rng(97).normal(0, 1 / np.sqrt(512), size=512)
+    got = _layer_scores_gpu(x, ncand, w, candidates_only)
+    ref = oracle.layer_scores(x.x, x.w1[0], x.offsets, ncand, x.ts, x.rab_pos[0], x.rab_time[0],
+                              x.alpha, w, x.H, x.d, eps=x.eps)
+    g = np.concatenate([got[b, :c] for b, c in enumerate(ncand)])
+    r = np.concatenate([ref[b, :c] for b, c in enumerate(ncand)])
+    assert_close(g, r, "bf16", f"last-layer scores (candidates_only={candidates_only})")
+
+
+def test_mfalcon_last_layer_scores_full_size_sampled_users():
+    """8 users x (2048 history + 512 candidates), D = 512, 4 heads of 128, in
+    one call; the oracle's scoring layer checks two users (a user's scores
+    depend on that user's rows alone)."""
+    n, c, B = 2048, 512, 8
+    x = synth.make_layer_stack(98, [n + c] * B, H=4, d=128, D=512, layers=1, P=1024, NT=32,
+                               alpha=1 / (n + c))
+    w = np.random.default_rng(99).normal(0, 1 / np.sqrt(512), size=512)
+    got = _layer_scores_gpu(x, [c] * B, w, True)
+    for b in (0, 7):
+        s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
+        ref = oracle.layer_scores(x.x[s0:s1], x.w1[0], [0, s1 - s0], [c], x.ts[s0:s1], x.rab_pos[0],
+                                  x.rab_time[0], x.alpha, w, x.H, x.d, eps=x.eps)
+        assert_close(got[b], ref[0], "bf16", f"full-size last-layer scores user {b}")

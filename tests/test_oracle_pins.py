@@ -422,3 +422,30 @@ def test_attn_rows_equals_full_oracle_at_those_rows():
     full_id = oracle.attn(x.q, x.k, x.v, x.offsets, x.ts, rp, rt, x.alpha,
                           num_candidates=x.num_candidates, act=oracle.ACT_IDENTITY)
     assert np.array_equal(got_id, full_id[rows])
+
+
+def test_layer_scores_are_composition_of_library_routines():
+    """The scoring layer: f1 (+ b1) by numpy matmul, SiLU by scipy's
+    logistic, the split U | V | Q | K, then the pinned M-FALCON scores; a
+    sequence without candidates and one of candidates only included."""
+    from scipy.special import expit
+    rng = np.random.default_rng(85)
+    H, d, D = 2, 16, 32
+    lengths, cands = [20, 9, 6, 13], [4, 0, 6, 1]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(off[-1])
+    X = rng.normal(0, 0.5, size=(T, D))
+    w1 = rng.uniform(-0.3, 0.3, size=(4 * H * d, D))
+    b1 = rng.normal(0, 0.1, size=4 * H * d)
+    ts = np.concatenate([np.cumsum(rng.integers(1, 500, size=L)) for L in lengths]).astype(np.int64)
+    rp = rng.normal(0, 0.1, size=24)
+    rt = rng.normal(0, 0.1, size=16)
+    w = rng.normal(0, 1.0 / np.sqrt(H * d), size=H * d)
+    got = oracle.layer_scores(X, w1, off, cands, ts, rp, rt, 0.05, w, H, d, b1=b1)
+    z = X @ w1.T + b1
+    z = z * expit(z)
+    hd = H * d
+    U, V, Q, K = (z[:, i * hd:(i + 1) * hd].reshape(T, H, d) for i in range(4))
+    ref = oracle.mfalcon_score(Q, K, V, U, off, cands, ts, rp, rt, 0.05, w)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    assert got.shape == (4, 6)
