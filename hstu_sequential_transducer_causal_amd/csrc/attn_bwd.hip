@@ -555,13 +555,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                     if (!st.tconst && !st.few) atomicAdd(&hist[P + tbv(r)], gv[r]);
                 }
             }
+            // one lane adds the block sums to this wave's own histogram:
+            // plain read-add-writes (an atomic at a uniform address becomes a
+            // scan over the active lanes)
             if (lane == 63) {
-                if (st.pos_clamped) atomicAdd(&hist[P - 1], gsum);
-                if (st.tconst) atomicAdd(&hist[P + st.tlo], gsum);
+                if (st.pos_clamped) hist[P - 1] += gsum;
+                if (st.tconst) hist[P + st.tlo] += gsum;
                 if (st.few) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        if (st.tlo + k <= st.thi) atomicAdd(&hist[P + st.tlo + k], tsum[k]);
+                        if (st.tlo + k <= st.thi) hist[P + st.tlo + k] += tsum[k];
                 }
             }
         };
