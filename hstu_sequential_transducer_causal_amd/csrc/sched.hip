@@ -400,6 +400,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
         a.ctrl[0] = (int)min((int64_t)npieces, a.cap_pieces);
         a.ctrl[1] = 0;
         a.ctrl[2] = any_split ? (int)min((int64_t)s.carry, a.cap) : 0;
+        for (int x = 0; x < kXcds; ++x) a.ctrl[kXcdCursor + 4 * x] = 0;
     }
 }
 
