@@ -197,7 +197,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             int w = total_work;
             for (int k = 0; k < kXcds; ++k) {
                 const int x = (my_xcd + k) & (kXcds - 1);
-                const int ww = atomicAdd(p.cursor + 4 * x, 1) * kXcds + x;
+                int32_t* cur = p.cursor + kXcdStride * x;
+                // a queue seen exhausted is skipped with a load, not an atomic
+                if (k > 0 && __hip_atomic_load(cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * kXcds + x >=
+                                 total_work)
+                    continue;
+                const int ww = atomicAdd(cur, 1) * kXcds + x;
                 if (ww < total_work) {
                     w = ww;
                     break;

@@ -48,16 +48,18 @@ constexpr int kMaxPosBuckets = 8192;
 // query-row slice.
 constexpr int kTsBlock = 32;
 // The bf16 attention core pulls work per accelerator die (XCD, each with its
-// own L2): kXcds cursors in the control block, 4 ints apart.
+// own L2): kXcds cursors in the control block, one 128-byte line apart.
 constexpr int kXcds = 8;
 constexpr int kXcdCursor = 32;
+constexpr int kXcdStride = 32;
+constexpr int kCtrlInts = kXcdCursor + kXcds * kXcdStride;
 
 // Workspace carve-up of the scheduler and the timestamp preparation (all
 // offsets 256-byte aligned).
 struct SchedLayout {
-    size_t off_ctrl;   // int32[64]: [0] piece count, [1] work cursor of the persistent kernel,
-                       // [2] split-block count, [kXcdCursor + 4 x] the bf16 core's cursor of
-                       // accelerator die (XCD) x
+    size_t off_ctrl;   // int32[kCtrlInts]: [0] piece count, [1] work cursor of the persistent
+                       // kernel, [2] split-block count, [kXcdCursor + kXcdStride x] the bf16
+                       // core's cursor of accelerator die (XCD) x
     size_t off_qscan;  // int32[B + 1] exclusive prefix of query tiles per sequence
     size_t off_items;  // WorkItem[cap_pieces]
     size_t off_split;  // SplitBlock[cap]

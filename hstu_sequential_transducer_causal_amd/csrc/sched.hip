@@ -400,7 +400,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
         a.ctrl[0] = (int)min((int64_t)npieces, a.cap_pieces);
         a.ctrl[1] = 0;
         a.ctrl[2] = any_split ? (int)min((int64_t)s.carry, a.cap) : 0;
-        for (int x = 0; x < kXcds; ++x) a.ctrl[kXcdCursor + 4 * x] = 0;
+        for (int x = 0; x < kXcds; ++x) a.ctrl[kXcdCursor + kXcdStride * x] = 0;
     }
 }
 
@@ -476,7 +476,7 @@ SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d,
     l.part_slots = split_d > 0 && H > 0 ? (int)std::min<size_t>(kMaxPartialSlots, l.cap * size_t(H) * 8) : 0;
     l.cap_pieces = l.cap + (H > 0 ? size_t(l.part_slots) / size_t(H) : 0);
     l.off_ctrl = align256(base);
-    l.off_qscan = align256(l.off_ctrl + 64 * sizeof(int32_t));
+    l.off_qscan = align256(l.off_ctrl + kCtrlInts * sizeof(int32_t));
     l.off_items = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
     l.off_split = align256(l.off_items + l.cap_pieces * sizeof(WorkItem));
     l.off_part = align256(l.off_split + l.cap * sizeof(SplitBlock));
