@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         if (w >= total_work) break;
         const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
         const int kbw = uni(s.item[3]);
-        const int kb_begin = kbw & 0xffff, kb_end = kbw >> 16;
+        const int kb_begin = kbw & 0xffff;
         const int prw = uni(s.item[4]);
         const int p0 = prw & 0xffff, p1 = prw >> 16;   // this piece's positions in the tile list
         const int slot = uni(s.item[5]), piece = uni(s.item[6]), npieces = uni(s.item[7]);

@@ -95,28 +95,6 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     }
 }
 
-// B operand fragments, for the 16-row chunk c of a [32][128] tile stored with
-// vswz, of a product whose contraction runs over the tile's rows (O += A V
-// over keys in the forward): for each 32-column block nb, lane l gets column
-// nb*32 + l % 32 at rows 16c + 4 (l / 32) + 0..3 and 16c + 8 + 4 (l / 32) +
-// 0..3 -- the row order in which a 32x32 accumulator, packed by 4-element
-// groups, holds the A operand (two transposed reads of 4 rows x 4 columns per
-// 16-lane group).
-__device__ __forceinline__ void read_v_chunk(const uint8_t* v_lds, int c, int lane, u32x4 (&vf)[4]) {
-    const int m = lane & 15;
-    const int dsub = ((lane >> 4) & 1) * 16;
-    const int key0 = c * 16 + 4 * (lane >> 5) + (m >> 2);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int col = nb * 32 + dsub + 4 * (m & 3);      // element column
-        const int chunk = col >> 3;
-        const int within = (col & 7) * 2;
-        const u32x2 v0 = ds_read_tr(v_lds + vswz(key0, chunk) + within);
-        const u32x2 v1 = ds_read_tr(v_lds + vswz(key0 + 8, chunk) + within);
-        vf[nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
-    }
-}
-
 // Fragment reads by 32-bit LDS address.  Every per-lane address of a tile is
 // one base XOR a constant: K fragment kc of lane l (row l % 32, chunk
 // 2 kc + l / 32, swizzled by row & 15) sits at base ^ (kc << 5), and the V^T
@@ -142,7 +120,13 @@ __device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
     const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
     return __builtin_bit_cast(u32x2, r);
 }
-// V^T fragments of a tile's two 16-key chunks (the layout of read_v_chunk)
+// B operand fragments of a [32][128] tile stored with vswz, for a product
+// whose contraction runs over the tile's rows (O += A V over keys in the
+// forward), for both 16-row chunks c: for each 32-column block nb, lane l gets
+// column nb*32 + l % 32 at rows 16c + 4 (l / 32) + 0..3 and 16c + 8 +
+// 4 (l / 32) + 0..3 -- the row order in which a 32x32 accumulator, packed by
+// 4-element groups, holds the A operand (two transposed reads of 4 rows x 4
+// columns per 16-lane group).  voff = v_lane_offset(lane).
 __device__ __forceinline__ void read_v_tile(uint32_t stage_base, uint32_t voff, u32x4 (&vf)[2][4]) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
