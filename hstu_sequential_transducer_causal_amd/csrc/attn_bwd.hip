@@ -545,15 +545,31 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 const int pb = wrow0 - st.j0 + lane - 31;
                 if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             }
+            if (!st.pos_clamped && !diag) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (gv[r] != 0.0f) {
-                    if (!st.pos_clamped && !diag) {
+                for (int r = 0; r < 16; ++r) {
+                    if (gv[r] != 0.0f) {
                         const int j = st.j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
                         atomicAdd(&hist[min(max(prow - min(j, n), 0), P - 1)], gv[r]);
                     }
-                    if (!st.tconst && !st.few) atomicAdd(&hist[P + tbv(r)], gv[r]);
                 }
+            }
+            if (!st.tconst && !st.few) {
+                // a lane's keys are in time order, so its time buckets come
+                // in runs: one atomic per run
+                float run = 0.0f;
+                int rb = tbv(0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int b = tbv(r);
+                    if (b != rb) {
+                        if (run != 0.0f) atomicAdd(&hist[P + rb], run);
+                        run = 0.0f;
+                        rb = b;
+                    }
+                    run += gv[r];
+                }
+                if (run != 0.0f) atomicAdd(&hist[P + rb], run);
             }
             // one lane adds the block sums to this wave's own histogram:
             // plain read-add-writes (an atomic at a uniform address becomes a
