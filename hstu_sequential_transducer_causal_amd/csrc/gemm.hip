@@ -6,20 +6,56 @@
 //
 //   C[m, n] = epi( sum_k A[m, k] B[n, k] + bias[n] ) (+ R[m, n])
 //
-// A (activations) and B (weights, out x in) are both K-contiguous, so both
-// feed v_mfma_f32_16x16x32_bf16 with 16-byte reads.  128 x 128 block tile,
-// BK = 64, 4 waves of 64 x 64, LDS tiles with a 16-byte XOR swizzle and a
-// register prefetch of the next K slice.  Requires N % 128 == 0 and
-// K % 64 == 0; M is arbitrary (rows are guarded).
+// A (activations, [M][K]) and B (weights, out x in, [N][K]) are both
+// K-contiguous, so a tile row of either is directly an MFMA operand row.
+//
+// Design (gfx950): a workgroup of 4 waves computes a 256 x 128 tile of C, each
+// wave 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16; three workgroups
+// share a CU, so one's prologue and epilogue overlap the others' MFMAs.  K
+// streams in slices of 32 through a 2-stage LDS ring (24 KiB a stage) filled
+// by direct-to-LDS buffer loads issued one slice ahead, so the data never
+// passes through registers; rows past M fall outside the buffer's range and
+// read as zeros.  A tile row is 64 bytes; its 16-byte chunks are XOR-swizzled
+// by (row / 4) % 4, so the 16 rows a 16-lane group reads at one logical chunk
+// hit distinct banks.  Per 16-wide K step a wave reads 6 fragments (16 bytes
+// a lane) for 8 MFMAs.  The epilogue stages the fp32 tile through the ring in
+// passes of 32 rows (72-float row pitch: conflict-free column writes),
+// then each lane finishes 8 consecutive columns of a row (bias, optional
+// pre-activation copy, SiLU, residual) and writes them with 16-byte stores --
+// whole 128-byte lines per 8 lanes.  Tiles are dealt to the dies so that each
+// die takes a contiguous run of the strip-major order: the N tiles of one A
+// strip share its L2.
+//
+// Requires N % 128 == 0, K % 32 == 0, row strides that are multiples of 8
+// elements and 16-byte aligned matrices; M is arbitrary.
 #include "internal.h"
-#include "hstu_device.h"
+#include "tile_ops.h"
 
 namespace hstu {
 
 namespace {
 
-constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int BM = 256, BN = 128, BK = 32;
+// Three workgroups per CU (48 KiB of LDS and 160 VGPRs each) with a 2-stage
+// ring measured faster than two with 3 stages or one with 4: the latency of
+// a tile's first loads and the epilogue's work are hidden by the other
+// workgroups rather than by a deeper ring.
+constexpr int kWgPerCu = 3;
+constexpr int kStages = 2;
+constexpr int kAhead = kStages - 1;              // slices in flight ahead of the one computed
 constexpr int kThreads = 256;
+constexpr int kRow = BK * 2;                     // bytes per tile row
+constexpr int kABytes = BM * kRow;               // 16 KiB
+constexpr int kBBytes = BN * kRow;               // 8 KiB
+constexpr int kStageBytes = kABytes + kBBytes;   // 24 KiB
+constexpr int kSmem = kStages * kStageBytes;     // 48 KiB
+constexpr int kLoadsA = kABytes / 1024 / 4;      // 1 KiB loads per wave and slice
+constexpr int kLoadsB = kBBytes / 1024 / 4;
+constexpr int kPitch = 72;                       // epilogue staging row pitch (floats)
+static_assert(kLoadsA + kLoadsB == 6, "the slice wait below counts 6 loads per wave");
+// epilogue staging: rows of the wave's 128-row tile per pass through the ring
+constexpr int kPassRows = kSmem >= 4 * 128 * kPitch * 4 ? 128 : kSmem >= 4 * 64 * kPitch * 4 ? 64 : 32;
+static_assert(4 * kPassRows * kPitch * 4 <= kSmem, "a pass of the staged tile fits the ring");
 
 struct Params {
     int64_t M;
@@ -31,101 +67,183 @@ struct Params {
     uint16_t* c; int64_t ldc;
     int silu;
     uint16_t* cp; int64_t ldcp;   // optional pre-activation output
+    int tiles_n;                  // N / BN
 };
 
-// Row r of a [128][64] bf16 tile occupies 128 bytes = 8 chunks of 16 bytes;
-// chunk x of row r is stored at position x ^ ((r >> 1) & 7).
-__device__ __forceinline__ int swz(int r, int x) { return (r * 8 + (x ^ ((r >> 1) & 7))) << 4; }
+// Physical 16-byte chunk of logical chunk x in tile row r (an involution).
+__device__ __forceinline__ uint32_t chunk_of(int r, int x) { return (uint32_t)(x ^ ((r >> 2) & 3)); }
 
-__global__ void __launch_bounds__(kThreads, 2) gemm_bf16_kernel(Params p) {
-    __shared__ __align__(16) uint8_t sa[TM * TK * 2];
-    __shared__ __align__(16) uint8_t sb[TN * TK * 2];
+// vmcnt(6 n): wait until at most n later slices' loads are in flight (other
+// counters untouched).
+__device__ __forceinline__ void wait_slice(int n) {
+    if (n >= 2)
+        __builtin_amdgcn_s_waitcnt(0x0F7C);
+    else if (n == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F76);
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+__global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int c16 = lane & 15;
-    const int g = lane >> 4;
+    const int l32 = lane & 31, h = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * TM;
-    const int n0 = blockIdx.x * TN;
 
-    f32x4 acc[4][4];
+    // die x (workgroups x, x + 8, ...) takes tiles [x * per + min(x, rem), ...)
+    const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+    const int per = nwg / 8, rem = nwg % 8, x = wg % 8;
+    const int t = x * per + min(x, rem) + wg / 8;
+    const int mt = t / p.tiles_n, nt = t - mt * p.tiles_n;
+    const int64_t m0 = (int64_t)mt * BM;
+    const int n0 = nt * BN;
+    const int rows = (int)min((int64_t)BM, p.M - m0);
+
+    const u32x4 ra = make_rsrc(p.a + m0 * p.lda, (uint32_t)(rows * p.lda * 2));
+    const u32x4 rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(BN * p.ldb * 2));
+
+    // loads: load m of wave w fills tile rows 16m .. 16m+15 of the wave's
+    // share (A: rows 64w + .., B: rows 32w + ..); lane l writes row 16m + l/4
+    // at physical chunk l % 4, so it fetches the logical chunk placed there.
+    // The swizzle does not depend on m; m moves 16 rows (a scalar offset).
+    const int q = lane >> 2, pch = lane & 3;
+    const int r_a = 64 * wave + q, r_b = 32 * wave + q;
+    const uint32_t voa = (uint32_t)(r_a * p.lda * 2) + (chunk_of(r_a, pch) << 4);
+    const uint32_t vob = (uint32_t)(r_b * p.ldb * 2) + (chunk_of(r_b, pch) << 4);
+    const uint32_t a16 = uniu((uint32_t)(16 * p.lda * 2)), b16 = uniu((uint32_t)(16 * p.ldb * 2));
+    const uint32_t sbase = lds_addr(smem);
+    auto issue = [&](int kt) {
+        const uint32_t st = sbase + (uint32_t)((kt % kStages) * kStageBytes);
+        const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+        for (int m = 0; m < kLoadsA; ++m)
+            dma16(ra, uniu(st + (uint32_t)((64 * wave + 16 * m) * kRow)), voa, uniu(kb + m * a16));
+#pragma unroll
+        for (int m = 0; m < kLoadsB; ++m)
+            dma16(rb, uniu(st + (uint32_t)(kABytes + (32 * wave + 16 * m) * kRow)), vob, uniu(kb + m * b16));
+    };
+
+    // fragments: lane l reads row (block base) + l % 32 at logical chunk
+    // 2 s + l / 32 for K step s; the row's swizzle (l % 32 / 4) % 4 is the same
+    // in every 32-row block, and chunk 2 s + c is chunk c XOR 2 s, i.e. the
+    // address XOR (s << 5)
+    const uint32_t qq = (uint32_t)((l32 >> 2) & 3);
+    const uint32_t fa = (uint32_t)((wm * 128 + l32) * kRow) + (((uint32_t)h ^ qq) << 4);
+    const uint32_t fb = (uint32_t)(kABytes + (wn * 64 + l32) * kRow) + (((uint32_t)h ^ qq) << 4);
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // staging: thread -> (row = tid / 8 + 32 * it, chunk = tid % 8)
-    const int srow = tid >> 3, sch = tid & 7;
-    u32x4 ra[4], rb[4];
-    auto prefetch = [&](int k0) {
+    const int nk = p.K / BK;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int r = srow + 32 * it;
-            const int64_t m = m0 + r;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            ra[it] = z;
-            if (m < p.M) ra[it] = *reinterpret_cast<const u32x4*>(p.a + m * p.lda + k0 + sch * 8);
-            rb[it] = *reinterpret_cast<const u32x4*>(p.b + (int64_t)(n0 + r) * p.ldb + k0 + sch * 8);
-        }
-    };
-    prefetch(0);
-    for (int k0 = 0; k0 < p.K; k0 += TK) {
+    for (int k = 0; k < kAhead; ++k)
+        if (k < nk) issue(k);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_slice(min(kAhead - 1, nk - 1 - kt));   // this wave's loads of slice kt have landed
+        lds_barrier();             // ... every wave's, and slice kt-1's stage is free
+        if (kt + kAhead < nk) issue(kt + kAhead);
+        const uint32_t st = sbase + (uint32_t)((kt % kStages) * kStageBytes);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int r = srow + 32 * it;
-            *reinterpret_cast<u32x4*>(sa + swz(r, sch)) = ra[it];
-            *reinterpret_cast<u32x4*>(sb + swz(r, sch)) = rb[it];
-        }
-        __syncthreads();
-        if (k0 + TK < p.K) prefetch(k0 + TK);
+        for (int s = 0; s < BK / 16; ++s) {
+            const uint32_t xa = (st + fa) ^ (uint32_t)(s << 5);
+            const uint32_t xb = (st + fb) ^ (uint32_t)(s << 5);
+            bf16x8 af[4], bfr[2];
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-            bf16x8 af[4], bfr[4];
+            for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(xa + (uint32_t)(i * 32 * kRow));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + i * 16 + c16;
-                af[i] = *reinterpret_cast<const bf16x8*>(sa + swz(r, 4 * kc + g));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn * 64 + j * 16 + c16;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(sb + swz(r, 4 * kc + g));
-            }
+            for (int j = 0; j < 2; ++j) bfr[j] = lds_read_b128(xb + (uint32_t)(j * 32 * kRow));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
-        __syncthreads();
     }
 
-    // epilogue: lane holds C[row 4g + r][col c16] of each 16 x 16 block
+    // epilogue: stage the wave's 128 x 64 fp32 tile, kPassRows at a time, in its
+    // quarter of the ring (result lane l holds column l % 32, rows 8 (r / 4) +
+    // 4 (l / 32) + r % 4 of each block), then finish 8 consecutive columns of
+    // a row per lane.  (A wave's LDS accesses complete in order: no barrier
+    // between its own writes and reads.)
+    lds_sync();
+    float* stg = reinterpret_cast<float*>(smem) + wave * kPassRows * kPitch;
+    const int c8 = (lane & 7) * 8;
+    const int n = n0 + wn * 64 + c8;
+    float bias[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + c16;
-        const float bias = p.bias ? p.bias[n] : 0.0f;
+    for (int k = 0; k < 8; ++k) bias[k] = 0.0f;
+    if (p.bias) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int k = 0; k < 8; ++k) bias[k] = p.bias[n + k];
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + r;
-                if (m < p.M) {
-                    float x = acc[i][j][r] + bias;
-                    if (p.cp) p.cp[m * p.ldcp + n] = f32_to_bf16_bits(x);
-                    if (p.silu) x = silu_fast(x);
-                    if (p.res) x += bf16_to_f32(p.res[m * p.ldr + n]);
-                    p.c[m * p.ldc + n] = f32_to_bf16_bits(x);
+    for (int pass = 0; pass < 128 / kPassRows; ++pass) {
+#pragma unroll
+    for (int i = 0; i < kPassRows / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                stg[(32 * i + 8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + 32 * j + l32] =
+                    acc[pass * (kPassRows / 32) + i][j][r];
+#pragma unroll 4
+    for (int it = 0; it < kPassRows / 8; ++it) {
+        const int rr = 8 * it + (lane >> 3);
+        const int64_t m = m0 + wm * 128 + kPassRows * pass + rr;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg + rr * kPitch + c8);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg + rr * kPitch + c8 + 4);
+        if (m < p.M) {
+            float xv[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                xv[k] = v0[k] + bias[k];
+                xv[4 + k] = v1[k] + bias[4 + k];
+            }
+            if (p.cp) {
+                const u32x4 w = {pack2(xv[0], xv[1]), pack2(xv[2], xv[3]), pack2(xv[4], xv[5]),
+                                 pack2(xv[6], xv[7])};
+                *reinterpret_cast<u32x4*>(p.cp + m * p.ldcp + n) = w;
+            }
+            if (p.silu) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xv[k] = silu_fast(xv[k]);
+            }
+            if (p.res) {
+                const u32x4 rv = *reinterpret_cast<const u32x4*>(p.res + m * p.ldr + n);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    xv[2 * k] += __uint_as_float(rv[k] << 16);
+                    xv[2 * k + 1] += __uint_as_float(rv[k] & 0xffff0000u);
                 }
             }
+            const u32x4 w = {pack2(xv[0], xv[1]), pack2(xv[2], xv[3]), pack2(xv[4], xv[5]),
+                             pack2(xv[6], xv[7])};
+            *reinterpret_cast<u32x4*>(p.c + m * p.ldc + n) = w;
         }
     }
+    }
 }
+
+bool aligned16(const void* q) { return ((uintptr_t)q & 15u) == 0; }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
     if (g.M <= 0) return hipSuccess;
+    if (g.N % BN || g.K % BK || g.K <= 0 || g.lda % 8 || g.ldb % 8 || g.ldc % 8 ||
+        (g.residual && g.ldr % 8) || (g.c_pre && g.ldcp % 8) || !aligned16(g.a) || !aligned16(g.b) ||
+        !aligned16(g.c) || (g.residual && !aligned16(g.residual)) || (g.c_pre && !aligned16(g.c_pre)))
+        return hipErrorInvalidValue;
+    if ((int64_t)BM * g.lda * 2 > 0x7fffffffLL || (int64_t)BN * g.ldb * 2 > 0x7fffffffLL)
+        return hipErrorInvalidValue;
     Params p;
     p.M = g.M; p.N = g.N; p.K = g.K;
     p.a = static_cast<const uint16_t*>(g.a); p.lda = g.lda;
@@ -135,8 +253,13 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
     p.c = static_cast<uint16_t*>(g.c); p.ldc = g.ldc;
     p.silu = g.silu;
     p.cp = static_cast<uint16_t*>(g.c_pre); p.ldcp = g.ldcp;
-    dim3 grid(g.N / TN, (unsigned)((g.M + TM - 1) / TM));
-    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(kThreads), 0, stream, p);
+    p.tiles_n = g.N / BN;
+    const int64_t tiles = ((g.M + BM - 1) / BM) * (int64_t)p.tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)tiles), dim3(kThreads), kSmem, stream, p);
     return hipGetLastError();
 }
 
