@@ -44,18 +44,26 @@ constexpr int kWgPerCu = 3;
 constexpr int kStages = 2;
 constexpr int kAhead = kStages - 1;              // slices in flight ahead of the one computed
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kWaveN = 64;                       // each wave: 128 rows x kWaveN columns of C
+constexpr int kBJ = kWaveN / 32;                 // 32x32 blocks across a wave's columns
+constexpr int kWavesN = BN / kWaveN;
+static_assert(kWaves / kWavesN * 128 == BM, "waves tile the block");
 constexpr int kRow = BK * 2;                     // bytes per tile row
-constexpr int kABytes = BM * kRow;               // 16 KiB
-constexpr int kBBytes = BN * kRow;               // 8 KiB
-constexpr int kStageBytes = kABytes + kBBytes;   // 24 KiB
-constexpr int kSmem = kStages * kStageBytes;     // 48 KiB
-constexpr int kLoadsA = kABytes / 1024 / 4;      // 1 KiB loads per wave and slice
-constexpr int kLoadsB = kBBytes / 1024 / 4;
-constexpr int kPitch = 72;                       // epilogue staging row pitch (floats)
-static_assert(kLoadsA + kLoadsB == 6, "the slice wait below counts 6 loads per wave");
+constexpr int kABytes = BM * kRow;
+constexpr int kBBytes = BN * kRow;
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kSmem = kStages * kStageBytes;
+constexpr int kRowsA = BM / kWaves, kRowsB = BN / kWaves;   // tile rows each wave loads
+constexpr int kLoadsA = kRowsA / 16, kLoadsB = kRowsB / 16; // 1 KiB loads (16 rows) per wave and slice
+constexpr int kLoads = kLoadsA + kLoadsB;
+static_assert(kLoads * (kAhead - 1) <= 15, "slice waits fit the vmcnt field");
+constexpr int kPitch = kWaveN + 8;               // epilogue staging row pitch (floats): 4 rows = 32 banks
+constexpr int kColGroups = kWaveN / 8;           // lanes per staged row (8 columns each)
 // epilogue staging: rows of the wave's 128-row tile per pass through the ring
-constexpr int kPassRows = kSmem >= 4 * 128 * kPitch * 4 ? 128 : kSmem >= 4 * 64 * kPitch * 4 ? 64 : 32;
-static_assert(4 * kPassRows * kPitch * 4 <= kSmem, "a pass of the staged tile fits the ring");
+constexpr int kPassRows = kSmem >= kWaves * 128 * kPitch * 4 ? 128
+                        : kSmem >= kWaves * 64 * kPitch * 4 ? 64 : 32;
+static_assert(kWaves * kPassRows * kPitch * 4 <= kSmem, "a pass of the staged tile fits the ring");
 
 struct Params {
     int64_t M;
@@ -73,13 +81,14 @@ struct Params {
 // Physical 16-byte chunk of logical chunk x in tile row r (an involution).
 __device__ __forceinline__ uint32_t chunk_of(int r, int x) { return (uint32_t)(x ^ ((r >> 2) & 3)); }
 
-// vmcnt(6 n): wait until at most n later slices' loads are in flight (other
-// counters untouched).
+// vmcnt(kLoads n): wait until at most n later slices' loads are in flight
+// (other counters untouched).
+constexpr int vm_field(int n) { return kLoads * n <= 15 ? kLoads * n : 15; }
 __device__ __forceinline__ void wait_slice(int n) {
     if (n >= 2)
-        __builtin_amdgcn_s_waitcnt(0x0F7C);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | vm_field(2));
     else if (n == 1)
-        __builtin_amdgcn_s_waitcnt(0x0F76);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | vm_field(1));
     else
         __builtin_amdgcn_s_waitcnt(0x0F70);
 }
@@ -92,7 +101,7 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
 
     // die x (workgroups x, x + 8, ...) takes tiles [x * per + min(x, rem), ...)
     const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
@@ -107,11 +116,12 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
     const u32x4 rb = make_rsrc(p.b + (int64_t)n0 * p.ldb, (uint32_t)(BN * p.ldb * 2));
 
     // loads: load m of wave w fills tile rows 16m .. 16m+15 of the wave's
-    // share (A: rows 64w + .., B: rows 32w + ..); lane l writes row 16m + l/4
-    // at physical chunk l % 4, so it fetches the logical chunk placed there.
-    // The swizzle does not depend on m; m moves 16 rows (a scalar offset).
+    // share (A: rows kRowsA w + .., B: rows kRowsB w + ..); lane l writes row
+    // 16m + l/4 at physical chunk l % 4, so it fetches the logical chunk placed
+    // there.  The swizzle does not depend on m; m moves 16 rows (a scalar
+    // offset).
     const int q = lane >> 2, pch = lane & 3;
-    const int r_a = 64 * wave + q, r_b = 32 * wave + q;
+    const int r_a = kRowsA * wave + q, r_b = kRowsB * wave + q;
     const uint32_t voa = (uint32_t)(r_a * p.lda * 2) + (chunk_of(r_a, pch) << 4);
     const uint32_t vob = (uint32_t)(r_b * p.ldb * 2) + (chunk_of(r_b, pch) << 4);
     const uint32_t a16 = uniu((uint32_t)(16 * p.lda * 2)), b16 = uniu((uint32_t)(16 * p.ldb * 2));
@@ -121,10 +131,10 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
         const uint32_t kb = (uint32_t)kt * (BK * 2);
 #pragma unroll
         for (int m = 0; m < kLoadsA; ++m)
-            dma16(ra, uniu(st + (uint32_t)((64 * wave + 16 * m) * kRow)), voa, uniu(kb + m * a16));
+            dma16(ra, uniu(st + (uint32_t)((kRowsA * wave + 16 * m) * kRow)), voa, uniu(kb + m * a16));
 #pragma unroll
         for (int m = 0; m < kLoadsB; ++m)
-            dma16(rb, uniu(st + (uint32_t)(kABytes + (32 * wave + 16 * m) * kRow)), vob, uniu(kb + m * b16));
+            dma16(rb, uniu(st + (uint32_t)(kABytes + (kRowsB * wave + 16 * m) * kRow)), vob, uniu(kb + m * b16));
     };
 
     // fragments: lane l reads row (block base) + l % 32 at logical chunk
@@ -133,13 +143,13 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
     // address XOR (s << 5)
     const uint32_t qq = (uint32_t)((l32 >> 2) & 3);
     const uint32_t fa = (uint32_t)((wm * 128 + l32) * kRow) + (((uint32_t)h ^ qq) << 4);
-    const uint32_t fb = (uint32_t)(kABytes + (wn * 64 + l32) * kRow) + (((uint32_t)h ^ qq) << 4);
+    const uint32_t fb = (uint32_t)(kABytes + (wn * kWaveN + l32) * kRow) + (((uint32_t)h ^ qq) << 4);
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][kBJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kBJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -156,15 +166,15 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
         for (int s = 0; s < BK / 16; ++s) {
             const uint32_t xa = (st + fa) ^ (uint32_t)(s << 5);
             const uint32_t xb = (st + fb) ^ (uint32_t)(s << 5);
-            bf16x8 af[4], bfr[2];
+            bf16x8 af[4], bfr[kBJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(xa + (uint32_t)(i * 32 * kRow));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = lds_read_b128(xb + (uint32_t)(j * 32 * kRow));
+            for (int j = 0; j < kBJ; ++j) bfr[j] = lds_read_b128(xb + (uint32_t)(j * 32 * kRow));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < kBJ; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     }
 
@@ -175,8 +185,8 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
     // between its own writes and reads.)
     lds_sync();
     float* stg = reinterpret_cast<float*>(smem) + wave * kPassRows * kPitch;
-    const int c8 = (lane & 7) * 8;
-    const int n = n0 + wn * 64 + c8;
+    const int c8 = (lane % kColGroups) * 8;
+    const int n = n0 + wn * kWaveN + c8;
     float bias[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) bias[k] = 0.0f;
@@ -189,14 +199,14 @@ __global__ void __launch_bounds__(kThreads, kWgPerCu) gemm_bf16_kernel(Params p)
 #pragma unroll
     for (int i = 0; i < kPassRows / 32; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kBJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 stg[(32 * i + 8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + 32 * j + l32] =
                     acc[pass * (kPassRows / 32) + i][j][r];
 #pragma unroll 4
-    for (int it = 0; it < kPassRows / 8; ++it) {
-        const int rr = 8 * it + (lane >> 3);
+    for (int it = 0; it < kPassRows * kColGroups / 64; ++it) {
+        const int rr = (64 / kColGroups) * it + lane / kColGroups;
         const int64_t m = m0 + wm * 128 + kPassRows * pass + rr;
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(stg + rr * kPitch + c8);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(stg + rr * kPitch + c8 + 4);
