@@ -23,8 +23,9 @@
 //     gradients do not depend on which workgroup took which item).  LDS float
 //     atomics are slow, so the common cases avoid them per element: a block
 //     of history rows sums its 63 position diagonals through a skewed LDS
-//     scratch, and a block spanning at most four time buckets sums them in
-//     registers; one atomic per bucket then adds each sum.
+//     scratch, a block of candidate rows (one position) sums its key columns
+//     across the lanes, and a block spanning at most four time buckets sums
+//     them in registers; one atomic per bucket then adds each sum.
 //   * attn_bwd_dkv_kernel: one work item = 128 keys x 1 head (a key-major
 //     work list: the 32-row query tiles that see the keys).  Per query tile:
 //     S = Q K^T and dO V^T with K and V in registers, then dV += A^T dO and
@@ -524,14 +525,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             // plain LDS writes and reads, take one atomic each (LDS float
             // atomics are slow).  Otherwise, and for time buckets beyond the
             // register sums, per element.
+            // When they are all candidate rows (all at position n), the bucket
+            // min(n - min(j, n), P - 1) depends on the key alone: the same
+            // scratch, unskewed, gives each key column's sum.
             const bool diag = !st.pos_clamped && wrow0 + 31 < n;
-            if (diag) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    scratch[(l32 + 31 - c) * kDiagPitch + l32] = gv[r];
-                }
-                // lane u: diagonal rho - c = u - 31 (cells off the band are 0)
+            const bool colwise = !st.pos_clamped && wrow0 >= n;
+            auto row_sum = [&]() {
+                // lane u sums row u of the wave's scratch (32 floats)
                 float dsum = 0.0f;
                 const f32x4* col = reinterpret_cast<const f32x4*>(scratch + lane * kDiagPitch);
 #pragma unroll
@@ -542,10 +542,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                     dsum += x[2];
                     dsum += x[3];
                 }
+                return dsum;
+            };
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    scratch[(l32 + 31 - c) * kDiagPitch + l32] = gv[r];
+                }
+                // lane u: diagonal rho - c = u - 31 (cells off the band are 0)
+                const float dsum = row_sum();
                 const int pb = wrow0 - st.j0 + lane - 31;
                 if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
+            } else if (colwise) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    scratch[c * kDiagPitch + l32] = gv[r];
+                }
+                // lane u < 32: key column u
+                const float dsum = row_sum();
+                const int pb = n - min(st.j0 + lane, n);
+                if (lane < 32 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             }
-            if (!st.pos_clamped && !diag) {
+            if (!st.pos_clamped && !diag && !colwise) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if (gv[r] != 0.0f) {
