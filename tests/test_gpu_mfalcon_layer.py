@@ -164,6 +164,31 @@ def test_single_layer_ragged_rows():
     assert_close(got, ref, "bf16", "1-layer ragged X_out")
 
 
+def test_single_layer_biases_in_place():
+    """f1 and f2 with their biases, X_out written over X (the f2 epilogue reads
+    each residual element before it writes that element); rows span two GEMM
+    row tiles with a ragged tail."""
+    import torch
+    from hstu_sequential_transducer_causal_amd import ops
+    x = synth.make_layer_stack(53, [1, 300, 77], H=4, d=128, D=512, layers=1, P=1024, NT=32,
+                               alpha=1 / 256)
+    rng = np.random.default_rng(54)
+    b1 = rng.normal(0, 0.2, size=4 * x.H * x.d).astype(np.float32)
+    b2 = rng.normal(0, 0.2, size=x.x.shape[1]).astype(np.float32)
+    xd = dev_tensor(x.x, "bf16")
+    out = ops.hstu_layer_fwd(xd, dev_tensor(x.w1[0], "bf16"), dev_tensor(x.w2[0], "bf16"),
+                             torch.from_numpy(x.offsets.astype(np.int32)).cuda(),
+                             torch.from_numpy(x.ts).cuda(), torch.from_numpy(x.rab_pos[0]).cuda(),
+                             torch.from_numpy(x.rab_time[0]).cuda(), x.alpha, H=x.H, d=x.d,
+                             max_seq_len=int(np.diff(x.offsets).max()), b1=torch.from_numpy(b1).cuda(),
+                             b2=torch.from_numpy(b2).cuda(), ln_eps=x.eps, x_out=xd)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == xd.data_ptr()
+    ref = oracle.layer(x.x, x.w1[0], x.w2[0], x.offsets, x.ts, x.rab_pos[0], x.rab_time[0], x.alpha,
+                       x.H, x.d, b1=b1, b2=b2, eps=x.eps)
+    assert_close(host_f32(xd), ref, "bf16", "1-layer biases, in place")
+
+
 def test_layer_stack_full_size_sampled_sequences():
     x = synth.config(5)
     log(f"cfg5 full: B={x.B} T={x.T}")
