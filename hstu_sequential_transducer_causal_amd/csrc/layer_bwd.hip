@@ -31,6 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kStages = 3;
 constexpr int kSumChunks = 64;
+constexpr int kTnWgPerCu = 2;     // gemm_tn_kernel workgroups resident per CU (48 KiB of LDS each)
 
 struct TnParams {
     const uint16_t* a; int64_t lda;   // [T, M]
@@ -66,7 +67,7 @@ __device__ __forceinline__ void wait_loads(int n) {
 
 // 128 x 128 output tile per workgroup; wave w computes rows 64 (w / 2) ..,
 // columns 64 (w % 2) .. as 2 x 2 blocks of 32 x 32.
-__global__ void __launch_bounds__(kThreads, 2) gemm_tn_kernel(TnParams p) {
+__global__ void __launch_bounds__(kThreads, kTnWgPerCu) gemm_tn_kernel(TnParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring_a[kStages * kTileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t ring_b[kStages * kTileBytes];
     const int lane = threadIdx.x & 63;
@@ -205,7 +206,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* in, int 
 int gemm_tn_splits(int64_t T, int M, int N) {
     const int tiles = (M / 128) * (N / 128);
     const int64_t tok_tiles = (T + 31) / 32;
-    int s = (2 * device_cu_count() + tiles - 1) / max(tiles, 1);
+    int s = (kTnWgPerCu * device_cu_count() + tiles - 1) / max(tiles, 1);
     s = (int)std::min<int64_t>(std::max(1, s), std::max<int64_t>(1, tok_tiles));
     return std::min(s, 64);
 }
