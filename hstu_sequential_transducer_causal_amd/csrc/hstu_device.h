@@ -1,13 +1,7 @@
 // hstu_device.h -- device-side building blocks shared by the gfx950 kernels.
 //
-// CDNA4 facts the kernels rely on:
-//   * wavefronts are 64 lanes;
-//   * v_mfma_f32_16x16x32_bf16 (builtin __builtin_amdgcn_mfma_f32_16x16x32_bf16):
-//       A operand: lane l holds row (l % 16), 8 consecutive k values of group l / 16;
-//       B operand: lane l holds column (l % 16), the same 8 k values of group l / 16;
-//       C/D      : lane l holds column (l % 16), rows 4 * (l / 16) + 0..3.
-//     Only the pairing of A and B k-slots matters for the product, and both
-//     operands use the same slot order, so any consistent k order is valid.
+// Wavefronts are 64 lanes; the MFMA layouts the kernels use are described
+// with the 32x32x16 helper in tile_ops.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,10 +16,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // SiLU(x) = x / (1 + 2^(-x log2 e)) with the hardware exp2 and reciprocal
 // (both ~1 ulp).  x -> -inf gives -0, x -> +inf gives x.
