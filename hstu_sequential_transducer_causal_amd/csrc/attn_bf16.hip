@@ -559,7 +559,23 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             read_v(it);
         };
 
-        if (ntiles > 0) {
+        // The tile list runs over keys in increasing order, so the tiles past
+        // the one holding this wave's last valid row hold no pair its rows
+        // see (a history row sees keys up to itself, a candidate the history
+        // and itself): the wave computes the first nuse tiles of the piece and
+        // only keeps the ring going (barriers and its share of the loads) for
+        // the rest.
+        int nuse = ntiles;
+        if (wrow0 >= Lq) {
+            nuse = 0;
+        } else if (!kCross) {
+            const int kt_last = min(wrow0 + 31, L - 1) / BN;
+            const int pos_last = kt_last < a_end ? kt_last : a_end + (kt_last - kb_begin);
+            nuse = min(ntiles, max(0, pos_last + 1 - p0));
+        }
+        nuse = uni(nuse);
+
+        if (nuse > 0) {
             f32x16 accA, accB;
             float caddA = 0.0f, caddB = 0.0f;
             // prologue: S(0), V(0)
@@ -574,11 +590,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 read_v(0);
             }
             int it = 1;
-            for (; it + 1 < ntiles; it += 2) {
+            for (; it + 1 < nuse; it += 2) {
                 step(it, accA, caddA, accB, caddB);
                 step(it + 1, accB, caddB, accA, caddA);
             }
-            if (it < ntiles) {
+            if (it < nuse) {
                 step(it, accA, caddA, accB, caddB);
                 accA = accB;
                 caddA = caddB;
@@ -591,12 +607,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int r = 0; r < 16; ++r) act_one(accA, c2, r);
             }
             u32x4 pk[2];
-            tile_pack(ntiles - 1, accA, pk);
+            tile_pack(nuse - 1, accA, pk);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
                     oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
+        }
+        for (int it = nuse; it < ntiles; ++it) {
+            tile_sync(it);
+            issue_rest(it);
         }
 
         // ---------- O = alpha * acc, rows < L only: bf16 into O, or fp32 into
