@@ -619,8 +619,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             issue_rest(it);
         }
 
-        // ---------- O = alpha * acc, rows < L only: bf16 into O, or fp32 into
-        //            the piece's partial slot when the row block is split
+        // ---------- O = alpha * acc, rows < L only: bf16 into O (non-temporal:
+        //            the epilogue reads it once, and the tiles the other items
+        //            still read keep the caches), or fp32 into the piece's
+        //            partial slot when the row block is split
         // lane holds O[row 8 (r / 4) + 4 h2 + r % 4][d = nb * 32 + l32]
         if (slot < 0) {
 #pragma unroll
@@ -629,7 +631,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 if (ro < Lq) {
                     uint16_t* op = p.o + (row0q + ro) * p.os + h * HD + l32;
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(alpha_eff * oacc[nb][r]);
+                    for (int nb = 0; nb < 4; ++nb) __builtin_nontemporal_store(f32_to_bf16_bits(alpha_eff * oacc[nb][r]), op + nb * 32);
                 }
             }
         } else {
