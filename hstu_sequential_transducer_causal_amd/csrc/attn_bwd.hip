@@ -674,6 +674,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             finish(stA, gv);
         }
 
+        // ---- (gradient rows are written once: non-temporal stores, which
+        //      leave the caches to the tiles other items still read)
         // ---- dQ = alpha * acc for rows < L; lane holds column nb*32 + l32 at
         //      rows wrow0 + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
@@ -682,7 +684,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             if (ro < L) {
                 uint16_t* op = p.dq + (row0 + ro) * p.dqs + h * HD + l32;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) op[nb * 32] = f32_to_bf16_bits(p.alpha * dqa[nb][r]);
+                for (int nb = 0; nb < 4; ++nb) __builtin_nontemporal_store(f32_to_bf16_bits(p.alpha * dqa[nb][r]), op + nb * 32);
             }
         }
         // ---- this item's table-gradient histogram -> its partial row
@@ -1014,8 +1016,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
                 uint16_t* vp = p.dv + (row0 + ko) * p.dvs + h * HD + l32;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
-                    kp[nb * 32] = f32_to_bf16_bits(p.alpha * dka[nb][r]);
-                    vp[nb * 32] = f32_to_bf16_bits(p.alpha * dva[nb][r]);
+                    __builtin_nontemporal_store(f32_to_bf16_bits(p.alpha * dka[nb][r]), kp + nb * 32);
+                    __builtin_nontemporal_store(f32_to_bf16_bits(p.alpha * dva[nb][r]), vp + nb * 32);
                 }
             }
         }
