@@ -226,7 +226,7 @@ def bwd_record(x, dev, steps):
 class LayerBwdCase:
     """Gradients of one layer (layer 0 of the stack workload) from dLoss/dX_out."""
 
-    def __init__(self, x, dev):
+    def __init__(self, x, dev, saved=False):
         import torch
         import hstu_synth as synth
         from hstu_sequential_transducer_causal_amd import ops
@@ -250,14 +250,28 @@ class LayerBwdCase:
                                     drab_pos=self.out["drab_pos"], drab_time=self.out["drab_time"])
         self.args = a
         self.ws = torch.empty(max(1, ops.layer_bwd_workspace_bytes(a)), dtype=torch.uint8, device=dev)
+        self.saved = None
+        if saved:
+            # the training forward keeps Z, the pre-activation, O and Y (untimed)
+            kw = dict(H=x.H, d=x.d, max_seq_len=self.max_len)
+            need = ops.layer_saved_bytes(self.xin, self.w1, self.w2, self.off, self.ts, self.rp, self.rt,
+                                         x.alpha, **kw)
+            self.saved = torch.empty(need, dtype=torch.uint8, device=dev)
+            ops.hstu_layer_fwd(self.xin, self.w1, self.w2, self.off, self.ts, self.rp, self.rt, x.alpha,
+                               saved=self.saved, **kw)
+            torch.cuda.synchronize()
 
     def step(self, ev0=None, ev1=None):
         import ctypes
         import torch
         from hstu_sequential_transducer_causal_amd import _lib
         lib = _lib.load()
-        _lib.check(lib.hstu_layer_bwd(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(),
-                                      torch.cuda.current_stream().cuda_stream))
+        stream = torch.cuda.current_stream().cuda_stream
+        if self.saved is None:
+            _lib.check(lib.hstu_layer_bwd(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(), stream))
+        else:
+            _lib.check(lib.hstu_layer_bwd_saved(ctypes.byref(self.args), self.saved.data_ptr(), self.saved.numel(),
+                                                self.ws.data_ptr(), self.ws.numel(), stream))
 
 
 class CachedCase:
@@ -675,6 +689,16 @@ def main():
                                   "weight/data products of f1 and f2; the recomputed forward not counted"}
         others[xl.name + "_layer0_bwd"] = rec
         log(f"{xl.name} layer-0 gradients: {rec}")
+        del c
+        torch.cuda.empty_cache()
+        c = LayerBwdCase(xl, dev, saved=True)
+        st, _ = time_case(c, max(2, args.steps // 10), 1, core_events=False)
+        rec = {"ms_per_step": round(st, 4), "tflops": round(lf / (st * 1e-3) / 1e12, 2),
+               "saved_mib": round(c.saved.numel() / 2**20, 1),
+               "flop_convention": "as the recomputing gradients; Z, the pre-activation, O and Y kept by "
+                                  "hstu_layer_fwd_saved instead of recomputed"}
+        others[xl.name + "_layer0_bwd_saved"] = rec
+        log(f"{xl.name} layer-0 gradients from saved activations: {rec}")
         del c
         torch.cuda.empty_cache()
         for w in (3, 4):

@@ -176,6 +176,7 @@ EXPORTS = [
     "hstu_mfalcon_layer_workspace_bytes", "mfalcon_layer_score",
     "hstu_attn_bwd_workspace_bytes", "hstu_attn_bwd",
     "hstu_layer_bwd_workspace_bytes", "hstu_layer_bwd",
+    "hstu_layer_saved_bytes", "hstu_layer_fwd_saved", "hstu_layer_bwd_saved",
     "hstu_stochastic_length",
     "hstu_attn_schedule",
 ]
@@ -231,6 +232,13 @@ def load(path: str = LIB_PATH):
     lib.hstu_layer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(LayerBwdArgs)]
     lib.hstu_layer_bwd.restype = _i32
     lib.hstu_layer_bwd.argtypes = [ctypes.POINTER(LayerBwdArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_layer_saved_bytes.restype = ctypes.c_size_t
+    lib.hstu_layer_saved_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
+    lib.hstu_layer_fwd_saved.restype = _i32
+    lib.hstu_layer_fwd_saved.argtypes = [ctypes.POINTER(LayerArgs), _vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp]
+    lib.hstu_layer_bwd_saved.restype = _i32
+    lib.hstu_layer_bwd_saved.argtypes = [ctypes.POINTER(LayerBwdArgs), _vp, ctypes.c_size_t, _vp, ctypes.c_size_t,
+                                         _vp]
     lib.hstu_stochastic_length.restype = _i32
     lib.hstu_stochastic_length.argtypes = [ctypes.POINTER(SlArgs), _vp]
     lib.hstu_attn_schedule.restype = _i32

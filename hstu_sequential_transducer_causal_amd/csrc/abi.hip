@@ -642,6 +642,24 @@ struct LayerBwdWs {
     size_t z, pre, o, y, dy, dz, w1t, w2t, sched, attn, part, colsum, total;
 };
 
+// A training forward's saved activations: Z, f1's pre-activation, O, Y (bf16),
+// laid out as the first four regions of the gradient workspace.
+struct LayerSaved {
+    size_t z, pre, o, y, total;
+};
+
+LayerSaved layer_saved(const hstu_layer_args* l) {
+    const size_t T = size_t(l->num_rows);
+    const size_t hd = size_t(l->H) * l->d, zw = 4 * hd;
+    LayerSaved v;
+    v.z = 0;
+    v.pre = align256(v.z + T * zw * 2);
+    v.o = align256(v.pre + T * zw * 2);
+    v.y = align256(v.o + T * hd * 2);
+    v.total = align256(v.y + T * hd * 2);
+    return v;
+}
+
 LayerBwdWs layer_bwd_ws(const hstu_layer_bwd_args* g) {
     const hstu_layer_args* l = &g->layer;
     LayerBwdWs w;
@@ -683,19 +701,32 @@ size_t hstu_layer_workspace_bytes(const hstu_layer_args* l) {
     return layer_ws(l).total;
 }
 
-hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// One layer forward; with `saved`, Z, O and Y live there and f1 also writes
+// its pre-activation there (what the gradients need).
+hstu_status layer_fwd_run(const hstu_layer_args* l, void* ws, size_t ws_bytes, void* stream_, void* saved,
+                          size_t saved_bytes) {
     hstu_status st = validate_layer(l);
     if (st != HSTU_OK) return st;
     if (l->B == 0 || l->num_rows == 0) return ok();
     const LayerWs lw = layer_ws(l);
     st = check_workspace(ws, ws_bytes, lw.total);
     if (st != HSTU_OK) return st;
+    const LayerSaved sv = layer_saved(l);
+    if (saved) {
+        st = check_workspace(saved, saved_bytes, sv.total);
+        if (st != HSTU_OK) return st;
+    }
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     uint8_t* w = static_cast<uint8_t*>(ws);
+    uint8_t* sb = static_cast<uint8_t*>(saved);
     const int hd = l->H * l->d;
-    uint16_t* z = reinterpret_cast<uint16_t*>(w + lw.z);
-    uint16_t* o = reinterpret_cast<uint16_t*>(w + lw.o);
-    uint16_t* y = reinterpret_cast<uint16_t*>(w + lw.y);
+    uint16_t* z = reinterpret_cast<uint16_t*>(saved ? sb + sv.z : w + lw.z);
+    uint16_t* o = reinterpret_cast<uint16_t*>(saved ? sb + sv.o : w + lw.o);
+    uint16_t* y = reinterpret_cast<uint16_t*>(saved ? sb + sv.y : w + lw.y);
 
     // f1 + SiLU: Z = SiLU(X W1^T + b1) -> U | V | Q | K
     hstu::GemmArgs g1;
@@ -706,6 +737,10 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     g1.residual = nullptr; g1.ldr = 0;
     g1.c = z; g1.ldc = 4 * hd;
     g1.silu = 1;
+    if (saved) {
+        g1.c_pre = sb + sv.pre;
+        g1.ldcp = 4 * hd;
+    }
     hipError_t e = hstu::launch_gemm_bf16(g1, stream);
     if (e != hipSuccess) return device_error(e, "f1 launch");
 
@@ -730,6 +765,30 @@ hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, 
     e = hstu::launch_gemm_bf16(g2, stream);
     if (e != hipSuccess) return device_error(e, "f2 launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status hstu_layer_fwd(const hstu_layer_args* l, void* ws, size_t ws_bytes, void* stream) {
+    return layer_fwd_run(l, ws, ws_bytes, stream, nullptr, 0);
+}
+
+size_t hstu_layer_saved_bytes(const hstu_layer_args* l) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_layer(l);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return layer_saved(l).total;
+}
+
+hstu_status hstu_layer_fwd_saved(const hstu_layer_args* l, void* saved, size_t saved_bytes, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    if (l && l->struct_size == sizeof(hstu_layer_args) && l->B > 0 && l->num_rows > 0 && !saved)
+        return fail(HSTU_ERR_ARG, "saved is NULL");
+    return layer_fwd_run(l, ws, ws_bytes, stream, saved, saved_bytes);
 }
 
 size_t hstu_mfalcon_layer_workspace_bytes(const hstu_mfalcon_layer_args* m) {
@@ -890,7 +949,14 @@ size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* g) {
     return layer_bwd_ws(g).total;
 }
 
-hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_bytes, void* stream_) {
+}  // extern "C"
+
+namespace {
+
+// Layer gradients; with `saved` (a training forward's activations) Z, its
+// pre-activation, O and Y are read from there instead of recomputed.
+hstu_status layer_bwd_run(const hstu_layer_bwd_args* g, void* ws, size_t ws_bytes, void* stream_,
+                          const void* saved, size_t saved_bytes) {
     hstu_status st = validate_layer_bwd(g);
     if (st != HSTU_OK) return st;
     const hstu_layer_args* l = &g->layer;
@@ -919,6 +985,17 @@ hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_byt
     uint16_t* pre = reinterpret_cast<uint16_t*>(w + lw.pre);
     uint16_t* o = reinterpret_cast<uint16_t*>(w + lw.o);
     uint16_t* y = reinterpret_cast<uint16_t*>(w + lw.y);
+    if (saved) {
+        const LayerSaved sv = layer_saved(l);
+        st = check_workspace(const_cast<void*>(saved), saved_bytes, sv.total);
+        if (st != HSTU_OK) return st;
+        // (read only below: the gradients never write the saved activations)
+        uint8_t* sb = static_cast<uint8_t*>(const_cast<void*>(saved));
+        z = reinterpret_cast<uint16_t*>(sb + sv.z);
+        pre = reinterpret_cast<uint16_t*>(sb + sv.pre);
+        o = reinterpret_cast<uint16_t*>(sb + sv.o);
+        y = reinterpret_cast<uint16_t*>(sb + sv.y);
+    }
     uint16_t* dy = reinterpret_cast<uint16_t*>(w + lw.dy);
     uint16_t* dz = reinterpret_cast<uint16_t*>(w + lw.dz);
     uint16_t* w1t = reinterpret_cast<uint16_t*>(w + lw.w1t);
@@ -926,24 +1003,27 @@ hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_byt
     float* part = reinterpret_cast<float*>(w + lw.part);
     float* cpart = reinterpret_cast<float*>(w + lw.colsum);
 
-    // forward recomputation: Z and its pre-activation, then O and Y
-    hstu::GemmArgs g1;
-    g1.M = T; g1.N = zw; g1.K = D;
-    g1.a = l->x; g1.lda = D;
-    g1.b = l->w1; g1.ldb = D;
-    g1.bias = l->b1;
-    g1.residual = nullptr; g1.ldr = 0;
-    g1.c = z; g1.ldc = zw;
-    g1.silu = 1;
-    g1.c_pre = pre; g1.ldcp = zw;
-    hipError_t e = hstu::launch_gemm_bf16(g1, stream);
-    if (e != hipSuccess) return device_error(e, "f1 launch");
-    hstu_attn_args a = layer_attn_args(l, z, o, y);
-    Sched s = carve_sched(&a, ws, lw.sched);
-    e = run_sched(&a, s, stream);
-    if (e == hipSuccess) e = run_core(&a, s, stream);
-    if (e == hipSuccess) e = run_ln_gate(&a, s, nullptr, nullptr, 0, false, stream);
-    if (e != hipSuccess) return device_error(e, "attention launch");
+    hipError_t e = hipSuccess;
+    if (!saved) {
+        // forward recomputation: Z and its pre-activation, then O and Y
+        hstu::GemmArgs g1;
+        g1.M = T; g1.N = zw; g1.K = D;
+        g1.a = l->x; g1.lda = D;
+        g1.b = l->w1; g1.ldb = D;
+        g1.bias = l->b1;
+        g1.residual = nullptr; g1.ldr = 0;
+        g1.c = z; g1.ldc = zw;
+        g1.silu = 1;
+        g1.c_pre = pre; g1.ldcp = zw;
+        e = hstu::launch_gemm_bf16(g1, stream);
+        if (e != hipSuccess) return device_error(e, "f1 launch");
+        hstu_attn_args a = layer_attn_args(l, z, o, y);
+        Sched s = carve_sched(&a, ws, lw.sched);
+        e = run_sched(&a, s, stream);
+        if (e == hipSuccess) e = run_core(&a, s, stream);
+        if (e == hipSuccess) e = run_ln_gate(&a, s, nullptr, nullptr, 0, false, stream);
+        if (e != hipSuccess) return device_error(e, "attention launch");
+    }
 
     // f2: dY = dX_out W2 (through W2^T), dW2 = dX_out^T Y, db2 = sum_t dX_out
     e = hstu::launch_transpose(l->w2, D, hd, w2t, stream);
@@ -999,6 +1079,21 @@ hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_byt
     e = hstu::launch_gemm_bf16(gx, stream);
     if (e != hipSuccess) return device_error(e, "dX launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* g, void* ws, size_t ws_bytes, void* stream) {
+    return layer_bwd_run(g, ws, ws_bytes, stream, nullptr, 0);
+}
+
+hstu_status hstu_layer_bwd_saved(const hstu_layer_bwd_args* g, const void* saved, size_t saved_bytes, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    if (g && g->struct_size == sizeof(hstu_layer_bwd_args) && g->layer.B > 0 && g->layer.num_rows > 0 && !saved)
+        return fail(HSTU_ERR_ARG, "saved is NULL");
+    return layer_bwd_run(g, ws, ws_bytes, stream, saved, saved_bytes);
 }
 
 size_t hstu_attn_bwd_workspace_bytes(const hstu_attn_bwd_args* g) {

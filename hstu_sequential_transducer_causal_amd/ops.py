@@ -352,8 +352,10 @@ def mfalcon_layer_score(x, w1, seq_offsets, num_candidates, timestamps, rab_pos,
 
 def hstu_layer_fwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int,
                    d: int, max_seq_len: int, b1=None, b2=None, num_candidates=None,
-                   ln_eps: float = 1e-5, x_out=None, workspace=None, stream=None):
-    """One HSTU layer (f1 + SiLU, attention, LN * U, f2 + residual); returns X_out."""
+                   ln_eps: float = 1e-5, x_out=None, workspace=None, saved=None, stream=None):
+    """One HSTU layer (f1 + SiLU, attention, LN * U, f2 + residual); returns X_out.
+    With `saved` (a uint8 device tensor of layer_saved_bytes() bytes) the
+    activations the gradients need are kept there (hstu_layer_fwd_saved)."""
     lib = _lib.load()
     if x_out is None:
         x_out = torch.empty_like(x)
@@ -363,9 +365,21 @@ def hstu_layer_fwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha,
     need = lib.hstu_layer_workspace_bytes(ctypes.byref(l))
     if workspace is None:
         workspace = _empty_ws(need, x.device)
-    _lib.check(lib.hstu_layer_fwd(ctypes.byref(l), workspace.data_ptr(), workspace.numel(),
-                                  _stream_ptr(stream)))
+    if saved is None:
+        _lib.check(lib.hstu_layer_fwd(ctypes.byref(l), workspace.data_ptr(), workspace.numel(),
+                                      _stream_ptr(stream)))
+    else:
+        _lib.check(lib.hstu_layer_fwd_saved(ctypes.byref(l), saved.data_ptr(), saved.numel(),
+                                            workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
     return x_out
+
+
+def layer_saved_bytes(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, *, H: int, d: int,
+                      max_seq_len: int, num_candidates=None) -> int:
+    """Bytes of the buffer hstu_layer_fwd_saved keeps the activations in."""
+    l = make_layer_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, H=H, d=d,
+                        max_seq_len=max_seq_len, x_out=x, num_candidates=num_candidates)
+    return int(_lib.load().hstu_layer_saved_bytes(ctypes.byref(l)))
 
 
 def make_layer_bwd_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out, *,
@@ -392,7 +406,7 @@ def layer_bwd_workspace_bytes(g: _lib.LayerBwdArgs) -> int:
 def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out, *, H: int,
                    d: int, max_seq_len: int, b1=None, b2=None, num_candidates=None,
                    ln_eps: float = 1e-5, want_bias: bool = True, want_rab: bool = True, dx=None,
-                   workspace=None, stream=None):
+                   workspace=None, saved=None, stream=None):
     """Gradients of one HSTU layer for dLoss/dX_out: returns a dict with dx
     (bf16 [rows, D]), dw1 [4Hd, D], dw2 [D, Hd] and, if asked for, db1, db2,
     drab_pos, drab_time (all float32)."""
@@ -416,8 +430,12 @@ def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha,
         _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), None, 0, _stream_ptr(stream)))
     if workspace is None:
         workspace = _empty_ws(need, dev)
-    _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), workspace.data_ptr(), workspace.numel(),
-                                  _stream_ptr(stream)))
+    if saved is None:
+        _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), workspace.data_ptr(), workspace.numel(),
+                                      _stream_ptr(stream)))
+    else:   # the activations a training forward kept (hstu_layer_bwd_saved)
+        _lib.check(lib.hstu_layer_bwd_saved(ctypes.byref(g), saved.data_ptr(), saved.numel(),
+                                            workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
     return out
 
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 7
+#define HSTU_ABI_VERSION 8
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -368,6 +368,27 @@ size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* args);
 
 hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* args, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* The same layer and gradients with the forward's activations kept instead
+ * of recomputed (the section above): hstu_layer_fwd_saved computes what
+ * hstu_layer_fwd computes and also writes, into the caller's buffer `saved`
+ * (device, 16-byte aligned, hstu_layer_saved_bytes() bytes), Z = SiLU(X W1^T
+ * + b1) (U | V | Q | K), the pre-activation X W1^T + b1, O and Y (bf16,
+ * num_rows rows each, about 2 * (2 * 4*H*d + 2 * H*d) bytes per row);
+ * hstu_layer_bwd_saved computes what hstu_layer_bwd computes from them,
+ * reading `saved` only, without running f1, the attention or the gate
+ * forward again.  Both calls must see the same layer arguments, weights and
+ * inputs.  Workspaces: hstu_layer_workspace_bytes and
+ * hstu_layer_bwd_workspace_bytes.  Errors: as hstu_layer_fwd and
+ * hstu_layer_bwd; HSTU_ERR_ARG for a NULL `saved` with a non-empty batch,
+ * HSTU_ERR_WORKSPACE for a misaligned or too small one. */
+size_t hstu_layer_saved_bytes(const hstu_layer_args* args);
+
+hstu_status hstu_layer_fwd_saved(const hstu_layer_args* args, void* saved, size_t saved_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+hstu_status hstu_layer_bwd_saved(const hstu_layer_bwd_args* args, const void* saved, size_t saved_bytes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------ stochastic length */
 /* Stochastic length on the device ("行动胜于言语：万亿参数序列转导器用于生成式

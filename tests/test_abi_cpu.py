@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 7
+    assert lib.hstu_abi_version() == 8
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -288,6 +288,31 @@ def test_layer_bwd_workspace_errors(lib):
     assert need >= 3 * 200 * 2048 * 2
     assert lib.hstu_layer_bwd(ctypes.byref(g), None, 0, None) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_layer_bwd(ctypes.byref(g), 0x20000, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
+
+
+def test_layer_saved_pair_errors(lib):
+    """The training pair checks its saved-activation buffer before any launch:
+    Z and the pre-activation (rows x 4Hd bf16), O and Y (rows x Hd bf16)."""
+    g = _valid_layer_bwd()
+    l = g.layer
+    l.x_out = 0x10000
+    need_saved = lib.hstu_layer_saved_bytes(ctypes.byref(l))
+    assert need_saved == 2 * 200 * 2048 * 2 + 2 * 200 * 512 * 2
+    ws_f = lib.hstu_layer_workspace_bytes(ctypes.byref(l))
+    ws_b = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(g))
+    assert lib.hstu_layer_fwd_saved(ctypes.byref(l), None, 0, 0x20000, ws_f, None) == _lib.HSTU_ERR_ARG
+    assert lib.hstu_layer_fwd_saved(ctypes.byref(l), 0x30000, need_saved - 1, 0x20000, ws_f,
+                                    None) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_layer_fwd_saved(ctypes.byref(l), 0x30008, need_saved, 0x20000, ws_f,
+                                    None) == _lib.HSTU_ERR_WORKSPACE   # misaligned
+    assert lib.hstu_layer_bwd_saved(ctypes.byref(g), None, 0, 0x20000, ws_b, None) == _lib.HSTU_ERR_ARG
+    assert lib.hstu_layer_bwd_saved(ctypes.byref(g), 0x30000, need_saved - 1, 0x20000, ws_b,
+                                    None) == _lib.HSTU_ERR_WORKSPACE
+    # invalid layer arguments: no size, and the plain calls' errors
+    l.struct_size = 4
+    assert lib.hstu_layer_saved_bytes(ctypes.byref(l)) == 0
+    assert lib.hstu_layer_fwd_saved(ctypes.byref(l), 0x30000, need_saved, 0x20000, ws_f,
+                                    None) == _lib.HSTU_ERR_ARG
 
 
 def _valid_sl():

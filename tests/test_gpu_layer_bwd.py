@@ -117,3 +117,39 @@ def test_layer_bwd_full_size_first_layer():
     pa, pb = _run(xa, g[ra]), _run(xb, g[rb])
     for k in ("dw1", "db1", "dw2", "db2", "drab_pos", "drab_time"):
         assert_close(full[k], pa[k].astype(np.float64) + pb[k], "bf16", f"cfg5 {k} = sum of halves")
+
+
+def test_layer_saved_pair_equals_recomputation():
+    """hstu_layer_fwd_saved gives hstu_layer_fwd's X_out bit for bit, and
+    hstu_layer_bwd_saved (reading the kept Z, pre-activation, O, Y) gives
+    hstu_layer_bwd's gradients bit for bit (both run the same kernels on the
+    same inputs; the saved pair only skips the recomputation)."""
+    import torch
+    from hstu_sequential_transducer_causal_amd import ops
+    x = synth.make_layer_stack(75, [1, 300, 77, 512], H=4, d=128, D=512, layers=1, P=1024, NT=32,
+                               alpha=1 / 512)
+    b1, b2 = (torch.from_numpy(b.astype(np.float32)).cuda() for b in _biases(x, 76))
+    g = synth.upstream_grad(77, x.x.shape)
+    xd = dev_tensor(x.x, "bf16")
+    w1, w2 = dev_tensor(x.w1[0], "bf16"), dev_tensor(x.w2[0], "bf16")
+    off = torch.from_numpy(x.offsets.astype(np.int32)).cuda()
+    ts = torch.from_numpy(x.ts).cuda()
+    rp, rt = torch.from_numpy(x.rab_pos[0]).cuda(), torch.from_numpy(x.rab_time[0]).cuda()
+    kw = dict(H=x.H, d=x.d, max_seq_len=int(np.diff(x.offsets).max()))
+    need = ops.layer_saved_bytes(xd, w1, w2, off, ts, rp, rt, x.alpha, **kw)
+    T, hd = x.x.shape[0], x.H * x.d
+    assert need >= 2 * T * 4 * hd * 2 + 2 * T * hd * 2
+    saved = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # stale bytes everywhere
+    plain = ops.hstu_layer_fwd(xd, w1, w2, off, ts, rp, rt, x.alpha, b1=b1, b2=b2, ln_eps=x.eps, **kw)
+    kept = ops.hstu_layer_fwd(xd, w1, w2, off, ts, rp, rt, x.alpha, b1=b1, b2=b2, ln_eps=x.eps, saved=saved,
+                              **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, kept)
+    gd = dev_tensor(g, "bf16")
+    ref = ops.hstu_layer_bwd(xd, w1, w2, off, ts, rp, rt, x.alpha, gd, b1=b1, b2=b2, ln_eps=x.eps, **kw)
+    got = ops.hstu_layer_bwd(xd, w1, w2, off, ts, rp, rt, x.alpha, gd, b1=b1, b2=b2, ln_eps=x.eps,
+                             saved=saved, **kw)
+    torch.cuda.synchronize()
+    for k in ("dx", "dw1", "db1", "dw2", "db2", "drab_pos", "drab_time"):
+        assert torch.equal(ref[k], got[k]), k
+    log(f"saved pair: {need / 2**20:.1f} MiB kept, X_out and all gradients identical")
