@@ -426,7 +426,8 @@ def test_attn_rows_equals_full_oracle_at_those_rows():
 
 def test_layer_scores_are_composition_of_library_routines():
     """The scoring layer: f1 (+ b1) by numpy matmul, SiLU by scipy's
-    logistic, the split U | V | Q | K, then the pinned M-FALCON scores; a
+    logistic, the split U | V | Q | K, then the scores by the library route
+    (pinned attention, torch's layer_norm, the gate, numpy's dot with w); a
     sequence without candidates and one of candidates only included."""
     from scipy.special import expit
     rng = np.random.default_rng(85)
@@ -446,6 +447,71 @@ def test_layer_scores_are_composition_of_library_routines():
     z = z * expit(z)
     hd = H * d
     U, V, Q, K = (z[:, i * hd:(i + 1) * hd].reshape(T, H, d) for i in range(4))
-    ref = oracle.mfalcon_score(Q, K, V, U, off, cands, ts, rp, rt, 0.05, w)
+    ref = _scores_by_library_route(Q, K, V, U, off, cands, ts, rp, rt, 0.05, w, 1e-5)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
     assert got.shape == (4, 6)
+
+
+# ---------------------------------------------------------------------------
+# M-FALCON scores
+# ---------------------------------------------------------------------------
+def _scores_by_library_route(q, k, v, u, off, cands, ts, rp, rt, alpha, w, eps):
+    """Scores without the oracle's score step: the pinned attention, torch's
+    layer_norm over the H*d_v values of a row, the U gate, then numpy's dot
+    with w at each candidate row n_b + c."""
+    import torch
+    T, H, d = q.shape
+    O = oracle.attn(q, k, v, off, ts, rp, rt, alpha, num_candidates=cands).reshape(T, H * d)
+    Y = torch.nn.functional.layer_norm(torch.from_numpy(O), (H * d,), eps=eps).numpy()
+    Y = Y * u.reshape(T, H * d)
+    B = len(off) - 1
+    ref = np.zeros((B, max(1, int(np.max(cands)))))
+    for b in range(B):
+        n = int(off[b + 1] - off[b]) - int(cands[b])
+        for c in range(int(cands[b])):
+            ref[b, c] = Y[int(off[b]) + n + c] @ w
+    return ref[:, :int(np.max(cands))]
+
+
+def test_golden_mfalcon_score():
+    """Hand-worked scores (closed forms in ln 3 through sigma(ln 3) = 3/4)."""
+    g = _load("mfalcon_score_ln3_4x4.json")
+    env = {"ln3": math.log(3), "sqrt": math.sqrt}
+    T, H, d = g["offsets"][-1], g["H"], g["d"]
+    arr = lambda key: np.array(g[key], dtype=np.float64).reshape(T, H, d)
+    rp = np.array([eval(str(x), env) for x in g["rab_pos"]], dtype=np.float64)
+    rt = np.array(g["rab_time"], dtype=np.float64)
+    got = oracle.mfalcon_score(arr("q"), arr("k"), arr("v"), arr("u"), g["offsets"],
+                               g["num_candidates"], np.array(g["ts"], dtype=np.int64), rp, rt,
+                               g["alpha"], np.array(g["w"], dtype=np.float64), eps=g["eps"])
+    exp = np.array([[eval(s, env) for s in g["expected_scores"]]])
+    np.testing.assert_allclose(got, exp, rtol=1e-13, atol=0)
+
+
+def test_mfalcon_score_matches_library_route():
+    """Users with no candidates, only candidates, one candidate, and
+    candidates that start inside a 32- or 128-row block; per-row U and an
+    asymmetric w, so a dropped gate, a reversed or rescaled w, or a score
+    read at the wrong row changes the result."""
+    rng = np.random.default_rng(86)
+    H, d = 2, 8
+    lengths = [45, 9, 6, 140, 1, 33]
+    cands = [6, 0, 6, 12, 1, 1]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(off[-1])
+    q, k, v, u = (rng.normal(0, 0.5, size=(T, H, d)) for _ in range(4))
+    ts = np.zeros(T, dtype=np.int64)
+    for b, L in enumerate(lengths):
+        n = L - cands[b]
+        t = np.cumsum(rng.integers(1, 400, size=L)).astype(np.int64)
+        if cands[b] and n:
+            t[n:] = t[n - 1]
+        ts[off[b]:off[b + 1]] = t
+    rp = rng.normal(0, 0.1, size=64)
+    rt = rng.normal(0, 0.1, size=32)
+    w = rng.normal(0, 1.0 / np.sqrt(H * d), size=H * d)
+    got = oracle.mfalcon_score(q, k, v, u, off, cands, ts, rp, rt, 1 / 160, w)
+    ref = _scores_by_library_route(q, k, v, u, off, cands, ts, rp, rt, 1 / 160, w, 1e-5)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-13)
+    # entries past a user's candidate count are never written
+    assert np.all(got[1] == 0.0) and np.all(got[4, 1:] == 0.0)
