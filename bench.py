@@ -249,7 +249,7 @@ class LayerBwdCase:
                                     dx=self.out["dx"], dw1=self.out["dw1"], dw2=self.out["dw2"],
                                     drab_pos=self.out["drab_pos"], drab_time=self.out["drab_time"])
         self.args = a
-        self.ws = torch.empty(max(1, ops.layer_bwd_workspace_bytes(a)), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(1, ops.layer_bwd_workspace_bytes(a, saved=saved)), dtype=torch.uint8, device=dev)
         self.saved = None
         if saved:
             # the training forward keeps Z, the pre-activation, O and Y (untimed)

@@ -660,16 +660,19 @@ LayerSaved layer_saved(const hstu_layer_args* l) {
     return v;
 }
 
-LayerBwdWs layer_bwd_ws(const hstu_layer_bwd_args* g) {
+// With `saved`, the four regions of the recomputed forward are empty (the
+// gradients read the kept activations instead) and the layout starts at dY.
+LayerBwdWs layer_bwd_ws(const hstu_layer_bwd_args* g, bool saved = false) {
     const hstu_layer_args* l = &g->layer;
     LayerBwdWs w;
     const size_t T = size_t(l->num_rows);
+    const size_t Tf = saved ? 0 : T;
     const size_t hd = size_t(l->H) * l->d, zw = 4 * hd, D = size_t(l->D);
     w.z = 0;
-    w.pre = align256(w.z + T * zw * 2);
-    w.o = align256(w.pre + T * zw * 2);
-    w.y = align256(w.o + T * hd * 2);
-    w.dy = align256(w.y + T * hd * 2);
+    w.pre = align256(w.z + Tf * zw * 2);
+    w.o = align256(w.pre + Tf * zw * 2);
+    w.y = align256(w.o + Tf * hd * 2);
+    w.dy = align256(w.y + Tf * hd * 2);
     w.dz = align256(w.dy + T * hd * 2);
     w.w1t = align256(w.dz + T * zw * 2);
     w.w2t = align256(w.w1t + D * zw * 2);
@@ -786,8 +789,15 @@ size_t hstu_layer_saved_bytes(const hstu_layer_args* l) {
 
 hstu_status hstu_layer_fwd_saved(const hstu_layer_args* l, void* saved, size_t saved_bytes, void* ws,
                                  size_t ws_bytes, void* stream) {
-    if (l && l->struct_size == sizeof(hstu_layer_args) && l->B > 0 && l->num_rows > 0 && !saved)
-        return fail(HSTU_ERR_ARG, "saved is NULL");
+    if (l && l->struct_size == sizeof(hstu_layer_args) && l->B > 0 && l->num_rows > 0) {
+        if (!saved) return fail(HSTU_ERR_ARG, "saved is NULL");
+        // the gradients read X again (dW1 = dP^T X), and the saved buffer does
+        // not keep it: X_out written over X would corrupt them silently
+        const size_t xb = size_t(l->num_rows) * size_t(l->D) * 2;
+        const uintptr_t x0 = uintptr_t(l->x), o0 = uintptr_t(l->x_out);
+        if (l->x && l->x_out && x0 < o0 + xb && o0 < x0 + xb)
+            return fail(HSTU_ERR_ARG, "x_out must not overlap x in a training forward (the gradients read x)");
+    }
     return layer_fwd_run(l, ws, ws_bytes, stream, saved, saved_bytes);
 }
 
@@ -949,6 +959,15 @@ size_t hstu_layer_bwd_workspace_bytes(const hstu_layer_bwd_args* g) {
     return layer_bwd_ws(g).total;
 }
 
+size_t hstu_layer_bwd_saved_workspace_bytes(const hstu_layer_bwd_args* g) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    hstu_status st = validate_layer_bwd(g);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != HSTU_OK) return 0;
+    return layer_bwd_ws(g, true).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -975,7 +994,7 @@ hstu_status layer_bwd_run(const hstu_layer_bwd_args* g, void* ws, size_t ws_byte
         clear(g->drab_time, sizeof(float) * l->num_time_buckets);
         return e == hipSuccess ? ok() : device_error(e, "clearing the gradients");
     }
-    const LayerBwdWs lw = layer_bwd_ws(g);
+    const LayerBwdWs lw = layer_bwd_ws(g, saved != nullptr);
     st = check_workspace(ws, ws_bytes, lw.total);
     if (st != HSTU_OK) return st;
     uint8_t* w = static_cast<uint8_t*>(ws);

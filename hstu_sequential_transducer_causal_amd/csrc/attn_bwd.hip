@@ -263,8 +263,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     // per wave, a scratch in which the block's G is written skewed and
     // transposed (column rho - c + 31, row rho; kDiagPitch floats per
     // column), so that each column holds one diagonal and its 32 entries are
-    // read with 8 16-byte loads.  Only the band rho <= column <= rho + 31 is
-    // ever written, so with the scratch zeroed once the rest reads as zero.
+    // read with 8 16-byte loads.  The diagonal path writes only the band rho
+    // <= column <= rho + 31 and relies on the rest reading as zero: the
+    // scratch is zeroed once, and the column path (which fills columns 0-31
+    // whole) clears its cells again after reading them.
     float* scratch_all = hist_all + 4 * hw;
 
     const int tid = threadIdx.x;
@@ -562,6 +564,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 }
                 // lane u < 32: key column u
                 const float dsum = row_sum();
+                // the diagonal path reads these cells as zero off its band
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    scratch[c * kDiagPitch + l32] = 0.0f;
+                }
                 const int pb = n - min(st.j0 + lane, n);
                 if (lane < 32 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             }

@@ -399,8 +399,11 @@ def make_layer_bwd_args(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, a
     return g
 
 
-def layer_bwd_workspace_bytes(g: _lib.LayerBwdArgs) -> int:
-    return int(_lib.load().hstu_layer_bwd_workspace_bytes(ctypes.byref(g)))
+def layer_bwd_workspace_bytes(g: _lib.LayerBwdArgs, saved: bool = False) -> int:
+    """Workspace of hstu_layer_bwd, or (saved) of hstu_layer_bwd_saved."""
+    lib = _lib.load()
+    f = lib.hstu_layer_bwd_saved_workspace_bytes if saved else lib.hstu_layer_bwd_workspace_bytes
+    return int(f(ctypes.byref(g)))
 
 
 def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha, dx_out, *, H: int,
@@ -425,7 +428,7 @@ def hstu_layer_bwd(x, w1, w2, seq_offsets, timestamps, rab_pos, rab_time, alpha,
                             dw2=out["dw2"], b1=b1, b2=b2, db1=out["db1"], db2=out["db2"],
                             drab_pos=out["drab_pos"], drab_time=out["drab_time"],
                             num_candidates=num_candidates, ln_eps=ln_eps)
-    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(g))
+    need = layer_bwd_workspace_bytes(g, saved=saved is not None)
     if need == 0:
         _lib.check(lib.hstu_layer_bwd(ctypes.byref(g), None, 0, _stream_ptr(stream)))
     if workspace is None:

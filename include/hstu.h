@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 8
+#define HSTU_ABI_VERSION 9
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -378,11 +378,19 @@ hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* args, void* workspace, siz
  * hstu_layer_bwd_saved computes what hstu_layer_bwd computes from them,
  * reading `saved` only, without running f1, the attention or the gate
  * forward again.  Both calls must see the same layer arguments, weights and
- * inputs.  Workspaces: hstu_layer_workspace_bytes and
- * hstu_layer_bwd_workspace_bytes.  Errors: as hstu_layer_fwd and
- * hstu_layer_bwd; HSTU_ERR_ARG for a NULL `saved` with a non-empty batch,
- * HSTU_ERR_WORKSPACE for a misaligned or too small one. */
+ * inputs; X must still hold the forward's input when the gradients run, so
+ * hstu_layer_fwd_saved rejects an x_out that overlaps x (unlike
+ * hstu_layer_fwd).  Workspaces: hstu_layer_workspace_bytes for the forward,
+ * hstu_layer_bwd_saved_workspace_bytes for the gradients (no room for a
+ * recomputed forward; any workspace of hstu_layer_bwd_workspace_bytes also
+ * fits).  Errors: as hstu_layer_fwd and hstu_layer_bwd; HSTU_ERR_ARG for a
+ * NULL `saved` with a non-empty batch or an x_out overlapping x,
+ * HSTU_ERR_WORKSPACE for a misaligned or too small buffer. */
 size_t hstu_layer_saved_bytes(const hstu_layer_args* args);
+
+/* Workspace bytes for hstu_layer_bwd_saved (0 on invalid arguments): dY, dZ,
+ * transposed weights, the attention's and the weight products' scratch. */
+size_t hstu_layer_bwd_saved_workspace_bytes(const hstu_layer_bwd_args* args);
 
 hstu_status hstu_layer_fwd_saved(const hstu_layer_args* args, void* saved, size_t saved_bytes,
                                  void* workspace, size_t workspace_bytes, void* stream);

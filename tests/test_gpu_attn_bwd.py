@@ -147,3 +147,32 @@ def test_bwd_full_size(cfg):
     against the oracle."""
     x = synth.config(cfg)
     _check(x, f"bwd cfg{cfg} full size", seed=200 + cfg)
+
+
+def test_bwd_table_gradients_bucket_by_bucket():
+    """M-FALCON users of many shapes (so that workgroups take candidate-row
+    blocks and history-row blocks one after the other), no clamped bucket to
+    dominate, and the table gradients checked bucket by bucket.  G reaches
+    the histograms in fp32 from exact bf16 inputs, so every bucket must match
+    the oracle to fp32 accumulation error, far below the bf16 output bound: a
+    stale scratch cell from a previous block would show in its bucket."""
+    rng = np.random.default_rng(107)
+    B = 24
+    lengths = rng.integers(40, 420, size=B)
+    cands = np.minimum(lengths, rng.integers(1, 200, size=B))
+    cands[::5] = lengths[::5]          # users with candidates only
+    x = synth.make_attn(108, lengths.tolist(), H=2, d=128, P=1024, NT=32, alpha=1 / 512,
+                        dtype="bf16", num_candidates=cands.tolist())
+    d = DeviceAttn(x)
+    gnp = synth.upstream_grad(109, x.v.shape)
+    g = dev_tensor(gnp, "bf16")
+    _, _, _, _, drp, drt = _run_bwd(d, g)
+    _, _, _, rrp, rrt = oracle.attn_bwd(x.q, x.k, x.v, x.offsets, x.ts, x.rab_pos, x.rab_time,
+                                        x.alpha, gnp, num_candidates=x.num_candidates)
+    for got, ref, name in ((host_f32(drp), rrp, "d rab_pos"), (host_f32(drt), rrt, "d rab_time")):
+        scale = float(np.abs(ref).max())
+        err = np.abs(got.astype(np.float64) - ref)
+        worst = int(err.argmax())
+        log(f"{name} bucket by bucket: max err / max|ref| = {err.max() / scale:.3e} at bucket {worst}"
+            f" (ref {ref[worst]:.4e}, got {got[worst]:.4e})")
+        assert np.all(err <= 1e-3 * scale + 1e-3 * np.abs(ref)), name

@@ -125,7 +125,7 @@ def test_layer_saved_pair_equals_recomputation():
     hstu_layer_bwd's gradients bit for bit (both run the same kernels on the
     same inputs; the saved pair only skips the recomputation)."""
     import torch
-    from hstu_sequential_transducer_causal_amd import ops
+    from hstu_sequential_transducer_causal_amd import _lib, ops
     x = synth.make_layer_stack(75, [1, 300, 77, 512], H=4, d=128, D=512, layers=1, P=1024, NT=32,
                                alpha=1 / 512)
     b1, b2 = (torch.from_numpy(b.astype(np.float32)).cuda() for b in _biases(x, 76))
@@ -145,6 +145,10 @@ def test_layer_saved_pair_equals_recomputation():
                               **kw)
     torch.cuda.synchronize()
     assert torch.equal(plain, kept)
+    # X_out written over X would leave the gradients a wrong X: refused before any launch
+    with pytest.raises(_lib.HstuError, match="overlap"):
+        ops.hstu_layer_fwd(xd, w1, w2, off, ts, rp, rt, x.alpha, b1=b1, b2=b2, ln_eps=x.eps, saved=saved,
+                           x_out=xd, **kw)
     gd = dev_tensor(g, "bf16")
     ref = ops.hstu_layer_bwd(xd, w1, w2, off, ts, rp, rt, x.alpha, gd, b1=b1, b2=b2, ln_eps=x.eps, **kw)
     got = ops.hstu_layer_bwd(xd, w1, w2, off, ts, rp, rt, x.alpha, gd, b1=b1, b2=b2, ln_eps=x.eps,
