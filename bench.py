@@ -10,7 +10,11 @@ in HBM before the timed region.
 Prints ONE JSON line.  `value` is unmasked attention TFLOP/s of the whole
 step; `roofline` is the attention-core kernel alone, timed with HIP events
 recorded around its launch on the same stream; `cpu_baseline` is the fp64
-oracle on a bounded sample of the same workload (host cores of this machine).
+oracle on a bounded sample of the same workload (host cores of this box);
+`parity` is one step of the same call checked against that oracle run (max
+and mean |err| / max|ref|).  Order: the parity check and the CPU baseline,
+the other workloads (each with its own sampled parity check), then the
+headline's W warm-up and K timed steps.
 Other workloads (bf16 batch of 64, M-FALCON ranking, the 4-layer stack) and
 the gradients (hstu_attn_bwd from dLoss/dY on the long-sequence and M-FALCON
 workloads; hstu_layer_bwd on one layer of the stack) and stochastic length
@@ -518,23 +522,76 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(x, nseq):
-    """The oracle as it stands, on the first nseq sequences of the workload."""
+    """The oracle as it stands, on the first nseq sequences of the workload
+    (all when nseq <= 0); returns the record and the oracle's O of those rows."""
     import oracle
     from hstu_sequential_transducer_causal_amd import flops
     seqs = list(range(x.B if nseq <= 0 else min(nseq, x.B)))
     L = np.diff(x.offsets)
     s1 = int(x.offsets[seqs[-1] + 1])
+    nc = None if x.num_candidates is None else x.num_candidates[:len(seqs)]
     t0 = time.perf_counter()
-    oracle.attn(x.q[:s1], x.k[:s1], x.v[:s1], x.offsets[:len(seqs) + 1], x.ts[:s1], x.rab_pos,
-                x.rab_time, x.alpha)
+    ref = oracle.attn(x.q[:s1], x.k[:s1], x.v[:s1], x.offsets[:len(seqs) + 1], x.ts[:s1], x.rab_pos,
+                      x.rab_time, x.alpha, num_candidates=nc)
     dt = time.perf_counter() - t0
-    fl = flops.attn_flops(L[seqs], x.H, x.d, x.d)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"fp64 oracle attention (no epilogue) on sequences {seqs} of the same "
-                      f"workload (lengths {[int(v) for v in L[seqs]]}, {x.H} heads), "
-                      f"{fl / 1e9:.1f} GFLOP"}
+    fl = flops.attn_flops(L[seqs], x.H, x.d, x.d, nc)
+    rec = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+           "cpu_model": cpu_model(), "kind": "oracle", "seconds": dt,
+           "sample": f"fp64 oracle attention (no epilogue) on sequences {seqs} of the same "
+                     f"workload (lengths {[int(v) for v in L[seqs]]}, {x.H} heads), "
+                     f"{fl / 1e9:.1f} GFLOP"}
+    return rec, ref
+
+
+def _err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = float(np.abs(ref).max()) or 1.0
+    e = np.abs(got - ref)
+    return {"max_err_rel": float(f"{e.max() / scale:.3e}"), "mean_err_rel": float(f"{e.mean() / scale:.3e}")}
+
+
+def parity_record(case, x, ref_o=None, nseq=0):
+    """One step of `case` against the oracle on its first nseq sequences (all
+    when nseq <= 0; ref_o: the oracle's O of those rows if already computed):
+    max and mean |err| / max|ref| of O, and of Y (or, for M-FALCON, of the
+    scores); bf16 bounds 2e-2 (max) and 2e-3 (mean)."""
+    import torch
+    import oracle
+    case.step()
+    torch.cuda.synchronize()
+    seqs = list(range(x.B if nseq <= 0 else min(nseq, x.B)))
+    s1 = int(x.offsets[seqs[-1] + 1])
+    nc = None if x.num_candidates is None else x.num_candidates[:len(seqs)]
+    if ref_o is None:
+        ref_o = oracle.attn(x.q[:s1], x.k[:s1], x.v[:s1], x.offsets[:len(seqs) + 1], x.ts[:s1],
+                            x.rab_pos, x.rab_time, x.alpha, num_candidates=nc)
+    o = case.o[:s1].float().cpu().numpy()
+    rec = {"sample": f"sequences {seqs[0]}..{seqs[-1]} of {x.B} ({s1} rows)", "O": _err(o, ref_o)}
+    if case.with_scores:
+        ref_s = oracle.mfalcon_score(x.q[:s1], x.k[:s1], x.v[:s1], x.u[:s1], x.offsets[:len(seqs) + 1], nc,
+                                     x.ts[:s1], x.rab_pos, x.rab_time, x.alpha, x.w, eps=x.eps)
+        got_s = case.scores[:len(seqs), :ref_s.shape[1]].cpu().numpy()
+        rec["scores"] = _err(got_s, ref_s)
+    else:
+        ref_y = oracle.ln_gate(ref_o.reshape(s1, -1), x.u[:s1].reshape(s1, -1), eps=x.eps)
+        rec["Y"] = _err(case.y[:s1].float().cpu().numpy().reshape(s1, -1), ref_y)
+    rec["pass"] = all(v["max_err_rel"] <= 2e-2 and v["mean_err_rel"] <= 2e-3
+                      for k, v in rec.items() if isinstance(v, dict))
+    return rec
 
 
 def main():
@@ -588,30 +645,20 @@ def main():
         fl = flops.attn_flops(L, x.H, x.d, x.d, x.num_candidates)
         attn_fl_core = fl
     log(f"workload {x.name}: B={x.B} T={x.T} GFLOP/step={fl / 1e9:.2f}")
-    ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5))
-    value = fl / (ms_step * 1e-3) / 1e12
-    tokens_s = x.T / (ms_step * 1e-3)
-    log(f"step {ms_step:.3f} ms, core {core_ms} ms, {value:.1f} TFLOP/s")
 
-    roofline = None
-    if core_ms:
-        ach = attn_fl_core / (core_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                    "kernel": "attn_bf16_kernel", "core_ms": round(core_ms, 4)}
+    # correctness of this very call path first: one step against the oracle
+    # (the oracle's run on the host cores is also the CPU baseline)
+    cpu_rec, parity = None, None
+    if wl != 5:
+        if not args.no_cpu_baseline:
+            log("timing the oracle (CPU baseline) and checking one step against it")
+            cpu_rec, ref_o = cpu_baseline(x, args.cpu_sample_seqs)
+            parity = parity_record(case, x, ref_o, args.cpu_sample_seqs)
+        else:
+            parity = parity_record(case, x, None, 2)
+        log(f"parity: {parity}")
 
-    line = {
-        "metric": "HSTU attention fwd TFLOP/s (unmasked) + jagged tokens/s; % bf16 MFMA peak",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": x.name, "global_batch": x.B, "tokens": x.T,
-                   "max_seq_len": int(L.max()), "heads": x.H, "head_dim": x.d},
-        "tokens_per_s": round(tokens_s, 1),
-        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "roofline": roofline,
-    }
-
+    others = None
     if not args.no_others:
         others = {}
         for w in (2, 4, 5):
@@ -629,6 +676,8 @@ def main():
                 st, ce = time_case(c, max(3, args.steps // 3), 2)
             rec = {"ms_per_step": round(st, 4), "tflops": round(flo / (st * 1e-3) / 1e12, 2),
                    "tokens_per_s": round(xo.T / (st * 1e-3), 1), "tokens": xo.T}
+            if w != 5:
+                rec["parity"] = parity_record(c, xo, None, 4 if w == 2 else 2)
             if ce:
                 rec["core_ms"] = round(ce, 4)
                 rec["core_tflops"] = round(flo / (ce * 1e-3) / 1e12, 2)
@@ -707,12 +756,35 @@ def main():
             others[xb.name + "_bwd"] = rec
             log(f"{xb.name} gradients: {rec}")
             torch.cuda.empty_cache()
-        line["other_workloads"] = others
 
-    line["cpu_baseline"] = None
-    if not args.no_cpu_baseline and wl != 5:
-        log("timing the oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+    # the headline: W untimed warm-up steps, then K timed steps
+    ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5))
+    value = fl / (ms_step * 1e-3) / 1e12
+    tokens_s = x.T / (ms_step * 1e-3)
+    log(f"step {ms_step:.3f} ms, core {core_ms} ms, {value:.1f} TFLOP/s")
+
+    roofline = None
+    if core_ms:
+        ach = attn_fl_core / (core_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                    "kernel": "attn_bf16_kernel", "core_ms": round(core_ms, 4)}
+
+    line = {
+        "metric": "HSTU attention fwd TFLOP/s (unmasked) + jagged tokens/s; % bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": x.name, "global_batch": x.B, "tokens": x.T,
+                   "max_seq_len": int(L.max()), "heads": x.H, "head_dim": x.d},
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "parity": parity,
+    }
+    if others is not None:
+        line["other_workloads"] = others
+    line["cpu_baseline"] = cpu_rec
     print(json.dumps(line), flush=True)
 
 

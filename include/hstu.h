@@ -374,7 +374,9 @@ hstu_status hstu_layer_bwd(const hstu_layer_bwd_args* args, void* workspace, siz
  * hstu_layer_fwd computes and also writes, into the caller's buffer `saved`
  * (device, 16-byte aligned, hstu_layer_saved_bytes() bytes), Z = SiLU(X W1^T
  * + b1) (U | V | Q | K), the pre-activation X W1^T + b1, O and Y (bf16,
- * num_rows rows each, about 2 * (2 * 4*H*d + 2 * H*d) bytes per row);
+ * num_rows rows each, about 2 * (2 * 4*H*d + 2 * H*d) bytes per row), in
+ * that order, row-major with no row padding, each region starting at the
+ * next multiple of 256 bytes after the previous one (Z at byte 0);
  * hstu_layer_bwd_saved computes what hstu_layer_bwd computes from them,
  * reading `saved` only, without running f1, the attention or the gate
  * forward again.  Both calls must see the same layer arguments, weights and
