@@ -67,6 +67,8 @@ constexpr int BN = kBf16TileN;   // 32 keys per tile
 constexpr int HD = 128;          // head dim
 constexpr int kThreads = 256;
 constexpr int kStages = 4;       // LDS ring depth: tiles t .. t+3 in flight
+constexpr int kStageBytes = BN * kRowBytes;   // one K (or V) tile in LDS
+
 
 
 struct Params {
@@ -90,7 +92,7 @@ struct Params {
     int nblk;
     const uint32_t* stats;
     const uint32_t* enc;
-    int pos_copy;   // floats per shifted copy of the reversed position table
+    int pos_pairs;  // entries of the reversed position table, as pairs (two floats each)
     // cross mode: queries (and O) in their own row space; the fields above
     // then describe the keys (a history cache)
     const int32_t* q_offsets;
@@ -103,7 +105,7 @@ struct Params {
 struct Smem {
     uint8_t k[kStages][BN * kRowBytes];   // [32 keys][128 d], 16-B chunk c of row r at c ^ (r & 15)
     uint8_t v[kStages][BN * kRowBytes];   // [32 keys][128 d], 16-B chunk c of row r at c ^ 4 (r & 3)
-    uint32_t tsk[kStages][64];            // [0..31] key codes, [32..33] key block range
+    uint32_t tsk[kStages][4][64];         // wave w's load: codes of keys 8w .. 8w+7 at [w][0..7]
     float tt_fast[32];                    // by leading-zero count of 2|dt| + 1
     float tt_wide[65];                    // by bit length of |dt|
     int32_t item[8];
@@ -113,44 +115,55 @@ struct Smem {
 // Per-item state of the tile loads.  Wave w fills key rows 8w .. 8w+7 of the
 // K and V tiles with 2 buffer loads each: lane l of load m writes 16 bytes at
 // row 8w + 4m + l/16, physical chunk l % 16, so it fetches the logical chunk
-// that the swizzle puts there.  Wave 0 also loads the 32 key codes with one
-// 4-byte-per-lane load.
+// that the swizzle puts there; and the codes of keys 8w .. 8w+7 with one
+// 4-byte-per-lane load (lanes 8-63 read out of range and write zeros into
+// the rest of the wave's own 64-entry region).  Every wave thus issues the
+// same 5 loads per tile, and the wait for a tile is one constant count.
+// Tiles past the end of the list are loaded from out of range (zeros into a
+// stage nobody reads), so the ring needs no special last tiles either.
 struct TileDma {
     u32x4 krs, vrs, wrs;
     uint32_t koff[2], voff[2];
     uint32_t ktile, vtile;        // bytes per key tile in K and V
-    uint32_t code_off;            // lane < 32: byte offset of the sequence's code `lane`; else out of range
+    uint32_t code_off;            // lane < 8: byte offset of the code of key 8 wave + lane; else out of range
 };
+
+constexpr int kLoadsPerTile = 5;
+constexpr uint32_t kFarOffset = 0x40000000u;   // past every buffer's range (num_records < 2^31)
+
+// Scalar offset of key tile kt, or (far) an offset past the buffer's range.
+__device__ __forceinline__ uint32_t tile_soff(int kt, bool far, uint32_t tile_bytes) {
+    return far ? kFarOffset : (uint32_t)kt * tile_bytes;
+}
 
 // The three parts of a tile's loads go out at different points of the
 // previous tiles' work, so that no wave stalls long on a full load queue.
-__device__ __forceinline__ void issue_k(const TileDma& d, Smem& s, int stage, int kt, int wave) {
+__device__ __forceinline__ void issue_k(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
     const uint32_t kl = lds_addr(s.k[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
-    const uint32_t ksoff = uniu((uint32_t)kt * d.ktile);
+    const uint32_t ksoff = uniu(tile_soff(kt, far, d.ktile));
 #pragma unroll
     for (int m = 0; m < 2; ++m) dma16(d.krs, uniu(kl + m * 1024), d.koff[m], ksoff);
 }
-__device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, int kt, int wave) {
+__device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
     const uint32_t vl = lds_addr(s.v[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
-    const uint32_t vsoff = uniu((uint32_t)kt * d.vtile);
+    const uint32_t vsoff = uniu(tile_soff(kt, far, d.vtile));
 #pragma unroll
     for (int m = 0; m < 2; ++m) dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
 }
-// Wave 0 only: the tile's 32 key codes (lanes 32-63 write zeros; codes of
-// keys past the sequence end are other rows' or zeros, and those keys are
-// masked).  The lane's offset is fixed per item, the tile is the scalar offset.
-__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt) {
-    const uint32_t lds = uniu(lds_addr(s.tsk[0]) + (uint32_t)(stage * 64 * 4));
-    const uint32_t soff = uniu((uint32_t)kt * (uint32_t)(BN * 4));
+// The codes of keys 8 wave .. 8 wave + 7 (codes of keys past the sequence end
+// are other rows' or zeros, and those keys are masked).  The lane's offset is
+// fixed per item, the tile is the scalar offset.
+__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
+    const uint32_t lds = uniu(lds_addr(s.tsk[0]) + (uint32_t)((stage * 4 + wave) * 64 * 4));
+    const uint32_t soff = uniu(tile_soff(kt, far, (uint32_t)(BN * 4)));
     asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(d.code_off), "s"(d.wrs), "s"(soff),
                  "{m0}"(lds)
                  : "memory");
 }
-__device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, int L, int wave,
-                                           int lane) {
-    issue_k(d, s, stage, kt, wave);
-    issue_v(d, s, stage, kt, wave);
-    if (wave == 0) issue_codes(d, s, stage, kt);
+__device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
+    issue_k(d, s, stage, kt, far, wave);
+    issue_v(d, s, stage, kt, far, wave);
+    issue_codes(d, s, stage, kt, far, wave);
 }
 
 // kCross: the queries are candidates in their own buffers, each seeing every
@@ -171,10 +184,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
     const bool shared_tables = (p.rp_hs == 0) && (p.rt_hs == 0);
     const int P = p.P;
     const int Dhi = P + 63;              // position difference of reversed-table entry 0
-    const int CS = p.pos_copy;
     const float kNegLog2e = -kLog2e;
     const float alpha_eff = kSilu ? -p.alpha * 0.69314718055994531f : p.alpha;
-    const int per_tile = uni(wave == 0 ? 5 : 4);   // buffer loads per tile of this wave
     const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
     const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
     // key block ranges through the scalar cache (uniform addresses)
@@ -217,7 +228,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         }
         lds_sync();
         const int w = uni(s.work);
-        if (w >= total_work) break;
+        if (w >= total_work) {
+            wait_vmcnt(0);   // no load of the ring may land in LDS after the workgroup ends
+            break;
+        }
         const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
         const int kbw = uni(s.item[3]);
         const int kb_begin = kbw & 0xffff;
@@ -240,10 +254,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
             const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
             const float* rt = p.rab_time + (int64_t)h * p.rt_hs;
-            // copy c holds Rv[w - c], Rv[u] = rab_pos[clamp(Dhi - u, 0, P-1)]
-            for (int e = tid; e < 2 * CS; e += kThreads) {
-                const int c = e / CS;
-                const int u = e - c * CS - c;
+            // pair u holds (Rv[u], Rv[u + 1]), Rv[u] = rab_pos[clamp(Dhi - u, 0, P-1)]:
+            // any two neighbouring entries are one aligned 8-byte read
+            for (int e = tid; e < 2 * p.pos_pairs; e += kThreads) {
+                const int u = (e >> 1) + (e & 1);
                 const int dd = min(max(Dhi - u, 0), P - 1);
                 ptab[e] = rp[dd];
             }
@@ -271,16 +285,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             }
             dma.ktile = (uint32_t)(BN * p.ks * 2);
             dma.vtile = (uint32_t)(BN * p.vs * 2);
-            dma.code_off = lane < 32 ? (uint32_t)(enc_base + 4 * (row0 + lane)) : 0x80000000u;
+            dma.code_off = lane < 8 ? (uint32_t)(enc_base + 4 * (row0 + 8 * wave + lane)) : kFarOffset;
         }
         const int ntiles = p1 - p0;
+        // key tile of list position it (positions past the end are loaded
+        // from out of range)
         auto tile_of = [&](int it) {
             const int pos = p0 + it;
             return pos < a_end ? pos : kb_begin + (pos - a_end);
         };
+        // load groups: after the barrier of tile t go out V(t+2), then (mid-step)
+        // K(t+3) and the codes of t+3, 5 loads per group; the prologue sends
+        // the groups of t = -3 (its V part from out of range), -2 and -1
+        issue_v(dma, s, kStages - 1, 0, true, wave);
 #pragma unroll
-        for (int pre = 0; pre < kStages - 1; ++pre)
-            if (pre < ntiles) issue_tile(dma, s, pre, tile_of(pre), L, wave, lane);
+        for (int pre = 0; pre < kStages - 1; ++pre) {
+            if (pre > 0) issue_v(dma, s, pre - 1, tile_of(pre - 1), pre - 1 >= ntiles, wave);
+            issue_k(dma, s, pre, tile_of(pre), pre >= ntiles, wave);
+            issue_codes(dma, s, pre, tile_of(pre), pre >= ntiles, wave);
+        }
 
         // ---- this wave's 32 query rows
         const int wrow0 = qt * BM + wave * 32;
@@ -314,15 +337,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const int vis_lim = kCross ? (i < Lq ? n - 1 : -1) : (i >= L ? -1 : (i < n ? i : n - 1));
         const int vis_self = kCross ? -1 : ((i >= n && i < L) ? i : -1);
         const bool cand_rows = kCross ? false : wrow0 + 31 >= n;   // the block holds candidate rows
-        const int prow_min = kCross ? n : uni(min(wrow0, n));
         // time table by leading-zero count, one entry per lane (lanes 32-63
         // repeat 0-31), read with readlane for block-uniform buckets
         int ttv = __builtin_bit_cast(int, p.rab_time[(int64_t)h * p.rt_hs + min(p.NT - 1, 31 - l32)]);
-        float pos_far = p.rab_pos[(int64_t)h * p.rp_hs + P - 1];   // every clamped difference
         // These item-level loads complete here: a value still in flight at
         // the loop entry would make the compiler wait for every load (the
         // tile loads included) at its first use in each iteration.
-        asm volatile("" : "+v"(pos_far), "+v"(ttv), "+v"(tie), "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
+        asm volatile("" : "+v"(ttv), "+v"(tie), "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]),
                      "+v"(qf[5]), "+v"(qf[6]), "+v"(qf[7]));
 
         f32x16 oacc[4];
@@ -339,20 +360,46 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         //      busy), and V(it) is read into registers for the next iteration.
         u32x2 krange_next = {0u, 0u};
         if (!kCross || ntiles > 0) krange_next = kstats[bbase + tile_of(0)];
-        u32x4 vf[2][4];
-        const uint32_t koff_lane = k_lane_offset(lane), voff_lane = v_lane_offset(lane);
-        const uint32_t ptab_lds = lds_addr(ptab);
+        // Per-lane LDS addresses of the fragments in stage 0 (a stage's base
+        // is then an immediate offset: the tile loop is unrolled by the ring
+        // depth, so every step knows its stage at compile time).  K fragment
+        // kc of lane l sits at the lane's base XOR kc << 5, and the V^T
+        // fragments of column block nb at its V base XOR nb << 6 (the
+        // swizzles move whole 16- or 64-byte units); the key codes of the
+        // lane's keys 8q + 4h2 .. +3 at its code base + 256 q.  Kept opaque,
+        // so that they stay in registers instead of being recomputed per tile.
+        uint32_t kx[8], vx[4], cx;
+        {
+            const uint32_t kb = lds_addr(s.k[0]) + k_lane_offset(lane);
+            const uint32_t vb = lds_addr(s.v[0]) + v_lane_offset(lane);
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) kx[kc] = kb ^ (uint32_t)(kc << 5);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) vx[nb] = vb ^ (uint32_t)(nb << 6);
+            cx = lds_addr(&s.tsk[0][0][4 * h2]);
+#pragma unroll
+            for (int kc = 0; kc < 8; ++kc) asm volatile("" : "+v"(kx[kc]));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) asm volatile("" : "+v"(vx[nb]));
+            asm volatile("" : "+v"(cx));
+        }
+        const uint32_t ptab_hi = lds_addr(ptab) + 8u * (uint32_t)Dhi;   // pair Dhi: difference 0
         const int prow4 = prow - 4 * h2;   // the position term's row part for this lane's keys
 
-        // the barrier of tile it (its loads have landed, every wave is done
-        // with tile it-1's stage: V(it-1) was read before it), then the K
-        // part of tile it+3's loads into that stage
-        auto tile_sync = [&](int it) {
-            const int later = min(kStages - 2, ntiles - 1 - it);
-            wait_vmcnt(later * per_tile);
-            lds_sync();
-            if (it + kStages - 1 < ntiles)
-                issue_k(dma, s, (it + kStages - 1) & (kStages - 1), tile_of(it + kStages - 1), wave);
+        // the barrier of tile it.  Before it this wave's K(it), codes(it) and
+        // V(it) have landed (in flight may stay the rest of the group of
+        // it-2, K and codes of it+1, and the whole group of it-1: 8 loads),
+        // after it every wave's have.  Then V(it+2) goes into the V half of
+        // stage it+2 = it-2, whose V(it-2) every wave has consumed (its AV
+        // products ran in step it-1).  No wait for this wave's own LDS reads
+        // is needed: every read of step it-1 was consumed in that step (V(it-1)
+        // is read in step it, from the half V(it+3) refills after the next
+        // barrier).
+        auto tile_sync = [&](int it, int st) {
+            wait_vmcnt(kLoadsPerTile + 3);
+            lds_barrier();
+            const int t2 = it + kStages - 2;
+            issue_v(dma, s, (st + kStages - 2) & (kStages - 1), tile_of(t2), t2 >= ntiles, wave);
         };
 
         // bias of tile it (as the initial accumulator, plus a constant) and
@@ -362,38 +409,37 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             bool wide;
             int czlo, czhi, j0;
         };
-        auto tile_bias = [&](int it, f32x16& acc, float& cadd, bf16x8 (&kf)[8]) -> TileFacts {
+        const int xmax = P + 31;   // a lane's first difference past this: all 32 clamp to P-1
+        auto tile_bias = [&](int it, int st, f32x16& acc, float& cadd, bf16x8 (&kf)[8]) -> TileFacts {
             const int kt = tile_of(it);
             const int j0 = kt * BN;
-            const int stage = it & (kStages - 1);
-            const uint8_t* k_lds = s.k[stage];
 
             // block-uniform facts (scalar; the key block's code range was
             // loaded one tile ahead)
             const uint32_t kmn = uniu(krange_next[0]), kmx = uniu(krange_next[1]);
             if (it + 1 < ntiles) krange_next = kstats[bbase + tile_of(it + 1)];
             const bool wide = rows_wide || kmn > kmx;
-            const uint32_t lo = rmin >= kmx ? rmin - kmx : (kmn >= rmax ? kmn - rmax : 0u);
-            const uint32_t hi = max(rmax >= kmn ? rmax - kmn : 0u, kmx >= rmin ? kmx - rmin : 0u);
+            // outside wide blocks every code lies within 2^30 of 2^31, so code
+            // differences are exact as signed 32-bit values (scalar max, no
+            // saturating subtraction, which only the VALU has)
+            const int g1 = (int)(rmin - kmx), g2 = (int)(kmn - rmax);
+            const uint32_t lo = (uint32_t)max(uni(max(g1, g2)), 0);   // nearest pair (0: ranges overlap)
+            const uint32_t hi = (uint32_t)max((int)(rmax - kmn), (int)(kmx - rmin));   // farthest pair
             const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
-            const bool pos_clamped = prow_min - (j0 + 31) >= P - 1;
 
-            // LDS reads: position entries when needed, then K (the key codes,
-            // when needed, are read by time_bias)
+            // LDS reads: position entries, then K (the key codes, when
+            // needed, are read by time_bias)
             // position bias: lane (row i, keys j0 + 8q + 4h2 + t) reads
-            // reversed-table entries u0 + 8q + t; a block whose differences
-            // all clamp takes rab_pos[P-1] as a constant
+            // reversed-table entries u0 + 8q + t (differences x - 8q - t);
+            // clamping x to [0, P + 31] keeps every read in the table and
+            // changes no value a visible pair reads (past P + 31 all 32 clamp
+            // to P - 1; below 0 the keys are past the row, masked)
             cadd = 0.0f;
-            if (pos_clamped) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-                cadd = pos_far;
-            } else {
-                // entries u0 + 8q + t, u0 = Dhi - x, from copy c = u0 & 1 at
-                // float index c * (CS + 1) + u0: one base, immediate offsets
-                const int x = min(max(prow4 - j0, 0), P + 26);
-                const int u0 = Dhi - x;
-                const uint32_t pa = ptab_lds + 4u * (uint32_t)u0 + (uint32_t)(u0 & 1) * (4u * (uint32_t)CS + 4u);
+            {
+                // entries u0 + 8q + t, u0 = Dhi - x: pairs u0 + 8q and
+                // u0 + 8q + 2, at one base with immediate offsets
+                const int x = min(max(prow4 - j0, 0), xmax);
+                const uint32_t pa = ptab_hi - 8u * (uint32_t)x;
                 typedef float f32x2v __attribute__((ext_vector_type(2)));
                 typedef __attribute__((address_space(3))) const f32x2v lds_f2;
                 const lds_f2* pp = (const lds_f2*)(uintptr_t)pa;
@@ -401,27 +447,26 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int q = 0; q < 4; ++q) {
 #pragma unroll
                     for (int t2 = 0; t2 < 2; ++t2) {
-                        const f32x2v pv = pp[4 * q + t2];
+                        const f32x2v pv = pp[8 * q + 2 * t2];
                         acc[4 * q + 2 * t2] = pv[0];
                         acc[4 * q + 2 * t2 + 1] = pv[1];
                     }
                 }
             }
-            uint32_t ko = koff_lane;
-            asm volatile("" : "+v"(ko));   // recomputed per tile: keeps one register live, not eight
-            const uint32_t kb = lds_addr(k_lds) + ko;
 #pragma unroll
-            for (int kc = 0; kc < 8; ++kc) kf[kc] = lds_read_b128(kb ^ (uint32_t)(kc << 5));
+            for (int kc = 0; kc < 8; ++kc) kf[kc] = lds_read_b128(kx[kc] + (uint32_t)(st * kStageBytes));
             return TileFacts{wide, czlo, czhi, j0};
         };
-        auto time_bias = [&](int it, const TileFacts& f, f32x16& acc, float& cadd) {
+        auto time_bias = [&](int st, const TileFacts& f, f32x16& acc, float& cadd) {
                 const bool wide = f.wide;
                 const int czlo = f.czlo, czhi = f.czhi, j0 = f.j0;
-                const uint32_t* tsk = s.tsk[it & (kStages - 1)];
+                // keys 8q + 4h2 + t sit in wave q's region at 4h2 + t
                 u32x4 codes[4];
                 if (!wide && czlo != czhi) {
+                    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) codes[q] = *reinterpret_cast<const u32x4*>(&tsk[8 * q + 4 * h2]);
+                    for (int q = 0; q < 4; ++q)
+                        codes[q] = *(lds_u32x4*)(uintptr_t)(cx + (uint32_t)(st * 4 * 64 * 4 + 256 * q));
                 }
                 // time bias: constant over the block (most blocks), one of two
                 // buckets split at a power of two, or per element
@@ -430,15 +475,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     if (czlo == czhi) {
                         cadd += tlo;
                     } else {
-                        // |e_i - e_j| + 1 < 2^(32 - czlo) exactly when the bucket is czlo
+                        // g = |e_i - e_j| + 1 lies in [2^(31 - czlo), 2^(33 - czlo)),
+                        // and the bucket is czhi exactly when bit 32 - czlo of g
+                        // is set: g >> (32 - czlo) is 0 or 1, the bucket's share
+                        // of thi - tlo (tlo is the block constant)
                         const float thi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czhi));
-                        uint32_t thr = 1u << (32 - czlo);
-                        asm volatile("" : "+s"(thr));   // opaque: one compare per element, not a shift and a compare
+                        const float dt = thi - tlo;
+                        const uint32_t sh = (uint32_t)(32 - czlo);
+                        cadd += tlo;
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
-                                acc[4 * q + t] += sad_u32(tie, codes[q][t], 1u) >= thr ? thi : tlo;
+                                acc[4 * q + t] = __builtin_fmaf((float)(sad_u32(tie, codes[q][t], 1u) >> sh), dt,
+                                                                acc[4 * q + t]);
                     }
                 } else if (!wide) {
 #pragma unroll
@@ -507,33 +557,42 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int e = 0; e < 4; ++e) pk[c][e] = pack_bf16x2(a[8 * c + 2 * e], a[8 * c + 2 * e + 1]);
         };
 
-        // the V and key-code parts of tile it+3's loads
-        auto issue_rest = [&](int it) {
-            if (it + kStages - 1 < ntiles) {
-                const int st3 = (it + kStages - 1) & (kStages - 1), kt3 = tile_of(it + kStages - 1);
-                issue_v(dma, s, st3, kt3, wave);
-                if (wave == 0) issue_codes(dma, s, st3, kt3);
-            }
+        // the K and key-code parts of tile it+3's loads, into the K half of
+        // stage it+3 = it-1
+        auto issue_rest = [&](int it, int st) {
+            const int t3 = it + kStages - 1;
+            const int st3 = (st + kStages - 1) & (kStages - 1), kt3 = tile_of(t3);
+            issue_k(dma, s, st3, kt3, t3 >= ntiles, wave);
+            issue_codes(dma, s, st3, kt3, t3 >= ntiles, wave);
         };
 
-        auto read_v = [&](int it) {
-            uint32_t vo = voff_lane;
-            asm volatile("" : "+v"(vo));
-            read_v_tile(lds_addr(s.v[it & (kStages - 1)]), vo, vf);
+        // V^T fragments of the tile in stage st (see read_v_tile)
+        auto read_v = [&](int st, u32x4 (&vf)[2][4]) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const uint32_t a = vx[nb] + (uint32_t)(st * kStageBytes);
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const u32x2 v0 = lds_read_tr(a + c * 16 * kRowBytes);
+                    const u32x2 v1 = lds_read_tr(a + c * 16 * kRowBytes + 8 * kRowBytes);
+                    vf[c][nb] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+                }
+            }
         };
 
         // one pipeline step: S(it) into accN while tile it-1 (S in accC)
         // is finished
-        auto step = [&](int it, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
-            tile_sync(it);
+        // (st = it & 3: a compile-time constant in the unrolled loop)
+        auto step = [&](int st, int it, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
+            tile_sync(it, st);
             bf16x8 kf[8];
-            const TileFacts f = tile_bias(it, accN, caddN, kf);
+            const TileFacts f = tile_bias(it, st, accN, caddN, kf);
             const float c2 = act_const(caddC);
             // the first activations cover the LDS latency of this tile's reads
 #pragma unroll
             for (int r = 0; r < 4; ++r) act_one(accC, c2, r);
-            time_bias(it, f, accN, caddN);
-            issue_rest(it);
+            time_bias(st, f, accN, caddN);
+            issue_rest(it, st);
             // S(it) = K Q^T: a dependent chain of 8 MFMAs, each followed by
             // the activation of 1.5 elements of S(it-1)
 #pragma unroll
@@ -549,6 +608,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // then VALU
             }
+            // V(it-1) now, in the registers the K fragments just freed: its
+            // LDS latency is covered by the rest of the activation and the
+            // packing, and no fragments stay live across the step
+            u32x4 vf[2][4];
+            read_v((st + kStages - 1) & (kStages - 1), vf);
             u32x4 pk[2];
             tile_pack(it - 1, accC, pk);
 #pragma unroll
@@ -556,7 +620,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
                     oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
-            read_v(it);
         };
 
         // The tile list runs over keys in increasing order, so the tiles past
@@ -578,27 +641,34 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         if (nuse > 0) {
             f32x16 accA, accB;
             float caddA = 0.0f, caddB = 0.0f;
-            // prologue: S(0), V(0)
+            // prologue: S(0)
             {
-                tile_sync(0);
+                tile_sync(0, 0);
                 bf16x8 kf[8];
-                const TileFacts f = tile_bias(0, accA, caddA, kf);
+                const TileFacts f = tile_bias(0, 0, accA, caddA, kf);
                 time_bias(0, f, accA, caddA);
-                issue_rest(0);
+                issue_rest(0, 0);
 #pragma unroll
                 for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], accA);
-                read_v(0);
             }
+            // steps 1, 2, 3, 4, ...: stages 1, 2, 3, 0, ..., S alternating
+            // between the two accumulators; four steps per iteration, then
+            // the last 0-3 with the stage computed
             int it = 1;
+            for (; it + 3 < nuse; it += 4) {
+                step(1, it, accA, caddA, accB, caddB);
+                step(2, it + 1, accB, caddB, accA, caddA);
+                step(3, it + 2, accA, caddA, accB, caddB);
+                step(0, it + 3, accB, caddB, accA, caddA);
+            }
             for (; it + 1 < nuse; it += 2) {
-                step(it, accA, caddA, accB, caddB);
-                step(it + 1, accB, caddB, accA, caddA);
+                step(it & (kStages - 1), it, accA, caddA, accB, caddB);
+                step((it + 1) & (kStages - 1), it + 1, accB, caddB, accA, caddA);
             }
             if (it < nuse) {
-                step(it, accA, caddA, accB, caddB);
+                step(it & (kStages - 1), it, accA, caddA, accB, caddB);
                 accA = accB;
                 caddA = caddB;
-                ++it;
             }
             // epilogue: finish the last tile
             {
@@ -606,6 +676,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) act_one(accA, c2, r);
             }
+            u32x4 vf[2][4];
+            read_v((nuse - 1) & (kStages - 1), vf);
             u32x4 pk[2];
             tile_pack(nuse - 1, accA, pk);
 #pragma unroll
@@ -615,8 +687,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                     oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
         }
         for (int it = nuse; it < ntiles; ++it) {
-            tile_sync(it);
-            issue_rest(it);
+            tile_sync(it, it & (kStages - 1));
+            issue_rest(it, it & (kStages - 1));
         }
 
         // ---------- O = alpha * acc, rows < L only: bf16 into O (non-temporal:
@@ -675,10 +747,10 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.cursor = const_cast<int32_t*>(a.ctrl) + kXcdCursor;   // the per-XCD cursors
     p.stats = a.stats; p.enc = a.enc;
     p.partial = a.partial; p.rowmap = a.rowmap; p.nblk = a.nblk;
-    p.pos_copy = ((a.P + 128 + 4) + 3) & ~3;
+    p.pos_pairs = a.P + 63 + 28;   // pairs read: u0 + 26 <= Dhi + 26
     p.q_offsets = a.q_offsets; p.ts_q = a.ts_q; p.enc_q = a.enc_q; p.stats_q = a.stats_q; p.nblk_q = a.nblk_q;
     const bool cross = a.q_offsets != nullptr;
-    const size_t smem = ((sizeof(Smem) + 15) & ~size_t(15)) + sizeof(float) * 2 * size_t(p.pos_copy);
+    const size_t smem = ((sizeof(Smem) + 15) & ~size_t(15)) + sizeof(float) * 2 * size_t(p.pos_pairs);
     const void* fn = cross ? (a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true, true>)
                                          : reinterpret_cast<const void*>(attn_bf16_kernel<false, true>))
                            : (a.act == 0 ? reinterpret_cast<const void*>(attn_bf16_kernel<true, false>)

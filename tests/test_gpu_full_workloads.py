@@ -6,8 +6,8 @@ bf16 workloads against the fp64 oracle, element by element.
 - M-FALCON, 8 users x (2048 history + 512 candidates), 4 heads (O, Y and
   every candidate's score);
 - the 4-layer stack: each layer run on the oracle's own input to that layer
-  (rounded to bf16), its increment X_out - X_in and its Y compared with the
-  oracle's, on sampled sequences (the fp64 oracle needs about a minute for
+  (rounded to bf16), its Y and its update X_out - X_in compared with the
+  oracle's on sampled sequences (the fp64 oracle needs about a minute for
   the whole stack), after the whole-batch GPU call.
 
 Each comparison logs max and mean |err| / max|ref| for the whole workload
@@ -89,6 +89,29 @@ def test_mfalcon_every_user():
         assert mx <= 2e-2 and mean <= 2e-3, f"cfg4 user {b} scores: max {mx:.3e} mean {mean:.3e}"
 
 
+def _check_increment(got_inc, out, xin, what):
+    """The layer's update X_out - X_in against the oracle's.  X_out is bf16
+    and the update is far smaller than X (|X| up to ~2.3, the update up to
+    ~0.08 in the stack workload), so X_out's own rounding (half a bf16 ulp of
+    X_out) is larger than the update's error bound.  Compared here: the
+    oracle's output in the output's dtype, bf16(out) - X_in; every element
+    within one bf16 ulp of X_out (a rounding that fell the other way) plus
+    2e-2 max|update|, and the mean within 2e-3 max|update| (an error in the
+    update moves the rounding of a share of the elements, so the mean sees
+    it)."""
+    ref_inc = out - xin
+    scale = float(np.abs(ref_inc).max())
+    ref_out = synth.bf16_round(out.astype(np.float32)).astype(np.float64)
+    err = np.abs(got_inc - (ref_out - xin))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref_out), 2.0 ** -100))) - 7)
+    excess = float(np.max(err - ulp)) / scale
+    mean = float(err.mean()) / scale
+    log(f"{what} X_out - X_in: mean_err/max|update| = {mean:.3e}, max (err - 1 ulp of X_out)/max|update| = "
+        f"{excess:.3e}, raw max_err/max|update| = {float(err.max()) / scale:.3e}")
+    assert mean <= 2e-3, f"{what}: update mean err {mean:.3e}"
+    assert excess <= 2e-2, f"{what}: update err beyond one ulp of X_out {excess:.3e}"
+
+
 def _saved_y(saved, T, H, d):
     """Y from a training forward's saved buffer: Z | pre-activation | O | Y,
     each region at the next multiple of 256 bytes."""
@@ -148,6 +171,6 @@ def test_stack_each_layer_increment_and_y():
             O = oracle.attn(Q.reshape(n, x.H, x.d), K.reshape(n, x.H, x.d), V.reshape(n, x.H, x.d),
                             [0, n], x.ts[s0:s1], x.rab_pos[l], x.rab_time[l], x.alpha)
             Y = oracle.ln_gate(O.reshape(n, hd), U, eps=x.eps)
-            assert_close(inc_g[s0:s1], out - xin, "bf16", f"cfg5 layer {l} seq {b} (L={n}) X_out - X_in")
             assert_close(y_g[s0:s1], Y, "bf16", f"cfg5 layer {l} seq {b} Y")
+            _check_increment(inc_g[s0:s1], out, xin, f"cfg5 layer {l} seq {b} (L={n})")
             cur[b] = out
