@@ -160,6 +160,22 @@ __device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage
                  "{m0}"(lds)
                  : "memory");
 }
+// In-place updates of an accumulator element (the bias of the MFMA's initial
+// accumulator).  Tied operands keep the element in its register on every path
+// through the time-bias branches: with plain code the compiler gave the
+// branches different registers and, on the common constant-bucket path,
+// copied the whole accumulator after waiting for every LDS read in flight.
+// (The inputs come from LDS reads, integer conversions or plain VALU
+// results, never from a transcendental, so no wait states are needed.)
+__device__ __forceinline__ float acc_add(float acc, float x) {
+    asm("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(x));
+    return acc;
+}
+__device__ __forceinline__ float acc_fmac(float acc, float a, float b) {
+    asm("v_fmac_f32 %0, %1, %2" : "+v"(acc) : "v"(a), "v"(b));
+    return acc;
+}
+
 __device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
     issue_k(d, s, stage, kt, far, wave);
     issue_v(d, s, stage, kt, far, wave);
@@ -408,6 +424,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         struct TileFacts {
             bool wide;
             int czlo, czhi, j0;
+            uint32_t pa;   // LDS address of the lane's position entries
         };
         const int xmax = P + 31;   // a lane's first difference past this: all 32 clamp to P-1
         auto tile_bias = [&](int it, int st, f32x16& acc, float& cadd, bf16x8 (&kf)[8]) -> TileFacts {
@@ -427,54 +444,59 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             const uint32_t hi = (uint32_t)max((int)(rmax - kmn), (int)(kmx - rmin));   // farthest pair
             const int czlo = (int)clz_gap(lo), czhi = (int)clz_gap(hi);   // czhi <= czlo
 
-            // LDS reads: position entries, then K (the key codes, when
-            // needed, are read by time_bias)
+            // K fragments now; the position entries (and the key codes, when
+            // needed) are read by time_bias, on each of its paths
             // position bias: lane (row i, keys j0 + 8q + 4h2 + t) reads
             // reversed-table entries u0 + 8q + t (differences x - 8q - t);
             // clamping x to [0, P + 31] keeps every read in the table and
             // changes no value a visible pair reads (past P + 31 all 32 clamp
             // to P - 1; below 0 the keys are past the row, masked)
             cadd = 0.0f;
-            {
-                // entries u0 + 8q + t, u0 = Dhi - x: pairs u0 + 8q and
-                // u0 + 8q + 2, at one base with immediate offsets
-                const int x = min(max(prow4 - j0, 0), xmax);
-                const uint32_t pa = ptab_hi - 8u * (uint32_t)x;
-                typedef float f32x2v __attribute__((ext_vector_type(2)));
-                typedef __attribute__((address_space(3))) const f32x2v lds_f2;
-                const lds_f2* pp = (const lds_f2*)(uintptr_t)pa;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) {
-                        const f32x2v pv = pp[8 * q + 2 * t2];
-                        acc[4 * q + 2 * t2] = pv[0];
-                        acc[4 * q + 2 * t2 + 1] = pv[1];
-                    }
-                }
-            }
+            const int x = min(max(prow4 - j0, 0), xmax);
+            const uint32_t pa = ptab_hi - 8u * (uint32_t)x;   // u0 = Dhi - x
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) kf[kc] = lds_read_b128(kx[kc] + (uint32_t)(st * kStageBytes));
-            return TileFacts{wide, czlo, czhi, j0};
+            return TileFacts{wide, czlo, czhi, j0, pa};
+        };
+        // the position entries u0 + 8q + t as the pairs u0 + 8q and u0 + 8q + 2,
+        // at one base with immediate offsets.  (Read on each path of
+        // time_bias: every definition of the bias then lies on one path, and
+        // the register allocator keeps it in place instead of copying it.)
+        auto load_pos = [&](uint32_t pa, f32x16& acc) {
+            typedef float f32x2v __attribute__((ext_vector_type(2)));
+            typedef __attribute__((address_space(3))) const f32x2v lds_f2;
+            const lds_f2* pp = (const lds_f2*)(uintptr_t)pa;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const f32x2v pv = pp[8 * q + 2 * t2];
+                    acc[4 * q + 2 * t2] = pv[0];
+                    acc[4 * q + 2 * t2 + 1] = pv[1];
+                }
+            }
         };
         auto time_bias = [&](int st, const TileFacts& f, f32x16& acc, float& cadd) {
                 const bool wide = f.wide;
                 const int czlo = f.czlo, czhi = f.czhi, j0 = f.j0;
                 // keys 8q + 4h2 + t sit in wave q's region at 4h2 + t
                 u32x4 codes[4];
-                if (!wide && czlo != czhi) {
+                auto load_codes = [&]() {
                     typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         codes[q] = *(lds_u32x4*)(uintptr_t)(cx + (uint32_t)(st * 4 * 64 * 4 + 256 * q));
-                }
+                };
                 // time bias: constant over the block (most blocks), one of two
                 // buckets split at a power of two, or per element
                 if (!wide && czlo - czhi <= 1) {
                     const float tlo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ttv, czlo));
                     if (czlo == czhi) {
+                        load_pos(f.pa, acc);
                         cadd += tlo;
                     } else {
+                        load_codes();
+                        load_pos(f.pa, acc);
                         // g = |e_i - e_j| + 1 lies in [2^(31 - czlo), 2^(33 - czlo)),
                         // and the bucket is czhi exactly when bit 32 - czlo of g
                         // is set: g >> (32 - czlo) is 0 or 1, the bucket's share
@@ -487,16 +509,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                         for (int q = 0; q < 4; ++q)
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
-                                acc[4 * q + t] = __builtin_fmaf((float)(sad_u32(tie, codes[q][t], 1u) >> sh), dt,
-                                                                acc[4 * q + t]);
+                                acc[4 * q + t] = acc_fmac(acc[4 * q + t], (float)(sad_u32(tie, codes[q][t], 1u) >> sh), dt);
                     }
                 } else if (!wide) {
+                    load_codes();
+                    load_pos(f.pa, acc);
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            acc[4 * q + t] += s.tt_fast[__builtin_clz(sad_u32(tie, codes[q][t], 1u))];
+                            acc[4 * q + t] = acc_add(acc[4 * q + t], s.tt_fast[__builtin_clz(sad_u32(tie, codes[q][t], 1u))]);
                 } else {
+                    load_pos(f.pa, acc);
                     const int64_t* tsb = p.ts + row0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -506,7 +530,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                             const int64_t tj = j < L ? tsb[j] : t_first;
                             const int64_t dt = ti64 - tj;
                             const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                            acc[4 * q + t] += s.tt_wide[bit_length_u64(ad)];
+                            acc[4 * q + t] = acc_add(acc[4 * q + t], s.tt_wide[bit_length_u64(ad)]);
                         }
                     }
                 }
@@ -586,18 +610,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         auto step = [&](int st, int it, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
             tile_sync(it, st);
             bf16x8 kf[8];
-            const TileFacts f = tile_bias(it, st, accN, caddN, kf);
+            // the bias goes in as the first MFMA's C operand only: the chain
+            // then writes the loop's accumulator registers directly
+            f32x16 bias;
+            const TileFacts f = tile_bias(it, st, bias, caddN, kf);
             const float c2 = act_const(caddC);
             // the first activations cover the LDS latency of this tile's reads
 #pragma unroll
             for (int r = 0; r < 4; ++r) act_one(accC, c2, r);
-            time_bias(st, f, accN, caddN);
+            time_bias(st, f, bias, caddN);
             issue_rest(it, st);
             // S(it) = K Q^T: a dependent chain of 8 MFMAs, each followed by
             // the activation of 1.5 elements of S(it-1)
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) {
-                accN = mfma32(kf[kc], qf[kc], accN);
+                accN = mfma32(kf[kc], qf[kc], kc == 0 ? bias : accN);
                 if (kc < 6) {
                     act_one(accC, c2, 4 + 2 * kc);
                     act_one(accC, c2, 5 + 2 * kc);
@@ -645,11 +672,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             {
                 tile_sync(0, 0);
                 bf16x8 kf[8];
-                const TileFacts f = tile_bias(0, 0, accA, caddA, kf);
-                time_bias(0, f, accA, caddA);
+                f32x16 bias;
+                const TileFacts f = tile_bias(0, 0, bias, caddA, kf);
+                time_bias(0, f, bias, caddA);
                 issue_rest(0, 0);
 #pragma unroll
-                for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], accA);
+                for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], kc == 0 ? bias : accA);
             }
             // steps 1, 2, 3, 4, ...: stages 1, 2, 3, 0, ..., S alternating
             // between the two accumulators; four steps per iteration, then
