@@ -170,6 +170,7 @@ class SlArgs(ctypes.Structure):
 EXPORTS = [
     "hstu_abi_version", "hstu_status_string", "hstu_last_error",
     "hstu_attn_workspace_bytes", "hstu_attn_fwd",
+    "hstu_attn_fwd_noalloc", "hstu_attn_noalloc_scratch_bytes",
     "hstu_mfalcon_workspace_bytes", "mfalcon_score",
     "hstu_mfalcon_cached_workspace_bytes", "mfalcon_score_cached",
     "hstu_layer_workspace_bytes", "hstu_layer_fwd",
@@ -209,6 +210,10 @@ def load(path: str = LIB_PATH):
     lib.hstu_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.hstu_attn_fwd.restype = _i32
     lib.hstu_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t, _vp]
+    lib.hstu_attn_fwd_noalloc.restype = _i32
+    lib.hstu_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.hstu_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.hstu_attn_noalloc_scratch_bytes.argtypes = []
     lib.hstu_mfalcon_workspace_bytes.restype = ctypes.c_size_t
     lib.hstu_mfalcon_workspace_bytes.argtypes = [ctypes.POINTER(MfalconArgs)]
     lib.mfalcon_score.restype = _i32

@@ -139,9 +139,16 @@ hstu::SchedLayout sched_layout_for(const hstu_attn_args* a, size_t base) {
                               bf16 ? a->num_rows : 0, base);
 }
 
-Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base) {
+// The same layout with at most max_slots split-partial slots.
+hstu::SchedLayout sched_layout_for_slots(const hstu_attn_args* a, int max_slots, size_t base = 0) {
+    const bool bf16 = a->dtype == HSTU_BF16;
+    return hstu::sched_layout(a->B, a->H, a->max_seq_len, tile_m_for(a->dtype), bf16 ? a->d_v : 0,
+                              bf16 ? a->num_rows : 0, base, max_slots);
+}
+
+Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base, int max_slots = hstu::kMaxPartialSlots) {
     Sched s;
-    s.layout = sched_layout_for(a, base);
+    s.layout = sched_layout_for_slots(a, max_slots, base);
     uint8_t* w = static_cast<uint8_t*>(ws);
     s.ctrl = reinterpret_cast<int32_t*>(w + s.layout.off_ctrl);
     s.qscan = reinterpret_cast<int32_t*>(w + s.layout.off_qscan);
@@ -264,6 +271,42 @@ hipError_t run_ln_gate(const hstu_attn_args* a, const Sched& s, const float* w, 
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- the scratch buffer of hstu_attn_fwd_noalloc
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid it): a file-scope
+// device array that every GPU the library runs on holds from module load to
+// the end of the process.  Host code must not pass the array's name to a
+// kernel (on the host it is only a stand-in, not the device address): its
+// device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept.  Calls on one GPU share the array (and
+// leave their contents in it); the scheduler kernel rewrites every word a
+// call reads before the call reads it, including the work cursors, so
+// nothing needs clearing -- but calls that may overlap on one GPU (streams
+// without ordering between them) race.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // ---- M-FALCON against a history cache
 
@@ -434,6 +477,52 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, void* ws, size_t ws_bytes, vo
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     Sched s = carve_sched(a, ws, 0);
     hipError_t e = run_sched(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "scheduler launch");
+    e = run_core(a, s, stream);
+    if (e != hipSuccess) return device_error(e, "attention launch");
+    if (a->y) {
+        e = run_ln_gate(a, s, nullptr, nullptr, 0, false, stream);
+        if (e != hipSuccess) return device_error(e, "epilogue launch");
+    } else {
+        e = run_combine(a, s, stream);
+        if (e != hipSuccess) return device_error(e, "split combine launch");
+    }
+    return ok();
+}
+
+size_t hstu_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_args* a, void* stream_) {
+    hstu_status st = validate_attn(a, false);
+    if (st != HSTU_OK) return st;
+    if (a->B == 0) return ok();
+    // the layout hstu_attn_fwd would use, with as many split-partial slots
+    // as still fit (each holds BM x d_v fp32): the size check is host
+    // arithmetic, done before any HIP call
+    hstu::SchedLayout l = sched_layout_for(a, 0);
+    if (l.bytes > kNoAllocScratchBytes && l.part_slots > 0) {
+        const size_t slot_bytes = size_t(hstu::kBf16TileM) * size_t(a->d_v) * sizeof(float);
+        const size_t fixed = sched_layout_for_slots(a, 0).bytes;
+        const int fit = fixed >= kNoAllocScratchBytes ? 0 : (int)((kNoAllocScratchBytes - fixed) / slot_bytes);
+        // the item list grows with the slots as well: step down until it fits
+        int slots = std::min(fit, l.part_slots);
+        for (;;) {
+            l = sched_layout_for_slots(a, slots);
+            if (l.bytes <= kNoAllocScratchBytes || slots == 0) break;
+            slots = slots * 7 / 8;
+        }
+    }
+    if (l.bytes > kNoAllocScratchBytes)
+        return fail(HSTU_ERR_WORKSPACE,
+                    "hstu_attn_fwd_noalloc: the call needs %zu bytes of scratch, more than the %zu the library holds "
+                    "per GPU (use hstu_attn_fwd with a workspace)",
+                    l.bytes, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return device_error(e, "locating the library's scratch buffer");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    Sched s = carve_sched(a, ws, 0, l.part_slots);
+    e = run_sched(a, s, stream);
     if (e != hipSuccess) return device_error(e, "scheduler launch");
     e = run_core(a, s, stream);
     if (e != hipSuccess) return device_error(e, "attention launch");

@@ -78,7 +78,7 @@ struct SchedLayout {
 
 // split_d: head dim of the partial slots (0 disables splitting).
 SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d, int64_t num_rows,
-                         size_t base_offset);
+                         size_t base_offset, int max_part_slots = kMaxPartialSlots);
 
 struct SchedArgs {
     int B;

@@ -467,13 +467,17 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d, int64_t num_rows,
-                         size_t base) {
+                         size_t base, int max_part_slots) {
     SchedLayout l;
     l.cap = size_t(B) * size_t((max_seq_len + tile_m - 1) / tile_m);
     l.nblk = (max_seq_len + kTsBlock - 1) / kTsBlock;
     l.cap_blk = size_t(B) * size_t(l.nblk);
-    // partial slots: at most kMaxPartialSlots, and no more than 8 per row block and head
-    l.part_slots = split_d > 0 && H > 0 ? (int)std::min<size_t>(kMaxPartialSlots, l.cap * size_t(H) * 8) : 0;
+    // partial slots: at most max_part_slots (<= kMaxPartialSlots), and no
+    // more than 8 per row block and head
+    l.part_slots = split_d > 0 && H > 0
+                       ? (int)std::min<size_t>(size_t(std::max(0, std::min(max_part_slots, kMaxPartialSlots))),
+                                               l.cap * size_t(H) * 8)
+                       : 0;
     l.cap_pieces = l.cap + (H > 0 ? size_t(l.part_slots) / size_t(H) : 0);
     l.off_ctrl = align256(base);
     l.off_qscan = align256(l.off_ctrl + kCtrlInts * sizeof(int32_t));

@@ -119,6 +119,24 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
     return o, (y if u is not None else None)
 
 
+def hstu_attn_fwd_noalloc(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
+                          max_seq_len: int, seq_lengths=None, num_candidates=None, u=None,
+                          ln_eps: float = 1e-5, act: int = _lib.HSTU_ACT_SILU, o=None, y=None,
+                          stream=None):
+    """hstu_attn_fwd without a workspace (the library's own scratch buffer;
+    for callers that cannot allocate).  o and y must be given: the call
+    allocates nothing."""
+    lib = _lib.load()
+    if o is None or (u is not None and y is None):
+        raise ValueError("hstu_attn_fwd_noalloc allocates nothing: pass o (and y with u)")
+    args = make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha,
+                          max_seq_len=max_seq_len, o=o, seq_lengths=seq_lengths,
+                          num_candidates=num_candidates, u=u, y=y if u is not None else None,
+                          ln_eps=ln_eps, act=act)
+    _lib.check(lib.hstu_attn_fwd_noalloc(ctypes.byref(args), _stream_ptr(stream)))
+    return o, (y if u is not None else None)
+
+
 def make_attn_bwd_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
                        max_seq_len: int, dq, dk, dv, dout=None, dy=None, o=None, u=None,
                        du=None, ln_eps: float = 1e-5, seq_lengths=None, num_candidates=None,

@@ -34,7 +34,9 @@
  *   - All data pointers are DEVICE pointers unless stated otherwise.  The
  *     caller owns every buffer; the library never allocates or frees device
  *     memory.  Scratch memory is a caller-provided workspace whose size is
- *     returned by the matching *_workspace_bytes() query.
+ *     returned by the matching *_workspace_bytes() query -- except for
+ *     hstu_attn_fwd_noalloc, whose scratch is a fixed device array of the
+ *     library (loaded with it on each GPU).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every entry point
  *     checks its arguments synchronously, then enqueues its kernels on
  *     `stream` and returns without synchronising.  Device-side faults surface
@@ -145,6 +147,23 @@ size_t hstu_attn_workspace_bytes(const hstu_attn_args* args);
  * HSTU_ERR_DEVICE. */
 hstu_status hstu_attn_fwd(const hstu_attn_args* args, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* hstu_attn_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, kernels and results, but no workspace: the work list,
+ * timestamp codes and split-block partial sums live in a scratch buffer the
+ * library holds on every GPU it runs on (hstu_attn_noalloc_scratch_bytes()
+ * bytes, 32 MiB, from module load to the end of the process).  The call
+ * allocates and frees nothing; it may use fewer split-block partial slots
+ * than hstu_attn_fwd (rows then match to rounding, not bit for bit).  Calls
+ * on one GPU share its buffer: calls that may overlap on one GPU (streams
+ * with no ordering between them) race.  Errors: as hstu_attn_fwd, and
+ * HSTU_ERR_WORKSPACE (before any launch) when the call needs more scratch
+ * than the buffer holds. */
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_args* args, void* stream);
+
+/* Bytes of the library-held scratch buffer of hstu_attn_fwd_noalloc. */
+size_t hstu_attn_noalloc_scratch_bytes(void);
 
 /* --------------------------------------------------- M-FALCON ranking pass */
 /* One forward pass scoring b_m candidates per user against the shared

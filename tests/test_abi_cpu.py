@@ -454,3 +454,18 @@ def test_mfalcon_layer_validation(lib):
     m.struct_size = 4
     assert lib.mfalcon_layer_score(ctypes.byref(m), None, 0, None) == _lib.HSTU_ERR_ARG
     assert lib.hstu_mfalcon_layer_workspace_bytes(ctypes.byref(m)) == 0
+
+
+def test_noalloc_entry_point_host_checks(lib):
+    """hstu_attn_fwd_noalloc: the same argument checks as hstu_attn_fwd, and a
+    call needing more scratch than the library's fixed buffer is refused
+    before any launch (no GPU here: every case must fail on the host)."""
+    assert lib.hstu_attn_noalloc_scratch_bytes() == 32 << 20
+    for name, mut, status in MUTATIONS:
+        a = _valid_args()
+        mut(a)
+        assert lib.hstu_attn_fwd_noalloc(ctypes.byref(a), None) == status, name
+    a = _valid_args()
+    a.num_rows = 5_000_000            # 8 bytes of codes and split map per row: 40 MB
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.HSTU_ERR_WORKSPACE
+    assert b"noalloc" in lib.hstu_last_error()
