@@ -218,6 +218,108 @@ __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
     }
 }
 
+// The common case -- bf16, a packed causal batch (no padding, no candidates,
+// no scores), Y wanted -- with R rows per wave: the map entries and operand
+// rows of all R rows are fetched before any arithmetic, so that a wave keeps
+// R times more bytes in flight (one row of H*d_v = 512 values is only 2 KB
+// of loads).  Split rows (map entry >= 0) take their O from the partial sums
+// as in ln_gate_kernel.
+template <int NCH, int R>
+__global__ void __launch_bounds__(kThreads) ln_gate_rows_kernel(LnGateArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row0 = ((int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6)) * R;
+    const int64_t lo = a.offsets[0], hi = min((int64_t)a.offsets[a.B], a.num_rows);
+    const int W = a.width;
+    if (row0 >= hi || row0 + R <= lo) return;
+    // Loads are unconditional, from rows clamped into [lo, hi) and columns
+    // clamped into the row, so that no branch joins in-flight registers;
+    // the pairs stay raw bf16 until the last load is issued, which keeps
+    // every load of the wave in flight together.
+    int code[R];
+    u32x4 xr[R][NCH], ur[R][NCH];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int64_t row = min(max(row0 + k, lo), hi - 1);
+        code[k] = a.rowmap ? a.rowmap[row] : -1;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * 64 + lane) * 8 < W ? (c * 64 + lane) * 8 : 0;
+            xr[k][c] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.o) + row * a.o_stride + col));
+            ur[k][c] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.u) + row * a.u_stride + col));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int64_t row = row0 + k;
+        if (!(row >= lo && row < hi)) continue;
+        if (code[k] >= 0) {
+            // O of a split row: slot | pieces << 16 | (row within block) << 23
+            const int slot = code[k] & 0xffff, np = (code[k] >> 16) & 0x7f, lr = code[k] >> 23;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int col = (c * 64 + lane) * 8;
+                if (col < W) {
+                    const int h = col / a.d;
+                    const int cc = col - h * a.d;
+                    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    for (int pc = 0; pc < np; ++pc) {
+                        const float* src = a.partial + ((int64_t)(slot + pc) * a.H + h) * a.BM * a.d +
+                                           (int64_t)lr * a.d + cc;
+                        const f32x4 p0 = *reinterpret_cast<const f32x4*>(src);
+                        const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            acc[e] += p0[e];
+                            acc[4 + e] += p1[e];
+                        }
+                    }
+                    u32x4 r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+                    xr[k][c] = r;
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + row * a.o_stride + col) = r;
+                }
+            }
+        }
+        float x[NCH][8], u[NCH][8];
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            if ((c * 64 + lane) * 8 < W)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[c][2 * e] = __uint_as_float(xr[k][c][e] << 16);
+                    x[c][2 * e + 1] = __uint_as_float(xr[k][c][e] & 0xffff0000u);
+                    u[c][2 * e] = __uint_as_float(ur[k][c][e] << 16);
+                    u[c][2 * e + 1] = __uint_as_float(ur[k][c][e] & 0xffff0000u);
+                    sum += x[c][2 * e] + x[c][2 * e + 1];
+                }
+        const float mean = wave_sum(sum) / (float)W;
+        float sq = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            if ((c * 64 + lane) * 8 < W)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dlt = x[c][e] - mean;
+                    sq = fmaf(dlt, dlt, sq);
+                }
+        const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)W + a.eps);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int col = (c * 64 + lane) * 8;
+            if (col < W) {
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = (x[c][e] - mean) * rstd * u[c][e];
+                Vec8<true>::store(a.y, row * a.y_stride + col, y);
+            }
+        }
+    }
+}
+
 // Gradients of Y = LN(O) (.) U for bf16 rows (one wave per row): with
 // xhat = (O - mean) rstd,
 //   dU = xhat (.) dY,   g = dY (.) U,   dO = rstd (g - mean(g) - xhat mean(g xhat))
@@ -297,6 +399,16 @@ __global__ void __launch_bounds__(kThreads) ln_gate_bwd_kernel(LnGateBwdArgs a) 
 template <bool BF16>
 hipError_t launch_typed(const LnGateArgs& a, hipStream_t stream) {
     const int nch = (a.width + 511) / 512;
+    if (BF16 && a.B > 0 && !a.lengths && !a.ncand && !a.cross && !a.w && a.y && nch <= 2 && !a.cand_only) {
+        if (nch == 1) {
+            const dim3 g((unsigned)((a.num_rows + 4 * kRowsPerBlock - 1) / (4 * kRowsPerBlock)));
+            hipLaunchKernelGGL((ln_gate_rows_kernel<1, 4>), g, dim3(kThreads), 0, stream, a);
+        } else {
+            const dim3 g((unsigned)((a.num_rows + 2 * kRowsPerBlock - 1) / (2 * kRowsPerBlock)));
+            hipLaunchKernelGGL((ln_gate_rows_kernel<2, 2>), g, dim3(kThreads), 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock));
     switch (nch) {
         case 1: hipLaunchKernelGGL((ln_gate_kernel<BF16, 1>), grid, dim3(kThreads), 0, stream, a); break;
