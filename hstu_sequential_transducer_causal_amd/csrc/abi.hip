@@ -401,13 +401,17 @@ hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
         const int64_t widest = std::max(a.q_stride, gstride);
         if (int64_t(a.max_seq_len) * 2 * widest > int64_t(0x7fffffff))
             return fail(HSTU_ERR_UNSUPPORTED, "max_seq_len * Q/dO row bytes must stay below 2^31");
+        // one 32-row query tile's G blocks (fp32, every head) in one buffer range
+        if ((int64_t(a.max_seq_len) / 32 + 1) * a.H * 4096 > int64_t(0x7fffffff))
+            return fail(HSTU_ERR_UNSUPPORTED, "(max_seq_len / 32 + 1) * H * 4096 must stay below 2^31");
     }
     return HSTU_OK;
 }
 
 struct BwdWs {
     hstu::SchedLayout q, kv;   // query-major and key-major work lists
-    size_t dout, part, part2, total;
+    size_t dout, part, part2, gbase, gbuf, total;
+    int64_t gcap;              // G blocks (32 x 32 fp32, per head) the buffer holds
 };
 
 BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
@@ -419,8 +423,11 @@ BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
     w.part = align256(w.dout + (g->dy ? size_t(a.num_rows) * size_t(a.H) * size_t(a.d_v) * 2 : 0));
     w.part2 = align256(w.part + sizeof(float) * hstu::attn_bwd_rab_part_floats(
                                                     (int64_t)w.q.cap, a.H, a.num_pos_buckets, a.num_time_buckets));
-    w.total = align256(w.part2 + sizeof(float) * hstu::attn_bwd_rab_part2_floats(a.H, a.num_pos_buckets,
+    w.gbase = align256(w.part2 + sizeof(float) * hstu::attn_bwd_rab_part2_floats(a.H, a.num_pos_buckets,
                                                                                   a.num_time_buckets));
+    w.gbuf = align256(w.gbase + sizeof(int64_t) * size_t(a.B > 0 ? a.B : 0));
+    w.gcap = hstu::attn_bwd_g_blocks(a.B, a.max_seq_len, a.num_rows);
+    w.total = align256(w.gbuf + size_t(w.gcap) * size_t(a.H) * 1024 * sizeof(float));
     return w;
 }
 
@@ -1297,6 +1304,10 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
     b.num_rows = a->num_rows;
     b.rab_part = reinterpret_cast<float*>(wb + w.part);
     b.rab_part2 = reinterpret_cast<float*>(wb + w.part2);
+    b.gbase = reinterpret_cast<int64_t*>(wb + w.gbase);
+    b.gbuf = reinterpret_cast<float*>(wb + w.gbuf);
+    b.gcap = w.gcap;
+    b.B = a->B;
     b.ev_dq_begin = static_cast<hipEvent_t>(g->ev_dq_begin);
     b.ev_dq_end = static_cast<hipEvent_t>(g->ev_dq_end);
     b.ev_dkv_begin = static_cast<hipEvent_t>(g->ev_dkv_begin);

@@ -77,6 +77,9 @@ struct BwdParams {
     const uint32_t* stats;
     const uint32_t* enc;
     float* rab_part;                        // [work][P + NT] (dq kernel)
+    float* gbuf;                            // G blocks (written by dK/dV, read by dQ)
+    const int64_t* gbase;
+    int64_t gcap;
 };
 
 // Small LDS state after the tile ring.
@@ -157,10 +160,6 @@ __device__ __forceinline__ TimeBlock time_block(uint32_t amn, uint32_t amx, uint
 // Floats per copy of the dK/dV kernel's padded position table (P + 128,
 // rounded up to a multiple of 4).
 __host__ __device__ __forceinline__ int ptab2_width(int P) { return (P + 128 + 3) & ~3; }
-// Floats per copy of the dQ kernel's reversed position table (covers the
-// entries u0 + 0 .. 31 for every clamped u0 = P + 63 - x, x in [0, P + 26],
-// plus the shift of the second copy).
-__host__ __device__ __forceinline__ int rtab_width(int P) { return (P + 132 + 3) & ~3; }
 
 // Activation value and slope: SiLU (x s, s + x s (1 - s) with s = sigmoid(x))
 // or the identity (x, 1).
@@ -240,26 +239,51 @@ __device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int tot
 }
 
 // ---------------------------------------------------------------------------
-// dQ and the table gradients (query-major)
+// dQ and the table gradients (query-major), from the G blocks the dK/dV
+// kernel stored
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, const void* ws_base, uint32_t ws_bytes) {
+// A block of G arrives as the dK/dV kernel held it: lane = key (l % 32), the
+// 16 values of queries 8 (r / 4) + 4 (l / 32) + r % 4.  dQ contracts over
+// keys, so the block is turned over first, by two MFMAs against the identity:
+// packed to bf16 it is an A operand with the keys as rows and the queries as
+// the contraction, and the product with the identity on the queries is the
+// block with the queries as columns -- lane = query, the 16 values of keys
+// 8 (r / 4) + 4 (l / 32) + r % 4, the orientation of dQ's own S^T.  G goes
+// through as two bf16 halves (hi = bf16(G), lo = bf16(G - hi), 16
+// significant bits in all), accumulated exactly in fp32, so the table
+// gradients see G to within 2^-17 of itself; the dQ product takes it
+// rounded to bf16.
+__device__ __forceinline__ void identity_frags(int lane, bf16x8 (&idf)[2]) {
+    // B operand lane l: column n = l % 32, k slots 8 (l / 32) + e; slot e of
+    // chunk c stands for query 16 c + 8 (e / 4) + 4 (l / 32) + e % 4
+    const int n = lane & 31, h2 = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if ((n >> 4) == c && ((n >> 2) & 1) == h2) {
+            const int e = 4 * ((n >> 3) & 1) + (n & 3);
+            z[e >> 1] = 0x3F80u << (16 * (e & 1));
+        }
+        idf[c] = __builtin_bit_cast(bf16x8, z);
+    }
+}
+
+__device__ __forceinline__ int64_t tri(int q) { return (int64_t)q * (q + 1) / 2; }
+
+// A G block is stored when it holds a visible pair: k <= q, and history keys
+// in the key tile or the diagonal tile (candidate keys are seen by their own
+// row alone).
+__device__ __forceinline__ bool g_block_live(int q, int k, int n) { return k <= q && (32 * k < n || k == q); }
+
+__global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, const void* ws_base, uint32_t ws_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* ring_k = smem;                          // K, kswz: A operand of S^T = K Q^T
-    uint8_t* ring_kt = smem + kStages * kTileBytes;  // K, vswz: B operand of dQ += G K
-    uint8_t* ring_v = smem + 2 * kStages * kTileBytes;   // V, kswz: A operand of V dO^T
-    Small& s = small_of<3>(smem);
-    // the position table reversed, in two copies shifted by one (as in the
-    // forward): copy c holds R[w - c] at w, R[u] = rab_pos[clamp(Dhi - u, 0,
-    // P - 1)], so a lane reads the entries of its row against 2 keys with one
-    // aligned 8-byte load; rab_pos[pb] itself is R[Dhi - pb]
-    const int rw = rtab_width(p.P);
-    const int Dhi = p.P + 63;
-    float* rtab = ptab_of<3>(smem);
+    uint8_t* ring_kt = smem;   // K, vswz: B operand of dQ += G K
+    Small& s = small_of<1>(smem);
     // one histogram per wave ([P] position, then [NT] time buckets), so that
     // the order of the additions into each does not depend on how the waves
     // interleave; added in wave order at the end of the item
     const int hw = (p.P + p.NT + 3) & ~3;
-    float* hist_all = rtab + 2 * rw;
+    float* hist_all = ptab_of<1>(smem);
     // per wave, a scratch in which the block's G is written skewed and
     // transposed (column rho - c + 31, row rho; kDiagPitch floats per
     // column), so that each column holds one diagonal and its 32 entries are
@@ -275,13 +299,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
     const int l32 = lane & 31;
     const int h2 = lane >> 5;
     const int total_work = p.ctrl[0] * p.H;
-    const bool shared_tables = (p.rp_hs == 0) && (p.rt_hs == 0);
-    const bool silu = p.act == 0;
     const int P = p.P, NT = p.NT;
-    const int per_tile = uni(wave == 0 ? 7 : 6);
     const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
     const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
-    int loaded_head = -1;
+    bf16x8 idf[2];
+    identity_frags(lane, idf);
 
     float* hist = hist_all + wave * hw;
     float* scratch = scratch_all + wave * (64 * kDiagPitch);
@@ -301,61 +323,53 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
         const int n = uni(p.ncand ? L - p.ncand[b] : L);
         const int bbase = b * p.nblk;
 
-        if (loaded_head < 0 || (!shared_tables && loaded_head != h)) {
-            const float* rp = p.rab_pos + (int64_t)h * p.rp_hs;
-            const float* rt = p.rab_time + (int64_t)h * p.rt_hs;
-            for (int e = tid; e < 2 * rw; e += kThreads) {
-                const int c = e >= rw ? 1 : 0;
-                const int u = e - c * rw - c;
-                rtab[e] = rp[min(max(Dhi - u, 0), P - 1)];
-            }
-            if (tid < 32) s.tt_fast[tid] = rt[min(NT - 1, 31 - tid)];
-            if (tid < 65) s.tt_wide[tid] = rt[min(NT - 1, tid)];
-            loaded_head = h;
-            lds_wait();   // visible to all after the first tile's barrier
-        }
-
         auto tile_of = [&](int pos) { return pos < a_end ? pos : kb_begin + (pos - a_end); };
-        const TileSrc sk = tile_src(p.k + row0 * p.ks + h * HD, p.ks, L, lane, wave, false);
         const TileSrc skt = tile_src(p.k + row0 * p.ks + h * HD, p.ks, L, lane, wave, true);
-        const TileSrc sv = tile_src(p.v + row0 * p.vs + h * HD, p.vs, L, lane, wave, false);
         const int64_t enc_row0 = enc_base + 4 * row0;
+
+        // ---- this wave's query tile q and the G blocks of its row: one
+        //      buffer range from block (q, 0) on, so that the blocks it does
+        //      not read (or that lie past the buffer's capacity) arrive as
+        //      zeros without a memory access
+        const int q = qt * (kBlk / 32) + wave;
+        const int wrow0 = q * 32;
+        const bool wave_rows = wrow0 < L;
+        __amdgpu_buffer_rsrc_t grs;
+        {
+            const int64_t blk0 = wave_rows ? p.gbase[b] + tri(q) : 0;
+            const int64_t room = max((int64_t)0, min((int64_t)(q + 1), p.gcap - blk0));
+            grs = __builtin_amdgcn_make_buffer_rsrc(p.gbuf + blk0 * p.H * 1024, (short)0,
+                                                    wave_rows ? (int)(room * p.H * 4096) : 0, 0x00020000);
+        }
+        const uint32_t glane = (uint32_t)(lane * 64);
+        auto g_live = [&](int k) { return wave_rows && g_block_live(q, k, n); };
+        // (every step issues its four loads, past the list's end from out of
+        // range, so that the compiler sees the same loads in flight on every
+        // path and waits for a block only when it is used)
+        auto load_g = [&](int pos, f32x16& g) {
+            const int k = tile_of(pos);
+            const uint32_t off = pos < ntiles && g_live(k) ? (uint32_t)((k * p.H + h) * 4096) + glane : 0x80000000u;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 x = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, off + 16 * m, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) g[4 * m + e] = x[e];
+            }
+        };
         auto issue = [&](int stage, int tile) {
-            issue_part(sk, ring_k, stage, tile, wave);
             issue_part(skt, ring_kt, stage, tile, wave);
-            issue_part(sv, ring_v, stage, tile, wave);
             if (wave == 0) issue_codes(wrs, enc_row0, s, stage, tile, L, lane);
         };
-#pragma unroll
-        for (int pre = 0; pre < kStages - 1; ++pre)
-            if (pre < ntiles) issue(pre, tile_of(pre));
 
-        // ---- this wave's 32 query rows: Q and dO as B operands (lane = row)
-        const int wrow0 = qt * kBlk + wave * 32;
         const int i = wrow0 + l32;
         const bool row_valid = i < L;
-        bf16x8 qf[8], gf[8];
-        {
-            const uint16_t* qp = p.q + (row0 + i) * p.qs + h * HD + h2 * 8;
-            const uint16_t* gp = p.g + (row0 + i) * p.gs + h * HD + h2 * 8;
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                qf[kc] = load_frag(qp + kc * 16, row_valid);
-                gf[kc] = load_frag(gp + kc * 16, row_valid);
-            }
-        }
         const int64_t t_first = p.ts[row0];
         int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
         uint32_t ei = row_valid ? p.enc[row0 + i] : 0x80000000u;
-        const bool wave_rows = wrow0 < L;
-        const int qblk = bbase + qt * (kBlk / 32) + wave;
+        const int qblk = bbase + q;
         uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
         uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
-#pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
-            settle(qf[kc]);
-            settle(gf[kc]);
-        }
         settle(ti64);
         settle(ei);
         settle(rmin);
@@ -364,8 +378,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
         rmax = uniu(rmax);
         const int prow = min(i, n);
         const int prow_min = uni(min(wrow0, n));
-        const int vis_lim = i >= L ? -1 : (i < n ? i : n - 1);
-        const int vis_self = (i >= n && i < L) ? i : -1;
+
+        f32x16 gA, gB;
+        if (0 < ntiles) issue(0, tile_of(0));
+        load_g(0, gA);
+        if (1 < ntiles) issue(1, tile_of(1));
+        load_g(1, gB);
 
         f32x16 dqa[4];
 #pragma unroll
@@ -374,33 +392,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             for (int r = 0; r < 16; ++r) dqa[nb][r] = 0.0f;
 
         const StatsPtr kstats = stats_ptr(p.stats);
-        // ---- software pipeline over the key tiles: step t builds S^T(t)
-        //      (bias as the initial accumulator) and (dO V^T)^T(t) while the
-        //      activation slope and G of tile t-1 run on the VALU between those
-        //      MFMAs; then tile t-1's mask, block sums, dQ += G K and histogram
-        //      updates.  Tile t's K^T fragments (for dQ) are read into
-        //      registers at the end of step t, and its time buckets are kept
-        //      packed, so its stage may be refilled after the next barrier.
-        const uint32_t a_off = k_lane_offset(lane), t_off = v_lane_offset(lane);
-        const float pos_far = rtab[Dhi - (P - 1)];
-        u32x4 trk[2][4];   // K^T fragments of the tile being finished
+        const uint32_t t_off = v_lane_offset(lane);
         struct Tile {
-            float cadd;
             int j0, tlo, thi;
-            bool full, pos_clamped, tconst, few;
+            bool pos_clamped, tconst, few;
             uint32_t tb4[4];   // time bucket of element r in byte r % 4 of word r / 4
         };
 
-        auto sync = [&](int t) {
-            wait_tile(t + 1 < ntiles ? per_tile : 0);   // tile t has landed (t+1 may be in flight)
-            lds_sync();                                   // and every wave is done with tile t-1's stage
-            if (t + kStages - 1 < ntiles) issue((t + kStages - 1) % kStages, tile_of(t + kStages - 1));
-        };
-
-        auto prep = [&](int t, f32x16& sacc, bf16x8 (&ka)[8], bf16x8 (&va)[8]) -> Tile {
-            const int kt = tile_of(t);
+        // block classification and, for blocks spanning several time buckets,
+        // the bucket of every element
+        auto classify = [&](int kt, int stage) -> Tile {
             const int j0 = kt * 32;
-            const int stage = t % kStages;
             const u32x2 kr = kstats[bbase + kt];
             const TimeBlock tb = time_block(rmin, rmax, kr[0], kr[1]);
             Tile st;
@@ -410,46 +412,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             st.tlo = min(NT - 1, 31 - tb.cz);
             st.thi = min(NT - 1, 31 - tb.czhi);
             st.few = !tb.constant && !tb.wide && st.thi - st.tlo < 4;
-            st.full = (j0 + 32 <= n) && (j0 + 31 <= wrow0) && (wrow0 + 31 < L);
-            st.cadd = 0.0f;
-            if (st.pos_clamped) st.cadd += pos_far;
-            if (tb.constant) st.cadd += s.tt_fast[tb.cz];
-            // position bias (keys j = j0 + c, c = 8q + 4h2 + t): a block of
-            // history keys reads entries u0 + 8q + t of the reversed table,
-            // a block holding candidate keys per element
-            if (st.pos_clamped) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-            } else if (j0 + 31 < n) {
-                const int x = min(max(prow - (j0 + 4 * h2), 0), P + 26);
-                const int u0 = Dhi - x;
-                const int c = u0 & 1;
-                const float* pp = rtab + c * rw + (u0 + c);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) {
-                        const float2 pv = *reinterpret_cast<const float2*>(pp + 8 * q + 2 * t2);
-                        sacc[4 * q + 2 * t2] = pv.x;
-                        sacc[4 * q + 2 * t2 + 1] = pv.y;
-                    }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    sacc[r] = rtab[Dhi - min(max(prow - min(j, n), 0), P - 1)];
-                }
-            }
-            const uint8_t* k_lds = ring_k + stage * kTileBytes;
-            const uint8_t* v_lds = ring_v + stage * kTileBytes;
-            uint32_t ao = a_off;
-            asm volatile("" : "+v"(ao));
-            const uint32_t kb = lds_addr(k_lds) + ao, vb = lds_addr(v_lds) + ao;
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                ka[kc] = lds_read_b128(kb ^ (uint32_t)(kc << 5));
-                va[kc] = lds_read_b128(vb ^ (uint32_t)(kc << 5));
-            }
 #pragma unroll
             for (int w4 = 0; w4 < 4; ++w4) st.tb4[w4] = 0u;
             if (!tb.constant) {
@@ -459,17 +421,13 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                     const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
                     int tbr;
                     if (!tb.wide) {
-                        const uint32_t z = __builtin_clz(sad_u32(ei, codes[c], 1u));
-                        sacc[r] += s.tt_fast[z];
-                        tbr = min(NT - 1, 31 - (int)z);
+                        tbr = min(NT - 1, 31 - (int)__builtin_clz(sad_u32(ei, codes[c], 1u)));
                     } else {
                         const int j = j0 + c;
                         const int64_t tj = j < L ? p.ts[row0 + j] : t_first;
                         const int64_t dt = ti64 - tj;
                         const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
-                        const int bl = bit_length_u64(ad);
-                        sacc[r] += s.tt_wide[bl];
-                        tbr = min(NT - 1, bl);
+                        tbr = min(NT - 1, bit_length_u64(ad));
                     }
                     st.tb4[r >> 2] |= (uint32_t)tbr << (8 * (r & 3));
                 }
@@ -477,15 +435,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             return st;
         };
 
-        auto finish = [&](const Tile& st, float (&gv)[16]) {
-            // mask (blocks with invisible pairs)
-            if (!st.full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = st.j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    gv[r] = ((j <= vis_lim) | (j == vis_self)) ? gv[r] : 0.0f;
-                }
-            }
+        // table-gradient histogram updates of one block (G in the dQ
+        // orientation, invisible pairs already zero)
+        auto hist_block = [&](const Tile& st, const f32x16& gv) {
             auto tbv = [&](int r) { return (int)((st.tb4[r >> 2] >> (8 * (r & 3))) & 0xffu); };
             // block sums (cross-lane, no LDS)
             // (a block spanning few time buckets sums buckets tlo+1 .. thi
@@ -513,23 +465,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                     if (st.tlo + k <= st.thi) tsum[k] = wave_total(tsum[k]);
                 tsum[0] = ((gsum - tsum[1]) - tsum[2]) - tsum[3];
             }
-            // dQ += G K over the tile's two 16-key chunks
-            bf16x8 pg[2];
-            pack_a(gv, pg);
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                    dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, trk[c][nb]), dqa[nb]);
-            // histogram updates.  When the wave's rows are all history rows,
-            // the position bucket of a visible pair is min(i - j, P - 1): the
-            // block's 63 diagonals, summed through the skewed scratch with
-            // plain LDS writes and reads, take one atomic each (LDS float
-            // atomics are slow).  Otherwise, and for time buckets beyond the
-            // register sums, per element.
-            // When they are all candidate rows (all at position n), the bucket
-            // min(n - min(j, n), P - 1) depends on the key alone: the same
-            // scratch, unskewed, gives each key column's sum.
+            // When the wave's rows are all history rows, the position bucket
+            // of a visible pair is min(i - j, P - 1): the block's 63
+            // diagonals, summed through the skewed scratch with plain LDS
+            // writes and reads, take one atomic each (LDS float atomics are
+            // slow).  When they are all candidate rows (all at position n),
+            // the bucket min(n - min(j, n), P - 1) depends on the key alone:
+            // the same scratch, unskewed, gives each key column's sum.
+            // Otherwise, and for time buckets beyond the register sums, per
+            // element.
             const bool diag = !st.pos_clamped && wrow0 + 31 < n;
             const bool colwise = !st.pos_clamped && wrow0 >= n;
             auto row_sum = [&]() {
@@ -589,11 +533,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
                 int rb = tbv(0);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int b = tbv(r);
-                    if (b != rb) {
+                    const int bk = tbv(r);
+                    if (bk != rb) {
                         if (run != 0.0f) atomicAdd(&hist[P + rb], run);
                         run = 0.0f;
-                        rb = b;
+                        rb = bk;
                     }
                     run += gv[r];
                 }
@@ -613,74 +557,74 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dq_kernel(BwdParams p, c
             }
         };
 
-        auto read_tr = [&](int t) {
-            uint32_t to = t_off;
-            asm volatile("" : "+v"(to));
-            read_v_tile(lds_addr(ring_kt + (t % kStages) * kTileBytes), to, trk);
-        };
-
-        auto act_g = [&](const f32x16& sacc, const f32x16& gacc, float cadd, int r, float (&gv)[16]) {
-            float a, slope;
-            act_and_slope(sacc[r] + cadd, silu, a, slope);
-            gv[r] = gacc[r] * slope;
-        };
-
-        auto step = [&](int t, f32x16& sC, f32x16& gC, const Tile& stC, f32x16& sN, f32x16& gN) -> Tile {
-            sync(t);
-            bf16x8 ka[8], va[8];
-            const Tile stN = prep(t, sN, ka, va);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) gN[r] = 0.0f;
-            float gv[16];
-#pragma unroll
-            for (int kc = 0; kc < 8; ++kc) {
-                gN = mfma32(va[kc], gf[kc], gN);
-                act_g(sC, gC, stC.cadd, 2 * kc, gv);
-                sN = mfma32(ka[kc], qf[kc], sN);
-                act_g(sC, gC, stC.cadd, 2 * kc + 1, gv);
+        // step t: tile t's K (and codes) have landed and so has its G block,
+        // loaded two steps ahead into the register set it now frees
+        auto step = [&](int t, f32x16& g) {
+            // tile t has landed (tile t+1's loads, and G of t+1, may be in flight)
+            if (t + 1 < ntiles) {
+                if (wave == 0)
+                    __builtin_amdgcn_s_waitcnt(0x0F77);
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F76);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F74);
             }
+            lds_sync();                                   // and every wave is done with tile t-1's stage
+            if (t + 2 < ntiles) issue((t + 2) % kStages, tile_of(t + 2));
+            const int kt = tile_of(t);
+            const bool live = g_live(kt);
+            bf16x8 hi[2], lo[2];
+            if (live) {
+                float res[16], gl[16];
 #pragma unroll
-            for (int kc = 0; kc < 16; ++kc) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
-            }
-            finish(stC, gv);
-            read_tr(t);
-            return stN;
-        };
-
-        if (ntiles > 0) {
-            f32x16 sA, gA, sB, gB;
-            Tile stA, stB;
-            {
-                sync(0);
-                bf16x8 ka[8], va[8];
-                stA = prep(0, sA, ka, va);
+                for (int r = 0; r < 16; ++r) gl[r] = g[r];
+                pack_a(gl, hi);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) gA[r] = 0.0f;
+                for (int c = 0; c < 2; ++c) {
+                    const u32x4 u = __builtin_bit_cast(u32x4, hi[c]);
 #pragma unroll
-                for (int kc = 0; kc < 8; ++kc) {
-                    gA = mfma32(va[kc], gf[kc], gA);
-                    sA = mfma32(ka[kc], qf[kc], sA);
+                    for (int e = 0; e < 4; ++e) {
+                        res[8 * c + 2 * e] = gl[8 * c + 2 * e] - __uint_as_float(u[e] << 16);
+                        res[8 * c + 2 * e + 1] = gl[8 * c + 2 * e + 1] - __uint_as_float(u[e] & 0xffff0000u);
+                    }
                 }
-                read_tr(0);
+                pack_a(res, lo);
             }
-            int t = 1;
-            for (; t + 1 < ntiles; t += 2) {
-                stB = step(t, sA, gA, stA, sB, gB);
-                stA = step(t + 1, sB, gB, stB, sA, gA);
-            }
-            if (t < ntiles) {
-                stB = step(t, sA, gA, stA, sB, gB);
-                sA = sB;
-                gA = gB;
-                stA = stB;
-            }
-            float gv[16];
+            load_g(t + 2, g);
+            if (live) {
+                const int stage = t % kStages;
+                u32x4 trk[2][4];
+                uint32_t to = t_off;
+                asm volatile("" : "+v"(to));
+                read_v_tile(lds_addr(ring_kt + stage * kTileBytes), to, trk);
+                const Tile st = classify(kt, stage);
+                f32x16 gt;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) act_g(sA, gA, stA.cadd, r, gv);
-            finish(stA, gv);
+                for (int r = 0; r < 16; ++r) gt[r] = 0.0f;
+                gt = mfma32(hi[0], idf[0], gt);
+                gt = mfma32(hi[1], idf[1], gt);
+                gt = mfma32(lo[0], idf[0], gt);
+                gt = mfma32(lo[1], idf[1], gt);
+                float gq[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) gq[r] = gt[r];
+                bf16x8 pg[2];
+                pack_a(gq, pg);
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, trk[c][nb]), dqa[nb]);
+                hist_block(st, gt);
+            }
+        };
+
+        int t = 0;
+        for (; t + 1 < ntiles; t += 2) {
+            step(t, gA);
+            step(t + 1, gB);
         }
+        if (t < ntiles) step(t, gA);
 
         // ---- (gradient rows are written once: non-temporal stores, which
         //      leave the caches to the tiles other items still read)
@@ -813,6 +757,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
         kmx = uniu(kmx);
         const int pkey = min(j, n);
         const int pkey_max = uni(min(k0w + 31, n));
+        // G blocks of this wave's key tile kw: block (q, kw) of the sequence
+        // at gblk0 + q (q + 1) / 2
+        const int kw = kblock * (kBlk / 32) + wave;
+        const int64_t gblk0 = uni(p.gbase[b]) + kw;
 
         f32x16 dka[4], dva[4];
 #pragma unroll
@@ -936,6 +884,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
                     av[r] = vis ? av[r] : 0.0f;
                     gv[r] = vis ? gv[r] : 0.0f;
                 }
+            }
+            // G of a block the dQ kernel reads, as this lane holds it
+            const int qt32 = st.r0 >> 5;
+            const int64_t gblk = gblk0 + tri(qt32);
+            if (wave_keys && g_block_live(qt32, kw, n) && gblk < p.gcap) {
+                f32x4* dst = reinterpret_cast<f32x4*>(p.gbuf + (gblk * p.H + h) * 1024 + lane * 16);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    __builtin_nontemporal_store(f32x4{gv[4 * m], gv[4 * m + 1], gv[4 * m + 2], gv[4 * m + 3]}, dst + m);
             }
             bf16x8 pa[2], pg[2];
             pack_a(av, pa);
@@ -1082,10 +1039,40 @@ __global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2,
     dst[(per_head ? h * (is_pos ? P : NT) : 0) + idx] = alpha * acc;
 }
 
+// Per-sequence first G block: the exclusive prefix of ceil(L / 32)
+// (ceil(L / 32) + 1) / 2 over the batch (one workgroup; each thread sums a
+// contiguous run of sequences, then the runs are scanned in LDS).
+__global__ void __launch_bounds__(1024) g_base_kernel(const int32_t* offsets, const int32_t* lengths, int B,
+                                                      int64_t* gbase) {
+    __shared__ int64_t sums[1024];
+    const int tid = threadIdx.x;
+    const int per = (B + 1023) / 1024;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    auto blocks_of = [&](int b) {
+        const int L = lengths ? lengths[b] : offsets[b + 1] - offsets[b];
+        return tri((max(L, 0) + 31) / 32);
+    };
+    int64_t mine = 0;
+    for (int b = b0; b < b1; ++b) mine += blocks_of(b);
+    sums[tid] = mine;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int64_t x = tid >= d ? sums[tid - d] : 0;
+        __syncthreads();
+        sums[tid] += x;
+        __syncthreads();
+    }
+    int64_t run = sums[tid] - mine;
+    for (int b = b0; b < b1; ++b) {
+        gbase[b] = run;
+        run += blocks_of(b);
+    }
+}
+
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
-    if (hist)   // the dQ kernel: reversed table, histograms, diagonal scratch
-        b += sizeof(float) * (2 * (size_t)rtab_width(P) + 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch));
+    if (hist)   // the dQ kernel: histograms, diagonal scratch
+        b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch);
     else        // the dK/dV kernel: the table and its padded copies
         b += sizeof(float) * ((size_t)((P + 3) & ~3) + 2 * (size_t)ptab2_width(P));
     return b;
@@ -1111,13 +1098,25 @@ BwdParams make_params(const AttnBwdArgs& a) {
     p.stats = a.stats;
     p.enc = a.enc;
     p.rab_part = a.rab_part;
+    p.gbuf = a.gbuf;
+    p.gbase = a.gbase;
+    p.gcap = a.gcap;
     return p;
 }
 
 }  // namespace
 
 bool attn_bwd_tables_fit(int P, int NT) {
-    return smem_bytes(3, P, NT, true) <= 160 * 1024 && smem_bytes(4, P, NT, false) <= 160 * 1024;
+    return smem_bytes(1, P, NT, true) <= 160 * 1024 && smem_bytes(4, P, NT, false) <= 160 * 1024;
+}
+
+int64_t attn_bwd_g_blocks(int B, int max_seq_len, int64_t num_rows) {
+    // sum over sequences of m (m + 1) / 2, m = ceil(L / 32) <= M: at most
+    // (M + 1) / 2 per 32-row tile, and at most num_rows / 32 + B tiles
+    const int64_t M = (max(max_seq_len, 0) + 31) / 32;
+    const int64_t by_tiles = ((M + 1) * (num_rows / 32 + 1 + B) + 1) / 2;
+    const int64_t by_seqs = (int64_t)B * (M * (M + 1) / 2);
+    return min(by_tiles, by_seqs);
 }
 
 size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT) {
@@ -1132,17 +1131,11 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
     const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
 
-    BwdParams pq = make_params(a);
-    pq.items = a.q_items; pq.ctrl = a.q_ctrl; pq.cursor = a.q_ctrl + 1;
-    const size_t smq = smem_bytes(3, a.P, a.NT, true);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dq_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smq);
-    if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL(attn_bwd_dq_kernel, dim3(grid), dim3(kThreads), smq, stream, a.ev_dq_begin,
-                          a.ev_dq_end, 0, pq, ws_base, wsb);
-    e = hipGetLastError();
+    hipLaunchKernelGGL(g_base_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.lengths, a.B, a.gbase);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
+    // dK, dV and the G blocks, then dQ and the table gradients from G
     BwdParams pk = make_params(a);
     pk.items = a.kv_items; pk.ctrl = a.kv_ctrl; pk.cursor = a.kv_ctrl + 1;
     const size_t smk = smem_bytes(4, a.P, a.NT, false);
@@ -1151,6 +1144,19 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipExtLaunchKernelGGL(attn_bwd_dkv_kernel, dim3(grid), dim3(kThreads), smk, stream, a.ev_dkv_begin,
                           a.ev_dkv_end, 0, pk, ws_base, wsb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    BwdParams pq = make_params(a);
+    pq.items = a.q_items; pq.ctrl = a.q_ctrl; pq.cursor = a.q_ctrl + 1;
+    const size_t smq = smem_bytes(1, a.P, a.NT, true);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dq_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smq);
+    if (e != hipSuccess) return e;
+    // two workgroups per CU when their LDS allows it
+    const int qgrid = smq <= 80 * 1024 ? 2 * grid : grid;
+    hipExtLaunchKernelGGL(attn_bwd_dq_kernel, dim3(qgrid), dim3(kThreads), smq, stream, a.ev_dq_begin,
+                          a.ev_dq_end, 0, pq, ws_base, wsb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -214,13 +214,26 @@ struct AttnBwdArgs {
     int64_t num_rows;
     float* rab_part;             // [work][P + NT]
     float* rab_part2;            // [heads][chunks][P + NT]
+    // G = dLoss/dS of every 32x32 block (query tile q, key tile k <= q) that
+    // holds a visible pair, fp32, written by the dK/dV kernel and read by the
+    // dQ kernel: block (b, q, k) of head h at ((gbase[b] + q (q + 1) / 2 + k)
+    // * H + h) * 1024 floats, gbase the per-sequence prefix of
+    // ceil(L / 32) (ceil(L / 32) + 1) / 2; blocks at or past gcap are
+    // neither written nor read.
+    float* gbuf;
+    int64_t* gbase;              // [B]
+    int64_t gcap;
+    int B;
     hipEvent_t ev_dq_begin, ev_dq_end, ev_dkv_begin, ev_dkv_end;   // optional
 };
 
 size_t attn_bwd_rab_part_floats(int64_t cap, int H, int P, int NT);
 size_t attn_bwd_rab_part2_floats(int H, int P, int NT);
-// The dQ kernel keeps the position and time tables and four per-wave
-// histograms of their gradients in LDS next to its tile ring.
+// Blocks of G a batch can hold at most (every sequence no longer than
+// max_seq_len, num_rows rows in all).
+int64_t attn_bwd_g_blocks(int B, int max_seq_len, int64_t num_rows);
+// The dQ kernel keeps four per-wave histograms of the table gradients in LDS
+// next to its tile ring; the dK/dV kernel keeps the position table.
 bool attn_bwd_tables_fit(int P, int NT);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
