@@ -213,16 +213,20 @@ def bwd_record(x, dev, steps):
     L = np.diff(x.offsets)
     pairs = flops.visible_pairs(L, x.num_candidates)
     alg = flops.attn_bwd_flops(L, x.H, x.d, x.num_candidates)
-    ex_dq = pairs * x.H * 6 * x.d      # S, dO V^T, dQ
+    gblk = flops.grad_blocks(L, x.num_candidates) * x.H
+    ex_dq = pairs * x.H * 2 * x.d + gblk * 4 * 32768   # G K, and the transpose of each G block
     ex_dkv = pairs * x.H * 8 * x.d     # S, dO V^T, dV, dK
+    g_bytes = gblk * 32 * 32 * 4       # G blocks, fp32: written by dK/dV, read by dQ
     rec = {"ms_per_step": round(ms, 4), "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
            "tokens_per_s": round(x.T / (ms * 1e-3), 1), "tokens": x.T,
            "dq_kernel_ms": round(dq, 4), "dkv_kernel_ms": round(dkv, 4),
            "dq_kernel_tflops_executed": round(ex_dq / (dq * 1e-3) / 1e12, 2),
            "dkv_kernel_tflops_executed": round(ex_dkv / (dkv * 1e-3) / 1e12, 2),
            "dkv_kernel_frac_bf16_peak": round(ex_dkv / (dkv * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "g_blocks_bytes": g_bytes, "dq_kernel_g_read_gbs": round(g_bytes / (dq * 1e-3) / 1e9, 1),
            "flop_convention": "tflops: 8*d per visible pair and head (dV, dO V^T, dQ, dK); "
-                              "executed: with the recomputed S in each kernel"}
+                              "executed: dK/dV 8*d per pair (S recomputed), dQ 2*d per pair (G K from "
+                              "the stored G) plus 4 32x32x16 MFMAs per stored block (its transpose)"}
     del c
     return rec
 

@@ -28,6 +28,22 @@ def visible_pairs(lengths: Sequence[int], num_candidates: Optional[Sequence[int]
     return int(np.sum(n * (n + 1) // 2 + c * (n + 1)))
 
 
+def grad_blocks(lengths, num_candidates=None) -> int:
+    """32x32 blocks (query tile q, key tile k) holding a visible pair, per
+    head: k <= q with history keys in tile k, or the diagonal tile of
+    candidate keys (each candidate is seen by its own row alone).  The
+    gradient kernels store G = dLoss/dS for exactly these blocks."""
+    L = np.asarray(lengths, dtype=np.int64)
+    c = np.zeros_like(L) if num_candidates is None else np.asarray(num_candidates, dtype=np.int64)
+    total = 0
+    for Lb, cb in zip(L.tolist(), c.tolist()):
+        nq = -(-Lb // 32)
+        nh = -(-(Lb - cb) // 32)
+        q = np.arange(nq, dtype=np.int64)
+        total += int(np.sum(np.where(q < nh, q + 1, nh + 1)))
+    return total
+
+
 def attn_flops(lengths, H: int, d_qk: int, d_v: int, num_candidates=None) -> int:
     """Unmasked attention FLOPs: sum over heads of (2*d_qk + 2*d_v) per visible pair."""
     return int(visible_pairs(lengths, num_candidates)) * H * (2 * d_qk + 2 * d_v)

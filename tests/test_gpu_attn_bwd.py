@@ -153,9 +153,10 @@ def test_bwd_table_gradients_bucket_by_bucket():
     """M-FALCON users of many shapes (so that workgroups take candidate-row
     blocks and history-row blocks one after the other), no clamped bucket to
     dominate, and the table gradients checked bucket by bucket.  G reaches
-    the histograms in fp32 from exact bf16 inputs, so every bucket must match
-    the oracle to fp32 accumulation error, far below the bf16 output bound: a
-    stale scratch cell from a previous block would show in its bucket."""
+    the histograms to within 2^-17 of itself (two bf16 halves) from exact
+    bf16 inputs and is summed in fp32, so every bucket must match the oracle
+    far below the bf16 output bound: a stale scratch cell from a previous
+    block would show in its bucket."""
     rng = np.random.default_rng(107)
     B = 24
     lengths = rng.integers(40, 420, size=B)

@@ -79,6 +79,21 @@ def test_position_bucket_and_candidate_positions():
     assert oracle.pos_bucket(9, 9, 4, 100) == 0
 
 
+def test_gradient_block_count_brute_force():
+    """The gradient kernels store G for every 32x32 block that holds a
+    visible pair; flops.grad_blocks counts them in closed form."""
+    for L, c in [(1, 0), (32, 0), (33, 0), (70, 0), (70, 6), (70, 38), (64, 64), (95, 31)]:
+        n = L - c
+        want = 0
+        for q in range(-(-L // 32)):
+            for k in range(q + 1):
+                if any(oracle.visible(i, j, L, n)
+                       for i in range(32 * q, min(L, 32 * q + 32))
+                       for j in range(32 * k, min(L, 32 * k + 32))):
+                    want += 1
+        assert flops.grad_blocks([L], [c]) == want, (L, c)
+
+
 def test_mask_pair_counts_closed_form():
     # causal: L(L+1)/2 pairs; M-FALCON: n(n+1)/2 + c(n+1)
     for L in [1, 2, 7, 33]:
