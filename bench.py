@@ -214,7 +214,7 @@ def bwd_record(x, dev, steps):
     pairs = flops.visible_pairs(L, x.num_candidates)
     alg = flops.attn_bwd_flops(L, x.H, x.d, x.num_candidates)
     gblk = flops.grad_blocks(L, x.num_candidates) * x.H
-    ex_dq = pairs * x.H * 2 * x.d + gblk * 4 * 32768   # G K, and the transpose of each G block
+    ex_dq = pairs * x.H * 2 * x.d + gblk * 2 * 32768   # G K, and the transpose of each G block
     ex_dkv = pairs * x.H * 8 * x.d     # S, dO V^T, dV, dK
     g_bytes = gblk * 32 * 32 * 4       # G blocks, fp32: written by dK/dV, read by dQ
     rec = {"ms_per_step": round(ms, 4), "tflops": round(alg / (ms * 1e-3) / 1e12, 2),
@@ -226,7 +226,7 @@ def bwd_record(x, dev, steps):
            "g_blocks_bytes": g_bytes, "dq_kernel_g_read_gbs": round(g_bytes / (dq * 1e-3) / 1e9, 1),
            "flop_convention": "tflops: 8*d per visible pair and head (dV, dO V^T, dQ, dK); "
                               "executed: dK/dV 8*d per pair (S recomputed), dQ 2*d per pair (G K from "
-                              "the stored G) plus 4 32x32x16 MFMAs per stored block (its transpose)"}
+                              "the stored G) plus 2 32x32x16 MFMAs per stored block (its transpose)"}
     del c
     return rec
 

@@ -410,7 +410,7 @@ hstu_status validate_bwd(const hstu_attn_bwd_args* g) {
 
 struct BwdWs {
     hstu::SchedLayout q, kv;   // query-major and key-major work lists
-    size_t dout, part, part2, gbase, gbuf, total;
+    size_t dout, part, part2, gbase, gbuf, kp, total;
     int64_t gcap;              // G blocks (32 x 32 fp32, per head) the buffer holds
 };
 
@@ -427,7 +427,8 @@ BwdWs bwd_ws(const hstu_attn_bwd_args* g) {
                                                                                   a.num_time_buckets));
     w.gbuf = align256(w.gbase + sizeof(int64_t) * size_t(a.B > 0 ? a.B : 0));
     w.gcap = hstu::attn_bwd_g_blocks(a.B, a.max_seq_len, a.num_rows);
-    w.total = align256(w.gbuf + size_t(w.gcap) * size_t(a.H) * 1024 * sizeof(float));
+    w.kp = align256(w.gbuf + size_t(w.gcap) * size_t(a.H) * 1024 * sizeof(float));
+    w.total = align256(w.kp + size_t(a.B > 0 ? a.B : 0) * size_t(w.q.nblk) * size_t(a.H) * 8192);
     return w;
 }
 
@@ -1307,6 +1308,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
     b.gbase = reinterpret_cast<int64_t*>(wb + w.gbase);
     b.gbuf = reinterpret_cast<float*>(wb + w.gbuf);
     b.gcap = w.gcap;
+    b.kp = wb + w.kp;
     b.B = a->B;
     b.ev_dq_begin = static_cast<hipEvent_t>(g->ev_dq_begin);
     b.ev_dq_end = static_cast<hipEvent_t>(g->ev_dq_end);

@@ -80,6 +80,7 @@ struct BwdParams {
     float* gbuf;                            // G blocks (written by dK/dV, read by dQ)
     const int64_t* gbase;
     int64_t gcap;
+    uint16_t* kp;                           // K fragments for G K (written by dK/dV, read by dQ)
 };
 
 // Small LDS state after the tile ring.
@@ -239,20 +240,18 @@ __device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int tot
 }
 
 // ---------------------------------------------------------------------------
-// dQ and the table gradients (query-major), from the G blocks the dK/dV
-// kernel stored
+// dQ and the table gradients (query-major), from the G blocks and the K
+// fragments the dK/dV kernel stored
 // ---------------------------------------------------------------------------
-// A block of G arrives as the dK/dV kernel held it: lane = key (l % 32), the
-// 16 values of queries 8 (r / 4) + 4 (l / 32) + r % 4.  dQ contracts over
-// keys, so the block is turned over first, by two MFMAs against the identity:
-// packed to bf16 it is an A operand with the keys as rows and the queries as
-// the contraction, and the product with the identity on the queries is the
-// block with the queries as columns -- lane = query, the 16 values of keys
-// 8 (r / 4) + 4 (l / 32) + r % 4, the orientation of dQ's own S^T.  G goes
-// through as two bf16 halves (hi = bf16(G), lo = bf16(G - hi), 16
-// significant bits in all), accumulated exactly in fp32, so the table
-// gradients see G to within 2^-17 of itself; the dQ product takes it
-// rounded to bf16.
+// A block of G arrives as the dK/dV kernel held it: lane = key b (l % 32),
+// the 16 values of queries a = 8 (r / 4) + 4 (l / 32) + r % 4.  The table
+// gradients are summed in that order, from the exact fp32 values.  dQ
+// contracts over keys, so for G K the block is turned over first, by two
+// MFMAs against the identity: packed to bf16 it is an A operand with the keys
+// as rows and the queries as the contraction, and its product with the
+// identity on the queries is the block with the queries as columns (lane =
+// query, the 16 values of keys 8 (r / 4) + 4 (l / 32) + r % 4), whose packed
+// accumulator is the A operand of G K, exactly bf16(G).
 __device__ __forceinline__ void identity_frags(int lane, bf16x8 (&idf)[2]) {
     // B operand lane l: column n = l % 32, k slots 8 (l / 32) + e; slot e of
     // chunk c stands for query 16 c + 8 (e / 4) + 4 (l / 32) + e % 4
@@ -275,22 +274,26 @@ __device__ __forceinline__ int64_t tri(int q) { return (int64_t)q * (q + 1) / 2;
 // row alone).
 __device__ __forceinline__ bool g_block_live(int q, int k, int n) { return k <= q && (32 * k < n || k == q); }
 
-__global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, const void* ws_base, uint32_t ws_bytes) {
+// The K fragments of one 32-key tile and head as G K reads them (B operand
+// of chunk c, column block nb, at fragment 4 c + nb): lane l holds column
+// 32 nb + l % 32 at keys 16 c + 8 (e / 4) + 4 (l / 32) + e % 4.  8 KiB per
+// tile, 1 KiB per fragment, lane-major.
+constexpr int kKpBytes = 8 * 64 * 16;
+
+__global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* ring_kt = smem;   // K, vswz: B operand of dQ += G K
-    Small& s = small_of<1>(smem);
+    __shared__ int32_t item[8];
+    __shared__ __attribute__((aligned(16))) uint32_t qcodes[4][32];   // each wave's 32 query codes
     // one histogram per wave ([P] position, then [NT] time buckets), so that
     // the order of the additions into each does not depend on how the waves
     // interleave; added in wave order at the end of the item
     const int hw = (p.P + p.NT + 3) & ~3;
-    float* hist_all = ptab_of<1>(smem);
-    // per wave, a scratch in which the block's G is written skewed and
-    // transposed (column rho - c + 31, row rho; kDiagPitch floats per
+    float* hist_all = reinterpret_cast<float*>(smem);
+    // per wave, a scratch in which a block's G is written skewed (column
+    // a - b + 31, row a for query a and key b; kDiagPitch floats per
     // column), so that each column holds one diagonal and its 32 entries are
-    // read with 8 16-byte loads.  The diagonal path writes only the band rho
-    // <= column <= rho + 31 and relies on the rest reading as zero: the
-    // scratch is zeroed once, and the column path (which fills columns 0-31
-    // whole) clears its cells again after reading them.
+    // read with 8 16-byte loads.  Only the band a <= column <= a + 31 is ever
+    // written; the rest stays zero from the start.
     float* scratch_all = hist_all + 4 * hw;
 
     const int tid = threadIdx.x;
@@ -300,8 +303,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
     const int h2 = lane >> 5;
     const int total_work = p.ctrl[0] * p.H;
     const int P = p.P, NT = p.NT;
-    const u32x4 wrs = make_rsrc(ws_base, ws_bytes);
-    const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
     bf16x8 idf[2];
     identity_frags(lane, idf);
 
@@ -310,80 +311,78 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
     for (int e = tid; e < 4 * hw + 4 * 64 * kDiagPitch; e += kThreads) hist_all[e] = 0.0f;
 
     for (;;) {
-        fetch_item(p, s, total_work, tid);
-        const int w = uni(s.work);
+        if (tid == 0) {
+            const int w = atomicAdd(p.cursor, 1);
+            item[0] = w;
+            if (w < total_work) {
+                const WorkItem it = p.items[w / p.H];
+                item[1] = it.b; item[2] = it.qt; item[3] = it.a_end; item[4] = it.kb; item[5] = it.pr;
+            }
+        }
+        lds_sync();
+        const int w = uni(item[0]);
         if (w >= total_work) break;
-        const int b = uni(s.item[0]), qt = uni(s.item[1]), a_end = uni(s.item[2]);
-        const int kbw = uni(s.item[3]);
-        const int kb_begin = kbw & 0xffff;
-        const int ntiles = uni(s.item[4]) >> 16;
+        const int b = uni(item[1]), qt = uni(item[2]), a_end = uni(item[3]);
+        const int kb_begin = uni(item[4]) & 0xffff;
+        const int ntiles = uni(item[5]) >> 16;
         const int h = w % p.H;
         const int64_t row0 = uni(p.offsets[b]);
         const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
         const int n = uni(p.ncand ? L - p.ncand[b] : L);
         const int bbase = b * p.nblk;
-
         auto tile_of = [&](int pos) { return pos < a_end ? pos : kb_begin + (pos - a_end); };
-        const TileSrc skt = tile_src(p.k + row0 * p.ks + h * HD, p.ks, L, lane, wave, true);
-        const int64_t enc_row0 = enc_base + 4 * row0;
 
-        // ---- this wave's query tile q and the G blocks of its row: one
-        //      buffer range from block (q, 0) on, so that the blocks it does
-        //      not read (or that lie past the buffer's capacity) arrive as
-        //      zeros without a memory access
+        // ---- this wave's query tile q: G blocks of its row (one buffer
+        //      range from block (q, 0) on), K fragments of the sequence and
+        //      head, key codes of the sequence.  Blocks the wave does not read
+        //      (past its diagonal, candidates of other rows, past the list's
+        //      end) are loaded from out of range and arrive as zeros without a
+        //      memory access, so that every step issues the same loads and the
+        //      compiler's waits count exactly.
         const int q = qt * (kBlk / 32) + wave;
         const int wrow0 = q * 32;
         const bool wave_rows = wrow0 < L;
-        __amdgpu_buffer_rsrc_t grs;
+        __amdgpu_buffer_rsrc_t grs, krs, ers;
         {
             const int64_t blk0 = wave_rows ? p.gbase[b] + tri(q) : 0;
             const int64_t room = max((int64_t)0, min((int64_t)(q + 1), p.gcap - blk0));
             grs = __builtin_amdgcn_make_buffer_rsrc(p.gbuf + blk0 * p.H * 1024, (short)0,
                                                     wave_rows ? (int)(room * p.H * 4096) : 0, 0x00020000);
+            krs = __builtin_amdgcn_make_buffer_rsrc(p.kp + ((int64_t)b * p.H + h) * p.nblk * (kKpBytes / 2),
+                                                    (short)0, p.nblk * kKpBytes, 0x00020000);
+            ers = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(p.enc) + row0, (short)0, L * 4,
+                                                    0x00020000);
         }
-        const uint32_t glane = (uint32_t)(lane * 64);
-        auto g_live = [&](int k) { return wave_rows && g_block_live(q, k, n); };
-        // (every step issues its four loads, past the list's end from out of
-        // range, so that the compiler sees the same loads in flight on every
-        // path and waits for a block only when it is used)
-        auto load_g = [&](int pos, f32x16& g) {
-            const int k = tile_of(pos);
-            const uint32_t off = pos < ntiles && g_live(k) ? (uint32_t)((k * p.H + h) * 4096) + glane : 0x80000000u;
+        auto g_live = [&](int pos) { return pos < ntiles && wave_rows && g_block_live(q, tile_of(pos), n); };
+        auto load_g = [&](int pos, f32x16& g, uint32_t& kcode) {
+            const bool live = g_live(pos);
+            const uint32_t off = live ? (uint32_t)((tile_of(pos) * p.H + h) * 4096 + lane * 64) : 0x80000000u;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const f32x4 x = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, off + 16 * m, 0, 0));
+                const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, off + 16 * m, 0, 0));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) g[4 * m + e] = x[e];
             }
+            kcode = __builtin_amdgcn_raw_buffer_load_b32(ers, live ? (uint32_t)((tile_of(pos) * 32 + l32) * 4) : 0x80000000u, 0, 0);
         };
-        auto issue = [&](int stage, int tile) {
-            issue_part(skt, ring_kt, stage, tile, wave);
-            if (wave == 0) issue_codes(wrs, enc_row0, s, stage, tile, L, lane);
+        auto load_k = [&](int pos, u32x4 (&kf)[2][4]) {
+            const uint32_t off = g_live(pos) ? (uint32_t)(tile_of(pos) * kKpBytes + lane * 16) : 0x80000000u;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    kf[c][nb] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + (4 * c + nb) * 1024, 0, 0);
         };
 
-        const int i = wrow0 + l32;
-        const bool row_valid = i < L;
+        // the codes of this wave's 32 queries, read back by groups of four
+        if (lane < 32) qcodes[wave][lane] = __builtin_amdgcn_raw_buffer_load_b32(ers, (uint32_t)((wrow0 + lane) * 4), 0, 0);
         const int64_t t_first = p.ts[row0];
-        int64_t ti64 = row_valid ? p.ts[row0 + i] : t_first;
-        uint32_t ei = row_valid ? p.enc[row0 + i] : 0x80000000u;
         const int qblk = bbase + q;
         uint32_t rmin = wave_rows ? p.stats[2 * qblk] : 0x80000000u;
         uint32_t rmax = wave_rows ? p.stats[2 * qblk + 1] : 0x80000000u;
-        settle(ti64);
-        settle(ei);
-        settle(rmin);
-        settle(rmax);
         rmin = uniu(rmin);
         rmax = uniu(rmax);
-        const int prow = min(i, n);
         const int prow_min = uni(min(wrow0, n));
-
-        f32x16 gA, gB;
-        if (0 < ntiles) issue(0, tile_of(0));
-        load_g(0, gA);
-        if (1 < ntiles) issue(1, tile_of(1));
-        load_g(1, gB);
 
         f32x16 dqa[4];
 #pragma unroll
@@ -392,53 +391,47 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
             for (int r = 0; r < 16; ++r) dqa[nb][r] = 0.0f;
 
         const StatsPtr kstats = stats_ptr(p.stats);
-        const uint32_t t_off = v_lane_offset(lane);
-        struct Tile {
-            int j0, tlo, thi;
-            bool pos_clamped, tconst, few;
-            uint32_t tb4[4];   // time bucket of element r in byte r % 4 of word r / 4
-        };
 
-        // block classification and, for blocks spanning several time buckets,
-        // the bucket of every element
-        auto classify = [&](int kt, int stage) -> Tile {
+        // table-gradient histogram updates of one block, G as stored (lane =
+        // key j0 + l32, element r = query wrow0 + 8 (r / 4) + 4 h2 + r % 4,
+        // invisible pairs already zero)
+        auto hist_block = [&](int kt, const f32x16& gv, uint32_t kcode) {
             const int j0 = kt * 32;
+            const int j = j0 + l32;
             const u32x2 kr = kstats[bbase + kt];
             const TimeBlock tb = time_block(rmin, rmax, kr[0], kr[1]);
-            Tile st;
-            st.j0 = j0;
-            st.pos_clamped = prow_min - min(j0 + 31, n) >= P - 1;
-            st.tconst = tb.constant;
-            st.tlo = min(NT - 1, 31 - tb.cz);
-            st.thi = min(NT - 1, 31 - tb.czhi);
-            st.few = !tb.constant && !tb.wide && st.thi - st.tlo < 4;
+            const bool pos_clamped = prow_min - min(j0 + 31, n) >= P - 1;
+            const bool tconst = tb.constant;
+            const int tlo = min(NT - 1, 31 - tb.cz);
+            const int thi = min(NT - 1, 31 - tb.czhi);
+            const bool few = !tb.constant && !tb.wide && thi - tlo < 4;
+            // time bucket of element r (keys and queries in time order: along
+            // r the buckets do not decrease)
+            uint32_t tb4[4] = {0u, 0u, 0u, 0u};
+            if (!tconst) {
+                int64_t tj64 = 0;
+                if (tb.wide) tj64 = j < L ? p.ts[row0 + j] : t_first;
+                u32x4 qc[4];   // queries 8 q + 4 h2 + 0..3
+                if (!tb.wide) {
 #pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) st.tb4[w4] = 0u;
-            if (!tb.constant) {
-                const uint32_t* codes = s.codes[stage];
+                    for (int g4 = 0; g4 < 4; ++g4) qc[g4] = *reinterpret_cast<const u32x4*>(&qcodes[wave][8 * g4 + 4 * h2]);
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
                     int tbr;
                     if (!tb.wide) {
-                        tbr = min(NT - 1, 31 - (int)__builtin_clz(sad_u32(ei, codes[c], 1u)));
+                        tbr = min(NT - 1, 31 - (int)__builtin_clz(sad_u32(qc[r >> 2][r & 3], kcode, 1u)));
                     } else {
-                        const int j = j0 + c;
-                        const int64_t tj = j < L ? p.ts[row0 + j] : t_first;
-                        const int64_t dt = ti64 - tj;
+                        const int i = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        const int64_t ti = i < L ? p.ts[row0 + i] : t_first;
+                        const int64_t dt = ti - tj64;
                         const uint64_t ad = dt < 0 ? (uint64_t)0 - (uint64_t)dt : (uint64_t)dt;
                         tbr = min(NT - 1, bit_length_u64(ad));
                     }
-                    st.tb4[r >> 2] |= (uint32_t)tbr << (8 * (r & 3));
+                    tb4[r >> 2] |= (uint32_t)tbr << (8 * (r & 3));
                 }
             }
-            return st;
-        };
-
-        // table-gradient histogram updates of one block (G in the dQ
-        // orientation, invisible pairs already zero)
-        auto hist_block = [&](const Tile& st, const f32x16& gv) {
-            auto tbv = [&](int r) { return (int)((st.tb4[r >> 2] >> (8 * (r & 3))) & 0xffu); };
+            auto tbv = [&](int r) { return (int)((tb4[r >> 2] >> (8 * (r & 3))) & 0xffu); };
             // block sums (cross-lane, no LDS)
             // (a block spanning few time buckets sums buckets tlo+1 .. thi
             // per element and takes bucket tlo as the rest of the total)
@@ -446,11 +439,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
             float tsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int r = 0; r < 16; ++r) gsum += gv[r];
-            if (st.few) {
-                const int nk = st.thi - st.tlo;   // 1 .. 3
+            if (few) {
+                const int nk = thi - tlo;   // 1 .. 3
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int k = tbv(r) - st.tlo;
+                    const int k = tbv(r) - tlo;
                     tsum[1] += (k == 1) ? gv[r] : 0.0f;
                     if (nk >= 2) {
                         tsum[2] += (k == 2) ? gv[r] : 0.0f;
@@ -458,26 +451,32 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
                     }
                 }
             }
-            if (st.pos_clamped || st.tconst || st.few) gsum = wave_total(gsum);
-            if (st.few) {
+            const bool colwise = !pos_clamped && wrow0 >= n;
+            float csum = 0.0f;
+            if (colwise) csum = gsum;   // (before the wave reduction below)
+            if (pos_clamped || tconst || few) gsum = wave_total(gsum);
+            if (few) {
 #pragma unroll
                 for (int k = 1; k < 4; ++k)
-                    if (st.tlo + k <= st.thi) tsum[k] = wave_total(tsum[k]);
+                    if (tlo + k <= thi) tsum[k] = wave_total(tsum[k]);
                 tsum[0] = ((gsum - tsum[1]) - tsum[2]) - tsum[3];
             }
-            // When the wave's rows are all history rows, the position bucket
-            // of a visible pair is min(i - j, P - 1): the block's 63
+            // Position buckets.  When the wave's rows are all history rows,
+            // the bucket of a visible pair is min(i - j, P - 1): the block's 63
             // diagonals, summed through the skewed scratch with plain LDS
             // writes and reads, take one atomic each (LDS float atomics are
             // slow).  When they are all candidate rows (all at position n),
-            // the bucket min(n - min(j, n), P - 1) depends on the key alone:
-            // the same scratch, unskewed, gives each key column's sum.
-            // Otherwise, and for time buckets beyond the register sums, per
-            // element.
-            const bool diag = !st.pos_clamped && wrow0 + 31 < n;
-            const bool colwise = !st.pos_clamped && wrow0 >= n;
-            auto row_sum = [&]() {
-                // lane u sums row u of the wave's scratch (32 floats)
+            // the bucket min(n - min(j, n), P - 1) depends on the key alone,
+            // which is this lane's: its 16 values, and the other half-wave's
+            // 16 of the same key, make one sum.  Otherwise per element.
+            const bool diag = !pos_clamped && wrow0 + 31 < n;
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int a = 8 * (r >> 2) + 4 * h2 + (r & 3);
+                    scratch[(a + 31 - l32) * kDiagPitch + a] = gv[r];
+                }
+                // lane u sums column u: diagonal a - b = u - 31
                 float dsum = 0.0f;
                 const f32x4* col = reinterpret_cast<const f32x4*>(scratch + lane * kDiagPitch);
 #pragma unroll
@@ -488,47 +487,23 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
                     dsum += x[2];
                     dsum += x[3];
                 }
-                return dsum;
-            };
-            if (diag) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    scratch[(l32 + 31 - c) * kDiagPitch + l32] = gv[r];
-                }
-                // lane u: diagonal rho - c = u - 31 (cells off the band are 0)
-                const float dsum = row_sum();
-                const int pb = wrow0 - st.j0 + lane - 31;
+                const int pb = wrow0 - j0 + lane - 31;
                 if (lane < 63 && pb >= 0 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
             } else if (colwise) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    scratch[c * kDiagPitch + l32] = gv[r];
-                }
-                // lane u < 32: key column u
-                const float dsum = row_sum();
-                // the diagonal path reads these cells as zero off its band
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int c = 8 * (r >> 2) + 4 * h2 + (r & 3);
-                    scratch[c * kDiagPitch + l32] = 0.0f;
-                }
-                const int pb = n - min(st.j0 + lane, n);
-                if (lane < 32 && dsum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], dsum);
-            }
-            if (!st.pos_clamped && !diag && !colwise) {
+                csum += __shfl_xor(csum, 32, 64);
+                const int pb = n - min(j, n);
+                if (lane < 32 && csum != 0.0f) atomicAdd(&hist[min(pb, P - 1)], csum);
+            } else if (!pos_clamped) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if (gv[r] != 0.0f) {
-                        const int j = st.j0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-                        atomicAdd(&hist[min(max(prow - min(j, n), 0), P - 1)], gv[r]);
+                        const int i = wrow0 + 8 * (r >> 2) + 4 * h2 + (r & 3);
+                        atomicAdd(&hist[min(max(min(i, n) - min(j, n), 0), P - 1)], gv[r]);
                     }
                 }
             }
-            if (!st.tconst && !st.few) {
-                // a lane's keys are in time order, so its time buckets come
-                // in runs: one atomic per run
+            if (!tconst && !few) {
+                // buckets come in runs along r: one atomic per run
                 float run = 0.0f;
                 int rb = tbv(0);
 #pragma unroll
@@ -547,64 +522,41 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
             // plain read-add-writes (an atomic at a uniform address becomes a
             // scan over the active lanes)
             if (lane == 63) {
-                if (st.pos_clamped) hist[P - 1] += gsum;
-                if (st.tconst) hist[P + st.tlo] += gsum;
-                if (st.few) {
+                if (pos_clamped) hist[P - 1] += gsum;
+                if (tconst) hist[P + tlo] += gsum;
+                if (few) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        if (st.tlo + k <= st.thi) hist[P + st.tlo + k] += tsum[k];
+                        if (tlo + k <= thi) hist[P + tlo + k] += tsum[k];
                 }
             }
         };
 
-        // step t: tile t's K (and codes) have landed and so has its G block,
-        // loaded two steps ahead into the register set it now frees
-        auto step = [&](int t, f32x16& g) {
-            // tile t has landed (tile t+1's loads, and G of t+1, may be in flight)
-            if (t + 1 < ntiles) {
-                if (wave == 0)
-                    __builtin_amdgcn_s_waitcnt(0x0F77);
-                else
-                    __builtin_amdgcn_s_waitcnt(0x0F76);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F74);
-            }
-            lds_sync();                                   // and every wave is done with tile t-1's stage
-            if (t + 2 < ntiles) issue((t + 2) % kStages, tile_of(t + 2));
+        // ---- the tiles: G and the key codes two tiles ahead (two register
+        //      sets), the K fragments one tile ahead, loaded after this
+        //      tile's G K (the loads are issued in the order they are needed)
+        f32x16 gA, gB;
+        uint32_t kcA, kcB;
+        u32x4 kf[2][4];
+        load_g(0, gA, kcA);
+        load_k(0, kf);
+        load_g(1, gB, kcB);
+
+        auto step = [&](int t, f32x16& g, uint32_t& kcode) {
             const int kt = tile_of(t);
-            const bool live = g_live(kt);
-            bf16x8 hi[2], lo[2];
+            const bool live = g_live(t);
             if (live) {
-                float res[16], gl[16];
+                hist_block(kt, g, kcode);
+                float gl[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) gl[r] = g[r];
+                bf16x8 hi[2];
                 pack_a(gl, hi);
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const u32x4 u = __builtin_bit_cast(u32x4, hi[c]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        res[8 * c + 2 * e] = gl[8 * c + 2 * e] - __uint_as_float(u[e] << 16);
-                        res[8 * c + 2 * e + 1] = gl[8 * c + 2 * e + 1] - __uint_as_float(u[e] & 0xffff0000u);
-                    }
-                }
-                pack_a(res, lo);
-            }
-            load_g(t + 2, g);
-            if (live) {
-                const int stage = t % kStages;
-                u32x4 trk[2][4];
-                uint32_t to = t_off;
-                asm volatile("" : "+v"(to));
-                read_v_tile(lds_addr(ring_kt + stage * kTileBytes), to, trk);
-                const Tile st = classify(kt, stage);
                 f32x16 gt;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) gt[r] = 0.0f;
                 gt = mfma32(hi[0], idf[0], gt);
                 gt = mfma32(hi[1], idf[1], gt);
-                gt = mfma32(lo[0], idf[0], gt);
-                gt = mfma32(lo[1], idf[1], gt);
                 float gq[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) gq[r] = gt[r];
@@ -614,20 +566,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb)
-                        dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, trk[c][nb]), dqa[nb]);
-                hist_block(st, gt);
+                        dqa[nb] = mfma32(pg[c], __builtin_bit_cast(bf16x8, kf[c][nb]), dqa[nb]);
             }
+            load_k(t + 1, kf);
+            load_g(t + 2, g, kcode);
         };
 
         int t = 0;
         for (; t + 1 < ntiles; t += 2) {
-            step(t, gA);
-            step(t + 1, gB);
+            step(t, gA, kcA);
+            step(t + 1, gB, kcB);
         }
-        if (t < ntiles) step(t, gA);
+        if (t < ntiles) step(t, gA, kcA);
 
-        // ---- (gradient rows are written once: non-temporal stores, which
-        //      leave the caches to the tiles other items still read)
+        // ---- (gradient rows are written once: non-temporal stores)
         // ---- dQ = alpha * acc for rows < L; lane holds column nb*32 + l32 at
         //      rows wrow0 + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
@@ -646,7 +598,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p, c
             part[e] = ((hist_all[e] + hist_all[hw + e]) + hist_all[2 * hw + e]) + hist_all[3 * hw + e];
             hist_all[e] = hist_all[hw + e] = hist_all[2 * hw + e] = hist_all[3 * hw + e] = 0.0f;
         }
-        lds_sync();   // histogram cleared and LDS free before the next item
+        lds_sync();   // histogram cleared before the next item
     }
 }
 
@@ -761,6 +713,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
         // at gblk0 + q (q + 1) / 2
         const int kw = kblock * (kBlk / 32) + wave;
         const int64_t gblk0 = uni(p.gbase[b]) + kw;
+        // this key tile's K as the dQ kernel's G K reads it: the B operand
+        // with the features as columns and the keys as the contraction,
+        // turned over from kf (keys as rows) by two MFMAs per 32-feature
+        // block against the identity on the features (exact), then packed
+        if (wave_keys) {
+            bf16x8 ik[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                if ((l32 >> 4) == c && ((l32 >> 3) & 1) == h2) {
+                    const int e = l32 & 7;
+                    z[e >> 1] = 0x3F80u << (16 * (e & 1));
+                }
+                ik[c] = __builtin_bit_cast(bf16x8, z);
+            }
+            uint8_t* kpd = reinterpret_cast<uint8_t*>(p.kp) + (((int64_t)b * p.H + h) * p.nblk + kw) * kKpBytes +
+                           lane * 16;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                f32x16 c32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) c32[r] = 0.0f;
+                c32 = mfma32(kf[2 * nb], ik[0], c32);
+                c32 = mfma32(kf[2 * nb + 1], ik[1], c32);
+                float cf[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cf[r] = c32[r];
+                bf16x8 pk[2];
+                pack_a(cf, pk);
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, pk[c]),
+                                                reinterpret_cast<u32x4*>(kpd + (4 * c + nb) * 1024));
+            }
+        }
 
         f32x16 dka[4], dva[4];
 #pragma unroll
@@ -1071,8 +1058,8 @@ __global__ void __launch_bounds__(1024) g_base_kernel(const int32_t* offsets, co
 
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
-    if (hist)   // the dQ kernel: histograms, diagonal scratch
-        b += sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch);
+    if (hist)   // the dQ kernel: histograms and diagonal scratch only
+        return sizeof(float) * 4 * ((size_t)((P + NT + 3) & ~3) + 64 * kDiagPitch);
     else        // the dK/dV kernel: the table and its padded copies
         b += sizeof(float) * ((size_t)((P + 3) & ~3) + 2 * (size_t)ptab2_width(P));
     return b;
@@ -1101,6 +1088,7 @@ BwdParams make_params(const AttnBwdArgs& a) {
     p.gbuf = a.gbuf;
     p.gbase = a.gbase;
     p.gcap = a.gcap;
+    p.kp = static_cast<uint16_t*>(a.kp);
     return p;
 }
 
@@ -1156,7 +1144,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     // two workgroups per CU when their LDS allows it
     const int qgrid = smq <= 80 * 1024 ? 2 * grid : grid;
     hipExtLaunchKernelGGL(attn_bwd_dq_kernel, dim3(qgrid), dim3(kThreads), smq, stream, a.ev_dq_begin,
-                          a.ev_dq_end, 0, pq, ws_base, wsb);
+                          a.ev_dq_end, 0, pq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

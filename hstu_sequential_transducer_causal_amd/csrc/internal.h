@@ -223,6 +223,10 @@ struct AttnBwdArgs {
     float* gbuf;
     int64_t* gbase;              // [B]
     int64_t gcap;
+    // K of every 32-key tile and head in the order the dQ kernel's G K reads
+    // it (8 KiB each, tile kt of sequence b and head h at (b H + h) nblk + kt),
+    // written by the dK/dV kernel
+    void* kp;
     int B;
     hipEvent_t ev_dq_begin, ev_dq_end, ev_dkv_begin, ev_dkv_end;   // optional
 };
@@ -232,8 +236,8 @@ size_t attn_bwd_rab_part2_floats(int H, int P, int NT);
 // Blocks of G a batch can hold at most (every sequence no longer than
 // max_seq_len, num_rows rows in all).
 int64_t attn_bwd_g_blocks(int B, int max_seq_len, int64_t num_rows);
-// The dQ kernel keeps four per-wave histograms of the table gradients in LDS
-// next to its tile ring; the dK/dV kernel keeps the position table.
+// The dQ kernel keeps four per-wave histograms of the table gradients in LDS;
+// the dK/dV kernel keeps the position table next to its tile ring.
 bool attn_bwd_tables_fit(int P, int NT);
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
