@@ -323,9 +323,9 @@ hstu_status mfalcon_layer_score(const hstu_mfalcon_layer_args* args, void* works
  * per-head tables; NULL skips one.  The table gradients are summed in a
  * fixed order (run-to-run identical).  attn.y, attn.o (without dy) and the
  * attention events are not used.
- * Limits: bf16 with d = 128; num_pos_buckets + num_time_buckets at most
- * about 2600 (the tables and per-wave histograms of their gradients share a
- * workgroup's LDS with the tile ring).
+ * Limits: bf16 with d = 128; num_pos_buckets at most about 5200 (the
+ * position table and its padded copies share the dK/dV kernel's LDS with its
+ * tile ring); (max_seq_len / 32 + 1) * H * 4096 below 2^31.
  * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED (fp32, d != 128, tables too
  * long), HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
 typedef struct hstu_attn_bwd_args {
@@ -346,9 +346,14 @@ typedef struct hstu_attn_bwd_args {
 } hstu_attn_bwd_args;
 
 /* Workspace bytes for hstu_attn_bwd (0 on invalid arguments): two work lists,
- * the timestamp codes, dO when dy is given (rows x H*128 bf16) and one fp32
- * row of num_pos_buckets + num_time_buckets table-gradient partial sums per
- * (128-row block, head). */
+ * the timestamp codes, dO when dy is given (rows x H*128 bf16), one fp32 row
+ * of num_pos_buckets + num_time_buckets table-gradient partial sums per
+ * (128-row block, head), K of every 32-key tile and head in the dQ kernel's
+ * operand order (8 KiB each, B * ceil(max_seq_len / 32) * H of them), and
+ * dLoss/dS of every 32 x 32 block holding a visible pair, fp32 (4 KiB per
+ * block and head; the count is bounded from B, max_seq_len and the row
+ * count: at most (ceil(max_seq_len / 32) + 1) / 2 blocks per 32-row tile).
+ * The last grows with the visible pairs: about 4 bytes per pair and head. */
 size_t hstu_attn_bwd_workspace_bytes(const hstu_attn_bwd_args* args);
 
 hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* args, void* workspace, size_t workspace_bytes,
@@ -365,7 +370,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* args, void* workspace, size_
  * The forward intermediates (Z, O, Y) are recomputed from layer's inputs.
  * Token sums run in a fixed order (run-to-run identical results).
  * Requirements beyond hstu_layer_fwd's: D % 128 == 0, H*d % 128 == 0,
- * num_pos_buckets + num_time_buckets <= ~2600.
+ * num_pos_buckets <= ~5200.
  * Errors: HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE. */
 typedef struct hstu_layer_bwd_args {
     uint32_t struct_size;      /* = sizeof(hstu_layer_bwd_args) */
