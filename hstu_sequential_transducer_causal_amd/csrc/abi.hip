@@ -125,6 +125,7 @@ struct Sched {
     int32_t* ctrl;
     int32_t* qscan;
     hstu::WorkItem* items;
+    hstu::ItemSeq* item_seq;
     hstu::SplitBlock* split;
     float* partial;
     uint32_t* stats;
@@ -153,6 +154,7 @@ Sched carve_sched(const hstu_attn_args* a, void* ws, size_t base, int max_slots 
     s.ctrl = reinterpret_cast<int32_t*>(w + s.layout.off_ctrl);
     s.qscan = reinterpret_cast<int32_t*>(w + s.layout.off_qscan);
     s.items = reinterpret_cast<hstu::WorkItem*>(w + s.layout.off_items);
+    s.item_seq = reinterpret_cast<hstu::ItemSeq*>(w + s.layout.off_item_seq);
     s.split = reinterpret_cast<hstu::SplitBlock*>(w + s.layout.off_split);
     s.partial = reinterpret_cast<float*>(w + s.layout.off_part);
     s.stats = reinterpret_cast<uint32_t*>(w + s.layout.off_stats);
@@ -181,6 +183,7 @@ hstu::SchedArgs make_sched_args(const hstu_attn_args* a, const Sched& s, bool ca
     sa.ctrl = s.ctrl;
     sa.qscan = s.qscan;
     sa.items = s.items;
+    sa.item_seq = s.item_seq;
     const bool bf16 = a->dtype == HSTU_BF16;
     sa.ts = a->timestamps;
     sa.enc = bf16 ? s.enc : nullptr;
@@ -211,6 +214,7 @@ hipError_t run_core(const hstu_attn_args* a, const Sched& s, hipStream_t stream)
     c.act = a->act;
     c.o = a->o; c.o_stride = a->o_stride;
     c.items = s.items;
+    c.item_seq = s.item_seq;
     c.ctrl = s.ctrl;
     c.cursor = s.ctrl + 1;
     c.partial = s.partial;
@@ -439,6 +443,7 @@ Sched carve_layout(const hstu::SchedLayout& l, void* ws) {
     s.ctrl = reinterpret_cast<int32_t*>(w + l.off_ctrl);
     s.qscan = reinterpret_cast<int32_t*>(w + l.off_qscan);
     s.items = reinterpret_cast<hstu::WorkItem*>(w + l.off_items);
+    s.item_seq = reinterpret_cast<hstu::ItemSeq*>(w + l.off_item_seq);
     s.split = reinterpret_cast<hstu::SplitBlock*>(w + l.off_split);
     s.partial = nullptr;
     s.stats = reinterpret_cast<uint32_t*>(w + l.off_stats);
@@ -998,7 +1003,7 @@ hstu_status mfalcon_score_cached(const hstu_mfalcon_cached_args* m, void* ws, si
     ca.split = sc.split;
     ca.offsets = m->cand_offsets; ca.lengths = nullptr; ca.ncand = nullptr;
     ca.tile_m = hstu::kBf16TileM; ca.tile_n = hstu::kBf16TileN;
-    ca.ctrl = sc.ctrl; ca.qscan = sc.qscan; ca.items = sc.items;
+    ca.ctrl = sc.ctrl; ca.qscan = sc.qscan; ca.items = sc.items; ca.item_seq = nullptr;
     ca.ts = m->ts_cand; ca.enc = sc.enc; ca.stats = sc.stats;
     ca.nblk = w.cand.nblk; ca.cap_blk = (int64_t)w.cand.cap_blk;
     ca.kv_offsets = m->hist_offsets; ca.ref_offsets = m->hist_offsets; ca.ref_ts = m->ts_hist;

@@ -85,6 +85,7 @@ struct Params {
     float alpha;
     uint16_t* o; int64_t os;
     const WorkItem* items;
+    const ItemSeq* item_seq;   // NULL: the sequence offsets are read per item
     const int32_t* ctrl;
     int32_t* cursor;
     float* partial;
@@ -108,7 +109,7 @@ struct Smem {
     uint32_t tsk[kStages][4][64];         // wave w's load: codes of keys 8w .. 8w+7 at [w][0..7]
     float tt_fast[32];                    // by leading-zero count of 2|dt| + 1
     float tt_wide[65];                    // by bit length of |dt|
-    int32_t item[8];
+    int32_t item[11];   // the WorkItem, then the ItemSeq's row0, L, n
     int32_t work;
 };
 
@@ -238,8 +239,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             s.work = w;
             if (w < total_work) {
                 const WorkItem it = p.items[w / p.H];
+                ItemSeq sq = {0, 0, 0, 0};
+                if (!kCross && p.item_seq) sq = p.item_seq[w / p.H];   // (same round trip as the item)
                 s.item[0] = it.b; s.item[1] = it.qt; s.item[2] = it.a_end; s.item[3] = it.kb;
                 s.item[4] = it.pr; s.item[5] = it.slot; s.item[6] = it.k; s.item[7] = it.n;
+                s.item[8] = sq.row0; s.item[9] = sq.L; s.item[10] = sq.n;
             }
         }
         lds_sync();
@@ -258,9 +262,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 
         // wave-uniform by construction; readfirstlane lets the compiler keep
         // them (and the buffer descriptors built from them) in SGPRs
-        const int64_t row0 = uni(p.offsets[b]);
-        const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
-        const int n = kCross ? L : uni(p.ncand ? L - p.ncand[b] : L);
+        const bool have_seq = !kCross && p.item_seq != nullptr;
+        const int64_t row0 = have_seq ? (int64_t)uni(s.item[8]) : (int64_t)uni(p.offsets[b]);
+        const int L = have_seq ? uni(s.item[9]) : uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
+        const int n = kCross ? L : (have_seq ? uni(s.item[10]) : uni(p.ncand ? L - p.ncand[b] : L));
         const int bbase = b * p.nblk;
         // query rows: the sequence's own, or (cross) the candidates'
         const int64_t row0q = kCross ? (int64_t)uni(p.q_offsets[b]) : row0;
@@ -771,7 +776,7 @@ hipError_t launch_attn_bf16(const AttnCoreArgs& a, hipStream_t stream) {
     p.rab_time = a.rab_time; p.NT = a.NT; p.rt_hs = a.rt_head_stride;
     p.alpha = a.alpha;
     p.o = static_cast<uint16_t*>(a.o); p.os = a.o_stride;
-    p.items = a.items; p.ctrl = a.ctrl;
+    p.items = a.items; p.item_seq = a.item_seq; p.ctrl = a.ctrl;
     p.cursor = const_cast<int32_t*>(a.ctrl) + kXcdCursor;   // the per-XCD cursors
     p.stats = a.stats; p.enc = a.enc;
     p.partial = a.partial; p.rowmap = a.rowmap; p.nblk = a.nblk;

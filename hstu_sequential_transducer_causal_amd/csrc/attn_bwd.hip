@@ -251,22 +251,7 @@ __device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int tot
 // as rows and the queries as the contraction, and its product with the
 // identity on the queries is the block with the queries as columns (lane =
 // query, the 16 values of keys 8 (r / 4) + 4 (l / 32) + r % 4), whose packed
-// accumulator is the A operand of G K, exactly bf16(G).
-__device__ __forceinline__ void identity_frags(int lane, bf16x8 (&idf)[2]) {
-    // B operand lane l: column n = l % 32, k slots 8 (l / 32) + e; slot e of
-    // chunk c stands for query 16 c + 8 (e / 4) + 4 (l / 32) + e % 4
-    const int n = lane & 31, h2 = lane >> 5;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if ((n >> 4) == c && ((n >> 2) & 1) == h2) {
-            const int e = 4 * ((n >> 3) & 1) + (n & 3);
-            z[e >> 1] = 0x3F80u << (16 * (e & 1));
-        }
-        idf[c] = __builtin_bit_cast(bf16x8, z);
-    }
-}
-
+// accumulator is the A operand of G K, exactly bf16(G) (transpose_identity).
 __device__ __forceinline__ int64_t tri(int q) { return (int64_t)q * (q + 1) / 2; }
 
 // A G block is stored when it holds a visible pair: k <= q, and history keys
@@ -304,7 +289,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p) {
     const int total_work = p.ctrl[0] * p.H;
     const int P = p.P, NT = p.NT;
     bf16x8 idf[2];
-    identity_frags(lane, idf);
+    transpose_identity(lane, idf);
 
     float* hist = hist_all + wave * hw;
     float* scratch = scratch_all + wave * (64 * kDiagPitch);

@@ -28,6 +28,16 @@ struct WorkItem {
     int32_t n;      // pieces of the block
 };
 
+// The sequence of a work item, as the scheduler saw it (written next to the
+// item, so that a kernel fetching the item does not wait a second round trip
+// for the sequence's offsets): first row, length, history rows.
+struct ItemSeq {
+    int32_t row0;
+    int32_t L;
+    int32_t n;
+    int32_t pad;
+};
+
 // A split row block: its pieces' partial sums sit in slots slot .. slot+n-1.
 struct SplitBlock {
     int32_t b;
@@ -62,6 +72,7 @@ struct SchedLayout {
                        // core's cursor of accelerator die (XCD) x
     size_t off_qscan;  // int32[B + 1] exclusive prefix of query tiles per sequence
     size_t off_items;  // WorkItem[cap_pieces]
+    size_t off_item_seq;   // ItemSeq[cap_pieces]
     size_t off_split;  // SplitBlock[cap]
     size_t off_part;   // float[part_slots][BM][d]: partial sums of split pieces
     size_t off_stats;  // uint32x2[cap_blk]: encoded timestamp range of 32-row block j of
@@ -98,6 +109,7 @@ struct SchedArgs {
     int32_t* ctrl;
     int32_t* qscan;
     WorkItem* items;
+    ItemSeq* item_seq = nullptr;   // NULL: not written
     // Timestamp codes (bf16 core; enc == NULL skips them): per row
     // e = 2 (t - t_first) + 2^31 (t_first: the sequence's first row) and,
     // per 32-row block, the range [min e, max e]; a block with some
@@ -142,6 +154,7 @@ struct AttnCoreArgs {
     int act;
     void* o; int64_t o_stride;
     const WorkItem* items;
+    const ItemSeq* item_seq = nullptr;   // NULL: read the sequence offsets instead
     const int32_t* ctrl;   // [0] = item count
     int32_t* cursor;       // persistent work cursor (zeroed by the scheduler)
     float* partial;        // partial slots of split pieces (bf16 core only)

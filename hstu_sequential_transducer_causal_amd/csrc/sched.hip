@@ -347,10 +347,16 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
         const int f = base + tid;
         int b = 0, qt = 0, c = 0, np = 1;
         Ranges r = {0, 0, 0};
+        ItemSeq sq = {0, 0, 0, 0};
         if (f < nitems) {
             r = item_of(f, b, qt);
             c = cost_of(r);
             np = any_split ? pieces_of(c, chunk) : 1;
+            if (a.item_seq) {
+                sq.row0 = a.offsets[b];
+                sq.L = in_lds ? s.len[b] : seq_length(a, b);
+                sq.n = in_lds ? s.nhist[b] : seq_history(a, b, sq.L);
+            }
         }
         int sx = 0, px = 0, nsplit = 0, nslots = 0;
         if (any_split) {
@@ -384,7 +390,10 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
                 it.slot = slot;
                 it.k = k;
                 it.n = np;
-                if (pos < a.cap_pieces) a.items[pos] = it;   // (lengths within max_seq_len always fit)
+                if (pos < a.cap_pieces) {   // (lengths within max_seq_len always fit)
+                    a.items[pos] = it;
+                    if (a.item_seq) a.item_seq[pos] = sq;
+                }
             }
         }
         if (any_split) {
@@ -482,7 +491,8 @@ SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d,
     l.off_ctrl = align256(base);
     l.off_qscan = align256(l.off_ctrl + kCtrlInts * sizeof(int32_t));
     l.off_items = align256(l.off_qscan + (size_t(B) + 1) * sizeof(int32_t));
-    l.off_split = align256(l.off_items + l.cap_pieces * sizeof(WorkItem));
+    l.off_item_seq = align256(l.off_items + l.cap_pieces * sizeof(WorkItem));
+    l.off_split = align256(l.off_item_seq + l.cap_pieces * sizeof(ItemSeq));
     l.off_part = align256(l.off_split + l.cap * sizeof(SplitBlock));
     l.off_stats = align256(l.off_part + size_t(l.part_slots) * size_t(tile_m) * size_t(split_d) * sizeof(float));
     l.off_enc = align256(l.off_stats + l.cap_blk * 2 * sizeof(uint32_t));

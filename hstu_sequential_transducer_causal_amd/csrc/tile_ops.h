@@ -140,6 +140,27 @@ __device__ __forceinline__ void read_v_tile(uint32_t stage_base, uint32_t voff, 
     }
 }
 
+// Turning a 32x32 accumulator over.  Packed to bf16 by 4-element groups, an
+// accumulator (lane l = column l % 32, values of rows 8 (r / 4) + 4 (l / 32)
+// + r % 4) is the A operand of two 32x32x16 products whose rows are its
+// columns and whose contraction runs over its rows: chunk c, slot e of lane
+// l standing for row 16 c + 8 (e / 4) + 4 (l / 32) + e % 4.  Against these
+// two B operands -- the identity over those rows -- the products give the
+// transpose in accumulator form: lane l = row l % 32, values of columns
+// 8 (r / 4) + 4 (l / 32) + r % 4.  Each bf16 value passes exactly.
+__device__ __forceinline__ void transpose_identity(int lane, bf16x8 (&idf)[2]) {
+    const int n = lane & 31, h2 = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if ((n >> 4) == c && ((n >> 2) & 1) == h2) {
+            const int e = 4 * ((n >> 3) & 1) + (n & 3);
+            z[e >> 1] = 0x3F80u << (16 * (e & 1));
+        }
+        idf[c] = __builtin_bit_cast(bf16x8, z);
+    }
+}
+
 // Bucket index (leading zeros of 2|dt| + 1) of an encoded gap 2|dt|.
 __device__ __forceinline__ uint32_t clz_gap(uint32_t gap2) { return __builtin_clz(gap2 + 1u); }
 
