@@ -95,6 +95,7 @@ struct SchedSmem {
     int qscan[kLdsSeq + 1];
     int len[kLdsSeq];
     int nhist[kLdsSeq];          // history rows n_b
+    int row0[kLdsSeq];           // first row offsets[b]
     uint16_t cost[kLdsItems];
 };
 
@@ -214,6 +215,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
             if (in_lds) {
                 s.len[b] = L;
                 s.nhist[b] = n;
+                s.row0[b] = a.offsets[b];
             }
         }
         int total;
@@ -353,7 +355,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
             c = cost_of(r);
             np = any_split ? pieces_of(c, chunk) : 1;
             if (a.item_seq) {
-                sq.row0 = a.offsets[b];
+                sq.row0 = in_lds ? s.row0[b] : a.offsets[b];
                 sq.L = in_lds ? s.len[b] : seq_length(a, b);
                 sq.n = in_lds ? s.nhist[b] : seq_history(a, b, sq.L);
             }
