@@ -181,6 +181,7 @@ EXPORTS = [
     "hstu_layer_bwd_saved_workspace_bytes",
     "hstu_stochastic_length",
     "hstu_attn_schedule",
+    "hstu_validate_offsets",
 ]
 
 _LIB = None
@@ -253,6 +254,8 @@ def load(path: str = LIB_PATH):
     lib.hstu_attn_schedule.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t,
                                        ctypes.POINTER(_i32), _i64, ctypes.POINTER(_i64),
                                        ctypes.POINTER(_i32), ctypes.POINTER(_i32), _vp]
+    lib.hstu_validate_offsets.restype = _i32
+    lib.hstu_validate_offsets.argtypes = [ctypes.POINTER(AttnArgs), _vp]
     _LIB = lib
     return lib
 

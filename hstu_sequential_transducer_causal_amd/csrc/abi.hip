@@ -120,6 +120,39 @@ hstu_status device_error(hipError_t e, const char* what) {
     return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The batch structure on the device (offsets, lengths, candidate counts),
+// checked by one small kernel: hstu_validate_offsets, and every call when the
+// environment sets HSTU_VALIDATE=1 (a synchronising debug aid).
+hstu_status device_check_batch(int B, int64_t num_rows, int max_seq_len, const int32_t* offsets,
+                               const int32_t* lengths, const int32_t* ncand, hipStream_t stream) {
+    hstu::ValidateArgs v;
+    v.B = B;
+    v.num_rows = num_rows;
+    v.max_seq_len = max_seq_len;
+    v.offsets = offsets;
+    v.lengths = lengths;
+    v.ncand = ncand;
+    int64_t first = -1;
+    const hipError_t e = hstu::validate_batch(v, stream, &first);
+    if (e != hipSuccess) return device_error(e, "batch validation");
+    if (first < 0) return ok();
+    static const char* const what[8] = {"", "offsets[0] < 0", "offsets decrease", "offsets[B] > num_rows",
+                                        "seq_lengths[b] outside [0, offsets[b+1] - offsets[b]]",
+                                        "length > max_seq_len", "num_candidates[b] outside [0, length]", ""};
+    return fail(HSTU_ERR_ARG, "sequence %lld: %s", (long long)(first / 8), what[first % 8]);
+}
+
+bool validate_env() {
+    const char* v = std::getenv("HSTU_VALIDATE");
+    return v && v[0] == '1' && v[1] == '\0';
+}
+
+hstu_status maybe_check_batch(const hstu_attn_args* a, hipStream_t stream) {
+    if (!validate_env()) return HSTU_OK;
+    return device_check_batch(a->B, a->num_rows, a->max_seq_len, a->seq_offsets, a->seq_lengths,
+                              a->num_candidates, stream);
+}
+
 struct Sched {
     hstu::SchedLayout layout;
     int32_t* ctrl;
@@ -484,6 +517,8 @@ hstu_status hstu_attn_fwd(const hstu_attn_args* a, void* ws, size_t ws_bytes, vo
     hstu_status st = validate_attn(a, false);
     if (st != HSTU_OK) return st;
     if (a->B == 0) return ok();
+    st = maybe_check_batch(a, static_cast<hipStream_t>(stream_));
+    if (st != HSTU_OK) return st;
     const size_t need = sched_layout_for(a, 0).bytes;
     st = check_workspace(ws, ws_bytes, need);
     if (st != HSTU_OK) return st;
@@ -564,6 +599,8 @@ hstu_status mfalcon_score(const hstu_mfalcon_args* m, void* ws, size_t ws_bytes,
     if (st != HSTU_OK) return st;
     if (m->score_stride < 1) return fail(HSTU_ERR_ARG, "score_stride < 1");
     if (a->B == 0) return ok();
+    st = maybe_check_batch(a, static_cast<hipStream_t>(stream_));
+    if (st != HSTU_OK) return st;
     if (!a->num_candidates) return fail(HSTU_ERR_ARG, "num_candidates is required for M-FALCON");
     if (!m->w || !m->scores) return fail(HSTU_ERR_ARG, "w and scores must be non-NULL");
     if (m->candidates_only && a->y)
@@ -817,6 +854,11 @@ hstu_status layer_fwd_run(const hstu_layer_args* l, void* ws, size_t ws_bytes, v
     hstu_status st = validate_layer(l);
     if (st != HSTU_OK) return st;
     if (l->B == 0 || l->num_rows == 0) return ok();
+    if (validate_env()) {
+        st = device_check_batch(l->B, l->num_rows, l->max_seq_len, l->seq_offsets, nullptr,
+                                l->num_candidates, static_cast<hipStream_t>(stream_));
+        if (st != HSTU_OK) return st;
+    }
     const LayerWs lw = layer_ws(l);
     st = check_workspace(ws, ws_bytes, lw.total);
     if (st != HSTU_OK) return st;
@@ -1367,6 +1409,18 @@ hstu_status hstu_stochastic_length(const hstu_sl_args* a, void* stream_) {
     hipError_t e = hstu::launch_stochastic_length(s, static_cast<hipStream_t>(stream_));
     if (e != hipSuccess) return device_error(e, "stochastic length launch");
     return ok();
+}
+
+hstu_status hstu_validate_offsets(const hstu_attn_args* a, void* stream_) {
+    if (!a) return fail(HSTU_ERR_ARG, "args is NULL");
+    if (a->struct_size != sizeof(hstu_attn_args))
+        return fail(HSTU_ERR_ARG, "struct_size %u != sizeof(hstu_attn_args) %zu", a->struct_size,
+                    sizeof(hstu_attn_args));
+    if (a->B < 0 || a->num_rows < 0 || a->max_seq_len < 0) return fail(HSTU_ERR_ARG, "B, num_rows and max_seq_len must be >= 0");
+    if (a->B == 0) return ok();
+    if (!a->seq_offsets) return fail(HSTU_ERR_ARG, "seq_offsets is NULL");
+    return device_check_batch(a->B, a->num_rows, a->max_seq_len, a->seq_offsets, a->seq_lengths,
+                              a->num_candidates, static_cast<hipStream_t>(stream_));
 }
 
 hstu_status hstu_attn_schedule(const hstu_attn_args* a, void* ws, size_t ws_bytes, int32_t* items_out,

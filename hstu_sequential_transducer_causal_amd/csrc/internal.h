@@ -38,6 +38,23 @@ struct ItemSeq {
     int32_t pad;
 };
 
+// Checks of the batch structure the kernels read from device memory without a
+// host copy: offsets[0] >= 0, offsets non-decreasing, offsets[B] <= num_rows,
+// 0 <= lengths[b] <= offsets[b+1] - offsets[b], every length <= max_seq_len,
+// 0 <= ncand[b] <= length.  Runs one workgroup, copies the first failure back
+// and synchronises the stream: *first = 8 b + check (check 1..6 in the order
+// above), or -1 for none.  The result lives in a device variable of the
+// library (one per GPU), so calls on one GPU must not overlap.
+struct ValidateArgs {
+    int B;
+    int64_t num_rows;
+    int max_seq_len;
+    const int32_t* offsets;
+    const int32_t* lengths;
+    const int32_t* ncand;
+};
+hipError_t validate_batch(const ValidateArgs& a, hipStream_t stream, int64_t* first);
+
 // A split row block: its pieces' partial sums sit in slots slot .. slot+n-1.
 struct SplitBlock {
     int32_t b;

@@ -503,6 +503,53 @@ SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d,
     return l;
 }
 
+namespace {
+
+__device__ int64_t g_validate_first;   // first failure of the last validate_batch on this GPU
+
+__global__ void __launch_bounds__(256) validate_batch_kernel(ValidateArgs a) {
+    __shared__ unsigned long long first;
+    if (threadIdx.x == 0) first = ~0ull;
+    __syncthreads();
+    for (int b = threadIdx.x; b < a.B; b += 256) {
+        const int64_t o0 = a.offsets[b], o1 = a.offsets[b + 1];
+        int check = 0;
+        int64_t L = o1 - o0;
+        if (b == 0 && o0 < 0) check = 1;
+        else if (o1 < o0) check = 2;
+        else if (b == a.B - 1 && o1 > a.num_rows) check = 3;
+        else {
+            if (a.lengths) {
+                const int64_t l = a.lengths[b];
+                if (l < 0 || l > L) check = 4;
+                L = l;
+            }
+            if (check == 0 && L > a.max_seq_len) check = 5;
+            if (check == 0 && a.ncand) {
+                const int64_t c = a.ncand[b];
+                if (c < 0 || c > L) check = 6;
+            }
+        }
+        if (check) atomicMin(&first, (unsigned long long)(8 * (int64_t)b + check));
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) g_validate_first = first == ~0ull ? -1 : (int64_t)first;
+}
+
+}  // namespace
+
+hipError_t validate_batch(const ValidateArgs& a, hipStream_t stream, int64_t* first) {
+    *first = -1;
+    if (a.B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(validate_batch_kernel, dim3(1), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess)
+        e = hipMemcpyFromSymbolAsync(first, HIP_SYMBOL(g_validate_first), sizeof(int64_t), 0,
+                                     hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return e;
+}
+
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
     const int64_t ts_groups = a.enc ? (a.cap_blk + kTsPerGroup - 1) / kTsPerGroup : 0;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + ts_groups)), dim3(kThreads), 0, stream, a);

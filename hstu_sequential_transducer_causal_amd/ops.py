@@ -3,7 +3,8 @@
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/hstu.h.  PyTorch provides device memory and the stream.
 Names follow the C ABI: hstu_attn_fwd, hstu_attn_bwd, mfalcon_score, mfalcon_score_cached,
-mfalcon_layer_score, hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule.
+mfalcon_layer_score, hstu_layer_fwd, hstu_layer_bwd, hstu_stochastic_length, hstu_attn_schedule,
+hstu_validate_offsets.
 """
 from __future__ import annotations
 
@@ -530,3 +531,19 @@ def hstu_attn_schedule(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, *, m
                                       ctypes.byref(count), ctypes.byref(tm), ctypes.byref(tn),
                                       _stream_ptr(stream)))
     return items[:count.value], tm.value, tn.value
+
+
+def hstu_validate_offsets(seq_offsets, *, num_rows: int, max_seq_len: int, seq_lengths=None,
+                          num_candidates=None, stream=None) -> None:
+    """Checks the device batch structure (offsets, lengths, candidate counts);
+    raises HstuError (HSTU_ERR_ARG) naming the first failing sequence."""
+    lib = _lib.load()
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.B = seq_offsets.numel() - 1
+    a.num_rows = num_rows
+    a.max_seq_len = max_seq_len
+    a.seq_offsets = seq_offsets.data_ptr()
+    a.seq_lengths = seq_lengths.data_ptr() if seq_lengths is not None else None
+    a.num_candidates = num_candidates.data_ptr() if num_candidates is not None else None
+    _lib.check(lib.hstu_validate_offsets(ctypes.byref(a), _stream_ptr(stream)))

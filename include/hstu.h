@@ -48,7 +48,11 @@
  *   - Device data (offsets, lengths, candidate counts) is trusted: it must
  *     satisfy 0 <= seq_offsets[b] <= seq_offsets[b+1] <= num_rows,
  *     0 <= L_b <= max_seq_len, 0 <= num_candidates[b] <= L_b; violating it is
- *     undefined behaviour (not checked on the device).
+ *     undefined behaviour unless it is checked: hstu_validate_offsets() checks
+ *     it on the device, and with the environment variable HSTU_VALIDATE=1
+ *     hstu_attn_fwd, mfalcon_score, hstu_layer_fwd and hstu_layer_fwd_saved
+ *     run that check before launching anything (synchronising the stream:
+ *     a debug aid, not for timed runs).
  */
 #ifndef HSTU_H_
 #define HSTU_H_
@@ -60,7 +64,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 9
+#define HSTU_ABI_VERSION 10
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -475,6 +479,22 @@ hstu_status hstu_stochastic_length(const hstu_sl_args* args, void* stream);
  * pieces over disjoint position ranges.  `count_out` (host) receives the
  * number of pieces.  Synchronises `stream`.  For tests of the scheduler
  * against a brute-force tile enumeration. */
+/* ------------------------------------------------------ batch validation */
+/* Checks the batch structure the other calls read from device memory without
+ * a host copy (the jagged layout of "Meta HSTU: как действия пользователя стали
+ * основой большой рекомендательной модели", section "Разная длина истории
+ * превращается в выигрыш по ресурсам", and the M-FALCON candidate counts of
+ * "生成式推荐（一）：HSTU", section "M-FALCON"): seq_offsets[0] >= 0, the
+ * offsets non-decreasing, seq_offsets[B] <= num_rows, 0 <= seq_lengths[b] <=
+ * seq_offsets[b+1] - seq_offsets[b] (when given), every L_b <= max_seq_len,
+ * 0 <= num_candidates[b] <= L_b (when given).  Only those fields of `args`
+ * are read, and only the pointers are checked on the host.  One small kernel
+ * on `stream`; synchronises `stream`.  Returns HSTU_OK, or HSTU_ERR_ARG with
+ * hstu_last_error() naming the first failing sequence and check
+ * (HSTU_ERR_DEVICE if the launch fails).  The result passes through a device
+ * variable of the library (one per GPU): calls on one GPU must not overlap. */
+hstu_status hstu_validate_offsets(const hstu_attn_args* args, void* stream);
+
 hstu_status hstu_attn_schedule(const hstu_attn_args* args, void* workspace, size_t workspace_bytes,
                                int32_t* items_out, int64_t cap, int64_t* count_out,
                                int32_t* tile_m_out, int32_t* tile_n_out, void* stream);

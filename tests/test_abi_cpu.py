@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 9
+    assert lib.hstu_abi_version() == 10
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
@@ -469,3 +469,21 @@ def test_noalloc_entry_point_host_checks(lib):
     a.num_rows = 5_000_000            # 8 bytes of codes and split map per row: 40 MB
     assert lib.hstu_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.HSTU_ERR_WORKSPACE
     assert b"noalloc" in lib.hstu_last_error()
+
+
+def test_validate_offsets_host_checks(lib):
+    """hstu_validate_offsets: the host-side argument errors, returned before
+    any device work (an empty batch is valid and touches nothing)."""
+    assert lib.hstu_validate_offsets(None, None) == _lib.HSTU_ERR_ARG
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs) + 8
+    assert lib.hstu_validate_offsets(ctypes.byref(a), None) == _lib.HSTU_ERR_ARG
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.B, a.num_rows, a.max_seq_len = 0, 0, 0
+    assert lib.hstu_validate_offsets(ctypes.byref(a), None) == _lib.HSTU_OK
+    a.B = -1
+    assert lib.hstu_validate_offsets(ctypes.byref(a), None) == _lib.HSTU_ERR_ARG
+    a.B, a.num_rows, a.max_seq_len = 3, 100, 64
+    a.seq_offsets = None
+    assert lib.hstu_validate_offsets(ctypes.byref(a), None) == _lib.HSTU_ERR_ARG
+    assert b"seq_offsets" in lib.hstu_last_error()
