@@ -1124,6 +1124,11 @@ hstu_status layer_bwd_run(const hstu_layer_bwd_args* g, void* ws, size_t ws_byte
     if (st != HSTU_OK) return st;
     const hstu_layer_args* l = &g->layer;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (l->B > 0 && l->num_rows > 0 && validate_env()) {
+        st = device_check_batch(l->B, l->num_rows, l->max_seq_len, l->seq_offsets, nullptr, l->num_candidates,
+                                stream);
+        if (st != HSTU_OK) return st;
+    }
     if (l->B == 0 || l->num_rows == 0) {   // empty batch: zero parameter gradients
         const size_t zw4 = size_t(4) * l->H * l->d;
         hipError_t e = hipSuccess;
@@ -1281,6 +1286,8 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
         if (e == hipSuccess && g->drab_time) e = hipMemsetAsync(g->drab_time, 0, sizeof(float) * size_t(ht) * NT, stream);
         return e == hipSuccess ? ok() : device_error(e, "clearing the table gradients");
     }
+    st = maybe_check_batch(a, stream);
+    if (st != HSTU_OK) return st;
     const BwdWs w = bwd_ws(g);
     st = check_workspace(ws, ws_bytes, w.total);
     if (st != HSTU_OK) return st;

@@ -50,9 +50,10 @@
  *     0 <= L_b <= max_seq_len, 0 <= num_candidates[b] <= L_b; violating it is
  *     undefined behaviour unless it is checked: hstu_validate_offsets() checks
  *     it on the device, and with the environment variable HSTU_VALIDATE=1
- *     hstu_attn_fwd, mfalcon_score, hstu_layer_fwd and hstu_layer_fwd_saved
- *     run that check before launching anything (synchronising the stream:
- *     a debug aid, not for timed runs).
+ *     hstu_attn_fwd, mfalcon_score, the layer calls (forward and gradients,
+ *     with or without saved activations) and hstu_attn_bwd run that check
+ *     before launching anything (synchronising the stream: a debug aid, not
+ *     for timed runs).
  */
 #ifndef HSTU_H_
 #define HSTU_H_

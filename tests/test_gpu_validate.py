@@ -77,7 +77,7 @@ def test_first_failure_is_reported():
     _fails("offsets decrease", 700, offsets=off, num_rows=int(off[-1]), max_seq_len=5, ncand=c)
 
 
-def test_hstu_validate_env_guards_the_forward_call():
+def test_hstu_validate_env_guards_the_calls():
     from hstu_sequential_transducer_causal_amd import _lib
     x = synth.make_attn(31, [40, 70, 33], H=2, d=128, P=128, NT=32, alpha=1 / 128, dtype="bf16")
     d = DeviceAttn(x)
@@ -91,6 +91,15 @@ def test_hstu_validate_env_guards_the_forward_call():
         with pytest.raises(_lib.HstuError) as e:
             run_attn(d)
         log(f"guarded forward: {e.value}")
+        assert e.value.status == _lib.HSTU_ERR_ARG and "sequence 1:" in str(e.value)
+        # the gradients are guarded the same way
+        import torch
+        from hstu_sequential_transducer_causal_amd import ops
+        g = torch.zeros_like(d.v)
+        with pytest.raises(_lib.HstuError) as e:
+            ops.hstu_attn_bwd(d.q, d.k, d.v, d.offsets, d.ts, d.rab_pos, d.rab_time, d.x.alpha,
+                              max_seq_len=d.max_seq_len, dout=g)
+        log(f"guarded gradients: {e.value}")
         assert e.value.status == _lib.HSTU_ERR_ARG and "sequence 1:" in str(e.value)
     finally:
         if old is None:
