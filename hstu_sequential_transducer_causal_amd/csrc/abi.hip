@@ -1324,15 +1324,13 @@ hstu_status hstu_attn_bwd(const hstu_attn_bwd_args* g, void* ws, size_t ws_bytes
     hstu::SchedArgs qa = make_sched_args(a, sq, false);
     qa.slots = 0;
     qa.part_slots = 0;
-    e = hstu::launch_sched(qa, stream);
-    if (e != hipSuccess) return device_error(e, "scheduler launch");
     hstu::SchedArgs ka = make_sched_args(a, skv, false);
     ka.kv_mode = 1;
     ka.slots = 0;
     ka.part_slots = 0;
     ka.enc = nullptr;
     ka.cap_blk = 0;
-    e = hstu::launch_sched(ka, stream);
+    e = hstu::launch_sched_pair(qa, ka, reinterpret_cast<int64_t*>(wb + w.gbase), stream);
     if (e != hipSuccess) return device_error(e, "scheduler launch");
 
     hstu::AttnBwdArgs b;

@@ -1011,36 +1011,6 @@ __global__ void __launch_bounds__(256) rab_grad_final_kernel(const float* part2,
     dst[(per_head ? h * (is_pos ? P : NT) : 0) + idx] = alpha * acc;
 }
 
-// Per-sequence first G block: the exclusive prefix of ceil(L / 32)
-// (ceil(L / 32) + 1) / 2 over the batch (one workgroup; each thread sums a
-// contiguous run of sequences, then the runs are scanned in LDS).
-__global__ void __launch_bounds__(1024) g_base_kernel(const int32_t* offsets, const int32_t* lengths, int B,
-                                                      int64_t* gbase) {
-    __shared__ int64_t sums[1024];
-    const int tid = threadIdx.x;
-    const int per = (B + 1023) / 1024;
-    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-    auto blocks_of = [&](int b) {
-        const int L = lengths ? lengths[b] : offsets[b + 1] - offsets[b];
-        return tri((max(L, 0) + 31) / 32);
-    };
-    int64_t mine = 0;
-    for (int b = b0; b < b1; ++b) mine += blocks_of(b);
-    sums[tid] = mine;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int64_t x = tid >= d ? sums[tid - d] : 0;
-        __syncthreads();
-        sums[tid] += x;
-        __syncthreads();
-    }
-    int64_t run = sums[tid] - mine;
-    for (int b = b0; b < b1; ++b) {
-        gbase[b] = run;
-        run += blocks_of(b);
-    }
-}
-
 size_t smem_bytes(int tiles, int P, int NT, bool hist) {
     size_t b = (size_t)tiles * kStages * kTileBytes + ((sizeof(Small) + 15) & ~size_t(15));
     if (hist)   // the dQ kernel: histograms and diagonal scratch only
@@ -1104,9 +1074,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     const size_t span = (size_t)((const uint8_t*)(a.enc + a.num_rows) - (const uint8_t*)a.stats);
     const uint32_t wsb = (uint32_t)(span > 0x7fffffffu ? 0x7fffffffu : span);
 
-    hipLaunchKernelGGL(g_base_kernel, dim3(1), dim3(1024), 0, stream, a.offsets, a.lengths, a.B, a.gbase);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
 
     // dK, dV and the G blocks, then dQ and the table gradients from G
     BwdParams pk = make_params(a);

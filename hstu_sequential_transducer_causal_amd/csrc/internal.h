@@ -147,6 +147,10 @@ struct SchedArgs {
 
 // Work list and timestamp codes, in one launch.
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+// The gradients' preparation in one launch: two work lists (only the first
+// may ask for timestamp codes) and gbase[b], the index of sequence b's first
+// 32x32 G block (B entries).
+hipError_t launch_sched_pair(const SchedArgs& a, const SchedArgs& b, int64_t* gbase, hipStream_t stream);
 
 // Attention core, bf16 with MFMA, d_qk = d_v = 128.
 constexpr int kBf16TileM = 128;

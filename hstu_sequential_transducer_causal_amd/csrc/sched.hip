@@ -420,9 +420,9 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
 // 32-row block (sequence b, block j at index b * nblk + j), the code range
 // [min e, max e]; a block with some |t - t_first| >= 2^30 gets the range
 // {0xffffffff, 0}.  One half-wave per block.
-__device__ void encode_timestamps(const SchedArgs& a) {
+__device__ void encode_timestamps(const SchedArgs& a, int first_block) {
     const int lane = threadIdx.x & 63;
-    const int64_t g = ((int64_t)blockIdx.x - 1) * kTsPerGroup + (threadIdx.x >> 5);
+    const int64_t g = ((int64_t)blockIdx.x - first_block) * kTsPerGroup + (threadIdx.x >> 5);
     const int b = (int)(g / a.nblk);
     const int j0 = (int)(g - (int64_t)b * a.nblk) * kTsBlock;
     bool active = g < a.cap_blk;
@@ -469,7 +469,54 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(SchedArgs a) {
     if (blockIdx.x == 0) {
         if (!a.skip_list) build_work_list(a, s);
     } else {
-        encode_timestamps(a);
+        encode_timestamps(a, 1);
+    }
+}
+
+// Where each sequence's 32x32 blocks of dLoss/dS start in the gradients' G
+// buffer: the exclusive prefix over sequences of T(ceil(L / 32)), T(n) =
+// n (n + 1) / 2, the blocks on and below the diagonal of an L x L causal
+// mask cut into 32-row and 32-column blocks.
+__device__ void g_block_prefix(const SchedArgs& a, int64_t* gbase) {
+    __shared__ int64_t sums[kThreads];
+    const int tid = threadIdx.x;
+    const int per = (a.B + kThreads - 1) / kThreads;
+    const int b0 = min(a.B, tid * per), b1 = min(a.B, b0 + per);
+    auto blocks_of = [&](int b) {
+        const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
+        const int64_t n = (max(L, 0) + 31) / 32;
+        return n * (n + 1) / 2;
+    };
+    int64_t mine = 0;
+    for (int b = b0; b < b1; ++b) mine += blocks_of(b);
+    sums[tid] = mine;
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {
+        const int64_t x = tid >= d ? sums[tid - d] : 0;
+        __syncthreads();
+        sums[tid] += x;
+        __syncthreads();
+    }
+    int64_t run = sums[tid] - mine;
+    for (int b = b0; b < b1; ++b) {
+        gbase[b] = run;
+        run += blocks_of(b);
+    }
+}
+
+// The gradients' preparation in one launch: workgroups 0 and 1 build the two
+// work lists, workgroup 2 the G-block prefix, the others encode the
+// timestamps of the first list's rows.
+__global__ void __launch_bounds__(kThreads) prep_pair_kernel(SchedArgs a, SchedArgs b, int64_t* gbase) {
+    __shared__ SchedSmem s;
+    if (blockIdx.x == 0) {
+        build_work_list(a, s);
+    } else if (blockIdx.x == 1) {
+        build_work_list(b, s);
+    } else if (blockIdx.x == 2) {
+        g_block_prefix(a, gbase);
+    } else {
+        encode_timestamps(a, 3);
     }
 }
 
@@ -501,6 +548,13 @@ SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d,
     l.off_rowmap = align256(l.off_enc + size_t(num_rows) * sizeof(uint32_t));
     l.bytes = align256(l.off_rowmap + (split_d > 0 ? size_t(num_rows) * sizeof(int32_t) : 0));
     return l;
+}
+
+hipError_t launch_sched_pair(const SchedArgs& a, const SchedArgs& b, int64_t* gbase, hipStream_t stream) {
+    if (a.skip_list || b.skip_list || b.enc || !gbase) return hipErrorInvalidValue;
+    const int64_t ts_groups = a.enc ? (a.cap_blk + kTsPerGroup - 1) / kTsPerGroup : 0;
+    hipLaunchKernelGGL(prep_pair_kernel, dim3((unsigned)(3 + ts_groups)), dim3(kThreads), 0, stream, a, b, gbase);
+    return hipGetLastError();
 }
 
 namespace {
