@@ -95,20 +95,27 @@ def _subset(x: synth.LayerInputs, seqs):
 
 def test_layer_bwd_full_size_first_layer():
     """Workload 5 at full size (32 sequences of 512..4096 rows), first layer.
-    dX of a sequence depends on that sequence alone: two sequences against the
-    oracle.  The parameter gradients sum over sequences: the full batch must
-    equal the sum of its two halves' gradients, and db2 the token sum of
-    dX_out."""
+    Three full-length sequences (the shortest, the longest and one more) as a
+    batch of their own against the oracle, every output: dX and the parameter
+    and table gradients, which sum over the batch's tokens.  In the full
+    batch, dX of a sequence depends on that sequence alone (the same three
+    against the same oracle run); the parameter gradients sum over sequences,
+    so the full batch's equal the sum of its two halves', and db2 is the token
+    sum of dX_out."""
     x = synth.config(5)
     g = synth.upstream_grad(310, x.x.shape)
     log(f"layer bwd cfg5 full size: B={x.B} T={x.T}")
     full = _run(x, g)
     L = np.diff(x.offsets)
-    for b in [int(np.argmin(L)), 3]:
-        xs, rows = _subset(x, [b])
-        ref = oracle.layer_bwd(xs.x, xs.w1[0], xs.w2[0], xs.offsets, xs.ts, xs.rab_pos[0],
-                               xs.rab_time[0], xs.alpha, xs.H, xs.d, g[rows], eps=xs.eps)
-        assert_close(full["dx"][rows], ref["dx"], "bf16", f"cfg5 seq {b} (L={L[b]}) dx")
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 3})
+    xs, rows = _subset(x, seqs)
+    sub = _run(xs, g[rows])
+    ref = oracle.layer_bwd(xs.x, xs.w1[0], xs.w2[0], xs.offsets, xs.ts, xs.rab_pos[0], xs.rab_time[0],
+                           xs.alpha, xs.H, xs.d, g[rows], eps=xs.eps)
+    what = f"cfg5 sequences {seqs} (L={[int(L[b]) for b in seqs]})"
+    for k in ("dx", "dw1", "db1", "dw2", "db2", "drab_pos", "drab_time"):
+        assert_close(sub[k], ref[k], "bf16", f"{what} {k}")
+    assert_close(full["dx"][rows], ref["dx"], "bf16", f"{what} dx in the full batch")
     np.testing.assert_allclose(full["db2"], g.astype(np.float64).sum(axis=0),
                                rtol=1e-4, atol=1e-3 * float(np.abs(g).sum(axis=0).max()))
     half = x.B // 2
