@@ -496,7 +496,8 @@ def time_case(case, steps, warmup, core_events=True):
     return ms_step, core_ms
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longseq_traffic.json")
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
+                 for f in ("attn_bf16_longseq_traffic.json", "attn_bf16_b64_traffic.json")]
 KERNEL_SRCS = [os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc", f)
                for f in ("attn_bf16.hip", "tile_ops.h", "hstu_device.h")]
 
@@ -511,18 +512,23 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the attention core from the committed counter
-    runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel factor), or None
-    when the kernel source changed since they were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_sha256_16") != kernel_hash():
-        return None
-    return int(t["bytes_per_launch"])
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention core on `workload` from the
+    committed counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    factor), or None when none covers that workload or the kernel source
+    changed since they were taken."""
+    for path in TRAFFIC_FILES:
+        try:
+            with open(path) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if t.get("workload", "").split(" ")[0] != workload:
+            continue
+        if t.get("kernel_sha256_16") != kernel_hash():
+            return None
+        return int(t["bytes_per_launch"])
+    return None
 
 
 def copy_calibration():
@@ -782,7 +788,7 @@ def main():
     if core_ms:
         ach = attn_fl_core / (core_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(x.name),
                     "kernel": "attn_bf16_kernel", "core_ms": round(core_ms, 4)}
 
     line = {
