@@ -48,15 +48,22 @@ constexpr int kTsPerGroup = kThreads / 32;
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Tile sizes are powers of two (launch_sched checks): tiles of 2^s rows.
+struct TileShift {
+    int m, n;   // log2 of the query (or key-major block) tile and the key tile
+};
+__device__ __forceinline__ int ceil_tiles(int x, int s) { return (x + (1 << s) - 1) >> s; }   // x >= 0
+inline bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
 struct Ranges {
     int a_end, kb_begin, kb_end;
 };
 
-__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int BN, bool kv_mode, bool cross) {
+__device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, TileShift ts, bool kv_mode, bool cross) {
     if (cross) {
         // candidate rows against a history cache of n keys: all of them
         Ranges r;
-        r.a_end = ceil_div(n, BN);
+        r.a_end = ceil_tiles(n, ts.n);
         r.kb_begin = r.kb_end = r.a_end;
         return r;
     }
@@ -65,23 +72,23 @@ __device__ __forceinline__ Ranges tile_ranges(int L, int n, int qt, int BM, int 
         // end for a block holding history keys (every later row and every
         // candidate sees them), to k1 for a block of candidates only (each is
         // seen by itself alone)
-        const int k0 = qt * BM, k1 = min(k0 + BM, L);
+        const int k0 = qt << ts.m, k1 = min(k0 + (1 << ts.m), L);
         Ranges r;
         r.a_end = 0;
-        r.kb_begin = k0 / BN;
-        r.kb_end = ceil_div(k0 < n ? L : k1, BN);
+        r.kb_begin = k0 >> ts.n;
+        r.kb_end = ceil_tiles(k0 < n ? L : k1, ts.n);
         return r;
     }
-    int q0 = qt * BM;
-    int q1 = min(q0 + BM, L);
+    int q0 = qt << ts.m;
+    int q1 = min(q0 + (1 << ts.m), L);
     Ranges r;
     if (q1 <= n) {
-        r.a_end = ceil_div(q1, BN);
+        r.a_end = ceil_tiles(q1, ts.n);
         r.kb_begin = r.kb_end = r.a_end;
     } else {
-        r.a_end = ceil_div(n, BN);
-        r.kb_begin = max(max(q0, n) / BN, r.a_end);
-        r.kb_end = max(ceil_div(q1, BN), r.kb_begin);
+        r.a_end = ceil_tiles(n, ts.n);
+        r.kb_begin = max(max(q0, n) >> ts.n, r.a_end);
+        r.kb_end = max(ceil_tiles(q1, ts.n), r.kb_begin);
     }
     return r;
 }
@@ -162,13 +169,13 @@ __device__ __forceinline__ int seq_history(const SchedArgs& a, int b, int L) {
 
 // First query tile of a sequence in the work list: 0, or with cand_only the
 // tile holding the first candidate row.
-__device__ __forceinline__ int first_tile(const SchedArgs& a, int n, int BM) { return a.cand_only ? n / BM : 0; }
+__device__ __forceinline__ int first_tile(const SchedArgs& a, int n, int sm) { return a.cand_only ? n >> sm : 0; }
 
 // Query tiles of a sequence in the work list (with cand_only, none for a
 // sequence without candidates).
-__device__ __forceinline__ int tile_count(const SchedArgs& a, int L, int n, int BM) {
+__device__ __forceinline__ int tile_count(const SchedArgs& a, int L, int n, int sm) {
     if (a.cand_only && L <= n) return 0;
-    return ceil_div(L, BM) - first_tile(a, n, BM);
+    return ceil_tiles(L, sm) - first_tile(a, n, sm);
 }
 
 // Pieces of a row block of c key tiles at piece size `chunk` (a block is
@@ -195,10 +202,10 @@ __device__ __forceinline__ int find_seq(Ptr qscan, int B, int f) {
 // Workgroup 0 of the preparation launch: the work list.
 __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
     const int tid = threadIdx.x;
-    const int BM = a.tile_m, BN = a.tile_n;
+    const TileShift tsh = {__builtin_ctz((unsigned)a.tile_m), __builtin_ctz((unsigned)a.tile_n)};
     const bool in_lds = a.B <= kLdsSeq;
     // costs (key tiles of an item) lie in [0, ceil(max_seq_len / BN)]
-    const int nbins = min(kMaxBins, ceil_div(a.max_seq_len, BN) + 2);
+    const int nbins = min(kMaxBins, ceil_tiles(a.max_seq_len, tsh.n) + 2);
 
     for (int i = tid; i < nbins; i += kThreads) s.hist[i] = 0;
     if (tid == 0) s.carry = 0;
@@ -211,7 +218,7 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
         if (b < a.B) {
             const int L = seq_length(a, b);
             const int n = seq_history(a, b, L);
-            nq = tile_count(a, L, n, BM);
+            nq = tile_count(a, L, n, tsh.m);
             if (in_lds) {
                 s.len[b] = L;
                 s.nhist[b] = n;
@@ -251,8 +258,8 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
             L = seq_length(a, b);
             n = seq_history(a, b, L);
         }
-        qt += first_tile(a, n, BM);
-        return tile_ranges(L, n, qt, BM, BN, a.kv_mode != 0, a.kv_offsets != nullptr);
+        qt += first_tile(a, n, tsh.m);
+        return tile_ranges(L, n, qt, tsh, a.kv_mode != 0, a.kv_offsets != nullptr);
     };
     auto cost_of = [](const Ranges& r) { return r.a_end + (r.kb_end - r.kb_begin); };
     auto cost_at = [&](int f) {
@@ -283,7 +290,11 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
     int chunk = 1 << 30;
     if (a.part_slots > 0 && a.slots > 0) {
         const unsigned long long units = (unsigned long long)work * (unsigned long long)a.H;
-        chunk = max(kMinPieceTiles, (int)min((units + a.slots - 1) / (unsigned long long)a.slots, 1ull << 20));
+        // (a 32-bit division when it fits: the 64-bit one is a long routine)
+        const unsigned long long per_slot =
+            units < (1ull << 31) ? (unsigned long long)(((uint32_t)units + (uint32_t)a.slots - 1u) / (uint32_t)a.slots)
+                                 : (units + a.slots - 1) / (unsigned long long)a.slots;
+        chunk = max(kMinPieceTiles, (int)min(per_slot, 1ull << 20));
         for (int round = 0; round < 24 && pieces_of(max_cost, chunk) > 1; ++round) {
             int mine = 0;
             for (int f = tid; f < nitems; f += kThreads) {
@@ -322,20 +333,34 @@ __device__ void build_work_list(const SchedArgs& a, SchedSmem& s) {
     }
     __syncthreads();
 
-    // 5. start position of each cost bin, largest cost first
-    if (tid == 0) s.carry = 0;
-    __syncthreads();
-    for (int base = 0; base < nbins; base += kThreads) {
-        const int bin = nbins - 1 - (base + tid);
-        const int c = bin >= 0 ? s.hist[bin] : 0;
-        int total;
-        const int ex = block_exclusive_scan(c, s.wave_tot, total);
-        const int carry = s.carry;
-        if (bin >= 0) s.hist[bin] = carry + ex;
-        __syncthreads();
-        if (tid == 0) s.carry = carry + total;
-        __syncthreads();
+    // 5. start position of each cost bin, largest cost first: one wave scans
+    //    the bins in that order (lane l takes positions [l per, l per + per),
+    //    position p being bin nbins - 1 - p)
+    if (tid < 64) {
+        const int per = (nbins + 63) / 64;
+        int sum = 0;
+        for (int k = 0; k < per; ++k) {
+            const int pos = tid * per + k;
+            if (pos < nbins) sum += s.hist[nbins - 1 - pos];
+        }
+        int x = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (tid >= o) x += y;
+        }
+        int run = x - sum;
+        for (int k = 0; k < per; ++k) {
+            const int pos = tid * per + k;
+            if (pos < nbins) {
+                const int c = s.hist[nbins - 1 - pos];
+                s.hist[nbins - 1 - pos] = run;
+                run += c;
+            }
+        }
+        if (tid == 63) s.carry = x;
     }
+    __syncthreads();
     const int npieces = s.carry;
 
     // 6. scatter the pieces into their bins; split blocks get consecutive
@@ -552,6 +577,7 @@ SchedLayout sched_layout(int B, int H, int max_seq_len, int tile_m, int split_d,
 
 hipError_t launch_sched_pair(const SchedArgs& a, const SchedArgs& b, int64_t* gbase, hipStream_t stream) {
     if (a.skip_list || b.skip_list || b.enc || !gbase) return hipErrorInvalidValue;
+    if (!pow2(a.tile_m) || !pow2(a.tile_n) || !pow2(b.tile_m) || !pow2(b.tile_n)) return hipErrorInvalidValue;
     const int64_t ts_groups = a.enc ? (a.cap_blk + kTsPerGroup - 1) / kTsPerGroup : 0;
     hipLaunchKernelGGL(prep_pair_kernel, dim3((unsigned)(3 + ts_groups)), dim3(kThreads), 0, stream, a, b, gbase);
     return hipGetLastError();
@@ -605,6 +631,7 @@ hipError_t validate_batch(const ValidateArgs& a, hipStream_t stream, int64_t* fi
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
+    if (!pow2(a.tile_m) || !pow2(a.tile_n)) return hipErrorInvalidValue;
     const int64_t ts_groups = a.enc ? (a.cap_blk + kTsPerGroup - 1) / kTsPerGroup : 0;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(1 + ts_groups)), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
