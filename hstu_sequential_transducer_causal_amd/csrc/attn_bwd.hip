@@ -72,7 +72,6 @@ struct BwdParams {
     uint16_t* dv; int64_t dvs;
     const WorkItem* items;
     const int32_t* ctrl;
-    int32_t* cursor;
     int nblk;
     const uint32_t* stats;
     const uint32_t* enc;
@@ -225,10 +224,36 @@ __device__ __forceinline__ float wave_total(float v) {
 typedef const __attribute__((address_space(4))) u32x2* StatsPtr;
 __device__ __forceinline__ StatsPtr stats_ptr(const uint32_t* p) { return (StatsPtr)(uintptr_t)p; }
 
-// Item fetch through the persistent cursor (thread 0), then shared.
-__device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int total_work, int tid) {
+// The accelerator die (XCD) the calling workgroup runs on.
+__device__ __forceinline__ int xcd_id() {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+    return (int)(xcc & (kXcds - 1));
+}
+
+// Next entry of the longest-first list for a workgroup on die my_xcd: the
+// die's own share (entries my_xcd, my_xcd + 8, ...) through its cursor, then
+// the other dies' remaining entries; total_work when none is left.  Entry
+// f H + k is row block f of head (k - b) mod H (head_of): a die then runs the
+// blocks of a few sequence-heads, whose K, V, Q and dO meet in its L2.
+__device__ __forceinline__ int pull_entry(const int32_t* ctrl, int total_work, int my_xcd) {
+    for (int k = 0; k < kXcds; ++k) {
+        const int x = (my_xcd + k) & (kXcds - 1);
+        int32_t* cur = const_cast<int32_t*>(ctrl) + kXcdCursor + kXcdStride * x;
+        // a queue seen exhausted is skipped with a load, not an atomic
+        if (k > 0 && __hip_atomic_load(cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * kXcds + x >= total_work)
+            continue;
+        const int w = atomicAdd(cur, 1) * kXcds + x;
+        if (w < total_work) return w;
+    }
+    return total_work;
+}
+__device__ __forceinline__ int head_of(int w, int b, int H) { return (w % H + H - b % H) % H; }
+
+// Item fetch (thread 0), then shared.
+__device__ __forceinline__ void fetch_item(const BwdParams& p, Small& s, int total_work, int tid, int my_xcd) {
     if (tid == 0) {
-        const int w = atomicAdd(p.cursor, 1);
+        const int w = pull_entry(p.ctrl, total_work, my_xcd);
         s.work = w;
         if (w < total_work) {
             const WorkItem it = p.items[w / p.H];
@@ -295,9 +320,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p) {
     float* scratch = scratch_all + wave * (64 * kDiagPitch);
     for (int e = tid; e < 4 * hw + 4 * 64 * kDiagPitch; e += kThreads) hist_all[e] = 0.0f;
 
+    const int my_xcd = xcd_id();
     for (;;) {
         if (tid == 0) {
-            const int w = atomicAdd(p.cursor, 1);
+            const int w = pull_entry(p.ctrl, total_work, my_xcd);
             item[0] = w;
             if (w < total_work) {
                 const WorkItem it = p.items[w / p.H];
@@ -310,7 +336,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p) {
         const int b = uni(item[1]), qt = uni(item[2]), a_end = uni(item[3]);
         const int kb_begin = uni(item[4]) & 0xffff;
         const int ntiles = uni(item[5]) >> 16;
-        const int h = w % p.H;
+        const int h = head_of(w, b, p.H);
         const int64_t row0 = uni(p.offsets[b]);
         const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
         const int n = uni(p.ncand ? L - p.ncand[b] : L);
@@ -578,7 +604,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bwd_dq_kernel(BwdParams p) {
         }
         // ---- this item's table-gradient histogram -> its partial row
         lds_sync();
-        float* part = p.rab_part + (int64_t)w * (P + NT);
+        // (row (w / H) H + h: the reduction takes a head's rows in list order)
+        float* part = p.rab_part + ((int64_t)(w / p.H) * p.H + h) * (P + NT);
         for (int e = tid; e < P + NT; e += kThreads) {
             part[e] = ((hist_all[e] + hist_all[hw + e]) + hist_all[2 * hw + e]) + hist_all[3 * hw + e];
             hist_all[e] = hist_all[hw + e] = hist_all[2 * hw + e] = hist_all[3 * hw + e] = 0.0f;
@@ -617,15 +644,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_bwd_dkv_kernel(BwdParams p, 
     const int64_t enc_base = (const uint8_t*)p.enc - (const uint8_t*)ws_base;
     int loaded_head = -1;
 
+    const int my_xcd = xcd_id();
     for (;;) {
-        fetch_item(p, s, total_work, tid);
+        fetch_item(p, s, total_work, tid, my_xcd);
         const int w = uni(s.work);
         if (w >= total_work) break;
         const int b = uni(s.item[0]), kblock = uni(s.item[1]);
         const int kbw = uni(s.item[3]);
         const int rt_begin = kbw & 0xffff;
         const int ntiles = uni(s.item[4]) >> 16;
-        const int h = w % p.H;
+        const int h = head_of(w, b, p.H);
         const int64_t row0 = uni(p.offsets[b]);
         const int L = uni(p.lengths ? p.lengths[b] : p.offsets[b + 1] - (int)row0);
         const int n = uni(p.ncand ? L - p.ncand[b] : L);
@@ -1078,7 +1106,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
 
     // dK, dV and the G blocks, then dQ and the table gradients from G
     BwdParams pk = make_params(a);
-    pk.items = a.kv_items; pk.ctrl = a.kv_ctrl; pk.cursor = a.kv_ctrl + 1;
+    pk.items = a.kv_items; pk.ctrl = a.kv_ctrl;
     const size_t smk = smem_bytes(4, a.P, a.NT, false);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dkv_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smk);
@@ -1089,7 +1117,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
 
     BwdParams pq = make_params(a);
-    pq.items = a.q_items; pq.ctrl = a.q_ctrl; pq.cursor = a.q_ctrl + 1;
+    pq.items = a.q_items; pq.ctrl = a.q_ctrl;
     const size_t smq = smem_bytes(1, a.P, a.NT, true);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bwd_dq_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smq);

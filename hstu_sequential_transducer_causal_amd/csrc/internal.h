@@ -240,7 +240,7 @@ struct AttnBwdArgs {
     void* dv; int64_t dv_stride;
     float* drab_pos;             // [P] or [H][P]; NULL: not computed
     float* drab_time;            // [NT] or [H][NT]; NULL: not computed
-    const WorkItem* q_items;  int32_t* q_ctrl;    // query-major list (ctrl[1] is its cursor)
+    const WorkItem* q_items;  int32_t* q_ctrl;    // query-major list (with its per-die cursors)
     const WorkItem* kv_items; int32_t* kv_ctrl;   // key-major list
     int nblk;
     const uint32_t* stats;
