@@ -16,6 +16,9 @@
 //                      (8 bits per pass, LDS histogram) finds the cap-th
 //                      smallest key; a block scan then writes the kept source
 //                      rows in order (ties on the threshold key by index).
+//                      The keys of a sequence of up to kKeyCache events are
+//                      computed once and kept in LDS; longer ones recompute
+//                      them in every pass.
 //   sl_gather_kernel   copies the kept rows of up to 8 row-major tensors.
 #include <algorithm>
 
@@ -28,6 +31,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kSelThreads = 1024;            // the select kernel's workgroup
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kKeyCache = 16384;             // keys kept in LDS (64 KiB)
 
 constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull;
 constexpr uint64_t kM1 = 0xCA5A826395121157ull;
@@ -56,7 +62,9 @@ __device__ __forceinline__ uint32_t event_key(int j, int b, uint64_t step, uint6
     return (uint32_t)(x0 >> 32);
 }
 
-// Exclusive scan of one int per thread over the workgroup, with the total.
+// Exclusive scan of one int per thread over a workgroup of NW waves, with
+// the total.
+template <int NW>
 __device__ int block_scan(int v, int* wave_tot, int& total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
@@ -69,7 +77,7 @@ __device__ int block_scan(int v, int* wave_tot, int& total) {
     __syncthreads();
     int before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int s = wave_tot[i];
         before += i < w ? s : 0;
         tot += s;
@@ -91,7 +99,7 @@ __global__ void __launch_bounds__(kThreads) sl_offsets_kernel(SlArgs a) {
         int k = 0;
         if (b < a.B) k = max(0, min(cap_of(a, b), a.offsets[b + 1] - a.offsets[b]));
         int total;
-        const int ex = block_scan(k, wave_tot, total);
+        const int ex = block_scan<kWaves>(k, wave_tot, total);
         const int c = carry;
         if (b < a.B) a.out_offsets[b] = c + ex;
         __syncthreads();
@@ -101,11 +109,12 @@ __global__ void __launch_bounds__(kThreads) sl_offsets_kernel(SlArgs a) {
     if (threadIdx.x == 0) a.out_offsets[a.B] = carry;
 }
 
-__global__ void __launch_bounds__(kThreads) sl_select_kernel(SlArgs a) {
+__global__ void __launch_bounds__(kSelThreads) sl_select_kernel(SlArgs a) {
     __shared__ int hist[256];
-    __shared__ int wave_tot[kWaves];
+    __shared__ int wave_tot[kSelWaves];
     __shared__ uint32_t s_prefix, s_mask;
     __shared__ int s_remaining, s_lt, s_eq;
+    __shared__ uint32_t keys[kKeyCache];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t off = a.offsets[b];
@@ -113,10 +122,15 @@ __global__ void __launch_bounds__(kThreads) sl_select_kernel(SlArgs a) {
     const int k = max(0, min(cap_of(a, b), L));
     const int64_t out0 = a.out_offsets[b];
     if (k >= L) {
-        for (int j = tid; j < L; j += kThreads) a.out_index[out0 + j] = off + j;
+        for (int j = tid; j < L; j += kSelThreads) a.out_index[out0 + j] = off + j;
         return;
     }
     if (k == 0) return;
+
+    const bool cached = L <= kKeyCache;
+    if (cached)   // (visible after the first pass's first barrier)
+        for (int j = tid; j < L; j += kSelThreads) keys[j] = event_key(j, b, a.step, a.seed);
+    auto key_at = [&](int j) { return cached ? keys[j] : event_key(j, b, a.step, a.seed); };
 
     // the k-th smallest key, 8 bits at a time from the top
     if (tid == 0) {
@@ -125,23 +139,42 @@ __global__ void __launch_bounds__(kThreads) sl_select_kernel(SlArgs a) {
         s_remaining = k;
     }
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+        if (tid < 256) hist[tid] = 0;
         __syncthreads();
         const uint32_t prefix = s_prefix, mask = s_mask;
-        for (int j = tid; j < L; j += kThreads) {
-            const uint32_t u = event_key(j, b, a.step, a.seed);
+        for (int j = tid; j < L; j += kSelThreads) {
+            const uint32_t u = key_at(j);
             if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            int rem = s_remaining, cum = 0, d = 0;
-            for (; d < 255; ++d) {
-                if (cum + hist[d] >= rem) break;
-                cum += hist[d];
+        // the digit d: the first bin whose count, added to the bins below it,
+        // reaches the rank still to find (255 if none does).  One wave: lane l
+        // holds bins 4l .. 4l + 3 and their inclusive running total.
+        if (tid < 64) {
+            const int rem = s_remaining;
+            int c[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[i] = hist[4 * tid + i];
+            const int sum = (c[0] + c[1]) + (c[2] + c[3]);
+            int x = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (tid >= o) x += y;
             }
-            s_remaining = rem - cum;
-            s_prefix = prefix | ((uint32_t)d << shift);
-            s_mask = mask | (255u << shift);
+            const unsigned long long reach = __ballot(x >= rem);
+            const int owner = reach ? __ffsll((long long)reach) - 1 : 63;
+            if (tid == owner) {
+                int cum = x - sum, i = 0;
+                for (; i < 3; ++i) {
+                    if (cum + c[i] >= rem) break;
+                    cum += c[i];
+                }
+                const uint32_t d = (uint32_t)(4 * tid + i);
+                s_remaining = rem - cum;
+                s_prefix = prefix | (d << shift);
+                s_mask = mask | (255u << shift);
+            }
         }
         __syncthreads();
     }
@@ -154,18 +187,18 @@ __global__ void __launch_bounds__(kThreads) sl_select_kernel(SlArgs a) {
         s_eq = 0;   // key == thr seen so far
     }
     __syncthreads();
-    for (int base = 0; base < L; base += kThreads) {
+    for (int base = 0; base < L; base += kSelThreads) {
         const int j = base + tid;
         uint32_t u = 0xffffffffu;
         bool valid = j < L;
-        if (valid) u = event_key(j, b, a.step, a.seed);
+        if (valid) u = key_at(j);
         const bool eq = valid && u == thr;
         int eq_total;
-        const int eq_rank = block_scan(eq ? 1 : 0, wave_tot, eq_total);
+        const int eq_rank = block_scan<kSelWaves>(eq ? 1 : 0, wave_tot, eq_total);
         const int eq_before = s_eq;
         const bool keep = valid && (u < thr || (eq && eq_before + eq_rank < need_eq));
         int kept_total;
-        const int pos = block_scan(keep ? 1 : 0, wave_tot, kept_total);
+        const int pos = block_scan<kSelWaves>(keep ? 1 : 0, wave_tot, kept_total);
         const int kept_before = s_lt;
         if (keep) a.out_index[out0 + kept_before + pos] = off + j;
         __syncthreads();
@@ -209,7 +242,7 @@ hipError_t launch_stochastic_length(const SlArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(sl_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sl_select_kernel, dim3((unsigned)a.B), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(sl_select_kernel, dim3((unsigned)a.B), dim3(kSelThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.num_tensors <= 0 || a.num_rows <= 0) return e;
     const int64_t blocks = std::min<int64_t>(4 * (int64_t)device_cu_count(), (a.num_rows + 3) / 4 + 1);
