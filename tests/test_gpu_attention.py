@@ -50,6 +50,16 @@ def test_cfg1_fp32_d64():
     _check_full(x, "fp32 d64 ragged")
 
 
+def test_bf16_more_sequences_than_the_scheduler_keeps_in_lds():
+    """4500 short sequences (1..100 rows): past the 4096 the scheduler keeps
+    in LDS, so the list and the sequence data beside each item come from the
+    workspace copies; every row against the oracle."""
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(1, 101, size=4500).tolist()
+    x = synth.make_attn(78, lengths, H=1, d=128, P=128, NT=32, alpha=1 / 128, dtype="bf16")
+    _check_full(x, "bf16 4500 short sequences")
+
+
 def test_cfg2_bf16_small():
     _check_full(synth.config(2, batch=6, max_len=300), "cfg2 bf16 reduced")
 

@@ -53,6 +53,15 @@ def test_bwd_ragged_causal_clamped_positions():
     _check(x, "bwd ragged causal P=70")
 
 
+def test_bwd_more_sequences_than_the_scheduler_keeps_in_lds():
+    """4200 short sequences (1..48 rows): both work lists and the G-block
+    prefix past the scheduler's LDS copies."""
+    rng = np.random.default_rng(79)
+    lengths = rng.integers(1, 49, size=4200).tolist()
+    x = synth.make_attn(80, lengths, H=1, d=128, P=64, NT=32, alpha=1 / 128, dtype="bf16")
+    _check(x, "bwd 4200 short sequences")
+
+
 def test_bwd_mfalcon_edge_counts():
     x = synth.make_attn(62, [70, 70, 200, 129, 64, 300], H=2, d=128, P=1024, NT=32, alpha=1 / 256,
                         dtype="bf16", num_candidates=[0, 70, 1, 65, 63, 150])

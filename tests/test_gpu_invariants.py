@@ -89,6 +89,33 @@ def test_schedule_matches_bruteforce_tiles(case):
     assert cost == sorted(cost, reverse=True)
 
 
+@pytest.mark.parametrize("B,max_len", [(9000, 128), (5000, 400)])
+def test_schedule_beyond_the_lds_copies(B, max_len):
+    """More sequences than the scheduler keeps in LDS (4096), and more row
+    blocks than it keeps costs for (8192): the list is built from its
+    workspace copies (searches over the global prefix, costs recomputed).
+    9000 sequences of 1..128 rows are 9000 row blocks; 5000 of up to 400 rows
+    about 10 000."""
+    import torch
+    from hstu_sequential_transducer_causal_amd import ops
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(1, max_len + 1, size=B).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(off[-1])
+    dev = torch.device("cuda:0")
+    q = torch.zeros((T, 1, 128), dtype=torch.bfloat16, device=dev)   # (the list reads no rows)
+    ts = torch.zeros(T, dtype=torch.int64, device=dev)
+    items, tm, tn = ops.hstu_attn_schedule(q, q, q, torch.from_numpy(off).to(dev), ts,
+                                           torch.zeros(64, device=dev), torch.zeros(32, device=dev),
+                                           max_seq_len=int(lengths.max()))
+    got = _items_to_tiles(items)
+    want = set(map(tuple, oracle.tiles(off, tm, tn).tolist()))
+    log(f"schedule B={B}: {len(items)} items, {len(got)} tiles")
+    assert len(items) > 8192 and got == want
+    cost = [(r[4] >> 16) - (r[4] & 0xFFFF) for r in items.tolist()]
+    assert cost == sorted(cost, reverse=True)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_causality_future_rows_do_not_change_past_rows(dtype):
     if dtype == "bf16":
