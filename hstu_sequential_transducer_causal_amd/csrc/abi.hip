@@ -124,8 +124,10 @@ hstu_status device_error(hipError_t e, const char* what) {
 // checked by one small kernel: hstu_validate_offsets, and every call when the
 // environment sets HSTU_VALIDATE=1 (a synchronising debug aid).
 hstu_status device_check_batch(int B, int64_t num_rows, int max_seq_len, const int32_t* offsets,
-                               const int32_t* lengths, const int32_t* ncand, hipStream_t stream) {
+                               const int32_t* lengths, const int32_t* ncand, hipStream_t stream,
+                               bool packed = false) {
     hstu::ValidateArgs v;
+    v.packed = packed ? 1 : 0;
     v.B = B;
     v.num_rows = num_rows;
     v.max_seq_len = max_seq_len;
@@ -138,7 +140,8 @@ hstu_status device_check_batch(int B, int64_t num_rows, int max_seq_len, const i
     if (first < 0) return ok();
     static const char* const what[8] = {"", "offsets[0] < 0", "offsets decrease", "offsets[B] > num_rows",
                                         "seq_lengths[b] outside [0, offsets[b+1] - offsets[b]]",
-                                        "length > max_seq_len", "num_candidates[b] outside [0, length]", ""};
+                                        "length > max_seq_len", "num_candidates[b] outside [0, length]",
+                                        "a layer needs packed offsets (offsets[0] = 0, offsets[B] = num_rows)"};
     return fail(HSTU_ERR_ARG, "sequence %lld: %s", (long long)(first / 8), what[first % 8]);
 }
 
@@ -856,7 +859,7 @@ hstu_status layer_fwd_run(const hstu_layer_args* l, void* ws, size_t ws_bytes, v
     if (l->B == 0 || l->num_rows == 0) return ok();
     if (validate_env()) {
         st = device_check_batch(l->B, l->num_rows, l->max_seq_len, l->seq_offsets, nullptr,
-                                l->num_candidates, static_cast<hipStream_t>(stream_));
+                                l->num_candidates, static_cast<hipStream_t>(stream_), true);
         if (st != HSTU_OK) return st;
     }
     const LayerWs lw = layer_ws(l);
@@ -1126,7 +1129,7 @@ hstu_status layer_bwd_run(const hstu_layer_bwd_args* g, void* ws, size_t ws_byte
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (l->B > 0 && l->num_rows > 0 && validate_env()) {
         st = device_check_batch(l->B, l->num_rows, l->max_seq_len, l->seq_offsets, nullptr, l->num_candidates,
-                                stream);
+                                stream, true);
         if (st != HSTU_OK) return st;
     }
     if (l->B == 0 || l->num_rows == 0) {   // empty batch: zero parameter gradients

@@ -52,6 +52,7 @@ struct ValidateArgs {
     const int32_t* offsets;
     const int32_t* lengths;
     const int32_t* ncand;
+    int packed = 0;   // (layer calls) also offsets[0] == 0 and offsets[B] == num_rows
 };
 hipError_t validate_batch(const ValidateArgs& a, hipStream_t stream, int64_t* first);
 

@@ -598,6 +598,7 @@ __global__ void __launch_bounds__(256) validate_batch_kernel(ValidateArgs a) {
         if (b == 0 && o0 < 0) check = 1;
         else if (o1 < o0) check = 2;
         else if (b == a.B - 1 && o1 > a.num_rows) check = 3;
+        else if (a.packed && ((b == 0 && o0 != 0) || (b == a.B - 1 && o1 != a.num_rows))) check = 7;
         else {
             if (a.lengths) {
                 const int64_t l = a.lengths[b];

@@ -51,9 +51,10 @@
  *     undefined behaviour unless it is checked: hstu_validate_offsets() checks
  *     it on the device, and with the environment variable HSTU_VALIDATE=1
  *     hstu_attn_fwd, mfalcon_score, the layer calls (forward and gradients,
- *     with or without saved activations) and hstu_attn_bwd run that check
- *     before launching anything (synchronising the stream: a debug aid, not
- *     for timed runs).
+ *     with or without saved activations; for these also the packed layout,
+ *     seq_offsets[0] = 0 and seq_offsets[B] = num_rows) and hstu_attn_bwd run
+ *     that check before launching anything (synchronising the stream: a debug
+ *     aid, not for timed runs).
  */
 #ifndef HSTU_H_
 #define HSTU_H_

@@ -106,3 +106,35 @@ def test_hstu_validate_env_guards_the_calls():
             os.environ.pop("HSTU_VALIDATE", None)
         else:
             os.environ["HSTU_VALIDATE"] = old
+
+
+def test_hstu_validate_layer_needs_packed_rows():
+    """A layer's gradients sum over every row, so its batch must be packed:
+    with HSTU_VALIDATE=1 a layer call whose offsets end before num_rows is
+    refused, the same batch packed runs."""
+    import torch
+    from hstu_sequential_transducer_causal_amd import _lib, ops
+    from hstu_testlib import dev_tensor
+    x = synth.make_layer_stack(33, [40, 70, 33], H=2, d=128, D=256, layers=1, P=128, NT=32,
+                               alpha=1 / 128)
+    xd = dev_tensor(x.x, "bf16")
+    w1, w2 = dev_tensor(x.w1[0], "bf16"), dev_tensor(x.w2[0], "bf16")
+    ts = torch.from_numpy(x.ts).cuda()
+    rp, rt = torch.from_numpy(x.rab_pos[0]).cuda(), torch.from_numpy(x.rab_time[0]).cuda()
+    run = lambda off: ops.hstu_layer_fwd(xd, w1, w2, torch.from_numpy(off.astype(np.int32)).cuda(), ts, rp,
+                                         rt, x.alpha, H=x.H, d=x.d, max_seq_len=70, ln_eps=x.eps)
+    old = os.environ.get("HSTU_VALIDATE")
+    try:
+        os.environ["HSTU_VALIDATE"] = "1"
+        run(x.offsets)
+        short = np.array([0, 40, 110], dtype=np.int64)   # the last 33 rows in no sequence
+        with pytest.raises(_lib.HstuError) as e:
+            run(short)
+        log(f"guarded layer: {e.value}")
+        assert e.value.status == _lib.HSTU_ERR_ARG and "packed" in str(e.value)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("HSTU_VALIDATE", None)
+        else:
+            os.environ["HSTU_VALIDATE"] = old
