@@ -98,7 +98,7 @@ class AttnCase:
                                   num_candidates=self.nc, u=self.u, y=self.y)
         self.ws = torch.empty(max(1, ops.attn_workspace_bytes(args)), dtype=torch.uint8, device=dev)
 
-    def step(self, ev0=None, ev1=None):
+    def step(self, ev0=None, ev1=None, ev2=None, ev3=None):
         from hstu_sequential_transducer_causal_amd import ops
         if self.with_scores:
             ops.mfalcon_score(self.q, self.k, self.v, self.u, self.off, self.nc, self.ts, self.rp,
@@ -110,7 +110,7 @@ class AttnCase:
             ops.hstu_attn_fwd(self.q, self.k, self.v, self.off, self.ts, self.rp, self.rt,
                               self.x.alpha, max_seq_len=self.max_len, num_candidates=self.nc,
                               u=self.u, ln_eps=self.x.eps, o=self.o, y=self.y, workspace=self.ws,
-                              ev_core_begin=ev0, ev_core_end=ev1)
+                              ev_core_begin=ev0, ev_core_end=ev1, ev_epi_begin=ev2, ev_epi_end=ev3)
 
 
 class StackCase:
@@ -465,26 +465,28 @@ def sl_sweep_record(dev, steps):
     return out
 
 
-def time_case(case, steps, warmup, core_events=True):
+def time_case(case, steps, warmup, core_events=True, epi_events=False):
     """Wall time per step (synchronised bracket) and mean core-kernel time (HIP
-    events carried by the core launch on every EVENT_STRIDE-th timed step)."""
+    events carried by the core launch on every EVENT_STRIDE-th timed step);
+    with epi_events also the epilogue launch's mean time, left in
+    case.epi_ms."""
     import torch
     for _ in range(warmup):
         case.step()
     torch.cuda.synchronize()
     evs = []
+    nev = 4 if epi_events else 2
     if core_events:
         for _ in range(0, steps, EVENT_STRIDE):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(); b.record()           # materialise the HIP events
-            evs.append((a, b))
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+            for ev in e:
+                ev.record()                  # materialise the HIP events
+            evs.append(e)
         torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if core_events and i % EVENT_STRIDE == 0:
-            a, b = evs[i // EVENT_STRIDE]
-            case.step(a.cuda_event, b.cuda_event)
+            case.step(*(ev.cuda_event for ev in evs[i // EVENT_STRIDE]))
         else:
             case.step()
     torch.cuda.synchronize()
@@ -492,7 +494,9 @@ def time_case(case, steps, warmup, core_events=True):
     ms_step = (t1 - t0) * 1e3 / steps
     core_ms = None
     if core_events:
-        core_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        core_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        if epi_events:
+            case.epi_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     return ms_step, core_ms
 
 
@@ -779,7 +783,8 @@ def main():
             torch.cuda.empty_cache()
 
     # the headline: W untimed warm-up steps, then K timed steps
-    ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5))
+    ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5),
+                                 epi_events=(wl in (2, 3)))
     value = fl / (ms_step * 1e-3) / 1e12
     tokens_s = x.T / (ms_step * 1e-3)
     log(f"step {ms_step:.3f} ms, core {core_ms} ms, {value:.1f} TFLOP/s")
@@ -791,6 +796,15 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(x.name),
                     "kernel": "attn_bf16_kernel", "core_ms": round(core_ms, 4)}
 
+    epilogue = None
+    if getattr(case, "epi_ms", None):
+        # LayerNorm(O) * U: O and U read once, Y written once (bf16)
+        eb = 3 * x.T * x.H * x.d * 2
+        gbs = eb / (case.epi_ms * 1e-3) / 1e9
+        epilogue = {"bound": "hbm", "kernel": "ln_gate_rows_kernel", "ms": round(case.epi_ms, 4),
+                    "bytes": eb, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
     line = {
         "metric": "HSTU attention fwd TFLOP/s (unmasked) + jagged tokens/s; % bf16 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -801,6 +815,7 @@ def main():
         "tokens_per_s": round(tokens_s, 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
+        "epilogue": epilogue,
         "parity": parity,
     }
     if others is not None:

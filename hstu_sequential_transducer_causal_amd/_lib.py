@@ -48,6 +48,7 @@ class AttnArgs(ctypes.Structure):
         ("y", _vp), ("y_stride", _i64),
         ("ln_eps", _f32),
         ("ev_core_begin", _vp), ("ev_core_end", _vp),
+        ("ev_epi_begin", _vp), ("ev_epi_end", _vp),
     ]
 
 

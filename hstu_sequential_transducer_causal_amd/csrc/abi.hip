@@ -307,6 +307,8 @@ hipError_t run_ln_gate(const hstu_attn_args* a, const Sched& s, const float* w, 
     l.d = a->d_v;
     l.BM = hstu::kBf16TileM;
     l.cand_only = cand_only ? 1 : 0;
+    l.ev_begin = static_cast<hipEvent_t>(a->ev_epi_begin);
+    l.ev_end = static_cast<hipEvent_t>(a->ev_epi_end);
     return hstu::launch_ln_gate(l, stream);
 }
 

@@ -16,6 +16,8 @@
 // Rows of a row block that the bf16 attention core split over key ranges
 // arrive as fp32 partial sums: their O is the sum of those, rounded to bf16
 // as the core rounds O, and is written to O here before it is normalised.
+#include <hip/hip_ext.h>
+
 #include "internal.h"
 #include "hstu_device.h"
 #include "../../include/hstu.h"
@@ -402,20 +404,20 @@ hipError_t launch_typed(const LnGateArgs& a, hipStream_t stream) {
     if (BF16 && a.B > 0 && !a.lengths && !a.ncand && !a.cross && !a.w && a.y && nch <= 2 && !a.cand_only) {
         if (nch == 1) {
             const dim3 g((unsigned)((a.num_rows + 4 * kRowsPerBlock - 1) / (4 * kRowsPerBlock)));
-            hipLaunchKernelGGL((ln_gate_rows_kernel<1, 4>), g, dim3(kThreads), 0, stream, a);
+            hipExtLaunchKernelGGL((ln_gate_rows_kernel<1, 4>), g, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a);
         } else {
             const dim3 g((unsigned)((a.num_rows + 2 * kRowsPerBlock - 1) / (2 * kRowsPerBlock)));
-            hipLaunchKernelGGL((ln_gate_rows_kernel<2, 2>), g, dim3(kThreads), 0, stream, a);
+            hipExtLaunchKernelGGL((ln_gate_rows_kernel<2, 2>), g, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a);
         }
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((a.num_rows + kRowsPerBlock - 1) / kRowsPerBlock));
     switch (nch) {
-        case 1: hipLaunchKernelGGL((ln_gate_kernel<BF16, 1>), grid, dim3(kThreads), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((ln_gate_kernel<BF16, 2>), grid, dim3(kThreads), 0, stream, a); break;
+        case 1: hipExtLaunchKernelGGL((ln_gate_kernel<BF16, 1>), grid, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a); break;
+        case 2: hipExtLaunchKernelGGL((ln_gate_kernel<BF16, 2>), grid, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a); break;
         case 3:
-        case 4: hipLaunchKernelGGL((ln_gate_kernel<BF16, 4>), grid, dim3(kThreads), 0, stream, a); break;
-        default: hipLaunchKernelGGL((ln_gate_kernel<BF16, 8>), grid, dim3(kThreads), 0, stream, a); break;
+        case 4: hipExtLaunchKernelGGL((ln_gate_kernel<BF16, 4>), grid, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a); break;
+        default: hipExtLaunchKernelGGL((ln_gate_kernel<BF16, 8>), grid, dim3(kThreads), 0, stream, a.ev_begin, a.ev_end, 0, a); break;
     }
     return hipGetLastError();
 }

@@ -326,6 +326,8 @@ struct LnGateArgs {
     const float* rab_pos = nullptr; int rp_hs = 0;
     const float* rab_time = nullptr; int rt_hs = 0;
     float alpha = 0.0f;
+    // optional events stamped with the start / end of the launch
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
 };
 
 hipError_t launch_ln_gate(const LnGateArgs& a, hipStream_t stream);

@@ -48,7 +48,8 @@ def _empty_ws(nbytes: int, device) -> torch.Tensor:
 def make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
                    max_seq_len: int, o: torch.Tensor, seq_lengths=None, num_candidates=None,
                    u=None, y=None, ln_eps: float = 1e-5, act: int = _lib.HSTU_ACT_SILU,
-                   ev_core_begin=None, ev_core_end=None) -> _lib.AttnArgs:
+                   ev_core_begin=None, ev_core_end=None, ev_epi_begin=None,
+                   ev_epi_end=None) -> _lib.AttnArgs:
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
     H, d_qk = (q.shape[1], q.shape[2]) if q.dim() == 3 else (None, None)
@@ -89,13 +90,16 @@ def make_attn_args(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *
     a.ln_eps = float(ln_eps)
     a.ev_core_begin = ev_core_begin
     a.ev_core_end = ev_core_end
+    a.ev_epi_begin = ev_epi_begin
+    a.ev_epi_end = ev_epi_end
     return a
 
 
 def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
                   max_seq_len: int, seq_lengths=None, num_candidates=None, u=None,
                   ln_eps: float = 1e-5, act: int = _lib.HSTU_ACT_SILU, o=None, y=None,
-                  workspace=None, stream=None, ev_core_begin=None, ev_core_end=None):
+                  workspace=None, stream=None, ev_core_begin=None, ev_core_end=None,
+                  ev_epi_begin=None, ev_epi_end=None):
     """O (and Y = LayerNorm(O) * U when ``u`` is given) of the jagged batch.
 
     q, k: [rows, H, d_qk]; v, u: [rows, H, d_v]; seq_offsets int32 [B+1];
@@ -111,7 +115,7 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, alpha, *,
                           max_seq_len=max_seq_len, o=o, seq_lengths=seq_lengths,
                           num_candidates=num_candidates, u=u, y=y if u is not None else None,
                           ln_eps=ln_eps, act=act, ev_core_begin=ev_core_begin,
-                          ev_core_end=ev_core_end)
+                          ev_core_end=ev_core_end, ev_epi_begin=ev_epi_begin, ev_epi_end=ev_epi_end)
     need = lib.hstu_attn_workspace_bytes(ctypes.byref(args))
     if workspace is None:
         workspace = _empty_ws(need, q.device)

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 10
+#define HSTU_ABI_VERSION 11
 
 /* ------------------------------------------------------------------ status */
 typedef int32_t hstu_status;
@@ -126,6 +126,10 @@ typedef struct hstu_attn_args {
        packets between kernels); for timing that kernel alone; NULL = none */
     void* ev_core_begin;
     void* ev_core_end;
+    /* optional hipEvent_t stamped with the start / end of the epilogue kernel
+       (LayerNorm (.) U, when y != NULL) in the same way; NULL = none */
+    void* ev_epi_begin;
+    void* ev_epi_end;
 } hstu_attn_args;
 
 /* Version of this ABI (HSTU_ABI_VERSION). */

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.hstu_abi_version() == 10
+    assert lib.hstu_abi_version() == 11
     for s in [0, -1, -2, -3, -4, 99]:
         assert lib.hstu_status_string(s)
 
