@@ -60,6 +60,14 @@ def test_bf16_more_sequences_than_the_scheduler_keeps_in_lds():
     _check_full(x, "bf16 4500 short sequences")
 
 
+def test_bf16_three_heads():
+    """An odd head count through the per-die work queues (head rotated by the
+    sequence)."""
+    x = synth.make_attn(65, [50, 130, 7, 260, 1, 129], H=3, d=128, P=256, NT=32, alpha=1 / 256,
+                        dtype="bf16")
+    _check_full(x, "bf16 three heads")
+
+
 def test_cfg2_bf16_small():
     _check_full(synth.config(2, batch=6, max_len=300), "cfg2 bf16 reduced")
 

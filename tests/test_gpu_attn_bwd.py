@@ -62,6 +62,16 @@ def test_bwd_more_sequences_than_the_scheduler_keeps_in_lds():
     _check(x, "bwd 4200 short sequences")
 
 
+def test_bwd_three_heads():
+    """An odd head count: entries of the work list spread over the eight
+    per-die queues with the head rotated by the sequence; every head's
+    outputs and the per-head tables' gradients against the oracle."""
+    x = synth.make_attn(64, [50, 130, 7, 260, 1], H=3, d=128, P=256, NT=32, alpha=1 / 256,
+                        dtype="bf16")
+    x.rab_pos = np.stack([x.rab_pos, x.rab_pos[::-1].copy(), 0.5 * x.rab_pos]).astype(np.float32)
+    _check(x, "bwd three heads, per-head position tables")
+
+
 def test_bwd_mfalcon_edge_counts():
     x = synth.make_attn(62, [70, 70, 200, 129, 64, 300], H=2, d=128, P=1024, NT=32, alpha=1 / 256,
                         dtype="bf16", num_candidates=[0, 70, 1, 65, 63, 150])
