@@ -74,22 +74,43 @@ struct Vec8 {
     }
 };
 
+// Batches of up to this many sequences have their offsets copied into LDS by
+// each workgroup of ln_gate_kernel (one coalesced read), so that the rows'
+// sequence searches do not wait on memory at every step.
+constexpr int kOffLds = 1024;
+
 template <bool BF16, int NCH>
 __global__ void __launch_bounds__(kThreads) ln_gate_kernel(LnGateArgs a) {
+    __shared__ int32_t s_off[kOffLds + 1], s_len[kOffLds], s_nc[kOffLds];
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const bool need_seq = a.lengths || a.ncand || a.cross;
+    const bool off_lds = need_seq && a.B > 0 && a.B <= kOffLds;   // (uniform)
+    if (off_lds) {
+        for (int i = threadIdx.x; i <= a.B; i += kThreads) {
+            s_off[i] = a.offsets[i];
+            if (i < a.B) {
+                if (a.lengths) s_len[i] = a.lengths[i];
+                if (a.ncand) s_nc[i] = a.ncand[i];
+            }
+        }
+        __syncthreads();
+    }
+    const int32_t* off = off_lds ? s_off : a.offsets;
+    const int32_t* lens = off_lds ? s_len : a.lengths;
+    const int32_t* ncs = off_lds ? s_nc : a.ncand;
     if (a.B <= 0 || row >= a.num_rows) return;
-    if (row < a.offsets[0] || row >= a.offsets[a.B]) return;
+    if (row < off[0] || row >= off[a.B]) return;
     // A packed causal batch needs no sequence lookup: every row in range is a
     // valid history row.
     int b = 0, r = 0, n = 0;
     bool want_score = false;
-    if (a.lengths || a.ncand || a.cross) {
-        b = seq_of_row(a.offsets, a.B, row);
-        r = (int)(row - a.offsets[b]);
-        const int L = a.lengths ? a.lengths[b] : a.offsets[b + 1] - a.offsets[b];
+    if (need_seq) {
+        b = seq_of_row(off, a.B, row);
+        r = (int)(row - off[b]);
+        const int L = a.lengths ? lens[b] : off[b + 1] - off[b];
         if (r >= L) return;  // padding row: never read or written
-        n = a.cross ? 0 : (a.ncand ? L - a.ncand[b] : L);
+        n = a.cross ? 0 : (a.ncand ? L - ncs[b] : L);
         want_score = a.w != nullptr && r >= n;
     }
     // (with cand_only only the candidate rows are covered by this call's map)
