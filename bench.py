@@ -507,12 +507,16 @@ KERNEL_SRCS = [os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc
 
 
 def kernel_hash() -> str:
-    """Hash of the sources the attention-core kernel is compiled from."""
+    """Hash of the sources the attention-core kernel is compiled from and of
+    its compiler flags."""
     import hashlib
+    from hstu_sequential_transducer_causal_amd import build
     h = hashlib.sha256()
     for src in KERNEL_SRCS:
         with open(src, "rb") as f:
             h.update(f.read())
+    flags = [f for f in build.CXXFLAGS if f != "-I" and not os.path.isabs(f)]   # (no paths)
+    h.update(repr(flags + build.EXTRA_FLAGS.get("attn_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,6 +24,14 @@ CXXFLAGS = [
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 
+# Per-source additions.  The attention core is scheduled by LLVM's
+# iterative ILP strategy: measured 1.5-4 % faster on the forward workloads,
+# while the same flag made the key-gradient kernel slower (so it stays off
+# elsewhere).
+EXTRA_FLAGS = {
+    "attn_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -33,7 +41,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CXXFLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
