@@ -13,29 +13,36 @@
 //   drab_pos[pb(i, j)] += G_ij,   drab_time[tb(i, j)] += G_ij,
 // with SiLU'(x) = s + SiLU(x) (1 - s), s = sigmoid(x) (identity: 1).
 //
-// Two persistent kernels, with no atomics on the gradients of Q, K and V:
-//   * attn_bwd_dq_kernel: one work item = 128 query rows x 1 head (the
-//     forward's work list).  Per 32-key tile: S^T = K Q^T and (dO V^T)^T =
-//     V dO^T with Q and dO in registers, then G^T and dQ += G K.  G is also
-//     summed by position and time bucket into per-wave LDS histograms,
-//     written as one partial row per work item and added up in a fixed order
-//     by rab_grad_partial_kernel and rab_grad_final_kernel (so the table
-//     gradients do not depend on which workgroup took which item).  LDS float
-//     atomics are slow, so the common cases avoid them per element: a block
-//     of history rows sums its 63 position diagonals through a skewed LDS
-//     scratch, a block of candidate rows (one position) sums its key columns
-//     across the lanes, and a block spanning at most four time buckets sums
-//     them in registers; one atomic per bucket then adds each sum.
-//   * attn_bwd_dkv_kernel: one work item = 128 keys x 1 head (a key-major
-//     work list: the 32-row query tiles that see the keys).  Per query tile:
-//     S = Q K^T and dO V^T with K and V in registers, then dV += A^T dO and
-//     dK += G^T Q (A = SiLU(S) masked).
-// Both recompute S.  A tile feeds two products that read it in different
-// orders (rows as M, and rows as the contraction); it is staged twice, in the
-// two swizzles those reads are conflict-free in.  Tiles arrive by
-// direct-to-LDS buffer loads two tiles ahead of use (a 3-stage ring).  The
-// relative bias takes the forward's block-uniform shortcuts (a constant time
-// bucket, a fully clamped position bucket) and otherwise reads per element.
+// Two persistent kernels, with no atomics on the gradients of Q, K and V;
+// both pull their work lists per accelerator die (entry f H + k runs head
+// (k - b) mod H, so a die meets the same sequence-heads' operands in its L2):
+//   * attn_bwd_dkv_kernel (first): one work item = 128 keys x 1 head (a
+//     key-major work list: the 32-row query tiles that see the keys).  Per
+//     query tile: S = Q K^T and dO V^T with K and V in registers, then
+//     dV += A^T dO and dK += G^T Q (A = SiLU(S) masked).  It also stores, for
+//     the dQ kernel, G of every 32 x 32 block holding a visible pair (fp32, in
+//     its own register order: lane = key, 16 queries per lane) and its K
+//     fragments in the order G K reads them.  A tile feeds two products that
+//     read it in different orders (rows as M, and rows as the contraction); it
+//     is staged twice, in the two swizzles those reads are conflict-free in.
+//     Tiles arrive by direct-to-LDS buffer loads two tiles ahead of use (a
+//     3-stage ring).  The relative bias takes the forward's block-uniform
+//     shortcuts (a constant time bucket, a fully clamped position bucket) and
+//     otherwise reads per element.
+//   * attn_bwd_dq_kernel (second): one work item = 128 query rows x 1 head
+//     (the forward's work list); each wave streams its 32-row tile's G blocks
+//     and K fragments (buffer loads, fixed counts per step), turns each G
+//     block over with two identity MFMAs (lane = key to lane = query) and
+//     accumulates dQ += G K.  The exact fp32 G is also summed by position and
+//     time bucket into per-wave LDS histograms, written as one partial row per
+//     work item and added up in a fixed order by rab_grad_partial_kernel and
+//     rab_grad_final_kernel (so the table gradients do not depend on which
+//     workgroup took which item).  LDS float atomics are slow, so the common
+//     cases avoid them per element: a block of history rows sums its 63
+//     position diagonals through a skewed LDS scratch, a block of candidate
+//     rows (one position) sums its key columns across the lanes, and a block
+//     spanning at most four time buckets sums them in registers; one atomic
+//     per bucket then adds each sum.
 #include <hip/hip_ext.h>
 
 #include "internal.h"
