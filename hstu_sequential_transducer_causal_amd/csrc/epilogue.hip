@@ -9,9 +9,13 @@
 // LayerNorm runs over all H*d_v values of a row (biased variance, eps added
 // to the variance, no affine parameters).
 //
-// HBM-bound: one wave per row, 16-byte vector loads, the row held in
-// registers for a two-pass (mean, then centred variance) reduction with
-// wavefront shuffles; no LDS.
+// HBM-bound: 16-byte vector loads, the row held in registers for a two-pass
+// (mean, then centred variance) reduction with wavefront shuffles.  The
+// common case (bf16, packed, Y wanted, no scores) takes ln_gate_rows_kernel:
+// several rows per wave, all their loads issued before any arithmetic.
+// Everything else takes ln_gate_kernel (one wave per row), which for batches
+// of up to 1024 sequences first copies the batch structure into LDS for its
+// rows' sequence searches.  ln_gate_bwd_kernel is the gate's gradient.
 //
 // Rows of a row block that the bf16 attention core split over key ranges
 // arrive as fp32 partial sums: their O is the sum of those, rounded to bf16

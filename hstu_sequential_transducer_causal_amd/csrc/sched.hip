@@ -22,8 +22,11 @@
 // tiles) so that the persistent attention kernel, which takes items in list
 // order, balances its CUs like a longest-processing-time schedule.
 //
-// One workgroup of 1024 threads runs the whole build; it is a few
-// microseconds of work next to the attention core.
+// One workgroup of 1024 threads runs the whole build (a few microseconds next
+// to the attention core); the launch's other workgroups encode the timestamps
+// (prep_kernel).  The gradients build their two lists and the G-block prefix
+// in one launch (prep_pair_kernel).  The batch validator (validate_batch)
+// lives here too.
 #include <algorithm>
 
 #include "internal.h"
