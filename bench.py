@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=400)
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="seconds of untimed back-to-back steps before each case's warm-up (0: none)")
     p.add_argument("--workload", type=int, default=3, help="workload number 2..5 for the main line")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-others", action="store_true")
@@ -187,11 +189,37 @@ class BwdCase:
 # every EVENT_STRIDE-th timed step carries them; the others run bare.
 EVENT_STRIDE = 10
 
+# Before its warm-up steps every timed case first runs untimed steps back to
+# back for SETTLE_S seconds of wall time (--settle): after the host-side work
+# between cases (input generation, the oracle) the GPU's clocks have dropped,
+# and a short timed window (20 steps of 0.25 ms) would otherwise measure their
+# ramp, not the sustained rate.  The count of those steps is reported.
+SETTLE_S = 0.25
+SETTLE_LOG = []
+
+
+def settle(step, label=""):
+    """Run step() back to back, untimed, until SETTLE_S seconds have passed
+    (synchronising every 16 steps to read the clock); returns the count."""
+    import torch
+    n = 0
+    if SETTLE_S > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            for _ in range(16):
+                step()
+            n += 16
+            torch.cuda.synchronize()
+    SETTLE_LOG.append((label, n))
+    return n
+
 
 def time_bwd(case, steps, warmup):
     """Wall time per step and the mean dQ / dK-dV kernel times (HIP events
     carried by those launches on every EVENT_STRIDE-th timed step)."""
     import torch
+    settle(case.step, "bwd")
     for _ in range(warmup):
         case.step()
     torch.cuda.synchronize()
@@ -401,6 +429,7 @@ def sl_record(dev, steps):
     rows = [torch.randn(T, 1024, generator=g, device=dev).to(torch.bfloat16) for _ in range(4)]
     ts = torch.arange(T, dtype=torch.int64, device=dev) * 60
     tensors = (*rows, ts)
+    settle(lambda: ops.stochastic_length(off, synth.SL_CAP, seed=1, step=0, tensors=tensors), "sl")
     for _ in range(2):
         ops.stochastic_length(off, synth.SL_CAP, seed=1, step=0, tensors=tensors)
     torch.cuda.synchronize()
@@ -447,6 +476,7 @@ def sl_sweep_record(dev, steps):
             ops.hstu_attn_fwd(q.view(T, H, d), k.view(T, H, d), v.view(T, H, d), oo, t, rp, rt,
                               1.0 / synth.SL_MAX_RAW, max_seq_len=cap, u=u.view(T, H, d), o=o, y=y)
 
+        settle(lambda: step(0), f"sl alpha {alpha}")
         for i in range(2):
             step(i)
         torch.cuda.synchronize()
@@ -471,6 +501,7 @@ def time_case(case, steps, warmup, core_events=True, epi_events=False):
     with epi_events also the epilogue launch's mean time, left in
     case.epi_ms."""
     import torch
+    settle(case.step, getattr(case, "name", ""))
     for _ in range(warmup):
         case.step()
     torch.cuda.synchronize()
@@ -625,6 +656,8 @@ def parity_record(case, x, ref_o=None, nseq=0):
 
 def main():
     args = parse()
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -786,9 +819,10 @@ def main():
             log(f"{xb.name} gradients: {rec}")
             torch.cuda.empty_cache()
 
-    # the headline: W untimed warm-up steps, then K timed steps
+    # the headline: untimed settle steps, W untimed warm-up steps, then K timed steps
     ms_step, core_ms = time_case(case, args.steps, args.warmup, core_events=(wl != 5),
                                  epi_events=(wl in (2, 3)))
+    settle_steps = SETTLE_LOG[-1][1]
     value = fl / (ms_step * 1e-3) / 1e12
     tokens_s = x.T / (ms_step * 1e-3)
     log(f"step {ms_step:.3f} ms, core {core_ms} ms, {value:.1f} TFLOP/s")
@@ -812,7 +846,8 @@ def main():
     line = {
         "metric": "HSTU attention fwd TFLOP/s (unmasked) + jagged tokens/s; % bf16 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "settle": {"seconds": SETTLE_S, "steps": settle_steps},
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": x.name, "global_batch": x.B, "tokens": x.T,
                    "max_seq_len": int(L.max()), "heads": x.H, "head_dim": x.d},
