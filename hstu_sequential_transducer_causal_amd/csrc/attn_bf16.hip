@@ -137,16 +137,29 @@ __device__ __forceinline__ uint32_t tile_soff(int kt, bool far, uint32_t tile_by
     return far ? kFarOffset : (uint32_t)kt * tile_bytes;
 }
 
+// LDS byte addresses of the ring's parts as plain integers, taken once from
+// the shared array itself: an offset added to the generic Smem pointer and
+// cast back to LDS costs an aperture add and a null check at every use (7
+// scalar instructions per load group in the tile loop).
+struct RingLds {
+    uint32_t k, v, tsk;
+};
+__device__ __forceinline__ RingLds ring_lds(const uint8_t* smem_raw) {
+    const uint32_t b = lds_addr(smem_raw);
+    return RingLds{b + (uint32_t)offsetof(Smem, k), b + (uint32_t)offsetof(Smem, v),
+                   b + (uint32_t)offsetof(Smem, tsk)};
+}
+
 // The three parts of a tile's loads go out at different points of the
 // previous tiles' work, so that no wave stalls long on a full load queue.
-__device__ __forceinline__ void issue_k(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
-    const uint32_t kl = lds_addr(s.k[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+__device__ __forceinline__ void issue_k(const TileDma& d, const RingLds& r, int stage, int kt, bool far, int wave) {
+    const uint32_t kl = r.k + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
     const uint32_t ksoff = uniu(tile_soff(kt, far, d.ktile));
 #pragma unroll
     for (int m = 0; m < 2; ++m) dma16(d.krs, uniu(kl + m * 1024), d.koff[m], ksoff);
 }
-__device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
-    const uint32_t vl = lds_addr(s.v[0]) + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
+__device__ __forceinline__ void issue_v(const TileDma& d, const RingLds& r, int stage, int kt, bool far, int wave) {
+    const uint32_t vl = r.v + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
     const uint32_t vsoff = uniu(tile_soff(kt, far, d.vtile));
 #pragma unroll
     for (int m = 0; m < 2; ++m) dma16(d.vrs, uniu(vl + m * 1024), d.voff[m], vsoff);
@@ -154,8 +167,8 @@ __device__ __forceinline__ void issue_v(const TileDma& d, Smem& s, int stage, in
 // The codes of keys 8 wave .. 8 wave + 7 (codes of keys past the sequence end
 // are other rows' or zeros, and those keys are masked).  The lane's offset is
 // fixed per item, the tile is the scalar offset.
-__device__ __forceinline__ void issue_codes(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
-    const uint32_t lds = uniu(lds_addr(s.tsk[0]) + (uint32_t)((stage * 4 + wave) * 64 * 4));
+__device__ __forceinline__ void issue_codes(const TileDma& d, const RingLds& r, int stage, int kt, bool far, int wave) {
+    const uint32_t lds = uniu(r.tsk + (uint32_t)((stage * 4 + wave) * 64 * 4));
     const uint32_t soff = uniu(tile_soff(kt, far, (uint32_t)(BN * 4)));
     asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(d.code_off), "s"(d.wrs), "s"(soff),
                  "{m0}"(lds)
@@ -176,11 +189,28 @@ __device__ __forceinline__ float acc_fmac(float acc, float a, float b) {
     asm("v_fmac_f32 %0, %1, %2" : "+v"(acc) : "v"(a), "v"(b));
     return acc;
 }
-
-__device__ __forceinline__ void issue_tile(const TileDma& d, Smem& s, int stage, int kt, bool far, int wave) {
-    issue_k(d, s, stage, kt, far, wave);
-    issue_v(d, s, stage, kt, far, wave);
-    issue_codes(d, s, stage, kt, far, wave);
+// acc[t] += (code[t] <= lim ? x : 0) for four elements, each compare's mask
+// in VCC and used at once (compiled code keeps one mask per element live in
+// scalar registers); one block, so that the wait state the compiler puts
+// between inline-assembly blocks comes once per four elements.
+__device__ __forceinline__ void acc_add_if_le4(float& a0, float& a1, float& a2, float& a3, const u32x4& code,
+                                               uint32_t lim, float x) {
+    float s0, s1;
+    asm("v_cmp_le_u32 vcc, %6, %10\n\t"
+        "v_cndmask_b32 %4, 0, %11, vcc\n\t"
+        "v_cmp_le_u32 vcc, %7, %10\n\t"
+        "v_cndmask_b32 %5, 0, %11, vcc\n\t"
+        "v_add_f32 %0, %0, %4\n\t"
+        "v_cmp_le_u32 vcc, %8, %10\n\t"
+        "v_cndmask_b32 %4, 0, %11, vcc\n\t"
+        "v_add_f32 %1, %1, %5\n\t"
+        "v_cmp_le_u32 vcc, %9, %10\n\t"
+        "v_cndmask_b32 %5, 0, %11, vcc\n\t"
+        "v_add_f32 %2, %2, %4\n\t"
+        "v_add_f32 %3, %3, %5"
+        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "=&v"(s0), "=&v"(s1)
+        : "v"(code[0]), "v"(code[1]), "v"(code[2]), "v"(code[3]), "v"(lim), "v"(x)
+        : "vcc");
 }
 
 // kCross: the queries are candidates in their own buffers, each seeing every
@@ -191,6 +221,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
     extern __shared__ __align__(16) uint8_t smem_raw[];
     Smem& s = *reinterpret_cast<Smem*>(smem_raw);
     float* ptab = reinterpret_cast<float*>(smem_raw + ((sizeof(Smem) + 15) & ~size_t(15)));
+    const RingLds ring = ring_lds(smem_raw);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -318,12 +349,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // load groups: after the barrier of tile t go out V(t+2), then (mid-step)
         // K(t+3) and the codes of t+3, 5 loads per group; the prologue sends
         // the groups of t = -3 (its V part from out of range), -2 and -1
-        issue_v(dma, s, kStages - 1, 0, true, wave);
+        issue_v(dma, ring, kStages - 1, 0, true, wave);
 #pragma unroll
         for (int pre = 0; pre < kStages - 1; ++pre) {
-            if (pre > 0) issue_v(dma, s, pre - 1, tile_of(pre - 1), pre - 1 >= ntiles, wave);
-            issue_k(dma, s, pre, tile_of(pre), pre >= ntiles, wave);
-            issue_codes(dma, s, pre, tile_of(pre), pre >= ntiles, wave);
+            if (pre > 0) issue_v(dma, ring, pre - 1, tile_of(pre - 1), pre - 1 >= ntiles, wave);
+            issue_k(dma, ring, pre, tile_of(pre), pre >= ntiles, wave);
+            issue_codes(dma, ring, pre, tile_of(pre), pre >= ntiles, wave);
         }
 
         // ---- this wave's 32 query rows
@@ -391,13 +422,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // so that they stay in registers instead of being recomputed per tile.
         uint32_t kx[8], vx[4], cx;
         {
-            const uint32_t kb = lds_addr(s.k[0]) + k_lane_offset(lane);
-            const uint32_t vb = lds_addr(s.v[0]) + v_lane_offset(lane);
+            const uint32_t kb = ring.k + k_lane_offset(lane);
+            const uint32_t vb = ring.v + v_lane_offset(lane);
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) kx[kc] = kb ^ (uint32_t)(kc << 5);
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) vx[nb] = vb ^ (uint32_t)(nb << 6);
-            cx = lds_addr(&s.tsk[0][0][4 * h2]);
+            cx = ring.tsk + (uint32_t)(4 * h2 * sizeof(uint32_t));
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) asm volatile("" : "+v"(kx[kc]));
 #pragma unroll
@@ -420,7 +451,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             wait_vmcnt(kLoadsPerTile + 3);
             lds_barrier();
             const int t2 = it + kStages - 2;
-            issue_v(dma, s, (st + kStages - 2) & (kStages - 1), tile_of(t2), t2 >= ntiles, wave);
+            issue_v(dma, ring, (st + kStages - 2) & (kStages - 1), tile_of(t2), t2 >= ntiles, wave);
         };
 
         // bias of tile it (as the initial accumulator, plus a constant) and
@@ -430,6 +461,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             bool wide;
             int czlo, czhi, j0;
             uint32_t pa;   // LDS address of the lane's position entries
+            bool kfirst;   // every key code of the block <= every row code of the wave
         };
         const int xmax = P + 31;   // a lane's first difference past this: all 32 clamp to P-1
         auto tile_bias = [&](int it, int st, f32x16& acc, float& cadd, bf16x8 (&kf)[8]) -> TileFacts {
@@ -461,7 +493,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             const uint32_t pa = ptab_hi - 8u * (uint32_t)x;   // u0 = Dhi - x
 #pragma unroll
             for (int kc = 0; kc < 8; ++kc) kf[kc] = lds_read_b128(kx[kc] + (uint32_t)(st * kStageBytes));
-            return TileFacts{wide, czlo, czhi, j0, pa};
+            return TileFacts{wide, czlo, czhi, j0, pa, !wide && g1 >= 0};
         };
         // the position entries u0 + 8q + t as the pairs u0 + 8q and u0 + 8q + 2,
         // at one base with immediate offsets.  (Read on each path of
@@ -500,8 +532,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                         load_pos(f.pa, acc);
                         cadd += tlo;
                     } else {
-                        load_codes();
-                        load_pos(f.pa, acc);
                         // g = |e_i - e_j| + 1 lies in [2^(31 - czlo), 2^(33 - czlo)),
                         // and the bucket is czhi exactly when bit 32 - czlo of g
                         // is set: g >> (32 - czlo) is 0 or 1, the bucket's share
@@ -510,11 +540,32 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                         const float dt = thi - tlo;
                         const uint32_t sh = (uint32_t)(32 - czlo);
                         cadd += tlo;
+                        if (f.kfirst && rmin + 1u >= (1u << sh)) {
+                            // the block's keys are at or before the wave's rows
+                            // (every block off the diagonal of a time-ordered
+                            // sequence): g = e_i - e_j + 1, so the key is in
+                            // bucket czhi exactly when e_j <= e_i + 1 - 2^sh,
+                            // one compare and select per element (the bound
+                            // does not wrap: e_i >= rmin >= 2^sh - 1)
+                            const uint32_t lim = tie + 1u - (1u << sh);
+                            load_codes();
+                            load_pos(f.pa, acc);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
+                            for (int q = 0; q < 4; ++q) {
+                                float a0 = acc[4 * q], a1 = acc[4 * q + 1], a2 = acc[4 * q + 2], a3 = acc[4 * q + 3];
+                                acc_add_if_le4(a0, a1, a2, a3, codes[q], lim, dt);
+                                acc[4 * q] = a0; acc[4 * q + 1] = a1; acc[4 * q + 2] = a2; acc[4 * q + 3] = a3;
+                            }
+                        } else {
+                            load_codes();
+                            load_pos(f.pa, acc);
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                acc[4 * q + t] = acc_fmac(acc[4 * q + t], (float)(sad_u32(tie, codes[q][t], 1u) >> sh), dt);
+                            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    acc[4 * q + t] =
+                                        acc_fmac(acc[4 * q + t], (float)(sad_u32(tie, codes[q][t], 1u) >> sh), dt);
+                        }
                     }
                 } else if (!wide) {
                     load_codes();
@@ -591,8 +642,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         auto issue_rest = [&](int it, int st) {
             const int t3 = it + kStages - 1;
             const int st3 = (st + kStages - 1) & (kStages - 1), kt3 = tile_of(t3);
-            issue_k(dma, s, st3, kt3, t3 >= ntiles, wave);
-            issue_codes(dma, s, st3, kt3, t3 >= ntiles, wave);
+            issue_k(dma, ring, st3, kt3, t3 >= ntiles, wave);
+            issue_codes(dma, ring, st3, kt3, t3 >= ntiles, wave);
         };
 
         // V^T fragments of the tile in stage st (see read_v_tile)
