@@ -188,6 +188,66 @@ def test_identity_integer_inputs_bit_exact():
     assert np.array_equal(got, want), f"max diff {np.abs(got - want).max()}"
 
 
+def _two_bucket_blocks(x, NT):
+    """Counts of (32-row block, 32-key block) pairs at or below the diagonal
+    whose time-difference range [nearest, farthest] spans exactly two
+    neighbouring log2 buckets (bucket = bit length of |dt|): those with
+    every key at or before every row, and those whose ranges overlap."""
+    def bucket(dt):
+        return min(int(dt).bit_length(), NT - 1)
+    keys_first = overlap = 0
+    for b in range(x.B):
+        t = x.ts[x.offsets[b]:x.offsets[b + 1]]
+        L = len(t)
+        for r0 in range(0, L, 32):
+            rt = t[r0:min(r0 + 32, L)]
+            for k0 in range(0, r0 + 1, 32):
+                kt = t[k0:min(k0 + 32, L)]
+                lo = max(0, rt.min() - kt.max(), kt.min() - rt.max())
+                hi = max(rt.max() - kt.min(), kt.max() - rt.min())
+                if bucket(hi) - bucket(lo) == 1:
+                    if kt.max() <= rt.min():
+                        keys_first += 1
+                    else:
+                        overlap += 1
+    return keys_first, overlap
+
+
+def test_identity_two_bucket_time_blocks_bit_exact():
+    """Integer inputs and identity activation over timestamps whose 32x32
+    blocks often span exactly two log2 time buckets, both with every key
+    before the block's rows (the compare-and-select path) and overlapping
+    them (the sad-and-shift path): the GPU equals the oracle bit for bit."""
+    rng = np.random.default_rng(37)
+    lengths = [700, 260, 97]
+    x = synth.make_attn(37, lengths, H=2, d=128, P=1024, NT=32, alpha=1 / 64, dtype="bf16")
+    T = x.T
+    # regular 10 s steps; random 1-49 s steps; simultaneous events with a 1 s
+    # step at events 40 and 80 (32-row blocks spanning one second: buckets 0
+    # and 1 on the diagonal)
+    gaps = [np.full(700, 10, np.int64), rng.integers(1, 50, 260).astype(np.int64),
+            np.isin(np.arange(97), (40, 80)).astype(np.int64)]
+    for b in range(x.B):
+        s0, s1 = int(x.offsets[b]), int(x.offsets[b + 1])
+        x.ts[s0:s1] = 1_700_000_000 + np.cumsum(gaps[b][: s1 - s0])
+    keys_first, overlap = _two_bucket_blocks(x, 32)
+    log(f"two-bucket blocks: {keys_first} with keys first, {overlap} overlapping")
+    assert keys_first >= 20 and overlap >= 2
+    x.q = rng.integers(-1, 2, size=(T, 2, 128)).astype(np.float32)
+    x.k = (rng.random((T, 2, 128)) < 0.1).astype(np.float32)
+    x.v = rng.integers(-2, 3, size=(T, 2, 128)).astype(np.float32)
+    x.rab_pos = rng.integers(-3, 4, size=1024).astype(np.float32)
+    x.rab_time = rng.integers(-3, 4, size=32).astype(np.float32)
+    d = DeviceAttn(x)
+    o, _ = run_attn(d, with_u=False, act=1)
+    import torch
+    torch.cuda.synchronize()
+    ref = oracle_attn(x, act=1)
+    want = synth.bf16_round(ref.astype(np.float32))
+    got = host_f32(o)
+    assert np.array_equal(got, want), f"max diff {np.abs(got - want).max()}"
+
+
 def test_fp32_identity_integer_inputs_exact():
     rng = np.random.default_rng(32)
     x = synth.make_attn(32, [3, 64, 65, 100], H=2, d=32, P=50, NT=32, alpha=1 / 64, dtype="f32")
