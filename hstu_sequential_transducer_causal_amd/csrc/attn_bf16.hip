@@ -16,8 +16,9 @@
 //     directly the A operand of O += A V.  Q stays in registers.
 //   * K and V tiles are staged row-major into a 4-stage LDS ring by buffer
 //     loads that write LDS directly (no registers, no VALU; rows past the
-//     sequence end fall outside the buffer's range and arrive as zeros), three
-//     tiles ahead of their use.  V is read transposed by ds_read_b64_tr_b16,
+//     sequence end fall outside the buffer's range and arrive as zeros),
+//     issued in pairs of tiles one to two steps ahead of their use, with one
+//     workgroup barrier per two tiles.  V is read transposed by ds_read_b64_tr_b16,
 //     so the B operand of A V needs no shuffle.
 //   * Timestamps arrive pre-encoded (a small preparation kernel): per row
 //     e = 2 (t - t_first) + 2^31, exact when |t - t_first| < 2^30, and per
@@ -119,9 +120,9 @@ struct Smem {
 // that the swizzle puts there; and the codes of keys 8w .. 8w+7 with one
 // 4-byte-per-lane load (lanes 8-63 read out of range and write zeros into
 // the rest of the wave's own 64-entry region).  Every wave thus issues the
-// same 5 loads per tile, and the wait for a tile is one constant count.
-// Tiles past the end of the list are loaded from out of range (zeros into a
-// stage nobody reads), so the ring needs no special last tiles either.
+// same 5 loads per tile.  Tiles past the end of the list are loaded from out
+// of range (zeros into a stage nobody reads), so the ring needs no special
+// last tiles either.
 struct TileDma {
     u32x4 krs, vrs, wrs;
     uint32_t koff[2], voff[2];
@@ -129,7 +130,6 @@ struct TileDma {
     uint32_t code_off;            // lane < 8: byte offset of the code of key 8 wave + lane; else out of range
 };
 
-constexpr int kLoadsPerTile = 5;
 constexpr uint32_t kFarOffset = 0x40000000u;   // past every buffer's range (num_records < 2^31)
 
 // Scalar offset of key tile kt, or (far) an offset past the buffer's range.
@@ -150,8 +150,9 @@ __device__ __forceinline__ RingLds ring_lds(const uint8_t* smem_raw) {
                    b + (uint32_t)offsetof(Smem, tsk)};
 }
 
-// The three parts of a tile's loads go out at different points of the
-// previous tiles' work, so that no wave stalls long on a full load queue.
+// A pair of tiles' loads goes out in two parts: K and codes after the pair's
+// barrier, V in the middle of the step, so that no wave stalls long on a
+// full load queue.
 __device__ __forceinline__ void issue_k(const TileDma& d, const RingLds& r, int stage, int kt, bool far, int wave) {
     const uint32_t kl = r.k + (uint32_t)(stage * (BN * kRowBytes) + 2 * wave * 1024);
     const uint32_t ksoff = uniu(tile_soff(kt, far, d.ktile));
@@ -346,16 +347,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             const int pos = p0 + it;
             return pos < a_end ? pos : kb_begin + (pos - a_end);
         };
-        // load groups: after the barrier of tile t go out V(t+2), then (mid-step)
-        // K(t+3) and the codes of t+3, 5 loads per group; the prologue sends
-        // the groups of t = -3 (its V part from out of range), -2 and -1
-        issue_v(dma, ring, kStages - 1, 0, true, wave);
+        // loads go out in pairs of tiles at every second tile (pair_sync and
+        // pair_rest below); before the first pair's barrier: K and codes of
+        // tiles 0 and 1, V of tile 0
 #pragma unroll
-        for (int pre = 0; pre < kStages - 1; ++pre) {
-            if (pre > 0) issue_v(dma, ring, pre - 1, tile_of(pre - 1), pre - 1 >= ntiles, wave);
+        for (int pre = 0; pre < 2; ++pre) {
             issue_k(dma, ring, pre, tile_of(pre), pre >= ntiles, wave);
             issue_codes(dma, ring, pre, tile_of(pre), pre >= ntiles, wave);
         }
+        issue_v(dma, ring, 0, tile_of(0), 0 >= ntiles, wave);
 
         // ---- this wave's 32 query rows
         const int wrow0 = qt * BM + wave * 32;
@@ -438,20 +438,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         const uint32_t ptab_hi = lds_addr(ptab) + 8u * (uint32_t)Dhi;   // pair Dhi: difference 0
         const int prow4 = prow - 4 * h2;   // the position term's row part for this lane's keys
 
-        // the barrier of tile it.  Before it this wave's K(it), codes(it) and
-        // V(it) have landed (in flight may stay the rest of the group of
-        // it-2, K and codes of it+1, and the whole group of it-1: 8 loads),
-        // after it every wave's have.  Then V(it+2) goes into the V half of
-        // stage it+2 = it-2, whose V(it-2) every wave has consumed (its AV
-        // products ran in step it-1).  No wait for this wave's own LDS reads
-        // is needed: every read of step it-1 was consumed in that step (V(it-1)
-        // is read in step it, from the half V(it+3) refills after the next
-        // barrier).
-        auto tile_sync = [&](int it, int st) {
-            wait_vmcnt(kLoadsPerTile + 3);
+        // One barrier per two tiles, at every even tile it (tile t lives in
+        // stage t & 3).  Before it this wave waits for all of its loads: they
+        // were issued at or before the previous barrier and are K and codes of
+        // it and it+1 and V of it-1 and it, everything steps it and it+1 read
+        // (V(t) is read in step t+1); after it every wave's have landed and
+        // every wave has finished step it-1.  Then K and codes of it+2 and it+3
+        // go into stages it-2 and it-1, whose K and codes were last read in
+        // steps it-2 and it-1, and mid-step (pair_rest) V of it+1 and it+2
+        // into stages it-3 and it-2, whose V was last read in steps it-2 and
+        // it-1.  While a wave is in step it or it+1, no load in flight writes
+        // what those steps read (K and codes of it, it+1, V of it-1, it).  Odd
+        // tiles take no barrier and issue no loads.  Every wave takes the
+        // barriers of all even tiles up to ntiles, whichever tiles it computes.
+        auto pair_sync = [&](int it, int st) {
+            wait_vmcnt(0);
             lds_barrier();
-            const int t2 = it + kStages - 2;
-            issue_v(dma, ring, (st + kStages - 2) & (kStages - 1), tile_of(t2), t2 >= ntiles, wave);
+#pragma unroll
+            for (int dd = 2; dd <= 3; ++dd) {
+                const int t = it + dd;
+                const int s2 = (st + dd) & (kStages - 1);
+                issue_k(dma, ring, s2, tile_of(t), t >= ntiles, wave);
+                issue_codes(dma, ring, s2, tile_of(t), t >= ntiles, wave);
+            }
         };
 
         // bias of tile it (as the initial accumulator, plus a constant) and
@@ -637,13 +646,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
                 for (int e = 0; e < 4; ++e) pk[c][e] = pack_bf16x2(a[8 * c + 2 * e], a[8 * c + 2 * e + 1]);
         };
 
-        // the K and key-code parts of tile it+3's loads, into the K half of
-        // stage it+3 = it-1
-        auto issue_rest = [&](int it, int st) {
-            const int t3 = it + kStages - 1;
-            const int st3 = (st + kStages - 1) & (kStages - 1), kt3 = tile_of(t3);
-            issue_k(dma, ring, st3, kt3, t3 >= ntiles, wave);
-            issue_codes(dma, ring, st3, kt3, t3 >= ntiles, wave);
+        // V of tiles it+1 and it+2 (even it), into the V halves of stages
+        // it-3 and it-2
+        auto pair_rest = [&](int it, int st) {
+#pragma unroll
+            for (int dd = 1; dd <= 2; ++dd) {
+                const int t = it + dd;
+                issue_v(dma, ring, (st + dd) & (kStages - 1), tile_of(t), t >= ntiles, wave);
+            }
         };
 
         // V^T fragments of the tile in stage st (see read_v_tile)
@@ -663,8 +673,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         // one pipeline step: S(it) into accN while tile it-1 (S in accC)
         // is finished
         // (st = it & 3: a compile-time constant in the unrolled loop)
-        auto step = [&](int st, int it, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
-            tile_sync(it, st);
+        auto step = [&](int st, int it, bool even, f32x16& accC, float caddC, f32x16& accN, float& caddN) {
+            if (even) pair_sync(it, st);
             bf16x8 kf[8];
             // the bias goes in as the first MFMA's C operand only: the chain
             // then writes the loop's accumulator registers directly
@@ -675,7 +685,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
             for (int r = 0; r < 4; ++r) act_one(accC, c2, r);
             time_bias(st, f, bias, caddN);
-            issue_rest(it, st);
+            if (even) pair_rest(it, st);
             // S(it) = K Q^T: a dependent chain of 8 MFMAs, each followed by
             // the activation of 1.5 elements of S(it-1)
 #pragma unroll
@@ -721,40 +731,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
         }
         nuse = uni(nuse);
 
-        if (nuse > 0) {
-            f32x16 accA, accB;
-            float caddA = 0.0f, caddB = 0.0f;
-            // prologue: S(0)
-            {
-                tile_sync(0, 0);
-                bf16x8 kf[8];
-                f32x16 bias;
-                const TileFacts f = tile_bias(0, 0, bias, caddA, kf);
-                time_bias(0, f, bias, caddA);
-                issue_rest(0, 0);
-#pragma unroll
-                for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], kc == 0 ? bias : accA);
-            }
-            // steps 1, 2, 3, 4, ...: stages 1, 2, 3, 0, ..., S alternating
-            // between the two accumulators; four steps per iteration, then
-            // the last 0-3 with the stage computed
-            int it = 1;
-            for (; it + 3 < nuse; it += 4) {
-                step(1, it, accA, caddA, accB, caddB);
-                step(2, it + 1, accB, caddB, accA, caddA);
-                step(3, it + 2, accA, caddA, accB, caddB);
-                step(0, it + 3, accB, caddB, accA, caddA);
-            }
-            for (; it + 1 < nuse; it += 2) {
-                step(it & (kStages - 1), it, accA, caddA, accB, caddB);
-                step((it + 1) & (kStages - 1), it + 1, accB, caddB, accA, caddA);
-            }
-            if (it < nuse) {
-                step(it & (kStages - 1), it, accA, caddA, accB, caddB);
-                accA = accB;
-                caddA = caddB;
-            }
-            // epilogue: finish the last tile
+        f32x16 accA, accB;
+        float caddA = 0.0f, caddB = 0.0f;
+        // the activation of the last tile, S(nuse-1) in accA, and its A V
+        auto finish_last = [&]() {
             {
                 const float c2 = act_const(caddA);
 #pragma unroll
@@ -769,10 +749,54 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
                     oacc[nb] = mfma32(__builtin_bit_cast(bf16x8, pk[c]), __builtin_bit_cast(bf16x8, vf[c][nb]), oacc[nb]);
+        };
+        if (nuse > 0) {
+            // prologue: S(0)
+            {
+                pair_sync(0, 0);
+                bf16x8 kf[8];
+                f32x16 bias;
+                const TileFacts f = tile_bias(0, 0, bias, caddA, kf);
+                time_bias(0, f, bias, caddA);
+                pair_rest(0, 0);
+#pragma unroll
+                for (int kc = 0; kc < 8; ++kc) accA = mfma32(kf[kc], qf[kc], kc == 0 ? bias : accA);
+            }
+            // steps 1, 2, 3, 4, ...: stages 1, 2, 3, 0, ..., S alternating
+            // between the two accumulators; four steps per iteration, then
+            // the last 0-3 with the stage computed (it is odd at each loop's
+            // head, so every step's parity is known at compile time)
+            int it = 1;
+            for (; it + 3 < nuse; it += 4) {
+                step(1, it, false, accA, caddA, accB, caddB);
+                step(2, it + 1, true, accB, caddB, accA, caddA);
+                step(3, it + 2, false, accA, caddA, accB, caddB);
+                step(0, it + 3, true, accB, caddB, accA, caddA);
+            }
+            for (; it + 1 < nuse; it += 2) {
+                step(it & (kStages - 1), it, false, accA, caddA, accB, caddB);
+                step((it + 1) & (kStages - 1), it + 1, true, accB, caddB, accA, caddA);
+            }
+            if (it < nuse) {
+                step(it & (kStages - 1), it, false, accA, caddA, accB, caddB);
+                accA = accB;
+                caddA = caddB;
+            }
+            // the last tile nuse-1 even: its V landed at its own barrier
+            if (nuse & 1) finish_last();
         }
-        for (int it = nuse; it < ntiles; ++it) {
-            tile_sync(it, it & (kStages - 1));
-            issue_rest(it, it & (kStages - 1));
+        // the barriers (and loads) of the remaining even tiles up to ntiles;
+        // the last tile nuse-1 odd: its V lands by the barrier of tile nuse
+        int it_rest = nuse;
+        if (nuse > 0 && !(nuse & 1)) {
+            pair_sync(nuse, nuse & (kStages - 1));
+            finish_last();
+            pair_rest(nuse, nuse & (kStages - 1));
+            it_rest = nuse + 2;
+        }
+        for (int it = (it_rest + 1) & ~1; it <= ntiles; it += 2) {
+            pair_sync(it, it & (kStages - 1));
+            pair_rest(it, it & (kStages - 1));
         }
 
         // ---------- O = alpha * acc, rows < L only: bf16 into O (non-temporal:
