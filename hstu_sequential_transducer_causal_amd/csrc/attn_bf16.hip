@@ -831,7 +831,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
             if (qt * BM + lr < Lq)
                 p.rowmap[row0q + qt * BM + lr] = slot < 0 ? -1 : (slot | (npieces << 16) | (lr << 23));
         }
-        lds_barrier();   // this item's LDS use is over before the next item starts
+        // No barrier here: the next item's first LDS writes (its tile loads,
+        // a table reload) come after the barrier that publishes the next work
+        // index, which every wave reaches only once it is done with this
+        // item; tid 0's write of that index and the item record is safe
+        // earlier, since every wave read this item's record before its first
+        // tile barrier.
     }
 }
 
