@@ -27,6 +27,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -537,15 +538,23 @@ KERNEL_SRCS = [os.path.join(ROOT, "hstu_sequential_transducer_causal_amd", "csrc
                for f in ("attn_bf16.hip", "tile_ops.h", "hstu_device.h")]
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments, blank lines and runs of spaces
+    (string literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(" ".join(l.split()) for l in text.splitlines() if l.strip())
+
+
 def kernel_hash() -> str:
-    """Hash of the sources the attention-core kernel is compiled from and of
-    its compiler flags."""
+    """Hash of the code (comments left out) of the sources the attention-core
+    kernel is compiled from and of its compiler flags."""
     import hashlib
     from hstu_sequential_transducer_causal_amd import build
     h = hashlib.sha256()
     for src in KERNEL_SRCS:
-        with open(src, "rb") as f:
-            h.update(f.read())
+        with open(src, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     flags = [f for f in build.CXXFLAGS if f != "-I" and not os.path.isabs(f)]   # (no paths)
     h.update(repr(flags + build.EXTRA_FLAGS.get("attn_bf16.hip", [])).encode())
     return h.hexdigest()[:16]

@@ -42,8 +42,8 @@
 //   * Software pipeline over the key tiles: while S(t) is being built (its
 //     LDS reads, bias, and the dependent chain of 8 QK^T MFMAs), the
 //     activation of S(t-1) runs on the VALU between those MFMAs, and then
-//     O += A(t-1) V(t-1) is issued; V(t) is read into registers at the end of
-//     the step.  Fragment addresses are one per-lane base XOR constants, so
+//     V(t-1) is read into registers and O += A(t-1) V(t-1) is issued at the
+//     end of the step.  Fragment addresses are one per-lane base XOR constants, so
 //     the loop keeps two address registers and never touches scratch (a
 //     scratch reload would wait for every tile load in flight).
 //   * Persistent grid: workgroups pull items (longest first) from the
@@ -406,10 +406,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(Params p, const 
 
         // ---- software pipeline over the key tiles.  Iteration it builds
         //      S(it) while it finishes tile it-1: the activation of S(it-1)
-        //      runs on the VALU while S(it)'s LDS reads are in flight, then
-        //      the MFMAs of S(it) = K Q^T and of O += A(it-1) V(it-1) go out
-        //      interleaved (two independent chains keep the matrix pipe
-        //      busy), and V(it) is read into registers for the next iteration.
+        //      runs on the VALU while S(it)'s LDS reads are in flight and then
+        //      between the dependent MFMAs of S(it) = K Q^T; then V(it-1) is
+        //      read into registers and O += A(it-1) V(it-1) goes out.
         u32x2 krange_next = {0u, 0u};
         if (!kCross || ntiles > 0) krange_next = kstats[bbase + tile_of(0)];
         // Per-lane LDS addresses of the fragments in stage 0 (a stage's base

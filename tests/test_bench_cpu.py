@@ -39,3 +39,11 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    src = "int f(int x) {  // the input\n    /* twice */ return 2 * x;\n}\n"
+    same = "// a header\nint f(int x) {\n    return 2 * x;   /* doubled */\n}\n"
+    other = "int f(int x) {\n    return 3 * x;\n}\n"
+    assert bench._code_only(src) == bench._code_only(same)
+    assert bench._code_only(src) != bench._code_only(other)
